@@ -1,0 +1,682 @@
+// sd_runtime.hip - host runtime behind the C ABI of libsparse_decode.so:
+// configuration checks, device allocation, per-layer page pools and page
+// tables, per-call validation and kernel launches.  No exception crosses the
+// ABI; every failure is a negative status plus a message in sd_last_error().
+#include <hip/hip_runtime.h>
+
+#include <algorithm>
+#include <cmath>
+#include <cstdarg>
+#include <cstdio>
+#include <cstring>
+#include <new>
+#include <string>
+#include <vector>
+
+#include "sd_internal.h"
+
+using namespace sd;
+
+namespace {
+
+struct Layer {
+  LayerDev dev{};
+  int32_t *h_pt = nullptr;           // pinned host mirror of the page table
+  std::vector<int32_t> len;          // tokens per sequence
+  std::vector<int32_t> free_pages;   // stack; back() is handed out next
+};
+
+}  // namespace
+
+struct sd_ctx {
+  sd_config cfg{};
+  std::vector<int32_t> S, ppm;
+  int D = 0, Hq = 0, Hkv = 0, G = 0, pps = 0;
+  hipStream_t stream = nullptr;
+  int device = 0;
+  std::vector<HeadInfo> heads;
+  HeadInfo *d_heads = nullptr;
+  Dims dims{};
+  Scratch sc{};
+  std::vector<Layer> layers;
+  int32_t k_cap = 0, p_cap = 0;
+  std::vector<int32_t> kcap_h, ucap_h;
+  // attend -> fuse hand-over state
+  int pend_layer = -2;
+  std::vector<int32_t> pend_seqs;
+  int32_t pend_pcap = 0;
+  std::string err;
+  std::vector<void *> dev_allocs;
+};
+
+namespace {
+
+sd_status fail(sd_ctx *c, sd_status st, const char *fmt, ...) {
+  char buf[512];
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(buf, sizeof buf, fmt, ap);
+  va_end(ap);
+  if (c) c->err = buf;
+  return st;
+}
+
+#define SD_HIP(ctx, call)                                                    \
+  do {                                                                       \
+    hipError_t e_ = (call);                                                  \
+    if (e_ != hipSuccess)                                                    \
+      return fail(ctx, SD_EHIP, "%s failed: %s", #call, hipGetErrorString(e_)); \
+  } while (0)
+
+int64_t cdiv(int64_t a, int64_t b) { return (a + b - 1) / b; }
+
+// k for a sequence of N tokens on head h (budget as parts per million of N,
+// whole blocks, capped by the number of candidate blocks).
+int64_t n_candidates(int64_t N, int S, int n_s, int W) {
+  // blocks entirely inside the sinks: floor(ns/S); entirely inside the
+  // window: n_blk - ceil(wlo/S); the rest hold a token outside D.
+  int64_t ns = std::min<int64_t>(n_s, N), wlo = std::max<int64_t>(0, N - W);
+  if (ns >= wlo) return 0;
+  return cdiv(wlo, S) - ns / S;
+}
+
+int64_t k_of(int64_t N, int S, int ppm, int n_s, int W) {
+  int64_t den = 1000000LL * S;
+  int64_t k = (int64_t(ppm) * N + den - 1) / den;
+  return std::min(k, n_candidates(N, S, n_s, W));
+}
+
+// splitmix64: seeded permutation of the free list.
+uint64_t splitmix64(uint64_t &x) {
+  uint64_t z = (x += 0x9E3779B97F4A7C15ull);
+  z = (z ^ (z >> 30)) * 0xBF58476D1CE4E5B9ull;
+  z = (z ^ (z >> 27)) * 0x94D049BB133111EBull;
+  return z ^ (z >> 31);
+}
+
+template <class T>
+sd_status dev_alloc(sd_ctx *c, T **p, size_t count) {
+  *p = nullptr;
+  if (count == 0) count = 1;
+  hipError_t e = hipMalloc(reinterpret_cast<void **>(p), count * sizeof(T));
+  if (e != hipSuccess) {
+    (void)hipGetLastError();
+    return fail(c, SD_ENOMEM, "hipMalloc of %zu bytes failed: %s",
+                count * sizeof(T), hipGetErrorString(e));
+  }
+  c->dev_allocs.push_back(*p);
+  return SD_OK;
+}
+
+void free_all(sd_ctx *c) {
+  for (void *p : c->dev_allocs) (void)hipFree(p);
+  c->dev_allocs.clear();
+  for (auto &L : c->layers)
+    if (L.h_pt) (void)hipHostFree(L.h_pt);
+  c->layers.clear();
+}
+
+// Sequence arguments shared by the decode calls.
+sd_status check_seqs(sd_ctx *c, int32_t layer, int32_t n_seqs,
+                     const int32_t *seq_ids) {
+  if (layer < 0 || layer >= c->cfg.num_layers)
+    return fail(c, SD_EINVAL, "layer %d out of range [0,%d)", layer,
+                c->cfg.num_layers);
+  if (n_seqs < 0) return fail(c, SD_EINVAL, "n_seqs %d < 0", n_seqs);
+  if (n_seqs > 0 && !seq_ids) return fail(c, SD_EINVAL, "seq_ids is NULL");
+  std::vector<char> seen(c->cfg.max_seqs, 0);
+  for (int i = 0; i < n_seqs; ++i) {
+    int s = seq_ids[i];
+    if (s < 0 || s >= c->cfg.max_seqs)
+      return fail(c, SD_EINVAL, "seq_ids[%d]=%d out of range [0,%d)", i, s,
+                  c->cfg.max_seqs);
+    if (seen[s]) return fail(c, SD_EINVAL, "seq id %d repeated in one call", s);
+    seen[s] = 1;
+  }
+  return SD_OK;
+}
+
+void fill_batch(const sd_ctx *c, int layer, const int32_t *seq_ids, int base,
+                int n, SeqBatch *b, int *max_blocks) {
+  b->n = n;
+  int mb = 0;
+  for (int i = 0; i < n; ++i) {
+    b->seq[i] = seq_ids[base + i];
+    b->len[i] = c->layers[layer].len[seq_ids[base + i]];
+    for (int h = 0; h < c->Hkv; ++h)
+      mb = std::max<int>(mb, (int)cdiv(b->len[i], c->S[h]));
+  }
+  if (max_blocks) *max_blocks = mb;
+}
+
+__attribute__((format(printf, 3, 4))) void report(char *err, size_t err_len,
+                                                  const char *fmt, ...) {
+  if (!err || !err_len) return;
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(err, err_len, fmt, ap);
+  va_end(ap);
+}
+
+}  // namespace
+
+// ---------------------------------------------------------------------------
+extern "C" {
+
+sd_status sd_validate_config(const sd_config *cfg, char *err, size_t err_len) {
+#define bad(...) (report(err, err_len, __VA_ARGS__), SD_EINVAL)
+  if (!cfg) return bad("config is NULL");
+  if (cfg->max_seqs < 1) return bad("max_seqs %d < 1", cfg->max_seqs);
+  if (cfg->num_layers < 1) return bad("num_layers %d < 1", cfg->num_layers);
+  if (cfg->num_kv_heads < 1 || cfg->num_kv_heads > SD_MAX_KV_HEADS)
+    return bad("num_kv_heads %d outside [1,%d]", cfg->num_kv_heads, SD_MAX_KV_HEADS);
+  if (cfg->num_q_heads < 1 || cfg->num_q_heads % cfg->num_kv_heads != 0)
+    return bad("num_q_heads %d is not a positive multiple of num_kv_heads %d",
+               cfg->num_q_heads, cfg->num_kv_heads);
+  if (cfg->num_q_heads / cfg->num_kv_heads > SD_MAX_GROUP)
+    return bad("group size %d > %d", cfg->num_q_heads / cfg->num_kv_heads,
+               SD_MAX_GROUP);
+  if (cfg->head_dim != 64 && cfg->head_dim != 128)
+    return bad("head_dim %d not in {64,128}", cfg->head_dim);
+  if (cfg->page_size != SD_PAGE_SIZE)
+    return bad("page_size %d != %d", cfg->page_size, SD_PAGE_SIZE);
+  if (cfg->num_pages < 1) return bad("num_pages %d < 1", cfg->num_pages);
+  if (cfg->max_seq_len < 1) return bad("max_seq_len %d < 1", cfg->max_seq_len);
+  if (cfg->sink_tokens < 0) return bad("sink_tokens %d < 0", cfg->sink_tokens);
+  if (cfg->recent_window < 0) return bad("recent_window %d < 0", cfg->recent_window);
+  if (!cfg->block_size || !cfg->budget_ppm)
+    return bad("block_size / budget_ppm arrays are NULL");
+  for (int h = 0; h < cfg->num_kv_heads; ++h) {
+    int S = cfg->block_size[h];
+    if (S < SD_PAGE_SIZE || S > SD_MAX_BLOCK || S % SD_PAGE_SIZE != 0)
+      return bad("block_size[%d]=%d is not a multiple of %d in [%d,%d]", h, S,
+                 SD_PAGE_SIZE, SD_PAGE_SIZE, SD_MAX_BLOCK);
+    if (cfg->budget_ppm[h] < 0 || cfg->budget_ppm[h] > 1000000)
+      return bad("budget_ppm[%d]=%d outside [0,1000000]", h, cfg->budget_ppm[h]);
+  }
+  if (!(cfg->softmax_scale >= 0.0f) || std::isinf(cfg->softmax_scale))
+    return bad("softmax_scale must be finite and >= 0");
+  if (!(cfg->maw_decay >= 0.0f && cfg->maw_decay < 1.0f))
+    return bad("maw_decay %g outside [0,1)", (double)cfg->maw_decay);
+  if (std::isnan(cfg->maw_beta) || std::isinf(cfg->maw_beta))
+    return bad("maw_beta must be finite");
+  if (err && err_len) err[0] = 0;
+  return SD_OK;
+#undef bad
+}
+
+sd_status sparse_decode_init(const sd_config *cfg, sd_ctx **out) {
+  if (!out) return SD_EINVAL;
+  *out = nullptr;
+  char msg[256];
+  sd_status st = sd_validate_config(cfg, msg, sizeof msg);
+  sd_ctx *c = new (std::nothrow) sd_ctx();
+  if (!c) return SD_ENOMEM;
+  if (st != SD_OK) {
+    c->err = msg;
+    *out = c;  // caller can read the message, then destroy
+    return st;
+  }
+  c->cfg = *cfg;
+  c->Hq = cfg->num_q_heads;
+  c->Hkv = cfg->num_kv_heads;
+  c->G = c->Hq / c->Hkv;
+  c->D = cfg->head_dim;
+  c->pps = (int)cdiv(cfg->max_seq_len, kPage);
+  c->S.assign(cfg->block_size, cfg->block_size + c->Hkv);
+  c->ppm.assign(cfg->budget_ppm, cfg->budget_ppm + c->Hkv);
+  c->cfg.block_size = nullptr;
+  c->cfg.budget_ppm = nullptr;
+  c->stream = reinterpret_cast<hipStream_t>(cfg->stream);
+  *out = c;
+  if (hipGetDevice(&c->device) != hipSuccess)
+    return fail(c, SD_EHIP, "no HIP device");
+
+  const int max_seqs = cfg->max_seqs;
+  // per-head geometry, capacities
+  c->heads.resize(c->Hkv);
+  c->kcap_h.resize(c->Hkv);
+  c->ucap_h.resize(c->Hkv);
+  int64_t summ_elems = 0, maw_elems = 0;
+  int key_stride = 1;
+  for (int h = 0; h < c->Hkv; ++h) {
+    HeadInfo &hi = c->heads[h];
+    hi.S = c->S[h];
+    hi.ppm = c->ppm[h];
+    hi.nbmax = (int)cdiv(cfg->max_seq_len, hi.S);
+    hi.chunk_blocks = kChunkTokens / hi.S;
+    hi.summ_off = summ_elems;
+    hi.maw_off = maw_elems;
+    summ_elems += (int64_t)max_seqs * (c->D / 4) * hi.nbmax * 8;
+    maw_elems += (int64_t)max_seqs * hi.nbmax;
+    key_stride = std::max(key_stride, hi.nbmax);
+    int64_t kc = 0;
+    for (int64_t N : {(int64_t)cfg->max_seq_len})
+      kc = std::max<int64_t>(kc, cdiv((int64_t)hi.ppm * N, 1000000LL * hi.S));
+    kc = std::min<int64_t>(kc, hi.nbmax);
+    c->kcap_h[h] = (int)std::max<int64_t>(kc, 1);
+    int64_t uc = cdiv(cfg->sink_tokens, hi.S) + kc + cdiv(cfg->recent_window, hi.S) + 1;
+    c->ucap_h[h] = (int)std::min<int64_t>(uc, hi.nbmax);
+    c->k_cap = std::max(c->k_cap, c->kcap_h[h]);
+    c->p_cap = std::max<int32_t>(c->p_cap, (int32_t)cdiv(c->ucap_h[h], hi.chunk_blocks));
+  }
+  int u_cap = *std::max_element(c->ucap_h.begin(), c->ucap_h.end());
+
+  sd_status s;
+  if ((s = dev_alloc(c, &c->d_heads, c->Hkv)) != SD_OK) return s;
+  SD_HIP(c, hipMemcpy(c->d_heads, c->heads.data(), sizeof(HeadInfo) * c->Hkv,
+                      hipMemcpyHostToDevice));
+
+  c->dims.Hq = c->Hq;
+  c->dims.Hkv = c->Hkv;
+  c->dims.G = c->G;
+  c->dims.d = c->D;
+  c->dims.pages_per_seq = c->pps;
+  c->dims.n_sink = cfg->sink_tokens;
+  c->dims.window = cfg->recent_window;
+  float scale = cfg->softmax_scale > 0.0f ? cfg->softmax_scale
+                                          : (float)(1.0 / std::sqrt((double)c->D));
+  c->dims.scale_log2 = (float)((double)scale * 1.4426950408889634);
+  c->dims.maw_decay = cfg->maw_decay > 0.0f ? cfg->maw_decay : 0.95f;
+  c->dims.maw_beta = cfg->maw_beta;
+  c->dims.key_stride = key_stride;
+  c->dims.u_cap = u_cap;
+
+  // scratch
+  if ((s = dev_alloc(c, &c->sc.qpm, (size_t)kLaunchSeqs * c->Hq * c->D)) != SD_OK) return s;
+  if ((s = dev_alloc(c, &c->sc.keys, (size_t)max_seqs * c->Hkv * key_stride)) != SD_OK) return s;
+  if ((s = dev_alloc(c, &c->sc.flags, (size_t)max_seqs * c->Hkv * key_stride)) != SD_OK) return s;
+  if ((s = dev_alloc(c, &c->sc.lmass, (size_t)max_seqs * c->Hq * u_cap)) != SD_OK) return s;
+  if ((s = dev_alloc(c, &c->sc.ublk, (size_t)max_seqs * c->Hkv * u_cap)) != SD_OK) return s;
+  if ((s = dev_alloc(c, &c->sc.ucnt, (size_t)max_seqs * c->Hkv)) != SD_OK) return s;
+  SD_HIP(c, hipMemset(c->sc.ucnt, 0, sizeof(int32_t) * max_seqs * c->Hkv));
+  SD_HIP(c, hipMemset(c->sc.flags, 0, (size_t)max_seqs * c->Hkv * key_stride));
+
+  // layers
+  c->layers.resize(cfg->num_layers);
+  const size_t pool = (size_t)cfg->num_pages * c->Hkv * kPage * c->D;
+  for (int l = 0; l < cfg->num_layers; ++l) {
+    Layer &L = c->layers[l];
+    if ((s = dev_alloc(c, &L.dev.k, pool)) != SD_OK) return s;
+    if ((s = dev_alloc(c, &L.dev.v, pool)) != SD_OK) return s;
+    if ((s = dev_alloc(c, &L.dev.pt, (size_t)max_seqs * c->pps)) != SD_OK) return s;
+    if ((s = dev_alloc(c, &L.dev.summ, (size_t)summ_elems)) != SD_OK) return s;
+    if ((s = dev_alloc(c, &L.dev.maw, (size_t)maw_elems)) != SD_OK) return s;
+    SD_HIP(c, hipMemset(L.dev.pt, 0, sizeof(int32_t) * max_seqs * c->pps));
+    SD_HIP(c, hipMemset(L.dev.maw, 0, sizeof(float) * maw_elems));
+    SD_HIP(c, hipMemset(L.dev.summ, 0, sizeof(uint16_t) * summ_elems));
+    hipError_t e = hipHostMalloc(reinterpret_cast<void **>(&L.h_pt),
+                                 sizeof(int32_t) * max_seqs * c->pps, hipHostMallocDefault);
+    if (e != hipSuccess) return fail(c, SD_ENOMEM, "hipHostMalloc failed");
+    std::fill(L.h_pt, L.h_pt + (size_t)max_seqs * c->pps, 0);
+    L.len.assign(max_seqs, 0);
+    L.free_pages.resize(cfg->num_pages);
+    // back() is handed out first: page 0, 1, 2, ... in order
+    for (int p = 0; p < cfg->num_pages; ++p) L.free_pages[p] = cfg->num_pages - 1 - p;
+    if (cfg->page_shuffle_seed) {
+      uint64_t st64 = cfg->page_shuffle_seed * 0x100000001B3ull + (uint64_t)l;
+      for (int p = cfg->num_pages - 1; p > 0; --p) {
+        int j = (int)(splitmix64(st64) % (uint64_t)(p + 1));
+        std::swap(L.free_pages[p], L.free_pages[j]);
+      }
+    }
+  }
+  SD_HIP(c, hipDeviceSynchronize());
+  return SD_OK;
+}
+
+sd_status sparse_decode_destroy(sd_ctx *c) {
+  if (!c) return SD_EINVAL;
+  sd_status st = SD_OK;
+  if (!c->dev_allocs.empty() && hipStreamSynchronize(c->stream) != hipSuccess)
+    st = SD_EHIP;
+  free_all(c);
+  delete c;
+  return st;
+}
+
+sd_status sd_caps(const sd_ctx *c, int32_t *k_cap, int32_t *p_cap) {
+  if (!c) return SD_EINVAL;
+  if (k_cap) *k_cap = c->k_cap;
+  if (p_cap) *p_cap = c->p_cap;
+  return SD_OK;
+}
+
+const char *sd_last_error(const sd_ctx *c) {
+  if (!c) return "null context";
+  return c->err.c_str();
+}
+
+sd_status sd_sync(sd_ctx *c) {
+  if (!c) return SD_EINVAL;
+  SD_HIP(c, hipStreamSynchronize(c->stream));
+  return SD_OK;
+}
+
+sd_status sd_seq_len(const sd_ctx *c, int32_t layer, int32_t seq, int32_t *len) {
+  if (!c || !len) return SD_EINVAL;
+  if (layer < 0 || layer >= c->cfg.num_layers || seq < 0 || seq >= c->cfg.max_seqs)
+    return SD_EINVAL;
+  *len = c->layers[layer].len[seq];
+  return SD_OK;
+}
+
+sd_status append_kv(sd_ctx *c, int32_t layer, int32_t n_seqs,
+                    const int32_t *seq_ids, const int32_t *n_new,
+                    const void *k_bf16, const void *v_bf16) {
+  if (!c) return SD_EINVAL;
+  sd_status s = check_seqs(c, layer, n_seqs, seq_ids);
+  if (s != SD_OK) return s;
+  if (n_seqs > 0 && !n_new) return fail(c, SD_EINVAL, "n_new is NULL");
+  Layer &L = c->layers[layer];
+  int64_t total = 0, pages_needed = 0;
+  for (int i = 0; i < n_seqs; ++i) {
+    if (n_new[i] < 0) return fail(c, SD_EINVAL, "n_new[%d]=%d < 0", i, n_new[i]);
+    int64_t nl = (int64_t)L.len[seq_ids[i]] + n_new[i];
+    if (nl > c->cfg.max_seq_len)
+      return fail(c, SD_EINVAL, "sequence %d would hold %lld tokens > max_seq_len %d",
+                  seq_ids[i], (long long)nl, c->cfg.max_seq_len);
+    total += n_new[i];
+    pages_needed += cdiv(nl, kPage) - cdiv(L.len[seq_ids[i]], kPage);
+  }
+  if (total == 0) return SD_OK;
+  if (!k_bf16 || !v_bf16) return fail(c, SD_EINVAL, "k/v pointers are NULL");
+  if (pages_needed > (int64_t)L.free_pages.size())
+    return fail(c, SD_ENOMEM, "page pool of layer %d exhausted: need %lld pages, %zu free",
+                layer, (long long)pages_needed, L.free_pages.size());
+  // allocate pages (host mirror), then push the touched span to the device
+  int64_t lo = INT64_MAX, hi = -1;
+  for (int i = 0; i < n_seqs; ++i) {
+    int seq = seq_ids[i];
+    int64_t p0 = cdiv(L.len[seq], kPage), p1 = cdiv((int64_t)L.len[seq] + n_new[i], kPage);
+    for (int64_t p = p0; p < p1; ++p) {
+      L.h_pt[(size_t)seq * c->pps + p] = L.free_pages.back();
+      L.free_pages.pop_back();
+      lo = std::min<int64_t>(lo, (int64_t)seq * c->pps + p);
+      hi = std::max<int64_t>(hi, (int64_t)seq * c->pps + p);
+    }
+  }
+  if (hi >= 0)
+    SD_HIP(c, hipMemcpyAsync(L.dev.pt + lo, L.h_pt + lo, sizeof(int32_t) * (hi - lo + 1),
+                             hipMemcpyHostToDevice, c->stream));
+  int row = 0;
+  for (int base = 0; base < n_seqs; base += kLaunchSeqs) {
+    AppendBatch b{};
+    b.n = std::min(kLaunchSeqs, n_seqs - base);
+    int max_new = 0, max_touch = 0;
+    for (int i = 0; i < b.n; ++i) {
+      int seq = seq_ids[base + i];
+      b.seq[i] = seq;
+      b.old_len[i] = L.len[seq];
+      b.n_new[i] = n_new[base + i];
+      b.src_row[i] = row;
+      row += n_new[base + i];
+      max_new = std::max(max_new, b.n_new[i]);
+      if (b.n_new[i] > 0)
+        for (int h = 0; h < c->Hkv; ++h) {
+          int S = c->S[h];
+          int t = (b.old_len[i] + b.n_new[i] - 1) / S - b.old_len[i] / S + 1;
+          max_touch = std::max(max_touch, t);
+        }
+    }
+    SD_HIP(c, launch_append(L.dev, c->d_heads, c->dims, b, max_new, max_touch,
+                            static_cast<const uint16_t *>(k_bf16),
+                            static_cast<const uint16_t *>(v_bf16), c->stream));
+  }
+  for (int i = 0; i < n_seqs; ++i) L.len[seq_ids[i]] += n_new[i];
+  return SD_OK;
+}
+
+sd_status select_topk(sd_ctx *c, int32_t layer, int32_t n_seqs,
+                      const int32_t *seq_ids, const void *q_bf16,
+                      int32_t *blk_idx, int32_t *blk_cnt, int32_t k_cap) {
+  if (!c) return SD_EINVAL;
+  sd_status s = check_seqs(c, layer, n_seqs, seq_ids);
+  if (s != SD_OK) return s;
+  if (n_seqs == 0) return SD_OK;
+  if (!q_bf16 || !blk_idx || !blk_cnt)
+    return fail(c, SD_EINVAL, "q / blk_idx / blk_cnt pointer is NULL");
+  const Layer &L = c->layers[layer];
+  for (int i = 0; i < n_seqs; ++i)
+    for (int h = 0; h < c->Hkv; ++h) {
+      int64_t k = k_of(L.len[seq_ids[i]], c->S[h], c->ppm[h], c->cfg.sink_tokens,
+                       c->cfg.recent_window);
+      if (k > k_cap)
+        return fail(c, SD_EINVAL, "k_cap %d < %lld blocks needed (seq %d, kv head %d)",
+                    k_cap, (long long)k, seq_ids[i], h);
+    }
+  const uint16_t *q = static_cast<const uint16_t *>(q_bf16);
+  for (int base = 0; base < n_seqs; base += kLaunchSeqs) {
+    SeqBatch b;
+    int mb = 0;
+    fill_batch(c, layer, seq_ids, base, std::min(kLaunchSeqs, n_seqs - base), &b, &mb);
+    SD_HIP(c, launch_select(L.dev, c->d_heads, c->dims, c->sc, b, mb,
+                            q + (size_t)base * c->Hq * c->D,
+                            blk_idx + (size_t)base * c->Hkv * k_cap,
+                            blk_cnt + (size_t)base * c->Hkv, k_cap, c->stream));
+  }
+  return SD_OK;
+}
+
+sd_status sparse_attend(sd_ctx *c, int32_t layer, int32_t n_seqs,
+                        const int32_t *seq_ids, const void *q_bf16,
+                        const int32_t *blk_idx, const int32_t *blk_cnt,
+                        int32_t k_cap, float *o_part, float *lse_part,
+                        int32_t p_cap) {
+  if (!c) return SD_EINVAL;
+  sd_status s = check_seqs(c, layer, n_seqs, seq_ids);
+  if (s != SD_OK) return s;
+  if (n_seqs == 0) return SD_OK;
+  if (!q_bf16 || !blk_idx || !blk_cnt || !o_part || !lse_part)
+    return fail(c, SD_EINVAL, "a device pointer is NULL");
+  if (k_cap < 1) return fail(c, SD_EINVAL, "k_cap %d < 1", k_cap);
+  const Layer &L = c->layers[layer];
+  // every attended block must fit in p_cap chunks
+  for (int i = 0; i < n_seqs; ++i)
+    for (int h = 0; h < c->Hkv; ++h) {
+      int64_t N = L.len[seq_ids[i]];
+      int S = c->S[h];
+      int64_t k = std::min<int64_t>(k_cap, c->kcap_h[h]);
+      int64_t u = std::min<int64_t>(cdiv(N, S), cdiv(c->cfg.sink_tokens, S) + k +
+                                                    cdiv(c->cfg.recent_window, S) + 1);
+      int64_t need = cdiv(u, kChunkTokens / S);
+      if (need > p_cap)
+        return fail(c, SD_EINVAL, "p_cap %d < %lld partials needed (seq %d, kv head %d)",
+                    p_cap, (long long)need, seq_ids[i], h);
+    }
+  const uint16_t *q = static_cast<const uint16_t *>(q_bf16);
+  for (int base = 0; base < n_seqs; base += kLaunchSeqs) {
+    SeqBatch b;
+    fill_batch(c, layer, seq_ids, base, std::min(kLaunchSeqs, n_seqs - base), &b, nullptr);
+    SD_HIP(c, launch_attend(L.dev, c->d_heads, c->dims, c->sc, b,
+                            q + (size_t)base * c->Hq * c->D,
+                            blk_idx + (size_t)base * c->Hkv * k_cap,
+                            blk_cnt + (size_t)base * c->Hkv, k_cap,
+                            o_part + (size_t)base * c->Hq * p_cap * c->D,
+                            lse_part + (size_t)base * c->Hq * p_cap, p_cap, c->stream));
+  }
+  c->pend_layer = layer;
+  c->pend_seqs.assign(seq_ids, seq_ids + n_seqs);
+  c->pend_pcap = p_cap;
+  return SD_OK;
+}
+
+sd_status fuse_lse(sd_ctx *c, int32_t layer, int32_t n_seqs,
+                   const int32_t *seq_ids, const float *o_part,
+                   const float *lse_part, int32_t p_cap, float *o, float *lse) {
+  if (!c) return SD_EINVAL;
+  if (n_seqs < 0) return fail(c, SD_EINVAL, "n_seqs %d < 0", n_seqs);
+  if (n_seqs == 0) return SD_OK;
+  if (!o_part || !lse_part || !o || !lse)
+    return fail(c, SD_EINVAL, "a device pointer is NULL");
+  if (p_cap < 1) return fail(c, SD_EINVAL, "p_cap %d < 1", p_cap);
+  const bool with_maw = layer >= 0;
+  if (layer < -1) return fail(c, SD_EINVAL, "layer %d < -1", layer);
+  if (with_maw) {
+    sd_status s = check_seqs(c, layer, n_seqs, seq_ids);
+    if (s != SD_OK) return s;
+    if (c->pend_layer != layer ||
+        c->pend_seqs != std::vector<int32_t>(seq_ids, seq_ids + n_seqs))
+      return fail(c, SD_ESTATE,
+                  "fuse_lse(layer %d) does not follow sparse_attend of the same layer "
+                  "and sequences", layer);
+  }
+  for (int base = 0; base < n_seqs; base += kLaunchSeqs) {
+    SeqBatch b;
+    const int n = std::min(kLaunchSeqs, n_seqs - base);
+    if (with_maw) {
+      fill_batch(c, layer, seq_ids, base, n, &b, nullptr);
+    } else {
+      b.n = n;
+      for (int i = 0; i < n; ++i) b.seq[i] = b.len[i] = 0;
+    }
+    SD_HIP(c, launch_fuse(with_maw ? &c->layers[layer].dev : nullptr, c->d_heads,
+                          c->dims, c->sc, b, with_maw,
+                          o_part + (size_t)base * c->Hq * p_cap * c->D,
+                          lse_part + (size_t)base * c->Hq * p_cap, p_cap,
+                          o + (size_t)base * c->Hq * c->D,
+                          lse + (size_t)base * c->Hq, c->stream));
+  }
+  if (with_maw) c->pend_layer = -2;
+  return SD_OK;
+}
+
+sd_status sparse_decode_step(sd_ctx *c, int32_t layer, int32_t n_seqs,
+                             const int32_t *seq_ids, const void *q_bf16,
+                             int32_t *blk_idx, int32_t *blk_cnt, int32_t k_cap,
+                             float *o_part, float *lse_part, int32_t p_cap,
+                             float *o, float *lse) {
+  sd_status s = select_topk(c, layer, n_seqs, seq_ids, q_bf16, blk_idx, blk_cnt, k_cap);
+  if (s != SD_OK) return s;
+  s = sparse_attend(c, layer, n_seqs, seq_ids, q_bf16, blk_idx, blk_cnt, k_cap, o_part,
+                    lse_part, p_cap);
+  if (s != SD_OK) return s;
+  return fuse_lse(c, layer, n_seqs, seq_ids, o_part, lse_part, p_cap, o, lse);
+}
+
+sd_status sd_release_seq(sd_ctx *c, int32_t seq) {
+  if (!c) return SD_EINVAL;
+  if (seq < 0 || seq >= c->cfg.max_seqs)
+    return fail(c, SD_EINVAL, "seq id %d out of range", seq);
+  SD_HIP(c, hipStreamSynchronize(c->stream));
+  for (auto &L : c->layers) {
+    int64_t np = cdiv(L.len[seq], kPage);
+    for (int64_t p = np - 1; p >= 0; --p)
+      L.free_pages.push_back(L.h_pt[(size_t)seq * c->pps + p]);
+    L.len[seq] = 0;
+    for (int h = 0; h < c->Hkv; ++h) {
+      const HeadInfo &hi = c->heads[h];
+      SD_HIP(c, launch_fill_f32(L.dev.maw + hi.maw_off + (size_t)seq * hi.nbmax,
+                                hi.nbmax, 0.0f, c->stream));
+    }
+  }
+  if (c->pend_layer >= 0 &&
+      std::find(c->pend_seqs.begin(), c->pend_seqs.end(), seq) != c->pend_seqs.end())
+    c->pend_layer = -2;
+  SD_HIP(c, hipStreamSynchronize(c->stream));
+  return SD_OK;
+}
+
+sd_status sd_debug_bytes(const sd_ctx *c, int32_t what, int32_t layer,
+                         int32_t seq, size_t *bytes) {
+  if (!c || !bytes) return SD_EINVAL;
+  if (layer < 0 || layer >= c->cfg.num_layers || seq < 0 || seq >= c->cfg.max_seqs)
+    return SD_EINVAL;
+  const int64_t len = c->layers[layer].len[seq];
+  size_t b = 0;
+  switch (what) {
+    case SD_DEBUG_PAGE_TABLE: b = sizeof(int32_t) * c->pps; break;
+    case SD_DEBUG_SUMMARY:
+      for (int h = 0; h < c->Hkv; ++h) b += sizeof(uint16_t) * cdiv(len, c->S[h]) * c->D * 2;
+      break;
+    case SD_DEBUG_MAW:
+      for (int h = 0; h < c->Hkv; ++h) b += sizeof(float) * cdiv(len, c->S[h]);
+      break;
+    case SD_DEBUG_K:
+    case SD_DEBUG_V: b = sizeof(uint16_t) * len * c->Hkv * c->D; break;
+    default: return SD_EINVAL;
+  }
+  *bytes = b;
+  return SD_OK;
+}
+
+sd_status sd_debug_copy(sd_ctx *c, int32_t what, int32_t layer, int32_t seq,
+                        void *host_dst, size_t bytes) {
+  if (!c) return SD_EINVAL;
+  size_t need = 0;
+  if (sd_debug_bytes(c, what, layer, seq, &need) != SD_OK)
+    return fail(c, SD_EINVAL, "bad debug request (what %d, layer %d, seq %d)", what, layer, seq);
+  if (bytes != need || (need && !host_dst))
+    return fail(c, SD_EINVAL, "debug copy needs %zu bytes, got %zu", need, bytes);
+  SD_HIP(c, hipStreamSynchronize(c->stream));
+  const Layer &L = c->layers[layer];
+  const int64_t len = L.len[seq];
+  const int D = c->D;
+  if (what == SD_DEBUG_PAGE_TABLE) {
+    SD_HIP(c, hipMemcpy(host_dst, L.dev.pt + (size_t)seq * c->pps, need, hipMemcpyDeviceToHost));
+  } else if (what == SD_DEBUG_SUMMARY) {
+    uint16_t *dst = static_cast<uint16_t *>(host_dst);
+    for (int h = 0; h < c->Hkv; ++h) {
+      const HeadInfo &hi = c->heads[h];
+      const int64_t nb = cdiv(len, hi.S);
+      std::vector<uint16_t> raw((size_t)(D / 4) * hi.nbmax * 8);
+      SD_HIP(c, hipMemcpy(raw.data(), L.dev.summ + hi.summ_off + (size_t)seq * raw.size(),
+                          raw.size() * sizeof(uint16_t), hipMemcpyDeviceToHost));
+      for (int64_t b = 0; b < nb; ++b)
+        for (int ch = 0; ch < D; ++ch) {
+          const size_t src = ((size_t)(ch / 4) * hi.nbmax + b) * 8 + 2 * (ch % 4);
+          dst[(b * D + ch) * 2 + 0] = raw[src];
+          dst[(b * D + ch) * 2 + 1] = raw[src + 1];
+        }
+      dst += nb * D * 2;
+    }
+  } else if (what == SD_DEBUG_MAW) {
+    float *dst = static_cast<float *>(host_dst);
+    for (int h = 0; h < c->Hkv; ++h) {
+      const HeadInfo &hi = c->heads[h];
+      const int64_t nb = cdiv(len, hi.S);
+      if (nb)
+        SD_HIP(c, hipMemcpy(dst, L.dev.maw + hi.maw_off + (size_t)seq * hi.nbmax,
+                            sizeof(float) * nb, hipMemcpyDeviceToHost));
+      dst += nb;
+    }
+  } else {
+    const uint16_t *pool = what == SD_DEBUG_K ? L.dev.k : L.dev.v;
+    uint16_t *dst = static_cast<uint16_t *>(host_dst);
+    const size_t page_elems = (size_t)c->Hkv * kPage * D;
+    std::vector<uint16_t> page(page_elems);
+    for (int64_t p = 0; p < cdiv(len, kPage); ++p) {
+      int pid = L.h_pt[(size_t)seq * c->pps + p];
+      SD_HIP(c, hipMemcpy(page.data(), pool + (size_t)pid * page_elems,
+                          page_elems * sizeof(uint16_t), hipMemcpyDeviceToHost));
+      for (int r = 0; r < kPage && p * kPage + r < len; ++r)
+        for (int h = 0; h < c->Hkv; ++h)
+          memcpy(dst + (((size_t)(p * kPage + r)) * c->Hkv + h) * D,
+                 page.data() + ((size_t)h * kPage + r) * D, sizeof(uint16_t) * D);
+    }
+  }
+  return SD_OK;
+}
+
+sd_status sd_debug_set_maw(sd_ctx *c, int32_t layer, int32_t seq,
+                           const float *host_src, size_t bytes) {
+  if (!c) return SD_EINVAL;
+  size_t need = 0;
+  if (sd_debug_bytes(c, SD_DEBUG_MAW, layer, seq, &need) != SD_OK)
+    return fail(c, SD_EINVAL, "bad MAW request (layer %d, seq %d)", layer, seq);
+  if (bytes != need || (need && !host_src))
+    return fail(c, SD_EINVAL, "MAW upload needs %zu bytes, got %zu", need, bytes);
+  SD_HIP(c, hipStreamSynchronize(c->stream));
+  const int64_t len = c->layers[layer].len[seq];
+  for (int h = 0; h < c->Hkv; ++h) {
+    const HeadInfo &hi = c->heads[h];
+    const int64_t nb = cdiv(len, hi.S);
+    if (nb)
+      SD_HIP(c, hipMemcpy(c->layers[layer].dev.maw + hi.maw_off + (size_t)seq * hi.nbmax,
+                          host_src, sizeof(float) * nb, hipMemcpyHostToDevice));
+    host_src += nb;
+  }
+  return SD_OK;
+}
+
+}  // extern "C"

@@ -1,0 +1,221 @@
+/*
+ * sparse_decode.h - C ABI of libsparse_decode.so: decode-step block-sparse
+ * top-score attention over a paged KV cache on one MI355X (gfx950).
+ *
+ * One decode step of one layer is four stream-ordered calls:
+ *
+ *   append_kv    the step's new token(s) join the paged store; per-block key
+ *                summaries are kept exact.
+ *   select_topk  every KV block is scored against the query and a top-k block
+ *                set is chosen per KV head under a token budget.
+ *   sparse_attend  split-K attention over the dense sinks + recent window and
+ *                the selected blocks, emitting normalised (O_i, lse_i)
+ *                partials.
+ *   fuse_lse     the partials are merged with the exact log-sum-exp identity
+ *                and the per-block moving average of attention weight (MAW)
+ *                is updated on the device.
+ *
+ * Pages whose method this follows (title; section or figure):
+ *   [FLX]  "An Efficient Hybrid Sparse Attention with CPU-GPU Parallelism for
+ *          Long-Context Inference" - block-sparse attention parameterised by
+ *          (block size, budget) with per-head top-k (Core claim; Figure 2(d);
+ *          Figure 8 "(blk, bgt)"), dense attention sinks (Figure 3(c)).
+ *   [SPIN] "Unifying Sparse Attention with Hierarchical Memory for Scalable
+ *          Long-Context LLM Serving" - sparsity granularities mapped onto a
+ *          shared page-based KV substrate (What carries the argument); Select
+ *          then Retrieve, decode only (Figure 3).
+ *   [HGCA] "HGCA: Hybrid GPU-CPU Attention for Long Context LLM Inference" -
+ *          dense recent window + sparse selected entries merged by the exact
+ *          LSE identity; MAW threshold beta / #dense entries (What carries the
+ *          argument); append vs decode processes (Figure 2).
+ *   [LFPS] "Learn from the Past: Fast Sparse Indexing for Large Language Model
+ *          Decoding" - decay r = 0.95 of the running score tables (What carries
+ *          the argument); block-based Quest baseline (Extended reading notes).
+ *
+ * Conventions for every call:
+ *   - Pointers marked "dev" are device pointers the caller owns (allocated on
+ *     the context's device); "host" pointers are read before the call returns.
+ *     Nothing is freed on the caller's behalf.
+ *   - bf16 tensors are raw 16-bit patterns (IEEE binary32 upper halves).
+ *   - Every argument is validated on the host before anything is enqueued; a
+ *     negative status means nothing was enqueued and sd_last_error() says why.
+ *   - Work is asynchronous on the configured stream.  Device faults surface as
+ *     SD_EHIP at the next sd_sync()/sparse_decode_destroy().
+ *   - A context is bound to one device and one stream and is not thread-safe.
+ *   - No C++ exception crosses this boundary.
+ */
+#ifndef SPARSE_DECODE_H
+#define SPARSE_DECODE_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef struct sd_ctx sd_ctx;
+typedef int32_t sd_status;
+
+#define SD_OK 0
+#define SD_EINVAL (-1)       /* bad argument or configuration               */
+#define SD_ENOMEM (-2)       /* page pool exhausted or device alloc failed  */
+#define SD_EHIP (-3)         /* a HIP runtime call failed                   */
+#define SD_EUNSUPPORTED (-4) /* valid request outside the built kernels     */
+#define SD_ESTATE (-5)       /* call out of order (e.g. fuse without attend) */
+
+/* Library limits. */
+#define SD_PAGE_SIZE 16         /* tokens per KV page                       */
+#define SD_MAX_GROUP 8          /* query heads per KV head                  */
+#define SD_MAX_KV_HEADS 64
+#define SD_MAX_BLOCK 64         /* largest block size in tokens             */
+
+typedef struct {
+  int32_t max_seqs;       /* sequence slots; seq ids are 0..max_seqs-1       */
+  int32_t num_layers;     /* independent layers (each owns its own pool)     */
+  int32_t num_q_heads;    /* Hq                                              */
+  int32_t num_kv_heads;   /* Hkv; Hq % Hkv == 0, Hq/Hkv <= SD_MAX_GROUP      */
+  int32_t head_dim;       /* d in {64, 128}                                  */
+  int32_t page_size;      /* must be SD_PAGE_SIZE                            */
+  int32_t num_pages;      /* pages per layer in the pool                     */
+  int32_t max_seq_len;    /* tokens per sequence                             */
+  int32_t sink_tokens;    /* n_s: first tokens always attended ([FLX] sinks) */
+  int32_t recent_window;  /* W: last tokens always attended ([HGCA] window)  */
+  const int32_t *block_size; /* host [Hkv]: block size per KV head, a multiple
+                                of 16 and <= 64 ([FLX] head-specific
+                                granularity)                                 */
+  const int32_t *budget_ppm; /* host [Hkv]: budget per KV head as parts per
+                                million of the current token count N; k =
+                                min(|candidates|, ceil(ppm*N/(1e6*S)))       */
+  float softmax_scale;    /* 0 -> 1/sqrt(head_dim)                           */
+  float maw_decay;        /* r in [0,1); 0 -> 0.95 ([LFPS] r = 0.95)         */
+  float maw_beta;         /* beta of the MAW flag; <= 0 turns the flag off   */
+  uint64_t page_shuffle_seed; /* 0: pages handed out in order; else a seeded
+                                 random permutation of the free list         */
+  void *stream;           /* hipStream_t; NULL = the default stream          */
+} sd_config;
+
+/* Host-only check of a configuration (no device is touched).  err may be NULL;
+ * otherwise up to err_len bytes of explanation are written on failure. */
+sd_status sd_validate_config(const sd_config *cfg, char *err, size_t err_len);
+
+/* Create a context on the current HIP device: allocates the per-layer KV
+ * pools [num_pages][Hkv][16][d] bf16 (K and V), page tables, block summaries,
+ * MAW tables and scratch.  All sequences start empty. */
+sd_status sparse_decode_init(const sd_config *cfg, sd_ctx **out);
+
+/* Synchronise the stream and free every device buffer of the context. */
+sd_status sparse_decode_destroy(sd_ctx *ctx);
+
+/* Sizes callers must allocate: k_cap = largest block count select_topk may
+ * write per (sequence, KV head); p_cap = largest number of split-K partials
+ * sparse_attend may write per query head. */
+sd_status sd_caps(const sd_ctx *ctx, int32_t *k_cap, int32_t *p_cap);
+
+/* Append n_new[i] tokens to sequence seq_ids[i] of one layer ([HGCA] append
+ * process, Figure 2; [SPIN] page substrate).  k_bf16, v_bf16: dev
+ * [sum_i n_new[i]][Hkv][d] bf16, rows of sequence i after those of i-1.
+ * Pages come from the layer's free list; if the pool cannot hold every new
+ * token the call fails with SD_ENOMEM and changes nothing.  The per-block
+ * min/max key summaries of every touched block are updated exactly (blocks of
+ * each KV head's own size).  New blocks start with MAW 0.
+ * seq_ids, n_new: host [n_seqs]; ids must be distinct. */
+sd_status append_kv(sd_ctx *ctx, int32_t layer, int32_t n_seqs,
+                    const int32_t *seq_ids, const int32_t *n_new,
+                    const void *k_bf16, const void *v_bf16);
+
+/* Score every block of each (sequence, KV head) and select its top-k blocks
+ * ([FLX] Core claim and Figure 2(d); Quest-style bound).  For block i,
+ * U_h(i) = sum_c max(q_hc*min_ic, q_hc*max_ic) is accumulated in double in
+ * channel order and the group score is the max over the KV head's query heads,
+ * rounded once to fp32.  Candidates are blocks with a token outside the dense
+ * set D = [0, n_s) U [N-W, N).  With maw_beta > 0 a block whose
+ * MAW*|D| > beta*S is ranked before all others ([HGCA] threshold).  Order:
+ * (flag desc, score desc, index asc); the first k are written ascending.
+ * q_bf16: dev [n_seqs][Hq][d].  blk_idx: dev [n_seqs][Hkv][k_cap] int32
+ * (entries past the count are left untouched).  blk_cnt: dev [n_seqs][Hkv]. */
+sd_status select_topk(sd_ctx *ctx, int32_t layer, int32_t n_seqs,
+                      const int32_t *seq_ids, const void *q_bf16,
+                      int32_t *blk_idx, int32_t *blk_cnt, int32_t k_cap);
+
+/* Split-K attention over T = D U tokens(selected blocks), a set ([HGCA] dense
+ * window + sparse entries; flash-decoding split).  The attended blocks of a
+ * (sequence, KV head) are cut into chunks; chunk p of query head h writes
+ * o_part[n][h][p][:] (fp32, normalised within the chunk) and
+ * lse_part[n][h][p] (natural log of the chunk's sum of exp(scaled logits));
+ * unused slots get lse = -inf and O = 0.  blk_idx / blk_cnt are as written by
+ * select_topk (ascending, distinct); entries outside [0, n_blk) are ignored.
+ * The per-block attention mass needed by fuse_lse is kept inside the context
+ * for this layer. */
+sd_status sparse_attend(sd_ctx *ctx, int32_t layer, int32_t n_seqs,
+                        const int32_t *seq_ids, const void *q_bf16,
+                        const int32_t *blk_idx, const int32_t *blk_cnt,
+                        int32_t k_cap, float *o_part, float *lse_part,
+                        int32_t p_cap);
+
+/* Exact LSE fusion of the partials ([HGCA] What carries the argument, in the
+ * max-subtracted form): lse = m + log sum_p e^{lse_p - m}, O = sum_p
+ * e^{lse_p - lse} O_p; parts with lse = -inf drop out.  o: dev [n_seqs][Hq][d]
+ * fp32, lse: dev [n_seqs][Hq] fp32.
+ * layer >= 0: must follow sparse_attend of the same layer and sequences; the
+ * MAW of every block of each (sequence, KV head) is then updated as
+ * MAW <- r*MAW + (1-r)*a with a the group-mean softmax mass of the block
+ * (0 if not attended) ([LFPS] decay; [HGCA] MAW).
+ * layer == -1: pure fusion of n_seqs*Hq heads, no MAW (seq_ids may be NULL). */
+sd_status fuse_lse(sd_ctx *ctx, int32_t layer, int32_t n_seqs,
+                   const int32_t *seq_ids, const float *o_part,
+                   const float *lse_part, int32_t p_cap, float *o, float *lse);
+
+/* Fused decode step: select_topk + sparse_attend + fuse_lse with identical
+ * results, in fewer launches.  blk_idx/blk_cnt/o_part/lse_part are still
+ * written (they are the caller's scratch and its record of the selection). */
+sd_status sparse_decode_step(sd_ctx *ctx, int32_t layer, int32_t n_seqs,
+                             const int32_t *seq_ids, const void *q_bf16,
+                             int32_t *blk_idx, int32_t *blk_cnt, int32_t k_cap,
+                             float *o_part, float *lse_part, int32_t p_cap,
+                             float *o, float *lse);
+
+/* Return a sequence slot to empty in every layer: its pages go back to the
+ * free lists, its length becomes 0 and its MAW table is cleared.  Waits for
+ * the stream first. */
+sd_status sd_release_seq(sd_ctx *ctx, int32_t seq_id);
+
+/* Current token count of a sequence in a layer (host-side bookkeeping). */
+sd_status sd_seq_len(const sd_ctx *ctx, int32_t layer, int32_t seq_id,
+                     int32_t *len);
+
+/* Wait for all work on the context's stream; reports deferred HIP errors. */
+sd_status sd_sync(sd_ctx *ctx);
+
+/* Text of the last error on this context (never NULL). */
+const char *sd_last_error(const sd_ctx *ctx);
+
+/* Debug/parity export of one sequence of one layer to host memory (waits for
+ * the stream).  Layouts:
+ *   SD_DEBUG_PAGE_TABLE  int32 [ceil(max_seq_len/16)] page ids (in use: the
+ *                        first ceil(len/16))
+ *   SD_DEBUG_SUMMARY     for each KV head h in order: bf16 pairs
+ *                        [ceil(len/S_h)][d][2] = (min, max)
+ *   SD_DEBUG_MAW         for each KV head h in order: fp32 [ceil(len/S_h)]
+ *   SD_DEBUG_K / _V      bf16 [len][Hkv][d], gathered through the page table
+ * bytes must equal the size reported by sd_debug_bytes. */
+#define SD_DEBUG_PAGE_TABLE 0
+#define SD_DEBUG_SUMMARY 1
+#define SD_DEBUG_MAW 2
+#define SD_DEBUG_K 3
+#define SD_DEBUG_V 4
+sd_status sd_debug_bytes(const sd_ctx *ctx, int32_t what, int32_t layer,
+                         int32_t seq_id, size_t *bytes);
+sd_status sd_debug_copy(sd_ctx *ctx, int32_t what, int32_t layer,
+                        int32_t seq_id, void *host_dst, size_t bytes);
+
+/* Overwrite the MAW table of one (layer, sequence) from host fp32 values laid
+ * out as SD_DEBUG_MAW (test hook for threshold cases; waits for the stream). */
+sd_status sd_debug_set_maw(sd_ctx *ctx, int32_t layer, int32_t seq_id,
+                           const float *host_src, size_t bytes);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* SPARSE_DECODE_H */

@@ -1,0 +1,313 @@
+"""GPU parity: the HIP path through the C ABI against the CPU oracle.
+
+Bars (in tests/harness.py): selected indices bit-exact except counted ties
+inside a 1e-6 relative score band; max |dO| <= 2e-3, max relative dO <= 1e-2
+where |O| >= 0.1, |d lse| <= 1e-4; summaries equal; MAW within 1e-5 + 1e-3 rel.
+"""
+import dataclasses
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import synth
+from tests import harness
+from tests.harness import log
+
+pytestmark = pytest.mark.gpu
+
+
+def _w(base, **over):
+    return dataclasses.replace(base, **over)
+
+
+@pytest.fixture(autouse=True)
+def _gpu():
+    if not torch.cuda.is_available():
+        pytest.skip("needs a GPU")
+    torch.cuda.set_device(0)
+    yield
+    torch.cuda.synchronize()
+
+
+@pytest.mark.parametrize("seed", range(10))
+def test_tiny_workload(seed):
+    log("case: tiny seed=%d" % seed)
+    st = harness.run_single_step(synth.tiny(), seed)
+    harness.assert_parity(st)
+    assert st["ties"] == 0
+
+
+@pytest.mark.parametrize("N", [1, 3, 17, 60, 68, 69, 100, 1000, 1007, 2049])
+def test_tiny_ragged_lengths(N):
+    """Ragged tails (partial pages and blocks), N inside the dense set, a
+    single token."""
+    log("case: tiny ragged N=%d" % N)
+    st = harness.run_single_step(synth.tiny(), 3, N=N)
+    harness.assert_parity(st)
+
+
+@pytest.mark.parametrize("S", [16, 32, 48, 64])
+def test_block_sizes(S):
+    w = _w(synth.tiny(), block_size=[S], N=3000, n_plant=4)
+    log("case: block size S=%d" % S)
+    harness.assert_parity(harness.run_single_step(w, 5))
+
+
+def test_full_budget_equals_dense():
+    w = _w(synth.tiny(), budget_ppm=[1_000_000], N=1500)
+    log("case: full budget")
+    x = synth.single_step(w, 7)
+    st = harness.run_single_step(w, 7)
+    harness.assert_parity(st)
+    q, K, V = synth.bits(x["q"]), synth.bits(x["K"]), synth.bits(x["V"])
+    O, lse = oracle.dense(q[0], np.ascontiguousarray(K[0, :, 0]),
+                          np.ascontiguousarray(V[0, :, 0]), 1500)
+    ma, mr, ml = harness.compare_outputs(st["gpu"]["o"][0], st["gpu"]["lse"][0], O, lse)
+    assert ma <= harness.ABS_TOL and ml <= harness.LSE_TOL
+
+
+def test_no_sinks_no_window():
+    w = _w(synth.tiny(), n_sink=0, window=0, N=2000)
+    log("case: no dense set")
+    harness.assert_parity(harness.run_single_step(w, 9))
+
+
+def test_zero_budget_dense_only():
+    w = _w(synth.tiny(), budget_ppm=[0], N=2000)
+    log("case: zero budget")
+    st = harness.run_single_step(w, 9)
+    harness.assert_parity(st)
+    assert st["gpu"]["blk_cnt"].max() == 0
+
+
+def test_page_shuffle_invariance():
+    """Scattered pages give bitwise the same results as sequential pages."""
+    w = _w(synth.llama32k(), B=2, N=4099)
+    log("case: page shuffle invariance")
+    a = harness.run_single_step(w, 1, shuffle_seed=0)
+    b = harness.run_single_step(w, 1, shuffle_seed=12345)
+    harness.assert_parity(a)
+    for k in ("blk_idx", "blk_cnt", "o", "lse"):
+        assert np.array_equal(a["gpu"][k], b["gpu"][k]), k
+
+
+def test_chunked_append_matches():
+    """Prefill in uneven pieces: same summaries and outputs as one piece."""
+    w = _w(synth.llama32k(), B=2, N=5000)
+    log("case: chunked append")
+    a = harness.run_single_step(w, 2, chunks=1)
+    b = harness.run_single_step(w, 2, chunks=7)
+    harness.assert_parity(b)
+    for k in ("blk_idx", "blk_cnt", "o", "lse"):
+        assert np.array_equal(a["gpu"][k], b["gpu"][k]), k
+
+
+def test_fused_step_equals_separate_calls():
+    w = _w(synth.llama32k(), B=2, N=6000)
+    log("case: fused step")
+    a = harness.run_single_step(w, 4, fused=False)
+    b = harness.run_single_step(w, 4, fused=True)
+    harness.assert_parity(b)
+    for k in ("blk_idx", "blk_cnt", "o", "lse"):
+        assert np.array_equal(a["gpu"][k], b["gpu"][k]), k
+
+
+def test_many_sequences_split_launches():
+    w = _w(synth.tiny(), B=80, N=700)
+    log("case: 80 sequences")
+    harness.assert_parity(harness.run_single_step(w, 11))
+
+
+@pytest.mark.parametrize("G,Hkv,d", [(1, 2, 128), (7, 4, 128), (8, 2, 64), (3, 3, 64)])
+def test_group_sizes(G, Hkv, d):
+    w = synth.Workload("g", B=2, Hq=G * Hkv, Hkv=Hkv, d=d, N=3333,
+                       block_size=[16, 32, 64][:1] * Hkv, budget_ppm=[50000] * Hkv,
+                       n_sink=4, window=128, plant_frac=0.02, sink_scale=4.0)
+    log("case: G=%d Hkv=%d d=%d" % (G, Hkv, d))
+    harness.assert_parity(harness.run_single_step(w, 13))
+
+
+def test_llama32k_full():
+    """The metric workload at full size: every unit against the oracle."""
+    log("case: llama32k full (B=8, 32/8 heads, d=128, N=32768)")
+    st = harness.run_single_step(synth.llama32k(), 0)
+    log("  ties=%d max|dO|=%.3g max rel=%.3g max|dlse|=%.3g" % (
+        st["ties"], st["max_abs"], st["max_rel"], st["max_dlse"]))
+    harness.assert_parity(st)
+    assert len(st["units"]) == 64
+
+
+@pytest.mark.parametrize("B,S,pct", [(1, 16, 2), (8, 32, 5), (32, 64, 10), (64, 16, 10),
+                                     (64, 64, 2)])
+def test_sweep_points(B, S, pct):
+    w = synth.sweep(B, S, pct)
+    log("case: sweep B=%d S=%d budget=%d%%" % (B, S, pct))
+    harness.assert_parity(harness.run_single_step(w, 21))
+
+
+def test_fuse_pure_identity():
+    """fuse_lse(layer=-1) on random partials equals the oracle fusion; -inf
+    partials drop out."""
+    w = synth.llama32k()
+    log("case: pure fusion")
+    eng = harness.make_engine(_w(w, B=2), 256)
+    try:
+        n, P, d = 3, eng.p_cap, w.d
+        g = torch.Generator().manual_seed(5)
+        o_part = torch.randn(n, w.Hq, P, d, generator=g)
+        lse_part = torch.randn(n, w.Hq, P, generator=g) * 5
+        lse_part[:, :, P // 2:] = -float("inf")
+        lse_part[0, 0, :] = -float("inf")     # an empty head
+        o = torch.empty(n, w.Hq, d, device="cuda")
+        lse = torch.empty(n, w.Hq, device="cuda")
+        eng.fuse_lse(-1, None, o_part.cuda(), lse_part.cuda(), o, lse, n_seqs=n)
+        eng.sync()
+        o, lse = o.cpu().numpy(), lse.cpu().numpy()
+        for i in range(n):
+            for h in range(w.Hq):
+                Oref, lref = oracle.fuse(o_part[i, h].double().numpy(),
+                                         lse_part[i, h].double().numpy())
+                if lref == -np.inf:
+                    assert lse[i, h] == -np.inf and np.all(o[i, h] == 0)
+                    continue
+                assert abs(lse[i, h] - lref) <= 1e-5
+                assert np.abs(o[i, h] - Oref).max() <= 1e-5
+    finally:
+        eng.close()
+
+
+def test_error_paths():
+    w = _w(synth.tiny(), N=2000)
+    log("case: error paths")
+    eng = harness.make_engine(w, 2048)
+    try:
+        x = synth.single_step(w, 0, N=2000)
+        K, V, q = x["K"].cuda(), x["V"].cuda(), x["q"].cuda()
+        harness.prefill(eng, 0, K, V)
+        bufs = eng.alloc_step(1)
+        # fuse before attend
+        st = eng.fuse_lse(0, [0], bufs["o_part"], bufs["lse_part"], bufs["o"],
+                          bufs["lse"], check=False)
+        assert st == -5
+        # k_cap too small
+        small = torch.zeros(1, 1, 1, dtype=torch.int32, device="cuda")
+        assert eng.select_topk(0, [0], q, small, bufs["blk_cnt"], check=False) == -1
+        # bad sequence / layer ids, repeated ids
+        assert eng.select_topk(0, [5], q, bufs["blk_idx"], bufs["blk_cnt"], check=False) == -1
+        assert eng.select_topk(3, [0], q, bufs["blk_idx"], bufs["blk_cnt"], check=False) == -1
+        # page pool exhaustion leaves the sequence unchanged
+        big = torch.zeros(4096, 1, w.d, dtype=torch.bfloat16, device="cuda")
+        assert eng.append_kv(0, [0], [4096], big, big, check=False) == -1  # > max_seq_len
+        assert eng.seq_len(0, 0) == 2000
+        # 2000 tokens at 25%: 1 + 32 + 5 attended blocks -> 3 chunks needed
+        # p_cap too small
+        tiny_part = torch.zeros(1, w.Hq, 1, w.d, device="cuda")
+        tiny_lse = torch.zeros(1, w.Hq, 1, device="cuda")
+        eng.select_topk(0, [0], q, bufs["blk_idx"], bufs["blk_cnt"])
+        assert eng.sparse_attend(0, [0], q, bufs["blk_idx"], bufs["blk_cnt"], tiny_part,
+                                 tiny_lse, check=False) == -1
+        eng.sync()
+    finally:
+        eng.close()
+
+
+def test_pool_exhaustion_enomem():
+    w = _w(synth.tiny(), N=64)
+    log("case: pool exhaustion")
+    eng = harness.make_engine(w, 4096, extra_pages=-10)   # 246 pages
+    try:
+        K = torch.zeros(4096, 1, w.d, dtype=torch.bfloat16, device="cuda")
+        eng.append_kv(0, [0], [3900], K, K)                 # 244 pages
+        assert eng.seq_len(0, 0) == 3900
+        assert eng.append_kv(0, [0], [100], K, K, check=False) == -2
+        assert eng.seq_len(0, 0) == 3900
+        eng.release_seq(0)
+        assert eng.seq_len(0, 0) == 0
+        eng.append_kv(0, [0], [246 * 16], K, K)
+        assert eng.seq_len(0, 0) == 246 * 16
+        eng.sync()
+    finally:
+        eng.close()
+
+
+def test_maw_flag_selection():
+    """MAW threshold flags rank blocks first (values set through the debug
+    hook; the oracle reads the same fp32 values widened to double)."""
+    w = _w(synth.llama32k(), B=2, N=8000, maw_beta=1.0)
+    log("case: MAW flag selection")
+    x = synth.single_step(w, 3, N=8000)
+    K, V, q = x["K"].cuda(), x["V"].cuda(), x["q"].cuda()
+    eng = harness.make_engine(w, 8064)
+    try:
+        harness.prefill(eng, 0, K, V)
+        nb = 8000 // 32
+        rng = np.random.default_rng(0)
+        maw_set, vals_by = {}, {}
+        for s in range(2):
+            vals = np.zeros(w.Hkv * nb, np.float32)
+            # threshold beta*S/|D| = 32/516; put some blocks far above it
+            for g in range(w.Hkv):
+                hot = rng.choice(np.arange(1, 230), size=12, replace=False)
+                vals[g * nb + hot] = 0.5
+                vals[g * nb + rng.choice(np.arange(1, 230), size=5)] = 0.01
+            eng.set_maw(0, s, vals)
+            for g in range(w.Hkv):
+                maw_set[(s, g)] = vals[g * nb:(g + 1) * nb].astype(np.float64)
+                vals_by[(s, g)] = maw_set[(s, g)].copy()
+        gpu = harness.run_gpu_step(eng, 0, [0, 1], q)
+        Kb, Vb = synth.bits(K), synth.bits(V)
+        st = harness.check_units(w, eng, 0, [0, 1], synth.bits(q), {0: Kb[0], 1: Kb[1]},
+                                 {0: Vb[0], 1: Vb[1]}, {0: 8000, 1: 8000}, gpu,
+                                 maw_state=maw_set)
+        harness.assert_parity(st)
+        for s in range(2):
+            for g in range(w.Hkv):
+                sel = set(gpu["blk_idx"][s, g, :gpu["blk_cnt"][s, g]].tolist())
+                hot = set(np.nonzero(vals_by[(s, g)] >= 0.5)[0].tolist())
+                assert hot <= sel, "flagged blocks must be selected first"
+    finally:
+        eng.close()
+
+
+def test_multistep_maw_lockstep():
+    """Several layers x decode steps with MAW on (a small loop workload):
+    lockstep parity every step, MAW tables compared every step."""
+    w = _w(synth.loop32(), B=2, N=3000, layers=2, steps=12)
+    log("case: multistep MAW lockstep")
+    eng = harness.make_engine(w, 3000 + 64, layers=w.layers)
+    try:
+        K_bits, V_bits, maw_state, dirs_l = {}, {}, {}, {}
+        for layer in range(w.layers):
+            dirs = synth.directions(w, 0, layer, 1, device="cuda")
+            K, V, _ = synth.prefill_with_directions(w, 0, layer, w.N - 1, dirs, device="cuda")
+            harness.prefill(eng, layer, K, V)
+            Kb, Vb = synth.bits(K), synth.bits(V)
+            K_bits[layer] = {b: Kb[b] for b in range(w.B)}
+            V_bits[layer] = {b: Vb[b] for b in range(w.B)}
+            maw_state[layer] = {}
+            dirs_l[layer] = dirs
+        N = w.N - 1
+        for step in range(w.steps):
+            N += 1
+            for layer in range(w.layers):
+                kn, vn = synth.step_kv(w, 0, layer, step, device="cuda")
+                eng.append_kv(layer, list(range(w.B)), [1] * w.B,
+                              kn.view(w.B, w.Hkv, w.d).contiguous(),
+                              vn.view(w.B, w.Hkv, w.d).contiguous())
+                knb, vnb = synth.bits(kn), synth.bits(vn)
+                for b in range(w.B):
+                    K_bits[layer][b] = np.concatenate([K_bits[layer][b], knb[b]], 0)
+                    V_bits[layer][b] = np.concatenate([V_bits[layer][b], vnb[b]], 0)
+                q = synth.loop_query(w, 0, layer, step, dirs_l[layer], device="cuda")
+                gpu = harness.run_gpu_step(eng, layer, list(range(w.B)), q)
+                st = harness.check_units(w, eng, layer, list(range(w.B)), synth.bits(q),
+                                         K_bits[layer], V_bits[layer],
+                                         {b: N for b in range(w.B)}, gpu,
+                                         maw_state=maw_state[layer],
+                                         check_summ=(step % 4 == 0))
+                harness.assert_parity(st)
+        log("  final N=%d" % N)
+    finally:
+        eng.close()
