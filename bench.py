@@ -115,15 +115,16 @@ def main():
     def step(s, ev=None):
         layer = s % L
         kn, vn = k_new[s % 64], v_new[s % 64]
+        if args.fused and ev is None:
+            eng.decode_step(layer, seqs, qs[layer], bufs["blk_idx"], bufs["blk_cnt"],
+                            bufs["o_part"], bufs["lse_part"], bufs["o"], bufs["lse"],
+                            k_new=kn, v_new=vn)
+            return
         if ev is not None:
             ev[0].record(stream)
         eng.append_kv(layer, seqs, [1] * w.B, kn, vn)
         if ev is not None:
             ev[1].record(stream)
-        if args.fused and ev is None:
-            eng.decode_step(layer, seqs, qs[layer], bufs["blk_idx"], bufs["blk_cnt"],
-                            bufs["o_part"], bufs["lse_part"], bufs["o"], bufs["lse"])
-            return
         eng.select_topk(layer, seqs, qs[layer], bufs["blk_idx"], bufs["blk_cnt"])
         if ev is not None:
             ev[2].record(stream)

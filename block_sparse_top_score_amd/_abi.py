@@ -57,6 +57,13 @@ def load(path: str = LIB_PATH):
     global _lib
     if _lib is not None:
         return _lib
+    # torch ships its own HIP runtime; when torch is used for memory and
+    # streams it must be loaded first so that the library binds to the same
+    # runtime instance (one device context, valid stream handles).
+    try:
+        import torch  # noqa: F401
+    except ImportError:
+        pass
     if not os.path.exists(path):
         raise RuntimeError(
             "libsparse_decode.so is not built (%s); run __graft_entry__.build() "
@@ -73,7 +80,7 @@ def load(path: str = LIB_PATH):
         "select_topk": (i32, [P, i32, i32, P, P, P, P, i32]),
         "sparse_attend": (i32, [P, i32, i32, P, P, P, P, i32, P, P, i32]),
         "fuse_lse": (i32, [P, i32, i32, P, P, P, i32, P, P]),
-        "sparse_decode_step": (i32, [P, i32, i32, P, P, P, P, i32, P, P, i32, P, P]),
+        "sparse_decode_step": (i32, [P, i32, i32, P, P, P, P, P, P, i32, P, P, i32, P, P]),
         "sd_release_seq": (i32, [P, i32]),
         "sd_seq_len": (i32, [P, i32, i32, ctypes.POINTER(i32)]),
         "sd_sync": (i32, [P]),
@@ -218,9 +225,11 @@ class SparseDecode:
         return st
 
     def decode_step(self, layer, seq_ids, q, blk_idx, blk_cnt, o_part, lse_part, o,
-                    lse, check=True):
+                    lse, k_new=None, v_new=None, check=True):
+        """Fused step; k_new/v_new ([n][Hkv][d] bf16) append one token first."""
         s, sp = _i32arr(seq_ids)
-        st = self.L.sparse_decode_step(self.ctx, layer, len(s), sp, _ptr(q),
+        st = self.L.sparse_decode_step(self.ctx, layer, len(s), sp, _ptr(k_new),
+                                       _ptr(v_new), _ptr(q),
                                        _ptr(blk_idx), _ptr(blk_cnt), blk_idx.shape[-1],
                                        _ptr(o_part), _ptr(lse_part), lse_part.shape[-1],
                                        _ptr(o), _ptr(lse))

@@ -14,6 +14,10 @@ namespace sd {
 constexpr int kPage = SD_PAGE_SIZE;  // tokens per KV page
 constexpr int kLaunchSeqs = 64;      // sequences per kernel launch
 constexpr int kChunkTokens = 256;    // token slots of one split-K chunk
+constexpr int kScoreTile = 256;      // blocks scored by one workgroup
+constexpr int kTopkLdsKeys = 4096;   // top-k keeps keys in LDS up to this
+constexpr int kFuseSlots = 256;      // partial slots per query head, at most
+constexpr int kFuseSelLds = 2048;    // fusion keeps the selection in LDS up to this
 
 // Per-KV-head constants, resident in device memory for the context's life
 // (read with uniform addresses, so they come through the scalar cache).
@@ -22,6 +26,8 @@ struct HeadInfo {
   int32_t ppm;           // budget, parts per million of N
   int32_t nbmax;         // ceil(max_seq_len / S): blocks per sequence
   int32_t chunk_blocks;  // kChunkTokens / S
+  int32_t kcap;          // most blocks ever selected on this head
+  int32_t pd;            // partial slots reserved for dense chunks
   int64_t summ_off;      // uint16 offset of this head's summary region
   int64_t maw_off;       // float offset of this head's MAW region
 };
@@ -56,48 +62,64 @@ struct Dims {
   int32_t Hq, Hkv, G, d;
   int32_t pages_per_seq;
   int32_t n_sink, window;
-  float scale_log2;  // softmax scale * log2(e)
+  float scale_log2;    // softmax scale * log2(e)
   float maw_decay;
   float maw_beta;
   int32_t key_stride;  // uint32 keys per (seq, kv head) in scratch
-  int32_t u_cap;       // attended-block slots per (seq, kv head)
+  int32_t ndt_cap;     // dense-touching block slots per (seq, kv head)
+  int32_t kcap;        // selected block slots per (seq, kv head)
 };
 
 // Scratch owned by the context.
 struct Scratch {
-  double2 *qpm;   // [kLaunchSeqs][Hq][d] (min(q,0), max(q,0)) in double
-  uint32_t *keys; // [max_seqs][Hkv][key_stride] order-preserving fp32 keys
-  uint8_t *flags; // [max_seqs][Hkv][key_stride] MAW threshold flags
-  float *lmass;   // [max_seqs][Hq][u_cap] per attended block log-mass
-  int32_t *ublk;  // [max_seqs][Hkv][u_cap] block id of attended slot u
-  int32_t *ucnt;  // [max_seqs][Hkv] number of attended blocks
+  unsigned long long *keyflag;  // [max_seqs][Hkv][key_stride] key | MAW flag << 32
+  uint32_t *keys;    // [max_seqs][Hkv][key_stride] top-k working keys (long units)
+  int32_t *ulist;    // [max_seqs][Hkv][key_stride] uncertain blocks (long units)
+  uint32_t *eps_max; // [max_seqs][Hkv] largest score error bound (float bits)
+  uint8_t *flags;    // [max_seqs][Hkv][key_stride] top-k working flags (long units)
+  float *lm_dense;   // [max_seqs][Hq][ndt_cap] log-mass of dense block slots
+  float *lm_sel;     // [max_seqs][Hq][kcap] log-mass of selected block slots
+  int32_t *usel;     // [max_seqs][Hkv][kcap] selected block ids (attend copy)
+  int32_t *ucnt;     // [max_seqs][Hkv] selected block count (attend copy)
+  uint32_t *arrive;  // [max_seqs][Hkv][2] last-arriver counters (kept at 0)
+};
+
+// Everything a kernel needs about the context (passed by value).
+struct Ctx {
+  LayerDev L;
+  const HeadInfo *heads;
+  Dims dm;
+  Scratch sc;
 };
 
 // ---- launchers (sd_kernels.hip) -------------------------------------------
 // Each returns hipSuccess or the launch error; none synchronises.
 
-hipError_t launch_append(const LayerDev &L, const HeadInfo *d_heads,
-                         const Dims &dm, const AppendBatch &b, int max_new,
+hipError_t launch_append(const Ctx &c, const AppendBatch &b, int max_new,
                          int max_touch_blocks, const uint16_t *k_new,
                          const uint16_t *v_new, hipStream_t st);
 
-hipError_t launch_select(const LayerDev &L, const HeadInfo *d_heads,
-                         const Dims &dm, const Scratch &sc, const SeqBatch &b,
-                         int max_blocks, const uint16_t *q, int32_t *blk_idx,
-                         int32_t *blk_cnt, int32_t k_cap, hipStream_t st);
+// Score + top-k (last arriver per unit).  With dense_o_part set, the
+// dchunks_x dense sink/window chunks per unit are attended in the same launch.
+hipError_t launch_select(const Ctx &c, const SeqBatch &b, int max_blocks,
+                         const uint16_t *q, int32_t *blk_idx, int32_t *blk_cnt,
+                         int32_t k_cap, int dchunks_x, float *dense_o_part,
+                         float *dense_lse_part, int32_t p_cap, hipStream_t st);
 
-hipError_t launch_attend(const LayerDev &L, const HeadInfo *d_heads,
-                         const Dims &dm, const Scratch &sc, const SeqBatch &b,
-                         const uint16_t *q, const int32_t *blk_idx,
-                         const int32_t *blk_cnt, int32_t k_cap, float *o_part,
-                         float *lse_part, int32_t p_cap, hipStream_t st);
+// fused = false: one workgroup per partial slot (dense chunks at [0, pd),
+// selected chunks after; unused slots emptied).  fused = true: selected
+// chunks only; the last workgroup of each unit fuses and updates MAW.
+hipError_t launch_attend(const Ctx &c, const SeqBatch &b, const uint16_t *q,
+                         const int32_t *blk_idx, const int32_t *blk_cnt,
+                         int32_t k_cap, float *o_part, float *lse_part,
+                         int32_t p_cap, bool fused, int max_sel_chunks, float *o,
+                         float *lse, hipStream_t st);
 
-// with_maw: update MAW from the attend scratch; L may be null otherwise.
-hipError_t launch_fuse(const LayerDev *L, const HeadInfo *d_heads,
-                       const Dims &dm, const Scratch &sc, const SeqBatch &b,
-                       bool with_maw, const float *o_part,
-                       const float *lse_part, int32_t p_cap, float *o,
-                       float *lse, hipStream_t st);
+// Fusion of the partials: with_maw = slots and MAW from the attend scratch
+// (layer call); otherwise every slot of p_cap is fused (layer -1).
+hipError_t launch_fuse(const Ctx &c, const SeqBatch &b, bool with_maw,
+                       const float *o_part, const float *lse_part,
+                       int32_t p_cap, float *o, float *lse, hipStream_t st);
 
 hipError_t launch_fill_f32(float *p, size_t n, float v, hipStream_t st);
 

@@ -16,6 +16,18 @@
 //   [LFPS] "Learn from the Past: Fast Sparse Indexing for Large Language
 //          Model Decoding": decay r = 0.95 of running score tables (What
 //          carries the argument); block-based Quest (Extended reading notes).
+//
+// Work decomposition of one (sequence, KV head) "unit":
+//   * score tiles: 256 blocks per workgroup, one lane per block; the last
+//     tile to finish (atomic arrival counter) runs the unit's top-k;
+//   * dense chunks: the blocks touching the sinks or the recent window,
+//     attended over their dense tokens only;
+//   * selected chunks: the selected blocks, attended over their tokens that
+//     are not dense (so every token of T = D U selected is counted once);
+//   * fusion: partial slots [0, dense chunks) and [pd, pd + selected chunks)
+//     merged with the LSE identity, then the MAW update of every block.
+// The fused step and the separate ABI calls run these same device functions
+// on the same slots, so their results are bitwise identical.
 #include <cfloat>
 #include <cmath>
 
@@ -25,33 +37,45 @@ namespace sd {
 
 namespace {
 
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+
 __device__ __forceinline__ float bf16_lo(uint32_t w) {
   return __uint_as_float(w << 16);
 }
 __device__ __forceinline__ float bf16_hi(uint32_t w) {
   return __uint_as_float(w & 0xffff0000u);
 }
+__device__ __forceinline__ int cdiv(int a, int b) { return (a + b - 1) / b; }
 
-// DPP lane exchange inside a 16-lane row (gfx9 encodings).
-template <int CTRL>
-__device__ __forceinline__ float dpp(float x) {
-  return __int_as_float(
-      __builtin_amdgcn_update_dpp(0, __float_as_int(x), CTRL, 0xF, 0xF, false));
+// Data that one workgroup publishes to the last-arriving workgroup of the same
+// unit inside one launch is written and read with relaxed device-scope atomic
+// accesses, which the gfx950 memory model keeps coherent across the XCDs
+// without L2 write-back or invalidation; a wait for the workgroup's memory
+// operations (vmcnt 0) orders them before its arrival increment.
+template <class T>
+__device__ __forceinline__ void st_dev(T *p, T v) {
+  __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
-constexpr int kQuadXor1 = 0xB1;       // quad_perm [1,0,3,2]
-constexpr int kQuadXor2 = 0x4E;       // quad_perm [2,3,0,1]
-constexpr int kRowHalfMirror = 0x141; // lane i <-> 7-i within 8
-constexpr int kRowMirror = 0x140;     // lane i <-> 15-i within 16
-
-// Sum over groups of L consecutive lanes (L = 8 or 16); every lane of the
-// group receives the group sum.
-template <int L>
-__device__ __forceinline__ float group_sum(float x) {
-  x += dpp<kQuadXor1>(x);
-  x += dpp<kQuadXor2>(x);
-  x += dpp<kRowHalfMirror>(x);
-  if constexpr (L == 16) x += dpp<kRowMirror>(x);
-  return x;
+template <class T>
+__device__ __forceinline__ T ld_dev(const T *p) {
+  return __hip_atomic_load(const_cast<T *>(p), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ void wait_vmem() {
+  __builtin_amdgcn_s_waitcnt(0x0f70);  // vmcnt(0): this wave's loads and stores are done
+}
+// Arrival of one workgroup of a unit; true in the last one to arrive.  Every
+// thread of the workgroup must call it.
+__device__ __forceinline__ bool arrive_last(uint32_t *counter, unsigned expected, int *flag) {
+  wait_vmem();
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    const unsigned prev = __hip_atomic_fetch_add(counter, 1u, __ATOMIC_RELAXED,
+                                                 __HIP_MEMORY_SCOPE_AGENT);
+    *flag = prev == expected - 1;
+  }
+  __syncthreads();
+  return *flag != 0;
 }
 
 __device__ __forceinline__ float wave_max(float x) {
@@ -70,45 +94,6 @@ __device__ __forceinline__ int wave_sum_i(int x) {
   return x;
 }
 
-// Geometry of one (sequence, KV head): dense set D = [0, ns) U [wlo, N)
-// ([FLX] sinks, [HGCA] recent window); head blocks [0, hb) touch the sinks,
-// tail blocks [tb, n_blk) touch the window.
-struct Geom {
-  int N, S, n_blk, ns, wlo, hb, tb;
-};
-__device__ __forceinline__ Geom geom(int N, int S, int n_s, int W) {
-  Geom g;
-  g.N = N;
-  g.S = S;
-  g.n_blk = (N + S - 1) / S;
-  g.ns = min(n_s, N);
-  g.wlo = max(0, N - W);
-  g.hb = (g.ns + S - 1) / S;
-  g.tb = (W > 0 && N > 0) ? g.wlo / S : g.n_blk;
-  if (g.hb >= g.tb) {  // every block touches D
-    g.hb = g.n_blk;
-    g.tb = g.n_blk;
-  }
-  return g;
-}
-
-// Block i is a candidate iff it holds a token outside D.
-__device__ __forceinline__ bool is_candidate(const Geom &g, int i) {
-  if (g.ns >= g.wlo) return false;
-  int lo = i * g.S, hi = min(lo + g.S, g.N);
-  return !(hi <= g.ns || lo >= g.wlo);
-}
-
-__device__ __forceinline__ int dense_count(const Geom &g) {
-  return g.ns + (g.N - g.wlo) - max(0, g.ns - g.wlo);
-}
-
-// k = min(n_cand, ceil(ppm * N / (1e6 * S))) in 64-bit integers.
-__device__ __forceinline__ int budget_blocks(int ppm, int N, int S) {
-  long long den = 1000000LL * S;
-  return (int)(((long long)ppm * N + den - 1) / den);
-}
-
 __device__ __forceinline__ int lower_bound(const int32_t *a, int n, int v) {
   int lo = 0, hi = n;
   while (lo < hi) {
@@ -118,87 +103,152 @@ __device__ __forceinline__ int lower_bound(const int32_t *a, int n, int v) {
   return lo;
 }
 
+// k = ceil(ppm * N / (1e6 * S)) in 64-bit integers (budget as a token
+// fraction of N, whole blocks; [FLX] Figure 2 and Figure 8).
+__device__ __forceinline__ int budget_blocks(int ppm, int N, int S) {
+  long long den = 1000000LL * S;
+  return (int)(((long long)ppm * N + den - 1) / den);
+}
+
+// Geometry of one unit.  D = [0, ns) U [wlo, N) ([FLX] sinks, [HGCA] recent
+// window); blocks [0, hb) touch the sinks, blocks [tb, n_blk) the window.
+struct UG {
+  int N, S, n_blk, ns, wlo, hb, tb, n_dt, kk, CB;
+};
+__device__ __forceinline__ UG unit_geom(int N, const HeadInfo &hi, const Dims &dm) {
+  UG g;
+  const int S = hi.S;
+  g.N = N;
+  g.S = S;
+  g.n_blk = cdiv(N, S);
+  g.ns = min(dm.n_sink, N);
+  g.wlo = max(0, N - dm.window);
+  g.hb = cdiv(g.ns, S);
+  g.tb = (dm.window > 0 && N > 0) ? g.wlo / S : g.n_blk;
+  if (g.hb >= g.tb) {  // every block touches D
+    g.hb = g.n_blk;
+    g.tb = g.n_blk;
+  }
+  g.n_dt = g.hb + (g.n_blk - g.tb);
+  const int n_cand = g.ns < g.wlo ? cdiv(g.wlo, S) - g.ns / S : 0;
+  g.kk = min(n_cand, budget_blocks(hi.ppm, N, S));
+  g.CB = hi.chunk_blocks;
+  return g;
+}
+
+__device__ __forceinline__ bool is_candidate(const UG &g, int i) {
+  if (g.ns >= g.wlo) return false;
+  const int lo = i * g.S, hi = min(lo + g.S, g.N);
+  return !(hi <= g.ns || lo >= g.wlo);
+}
+__device__ __forceinline__ int dense_count(const UG &g) {
+  return g.ns + (g.N - g.wlo) - max(0, g.ns - g.wlo);
+}
+// Dense-touching block of dense slot j.
+__device__ __forceinline__ int dense_block(const UG &g, int j) {
+  return j < g.hb ? j : g.tb + (j - g.hb);
+}
 __device__ __forceinline__ uint32_t order_key(float u) {
   if (u == 0.0f) u = 0.0f;  // -0 and +0 are the same score
-  uint32_t b = __float_as_uint(u);
+  const uint32_t b = __float_as_uint(u);
   return (b & 0x80000000u) ? ~b : (b | 0x80000000u);
 }
+
+// ---------------------------------------------------------------------------
+// Shared memory of the roles (one launch may host several roles).
+struct TopkSmem {
+  uint32_t keys[kTopkLdsKeys];
+  int32_t ulist[kTopkLdsKeys];
+  uint8_t flags[kTopkLdsKeys];
+  int hist[4][256];
+  int scan[4];
+  uint32_t red[4];
+  int vals[4];
+  float qs[SD_MAX_GROUP * 128];
+  double ud[256];
+  int last;
+};
+
+template <int G>
+struct FuseSmem {
+  float w[G][kFuseSlots];  // per-slot LSE weights
+  float lse[G];
+  float adense[kFuseSlots];
+  float asel[kFuseSelLds];
+  int32_t sel[kFuseSelLds];
+  int last;
+};
 
 // ---------------------------------------------------------------------------
 // append: scatter new K/V rows into their pages ([SPIN] page substrate;
 // [HGCA] append process, Figure 2).
 template <int D>
-__global__ __launch_bounds__(256) void k_append_kv(
-    uint16_t *__restrict__ kpool, uint16_t *__restrict__ vpool,
-    const int32_t *__restrict__ pt, AppendBatch b, int Hkv, int pps,
-    int tok_per_wg, const uint16_t *__restrict__ k_new,
-    const uint16_t *__restrict__ v_new) {
-  const int i = blockIdx.y;
+__device__ void append_scatter(const Ctx &c, const AppendBatch &b, int i,
+                               int wg_x, int tok_per_wg,
+                               const uint16_t *__restrict__ k_new,
+                               const uint16_t *__restrict__ v_new) {
   const int n_new = b.n_new[i];
-  const int t0 = blockIdx.x * tok_per_wg;
+  const int t0 = wg_x * tok_per_wg;
   if (t0 >= n_new) return;
   const int seq = b.seq[i];
   const int nt = min(tok_per_wg, n_new - t0);
-  constexpr int V8 = D / 8;  // uint4 per row
+  constexpr int V8 = D / 8;
+  const int Hkv = c.dm.Hkv;
   const int per_tok = Hkv * V8;
-  const uint4 *ks = reinterpret_cast<const uint4 *>(k_new) +
-                    (size_t)(b.src_row[i] + t0) * per_tok;
-  const uint4 *vs = reinterpret_cast<const uint4 *>(v_new) +
-                    (size_t)(b.src_row[i] + t0) * per_tok;
+  const uint4 *ks = reinterpret_cast<const uint4 *>(k_new) + (size_t)(b.src_row[i] + t0) * per_tok;
+  const uint4 *vs = reinterpret_cast<const uint4 *>(v_new) + (size_t)(b.src_row[i] + t0) * per_tok;
   for (int idx = threadIdx.x; idx < nt * per_tok; idx += blockDim.x) {
-    int t = idx / per_tok, r = idx - t * per_tok;
-    int h = r / V8, c8 = r - h * V8;
-    int pos = b.old_len[i] + t0 + t;
-    int page = pt[(size_t)seq * pps + pos / kPage];
-    size_t dst = (((size_t)page * Hkv + h) * kPage + (pos % kPage)) * V8 + c8;
-    reinterpret_cast<uint4 *>(kpool)[dst] = ks[idx];
-    reinterpret_cast<uint4 *>(vpool)[dst] = vs[idx];
+    const int t = idx / per_tok, r = idx - t * per_tok;
+    const int h = r / V8, c8 = r - h * V8;
+    const int pos = b.old_len[i] + t0 + t;
+    const int page = c.L.pt[(size_t)seq * c.dm.pages_per_seq + pos / kPage];
+    const size_t dst = (((size_t)page * Hkv + h) * kPage + (pos % kPage)) * V8 + c8;
+    reinterpret_cast<uint4 *>(c.L.k)[dst] = ks[idx];
+    reinterpret_cast<uint4 *>(c.L.v)[dst] = vs[idx];
   }
 }
 
 // append: exact per-block min/max key summaries of every touched block.
-// Thread = (touched block, channel quad); tokens of the block are folded in
-// logical order, starting from the stored summary if the block already held
-// tokens.  Layout per (seq, head): [d/4][nbmax][4 x (min, max)] bf16.
+// Thread = (touched block, channel quad); tokens are folded in logical order,
+// starting from the stored summary if the block already held tokens.  Layout
+// per (seq, head): [d/4][nbmax][4 x (min, max)] bf16, so that scoring reads
+// 16 contiguous bytes per lane with consecutive lanes on consecutive blocks.
 template <int D>
-__global__ __launch_bounds__(256) void k_append_summ(
-    uint16_t *__restrict__ summ, const HeadInfo *__restrict__ heads,
-    AppendBatch b, int Hkv, const uint16_t *__restrict__ k_new) {
-  const int h = blockIdx.y, i = blockIdx.z;
+__device__ void append_summ(const Ctx &c, const AppendBatch &b, int i, int h,
+                            int idx, const uint16_t *__restrict__ k_new) {
   const int n_new = b.n_new[i];
   if (n_new <= 0) return;
-  const HeadInfo hi = heads[h];
-  const int S = hi.S;
+  const HeadInfo hi = c.heads[h];
+  const int S = hi.S, Hkv = c.dm.Hkv;
   const int old_len = b.old_len[i], new_len = old_len + n_new;
   const int first = old_len / S, last = (new_len - 1) / S;
   const int n_touch = last - first + 1;
-  const int idx = blockIdx.x * blockDim.x + threadIdx.x;
   constexpr int C4 = D / 4;
   if (idx >= n_touch * C4) return;
   const int tb = idx / C4, c4 = idx - tb * C4;
   const int blk = first + tb;
   const int seq = b.seq[i];
-  uint16_t *sp = summ + hi.summ_off + (size_t)seq * C4 * hi.nbmax * 8 +
+  uint16_t *sp = c.L.summ + hi.summ_off + (size_t)seq * C4 * hi.nbmax * 8 +
                  ((size_t)c4 * hi.nbmax + blk) * 8;
   const int t_lo = max(blk * S, old_len), t_hi = min(blk * S + S, new_len);
   float mn[4], mx[4];
   uint16_t bmn[4], bmx[4];
-  const uint16_t *src0 = k_new + ((size_t)(b.src_row[i] + t_lo - old_len) * Hkv + h) * D + 4 * c4;
   int t = t_lo;
   if (blk * S < old_len) {
-    uint4 w = *reinterpret_cast<const uint4 *>(sp);
-    uint32_t ws[4] = {w.x, w.y, w.z, w.w};
+    const uint4 w = *reinterpret_cast<const uint4 *>(sp);
+    const uint32_t ws[4] = {w.x, w.y, w.z, w.w};
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
       bmn[j] = (uint16_t)(ws[j] & 0xffffu);
       bmx[j] = (uint16_t)(ws[j] >> 16);
     }
   } else {
-    uint2 w = *reinterpret_cast<const uint2 *>(src0);
-    uint32_t ws[2] = {w.x, w.y};
+    const uint16_t *src0 = k_new + ((size_t)(b.src_row[i] + t_lo - old_len) * Hkv + h) * D + 4 * c4;
+    const uint2 w = *reinterpret_cast<const uint2 *>(src0);
+    const uint32_t ws[2] = {w.x, w.y};
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
-      uint16_t x = (uint16_t)((ws[j >> 1] >> (16 * (j & 1))) & 0xffffu);
+      const uint16_t x = (uint16_t)((ws[j >> 1] >> (16 * (j & 1))) & 0xffffu);
       bmn[j] = x;
       bmx[j] = x;
     }
@@ -211,12 +261,12 @@ __global__ __launch_bounds__(256) void k_append_summ(
   }
   for (; t < t_hi; ++t) {
     const uint16_t *src = k_new + ((size_t)(b.src_row[i] + t - old_len) * Hkv + h) * D + 4 * c4;
-    uint2 w = *reinterpret_cast<const uint2 *>(src);
-    uint32_t ws[2] = {w.x, w.y};
+    const uint2 w = *reinterpret_cast<const uint2 *>(src);
+    const uint32_t ws[2] = {w.x, w.y};
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
-      uint16_t x = (uint16_t)((ws[j >> 1] >> (16 * (j & 1))) & 0xffffu);
-      float f = __uint_as_float((uint32_t)x << 16);
+      const uint16_t x = (uint16_t)((ws[j >> 1] >> (16 * (j & 1))) & 0xffffu);
+      const float f = __uint_as_float((uint32_t)x << 16);
       if (f < mn[j]) { mn[j] = f; bmn[j] = x; }
       if (f > mx[j]) { mx[j] = f; bmx[j] = x; }
     }
@@ -230,445 +280,661 @@ __global__ __launch_bounds__(256) void k_append_summ(
 }
 
 // ---------------------------------------------------------------------------
-// select, step 1: split each query value into (min(q,0), max(q,0)) in double,
-// so that max(q*m, q*M) = q- * m + q+ * M with one of the two terms zero.
-__global__ __launch_bounds__(256) void k_qprep(const uint16_t *__restrict__ q,
-                                               double2 *__restrict__ qpm,
-                                               int n) {
-  int idx = blockIdx.x * blockDim.x + threadIdx.x;
-  if (idx < n) {
-    double x = (double)__uint_as_float((uint32_t)q[idx] << 16);
-    qpm[idx] = make_double2(fmin(x, 0.0), fmax(x, 0.0));
-  }
+// score, approximate pass ([LFPS] block-based Quest bound, R2):
+//   U_h(i) = sum_c max(q_hc m_ic, q_hc M_ic) = sum_c q-_hc m_ic + q+_hc M_ic
+// with q- = min(q,0), q+ = max(q,0) (exact in bf16), so the bound of 16
+// blocks x 16 (padded) heads is a bf16 MFMA product: A = [q-, q+] per
+// channel, B = the (min, max) summaries exactly as stored (one 16-byte
+// summary chunk of 4 channels is one lane's 8 k-values).  The fp32 result A_i
+// (group max over the KV head's query heads, R1) carries an error bound
+// eps_i from a second MFMA over absolute values; the top-k then re-scores
+// exactly, in double and in channel order, every block whose approximate
+// score lies within the band of the k-th.
+__device__ __forceinline__ uint32_t key_to_bits(uint32_t k) {
+  return (k & 0x80000000u) ? (k & 0x7fffffffu) : ~k;
+}
+__device__ __forceinline__ float key_to_float(uint32_t k) {
+  return __uint_as_float(key_to_bits(k));
 }
 
-// select, step 2: block score ([LFPS] block-based Quest, Extended reading
-// notes): U_h(i) = sum_c max(q_hc m_ic, q_hc M_ic), accumulated in double in
-// channel order (the products of bf16 values are exact, so every partial sum
-// equals the plain sequential double sum); group score = max over the KV
-// head's query heads, rounded once to fp32 and mapped to an order-preserving
-// uint32 key (0 = not a candidate).  One lane per block; the query terms are
-// wave-uniform and come through the scalar cache.
+// fp32 error bound of an MFMA sum of n <= 256 products of bf16 values with
+// total magnitude E: 2 * gamma_256 * E (gamma_n = n u / (1 - n u),
+// u = 2^-24), plus one float rounding of the exact score.
+__device__ __forceinline__ float score_eps(float E, float A) {
+  return 3.1e-5f * E + 1.2e-7f * fabsf(A) + 1e-30f;
+}
+
 template <int D, int G>
-__global__ __launch_bounds__(64) void k_score(
-    const uint16_t *__restrict__ summ, const float *__restrict__ maw,
-    const HeadInfo *__restrict__ heads, SeqBatch b, Dims dm,
-    const double2 *__restrict__ qpm, uint32_t *__restrict__ keys,
-    uint8_t *__restrict__ flags) {
-  const int h = blockIdx.y, i = blockIdx.z;
-  const HeadInfo hi = heads[h];
-  const int N = b.len[i], seq = b.seq[i];
-  const Geom g = geom(N, hi.S, dm.n_sink, dm.window);
-  if ((int)blockIdx.x * 64 >= g.n_blk) return;
-  const int blk = blockIdx.x * 64 + threadIdx.x;
-  const bool live = blk < g.n_blk;
-  const int blk_c = live ? blk : g.n_blk - 1;
+__device__ void score_tile(const Ctx &c, int i, int seq, int h, const HeadInfo &hi,
+                           const UG &g, int tile, const uint16_t *__restrict__ q,
+                           uint32_t *red /* LDS [4] */) {
+  constexpr int MM = D / 16;    // MFMAs per 16 blocks (k = 2d values, 32 per MFMA)
+  constexpr int GPW = 4;        // 16-block groups per wave
   constexpr int C4 = D / 4;
-  const uint4 *sp = reinterpret_cast<const uint4 *>(
-                        summ + hi.summ_off + (size_t)seq * C4 * hi.nbmax * 8) + blk_c;
-  const double2 *qp = qpm + ((size_t)i * dm.Hq + (size_t)h * G) * D;
-  double acc[G];
+  const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
+  const int r16 = lane & 15, lgrp = lane >> 4;
+  const int base = tile * kScoreTile + wv * 64;
+  const bool active = base < g.n_blk;
+  const uint4 *sp = reinterpret_cast<const uint4 *>(c.L.summ + hi.summ_off +
+                                                    (size_t)seq * C4 * hi.nbmax * 8);
+  // every load of the tile is issued before any is used
+  uint4 kf[GPW][MM];
+  const int nb_last = max(g.n_blk - 1, 0);
 #pragma unroll
-  for (int gg = 0; gg < G; ++gg) acc[gg] = 0.0;
+  for (int gi = 0; gi < GPW; ++gi) {
+    const int blk = min(base + gi * 16 + r16, nb_last);
+#pragma unroll
+    for (int mm = 0; mm < MM; ++mm)
+      kf[gi][mm] = active ? sp[(size_t)(4 * mm + lgrp) * hi.nbmax + blk] : make_uint4(0, 0, 0, 0);
+  }
+  const int qh0 = h * G;
+  const uint16_t *qrow = q + ((size_t)i * c.dm.Hq + qh0 + min(r16, G - 1)) * D;
+  uint2 qw[MM];
+#pragma unroll
+  for (int mm = 0; mm < MM; ++mm)
+    qw[mm] = *reinterpret_cast<const uint2 *>(qrow + 4 * (4 * mm + lgrp));
+  __builtin_amdgcn_sched_barrier(0);
+  // A operand: lane = head r16 (zero rows past G), channel quad 4*mm + lgrp,
+  // pairs (q-, q+) matching the (min, max) pairs of the summaries
+  uint4 qa[MM];
+#pragma unroll
+  for (int mm = 0; mm < MM; ++mm) {
+    const uint32_t x[2] = {qw[mm].x, qw[mm].y};
+    uint32_t o4[4];
+#pragma unroll
+    for (int t = 0; t < 2; ++t) {
+      const uint32_t lo = x[t] & 0xffffu, hi16 = x[t] >> 16;
+      const uint32_t lo_neg = (lo & 0x8000u) ? lo : 0u, lo_pos = (lo & 0x8000u) ? 0u : lo;
+      const uint32_t hi_neg = (hi16 & 0x8000u) ? hi16 : 0u, hi_pos = (hi16 & 0x8000u) ? 0u : hi16;
+      o4[2 * t] = lo_neg | (lo_pos << 16);
+      o4[2 * t + 1] = hi_neg | (hi_pos << 16);
+    }
+    qa[mm] = r16 < G ? make_uint4(o4[0], o4[1], o4[2], o4[3]) : make_uint4(0, 0, 0, 0);
+  }
+  const uint32_t absm = 0x7fff7fffu;
+  float emax = 0.0f;
+#pragma unroll
+  for (int gi = 0; gi < GPW; ++gi) {
+    f32x4 acc = {0.f, 0.f, 0.f, 0.f}, acce = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int mm = 0; mm < MM; ++mm) {
+      const uint4 a = qa[mm], b = kf[gi][mm];
+      acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, a),
+                                                    __builtin_bit_cast(bf16x8, b), acc, 0, 0, 0);
+      const uint4 aa = make_uint4(a.x & absm, a.y & absm, a.z & absm, a.w & absm);
+      const uint4 ba = make_uint4(b.x & absm, b.y & absm, b.z & absm, b.w & absm);
+      acce = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, aa),
+                                                     __builtin_bit_cast(bf16x8, ba), acce, 0, 0, 0);
+    }
+    // lane (r16, lgrp) holds block r16 for heads 4*lgrp + jr
+    float A = -INFINITY, E = 0.0f;
+#pragma unroll
+    for (int jr = 0; jr < 4; ++jr)
+      if (lgrp * 4 + jr < G) {
+        A = fmaxf(A, acc[jr]);
+        E = fmaxf(E, acce[jr]);
+      }
+    if constexpr (G > 4) {
+      A = fmaxf(A, __shfl_xor(A, 16, 64));
+      E = fmaxf(E, __shfl_xor(E, 16, 64));
+    }
+    const int blk = base + gi * 16 + r16;
+    if (lgrp == 0 && blk < g.n_blk) {
+      const size_t ko = ((size_t)seq * c.dm.Hkv + h) * c.dm.key_stride + blk;
+      const bool cand = is_candidate(g, blk);
+      unsigned long long kv = cand ? order_key(A) : 0u;
+      if (cand) emax = fmaxf(emax, score_eps(E, A));
+      if (c.dm.maw_beta > 0.0f) {
+        const float mw = c.L.maw[hi.maw_off + (size_t)seq * hi.nbmax + blk];
+        if ((double)mw * (double)dense_count(g) > (double)c.dm.maw_beta * (double)hi.S)
+          kv |= 1ull << 32;
+      }
+      st_dev(&c.sc.keyflag[ko], kv);
+    }
+  }
+  // the unit's largest error bound (non-negative floats order as their bits)
+  uint32_t eb = __float_as_uint(emax);
+#pragma unroll
+  for (int o = 32; o >= 1; o >>= 1) eb = max(eb, (uint32_t)__shfl_xor((int)eb, o, 64));
+  if (lane == 0) red[wv] = eb;
+  __syncthreads();
+  if (threadIdx.x == 0)
+    __hip_atomic_fetch_max(&c.sc.eps_max[(size_t)seq * c.dm.Hkv + h],
+                           max(max(red[0], red[1]), max(red[2], red[3])), __ATOMIC_RELAXED,
+                           __HIP_MEMORY_SCOPE_AGENT);
+}
+
+// Exact score of one block for one query head: sum_c max(q_c m_c, q_c M_c)
+// in double in channel order, exactly the plain sequential double sum (the
+// products of bf16 values are exact).  All loads are issued first.
+template <int D>
+__device__ double exact_head_score(const Ctx &c, int seq, const HeadInfo &hi, int blk,
+                                   const float *qs /* LDS [D] of this head */) {
+  constexpr int C4 = D / 4;
+  const uint4 *sp = reinterpret_cast<const uint4 *>(c.L.summ + hi.summ_off +
+                                                    (size_t)seq * C4 * hi.nbmax * 8) + blk;
+  uint4 w[C4];
+#pragma unroll
+  for (int c4 = 0; c4 < C4; ++c4) w[c4] = sp[(size_t)c4 * hi.nbmax];
+  double acc = 0.0;
 #pragma unroll
   for (int c4 = 0; c4 < C4; ++c4) {
-    const uint4 w = sp[(size_t)c4 * hi.nbmax];
-    const uint32_t ws[4] = {w.x, w.y, w.z, w.w};
+    const uint32_t ws[4] = {w[c4].x, w[c4].y, w[c4].z, w[c4].w};
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
-      const double m = (double)bf16_lo(ws[j]);
-      const double M = (double)bf16_hi(ws[j]);
-#pragma unroll
-      for (int gg = 0; gg < G; ++gg) {
-        const double2 qq = qp[gg * D + 4 * c4 + j];
-        acc[gg] = fma(qq.x, m, acc[gg]);
-        acc[gg] = fma(qq.y, M, acc[gg]);
-      }
+      const double qv = (double)qs[4 * c4 + j];
+      const double a = qv * (double)bf16_lo(ws[j]), b = qv * (double)bf16_hi(ws[j]);
+      acc += a > b ? a : b;
     }
   }
-  double U = acc[0];
-#pragma unroll
-  for (int gg = 1; gg < G; ++gg) U = fmax(U, acc[gg]);
-  if (!live) return;
-  const size_t ko = ((size_t)seq * dm.Hkv + h) * dm.key_stride + blk;
-  keys[ko] = is_candidate(g, blk) ? order_key((float)U) : 0u;
-  if (dm.maw_beta > 0.0f) {
-    const float mw = maw[hi.maw_off + (size_t)seq * hi.nbmax + blk];
-    flags[ko] = ((double)mw * (double)dense_count(g) > (double)dm.maw_beta * (double)hi.S) ? 1 : 0;
-  }
+  return acc;
 }
 
-// Block-wide exclusive scan of one int per thread (256 threads).
+// Block-wide exclusive scan of one int per thread (256 threads): wave scans
+// plus the four wave totals.
 __device__ int block_excl_scan(int v, int *sh, int *total) {
-  const int tid = threadIdx.x;
-  sh[tid] = v;
-  __syncthreads();
-  for (int o = 1; o < 256; o <<= 1) {
-    int x = tid >= o ? sh[tid - o] : 0;
-    __syncthreads();
-    sh[tid] += x;
-    __syncthreads();
+  const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
+  int x = v;
+#pragma unroll
+  for (int o = 1; o < 64; o <<= 1) {
+    const int y = __shfl_up(x, o, 64);
+    if (lane >= o) x += y;
   }
-  int incl = sh[tid];
-  *total = sh[255];
+  if (lane == 63) sh[wv] = x;
   __syncthreads();
-  return incl - v;
+  int base = 0;
+  for (int w = 0; w < wv; ++w) base += sh[w];
+  *total = sh[0] + sh[1] + sh[2] + sh[3];
+  __syncthreads();
+  return base + x - v;
 }
 
-// select, step 3: per (seq, KV head) top-k of the keys, ordered by
-// (flag desc, score desc, index asc) ([FLX] per-head top-k; [HGCA] MAW
-// threshold first).  Radix select over 8-bit digits finds the k-th key T; the
-// output is compacted in ascending block order, taking keys > T and the
-// lowest-index keys == T.
-__global__ __launch_bounds__(256) void k_topk(const HeadInfo *__restrict__ heads,
-                                              SeqBatch b, Dims dm,
-                                              const uint32_t *__restrict__ keys_all,
-                                              const uint8_t *__restrict__ flags_all,
-                                              int32_t *__restrict__ blk_idx,
-                                              int32_t *__restrict__ blk_cnt,
-                                              int k_cap) {
-  __shared__ int hist[256];
-  __shared__ int scan_sh[256];
-  __shared__ int sh_vals[4];
-  const int h = blockIdx.x, i = blockIdx.y, tid = threadIdx.x;
-  const HeadInfo hi = heads[h];
-  const int N = b.len[i], seq = b.seq[i];
-  const Geom g = geom(N, hi.S, dm.n_sink, dm.window);
-  const int n = g.n_blk;
-  const uint32_t *keys = keys_all + ((size_t)seq * dm.Hkv + h) * dm.key_stride;
-  const uint8_t *flags = flags_all + ((size_t)seq * dm.Hkv + h) * dm.key_stride;
-  const bool use_flag = dm.maw_beta > 0.0f;
-
-  if (tid < 4) sh_vals[tid] = 0;
-  __syncthreads();
-  int lc = 0, lf = 0;
-  for (int j = tid; j < n; j += 256) {
-    uint32_t key = keys[j];
-    if (key) {
-      ++lc;
-      if (use_flag && flags[j]) ++lf;
-    }
-  }
-  lc = wave_sum_i(lc);
-  lf = wave_sum_i(lf);
-  if ((tid & 63) == 0) {
-    atomicAdd(&sh_vals[0], lc);
-    atomicAdd(&sh_vals[1], lf);
-  }
-  __syncthreads();
-  const int C = sh_vals[0], F = sh_vals[1];
-  const int kk = min(C, budget_blocks(hi.ppm, N, hi.S));
-  // subset for the radix step: flagged candidates when they alone fill k,
-  // otherwise the unflagged candidates (all flagged ones are taken).
-  const bool take_flagged = F < kk;
-  const int want_flag = take_flagged ? 0 : 1;
-  int kr = take_flagged ? kk - F : kk;
-  uint32_t prefix = 0, mask = 0;
-  const bool radix = kr > 0;
-  if (radix) {
-    for (int pass = 0; pass < 4; ++pass) {
-      const int shift = 24 - 8 * pass;
-      hist[tid] = 0;
-      __syncthreads();
-      for (int j = tid; j < n; j += 256) {
-        uint32_t key = keys[j];
-        int fl = use_flag ? flags[j] : 0;
-        if (key && fl == want_flag && (key & mask) == prefix)
-          atomicAdd(&hist[(key >> shift) & 255u], 1);
-      }
-      __syncthreads();
-      if (tid < 64) {
-        // lane l owns digits 4l..4l+3; find digit d with
-        // count(> d) < kr <= count(>= d), scanning from the top.
-        int c0 = hist[4 * tid], c1 = hist[4 * tid + 1], c2 = hist[4 * tid + 2],
-            c3 = hist[4 * tid + 3];
-        int s = c0 + c1 + c2 + c3;
-        // suffix sum over lanes > tid
-        int suf = s;
+__device__ __forceinline__ int block_sum(int v, int *sh) {
+  int tot;
+  (void)block_excl_scan(v, sh, &tot);
+  return tot;
+}
+__device__ __forceinline__ uint32_t block_max_u(uint32_t v, uint32_t *sh) {
 #pragma unroll
-        for (int o = 1; o < 64; o <<= 1) {
-          int x = __shfl_down(suf, o, 64);
-          if (tid + o < 64) suf += x;
+  for (int o = 32; o >= 1; o >>= 1) v = max(v, (uint32_t)__shfl_xor((int)v, o, 64));
+  if ((threadIdx.x & 63) == 0) sh[threadIdx.x >> 6] = v;
+  __syncthreads();
+  const uint32_t r = max(max(sh[0], sh[1]), max(sh[2], sh[3]));
+  __syncthreads();
+  return r;
+}
+__device__ __forceinline__ uint32_t block_min_u(uint32_t v, uint32_t *sh) {
+#pragma unroll
+  for (int o = 32; o >= 1; o >>= 1) v = min(v, (uint32_t)__shfl_xor((int)v, o, 64));
+  if ((threadIdx.x & 63) == 0) sh[threadIdx.x >> 6] = v;
+  __syncthreads();
+  const uint32_t r = min(min(sh[0], sh[1]), min(sh[2], sh[3]));
+  __syncthreads();
+  return r;
+}
+
+// kr-th largest of the keys of the items with in(j) true (j < n), by radix
+// select over the bits below the common prefix of the subset's min and max
+// (spreads the first digit), with per-wave histograms.  Returns T; kr becomes
+// the number of items equal to T that belong to the top kr.
+template <class KeyF, class InF>
+__device__ uint32_t radix_select(int n, int &kr, KeyF key, InF in, TopkSmem &sm) {
+  const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
+  uint32_t lo = 0xffffffffu, hi = 0u;
+  for (int j = tid; j < n; j += 256)
+    if (in(j)) {
+      const uint32_t k = key(j);
+      lo = min(lo, k);
+      hi = max(hi, k);
+    }
+  lo = block_min_u(lo, sm.red);
+  hi = block_max_u(hi, sm.red);
+  if (lo == hi) return lo;  // every key equal
+  int top = 31 - __clz((int)(lo ^ hi));  // highest differing bit
+  uint32_t prefix = lo & ~((top >= 31) ? 0xffffffffu : ((2u << top) - 1u));
+  uint32_t mask = (top >= 31) ? 0u : ~((2u << top) - 1u);
+  for (int hb = top; hb >= 0; hb -= 8) {
+    const int width = min(8, hb + 1);
+    const int shift = hb + 1 - width;
+    const uint32_t dmask = (1u << width) - 1u;
+    for (int x = tid; x < 4 * 256; x += 256) (&sm.hist[0][0])[x] = 0;
+    __syncthreads();
+    for (int j = tid; j < n; j += 256)
+      if (in(j)) {
+        const uint32_t k = key(j);
+        if ((k & mask) == prefix) atomicAdd(&sm.hist[wv][(k >> shift) & dmask], 1);
+      }
+    __syncthreads();
+    if (tid < 64) {
+      // lane l owns digits 4l..4l+3: find d with count(>d) < kr <= count(>=d)
+      int cs[4];
+#pragma unroll
+      for (int qd = 0; qd < 4; ++qd) {
+        const int dd = 4 * lane + qd;
+        cs[qd] = sm.hist[0][dd] + sm.hist[1][dd] + sm.hist[2][dd] + sm.hist[3][dd];
+      }
+      const int s4 = cs[0] + cs[1] + cs[2] + cs[3];
+      int suf = s4;
+#pragma unroll
+      for (int o = 1; o < 64; o <<= 1) {
+        const int x = __shfl_down(suf, o, 64);
+        if (lane + o < 64) suf += x;
+      }
+      int acc = suf - s4;  // items with digits >= 4(lane+1)
+      for (int qd = 3; qd >= 0; --qd) {
+        if (acc < kr && acc + cs[qd] >= kr) {
+          sm.vals[2] = 4 * lane + qd;
+          sm.vals[3] = acc;
         }
-        int above = suf - s;  // digits >= 4(tid+1)
-        int cs[4] = {c0, c1, c2, c3};
-        int acc = above;
-        for (int q = 3; q >= 0; --q) {
-          if (acc < kr && acc + cs[q] >= kr) {
-            sh_vals[2] = 4 * tid + q;
-            sh_vals[3] = acc;
-          }
-          acc += cs[q];
+        acc += cs[qd];
+      }
+    }
+    __syncthreads();
+    const int digit = sm.vals[2];
+    kr -= sm.vals[3];
+    prefix |= (uint32_t)digit << shift;
+    mask |= dmask << shift;
+    __syncthreads();
+  }
+  return prefix;
+}
+
+// top-k of one unit, ordered by (flag desc, exact fp32 score desc, index asc)
+// ([FLX] per-head top-k; [HGCA] MAW threshold first; R5, R11).  The k-th
+// approximate key T_a is found first; blocks above T_a + 2 eps are in, below
+// T_a - 2 eps out (eps = the unit's largest error bound: the k-th exact key
+// lies within eps of T_a), and the blocks in between are re-scored exactly,
+// one lane per (block, head), and ranked.  The output is compacted in
+// ascending block order.  256 threads; keys and flags live in LDS (InLds) or
+// in the global scratch for very long sequences.
+template <int D, int G, bool InLds>
+__device__ void topk_impl(const Ctx &c, int i, int seq, int h, const HeadInfo &hi,
+                          const UG &g, const uint16_t *__restrict__ q,
+                          int32_t *__restrict__ blk_idx, int32_t *__restrict__ blk_cnt,
+                          int k_cap, TopkSmem &sm) {
+  const int tid = threadIdx.x;
+  const int n = g.n_blk;
+  const size_t uo = ((size_t)seq * c.dm.Hkv + h) * c.dm.key_stride;
+  const unsigned long long *gkf = c.sc.keyflag + uo;
+  uint32_t *gkeys = c.sc.keys + uo;
+  uint8_t *gflags = c.sc.flags + uo;
+  const bool use_flag = c.dm.maw_beta > 0.0f;
+  uint32_t *keys = InLds ? sm.keys : gkeys;
+  uint8_t *flags = InLds ? sm.flags : gflags;
+  int32_t *ulist = InLds ? sm.ulist : c.sc.ulist + uo;
+  // one trip: keys, flags (category bits: 1 MAW flag, 2 sure in, 4
+  // uncertain), the query of the group, the unit's error bound
+  {
+    const uint16_t *qg = q + ((size_t)i * c.dm.Hq + (size_t)h * G) * D;
+    float qv[(G * D + 255) / 256];
+#pragma unroll
+    for (int r = 0; r < (G * D + 255) / 256; ++r) {
+      const int x = r * 256 + tid;
+      qv[r] = x < G * D ? __uint_as_float((uint32_t)qg[x] << 16) : 0.0f;
+    }
+    for (int j0 = 0; j0 < n; j0 += 4 * 256) {
+      unsigned long long kv[4];
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const int j = j0 + r * 256 + tid;
+        kv[r] = j < n ? ld_dev(&gkf[j]) : 0ull;
+      }
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const int j = j0 + r * 256 + tid;
+        if (j < n) {
+          keys[j] = (uint32_t)kv[r];
+          flags[j] = use_flag ? (uint8_t)((kv[r] >> 32) & 1) : 0;
         }
       }
-      __syncthreads();
-      const int digit = sh_vals[2];
-      kr -= sh_vals[3];
-      prefix |= (uint32_t)digit << shift;
-      mask |= 0xffu << shift;
-      __syncthreads();
+    }
+#pragma unroll
+    for (int r = 0; r < (G * D + 255) / 256; ++r) {
+      const int x = r * 256 + tid;
+      if (x < G * D) sm.qs[x] = qv[r];
     }
   }
-  const uint32_t T = prefix;
-  // ordered compaction
+  const double eps = (double)__uint_as_float(ld_dev(&c.sc.eps_max[(size_t)seq * c.dm.Hkv + h]));
+  __syncthreads();
+  if (tid == 0) st_dev(&c.sc.eps_max[(size_t)seq * c.dm.Hkv + h], 0u);  // for the next step
+
+  int lc = 0, lf = 0;
+  for (int j = tid; j < n; j += 256)
+    if (keys[j]) {
+      ++lc;
+      lf += flags[j] & 1;
+    }
+  const int C = block_sum(lc, sm.scan);
+  const int F = block_sum(lf, sm.scan);
+  const int kk = min(C, g.kk);
+  // radix subset: flagged candidates when they alone fill k, otherwise the
+  // unflagged candidates (every flagged one is taken).
+  const bool take_flagged = F < kk;
+  const int want = take_flagged ? 0 : 1;
+  const int k_sub = take_flagged ? kk - F : kk;
+  auto in_sub = [&](int j) { return keys[j] != 0u && (flags[j] & 1) == want; };
+  uint32_t T2 = 0;
+  int kr2 = 0;
+  if (k_sub > 0) {
+    int kr = k_sub;
+    const uint32_t Ta_key = radix_select(n, kr, [&](int j) { return keys[j]; }, in_sub, sm);
+    const double Ta = (double)key_to_float(Ta_key);
+    const double band_lo = Ta - 2.0 * eps, band_hi = Ta + 2.0 * eps;
+    // categories, and the uncertain blocks listed in index order
+    const int per = (n + 255) / 256;
+    const int j0 = min(n, tid * per), j1 = min(n, j0 + per);
+    int lin = 0, lunc = 0;
+    for (int j = j0; j < j1; ++j)
+      if (in_sub(j)) {
+        const double A = (double)key_to_float(keys[j]);
+        if (A > band_hi) {
+          flags[j] |= 2;
+          ++lin;
+        } else if (A >= band_lo) {
+          flags[j] |= 4;
+          ++lunc;
+        }
+      }
+    int n_unc;
+    int u = block_excl_scan(lunc, sm.scan, &n_unc);
+    const int n_in = block_sum(lin, sm.scan);
+    for (int j = j0; j < j1; ++j)
+      if (flags[j] & 4) ulist[u++] = j;
+    kr2 = k_sub - n_in;  // taken from the uncertain blocks (>= 1)
+    __syncthreads();
+    // exact keys of the uncertain blocks, one lane per (block, head)
+    constexpr int BPR = 256 / G;  // blocks per round
+    for (int u0 = 0; u0 < n_unc; u0 += BPR) {
+      const int uu = u0 + tid / G, gg = tid % G;
+      const bool on = tid < BPR * G && uu < n_unc;
+      double U = on ? exact_head_score<D>(c, seq, hi, ulist[uu], sm.qs + gg * D) : 0.0;
+      if (on) sm.ud[tid] = U;
+      __syncthreads();
+      if (tid < BPR && u0 + tid < n_unc) {
+        double best = sm.ud[tid * G];
+        for (int x = 1; x < G; ++x)
+          if (sm.ud[tid * G + x] > best) best = sm.ud[tid * G + x];
+        keys[ulist[u0 + tid]] = order_key((float)best);
+      }
+      __syncthreads();
+    }
+    T2 = radix_select(n, kr2, [&](int j) { return keys[j]; },
+                      [&](int j) { return (flags[j] & 4) != 0; }, sm);
+  }
+  // ordered compaction: contiguous index ranges per thread
   const int per = (n + 255) / 256;
   const int j0 = min(n, tid * per), j1 = min(n, j0 + per);
   int leq = 0;
-  if (radix)
-    for (int j = j0; j < j1; ++j) {
-      uint32_t key = keys[j];
-      int fl = use_flag ? flags[j] : 0;
-      if (key && fl == want_flag && key == T) ++leq;
-    }
+  for (int j = j0; j < j1; ++j)
+    if ((flags[j] & 4) && keys[j] == T2) ++leq;
   int tot;
-  const int eq_base = block_excl_scan(leq, scan_sh, &tot);
-  int eq_rank = eq_base;
-  int lsel = 0;
-  for (int j = j0; j < j1; ++j) {
-    uint32_t key = keys[j];
-    if (!key) continue;
-    int fl = use_flag ? flags[j] : 0;
-    bool s = false;
-    if (take_flagged && fl) s = true;
-    else if (radix && fl == want_flag) {
-      if (key > T) s = true;
-      else if (key == T) { s = eq_rank < kr; ++eq_rank; }
+  const int eq_base = block_excl_scan(leq, sm.scan, &tot);
+  auto chosen = [&](int j, int &eq_rank) -> bool {
+    if (!keys[j]) return false;
+    const int f = flags[j];
+    if (take_flagged && (f & 1)) return true;
+    if (f & 2) return true;
+    if (f & 4) {
+      if (keys[j] > T2) return true;
+      if (keys[j] == T2) return eq_rank++ < kr2;
     }
-    lsel += s;
-  }
-  int out = block_excl_scan(lsel, scan_sh, &tot);
-  // second pass writes (recomputing the same decisions)
+    return false;
+  };
+  int eq_rank = eq_base, lsel = 0;
+  for (int j = j0; j < j1; ++j) lsel += chosen(j, eq_rank) ? 1 : 0;
+  int out = block_excl_scan(lsel, sm.scan, &tot);
   eq_rank = eq_base;
-  int32_t *dst = blk_idx + ((size_t)i * dm.Hkv + h) * k_cap;
-  for (int j = j0; j < j1; ++j) {
-    uint32_t key = keys[j];
-    if (!key) continue;
-    int fl = use_flag ? flags[j] : 0;
-    bool s = false;
-    if (take_flagged && fl) s = true;
-    else if (radix && fl == want_flag) {
-      if (key > T) s = true;
-      else if (key == T) { s = eq_rank < kr; ++eq_rank; }
-    }
-    if (s && out < k_cap) dst[out++] = j;
-  }
-  if (tid == 0) blk_cnt[(size_t)i * dm.Hkv + h] = kk;
+  int32_t *dst = blk_idx + ((size_t)i * c.dm.Hkv + h) * k_cap;
+  for (int j = j0; j < j1; ++j)
+    if (chosen(j, eq_rank) && out < k_cap) dst[out++] = j;
+  if (tid == 0) blk_cnt[(size_t)i * c.dm.Hkv + h] = kk;
+}
+
+template <int D, int G>
+__device__ void topk_unit(const Ctx &c, int i, int seq, int h, const HeadInfo &hi,
+                          const UG &g, const uint16_t *__restrict__ q,
+                          int32_t *__restrict__ blk_idx, int32_t *__restrict__ blk_cnt,
+                          int k_cap, TopkSmem &sm) {
+  if (g.n_blk <= kTopkLdsKeys)
+    topk_impl<D, G, true>(c, i, seq, h, hi, g, q, blk_idx, blk_cnt, k_cap, sm);
+  else
+    topk_impl<D, G, false>(c, i, seq, h, hi, g, q, blk_idx, blk_cnt, k_cap, sm);
 }
 
 // ---------------------------------------------------------------------------
-// attend: split-K softmax attention of the G query heads of one KV head over
-// one chunk of its attended blocks (dense sinks + window + selected blocks,
-// each token once; [HGCA] What carries the argument).  Writes the chunk's
-// normalised O and lse per head, and the log of each block's softmax mass
-// (for the MAW update).  Lanes of a 16 (d=128) or 8 (d=64) lane group share
-// one K/V row, 16 bytes each.
+// DPP exchanges inside 16-lane rows (gfx9 encodings): every lane of a row
+// receives the row's max / sum.
+template <int CTRL>
+__device__ __forceinline__ float dppf(float x) {
+  return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), CTRL, 0xF, 0xF, false));
+}
+__device__ __forceinline__ float row_max16(float x) {
+  x = fmaxf(x, dppf<0xB1>(x));   // quad_perm [1,0,3,2]
+  x = fmaxf(x, dppf<0x4E>(x));   // quad_perm [2,3,0,1]
+  x = fmaxf(x, dppf<0x141>(x));  // row_half_mirror
+  x = fmaxf(x, dppf<0x140>(x));  // row_mirror
+  return x;
+}
+__device__ __forceinline__ float row_sum16(float x) {
+  x += dppf<0xB1>(x);
+  x += dppf<0x4E>(x);
+  x += dppf<0x141>(x);
+  x += dppf<0x140>(x);
+  return x;
+}
+
+// attend: softmax attention of the G query heads of one KV head over one
+// chunk of its blocks ([HGCA] What carries the argument: dense window plus
+// selected entries, each part with its own normalisation statistics).  Each
+// wave owns 4 pages of the chunk end to end: page lookup, q.K with one
+// v_mfma_f32_16x16x32_bf16 tile per 16-token page (q rows padded to 16),
+// softmax over its tokens with DPP row reductions, p*V on fp32 VALU.  The
+// four waves meet once to merge their (max, sum, O) and write the chunk's
+// normalised O, its lse and the log softmax mass of each block (for MAW).
 template <int D, int G>
-__global__ __launch_bounds__(256) void k_attend(
-    LayerDev L, const HeadInfo *__restrict__ heads, SeqBatch b, Dims dm,
-    Scratch sc, const uint16_t *__restrict__ q,
-    const int32_t *__restrict__ blk_idx, const int32_t *__restrict__ blk_cnt,
-    int k_cap, float *__restrict__ o_part, float *__restrict__ lse_part,
-    int p_cap) {
-  constexpr int LPR = D / 8;           // lanes per row
-  constexpr int RPW = 64 / LPR;        // rows per wave per step
-  constexpr int RPS = 4 * RPW;         // rows per workgroup step
-  constexpr int GP = G <= 4 ? 4 : 8;   // padded head count in LDS
-  constexpr int MAXCB = kChunkTokens / kPage;
-  __shared__ float p_sh[kChunkTokens][GP];
-  __shared__ float red_sh[4][G][D];
-  __shared__ float stat_sh[2][4][G];
-  __shared__ float bsum_sh[MAXCB][G];
-  __shared__ int blk_sh[MAXCB];
-  __shared__ unsigned long long mask_sh[MAXCB];
-  __shared__ int geo_sh[2];
+struct AttSmem {
+  static constexpr int GP = G <= 4 ? 4 : 8;
+  static constexpr int PPW = kChunkTokens / kPage / 4;  // pages per wave
+  float p[4][PPW * kPage][GP];  // per-wave softmax weights of its token slots
+  float wo[4][G][D];            // per-wave unnormalised O
+  float wm[4][G];               // per-wave max (log2 units)
+  float wz[4][G];               // per-wave sum
+  float pmass[4 * PPW][G];      // per-page mass relative to its wave max
+};
 
-  const int chunk = blockIdx.x, h = blockIdx.y, i = blockIdx.z;
+__device__ __forceinline__ unsigned long long bit_range(int a, int b) {
+  if (b <= a) return 0ull;
+  const unsigned long long hi = b >= 64 ? ~0ull : ((1ull << b) - 1ull);
+  const unsigned long long lo = (1ull << a) - 1ull;  // a < b <= 64
+  return hi & ~lo;
+}
+// Token mask of a block: its dense tokens (dense chunks) or its tokens outside
+// the dense set (selected chunks).
+__device__ __forceinline__ unsigned long long block_mask(const UG &g, int blk, bool dense) {
+  if (blk < 0 || blk >= g.n_blk) return 0ull;
+  const int lo = blk * g.S, cnt = min(g.S, g.N - lo);
+  const unsigned long long all = bit_range(0, cnt);
+  const unsigned long long dm = bit_range(0, min(max(g.ns - lo, 0), cnt)) |
+                                bit_range(min(max(g.wlo - lo, 0), cnt), cnt);
+  return dense ? dm : (all & ~dm);
+}
+
+template <int D, int G>
+__device__ void attend_chunk(const Ctx &c, int i, int seq, int h, const HeadInfo &hi,
+                             const UG &g, bool dense, int chunk, int cnt,
+                             const int32_t *__restrict__ sel,
+                             const uint16_t *__restrict__ q, float *__restrict__ o_part,
+                             float *__restrict__ lse_part, int p_cap,
+                             AttSmem<D, G> &sm) {
+  constexpr int GP = AttSmem<D, G>::GP;
+  constexpr int PPW = AttSmem<D, G>::PPW;
+  constexpr int KV4 = D / 32;                       // MFMA k-steps per page row
+  constexpr int LPR = D / 8, RPI = 64 / LPR, VIT = kPage / RPI;  // p*V layout
   const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
-  const HeadInfo hi = heads[h];
-  const int N = b.len[i], seq = b.seq[i], S = hi.S, CB = hi.chunk_blocks;
-  const Geom g = geom(N, S, dm.n_sink, dm.window);
-  const int32_t *sel = blk_idx + ((size_t)i * dm.Hkv + h) * k_cap;
+  const int S = g.S, CB = g.CB, PPB = S / kPage;
   const int qh0 = h * G;
-
-  if (tid == 0) {
-    int k = min(max(blk_cnt[(size_t)i * dm.Hkv + h], 0), k_cap);
-    int a = lower_bound(sel, k, g.hb), bb = lower_bound(sel, k, g.tb);
-    if (bb < a) bb = a;
-    // |U|, clamped to the scratch capacity (only reachable with inputs that
-    // violate the documented k_cap contract)
-    geo_sh[0] = min(g.hb + (bb - a) + (g.n_blk - g.tb), dm.u_cap);
-    geo_sh[1] = a;
-  }
-  __syncthreads();
-  const int nU = geo_sh[0], a_sel = geo_sh[1];
-  const int c0 = chunk * CB;
-  const size_t ohead = ((size_t)i * dm.Hq + qh0) * p_cap + chunk;
-  if (c0 >= nU) {  // empty slot: lse = -inf, O = 0
+  const int slot = dense ? chunk : hi.pd + chunk;
+  const int total = dense ? g.n_dt : cnt;
+  const int nb = min(CB, total - chunk * CB);
+  const size_t ohead = ((size_t)i * c.dm.Hq + qh0) * p_cap + slot;
+  if (nb <= 0) {  // empty slot: lse = -inf, O = 0
     for (int x = tid; x < G * D; x += 256)
-      o_part[(ohead + (size_t)(x / D) * p_cap) * D + (x % D)] = 0.0f;
-    if (tid < G) lse_part[ohead + (size_t)tid * p_cap] = -INFINITY;
+      st_dev(&o_part[(ohead + (size_t)(x / D) * p_cap) * D + (x % D)], 0.0f);
+    if (tid < G) st_dev(&lse_part[ohead + (size_t)tid * p_cap], -INFINITY);
     return;
   }
-  const int nb = min(CB, nU - c0);
-  const int mid = nU - g.hb - (g.n_blk - g.tb);  // selected blocks in [hb, tb)
-  if (tid < nb) {
-    const int j = c0 + tid;
-    int blk;
-    bool selected;
-    if (j < g.hb) {
-      blk = j;
-    } else if (j < g.hb + mid) {
-      blk = sel[a_sel + j - g.hb];
-    } else {
-      blk = g.tb + (j - g.hb - mid);
-    }
-    if (j >= g.hb && j < g.hb + mid) {
-      selected = true;
-    } else {
-      int k = min(max(blk_cnt[(size_t)i * dm.Hkv + h], 0), k_cap);
-      int p = lower_bound(sel, k, blk);
-      selected = p < k && sel[p] == blk;
-    }
-    unsigned long long m = 0ull;
-    if (blk >= 0 && blk < g.n_blk) {
-      const int lo = blk * S, cnt = min(S, N - lo);
-      for (int r = 0; r < cnt; ++r) {
-        const int t = lo + r;
-        if (selected || t < g.ns || t >= g.wlo) m |= 1ull << r;
-      }
-    } else {
-      blk = 0;
-    }
-    blk_sh[tid] = blk;
-    mask_sh[tid] = m;
-  }
-  __syncthreads();
+  const int npg = nb * PPB;
+  const int p0 = wv * PPW;
 
-  // query of this lane's channels (fixed for the whole kernel)
-  const int lg = lane / LPR, cl = lane % LPR;
-  float qv[G][8];
-#pragma unroll
-  for (int gg = 0; gg < G; ++gg) {
-    const uint4 w = *reinterpret_cast<const uint4 *>(
-        q + ((size_t)i * dm.Hq + qh0 + gg) * D + 8 * cl);
-    const uint32_t ws[4] = {w.x, w.y, w.z, w.w};
-#pragma unroll
-    for (int e = 0; e < 4; ++e) {
-      qv[gg][2 * e] = bf16_lo(ws[e]) * dm.scale_log2;
-      qv[gg][2 * e + 1] = bf16_hi(ws[e]) * dm.scale_log2;
+  // ---- page lookup for this wave's pages (lanes 0..PPW-1), made uniform ----
+  int my_page = 0, my_mask = 0;
+  if (lane < PPW) {
+    const int p = p0 + lane;
+    if (p < npg) {
+      const int jj = p / PPB, pp = p - jj * PPB;
+      const int j = chunk * CB + jj;
+      const int blk = dense ? dense_block(g, j) : sel[j];
+      const unsigned long long m = block_mask(g, blk, dense);
+      if (!dense && pp == 0) st_dev(&c.sc.usel[((size_t)seq * c.dm.Hkv + h) * c.dm.kcap + j], blk);
+      my_mask = (int)((m >> (pp * kPage)) & 0xffffull);
+      if (my_mask)
+        my_page = c.L.pt[(size_t)seq * c.dm.pages_per_seq + (blk * S + pp * kPage) / kPage];
     }
   }
+  int pg[PPW], pmk[PPW];
+#pragma unroll
+  for (int pi = 0; pi < PPW; ++pi) {
+    pg[pi] = __builtin_amdgcn_readlane(my_page, pi);
+    pmk[pi] = __builtin_amdgcn_readlane(my_mask, pi);
+  }
 
-  const int n_slots = nb * S;
-  const int32_t *pt = L.pt + (size_t)seq * dm.pages_per_seq;
-  // pass 1: scaled logits (log2 units) into p_sh; masked slots get -inf
-  for (int base = 0; base < n_slots; base += RPS) {
-    const int t = base + wv * RPW + lg;
-    float acc[G];
+  // ---- loads: K rows in the MFMA B layout, V rows in the p*V layout -------
+  const int r16 = lane & 15, lgrp = lane >> 4;
+  const int cl = lane % LPR, lg = lane / LPR;
+  uint4 kf[PPW][KV4];
+  uint4 vf[PPW][VIT];
 #pragma unroll
-    for (int gg = 0; gg < G; ++gg) acc[gg] = 0.0f;
-    bool on = false;
-    if (t < n_slots) {
-      const int jj = t / S, r = t - jj * S;
-      on = (mask_sh[jj] >> r) & 1ull;
-      if (on) {
-        const int pos = blk_sh[jj] * S + r;
-        const int page = pt[pos / kPage];
-        const uint4 w = *reinterpret_cast<const uint4 *>(
-            L.k + (((size_t)page * dm.Hkv + h) * kPage + (pos % kPage)) * D + 8 * cl);
-        const uint32_t ws[4] = {w.x, w.y, w.z, w.w};
+  for (int pi = 0; pi < PPW; ++pi) {
+    const size_t pbase = ((size_t)pg[pi] * c.dm.Hkv + h) * kPage;
+    const bool kon = (pmk[pi] >> r16) & 1;
 #pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          const float k0 = bf16_lo(ws[e]), k1 = bf16_hi(ws[e]);
+    for (int m = 0; m < KV4; ++m)
+      kf[pi][m] = kon ? *reinterpret_cast<const uint4 *>(c.L.k + (pbase + r16) * D +
+                                                         lgrp * (D / 4) + 8 * m)
+                      : make_uint4(0, 0, 0, 0);
+  }
 #pragma unroll
-          for (int gg = 0; gg < G; ++gg) {
-            acc[gg] = fmaf(qv[gg][2 * e], k0, acc[gg]);
-            acc[gg] = fmaf(qv[gg][2 * e + 1], k1, acc[gg]);
-          }
+  for (int pi = 0; pi < PPW; ++pi) {
+    const size_t pbase = ((size_t)pg[pi] * c.dm.Hkv + h) * kPage;
+#pragma unroll
+    for (int it = 0; it < VIT; ++it) {
+      const int r = it * RPI + lg;
+      vf[pi][it] = ((pmk[pi] >> r) & 1)
+                       ? *reinterpret_cast<const uint4 *>(c.L.v + (pbase + r) * D + 8 * cl)
+                       : make_uint4(0, 0, 0, 0);
+    }
+  }
+  // q in the MFMA A layout: row r16 = head (zero past G), same channel order
+  uint4 qa[KV4];
+#pragma unroll
+  for (int m = 0; m < KV4; ++m)
+    qa[m] = r16 < G ? *reinterpret_cast<const uint4 *>(
+                          q + ((size_t)i * c.dm.Hq + qh0 + r16) * D + lgrp * (D / 4) + 8 * m)
+                    : make_uint4(0, 0, 0, 0);
+
+  // ---- q.K: lane holds token r16 of page pi for heads 4*lgrp + jr --------
+  float sc[PPW][4];
+#pragma unroll
+  for (int pi = 0; pi < PPW; ++pi) {
+    f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+    if (p0 + pi < npg) {
+#pragma unroll
+      for (int m = 0; m < KV4; ++m)
+        acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, qa[m]),
+                                                      __builtin_bit_cast(bf16x8, kf[pi][m]),
+                                                      acc, 0, 0, 0);
+    }
+    const bool on = (pmk[pi] >> r16) & 1;
+#pragma unroll
+    for (int jr = 0; jr < 4; ++jr) sc[pi][jr] = on ? acc[jr] * c.dm.scale_log2 : -INFINITY;
+  }
+  // ---- softmax over the wave's tokens (per head = per (row, jr)) ----------
+  float wmax[4], wsum[4];
+#pragma unroll
+  for (int jr = 0; jr < 4; ++jr) {
+    float m = sc[0][jr];
+#pragma unroll
+    for (int pi = 1; pi < PPW; ++pi) m = fmaxf(m, sc[pi][jr]);
+    wmax[jr] = row_max16(m);
+  }
+  float pmass_l[PPW][4];
+#pragma unroll
+  for (int jr = 0; jr < 4; ++jr) {
+    float z = 0.0f;
+#pragma unroll
+    for (int pi = 0; pi < PPW; ++pi) {
+      const float pr = (sc[pi][jr] == -INFINITY) ? 0.0f : exp2f(sc[pi][jr] - wmax[jr]);
+      sc[pi][jr] = pr;
+      pmass_l[pi][jr] = row_sum16(pr);
+      z += pmass_l[pi][jr];
+    }
+    wsum[jr] = z;
+  }
+  // weights to LDS (wave-private region), per-wave stats
+  if (lgrp * 4 < G) {
+#pragma unroll
+    for (int pi = 0; pi < PPW; ++pi)
+      *reinterpret_cast<float4 *>(&sm.p[wv][pi * kPage + r16][lgrp * 4]) =
+          make_float4(sc[pi][0], sc[pi][1], sc[pi][2], sc[pi][3]);
+    if (r16 == 0) {
+#pragma unroll
+      for (int jr = 0; jr < 4; ++jr) {
+        const int head = lgrp * 4 + jr;
+        if (head < G) {
+          sm.wm[wv][head] = wmax[jr];
+          sm.wz[wv][head] = wsum[jr];
+#pragma unroll
+          for (int pi = 0; pi < PPW; ++pi) sm.pmass[p0 + pi][head] = pmass_l[pi][jr];
         }
       }
     }
-#pragma unroll
-    for (int gg = 0; gg < G; ++gg) acc[gg] = group_sum<LPR>(acc[gg]);
-    if (t < n_slots && cl == 0) {
-#pragma unroll
-      for (int gg = 0; gg < G; ++gg) p_sh[t][gg] = on ? acc[gg] : -INFINITY;
-    }
   }
-  __syncthreads();
+  __builtin_amdgcn_s_waitcnt(0xc07f);  // lgkmcnt(0): this wave's LDS writes are done
+  __builtin_amdgcn_wave_barrier();
 
-  // softmax statistics per head over the chunk
-  float mloc[G];
-#pragma unroll
-  for (int gg = 0; gg < G; ++gg) {
-    float x = -INFINITY;
-    for (int t = tid; t < n_slots; t += 256) x = fmaxf(x, p_sh[t][gg]);
-    x = wave_max(x);
-    if (lane == 0) stat_sh[0][wv][gg] = x;
-  }
-  __syncthreads();
-#pragma unroll
-  for (int gg = 0; gg < G; ++gg)
-    mloc[gg] = fmaxf(fmaxf(stat_sh[0][0][gg], stat_sh[0][1][gg]),
-                     fmaxf(stat_sh[0][2][gg], stat_sh[0][3][gg]));
-#pragma unroll
-  for (int gg = 0; gg < G; ++gg) {
-    float x = 0.0f;
-    for (int t = tid; t < n_slots; t += 256) {
-      const float s = p_sh[t][gg];
-      const float p = s == -INFINITY ? 0.0f : exp2f(s - mloc[gg]);
-      p_sh[t][gg] = p;
-      x += p;
-    }
-    x = wave_sum(x);
-    if (lane == 0) stat_sh[1][wv][gg] = x;
-  }
-  __syncthreads();
-  float zsum[G];
-#pragma unroll
-  for (int gg = 0; gg < G; ++gg)
-    zsum[gg] = (stat_sh[1][0][gg] + stat_sh[1][1][gg]) +
-               (stat_sh[1][2][gg] + stat_sh[1][3][gg]);
-  // per-block mass sums (MAW)
-  if (tid < nb * G) {
-    const int jj = tid / G, gg = tid % G;
-    float x = 0.0f;
-    for (int r = 0; r < S; ++r) x += p_sh[jj * S + r][gg];
-    bsum_sh[jj][gg] = x;
-  }
-
-  // pass 2: O = sum_t p_t v_t
+  // ---- p*V on fp32 VALU ---------------------------------------------------
   float o[G][8];
 #pragma unroll
   for (int gg = 0; gg < G; ++gg)
 #pragma unroll
     for (int e = 0; e < 8; ++e) o[gg][e] = 0.0f;
-  for (int base = 0; base < n_slots; base += RPS) {
-    const int t = base + wv * RPW + lg;
-    if (t < n_slots) {
-      const int jj = t / S, r = t - jj * S;
-      if ((mask_sh[jj] >> r) & 1ull) {
-        const int pos = blk_sh[jj] * S + r;
-        const int page = pt[pos / kPage];
-        const uint4 w = *reinterpret_cast<const uint4 *>(
-            L.v + (((size_t)page * dm.Hkv + h) * kPage + (pos % kPage)) * D + 8 * cl);
-        const uint32_t ws[4] = {w.x, w.y, w.z, w.w};
-        float pw[G];
 #pragma unroll
-        for (int gg = 0; gg < G; ++gg) pw[gg] = p_sh[t][gg];
+  for (int pi = 0; pi < PPW; ++pi) {
+    if (p0 + pi >= npg) continue;
 #pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          const float v0 = bf16_lo(ws[e]), v1 = bf16_hi(ws[e]);
+    for (int it = 0; it < VIT; ++it) {
+      const int t = pi * kPage + it * RPI + lg;
+      float pw[GP];
+      {
+        const float4 x = *reinterpret_cast<const float4 *>(&sm.p[wv][t][0]);
+        pw[0] = x.x; pw[1] = x.y; pw[2] = x.z; pw[3] = x.w;
+        if constexpr (GP == 8) {
+          const float4 y = *reinterpret_cast<const float4 *>(&sm.p[wv][t][4]);
+          pw[4] = y.x; pw[5] = y.y; pw[6] = y.z; pw[7] = y.w;
+        }
+      }
+      const uint32_t ws[4] = {vf[pi][it].x, vf[pi][it].y, vf[pi][it].z, vf[pi][it].w};
 #pragma unroll
-          for (int gg = 0; gg < G; ++gg) {
-            o[gg][2 * e] = fmaf(pw[gg], v0, o[gg][2 * e]);
-            o[gg][2 * e + 1] = fmaf(pw[gg], v1, o[gg][2 * e + 1]);
-          }
+      for (int e = 0; e < 4; ++e) {
+        const float v0 = bf16_lo(ws[e]), v1 = bf16_hi(ws[e]);
+#pragma unroll
+        for (int gg = 0; gg < G; ++gg) {
+          o[gg][2 * e] = fmaf(pw[gg], v0, o[gg][2 * e]);
+          o[gg][2 * e + 1] = fmaf(pw[gg], v1, o[gg][2 * e + 1]);
         }
       }
     }
   }
-  // reduce over the row groups of the wave (lanes with equal cl)
 #pragma unroll
   for (int gg = 0; gg < G; ++gg)
 #pragma unroll
@@ -682,102 +948,320 @@ __global__ __launch_bounds__(256) void k_attend(
 #pragma unroll
     for (int gg = 0; gg < G; ++gg)
 #pragma unroll
-      for (int e = 0; e < 8; ++e) red_sh[wv][gg][8 * cl + e] = o[gg][e];
+      for (int e = 0; e < 8; ++e) sm.wo[wv][gg][8 * cl + e] = o[gg][e];
   }
   __syncthreads();
-  for (int x = tid; x < G * D; x += 256) {
-    const int gg = x / D, c = x - gg * D;
-    const float v = (red_sh[0][gg][c] + red_sh[1][gg][c]) +
-                    (red_sh[2][gg][c] + red_sh[3][gg][c]);
-    const float z = zsum[gg];
-    o_part[(ohead + (size_t)gg * p_cap) * D + c] = z > 0.0f ? v / z : 0.0f;
-  }
+
+  // ---- merge the four waves -----------------------------------------------
   constexpr float kLn2 = 0.69314718055994530942f;
-  if (tid < G) {
-    const float z = zsum[tid];
-    lse_part[ohead + (size_t)tid * p_cap] =
-        z > 0.0f ? (mloc[tid] + log2f(z)) * kLn2 : -INFINITY;
+  for (int x = tid; x < G * D; x += 256) {
+    const int gg = x / D, ch = x - gg * D;
+    const float M = fmaxf(fmaxf(sm.wm[0][gg], sm.wm[1][gg]), fmaxf(sm.wm[2][gg], sm.wm[3][gg]));
+    float Z = 0.0f, v = 0.0f;
+    if (M != -INFINITY)
+#pragma unroll
+      for (int w = 0; w < 4; ++w) {
+        const float f = exp2f(sm.wm[w][gg] - M);
+        Z = fmaf(f, sm.wz[w][gg], Z);
+        v = fmaf(f, sm.wo[w][gg][ch], v);
+      }
+    st_dev(&o_part[(ohead + (size_t)gg * p_cap) * D + ch], Z > 0.0f ? v / Z : 0.0f);
+    if (ch == 0)
+      st_dev(&lse_part[ohead + (size_t)gg * p_cap], Z > 0.0f ? (M + log2f(Z)) * kLn2 : -INFINITY);
   }
-  if (tid < nb * G) {
-    const int jj = tid / G, gg = tid % G;
-    const float z = bsum_sh[jj][gg];
-    sc.lmass[((size_t)seq * dm.Hq + qh0 + gg) * dm.u_cap + c0 + jj] =
-        z > 0.0f ? (mloc[gg] + log2f(z)) * kLn2 : -INFINITY;
-    if (gg == 0) sc.ublk[((size_t)seq * dm.Hkv + h) * dm.u_cap + c0 + jj] = blk_sh[jj];
+  if (tid < nb * G) {  // log softmax mass of each block of the chunk (MAW)
+    const int jj = tid / G, gg = tid - jj * G;
+    const float M = fmaxf(fmaxf(sm.wm[0][gg], sm.wm[1][gg]), fmaxf(sm.wm[2][gg], sm.wm[3][gg]));
+    float z = 0.0f;
+    if (M != -INFINITY)
+      for (int pp = 0; pp < PPB; ++pp) {
+        const int p = jj * PPB + pp;
+        z = fmaf(exp2f(sm.wm[p / PPW][gg] - M), sm.pmass[p][gg], z);
+      }
+    const float lm = z > 0.0f ? (M + log2f(z)) * kLn2 : -INFINITY;
+    const int j = chunk * CB + jj;
+    if (dense)
+      st_dev(&c.sc.lm_dense[((size_t)seq * c.dm.Hq + qh0 + gg) * c.dm.ndt_cap + j], lm);
+    else
+      st_dev(&c.sc.lm_sel[((size_t)seq * c.dm.Hq + qh0 + gg) * c.dm.kcap + j], lm);
   }
-  if (chunk == 0 && tid == 0) sc.ucnt[(size_t)seq * dm.Hkv + h] = nU;
 }
 
 // ---------------------------------------------------------------------------
-// fuse: exact LSE fusion of the split-K partials of each query head ([HGCA]
-// What carries the argument, max-subtracted form), then the MAW update of
-// every block of the (seq, KV head): MAW <- r MAW + (1-r) a, with a the
-// group-mean softmax mass of the block ([LFPS] decay r; [HGCA] MAW).
+// fuse: exact LSE fusion of a unit's partials per query head ([HGCA] What
+// carries the argument, max-subtracted form) and, with MAW, the update of
+// every block: MAW <- r MAW + (1-r) a, a = group-mean softmax mass of the
+// block (0 if not attended) ([LFPS] decay r; [HGCA] MAW).  256 threads.
+// all_slots: fuse every slot of p_cap (lse = -inf ones drop out).
 template <int D, int G>
-__global__ __launch_bounds__(256) void k_fuse(
-    float *__restrict__ maw_all, const HeadInfo *__restrict__ heads,
-    SeqBatch b, Dims dm, Scratch sc, int with_maw,
-    const float *__restrict__ o_part, const float *__restrict__ lse_part,
-    int p_cap, float *__restrict__ o, float *__restrict__ lse) {
-  __shared__ float lse_sh[G];
-  __shared__ float m_sh[G];
-  const int h = blockIdx.x, i = blockIdx.y, tid = threadIdx.x;
-  const int lane = tid & 63, wv = tid >> 6;
+__device__ void fuse_unit(const Ctx &c, int i, int seq, int h, const HeadInfo &hi,
+                          const UG &g, bool with_maw, bool all_slots,
+                          const float *__restrict__ o_part,
+                          const float *__restrict__ lse_part, int p_cap,
+                          float *__restrict__ o, float *__restrict__ lse,
+                          FuseSmem<G> &sm) {
+  const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
   const int qh0 = h * G;
-  // per-head max and lse: wave gg handles head gg (and gg+4, ...)
+  int nd = 0, ns = 0, cnt = 0;
+  if (!all_slots) {
+    cnt = min(ld_dev(&c.sc.ucnt[(size_t)seq * c.dm.Hkv + h]), hi.kcap);
+    nd = cdiv(g.n_dt, g.CB);
+    ns = cdiv(cnt, g.CB);
+  }
+  const int n_slots = min(all_slots ? p_cap : nd + ns, kFuseSlots);
+  auto slot_of = [&](int u) { return (all_slots || u < nd) ? u : hi.pd + (u - nd); };
+  // per-head lse over the slots (wave gg handles heads gg, gg+4); the slot
+  // weights e^{lse_u - lse} go to LDS
+  constexpr int R = kFuseSlots / 64;
   for (int gg = wv; gg < G; gg += 4) {
-    const float *lp = lse_part + ((size_t)i * dm.Hq + qh0 + gg) * p_cap;
-    float m = -INFINITY;
-    for (int p = lane; p < p_cap; p += 64) m = fmaxf(m, lp[p]);
+    const float *lp = lse_part + ((size_t)i * c.dm.Hq + qh0 + gg) * p_cap;
+    float l[R];
+#pragma unroll
+    for (int r = 0; r < R; ++r) {
+      const int u = lane + 64 * r;
+      l[r] = u < n_slots ? ld_dev(&lp[slot_of(u)]) : -INFINITY;
+    }
+    float m = l[0];
+#pragma unroll
+    for (int r = 1; r < R; ++r) m = fmaxf(m, l[r]);
     m = wave_max(m);
     float z = 0.0f;
     if (m != -INFINITY)
-      for (int p = lane; p < p_cap; p += 64) {
-        const float l = lp[p];
-        if (l != -INFINITY) z += expf(l - m);
-      }
+#pragma unroll
+      for (int r = 0; r < R; ++r) z += l[r] == -INFINITY ? 0.0f : expf(l[r] - m);
     z = wave_sum(z);
-    if (lane == 0) {
-      m_sh[gg] = m;
-      lse_sh[gg] = m == -INFINITY ? -INFINITY : m + logf(z);
+    const float L = m == -INFINITY ? -INFINITY : m + logf(z);
+    if (lane == 0) sm.lse[gg] = L;
+#pragma unroll
+    for (int r = 0; r < R; ++r) {
+      const int u = lane + 64 * r;
+      sm.w[gg][u] = (L == -INFINITY || l[r] == -INFINITY) ? 0.0f : expf(l[r] - L);
     }
   }
   __syncthreads();
-  for (int x = tid; x < G * D; x += 256) {
-    const int gg = x / D, c = x - gg * D;
-    const float L = lse_sh[gg];
-    const size_t hb = ((size_t)i * dm.Hq + qh0 + gg) * p_cap;
-    float acc = 0.0f;
-    if (L != -INFINITY)
-      for (int p = 0; p < p_cap; ++p) {
-        const float l = lse_part[hb + p];
-        if (l != -INFINITY) acc = fmaf(expf(l - L), o_part[(hb + p) * D + c], acc);
+  // O = sum_u w_u O_u (loads issued unconditionally; zero weights select 0)
+  constexpr int NP = (G * D + 255) / 256;
+#pragma unroll
+  for (int rr = 0; rr < NP; ++rr) {
+    const int x = tid + 256 * rr;
+    if (x < G * D) {
+      const int gg = x / D, ch = x - gg * D;
+      const size_t hb = ((size_t)i * c.dm.Hq + qh0 + gg) * p_cap;
+      float a = 0.0f;
+#pragma unroll 8
+      for (int u = 0; u < n_slots; ++u) {
+        const float wgt = sm.w[gg][u];
+        const float ov = ld_dev(&o_part[(hb + slot_of(u)) * D + ch]);
+        a = fmaf(wgt, wgt != 0.0f ? ov : 0.0f, a);
       }
-    o[((size_t)i * dm.Hq + qh0 + gg) * D + c] = acc;
+      o[((size_t)i * c.dm.Hq + qh0 + gg) * D + ch] = a;
+    }
   }
-  if (tid < G) lse[(size_t)i * dm.Hq + qh0 + tid] = lse_sh[tid];
+  if (tid < G) lse[(size_t)i * c.dm.Hq + qh0 + tid] = sm.lse[tid];
   if (!with_maw) return;
 
-  const HeadInfo hi = heads[h];
-  const int N = b.len[i], seq = b.seq[i];
-  const int n_blk = (N + hi.S - 1) / hi.S;
-  const int nU = min(sc.ucnt[(size_t)seq * dm.Hkv + h], dm.u_cap);
-  const int32_t *ub = sc.ublk + ((size_t)seq * dm.Hkv + h) * dm.u_cap;
-  float *mw = maw_all + hi.maw_off + (size_t)seq * hi.nbmax;
-  const float r = dm.maw_decay;
-  for (int blk = tid; blk < n_blk; blk += 256) {
-    const int u = lower_bound(ub, nU, blk);
+  // ---- MAW update of every block of the unit -------------------------------
+  // group-mean mass of the attended slots first (independent loads), then one
+  // streaming pass over the blocks.
+  const int n_dt = min(g.n_dt, kFuseSlots);
+  const int32_t *gsel = c.sc.usel + ((size_t)seq * c.dm.Hkv + h) * c.dm.kcap;
+  const bool sel_lds = cnt <= kFuseSelLds;
+  for (int x = tid; x < n_dt + cnt; x += 256) {
+    const bool dn = x < n_dt;
+    const int u = dn ? x : x - n_dt;
     float a = 0.0f;
-    if (u < nU && ub[u] == blk) {
 #pragma unroll
-      for (int gg = 0; gg < G; ++gg) {
-        const float L = lse_sh[gg];
-        const float lm = sc.lmass[((size_t)seq * dm.Hq + qh0 + gg) * dm.u_cap + u];
-        if (L != -INFINITY && lm != -INFINITY) a += expf(lm - L);
-      }
-      a *= 1.0f / (float)G;
+    for (int gg = 0; gg < G; ++gg) {
+      const size_t row = (size_t)seq * c.dm.Hq + qh0 + gg;
+      const float lm = dn ? ld_dev(&c.sc.lm_dense[row * c.dm.ndt_cap + u])
+                          : ld_dev(&c.sc.lm_sel[row * c.dm.kcap + u]);
+      const float L = sm.lse[gg];
+      a += (L == -INFINITY || lm == -INFINITY) ? 0.0f : expf(lm - L);
     }
-    mw[blk] = fmaf(r, mw[blk], (1.0f - r) * a);
+    a *= 1.0f / (float)G;
+    if (dn) {
+      sm.adense[u] = a;
+    } else if (sel_lds) {
+      sm.asel[u] = a;
+      sm.sel[u] = ld_dev(&gsel[u]);
+    }
+  }
+  __syncthreads();
+  const int n = g.n_blk;
+  float *mw = c.L.maw + hi.maw_off + (size_t)seq * hi.nbmax;
+  const float r = c.dm.maw_decay;
+  for (int blk = tid; blk < n; blk += 256) {
+    const float old = mw[blk];
+    float a = 0.0f;
+    if (blk < g.hb) a += sm.adense[blk];
+    else if (blk >= g.tb) a += sm.adense[g.hb + (blk - g.tb)];
+    if (sel_lds) {
+      const int j = lower_bound(sm.sel, cnt, blk);
+      if (j < cnt && sm.sel[j] == blk) a += sm.asel[j];
+    } else {
+      // very large selections: search the global copy and recompute the mass
+      int lo = 0, hi2 = cnt;  // binary search over the published selection
+      while (lo < hi2) {
+        const int mid = (lo + hi2) >> 1;
+        if (ld_dev(&gsel[mid]) < blk) lo = mid + 1; else hi2 = mid;
+      }
+      const int j = lo;
+      if (j < cnt && ld_dev(&gsel[j]) == blk) {
+        float aa = 0.0f;
+        for (int gg = 0; gg < G; ++gg) {
+          const float lm = ld_dev(&c.sc.lm_sel[((size_t)seq * c.dm.Hq + qh0 + gg) * c.dm.kcap + j]);
+          const float L = sm.lse[gg];
+          aa += (L == -INFINITY || lm == -INFINITY) ? 0.0f : expf(lm - L);
+        }
+        a += aa * (1.0f / (float)G);
+      }
+    }
+    mw[blk] = fmaf(r, old, (1.0f - r) * a);
+  }
+}
+
+// ---------------------------------------------------------------------------
+// kernels
+
+// append: K/V scatter and summary roles by workgroup index.
+template <int D>
+__global__ __launch_bounds__(256) void k_prep(Ctx c, AppendBatch b, int tok_per_wg,
+                                              int n_scatter_x, int n_summ_x,
+                                              const uint16_t *__restrict__ k_new,
+                                              const uint16_t *__restrict__ v_new) {
+  int wg = blockIdx.x;
+  const int n_scatter = n_scatter_x * b.n;
+  const int n_summ = n_summ_x * c.dm.Hkv * b.n;
+  if (wg < n_scatter) {
+    append_scatter<D>(c, b, wg / n_scatter_x, wg % n_scatter_x, tok_per_wg, k_new, v_new);
+    return;
+  }
+  wg -= n_scatter;
+  if (wg < n_summ) {
+    const int x = wg % n_summ_x, hh = (wg / n_summ_x) % c.dm.Hkv, i = wg / (n_summ_x * c.dm.Hkv);
+    append_summ<D>(c, b, i, hh, x * 256 + threadIdx.x, k_new);
+    return;
+  }
+}
+
+// select (+ dense chunks): score tiles with a last-arriver top-k per unit;
+// dense attention chunks, which do not depend on the selection, share the
+// launch.
+template <int D, int G>
+__global__ __launch_bounds__(256) void k_select(Ctx c, SeqBatch b, int tiles_x,
+                                                int dchunks_x,
+                                                int32_t *__restrict__ blk_idx,
+                                                int32_t *__restrict__ blk_cnt, int k_cap,
+                                                const uint16_t *__restrict__ q,
+                                                float *__restrict__ o_part,
+                                                float *__restrict__ lse_part, int p_cap) {
+  constexpr size_t kBytes = sizeof(TopkSmem) > sizeof(AttSmem<D, G>) ? sizeof(TopkSmem)
+                                                                      : sizeof(AttSmem<D, G>);
+  __shared__ __align__(16) unsigned char smem_raw[kBytes];
+  TopkSmem &smem_topk = *reinterpret_cast<TopkSmem *>(smem_raw);
+  AttSmem<D, G> &smem_att = *reinterpret_cast<AttSmem<D, G> *>(smem_raw);
+  int wg = blockIdx.x;
+  const int n_score = tiles_x * c.dm.Hkv * b.n;
+  if (wg < n_score) {
+    const int tile = wg % tiles_x, h = (wg / tiles_x) % c.dm.Hkv, i = wg / (tiles_x * c.dm.Hkv);
+    const HeadInfo hi = c.heads[h];
+    const int seq = b.seq[i];
+    const UG g = unit_geom(b.len[i], hi, c.dm);
+    const int n_tiles = max(1, cdiv(g.n_blk, kScoreTile));
+    if (tile >= n_tiles) return;
+    score_tile<D, G>(c, i, seq, h, hi, g, tile, q, smem_topk.red);
+    // the last tile of the unit to arrive runs its top-k
+    uint32_t *ctr = &c.sc.arrive[((size_t)seq * c.dm.Hkv + h) * 2];
+    if (!arrive_last(ctr, (unsigned)n_tiles, &smem_topk.last)) return;
+    topk_unit<D, G>(c, i, seq, h, hi, g, q, blk_idx, blk_cnt, k_cap, smem_topk);
+    if (threadIdx.x == 0) st_dev(ctr, 0u);
+    return;
+  }
+  wg -= n_score;
+  const int ch = wg % dchunks_x, h = (wg / dchunks_x) % c.dm.Hkv, i = wg / (dchunks_x * c.dm.Hkv);
+  if (i >= b.n) return;
+  const HeadInfo hi = c.heads[h];
+  const UG g = unit_geom(b.len[i], hi, c.dm);
+  if (ch >= cdiv(g.n_dt, g.CB)) return;
+  attend_chunk<D, G>(c, i, b.seq[i], h, hi, g, true, ch, 0, nullptr, q, o_part, lse_part,
+                     p_cap, smem_att);
+}
+
+// attend, separate-call form: one workgroup per partial slot of each unit
+// (dense chunks at [0, pd), selected chunks after), unused slots emptied.
+template <int D, int G>
+__global__ __launch_bounds__(256) void k_attend_slots(Ctx c, SeqBatch b,
+                                                      const uint16_t *__restrict__ q,
+                                                      const int32_t *__restrict__ blk_idx,
+                                                      const int32_t *__restrict__ blk_cnt,
+                                                      int k_cap, float *__restrict__ o_part,
+                                                      float *__restrict__ lse_part, int p_cap) {
+  __shared__ AttSmem<D, G> sm;
+  const int slot = blockIdx.x, h = blockIdx.y, i = blockIdx.z;
+  const HeadInfo hi = c.heads[h];
+  const int seq = b.seq[i];
+  const UG g = unit_geom(b.len[i], hi, c.dm);
+  const int cnt = min(min(max(blk_cnt[(size_t)i * c.dm.Hkv + h], 0), k_cap), hi.kcap);
+  if (slot == 0 && threadIdx.x == 0) st_dev(&c.sc.ucnt[(size_t)seq * c.dm.Hkv + h], cnt);
+  const int32_t *sel = blk_idx + ((size_t)i * c.dm.Hkv + h) * k_cap;
+  if (slot < hi.pd) {
+    attend_chunk<D, G>(c, i, seq, h, hi, g, true, slot, cnt, sel, q, o_part, lse_part, p_cap, sm);
+  } else {
+    const int ch = slot - hi.pd;
+    // chunks past the selection write an empty slot
+    attend_chunk<D, G>(c, i, seq, h, hi, g, false, ch, cnt, sel, q, o_part, lse_part, p_cap, sm);
+  }
+}
+
+// attend, fused form: selected chunks; the last workgroup of each unit fuses
+// the unit's partials (dense ones from the select launch) and updates MAW.
+template <int D, int G>
+__global__ __launch_bounds__(256) void k_attend_fuse(Ctx c, SeqBatch b, int chunks_x,
+                                                     const uint16_t *__restrict__ q,
+                                                     const int32_t *__restrict__ blk_idx,
+                                                     const int32_t *__restrict__ blk_cnt,
+                                                     int k_cap, float *__restrict__ o_part,
+                                                     float *__restrict__ lse_part, int p_cap,
+                                                     float *__restrict__ o,
+                                                     float *__restrict__ lse) {
+  constexpr size_t kBytes = sizeof(FuseSmem<G>) > sizeof(AttSmem<D, G>) ? sizeof(FuseSmem<G>)
+                                                                         : sizeof(AttSmem<D, G>);
+  __shared__ __align__(16) unsigned char smem_raw[kBytes];
+  FuseSmem<G> &smem_fuse = *reinterpret_cast<FuseSmem<G> *>(smem_raw);
+  AttSmem<D, G> &smem_att = *reinterpret_cast<AttSmem<D, G> *>(smem_raw);
+  const int wg = blockIdx.x;
+  const int ch = wg % chunks_x, h = (wg / chunks_x) % c.dm.Hkv, i = wg / (chunks_x * c.dm.Hkv);
+  const HeadInfo hi = c.heads[h];
+  const int seq = b.seq[i];
+  const UG g = unit_geom(b.len[i], hi, c.dm);
+  const int cnt = min(min(max(blk_cnt[(size_t)i * c.dm.Hkv + h], 0), k_cap), hi.kcap);
+  const int n_active = max(1, cdiv(cnt, g.CB));
+  if (ch >= n_active) return;
+  if (ch == 0 && threadIdx.x == 0) st_dev(&c.sc.ucnt[(size_t)seq * c.dm.Hkv + h], cnt);
+  const int32_t *sel = blk_idx + ((size_t)i * c.dm.Hkv + h) * k_cap;
+  if (ch < cdiv(cnt, g.CB))
+    attend_chunk<D, G>(c, i, seq, h, hi, g, false, ch, cnt, sel, q, o_part, lse_part, p_cap,
+                       smem_att);
+  uint32_t *ctr = &c.sc.arrive[((size_t)seq * c.dm.Hkv + h) * 2 + 1];
+  if (!arrive_last(ctr, (unsigned)n_active, &smem_fuse.last)) return;
+  fuse_unit<D, G>(c, i, seq, h, hi, g, true, false, o_part, lse_part, p_cap, o, lse, smem_fuse);
+  if (threadIdx.x == 0) st_dev(ctr, 0u);
+}
+
+template <int D, int G>
+__global__ __launch_bounds__(256) void k_fuse(Ctx c, SeqBatch b, int with_maw,
+                                              const float *__restrict__ o_part,
+                                              const float *__restrict__ lse_part, int p_cap,
+                                              float *__restrict__ o, float *__restrict__ lse) {
+  __shared__ FuseSmem<G> sm;
+  const int h = blockIdx.x, i = blockIdx.y;
+  const HeadInfo hi = c.heads[h];
+  if (with_maw) {
+    const UG g = unit_geom(b.len[i], hi, c.dm);
+    fuse_unit<D, G>(c, i, b.seq[i], h, hi, g, true, false, o_part, lse_part, p_cap, o, lse, sm);
+  } else {
+    UG g{};
+    fuse_unit<D, G>(c, i, 0, h, hi, g, false, true, o_part, lse_part, p_cap, o, lse, sm);
   }
 }
 
@@ -791,153 +1275,90 @@ __global__ void k_fill_f32(float *p, size_t n, float v) {
 // ---------------------------------------------------------------------------
 // launchers
 
-hipError_t launch_append(const LayerDev &L, const HeadInfo *d_heads,
-                         const Dims &dm, const AppendBatch &b, int max_new,
+#define SD_DISPATCH_G(GG_VAR, ...)                        \
+  switch (GG_VAR) {                                       \
+    case 1: { constexpr int G_ = 1; __VA_ARGS__; } break; \
+    case 2: { constexpr int G_ = 2; __VA_ARGS__; } break; \
+    case 3: { constexpr int G_ = 3; __VA_ARGS__; } break; \
+    case 4: { constexpr int G_ = 4; __VA_ARGS__; } break; \
+    case 5: { constexpr int G_ = 5; __VA_ARGS__; } break; \
+    case 6: { constexpr int G_ = 6; __VA_ARGS__; } break; \
+    case 7: { constexpr int G_ = 7; __VA_ARGS__; } break; \
+    case 8: { constexpr int G_ = 8; __VA_ARGS__; } break; \
+    default: return hipErrorInvalidValue;                 \
+  }
+
+#define SD_DISPATCH_DG(DIM, GG_VAR, ...)   \
+  if ((DIM) == 128) {                      \
+    constexpr int D_ = 128;                \
+    SD_DISPATCH_G(GG_VAR, __VA_ARGS__)     \
+  } else {                                 \
+    constexpr int D_ = 64;                 \
+    SD_DISPATCH_G(GG_VAR, __VA_ARGS__)     \
+  }
+
+hipError_t launch_append(const Ctx &c, const AppendBatch &b, int max_new,
                          int max_touch_blocks, const uint16_t *k_new,
                          const uint16_t *v_new, hipStream_t st) {
-  if (b.n <= 0 || max_new <= 0) return hipSuccess;
   const int tpw = 16;
-  dim3 g1((max_new + tpw - 1) / tpw, b.n);
-  dim3 g2((max_touch_blocks * (dm.d / 4) + 255) / 256, dm.Hkv, b.n);
-  if (dm.d == 128) {
-    hipLaunchKernelGGL(k_append_kv<128>, g1, dim3(256), 0, st, L.k, L.v, L.pt, b,
-                       dm.Hkv, dm.pages_per_seq, tpw, k_new, v_new);
-    hipLaunchKernelGGL(k_append_summ<128>, g2, dim3(256), 0, st, L.summ, d_heads,
-                       b, dm.Hkv, k_new);
+  const int n_scatter_x = max_new > 0 ? (max_new + tpw - 1) / tpw : 0;
+  const int n_summ_x = max_new > 0 ? (max_touch_blocks * (c.dm.d / 4) + 255) / 256 : 0;
+  const int grid = n_scatter_x * b.n + n_summ_x * c.dm.Hkv * b.n;
+  if (grid == 0) return hipSuccess;
+  if (c.dm.d == 128)
+    hipLaunchKernelGGL(k_prep<128>, dim3(grid), dim3(256), 0, st, c, b, tpw, n_scatter_x,
+                       n_summ_x, k_new, v_new);
+  else
+    hipLaunchKernelGGL(k_prep<64>, dim3(grid), dim3(256), 0, st, c, b, tpw, n_scatter_x,
+                       n_summ_x, k_new, v_new);
+  return hipGetLastError();
+}
+
+hipError_t launch_select(const Ctx &c, const SeqBatch &b, int max_blocks,
+                         const uint16_t *q, int32_t *blk_idx, int32_t *blk_cnt,
+                         int32_t k_cap, int dchunks_x, float *dense_o_part,
+                         float *dense_lse_part, int32_t p_cap, hipStream_t st) {
+  if (b.n <= 0) return hipSuccess;
+  const int tiles_x = max(1, (max_blocks + kScoreTile - 1) / kScoreTile);
+  if (!dense_o_part) dchunks_x = 0;
+  const int grid = tiles_x * c.dm.Hkv * b.n + dchunks_x * c.dm.Hkv * b.n;
+  SD_DISPATCH_DG(c.dm.d, c.dm.G,
+                 hipLaunchKernelGGL((k_select<D_, G_>), dim3(grid), dim3(256), 0, st, c, b,
+                                    tiles_x, max(dchunks_x, 1), blk_idx, blk_cnt, k_cap, q,
+                                    dense_o_part, dense_lse_part, p_cap));
+  return hipGetLastError();
+}
+
+hipError_t launch_attend(const Ctx &c, const SeqBatch &b, const uint16_t *q,
+                         const int32_t *blk_idx, const int32_t *blk_cnt,
+                         int32_t k_cap, float *o_part, float *lse_part,
+                         int32_t p_cap, bool fused, int max_sel_chunks, float *o,
+                         float *lse, hipStream_t st) {
+  if (b.n <= 0) return hipSuccess;
+  if (!fused) {
+    dim3 grid(p_cap, c.dm.Hkv, b.n);
+    SD_DISPATCH_DG(c.dm.d, c.dm.G,
+                   hipLaunchKernelGGL((k_attend_slots<D_, G_>), grid, dim3(256), 0, st, c, b,
+                                      q, blk_idx, blk_cnt, k_cap, o_part, lse_part, p_cap));
   } else {
-    hipLaunchKernelGGL(k_append_kv<64>, g1, dim3(256), 0, st, L.k, L.v, L.pt, b,
-                       dm.Hkv, dm.pages_per_seq, tpw, k_new, v_new);
-    hipLaunchKernelGGL(k_append_summ<64>, g2, dim3(256), 0, st, L.summ, d_heads,
-                       b, dm.Hkv, k_new);
+    const int chunks_x = max(1, max_sel_chunks);
+    const int grid = chunks_x * c.dm.Hkv * b.n;
+    SD_DISPATCH_DG(c.dm.d, c.dm.G,
+                   hipLaunchKernelGGL((k_attend_fuse<D_, G_>), dim3(grid), dim3(256), 0, st,
+                                      c, b, chunks_x, q, blk_idx, blk_cnt, k_cap, o_part,
+                                      lse_part, p_cap, o, lse));
   }
   return hipGetLastError();
 }
 
-template <int D, int G>
-static void launch_score_t(dim3 grid, const LayerDev &L, const HeadInfo *d_heads,
-                           const SeqBatch &b, const Dims &dm, const Scratch &sc,
-                           hipStream_t st) {
-  hipLaunchKernelGGL((k_score<D, G>), grid, dim3(64), 0, st, L.summ, L.maw,
-                     d_heads, b, dm, sc.qpm, sc.keys, sc.flags);
-}
-
-template <int D>
-static hipError_t launch_score_d(dim3 grid, const LayerDev &L,
-                                 const HeadInfo *d_heads, const SeqBatch &b,
-                                 const Dims &dm, const Scratch &sc,
-                                 hipStream_t st) {
-  switch (dm.G) {
-    case 1: launch_score_t<D, 1>(grid, L, d_heads, b, dm, sc, st); break;
-    case 2: launch_score_t<D, 2>(grid, L, d_heads, b, dm, sc, st); break;
-    case 3: launch_score_t<D, 3>(grid, L, d_heads, b, dm, sc, st); break;
-    case 4: launch_score_t<D, 4>(grid, L, d_heads, b, dm, sc, st); break;
-    case 5: launch_score_t<D, 5>(grid, L, d_heads, b, dm, sc, st); break;
-    case 6: launch_score_t<D, 6>(grid, L, d_heads, b, dm, sc, st); break;
-    case 7: launch_score_t<D, 7>(grid, L, d_heads, b, dm, sc, st); break;
-    case 8: launch_score_t<D, 8>(grid, L, d_heads, b, dm, sc, st); break;
-    default: return hipErrorInvalidValue;
-  }
-  return hipSuccess;
-}
-
-hipError_t launch_select(const LayerDev &L, const HeadInfo *d_heads,
-                         const Dims &dm, const Scratch &sc, const SeqBatch &b,
-                         int max_blocks, const uint16_t *q, int32_t *blk_idx,
-                         int32_t *blk_cnt, int32_t k_cap, hipStream_t st) {
+hipError_t launch_fuse(const Ctx &c, const SeqBatch &b, bool with_maw,
+                       const float *o_part, const float *lse_part, int32_t p_cap,
+                       float *o, float *lse, hipStream_t st) {
   if (b.n <= 0) return hipSuccess;
-  const int nq = b.n * dm.Hq * dm.d;
-  hipLaunchKernelGGL(k_qprep, dim3((nq + 255) / 256), dim3(256), 0, st, q,
-                     sc.qpm, nq);
-  dim3 grid((max(max_blocks, 1) + 63) / 64, dm.Hkv, b.n);
-  hipError_t e = dm.d == 128 ? launch_score_d<128>(grid, L, d_heads, b, dm, sc, st)
-                             : launch_score_d<64>(grid, L, d_heads, b, dm, sc, st);
-  if (e != hipSuccess) return e;
-  hipLaunchKernelGGL(k_topk, dim3(dm.Hkv, b.n), dim3(256), 0, st, d_heads, b, dm,
-                     sc.keys, sc.flags, blk_idx, blk_cnt, k_cap);
-  return hipGetLastError();
-}
-
-template <int D, int G>
-static void launch_attend_t(const LayerDev &L, const HeadInfo *d_heads,
-                            const Dims &dm, const Scratch &sc,
-                            const SeqBatch &b, const uint16_t *q,
-                            const int32_t *blk_idx, const int32_t *blk_cnt,
-                            int32_t k_cap, float *o_part, float *lse_part,
-                            int32_t p_cap, hipStream_t st) {
-  hipLaunchKernelGGL((k_attend<D, G>), dim3(p_cap, dm.Hkv, b.n), dim3(256), 0, st,
-                     L, d_heads, b, dm, sc, q, blk_idx, blk_cnt, k_cap, o_part,
-                     lse_part, p_cap);
-}
-
-template <int D>
-static hipError_t launch_attend_d(const LayerDev &L, const HeadInfo *d_heads,
-                                  const Dims &dm, const Scratch &sc,
-                                  const SeqBatch &b, const uint16_t *q,
-                                  const int32_t *blk_idx, const int32_t *blk_cnt,
-                                  int32_t k_cap, float *o_part, float *lse_part,
-                                  int32_t p_cap, hipStream_t st) {
-#define SD_ATT(GG)                                                            \
-  case GG:                                                                    \
-    launch_attend_t<D, GG>(L, d_heads, dm, sc, b, q, blk_idx, blk_cnt, k_cap, \
-                           o_part, lse_part, p_cap, st);                      \
-    break;
-  switch (dm.G) {
-    SD_ATT(1) SD_ATT(2) SD_ATT(3) SD_ATT(4) SD_ATT(5) SD_ATT(6) SD_ATT(7) SD_ATT(8)
-    default: return hipErrorInvalidValue;
-  }
-#undef SD_ATT
-  return hipSuccess;
-}
-
-hipError_t launch_attend(const LayerDev &L, const HeadInfo *d_heads,
-                         const Dims &dm, const Scratch &sc, const SeqBatch &b,
-                         const uint16_t *q, const int32_t *blk_idx,
-                         const int32_t *blk_cnt, int32_t k_cap, float *o_part,
-                         float *lse_part, int32_t p_cap, hipStream_t st) {
-  if (b.n <= 0) return hipSuccess;
-  hipError_t e = dm.d == 128
-                     ? launch_attend_d<128>(L, d_heads, dm, sc, b, q, blk_idx, blk_cnt,
-                                            k_cap, o_part, lse_part, p_cap, st)
-                     : launch_attend_d<64>(L, d_heads, dm, sc, b, q, blk_idx, blk_cnt,
-                                           k_cap, o_part, lse_part, p_cap, st);
-  if (e != hipSuccess) return e;
-  return hipGetLastError();
-}
-
-template <int D>
-static hipError_t launch_fuse_d(const LayerDev *L, const HeadInfo *d_heads,
-                                const Dims &dm, const Scratch &sc,
-                                const SeqBatch &b, bool with_maw,
-                                const float *o_part, const float *lse_part,
-                                int32_t p_cap, float *o, float *lse,
-                                hipStream_t st) {
-  float *maw = L ? L->maw : nullptr;
-  dim3 grid(dm.Hkv, b.n);
-#define SD_FUSE(GG)                                                                 \
-  case GG:                                                                          \
-    hipLaunchKernelGGL((k_fuse<D, GG>), grid, dim3(256), 0, st, maw, d_heads, b, dm, \
-                       sc, with_maw ? 1 : 0, o_part, lse_part, p_cap, o, lse);      \
-    break;
-  switch (dm.G) {
-    SD_FUSE(1) SD_FUSE(2) SD_FUSE(3) SD_FUSE(4) SD_FUSE(5) SD_FUSE(6) SD_FUSE(7) SD_FUSE(8)
-    default: return hipErrorInvalidValue;
-  }
-#undef SD_FUSE
-  return hipSuccess;
-}
-
-hipError_t launch_fuse(const LayerDev *L, const HeadInfo *d_heads,
-                       const Dims &dm, const Scratch &sc, const SeqBatch &b,
-                       bool with_maw, const float *o_part,
-                       const float *lse_part, int32_t p_cap, float *o,
-                       float *lse, hipStream_t st) {
-  if (b.n <= 0) return hipSuccess;
-  hipError_t e = dm.d == 128
-                     ? launch_fuse_d<128>(L, d_heads, dm, sc, b, with_maw, o_part,
-                                          lse_part, p_cap, o, lse, st)
-                     : launch_fuse_d<64>(L, d_heads, dm, sc, b, with_maw, o_part,
-                                         lse_part, p_cap, o, lse, st);
-  if (e != hipSuccess) return e;
+  dim3 grid(c.dm.Hkv, b.n);
+  SD_DISPATCH_DG(c.dm.d, c.dm.G,
+                 hipLaunchKernelGGL((k_fuse<D_, G_>), grid, dim3(256), 0, st, c, b,
+                                    with_maw ? 1 : 0, o_part, lse_part, p_cap, o, lse));
   return hipGetLastError();
 }
 

@@ -40,7 +40,6 @@ struct sd_ctx {
   Scratch sc{};
   std::vector<Layer> layers;
   int32_t k_cap = 0, p_cap = 0;
-  std::vector<int32_t> kcap_h, ucap_h;
   // attend -> fuse hand-over state
   int pend_layer = -2;
   std::vector<int32_t> pend_seqs;
@@ -233,12 +232,11 @@ sd_status sparse_decode_init(const sd_config *cfg, sd_ctx **out) {
     return fail(c, SD_EHIP, "no HIP device");
 
   const int max_seqs = cfg->max_seqs;
-  // per-head geometry, capacities
+  // per-head geometry and capacities.  Partial slots of a unit: dense
+  // chunks at [0, pd), selected chunks at [pd, pd + ceil(kcap / CB)).
   c->heads.resize(c->Hkv);
-  c->kcap_h.resize(c->Hkv);
-  c->ucap_h.resize(c->Hkv);
   int64_t summ_elems = 0, maw_elems = 0;
-  int key_stride = 1;
+  int key_stride = 1, ndt_cap = 1;
   for (int h = 0; h < c->Hkv; ++h) {
     HeadInfo &hi = c->heads[h];
     hi.S = c->S[h];
@@ -250,18 +248,22 @@ sd_status sparse_decode_init(const sd_config *cfg, sd_ctx **out) {
     summ_elems += (int64_t)max_seqs * (c->D / 4) * hi.nbmax * 8;
     maw_elems += (int64_t)max_seqs * hi.nbmax;
     key_stride = std::max(key_stride, hi.nbmax);
-    int64_t kc = 0;
-    for (int64_t N : {(int64_t)cfg->max_seq_len})
-      kc = std::max<int64_t>(kc, cdiv((int64_t)hi.ppm * N, 1000000LL * hi.S));
-    kc = std::min<int64_t>(kc, hi.nbmax);
-    c->kcap_h[h] = (int)std::max<int64_t>(kc, 1);
-    int64_t uc = cdiv(cfg->sink_tokens, hi.S) + kc + cdiv(cfg->recent_window, hi.S) + 1;
-    c->ucap_h[h] = (int)std::min<int64_t>(uc, hi.nbmax);
-    c->k_cap = std::max(c->k_cap, c->kcap_h[h]);
-    c->p_cap = std::max<int32_t>(c->p_cap, (int32_t)cdiv(c->ucap_h[h], hi.chunk_blocks));
+    // k grows with N: its largest value is at max_seq_len
+    int64_t kc = std::min<int64_t>(cdiv((int64_t)hi.ppm * cfg->max_seq_len, 1000000LL * hi.S),
+                                   hi.nbmax);
+    hi.kcap = (int)std::max<int64_t>(kc, 1);
+    int64_t ndt = std::min<int64_t>(cdiv(cfg->sink_tokens, hi.S) +
+                                        cdiv(cfg->recent_window, hi.S) + 1, hi.nbmax);
+    ndt_cap = std::max<int>(ndt_cap, (int)ndt);
+    hi.pd = (int)cdiv(ndt, hi.chunk_blocks);
+    c->k_cap = std::max(c->k_cap, hi.kcap);
+    c->p_cap = std::max<int32_t>(c->p_cap, hi.pd + (int32_t)cdiv(hi.kcap, hi.chunk_blocks));
   }
-  int u_cap = *std::max_element(c->ucap_h.begin(), c->ucap_h.end());
 
+  if (c->p_cap > kFuseSlots)
+    return fail(c, SD_EUNSUPPORTED,
+                "%d partial slots per head exceed the fusion limit %d (lower the budget "
+                "or max_seq_len, or raise the block size)", c->p_cap, kFuseSlots);
   sd_status s;
   if ((s = dev_alloc(c, &c->d_heads, c->Hkv)) != SD_OK) return s;
   SD_HIP(c, hipMemcpy(c->d_heads, c->heads.data(), sizeof(HeadInfo) * c->Hkv,
@@ -280,16 +282,23 @@ sd_status sparse_decode_init(const sd_config *cfg, sd_ctx **out) {
   c->dims.maw_decay = cfg->maw_decay > 0.0f ? cfg->maw_decay : 0.95f;
   c->dims.maw_beta = cfg->maw_beta;
   c->dims.key_stride = key_stride;
-  c->dims.u_cap = u_cap;
+  c->dims.ndt_cap = ndt_cap;
+  c->dims.kcap = c->k_cap;
 
   // scratch
-  if ((s = dev_alloc(c, &c->sc.qpm, (size_t)kLaunchSeqs * c->Hq * c->D)) != SD_OK) return s;
   if ((s = dev_alloc(c, &c->sc.keys, (size_t)max_seqs * c->Hkv * key_stride)) != SD_OK) return s;
+  if ((s = dev_alloc(c, &c->sc.keyflag, (size_t)max_seqs * c->Hkv * key_stride)) != SD_OK) return s;
   if ((s = dev_alloc(c, &c->sc.flags, (size_t)max_seqs * c->Hkv * key_stride)) != SD_OK) return s;
-  if ((s = dev_alloc(c, &c->sc.lmass, (size_t)max_seqs * c->Hq * u_cap)) != SD_OK) return s;
-  if ((s = dev_alloc(c, &c->sc.ublk, (size_t)max_seqs * c->Hkv * u_cap)) != SD_OK) return s;
+  if ((s = dev_alloc(c, &c->sc.ulist, (size_t)max_seqs * c->Hkv * key_stride)) != SD_OK) return s;
+  if ((s = dev_alloc(c, &c->sc.eps_max, (size_t)max_seqs * c->Hkv)) != SD_OK) return s;
+  SD_HIP(c, hipMemset(c->sc.eps_max, 0, sizeof(uint32_t) * max_seqs * c->Hkv));
+  if ((s = dev_alloc(c, &c->sc.lm_dense, (size_t)max_seqs * c->Hq * ndt_cap)) != SD_OK) return s;
+  if ((s = dev_alloc(c, &c->sc.lm_sel, (size_t)max_seqs * c->Hq * c->k_cap)) != SD_OK) return s;
+  if ((s = dev_alloc(c, &c->sc.usel, (size_t)max_seqs * c->Hkv * c->k_cap)) != SD_OK) return s;
   if ((s = dev_alloc(c, &c->sc.ucnt, (size_t)max_seqs * c->Hkv)) != SD_OK) return s;
+  if ((s = dev_alloc(c, &c->sc.arrive, (size_t)max_seqs * c->Hkv * 2)) != SD_OK) return s;
   SD_HIP(c, hipMemset(c->sc.ucnt, 0, sizeof(int32_t) * max_seqs * c->Hkv));
+  SD_HIP(c, hipMemset(c->sc.arrive, 0, sizeof(uint32_t) * max_seqs * c->Hkv * 2));
   SD_HIP(c, hipMemset(c->sc.flags, 0, (size_t)max_seqs * c->Hkv * key_stride));
 
   // layers
@@ -361,13 +370,21 @@ sd_status sd_seq_len(const sd_ctx *c, int32_t layer, int32_t seq, int32_t *len) 
   return SD_OK;
 }
 
-sd_status append_kv(sd_ctx *c, int32_t layer, int32_t n_seqs,
-                    const int32_t *seq_ids, const int32_t *n_new,
-                    const void *k_bf16, const void *v_bf16) {
-  if (!c) return SD_EINVAL;
-  sd_status s = check_seqs(c, layer, n_seqs, seq_ids);
-  if (s != SD_OK) return s;
-  if (n_seqs > 0 && !n_new) return fail(c, SD_EINVAL, "n_new is NULL");
+namespace {
+
+Ctx kctx(const sd_ctx *c, int layer) {
+  Ctx k{};
+  if (layer >= 0) k.L = c->layers[layer].dev;
+  k.heads = c->d_heads;
+  k.dm = c->dims;
+  k.sc = c->sc;
+  return k;
+}
+
+// Host-side append: validate, take pages, push the touched page-table span,
+// launch the append kernel (optionally carrying the q split for the step).
+sd_status do_append(sd_ctx *c, int32_t layer, int32_t n_seqs, const int32_t *seq_ids,
+                    const int32_t *n_new, const void *k_bf16, const void *v_bf16) {
   Layer &L = c->layers[layer];
   int64_t total = 0, pages_needed = 0;
   for (int i = 0; i < n_seqs; ++i) {
@@ -379,12 +396,10 @@ sd_status append_kv(sd_ctx *c, int32_t layer, int32_t n_seqs,
     total += n_new[i];
     pages_needed += cdiv(nl, kPage) - cdiv(L.len[seq_ids[i]], kPage);
   }
-  if (total == 0) return SD_OK;
-  if (!k_bf16 || !v_bf16) return fail(c, SD_EINVAL, "k/v pointers are NULL");
+  if (total > 0 && (!k_bf16 || !v_bf16)) return fail(c, SD_EINVAL, "k/v pointers are NULL");
   if (pages_needed > (int64_t)L.free_pages.size())
     return fail(c, SD_ENOMEM, "page pool of layer %d exhausted: need %lld pages, %zu free",
                 layer, (long long)pages_needed, L.free_pages.size());
-  // allocate pages (host mirror), then push the touched span to the device
   int64_t lo = INT64_MAX, hi = -1;
   for (int i = 0; i < n_seqs; ++i) {
     int seq = seq_ids[i];
@@ -399,6 +414,7 @@ sd_status append_kv(sd_ctx *c, int32_t layer, int32_t n_seqs,
   if (hi >= 0)
     SD_HIP(c, hipMemcpyAsync(L.dev.pt + lo, L.h_pt + lo, sizeof(int32_t) * (hi - lo + 1),
                              hipMemcpyHostToDevice, c->stream));
+  const Ctx kc = kctx(c, layer);
   int row = 0;
   for (int base = 0; base < n_seqs; base += kLaunchSeqs) {
     AppendBatch b{};
@@ -419,12 +435,39 @@ sd_status append_kv(sd_ctx *c, int32_t layer, int32_t n_seqs,
           max_touch = std::max(max_touch, t);
         }
     }
-    SD_HIP(c, launch_append(L.dev, c->d_heads, c->dims, b, max_new, max_touch,
-                            static_cast<const uint16_t *>(k_bf16),
+    SD_HIP(c, launch_append(kc, b, max_new, max_touch, static_cast<const uint16_t *>(k_bf16),
                             static_cast<const uint16_t *>(v_bf16), c->stream));
   }
   for (int i = 0; i < n_seqs; ++i) L.len[seq_ids[i]] += n_new[i];
   return SD_OK;
+}
+
+int64_t k_of_seq(const sd_ctx *c, int64_t N, int h) {
+  return k_of(N, c->S[h], c->ppm[h], c->cfg.sink_tokens, c->cfg.recent_window);
+}
+
+sd_status check_kcap(sd_ctx *c, int layer, int n_seqs, const int32_t *seq_ids, int32_t k_cap) {
+  const Layer &L = c->layers[layer];
+  for (int i = 0; i < n_seqs; ++i)
+    for (int h = 0; h < c->Hkv; ++h) {
+      int64_t k = k_of_seq(c, L.len[seq_ids[i]], h);
+      if (k > k_cap)
+        return fail(c, SD_EINVAL, "k_cap %d < %lld blocks needed (seq %d, kv head %d)",
+                    k_cap, (long long)k, seq_ids[i], h);
+    }
+  return SD_OK;
+}
+
+}  // namespace
+
+sd_status append_kv(sd_ctx *c, int32_t layer, int32_t n_seqs,
+                    const int32_t *seq_ids, const int32_t *n_new,
+                    const void *k_bf16, const void *v_bf16) {
+  if (!c) return SD_EINVAL;
+  sd_status s = check_seqs(c, layer, n_seqs, seq_ids);
+  if (s != SD_OK) return s;
+  if (n_seqs > 0 && !n_new) return fail(c, SD_EINVAL, "n_new is NULL");
+  return do_append(c, layer, n_seqs, seq_ids, n_new, k_bf16, v_bf16);
 }
 
 sd_status select_topk(sd_ctx *c, int32_t layer, int32_t n_seqs,
@@ -436,24 +479,17 @@ sd_status select_topk(sd_ctx *c, int32_t layer, int32_t n_seqs,
   if (n_seqs == 0) return SD_OK;
   if (!q_bf16 || !blk_idx || !blk_cnt)
     return fail(c, SD_EINVAL, "q / blk_idx / blk_cnt pointer is NULL");
-  const Layer &L = c->layers[layer];
-  for (int i = 0; i < n_seqs; ++i)
-    for (int h = 0; h < c->Hkv; ++h) {
-      int64_t k = k_of(L.len[seq_ids[i]], c->S[h], c->ppm[h], c->cfg.sink_tokens,
-                       c->cfg.recent_window);
-      if (k > k_cap)
-        return fail(c, SD_EINVAL, "k_cap %d < %lld blocks needed (seq %d, kv head %d)",
-                    k_cap, (long long)k, seq_ids[i], h);
-    }
+  if ((s = check_kcap(c, layer, n_seqs, seq_ids, k_cap)) != SD_OK) return s;
+  const Ctx kc = kctx(c, layer);
   const uint16_t *q = static_cast<const uint16_t *>(q_bf16);
   for (int base = 0; base < n_seqs; base += kLaunchSeqs) {
     SeqBatch b;
     int mb = 0;
     fill_batch(c, layer, seq_ids, base, std::min(kLaunchSeqs, n_seqs - base), &b, &mb);
-    SD_HIP(c, launch_select(L.dev, c->d_heads, c->dims, c->sc, b, mb,
-                            q + (size_t)base * c->Hq * c->D,
-                            blk_idx + (size_t)base * c->Hkv * k_cap,
-                            blk_cnt + (size_t)base * c->Hkv, k_cap, c->stream));
+    const uint16_t *qb = q + (size_t)base * c->Hq * c->D;
+    SD_HIP(c, launch_select(kc, b, mb, qb, blk_idx + (size_t)base * c->Hkv * k_cap,
+                            blk_cnt + (size_t)base * c->Hkv, k_cap, 0, nullptr, nullptr, 0,
+                            c->stream));
   }
   return SD_OK;
 }
@@ -470,30 +506,19 @@ sd_status sparse_attend(sd_ctx *c, int32_t layer, int32_t n_seqs,
   if (!q_bf16 || !blk_idx || !blk_cnt || !o_part || !lse_part)
     return fail(c, SD_EINVAL, "a device pointer is NULL");
   if (k_cap < 1) return fail(c, SD_EINVAL, "k_cap %d < 1", k_cap);
-  const Layer &L = c->layers[layer];
-  // every attended block must fit in p_cap chunks
-  for (int i = 0; i < n_seqs; ++i)
-    for (int h = 0; h < c->Hkv; ++h) {
-      int64_t N = L.len[seq_ids[i]];
-      int S = c->S[h];
-      int64_t k = std::min<int64_t>(k_cap, c->kcap_h[h]);
-      int64_t u = std::min<int64_t>(cdiv(N, S), cdiv(c->cfg.sink_tokens, S) + k +
-                                                    cdiv(c->cfg.recent_window, S) + 1);
-      int64_t need = cdiv(u, kChunkTokens / S);
-      if (need > p_cap)
-        return fail(c, SD_EINVAL, "p_cap %d < %lld partials needed (seq %d, kv head %d)",
-                    p_cap, (long long)need, seq_ids[i], h);
-    }
+  if (p_cap < c->p_cap)
+    return fail(c, SD_EINVAL, "p_cap %d < %d partial slots per head (sd_caps)", p_cap, c->p_cap);
+  const Ctx kc = kctx(c, layer);
   const uint16_t *q = static_cast<const uint16_t *>(q_bf16);
   for (int base = 0; base < n_seqs; base += kLaunchSeqs) {
     SeqBatch b;
     fill_batch(c, layer, seq_ids, base, std::min(kLaunchSeqs, n_seqs - base), &b, nullptr);
-    SD_HIP(c, launch_attend(L.dev, c->d_heads, c->dims, c->sc, b,
-                            q + (size_t)base * c->Hq * c->D,
+    SD_HIP(c, launch_attend(kc, b, q + (size_t)base * c->Hq * c->D,
                             blk_idx + (size_t)base * c->Hkv * k_cap,
                             blk_cnt + (size_t)base * c->Hkv, k_cap,
                             o_part + (size_t)base * c->Hq * p_cap * c->D,
-                            lse_part + (size_t)base * c->Hq * p_cap, p_cap, c->stream));
+                            lse_part + (size_t)base * c->Hq * p_cap, p_cap, false, 0, nullptr,
+                            nullptr, c->stream));
   }
   c->pend_layer = layer;
   c->pend_seqs.assign(seq_ids, seq_ids + n_seqs);
@@ -515,12 +540,13 @@ sd_status fuse_lse(sd_ctx *c, int32_t layer, int32_t n_seqs,
   if (with_maw) {
     sd_status s = check_seqs(c, layer, n_seqs, seq_ids);
     if (s != SD_OK) return s;
-    if (c->pend_layer != layer ||
+    if (c->pend_layer != layer || c->pend_pcap != p_cap ||
         c->pend_seqs != std::vector<int32_t>(seq_ids, seq_ids + n_seqs))
       return fail(c, SD_ESTATE,
-                  "fuse_lse(layer %d) does not follow sparse_attend of the same layer "
-                  "and sequences", layer);
+                  "fuse_lse(layer %d) does not follow sparse_attend of the same layer, "
+                  "sequences and p_cap", layer);
   }
+  const Ctx kc = kctx(c, with_maw ? layer : -1);
   for (int base = 0; base < n_seqs; base += kLaunchSeqs) {
     SeqBatch b;
     const int n = std::min(kLaunchSeqs, n_seqs - base);
@@ -530,28 +556,76 @@ sd_status fuse_lse(sd_ctx *c, int32_t layer, int32_t n_seqs,
       b.n = n;
       for (int i = 0; i < n; ++i) b.seq[i] = b.len[i] = 0;
     }
-    SD_HIP(c, launch_fuse(with_maw ? &c->layers[layer].dev : nullptr, c->d_heads,
-                          c->dims, c->sc, b, with_maw,
-                          o_part + (size_t)base * c->Hq * p_cap * c->D,
+    SD_HIP(c, launch_fuse(kc, b, with_maw, o_part + (size_t)base * c->Hq * p_cap * c->D,
                           lse_part + (size_t)base * c->Hq * p_cap, p_cap,
-                          o + (size_t)base * c->Hq * c->D,
-                          lse + (size_t)base * c->Hq, c->stream));
+                          o + (size_t)base * c->Hq * c->D, lse + (size_t)base * c->Hq,
+                          c->stream));
   }
   if (with_maw) c->pend_layer = -2;
   return SD_OK;
 }
 
 sd_status sparse_decode_step(sd_ctx *c, int32_t layer, int32_t n_seqs,
-                             const int32_t *seq_ids, const void *q_bf16,
-                             int32_t *blk_idx, int32_t *blk_cnt, int32_t k_cap,
-                             float *o_part, float *lse_part, int32_t p_cap,
-                             float *o, float *lse) {
-  sd_status s = select_topk(c, layer, n_seqs, seq_ids, q_bf16, blk_idx, blk_cnt, k_cap);
+                             const int32_t *seq_ids, const void *k_new,
+                             const void *v_new, const void *q_bf16, int32_t *blk_idx,
+                             int32_t *blk_cnt, int32_t k_cap, float *o_part,
+                             float *lse_part, int32_t p_cap, float *o, float *lse) {
+  if (!c) return SD_EINVAL;
+  sd_status s = check_seqs(c, layer, n_seqs, seq_ids);
   if (s != SD_OK) return s;
-  s = sparse_attend(c, layer, n_seqs, seq_ids, q_bf16, blk_idx, blk_cnt, k_cap, o_part,
-                    lse_part, p_cap);
-  if (s != SD_OK) return s;
-  return fuse_lse(c, layer, n_seqs, seq_ids, o_part, lse_part, p_cap, o, lse);
+  if (n_seqs == 0) return SD_OK;
+  if (!q_bf16 || !blk_idx || !blk_cnt || !o_part || !lse_part || !o || !lse)
+    return fail(c, SD_EINVAL, "a device pointer is NULL");
+  if ((k_new == nullptr) != (v_new == nullptr))
+    return fail(c, SD_EINVAL, "k_new and v_new must both be given or both be NULL");
+  if (p_cap < c->p_cap)
+    return fail(c, SD_EINVAL, "p_cap %d < %d partial slots per head (sd_caps)", p_cap, c->p_cap);
+  // k after the optional one-token append
+  {
+    const Layer &L = c->layers[layer];
+    const int add = k_new ? 1 : 0;
+    for (int i = 0; i < n_seqs; ++i) {
+      if ((int64_t)L.len[seq_ids[i]] + add > c->cfg.max_seq_len)
+        return fail(c, SD_EINVAL, "sequence %d is full", seq_ids[i]);
+      for (int h = 0; h < c->Hkv; ++h) {
+        int64_t k = k_of_seq(c, L.len[seq_ids[i]] + add, h);
+        if (k > k_cap)
+          return fail(c, SD_EINVAL, "k_cap %d < %lld blocks needed (seq %d, kv head %d)",
+                      k_cap, (long long)k, seq_ids[i], h);
+      }
+    }
+  }
+  const uint16_t *q = static_cast<const uint16_t *>(q_bf16);
+  if (k_new) {
+    std::vector<int32_t> ones(n_seqs, 1);
+    if ((s = do_append(c, layer, n_seqs, seq_ids, ones.data(), k_new, v_new)) != SD_OK)
+      return s;
+  }
+  const Ctx kc = kctx(c, layer);
+  for (int base = 0; base < n_seqs; base += kLaunchSeqs) {
+    SeqBatch b;
+    int mb = 0;
+    const int n = std::min(kLaunchSeqs, n_seqs - base);
+    fill_batch(c, layer, seq_ids, base, n, &b, &mb);
+    const uint16_t *qb = q + (size_t)base * c->Hq * c->D;
+    int dchunks = 0, schunks = 0;
+    for (int i = 0; i < n; ++i)
+      for (int h = 0; h < c->Hkv; ++h) {
+        const HeadInfo &hi = c->heads[h];
+        dchunks = std::max(dchunks, hi.pd);
+        schunks = std::max<int>(schunks, (int)cdiv(k_of_seq(c, b.len[i], h), hi.chunk_blocks));
+      }
+    int32_t *bi = blk_idx + (size_t)base * c->Hkv * k_cap;
+    int32_t *bc = blk_cnt + (size_t)base * c->Hkv;
+    float *op = o_part + (size_t)base * c->Hq * p_cap * c->D;
+    float *lp = lse_part + (size_t)base * c->Hq * p_cap;
+    SD_HIP(c, launch_select(kc, b, mb, qb, bi, bc, k_cap, dchunks, op, lp, p_cap, c->stream));
+    SD_HIP(c, launch_attend(kc, b, qb, bi, bc, k_cap, op, lp, p_cap, true, schunks,
+                            o + (size_t)base * c->Hq * c->D, lse + (size_t)base * c->Hq,
+                            c->stream));
+  }
+  c->pend_layer = -2;
+  return SD_OK;
 }
 
 sd_status sd_release_seq(sd_ctx *c, int32_t seq) {

@@ -166,11 +166,18 @@ sd_status fuse_lse(sd_ctx *ctx, int32_t layer, int32_t n_seqs,
                    const int32_t *seq_ids, const float *o_part,
                    const float *lse_part, int32_t p_cap, float *o, float *lse);
 
-/* Fused decode step: select_topk + sparse_attend + fuse_lse with identical
- * results, in fewer launches.  blk_idx/blk_cnt/o_part/lse_part are still
- * written (they are the caller's scratch and its record of the selection). */
+/* Fused decode step of one layer: the optional append of one token per
+ * sequence (k_new, v_new: dev [n_seqs][Hkv][d] bf16, both NULL to skip), then
+ * select_topk + sparse_attend + fuse_lse with bitwise identical results, in
+ * three launches: [append + query split], [block scoring with the top-k of
+ * each (sequence, KV head) done by its last scoring workgroup, alongside the
+ * dense sink/window chunks], [selected-block chunks with the LSE fusion and
+ * MAW update done by the last chunk of each (sequence, KV head)].
+ * blk_idx/blk_cnt/o_part/lse_part are written as by the separate calls, except
+ * that partial slots a unit does not use are left unspecified. */
 sd_status sparse_decode_step(sd_ctx *ctx, int32_t layer, int32_t n_seqs,
-                             const int32_t *seq_ids, const void *q_bf16,
+                             const int32_t *seq_ids, const void *k_new,
+                             const void *v_new, const void *q_bf16,
                              int32_t *blk_idx, int32_t *blk_cnt, int32_t k_cap,
                              float *o_part, float *lse_part, int32_t p_cap,
                              float *o, float *lse);

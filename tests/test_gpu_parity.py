@@ -114,6 +114,47 @@ def test_fused_step_equals_separate_calls():
         assert np.array_equal(a["gpu"][k], b["gpu"][k]), k
 
 
+def test_fused_step_with_append_equals_separate_calls():
+    """sparse_decode_step with the one-token append equals append_kv +
+    select_topk + sparse_attend + fuse_lse, over several steps (MAW on)."""
+    w = _w(synth.llama32k(), B=3, N=3000, maw_beta=1.0)
+    log("case: fused step with append")
+    x = synth.single_step(w, 6, N=3000)
+    engs = [harness.make_engine(w, 3064) for _ in range(2)]
+    try:
+        for e in engs:
+            harness.prefill(e, 0, x["K"].cuda(), x["V"].cuda())
+        seqs = [0, 1, 2]
+        for step in range(5):
+            kn, vn = synth.step_kv(w, 6, 0, step, device="cuda")
+            kn = kn.view(w.B, w.Hkv, w.d).contiguous()
+            vn = vn.view(w.B, w.Hkv, w.d).contiguous()
+            q = synth.randn((w.B, w.Hq, w.d), 6, 700 + step, "cuda")
+            a = engs[0].alloc_step(3)
+            engs[0].append_kv(0, seqs, [1, 1, 1], kn, vn)
+            engs[0].select_topk(0, seqs, q, a["blk_idx"], a["blk_cnt"])
+            engs[0].sparse_attend(0, seqs, q, a["blk_idx"], a["blk_cnt"], a["o_part"], a["lse_part"])
+            engs[0].fuse_lse(0, seqs, a["o_part"], a["lse_part"], a["o"], a["lse"])
+            b = engs[1].alloc_step(3)
+            engs[1].decode_step(0, seqs, q, b["blk_idx"], b["blk_cnt"], b["o_part"],
+                                b["lse_part"], b["o"], b["lse"], k_new=kn, v_new=vn)
+            torch.cuda.synchronize()
+            for k in ("blk_cnt", "o", "lse"):
+                assert torch.equal(a[k], b[k]), (step, k)
+            for s_ in range(3):
+                for g in range(w.Hkv):
+                    n = int(a["blk_cnt"][s_, g])
+                    assert torch.equal(a["blk_idx"][s_, g, :n], b["blk_idx"][s_, g, :n])
+        for s_ in range(3):
+            ma = engs[0].debug(harness.SD_DEBUG_MAW, 0, s_)
+            mb = engs[1].debug(harness.SD_DEBUG_MAW, 0, s_)
+            assert np.array_equal(ma, mb)
+            assert ma.max() > 0
+    finally:
+        for e in engs:
+            e.close()
+
+
 def test_many_sequences_split_launches():
     w = _w(synth.tiny(), B=80, N=700)
     log("case: 80 sequences")
@@ -127,6 +168,43 @@ def test_group_sizes(G, Hkv, d):
                        n_sink=4, window=128, plant_frac=0.02, sink_scale=4.0)
     log("case: G=%d Hkv=%d d=%d" % (G, Hkv, d))
     harness.assert_parity(harness.run_single_step(w, 13))
+
+
+def test_tied_scores_resolved_exactly():
+    """Coarse integer keys make many block scores exactly equal: every tie at
+    the k-th key goes through the exact re-scoring and the index tie-break."""
+    w = _w(synth.tiny(), N=4096, n_plant=0)
+    log("case: tied scores")
+    x = synth.single_step(w, 3, N=4096)
+    g = torch.Generator().manual_seed(3)
+    K = torch.randint(-1, 2, x["K"].shape, generator=g).to(torch.bfloat16)
+    eng = harness.make_engine(w, 4160)
+    try:
+        harness.prefill(eng, 0, K.cuda(), x["V"].cuda())
+        gpu = harness.run_gpu_step(eng, 0, [0], x["q"].cuda())
+        Kb, Vb = synth.bits(K), synth.bits(x["V"])
+        st = harness.check_units(w, eng, 0, [0], synth.bits(x["q"]), {0: Kb[0]}, {0: Vb[0]},
+                                 {0: 4096}, gpu)
+        harness.assert_parity(st)
+        assert st["ties"] == 0
+    finally:
+        eng.close()
+
+
+def test_large_block_count_global_topk():
+    """More blocks per unit than the top-k keeps in LDS (global-memory path)."""
+    w = _w(synth.tiny(), N=70001, block_size=[16], budget_ppm=[30000])
+    log("case: 4376 blocks per unit")
+    harness.assert_parity(harness.run_single_step(w, 8))
+
+
+def test_qwen128k_full_single_step():
+    """Per-KV-head block sizes (16/64) and budgets (1-20%), G=7, N=131072."""
+    w = synth.qwen128k(0)
+    log("case: qwen128k S=%s ppm=%s" % (w.block_size, w.budget_ppm))
+    st = harness.run_single_step(w, 0)
+    log("  ties=%d max|dO|=%.3g max|dlse|=%.3g" % (st["ties"], st["max_abs"], st["max_dlse"]))
+    harness.assert_parity(st)
 
 
 def test_llama32k_full():
