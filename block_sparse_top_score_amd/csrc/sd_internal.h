@@ -15,7 +15,8 @@ constexpr int kPage = SD_PAGE_SIZE;  // tokens per KV page
 constexpr int kLaunchSeqs = 64;      // sequences per kernel launch
 constexpr int kChunkTokens = 256;    // token slots of one split-K chunk
 constexpr int kScoreTile = 256;      // blocks scored by one workgroup
-constexpr int kTopkLdsKeys = 4096;   // top-k keeps keys in LDS up to this
+constexpr int kTopkRegRows = 20;     // top-k rows of 64 block words kept in registers
+constexpr int kTopkUnc = 512;        // uncertain blocks the top-k lists in LDS
 constexpr int kFuseSlots = 256;      // partial slots per query head, at most
 constexpr int kFuseSelLds = 2048;    // fusion keeps the selection in LDS up to this
 
@@ -70,13 +71,15 @@ struct Dims {
   int32_t kcap;        // selected block slots per (seq, kv head)
 };
 
-// Scratch owned by the context.
+// Scratch owned by the context.  Per-unit arrays have key_stride entries, a
+// multiple of 64.
 struct Scratch {
   unsigned long long *keyflag;  // [max_seqs][Hkv][key_stride] key | MAW flag << 32
-  uint32_t *keys;    // [max_seqs][Hkv][key_stride] top-k working keys (long units)
-  int32_t *ulist;    // [max_seqs][Hkv][key_stride] uncertain blocks (long units)
-  uint32_t *eps_max; // [max_seqs][Hkv] largest score error bound (float bits)
-  uint8_t *flags;    // [max_seqs][Hkv][key_stride] top-k working flags (long units)
+  uint32_t *keys;    // [max_seqs][Hkv][key_stride] top-k words past LDS (long units)
+  int32_t *ulist;    // [max_seqs][Hkv][key_stride] uncertain blocks past LDS
+  uint32_t *ukeys;   // [max_seqs][Hkv][key_stride] their exact keys
+  uint32_t *unit_acc;  // [max_seqs][Hkv][2] error bound (float bits, max) and
+                       // flagged candidates (count) of the score tiles; 0 between steps
   float *lm_dense;   // [max_seqs][Hq][ndt_cap] log-mass of dense block slots
   float *lm_sel;     // [max_seqs][Hq][kcap] log-mass of selected block slots
   int32_t *usel;     // [max_seqs][Hkv][kcap] selected block ids (attend copy)

@@ -28,6 +28,7 @@
 //     merged with the LSE identity, then the MAW update of every block.
 // The fused step and the separate ABI calls run these same device functions
 // on the same slots, so their results are bitwise identical.
+#include <algorithm>
 #include <cfloat>
 #include <cmath>
 
@@ -157,15 +158,11 @@ __device__ __forceinline__ uint32_t order_key(float u) {
 // ---------------------------------------------------------------------------
 // Shared memory of the roles (one launch may host several roles).
 struct TopkSmem {
-  uint32_t keys[kTopkLdsKeys];
-  int32_t ulist[kTopkLdsKeys];
-  uint8_t flags[kTopkLdsKeys];
-  int hist[4][256];
-  int scan[4];
-  uint32_t red[4];
-  int vals[4];
+  int32_t ulist[kTopkUnc];  // uncertain blocks of the top-k, in index order
+  uint32_t ukey[kTopkUnc];  // their exact keys
   float qs[SD_MAX_GROUP * 128];
-  double ud[256];
+  double ud[64];
+  uint32_t red[8];
   int last;
 };
 
@@ -307,7 +304,7 @@ __device__ __forceinline__ float score_eps(float E, float A) {
 template <int D, int G>
 __device__ void score_tile(const Ctx &c, int i, int seq, int h, const HeadInfo &hi,
                            const UG &g, int tile, const uint16_t *__restrict__ q,
-                           uint32_t *red /* LDS [4] */) {
+                           uint32_t *red /* LDS [8] */) {
   constexpr int MM = D / 16;    // MFMAs per 16 blocks (k = 2d values, 32 per MFMA)
   constexpr int GPW = 4;        // 16-block groups per wave
   constexpr int C4 = D / 4;
@@ -353,6 +350,7 @@ __device__ void score_tile(const Ctx &c, int i, int seq, int h, const HeadInfo &
   }
   const uint32_t absm = 0x7fff7fffu;
   float emax = 0.0f;
+  int n_flag = 0;
 #pragma unroll
   for (int gi = 0; gi < GPW; ++gi) {
     f32x4 acc = {0.f, 0.f, 0.f, 0.f}, acce = {0.f, 0.f, 0.f, 0.f};
@@ -386,22 +384,32 @@ __device__ void score_tile(const Ctx &c, int i, int seq, int h, const HeadInfo &
       if (cand) emax = fmaxf(emax, score_eps(E, A));
       if (c.dm.maw_beta > 0.0f) {
         const float mw = c.L.maw[hi.maw_off + (size_t)seq * hi.nbmax + blk];
-        if ((double)mw * (double)dense_count(g) > (double)c.dm.maw_beta * (double)hi.S)
+        if ((double)mw * (double)dense_count(g) > (double)c.dm.maw_beta * (double)hi.S) {
           kv |= 1ull << 32;
+          n_flag += cand ? 1 : 0;
+        }
       }
       st_dev(&c.sc.keyflag[ko], kv);
     }
   }
   // the unit's largest error bound (non-negative floats order as their bits)
+  // and its flagged candidates, accumulated over the tiles
   uint32_t eb = __float_as_uint(emax);
 #pragma unroll
   for (int o = 32; o >= 1; o >>= 1) eb = max(eb, (uint32_t)__shfl_xor((int)eb, o, 64));
-  if (lane == 0) red[wv] = eb;
+  const int nf = wave_sum_i(n_flag);
+  if (lane == 0) {
+    red[wv] = eb;
+    red[4 + wv] = (uint32_t)nf;
+  }
   __syncthreads();
-  if (threadIdx.x == 0)
-    __hip_atomic_fetch_max(&c.sc.eps_max[(size_t)seq * c.dm.Hkv + h],
-                           max(max(red[0], red[1]), max(red[2], red[3])), __ATOMIC_RELAXED,
+  if (threadIdx.x == 0) {
+    uint32_t *acc = &c.sc.unit_acc[2 * ((size_t)seq * c.dm.Hkv + h)];
+    __hip_atomic_fetch_max(acc, max(max(red[0], red[1]), max(red[2], red[3])), __ATOMIC_RELAXED,
                            __HIP_MEMORY_SCOPE_AGENT);
+    const uint32_t f = red[4] + red[5] + red[6] + red[7];
+    if (f) __hip_atomic_fetch_add(acc + 1, f, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  }
 }
 
 // Exact score of one block for one query head: sum_c max(q_c m_c, q_c M_c)
@@ -430,275 +438,246 @@ __device__ double exact_head_score(const Ctx &c, int seq, const HeadInfo &hi, in
   return acc;
 }
 
-// Block-wide exclusive scan of one int per thread (256 threads): wave scans
-// plus the four wave totals.
-__device__ int block_excl_scan(int v, int *sh, int *total) {
-  const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
-  int x = v;
-#pragma unroll
-  for (int o = 1; o < 64; o <<= 1) {
-    const int y = __shfl_up(x, o, 64);
-    if (lane >= o) x += y;
-  }
-  if (lane == 63) sh[wv] = x;
-  __syncthreads();
-  int base = 0;
-  for (int w = 0; w < wv; ++w) base += sh[w];
-  *total = sh[0] + sh[1] + sh[2] + sh[3];
-  __syncthreads();
-  return base + x - v;
+// ---------------------------------------------------------------------------
+// Top-k of one unit, in one wave, ordered by (MAW flag desc, exact fp32 score
+// desc, index asc) ([FLX] per-head top-k; [HGCA] MAW threshold first; R5,
+// R11).
+//
+// Block j sits in lane j % 64 of row j / 64 as one word: 0 = not selectable,
+// 1 = taken by the flag tier, otherwise the order key of its approximate
+// score (keys of finite or infinite floats are >= 0x007fffff).  Rows below
+// kTopkRegRows stay in registers; later rows live in LDS, or in the global
+// scratch beyond the LDS the launch reserved.
+//   1. the k-th largest approximate key T_a of the ranked words, by bisection
+//      on the key value: one ballot + popcount per row and step;
+//   2. band: A > T_a + 2 eps is in, A < T_a - 2 eps out (eps = the unit's
+//      largest error bound, so the k-th exact score lies within eps of T_a);
+//      the blocks in between are listed in index order and re-scored
+//      exactly, one lane per (block, head);
+//   3. the kr2 still missing are the largest exact keys of that list (ties to
+//      the lower index), by bisection again;
+//   4. ordered compaction with ballots: ascending block indices.
+__device__ __forceinline__ int lanes_below(unsigned long long m) {
+  return (int)__builtin_amdgcn_mbcnt_hi((uint32_t)(m >> 32),
+                                        __builtin_amdgcn_mbcnt_lo((uint32_t)m, 0u));
 }
-
-__device__ __forceinline__ int block_sum(int v, int *sh) {
-  int tot;
-  (void)block_excl_scan(v, sh, &tot);
-  return tot;
-}
-__device__ __forceinline__ uint32_t block_max_u(uint32_t v, uint32_t *sh) {
-#pragma unroll
-  for (int o = 32; o >= 1; o >>= 1) v = max(v, (uint32_t)__shfl_xor((int)v, o, 64));
-  if ((threadIdx.x & 63) == 0) sh[threadIdx.x >> 6] = v;
-  __syncthreads();
-  const uint32_t r = max(max(sh[0], sh[1]), max(sh[2], sh[3]));
-  __syncthreads();
-  return r;
-}
-__device__ __forceinline__ uint32_t block_min_u(uint32_t v, uint32_t *sh) {
+__device__ __forceinline__ int count_lanes(bool p) { return __popcll(__ballot(p)); }
+__device__ __forceinline__ uint32_t wave_min_u(uint32_t v) {
 #pragma unroll
   for (int o = 32; o >= 1; o >>= 1) v = min(v, (uint32_t)__shfl_xor((int)v, o, 64));
-  if ((threadIdx.x & 63) == 0) sh[threadIdx.x >> 6] = v;
-  __syncthreads();
-  const uint32_t r = min(min(sh[0], sh[1]), min(sh[2], sh[3]));
-  __syncthreads();
-  return r;
+  return (uint32_t)__builtin_amdgcn_readfirstlane((int)v);
 }
-
-// kr-th largest of the keys of the items with in(j) true (j < n), by radix
-// select over the bits below the common prefix of the subset's min and max
-// (spreads the first digit), with per-wave histograms.  Returns T; kr becomes
-// the number of items equal to T that belong to the top kr.
-template <class KeyF, class InF>
-__device__ uint32_t radix_select(int n, int &kr, KeyF key, InF in, TopkSmem &sm) {
-  const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
-  uint32_t lo = 0xffffffffu, hi = 0u;
-  for (int j = tid; j < n; j += 256)
-    if (in(j)) {
-      const uint32_t k = key(j);
-      lo = min(lo, k);
-      hi = max(hi, k);
-    }
-  lo = block_min_u(lo, sm.red);
-  hi = block_max_u(hi, sm.red);
-  if (lo == hi) return lo;  // every key equal
-  int top = 31 - __clz((int)(lo ^ hi));  // highest differing bit
-  uint32_t prefix = lo & ~((top >= 31) ? 0xffffffffu : ((2u << top) - 1u));
-  uint32_t mask = (top >= 31) ? 0u : ~((2u << top) - 1u);
-  for (int hb = top; hb >= 0; hb -= 8) {
-    const int width = min(8, hb + 1);
-    const int shift = hb + 1 - width;
-    const uint32_t dmask = (1u << width) - 1u;
-    for (int x = tid; x < 4 * 256; x += 256) (&sm.hist[0][0])[x] = 0;
-    __syncthreads();
-    for (int j = tid; j < n; j += 256)
-      if (in(j)) {
-        const uint32_t k = key(j);
-        if ((k & mask) == prefix) atomicAdd(&sm.hist[wv][(k >> shift) & dmask], 1);
-      }
-    __syncthreads();
-    if (tid < 64) {
-      // lane l owns digits 4l..4l+3: find d with count(>d) < kr <= count(>=d)
-      int cs[4];
+__device__ __forceinline__ uint32_t wave_max_u(uint32_t v) {
 #pragma unroll
-      for (int qd = 0; qd < 4; ++qd) {
-        const int dd = 4 * lane + qd;
-        cs[qd] = sm.hist[0][dd] + sm.hist[1][dd] + sm.hist[2][dd] + sm.hist[3][dd];
-      }
-      const int s4 = cs[0] + cs[1] + cs[2] + cs[3];
-      int suf = s4;
-#pragma unroll
-      for (int o = 1; o < 64; o <<= 1) {
-        const int x = __shfl_down(suf, o, 64);
-        if (lane + o < 64) suf += x;
-      }
-      int acc = suf - s4;  // items with digits >= 4(lane+1)
-      for (int qd = 3; qd >= 0; --qd) {
-        if (acc < kr && acc + cs[qd] >= kr) {
-          sm.vals[2] = 4 * lane + qd;
-          sm.vals[3] = acc;
-        }
-        acc += cs[qd];
-      }
-    }
-    __syncthreads();
-    const int digit = sm.vals[2];
-    kr -= sm.vals[3];
-    prefix |= (uint32_t)digit << shift;
-    mask |= dmask << shift;
-    __syncthreads();
-  }
-  return prefix;
+  for (int o = 32; o >= 1; o >>= 1) v = max(v, (uint32_t)__shfl_xor((int)v, o, 64));
+  return (uint32_t)__builtin_amdgcn_readfirstlane((int)v);
 }
-
-// top-k of one unit, ordered by (flag desc, exact fp32 score desc, index asc)
-// ([FLX] per-head top-k; [HGCA] MAW threshold first; R5, R11).  The k-th
-// approximate key T_a is found first; blocks above T_a + 2 eps are in, below
-// T_a - 2 eps out (eps = the unit's largest error bound: the k-th exact key
-// lies within eps of T_a), and the blocks in between are re-scored exactly,
-// one lane per (block, head), and ranked.  The output is compacted in
-// ascending block order.  256 threads; keys and flags live in LDS (InLds) or
-// in the global scratch for very long sequences.
-template <int D, int G, bool InLds>
-__device__ void topk_impl(const Ctx &c, int i, int seq, int h, const HeadInfo &hi,
-                          const UG &g, const uint16_t *__restrict__ q,
-                          int32_t *__restrict__ blk_idx, int32_t *__restrict__ blk_cnt,
-                          int k_cap, TopkSmem &sm) {
-  const int tid = threadIdx.x;
-  const int n = g.n_blk;
-  const size_t uo = ((size_t)seq * c.dm.Hkv + h) * c.dm.key_stride;
-  const unsigned long long *gkf = c.sc.keyflag + uo;
-  uint32_t *gkeys = c.sc.keys + uo;
-  uint8_t *gflags = c.sc.flags + uo;
-  const bool use_flag = c.dm.maw_beta > 0.0f;
-  uint32_t *keys = InLds ? sm.keys : gkeys;
-  uint8_t *flags = InLds ? sm.flags : gflags;
-  int32_t *ulist = InLds ? sm.ulist : c.sc.ulist + uo;
-  // one trip: keys, flags (category bits: 1 MAW flag, 2 sure in, 4
-  // uncertain), the query of the group, the unit's error bound
-  {
-    const uint16_t *qg = q + ((size_t)i * c.dm.Hq + (size_t)h * G) * D;
-    float qv[(G * D + 255) / 256];
-#pragma unroll
-    for (int r = 0; r < (G * D + 255) / 256; ++r) {
-      const int x = r * 256 + tid;
-      qv[r] = x < G * D ? __uint_as_float((uint32_t)qg[x] << 16) : 0.0f;
-    }
-    for (int j0 = 0; j0 < n; j0 += 4 * 256) {
-      unsigned long long kv[4];
-#pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        const int j = j0 + r * 256 + tid;
-        kv[r] = j < n ? ld_dev(&gkf[j]) : 0ull;
-      }
-#pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        const int j = j0 + r * 256 + tid;
-        if (j < n) {
-          keys[j] = (uint32_t)kv[r];
-          flags[j] = use_flag ? (uint8_t)((kv[r] >> 32) & 1) : 0;
-        }
-      }
-    }
-#pragma unroll
-    for (int r = 0; r < (G * D + 255) / 256; ++r) {
-      const int x = r * 256 + tid;
-      if (x < G * D) sm.qs[x] = qv[r];
-    }
+// Largest t in [lo, hi] with count_ge(t) >= k, given count_ge(lo) >= k: the
+// k-th largest of the counted values.
+template <class CountF>
+__device__ __forceinline__ uint32_t bisect_kth(uint32_t lo, uint32_t hi, int k, CountF count_ge) {
+  while (lo < hi) {
+    const uint32_t mid = lo + ((hi - lo) >> 1) + 1u;  // lo < mid <= hi
+    if (count_ge(mid) >= k) lo = mid; else hi = mid - 1u;
   }
-  const double eps = (double)__uint_as_float(ld_dev(&c.sc.eps_max[(size_t)seq * c.dm.Hkv + h]));
-  __syncthreads();
-  if (tid == 0) st_dev(&c.sc.eps_max[(size_t)seq * c.dm.Hkv + h], 0u);  // for the next step
-
-  int lc = 0, lf = 0;
-  for (int j = tid; j < n; j += 256)
-    if (keys[j]) {
-      ++lc;
-      lf += flags[j] & 1;
-    }
-  const int C = block_sum(lc, sm.scan);
-  const int F = block_sum(lf, sm.scan);
-  const int kk = min(C, g.kk);
-  // radix subset: flagged candidates when they alone fill k, otherwise the
-  // unflagged candidates (every flagged one is taken).
-  const bool take_flagged = F < kk;
-  const int want = take_flagged ? 0 : 1;
-  const int k_sub = take_flagged ? kk - F : kk;
-  auto in_sub = [&](int j) { return keys[j] != 0u && (flags[j] & 1) == want; };
-  uint32_t T2 = 0;
-  int kr2 = 0;
-  if (k_sub > 0) {
-    int kr = k_sub;
-    const uint32_t Ta_key = radix_select(n, kr, [&](int j) { return keys[j]; }, in_sub, sm);
-    const double Ta = (double)key_to_float(Ta_key);
-    const double band_lo = Ta - 2.0 * eps, band_hi = Ta + 2.0 * eps;
-    // categories, and the uncertain blocks listed in index order
-    const int per = (n + 255) / 256;
-    const int j0 = min(n, tid * per), j1 = min(n, j0 + per);
-    int lin = 0, lunc = 0;
-    for (int j = j0; j < j1; ++j)
-      if (in_sub(j)) {
-        const double A = (double)key_to_float(keys[j]);
-        if (A > band_hi) {
-          flags[j] |= 2;
-          ++lin;
-        } else if (A >= band_lo) {
-          flags[j] |= 4;
-          ++lunc;
-        }
-      }
-    int n_unc;
-    int u = block_excl_scan(lunc, sm.scan, &n_unc);
-    const int n_in = block_sum(lin, sm.scan);
-    for (int j = j0; j < j1; ++j)
-      if (flags[j] & 4) ulist[u++] = j;
-    kr2 = k_sub - n_in;  // taken from the uncertain blocks (>= 1)
-    __syncthreads();
-    // exact keys of the uncertain blocks, one lane per (block, head)
-    constexpr int BPR = 256 / G;  // blocks per round
-    for (int u0 = 0; u0 < n_unc; u0 += BPR) {
-      const int uu = u0 + tid / G, gg = tid % G;
-      const bool on = tid < BPR * G && uu < n_unc;
-      double U = on ? exact_head_score<D>(c, seq, hi, ulist[uu], sm.qs + gg * D) : 0.0;
-      if (on) sm.ud[tid] = U;
-      __syncthreads();
-      if (tid < BPR && u0 + tid < n_unc) {
-        double best = sm.ud[tid * G];
-        for (int x = 1; x < G; ++x)
-          if (sm.ud[tid * G + x] > best) best = sm.ud[tid * G + x];
-        keys[ulist[u0 + tid]] = order_key((float)best);
-      }
-      __syncthreads();
-    }
-    T2 = radix_select(n, kr2, [&](int j) { return keys[j]; },
-                      [&](int j) { return (flags[j] & 4) != 0; }, sm);
-  }
-  // ordered compaction: contiguous index ranges per thread
-  const int per = (n + 255) / 256;
-  const int j0 = min(n, tid * per), j1 = min(n, j0 + per);
-  int leq = 0;
-  for (int j = j0; j < j1; ++j)
-    if ((flags[j] & 4) && keys[j] == T2) ++leq;
-  int tot;
-  const int eq_base = block_excl_scan(leq, sm.scan, &tot);
-  auto chosen = [&](int j, int &eq_rank) -> bool {
-    if (!keys[j]) return false;
-    const int f = flags[j];
-    if (take_flagged && (f & 1)) return true;
-    if (f & 2) return true;
-    if (f & 4) {
-      if (keys[j] > T2) return true;
-      if (keys[j] == T2) return eq_rank++ < kr2;
-    }
-    return false;
-  };
-  int eq_rank = eq_base, lsel = 0;
-  for (int j = j0; j < j1; ++j) lsel += chosen(j, eq_rank) ? 1 : 0;
-  int out = block_excl_scan(lsel, sm.scan, &tot);
-  eq_rank = eq_base;
-  int32_t *dst = blk_idx + ((size_t)i * c.dm.Hkv + h) * k_cap;
-  for (int j = j0; j < j1; ++j)
-    if (chosen(j, eq_rank) && out < k_cap) dst[out++] = j;
-  if (tid == 0) blk_cnt[(size_t)i * c.dm.Hkv + h] = kk;
+  return lo;
 }
 
 template <int D, int G>
 __device__ void topk_unit(const Ctx &c, int i, int seq, int h, const HeadInfo &hi,
                           const UG &g, const uint16_t *__restrict__ q,
                           int32_t *__restrict__ blk_idx, int32_t *__restrict__ blk_cnt,
-                          int k_cap, TopkSmem &sm) {
-  if (g.n_blk <= kTopkLdsKeys)
-    topk_impl<D, G, true>(c, i, seq, h, hi, g, q, blk_idx, blk_cnt, k_cap, sm);
-  else
-    topk_impl<D, G, false>(c, i, seq, h, hi, g, q, blk_idx, blk_cnt, k_cap, sm);
+                          int k_cap, TopkSmem &sm, uint32_t *lrows, int lrows_words) {
+  if (threadIdx.x >= 64) return;
+  const int lane = threadIdx.x;
+  const int n = g.n_blk, rows = cdiv(n, 64);
+  const size_t unit = (size_t)seq * c.dm.Hkv + h;
+  const size_t uo = unit * c.dm.key_stride;
+  const unsigned long long *gkf = c.sc.keyflag + uo;
+  constexpr int kRegWords = kTopkRegRows * 64;
+  // words of the rows past the registers
+  const bool mem_lds = rows * 64 - kRegWords <= lrows_words;
+  uint32_t *gw = c.sc.keys + uo;
+  auto mem_ld = [&](int j) -> uint32_t { return mem_lds ? lrows[j - kRegWords] : ld_dev(&gw[j]); };
+  auto mem_st = [&](int j, uint32_t v) {
+    if (mem_lds) lrows[j - kRegWords] = v; else st_dev(&gw[j], v);
+  };
+  // uncertain list: LDS up to kTopkUnc entries, global scratch after
+  int32_t *gul = c.sc.ulist + uo;
+  uint32_t *guk = c.sc.ukeys + uo;
+  auto ul_ld = [&](int p) -> int { return p < kTopkUnc ? sm.ulist[p] : ld_dev(&gul[p]); };
+  auto ul_st = [&](int p, int v) { if (p < kTopkUnc) sm.ulist[p] = v; else st_dev(&gul[p], v); };
+  auto uk_ld = [&](int p) -> uint32_t { return p < kTopkUnc ? sm.ukey[p] : ld_dev(&guk[p]); };
+  auto uk_st = [&](int p, uint32_t v) { if (p < kTopkUnc) sm.ukey[p] = v; else st_dev(&guk[p], v); };
+
+  // the score tiles' accumulators: error bound and flagged candidates
+  const double eps = (double)__uint_as_float(ld_dev(&c.sc.unit_acc[2 * unit]));
+  const bool use_flag = c.dm.maw_beta > 0.0f;
+  const int F = use_flag ? (int)ld_dev(&c.sc.unit_acc[2 * unit + 1]) : 0;
+  const int kk = g.kk;
+  // every flagged candidate is taken when they do not fill k on their own
+  // (the unflagged ones are ranked for the rest); otherwise only the flagged
+  // candidates are ranked
+  const bool take_flagged = F < kk;
+  const uint32_t want = take_flagged ? 0u : 1u;
+  const int k_sub = take_flagged ? kk - F : kk;
+  auto word_of = [&](unsigned long long kv) -> uint32_t {
+    const uint32_t key = (uint32_t)kv;
+    if (key == 0u) return 0u;
+    const uint32_t fl = use_flag ? (uint32_t)(kv >> 32) & 1u : 0u;
+    return fl == want ? key : (take_flagged ? 1u : 0u);
+  };
+
+  // 0. words (all loads in flight together), the group's query for re-scoring
+  uint32_t w[kTopkRegRows];
+  uint32_t lo = 0xffffffffu, hi_k = 0u;
+  {
+    const int jl = max(n - 1, 0);
+    unsigned long long kv[kTopkRegRows];
+#pragma unroll
+    for (int r = 0; r < kTopkRegRows; ++r) kv[r] = ld_dev(&gkf[min(r * 64 + lane, jl)]);
+    const uint16_t *qg = q + ((size_t)i * c.dm.Hq + (size_t)h * G) * D;
+    constexpr int QPL = (G * D + 63) / 64;
+#pragma unroll
+    for (int r = 0; r < QPL; ++r) {
+      const int x = r * 64 + lane;
+      if (x < G * D) sm.qs[x] = __uint_as_float((uint32_t)qg[x] << 16);
+    }
+#pragma unroll
+    for (int r = 0; r < kTopkRegRows; ++r) {
+      w[r] = r * 64 + lane < n ? word_of(kv[r]) : 0u;
+      if (w[r] >= 2u) {
+        lo = min(lo, w[r]);
+        hi_k = max(hi_k, w[r]);
+      }
+    }
+    for (int r0 = kTopkRegRows; r0 < rows; r0 += 8) {
+      unsigned long long kb[8];
+#pragma unroll
+      for (int x = 0; x < 8; ++x) kb[x] = ld_dev(&gkf[min((r0 + x) * 64 + lane, jl)]);
+#pragma unroll
+      for (int x = 0; x < 8; ++x) {
+        const int j = (r0 + x) * 64 + lane;
+        if (r0 + x < rows) {
+          const uint32_t v = j < n ? word_of(kb[x]) : 0u;
+          mem_st(j, v);
+          if (v >= 2u) {
+            lo = min(lo, v);
+            hi_k = max(hi_k, v);
+          }
+        }
+      }
+    }
+    wait_vmem();
+  }
+  auto count_ge = [&](uint32_t t) -> int {
+    int cnt = 0;
+#pragma unroll
+    for (int r = 0; r < kTopkRegRows; ++r) cnt += count_lanes(w[r] >= t);
+    for (int r = kTopkRegRows; r < rows; ++r) cnt += count_lanes(mem_ld(r * 64 + lane) >= t);
+    return cnt;
+  };
+
+  // 1-3. thresholds
+  double band_lo = INFINITY, band_hi = INFINITY;
+  uint32_t T2 = 0xffffffffu;
+  int kr2_eq = 0;
+  // classes: 0 out, 1 taken (flag tier or above the band), 2 uncertain
+  auto cls = [&](uint32_t v) -> int {
+    if (v < 2u) return (int)v;
+    const double A = (double)key_to_float(v);
+    return A > band_hi ? 1 : (A >= band_lo ? 2 : 0);
+  };
+  if (k_sub > 0) {
+    lo = wave_min_u(lo);
+    hi_k = wave_max_u(hi_k);
+    const uint32_t Ta_key = bisect_kth(lo, hi_k, k_sub, count_ge);
+    const double Ta = (double)key_to_float(Ta_key);
+    band_lo = Ta - 2.0 * eps;
+    band_hi = Ta + 2.0 * eps;
+    // list the uncertain blocks in index order; count the sure ones
+    int n_in = 0, n_unc = 0;
+    auto list_row = [&](int j, uint32_t v) {
+      const int k = cls(v);
+      const bool unc = k == 2;
+      const unsigned long long m = __ballot(unc);
+      if (unc) ul_st(n_unc + lanes_below(m), j);
+      n_unc += __popcll(m);
+      n_in += count_lanes(k == 1 && v >= 2u);
+    };
+#pragma unroll
+    for (int r = 0; r < kTopkRegRows; ++r) list_row(r * 64 + lane, w[r]);
+    for (int r = kTopkRegRows; r < rows; ++r) list_row(r * 64 + lane, mem_ld(r * 64 + lane));
+    wait_vmem();
+    const int kr2 = k_sub - n_in;  // >= 1: T_a's own block is uncertain
+    // exact keys of the uncertain blocks, one lane per (block, head)
+    constexpr int BPR = 64 / G;
+    for (int u0 = 0; u0 < n_unc; u0 += BPR) {
+      const int uu = u0 + lane / G, gg = lane % G;
+      double U = 0.0;
+      if (lane < BPR * G && uu < n_unc)
+        U = exact_head_score<D>(c, seq, hi, ul_ld(uu), sm.qs + gg * D);
+      sm.ud[lane] = U;
+      if (lane < BPR && u0 + lane < n_unc) {
+        double best = sm.ud[lane * G];
+        for (int x = 1; x < G; ++x) best = sm.ud[lane * G + x] > best ? sm.ud[lane * G + x] : best;
+        uk_st(u0 + lane, order_key((float)best));
+      }
+    }
+    wait_vmem();
+    // kr2-th largest exact key of the list
+    const int urows = cdiv(n_unc, 64);
+    const uint32_t e0 = lane < n_unc ? uk_ld(lane) : 0u;
+    uint32_t lo2 = lane < n_unc ? e0 : 0xffffffffu, hi2 = e0;
+    for (int r = 1; r < urows; ++r) {
+      const int p = r * 64 + lane;
+      if (p < n_unc) {
+        const uint32_t e = uk_ld(p);
+        lo2 = min(lo2, e);
+        hi2 = max(hi2, e);
+      }
+    }
+    lo2 = wave_min_u(lo2);
+    hi2 = wave_max_u(hi2);
+    auto ucount_ge = [&](uint32_t t) -> int {
+      int cnt = count_lanes(e0 >= t);
+      for (int r = 1; r < urows; ++r) {
+        const int p = r * 64 + lane;
+        cnt += count_lanes(p < n_unc && uk_ld(p) >= t);
+      }
+      return cnt;
+    };
+    T2 = bisect_kth(lo2, hi2, kr2, ucount_ge);
+    kr2_eq = kr2 - (T2 == 0xffffffffu ? 0 : ucount_ge(T2 + 1u));
+  }
+
+  // 4. ordered compaction
+  int32_t *dst = blk_idx + ((size_t)i * c.dm.Hkv + h) * k_cap;
+  int ub = 0, eb = 0, ob = 0;
+  auto emit_row = [&](int j, uint32_t v) {
+    const int k = cls(v);
+    const bool unc = k == 2;
+    const unsigned long long mu = __ballot(unc);
+    const uint32_t e = unc ? uk_ld(ub + lanes_below(mu)) : 0u;
+    ub += __popcll(mu);
+    const bool eq = unc && e == T2;
+    const unsigned long long me = __ballot(eq);
+    const bool ch = k == 1 || (unc && e > T2) || (eq && eb + lanes_below(me) < kr2_eq);
+    eb += __popcll(me);
+    const unsigned long long mc = __ballot(ch);
+    const int o = ob + lanes_below(mc);
+    if (ch && o < k_cap) dst[o] = j;
+    ob += __popcll(mc);
+  };
+#pragma unroll
+  for (int r = 0; r < kTopkRegRows; ++r)
+    if (r < rows) emit_row(r * 64 + lane, w[r]);
+  for (int r = kTopkRegRows; r < rows; ++r) emit_row(r * 64 + lane, mem_ld(r * 64 + lane));
+  if (lane == 0) {
+    blk_cnt[(size_t)i * c.dm.Hkv + h] = kk;
+    st_dev(&c.sc.unit_acc[2 * unit], 0u);  // cleared for the next step
+    st_dev(&c.sc.unit_acc[2 * unit + 1], 0u);
+  }
 }
 
 // ---------------------------------------------------------------------------
@@ -1154,10 +1133,10 @@ __global__ __launch_bounds__(256) void k_select(Ctx c, SeqBatch b, int tiles_x,
                                                 int32_t *__restrict__ blk_cnt, int k_cap,
                                                 const uint16_t *__restrict__ q,
                                                 float *__restrict__ o_part,
-                                                float *__restrict__ lse_part, int p_cap) {
-  constexpr size_t kBytes = sizeof(TopkSmem) > sizeof(AttSmem<D, G>) ? sizeof(TopkSmem)
-                                                                      : sizeof(AttSmem<D, G>);
-  __shared__ __align__(16) unsigned char smem_raw[kBytes];
+                                                float *__restrict__ lse_part, int p_cap,
+                                                int lrows_words) {
+  // dynamic LDS: max(AttSmem, TopkSmem + lrows_words top-k words)
+  extern __shared__ __align__(16) unsigned char smem_raw[];
   TopkSmem &smem_topk = *reinterpret_cast<TopkSmem *>(smem_raw);
   AttSmem<D, G> &smem_att = *reinterpret_cast<AttSmem<D, G> *>(smem_raw);
   int wg = blockIdx.x;
@@ -1170,10 +1149,11 @@ __global__ __launch_bounds__(256) void k_select(Ctx c, SeqBatch b, int tiles_x,
     const int n_tiles = max(1, cdiv(g.n_blk, kScoreTile));
     if (tile >= n_tiles) return;
     score_tile<D, G>(c, i, seq, h, hi, g, tile, q, smem_topk.red);
-    // the last tile of the unit to arrive runs its top-k
+    // the last tile of the unit to arrive runs its top-k (one wave)
     uint32_t *ctr = &c.sc.arrive[((size_t)seq * c.dm.Hkv + h) * 2];
     if (!arrive_last(ctr, (unsigned)n_tiles, &smem_topk.last)) return;
-    topk_unit<D, G>(c, i, seq, h, hi, g, q, blk_idx, blk_cnt, k_cap, smem_topk);
+    topk_unit<D, G>(c, i, seq, h, hi, g, q, blk_idx, blk_cnt, k_cap, smem_topk,
+                    reinterpret_cast<uint32_t *>(smem_raw + sizeof(TopkSmem)), lrows_words);
     if (threadIdx.x == 0) st_dev(ctr, 0u);
     return;
   }
@@ -1322,10 +1302,18 @@ hipError_t launch_select(const Ctx &c, const SeqBatch &b, int max_blocks,
   const int tiles_x = max(1, (max_blocks + kScoreTile - 1) / kScoreTile);
   if (!dense_o_part) dchunks_x = 0;
   const int grid = tiles_x * c.dm.Hkv * b.n + dchunks_x * c.dm.Hkv * b.n;
-  SD_DISPATCH_DG(c.dm.d, c.dm.G,
-                 hipLaunchKernelGGL((k_select<D_, G_>), dim3(grid), dim3(256), 0, st, c, b,
-                                    tiles_x, max(dchunks_x, 1), blk_idx, blk_cnt, k_cap, q,
-                                    dense_o_part, dense_lse_part, p_cap));
+  // top-k words past the register rows go to LDS while the launch stays
+  // within 64 KiB of LDS per workgroup, else to the global scratch
+  const int extra = max(0, (max_blocks + 63) / 64 - kTopkRegRows) * 64;
+  const size_t topk_bytes = sizeof(TopkSmem) + sizeof(uint32_t) * (size_t)extra;
+  const int lrows_words = topk_bytes <= 65536 ? extra : 0;
+  SD_DISPATCH_DG(c.dm.d, c.dm.G, {
+    const size_t smem = std::max(sizeof(AttSmem<D_, G_>),
+                                 sizeof(TopkSmem) + sizeof(uint32_t) * (size_t)lrows_words);
+    hipLaunchKernelGGL((k_select<D_, G_>), dim3(grid), dim3(256), smem, st, c, b, tiles_x,
+                       max(dchunks_x, 1), blk_idx, blk_cnt, k_cap, q, dense_o_part,
+                       dense_lse_part, p_cap, lrows_words);
+  });
   return hipGetLastError();
 }
 

@@ -281,17 +281,19 @@ sd_status sparse_decode_init(const sd_config *cfg, sd_ctx **out) {
   c->dims.scale_log2 = (float)((double)scale * 1.4426950408889634);
   c->dims.maw_decay = cfg->maw_decay > 0.0f ? cfg->maw_decay : 0.95f;
   c->dims.maw_beta = cfg->maw_beta;
+  key_stride = (int)cdiv(key_stride, 64) * 64;  // whole top-k rows of 64 blocks
   c->dims.key_stride = key_stride;
   c->dims.ndt_cap = ndt_cap;
   c->dims.kcap = c->k_cap;
 
   // scratch
-  if ((s = dev_alloc(c, &c->sc.keys, (size_t)max_seqs * c->Hkv * key_stride)) != SD_OK) return s;
-  if ((s = dev_alloc(c, &c->sc.keyflag, (size_t)max_seqs * c->Hkv * key_stride)) != SD_OK) return s;
-  if ((s = dev_alloc(c, &c->sc.flags, (size_t)max_seqs * c->Hkv * key_stride)) != SD_OK) return s;
-  if ((s = dev_alloc(c, &c->sc.ulist, (size_t)max_seqs * c->Hkv * key_stride)) != SD_OK) return s;
-  if ((s = dev_alloc(c, &c->sc.eps_max, (size_t)max_seqs * c->Hkv)) != SD_OK) return s;
-  SD_HIP(c, hipMemset(c->sc.eps_max, 0, sizeof(uint32_t) * max_seqs * c->Hkv));
+  const size_t per_unit = (size_t)max_seqs * c->Hkv * key_stride;
+  if ((s = dev_alloc(c, &c->sc.keys, per_unit)) != SD_OK) return s;
+  if ((s = dev_alloc(c, &c->sc.keyflag, per_unit)) != SD_OK) return s;
+  if ((s = dev_alloc(c, &c->sc.ulist, per_unit)) != SD_OK) return s;
+  if ((s = dev_alloc(c, &c->sc.ukeys, per_unit)) != SD_OK) return s;
+  if ((s = dev_alloc(c, &c->sc.unit_acc, (size_t)max_seqs * c->Hkv * 2)) != SD_OK) return s;
+  SD_HIP(c, hipMemset(c->sc.unit_acc, 0, sizeof(uint32_t) * max_seqs * c->Hkv * 2));
   if ((s = dev_alloc(c, &c->sc.lm_dense, (size_t)max_seqs * c->Hq * ndt_cap)) != SD_OK) return s;
   if ((s = dev_alloc(c, &c->sc.lm_sel, (size_t)max_seqs * c->Hq * c->k_cap)) != SD_OK) return s;
   if ((s = dev_alloc(c, &c->sc.usel, (size_t)max_seqs * c->Hkv * c->k_cap)) != SD_OK) return s;
@@ -299,7 +301,6 @@ sd_status sparse_decode_init(const sd_config *cfg, sd_ctx **out) {
   if ((s = dev_alloc(c, &c->sc.arrive, (size_t)max_seqs * c->Hkv * 2)) != SD_OK) return s;
   SD_HIP(c, hipMemset(c->sc.ucnt, 0, sizeof(int32_t) * max_seqs * c->Hkv));
   SD_HIP(c, hipMemset(c->sc.arrive, 0, sizeof(uint32_t) * max_seqs * c->Hkv * 2));
-  SD_HIP(c, hipMemset(c->sc.flags, 0, (size_t)max_seqs * c->Hkv * key_stride));
 
   // layers
   c->layers.resize(cfg->num_layers);
