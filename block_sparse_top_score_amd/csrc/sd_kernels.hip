@@ -161,7 +161,7 @@ struct TopkSmem {
   int32_t ulist[kTopkUnc];  // uncertain blocks of the top-k, in index order
   uint32_t ukey[kTopkUnc];  // their exact keys
   float qs[SD_MAX_GROUP * 128];
-  double ud[64];
+  double ud[16];
   uint32_t red[8];
   int last;
 };
@@ -306,11 +306,11 @@ __device__ void score_tile(const Ctx &c, int i, int seq, int h, const HeadInfo &
                            const UG &g, int tile, const uint16_t *__restrict__ q,
                            uint32_t *red /* LDS [8] */) {
   constexpr int MM = D / 16;    // MFMAs per 16 blocks (k = 2d values, 32 per MFMA)
-  constexpr int GPW = 4;        // 16-block groups per wave
+  constexpr int GPW = kScoreTile / 64;  // 16-block groups per wave
   constexpr int C4 = D / 4;
   const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
   const int r16 = lane & 15, lgrp = lane >> 4;
-  const int base = tile * kScoreTile + wv * 64;
+  const int base = tile * kScoreTile + wv * 16 * GPW;
   const bool active = base < g.n_blk;
   const uint4 *sp = reinterpret_cast<const uint4 *>(c.L.summ + hi.summ_off +
                                                     (size_t)seq * C4 * hi.nbmax * 8);
@@ -413,29 +413,92 @@ __device__ void score_tile(const Ctx &c, int i, int seq, int h, const HeadInfo &
 }
 
 // Exact score of one block for one query head: sum_c max(q_c m_c, q_c M_c)
-// in double in channel order, exactly the plain sequential double sum (the
-// products of bf16 values are exact).  All loads are issued first.
+// in double in channel order, the plain sequential double sum.  The larger
+// product is q_c M_c for q_c >= 0 and q_c m_c otherwise (m_c <= M_c; with
+// q_c = 0 both are zeros, which leave the sum unchanged), and a product of
+// two bf16 values is exact in double, so one fma per channel rounds as the
+// product-then-add of the definition.
+__device__ __forceinline__ float upper_term(float qv, uint32_t mm) {
+  return qv >= 0.0f ? bf16_hi(mm) : bf16_lo(mm);
+}
 template <int D>
-__device__ double exact_head_score(const Ctx &c, int seq, const HeadInfo &hi, int blk,
-                                   const float *qs /* LDS [D] of this head */) {
+__device__ double exact_score_seq(const Ctx &c, int seq, const HeadInfo &hi, int blk,
+                                  const float *qs /* LDS [D] of this head */) {
   constexpr int C4 = D / 4;
   const uint4 *sp = reinterpret_cast<const uint4 *>(c.L.summ + hi.summ_off +
                                                     (size_t)seq * C4 * hi.nbmax * 8) + blk;
-  uint4 w[C4];
-#pragma unroll
-  for (int c4 = 0; c4 < C4; ++c4) w[c4] = sp[(size_t)c4 * hi.nbmax];
   double acc = 0.0;
-#pragma unroll
   for (int c4 = 0; c4 < C4; ++c4) {
-    const uint32_t ws[4] = {w[c4].x, w[c4].y, w[c4].z, w[c4].w};
+    const uint4 w = sp[(size_t)c4 * hi.nbmax];
+    const uint32_t ws[4] = {w.x, w.y, w.z, w.w};
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
-      const double qv = (double)qs[4 * c4 + j];
-      const double a = qv * (double)bf16_lo(ws[j]), b = qv * (double)bf16_hi(ws[j]);
-      acc += a > b ? a : b;
+      const float qv = qs[4 * c4 + j];
+      acc = fma((double)qv, (double)upper_term(qv, ws[j]), acc);
     }
   }
   return acc;
+}
+
+__device__ __forceinline__ double dpp_quad_f64(double x, int which) {
+  const unsigned long long b = __double_as_longlong(x);
+  int lo = (int)(uint32_t)b, hi = (int)(uint32_t)(b >> 32);
+  if (which == 1) {
+    lo = __builtin_amdgcn_update_dpp(0, lo, 0xB1, 0xF, 0xF, false);  // quad_perm [1,0,3,2]
+    hi = __builtin_amdgcn_update_dpp(0, hi, 0xB1, 0xF, 0xF, false);
+  } else {
+    lo = __builtin_amdgcn_update_dpp(0, lo, 0x4E, 0xF, 0xF, false);  // quad_perm [2,3,0,1]
+    hi = __builtin_amdgcn_update_dpp(0, hi, 0x4E, 0xF, 0xF, false);
+  }
+  return __longlong_as_double((long long)(((unsigned long long)(uint32_t)hi << 32) | (uint32_t)lo));
+}
+__device__ __forceinline__ int dpp_quad_i32(int x, int which) {
+  return which == 1 ? __builtin_amdgcn_update_dpp(0, x, 0xB1, 0xF, 0xF, false)
+                    : __builtin_amdgcn_update_dpp(0, x, 0x4E, 0xF, 0xF, false);
+}
+
+// The same sum by the four lanes of a quad (lane % 4 = part; part p sums
+// channels [p D/4, (p+1) D/4)), returned in all four lanes.  Every product
+// p_c = q_c s_c has at most 16 significant bits, so it is a multiple of
+// 2^(e_c - 16) with |p_c| < 2^e_c; when sum_c |p_c| < 2^(min_c e_c + 36)
+// (half the 2^53 range, covering the rounding of that bound) every partial
+// sum in any order is exact, hence equal to the sequential sum.  Otherwise
+// the sequential sum is taken.  Every lane of the wave must call it.
+template <int D>
+__device__ double exact_score_quad(const Ctx &c, int seq, const HeadInfo &hi, int blk,
+                                   const float *qs /* LDS [D] of this head */, bool on) {
+  constexpr int C4 = D / 4, P4 = C4 / 4;  // channel quads per part
+  const int part = threadIdx.x & 3;
+  const uint4 *sp = reinterpret_cast<const uint4 *>(c.L.summ + hi.summ_off +
+                                                    (size_t)seq * C4 * hi.nbmax * 8) + blk;
+  uint4 w[P4];
+#pragma unroll
+  for (int t = 0; t < P4; ++t)
+    w[t] = on ? sp[(size_t)(part * P4 + t) * hi.nbmax] : make_uint4(0, 0, 0, 0);
+  double ps = 0.0, sabs = 0.0;
+  int emin = 4096;
+#pragma unroll
+  for (int t = 0; t < P4; ++t) {
+    const uint32_t ws[4] = {w[t].x, w[t].y, w[t].z, w[t].w};
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const float qv = qs[4 * (part * P4 + t) + j];
+      const double pr = (double)qv * (double)upper_term(qv, ws[j]);
+      ps += pr;
+      sabs += fabs(pr);
+      emin = min(emin, pr != 0.0 ? __builtin_amdgcn_frexp_exp(pr) : 4096);
+    }
+  }
+  ps += dpp_quad_f64(ps, 1);
+  ps += dpp_quad_f64(ps, 2);
+  sabs += dpp_quad_f64(sabs, 1);
+  sabs += dpp_quad_f64(sabs, 2);
+  emin = min(emin, dpp_quad_i32(emin, 1));
+  emin = min(emin, dpp_quad_i32(emin, 2));
+  // frexp exponents: |p| < 2^e; sabs < 2^(emin + 36) <=> frexp_exp(sabs) <= emin + 36
+  const bool exact = sabs == 0.0 || __builtin_amdgcn_frexp_exp(sabs) <= emin + 36;
+  if (on && !exact) ps = exact_score_seq<D>(c, seq, hi, blk, qs);
+  return ps;
 }
 
 // ---------------------------------------------------------------------------
@@ -448,29 +511,51 @@ __device__ double exact_head_score(const Ctx &c, int seq, const HeadInfo &hi, in
 // score (keys of finite or infinite floats are >= 0x007fffff).  Rows below
 // kTopkRegRows stay in registers; later rows live in LDS, or in the global
 // scratch beyond the LDS the launch reserved.
-//   1. the k-th largest approximate key T_a of the ranked words, by bisection
-//      on the key value: one ballot + popcount per row and step;
-//   2. band: A > T_a + 2 eps is in, A < T_a - 2 eps out (eps = the unit's
-//      largest error bound, so the k-th exact score lies within eps of T_a);
-//      the blocks in between are listed in index order and re-scored
-//      exactly, one lane per (block, head);
-//   3. the kr2 still missing are the largest exact keys of that list (ties to
-//      the lower index), by bisection again;
+//   1. bisection on the key value narrows [a, b], which always holds the
+//      k-th largest approximate key T_a (one ballot + popcount per row and
+//      step), until b - a is within the unit's error bound eps;
+//   2. band: A > b + 2 eps is in, A < a - 2 eps out (every approximate score
+//      lies within eps of its exact score, so the k-th exact score lies
+//      within eps of T_a); both edges are rounded outwards to float keys so
+//      that the tests are integer compares.  Blocks inside the band are
+//      listed in index order and re-scored exactly, one lane per (block,
+//      head);
+//   3. the kr2 still missing are the largest exact keys of that list (ties
+//      to the lower index), found by bisection; they are marked in an LDS
+//      bitmask of rows;
 //   4. ordered compaction with ballots: ascending block indices.
 __device__ __forceinline__ int lanes_below(unsigned long long m) {
   return (int)__builtin_amdgcn_mbcnt_hi((uint32_t)(m >> 32),
                                         __builtin_amdgcn_mbcnt_lo((uint32_t)m, 0u));
 }
 __device__ __forceinline__ int count_lanes(bool p) { return __popcll(__ballot(p)); }
+// Wave min / max of an unsigned value (uniform result): DPP inside rows of
+// 16 lanes, then the four row results.
+template <int CTRL>
+__device__ __forceinline__ uint32_t dppu(uint32_t x) {
+  return (uint32_t)__builtin_amdgcn_update_dpp(0, (int)x, CTRL, 0xF, 0xF, false);
+}
 __device__ __forceinline__ uint32_t wave_min_u(uint32_t v) {
-#pragma unroll
-  for (int o = 32; o >= 1; o >>= 1) v = min(v, (uint32_t)__shfl_xor((int)v, o, 64));
-  return (uint32_t)__builtin_amdgcn_readfirstlane((int)v);
+  v = min(v, dppu<0xB1>(v));   // quad_perm [1,0,3,2]
+  v = min(v, dppu<0x4E>(v));   // quad_perm [2,3,0,1]
+  v = min(v, dppu<0x141>(v));  // row_half_mirror
+  v = min(v, dppu<0x140>(v));  // row_mirror
+  const uint32_t a = min((uint32_t)__builtin_amdgcn_readlane((int)v, 0),
+                         (uint32_t)__builtin_amdgcn_readlane((int)v, 16));
+  const uint32_t b = min((uint32_t)__builtin_amdgcn_readlane((int)v, 32),
+                         (uint32_t)__builtin_amdgcn_readlane((int)v, 48));
+  return min(a, b);
 }
 __device__ __forceinline__ uint32_t wave_max_u(uint32_t v) {
-#pragma unroll
-  for (int o = 32; o >= 1; o >>= 1) v = max(v, (uint32_t)__shfl_xor((int)v, o, 64));
-  return (uint32_t)__builtin_amdgcn_readfirstlane((int)v);
+  v = max(v, dppu<0xB1>(v));
+  v = max(v, dppu<0x4E>(v));
+  v = max(v, dppu<0x141>(v));
+  v = max(v, dppu<0x140>(v));
+  const uint32_t a = max((uint32_t)__builtin_amdgcn_readlane((int)v, 0),
+                         (uint32_t)__builtin_amdgcn_readlane((int)v, 16));
+  const uint32_t b = max((uint32_t)__builtin_amdgcn_readlane((int)v, 32),
+                         (uint32_t)__builtin_amdgcn_readlane((int)v, 48));
+  return max(a, b);
 }
 // Largest t in [lo, hi] with count_ge(t) >= k, given count_ge(lo) >= k: the
 // k-th largest of the counted values.
@@ -487,7 +572,8 @@ template <int D, int G>
 __device__ void topk_unit(const Ctx &c, int i, int seq, int h, const HeadInfo &hi,
                           const UG &g, const uint16_t *__restrict__ q,
                           int32_t *__restrict__ blk_idx, int32_t *__restrict__ blk_cnt,
-                          int k_cap, TopkSmem &sm, uint32_t *lrows, int lrows_words) {
+                          int k_cap, TopkSmem &sm, uint32_t *lrows, int lrows_words,
+                          unsigned long long *dmask /* LDS, one word per row */) {
   if (threadIdx.x >= 64) return;
   const int lane = threadIdx.x;
   const int n = g.n_blk, rows = cdiv(n, 64);
@@ -510,10 +596,22 @@ __device__ void topk_unit(const Ctx &c, int i, int seq, int h, const HeadInfo &h
   auto uk_ld = [&](int p) -> uint32_t { return p < kTopkUnc ? sm.ukey[p] : ld_dev(&guk[p]); };
   auto uk_st = [&](int p, uint32_t v) { if (p < kTopkUnc) sm.ukey[p] = v; else st_dev(&guk[p], v); };
 
-  // the score tiles' accumulators: error bound and flagged candidates
-  const double eps = (double)__uint_as_float(ld_dev(&c.sc.unit_acc[2 * unit]));
+  // 0. every load in flight together: the score tiles' accumulators (error
+  // bound, flagged candidates), the register rows, the group's query
+  const uint32_t eps_bits = ld_dev(&c.sc.unit_acc[2 * unit]);
+  const uint32_t f_raw = ld_dev(&c.sc.unit_acc[2 * unit + 1]);
+  const int jl = max(n - 1, 0);
+  unsigned long long kv[kTopkRegRows];
+#pragma unroll
+  for (int r = 0; r < kTopkRegRows; ++r) kv[r] = ld_dev(&gkf[min(r * 64 + lane, jl)]);
+  constexpr int QPL = (G * D + 63) / 64;
+  const uint16_t *qg = q + ((size_t)i * c.dm.Hq + (size_t)h * G) * D;
+  uint16_t qv[QPL];
+#pragma unroll
+  for (int r = 0; r < QPL; ++r) qv[r] = qg[min(r * 64 + lane, G * D - 1)];
+
   const bool use_flag = c.dm.maw_beta > 0.0f;
-  const int F = use_flag ? (int)ld_dev(&c.sc.unit_acc[2 * unit + 1]) : 0;
+  const int F = use_flag ? (int)f_raw : 0;
   const int kk = g.kk;
   // every flagged candidate is taken when they do not fill k on their own
   // (the unflagged ones are ranked for the rest); otherwise only the flagged
@@ -521,103 +619,163 @@ __device__ void topk_unit(const Ctx &c, int i, int seq, int h, const HeadInfo &h
   const bool take_flagged = F < kk;
   const uint32_t want = take_flagged ? 0u : 1u;
   const int k_sub = take_flagged ? kk - F : kk;
-  auto word_of = [&](unsigned long long kv) -> uint32_t {
-    const uint32_t key = (uint32_t)kv;
+  auto word_of = [&](unsigned long long x) -> uint32_t {
+    const uint32_t key = (uint32_t)x;
     if (key == 0u) return 0u;
-    const uint32_t fl = use_flag ? (uint32_t)(kv >> 32) & 1u : 0u;
+    const uint32_t fl = use_flag ? (uint32_t)(x >> 32) & 1u : 0u;
     return fl == want ? key : (take_flagged ? 1u : 0u);
   };
-
-  // 0. words (all loads in flight together), the group's query for re-scoring
+  for (int r = lane; r < max(rows, kTopkRegRows); r += 64) dmask[r] = 0ull;
+#pragma unroll
+  for (int r = 0; r < QPL; ++r) {
+    const int x = r * 64 + lane;
+    if (x < G * D) sm.qs[x] = __uint_as_float((uint32_t)qv[r] << 16);
+  }
   uint32_t w[kTopkRegRows];
   uint32_t lo = 0xffffffffu, hi_k = 0u;
-  {
-    const int jl = max(n - 1, 0);
-    unsigned long long kv[kTopkRegRows];
+  uint32_t gm[8] = {0u, 0u, 0u, 0u, 0u, 0u, 0u, 0u};  // maxima of rows r mod 8
 #pragma unroll
-    for (int r = 0; r < kTopkRegRows; ++r) kv[r] = ld_dev(&gkf[min(r * 64 + lane, jl)]);
-    const uint16_t *qg = q + ((size_t)i * c.dm.Hq + (size_t)h * G) * D;
-    constexpr int QPL = (G * D + 63) / 64;
-#pragma unroll
-    for (int r = 0; r < QPL; ++r) {
-      const int x = r * 64 + lane;
-      if (x < G * D) sm.qs[x] = __uint_as_float((uint32_t)qg[x] << 16);
+  for (int r = 0; r < kTopkRegRows; ++r) {
+    w[r] = r * 64 + lane < n ? word_of(kv[r]) : 0u;
+    gm[r & 7] = max(gm[r & 7], w[r]);
+    if (w[r] >= 2u) {
+      lo = min(lo, w[r]);
+      hi_k = max(hi_k, w[r]);
     }
+  }
+  for (int r0 = kTopkRegRows; r0 < rows; r0 += 8) {
+    unsigned long long kb[8];
 #pragma unroll
-    for (int r = 0; r < kTopkRegRows; ++r) {
-      w[r] = r * 64 + lane < n ? word_of(kv[r]) : 0u;
-      if (w[r] >= 2u) {
-        lo = min(lo, w[r]);
-        hi_k = max(hi_k, w[r]);
-      }
-    }
-    for (int r0 = kTopkRegRows; r0 < rows; r0 += 8) {
-      unsigned long long kb[8];
+    for (int x = 0; x < 8; ++x) kb[x] = ld_dev(&gkf[min((r0 + x) * 64 + lane, jl)]);
 #pragma unroll
-      for (int x = 0; x < 8; ++x) kb[x] = ld_dev(&gkf[min((r0 + x) * 64 + lane, jl)]);
+    for (int x = 0; x < 8; ++x) {
+      const int j = (r0 + x) * 64 + lane;
+      if (r0 + x < rows) {
+        const uint32_t v = j < n ? word_of(kb[x]) : 0u;
+        mem_st(j, v);
 #pragma unroll
-      for (int x = 0; x < 8; ++x) {
-        const int j = (r0 + x) * 64 + lane;
-        if (r0 + x < rows) {
-          const uint32_t v = j < n ? word_of(kb[x]) : 0u;
-          mem_st(j, v);
-          if (v >= 2u) {
-            lo = min(lo, v);
-            hi_k = max(hi_k, v);
-          }
+        for (int y = 0; y < 8; ++y)
+          if (((r0 + x) & 7) == y) gm[y] = max(gm[y], v);
+        if (v >= 2u) {
+          lo = min(lo, v);
+          hi_k = max(hi_k, v);
         }
       }
     }
-    wait_vmem();
   }
+  wait_vmem();
   auto count_ge = [&](uint32_t t) -> int {
+    unsigned long long m[kTopkRegRows];
+#pragma unroll
+    for (int r = 0; r < kTopkRegRows; ++r) m[r] = __ballot(w[r] >= t);
     int cnt = 0;
 #pragma unroll
-    for (int r = 0; r < kTopkRegRows; ++r) cnt += count_lanes(w[r] >= t);
+    for (int r = 0; r < kTopkRegRows; ++r) cnt += __popcll(m[r]);
     for (int r = kTopkRegRows; r < rows; ++r) cnt += count_lanes(mem_ld(r * 64 + lane) >= t);
     return cnt;
   };
 
-  // 1-3. thresholds
-  double band_lo = INFINITY, band_hi = INFINITY;
-  uint32_t T2 = 0xffffffffu;
-  int kr2_eq = 0;
-  // classes: 0 out, 1 taken (flag tier or above the band), 2 uncertain
-  auto cls = [&](uint32_t v) -> int {
-    if (v < 2u) return (int)v;
-    const double A = (double)key_to_float(v);
-    return A > band_hi ? 1 : (A >= band_lo ? 2 : 0);
-  };
+  // 1-3. band and decisions.  Uncertain: kb_lo <= w <= kb_hi; in: w > kb_hi.
+  uint32_t kb_lo = 0xffffffffu, kb_hi = 0xffffffffu;
   if (k_sub > 0) {
-    lo = wave_min_u(lo);
-    hi_k = wave_max_u(hi_k);
-    const uint32_t Ta_key = bisect_kth(lo, hi_k, k_sub, count_ge);
-    const double Ta = (double)key_to_float(Ta_key);
-    band_lo = Ta - 2.0 * eps;
-    band_hi = Ta + 2.0 * eps;
+    const double eps = (double)__uint_as_float(eps_bits);
+    uint32_t a = wave_min_u(lo), b = wave_max_u(hi_k);
+    // invariant: #words >= a is cnt_a >= k_sub, #words > b is cnt_b1 < k_sub
+    const int n_cand = g.ns < g.wlo ? cdiv(g.wlo, g.S) - g.ns / g.S : 0;
+    int cnt_a = take_flagged ? n_cand - F : F, cnt_b1 = 0;
+    // lower bound on T_a: the k_sub-th largest of the maxima of the row
+    // groups (r mod NG; distinct blocks' keys), when there are enough of them
+    if (k_sub <= 512) {
+      const int NG = k_sub <= 256 ? 4 : 8;
+      if (NG == 4) {
+#pragma unroll
+        for (int y = 0; y < 4; ++y) gm[y] = max(gm[y], gm[y + 4]), gm[y + 4] = 0u;
+      }
+      int nv = 0;
+      uint32_t glo = 0xffffffffu, ghi = 0u;
+#pragma unroll
+      for (int y = 0; y < 8; ++y) {
+        nv += count_lanes(gm[y] >= 2u);
+        if (gm[y] >= 2u) glo = min(glo, gm[y]);
+        ghi = max(ghi, gm[y]);
+      }
+      if (nv >= k_sub) {
+        uint32_t ga = wave_min_u(glo), gb = wave_max_u(ghi);
+        for (int it = 0; it < 10 && ga < gb; ++it) {
+          const uint32_t mid = ga + ((gb - ga) >> 1) + 1u;
+          int cg = 0;
+#pragma unroll
+          for (int y = 0; y < 4; ++y) cg += count_lanes(gm[y] >= mid);
+          if (NG == 8) {
+#pragma unroll
+            for (int y = 4; y < 8; ++y) cg += count_lanes(gm[y] >= mid);
+          }
+          if (cg >= k_sub) ga = mid; else gb = mid - 1u;
+        }
+        a = ga;
+        cnt_a = count_ge(a);
+      }
+    }
+    auto wide = [&]() {
+      return a < b && (double)key_to_float(b) - (double)key_to_float(a) > eps;
+    };
+    if (wide() && cnt_a - cnt_b1 <= kTopkUnc) {
+      // the words in [a, b], up to 8 per lane; then
+      // count_ge(t) = above + #(x >= t) for a < t <= b + 1
+      const int above = cnt_b1;
+      int base = 0;
+      auto gather = [&](uint32_t v) {
+        const bool in = v >= a && v <= b;
+        const unsigned long long m = __ballot(in);
+        if (in && base + lanes_below(m) < kTopkUnc) sm.ukey[base + lanes_below(m)] = v;
+        base += __popcll(m);
+      };
+#pragma unroll
+      for (int r = 0; r < kTopkRegRows; ++r) gather(w[r]);
+      for (int r = kTopkRegRows; r < rows; ++r) gather(mem_ld(r * 64 + lane));
+      const int xr = cdiv(min(base, kTopkUnc), 64);
+      uint32_t x[kTopkUnc / 64];
+#pragma unroll
+      for (int y = 0; y < kTopkUnc / 64; ++y)
+        x[y] = y * 64 + lane < min(base, kTopkUnc) ? sm.ukey[y * 64 + lane] : 0u;
+      while (wide()) {
+        const uint32_t mid = a + ((b - a) >> 1) + 1u;
+        int cm = above;
+#pragma unroll
+        for (int y = 0; y < kTopkUnc / 64; ++y)
+          if (y < xr) cm += count_lanes(x[y] >= mid);
+        if (cm >= k_sub) { a = mid; cnt_a = cm; } else { b = mid - 1u; cnt_b1 = cm; }
+      }
+    }
+    while (wide()) {
+      const uint32_t mid = a + ((b - a) >> 1) + 1u;  // a < mid <= b
+      const int cm = count_ge(mid);
+      if (cm >= k_sub) { a = mid; cnt_a = cm; } else { b = mid - 1u; cnt_b1 = cm; }
+    }
+    kb_hi = order_key(__double2float_rd((double)key_to_float(b) + 2.0 * eps));
+    kb_lo = order_key(__double2float_ru((double)key_to_float(a) - 2.0 * eps));
     // list the uncertain blocks in index order; count the sure ones
     int n_in = 0, n_unc = 0;
     auto list_row = [&](int j, uint32_t v) {
-      const int k = cls(v);
-      const bool unc = k == 2;
+      const bool unc = v >= kb_lo && v <= kb_hi;
       const unsigned long long m = __ballot(unc);
       if (unc) ul_st(n_unc + lanes_below(m), j);
       n_unc += __popcll(m);
-      n_in += count_lanes(k == 1 && v >= 2u);
+      n_in += count_lanes(v > kb_hi);
     };
 #pragma unroll
     for (int r = 0; r < kTopkRegRows; ++r) list_row(r * 64 + lane, w[r]);
     for (int r = kTopkRegRows; r < rows; ++r) list_row(r * 64 + lane, mem_ld(r * 64 + lane));
     wait_vmem();
     const int kr2 = k_sub - n_in;  // >= 1: T_a's own block is uncertain
-    // exact keys of the uncertain blocks, one lane per (block, head)
-    constexpr int BPR = 64 / G;
+    // exact keys of the uncertain blocks, one lane quad per (block, head)
+    constexpr int BPR = 16 / G;  // blocks per round
     for (int u0 = 0; u0 < n_unc; u0 += BPR) {
-      const int uu = u0 + lane / G, gg = lane % G;
-      double U = 0.0;
-      if (lane < BPR * G && uu < n_unc)
-        U = exact_head_score<D>(c, seq, hi, ul_ld(uu), sm.qs + gg * D);
-      sm.ud[lane] = U;
+      const int pair = lane >> 2, uu = u0 + pair / G, gg = pair % G;
+      const bool on = pair < BPR * G && uu < n_unc;
+      const double U = exact_score_quad<D>(c, seq, hi, on ? ul_ld(uu) : 0,
+                                           sm.qs + (on ? gg : 0) * D, on);
+      if ((lane & 3) == 0) sm.ud[pair] = U;
       if (lane < BPR && u0 + lane < n_unc) {
         double best = sm.ud[lane * G];
         for (int x = 1; x < G; ++x) best = sm.ud[lane * G + x] > best ? sm.ud[lane * G + x] : best;
@@ -625,7 +783,20 @@ __device__ void topk_unit(const Ctx &c, int i, int seq, int h, const HeadInfo &h
       }
     }
     wait_vmem();
-    // kr2-th largest exact key of the list
+    // the kr2 largest exact keys of the list, ties to the lower index
+    if (n_unc <= 64) {
+      // rank of each entry: larger keys, then equal keys listed earlier
+      const uint32_t e = lane < n_unc ? sm.ukey[lane] : 0u;
+      int rank = 0;
+      for (int p = 0; p < n_unc; ++p) {
+        const uint32_t ep = (uint32_t)__builtin_amdgcn_readlane((int)e, p);
+        rank += (ep > e || (ep == e && p < lane)) ? 1 : 0;
+      }
+      if (lane < n_unc && rank < kr2) {
+        const int j = sm.ulist[lane];
+        atomicOr(&dmask[j >> 6], 1ull << (j & 63));
+      }
+    } else {
     const int urows = cdiv(n_unc, 64);
     const uint32_t e0 = lane < n_unc ? uk_ld(lane) : 0u;
     uint32_t lo2 = lane < n_unc ? e0 : 0xffffffffu, hi2 = e0;
@@ -647,32 +818,42 @@ __device__ void topk_unit(const Ctx &c, int i, int seq, int h, const HeadInfo &h
       }
       return cnt;
     };
-    T2 = bisect_kth(lo2, hi2, kr2, ucount_ge);
-    kr2_eq = kr2 - (T2 == 0xffffffffu ? 0 : ucount_ge(T2 + 1u));
+    const uint32_t T2 = bisect_kth(lo2, hi2, kr2, ucount_ge);
+    const int kr2_eq = kr2 - (T2 == 0xffffffffu ? 0 : ucount_ge(T2 + 1u));
+    int eqb = 0;
+    for (int r = 0; r < urows; ++r) {
+      const int p = r * 64 + lane;
+      const uint32_t e = r == 0 ? e0 : (p < n_unc ? uk_ld(p) : 0u);
+      const bool eq = p < n_unc && e == T2;
+      const unsigned long long me = __ballot(eq);
+      const bool take = (p < n_unc && e > T2) || (eq && eqb + lanes_below(me) < kr2_eq);
+      eqb += __popcll(me);
+      if (take) {
+        const int j = ul_ld(p);
+        atomicOr(&dmask[j >> 6], 1ull << (j & 63));
+      }
+    }
+    }
   }
 
   // 4. ordered compaction
   int32_t *dst = blk_idx + ((size_t)i * c.dm.Hkv + h) * k_cap;
-  int ub = 0, eb = 0, ob = 0;
-  auto emit_row = [&](int j, uint32_t v) {
-    const int k = cls(v);
-    const bool unc = k == 2;
-    const unsigned long long mu = __ballot(unc);
-    const uint32_t e = unc ? uk_ld(ub + lanes_below(mu)) : 0u;
-    ub += __popcll(mu);
-    const bool eq = unc && e == T2;
-    const unsigned long long me = __ballot(eq);
-    const bool ch = k == 1 || (unc && e > T2) || (eq && eb + lanes_below(me) < kr2_eq);
-    eb += __popcll(me);
+  int ob = 0;
+  auto emit_row = [&](int r, uint32_t v, unsigned long long dm) {
+    const bool ch = v == 1u || v > kb_hi || ((dm >> lane) & 1ull);
     const unsigned long long mc = __ballot(ch);
     const int o = ob + lanes_below(mc);
-    if (ch && o < k_cap) dst[o] = j;
+    if (ch && o < k_cap) dst[o] = r * 64 + lane;
     ob += __popcll(mc);
   };
+  {
+    unsigned long long dm[kTopkRegRows];
 #pragma unroll
-  for (int r = 0; r < kTopkRegRows; ++r)
-    if (r < rows) emit_row(r * 64 + lane, w[r]);
-  for (int r = kTopkRegRows; r < rows; ++r) emit_row(r * 64 + lane, mem_ld(r * 64 + lane));
+    for (int r = 0; r < kTopkRegRows; ++r) dm[r] = dmask[r];
+#pragma unroll
+    for (int r = 0; r < kTopkRegRows; ++r) emit_row(r, w[r], dm[r]);
+  }
+  for (int r = kTopkRegRows; r < rows; ++r) emit_row(r, mem_ld(r * 64 + lane), dmask[r]);
   if (lane == 0) {
     blk_cnt[(size_t)i * c.dm.Hkv + h] = kk;
     st_dev(&c.sc.unit_acc[2 * unit], 0u);  // cleared for the next step
@@ -1135,7 +1316,8 @@ __global__ __launch_bounds__(256) void k_select(Ctx c, SeqBatch b, int tiles_x,
                                                 float *__restrict__ o_part,
                                                 float *__restrict__ lse_part, int p_cap,
                                                 int lrows_words) {
-  // dynamic LDS: max(AttSmem, TopkSmem + lrows_words top-k words)
+  // dynamic LDS: max(AttSmem, TopkSmem + lrows_words top-k words + one
+  // 64-bit mask per top-k row)
   extern __shared__ __align__(16) unsigned char smem_raw[];
   TopkSmem &smem_topk = *reinterpret_cast<TopkSmem *>(smem_raw);
   AttSmem<D, G> &smem_att = *reinterpret_cast<AttSmem<D, G> *>(smem_raw);
@@ -1152,8 +1334,9 @@ __global__ __launch_bounds__(256) void k_select(Ctx c, SeqBatch b, int tiles_x,
     // the last tile of the unit to arrive runs its top-k (one wave)
     uint32_t *ctr = &c.sc.arrive[((size_t)seq * c.dm.Hkv + h) * 2];
     if (!arrive_last(ctr, (unsigned)n_tiles, &smem_topk.last)) return;
-    topk_unit<D, G>(c, i, seq, h, hi, g, q, blk_idx, blk_cnt, k_cap, smem_topk,
-                    reinterpret_cast<uint32_t *>(smem_raw + sizeof(TopkSmem)), lrows_words);
+    uint32_t *lrows = reinterpret_cast<uint32_t *>(smem_raw + sizeof(TopkSmem));
+    topk_unit<D, G>(c, i, seq, h, hi, g, q, blk_idx, blk_cnt, k_cap, smem_topk, lrows,
+                    lrows_words, reinterpret_cast<unsigned long long *>(lrows + lrows_words));
     if (threadIdx.x == 0) st_dev(ctr, 0u);
     return;
   }
@@ -1304,12 +1487,14 @@ hipError_t launch_select(const Ctx &c, const SeqBatch &b, int max_blocks,
   const int grid = tiles_x * c.dm.Hkv * b.n + dchunks_x * c.dm.Hkv * b.n;
   // top-k words past the register rows go to LDS while the launch stays
   // within 64 KiB of LDS per workgroup, else to the global scratch
-  const int extra = max(0, (max_blocks + 63) / 64 - kTopkRegRows) * 64;
-  const size_t topk_bytes = sizeof(TopkSmem) + sizeof(uint32_t) * (size_t)extra;
-  const int lrows_words = topk_bytes <= 65536 ? extra : 0;
+  const int rows = max(1, (max_blocks + 63) / 64);
+  const int extra = max(0, rows - kTopkRegRows) * 64;
+  const size_t fixed = sizeof(TopkSmem) + sizeof(unsigned long long) * (size_t)max(rows, kTopkRegRows);
+  if (fixed > 65536) return hipErrorInvalidValue;
+  const int lrows_words = fixed + sizeof(uint32_t) * (size_t)extra <= 65536 ? extra : 0;
   SD_DISPATCH_DG(c.dm.d, c.dm.G, {
     const size_t smem = std::max(sizeof(AttSmem<D_, G_>),
-                                 sizeof(TopkSmem) + sizeof(uint32_t) * (size_t)lrows_words);
+                                 fixed + sizeof(uint32_t) * (size_t)lrows_words);
     hipLaunchKernelGGL((k_select<D_, G_>), dim3(grid), dim3(256), smem, st, c, b, tiles_x,
                        max(dchunks_x, 1), blk_idx, blk_cnt, k_cap, q, dense_o_part,
                        dense_lse_part, p_cap, lrows_words);
