@@ -3,16 +3,22 @@ MI355X, on the Llama-3-8B-shaped 32K workload (B=8, 32 query / 8 KV heads,
 d=128, N=32768, block 32, budget 5% of tokens, 4 sinks + 512 recent tokens).
 
 One step = the whole hot path for one layer of one decode step: append the
-step's token to every sequence, score + top-k select, split-K attention,
-LSE fusion + MAW update.  Steps rotate over --layers independent layer
-instances (8 x 1.07 GB of KV) so the 105 MB per-step working set is not
-served from the 256 MB last-level cache.  Inputs are resident in HBM when the
-timed region starts.
+step's token to every sequence (k_prep), then score + top-k select, split-K
+attention over dense and selected chunks, LSE fusion and the MAW update
+(k_step, one launch).  Steps rotate over --layers independent layer instances
+(8 x 1.07 GB of KV) so that the ~105 MB per-step working set is not served
+from the 256 MB last-level cache.  Inputs are resident in HBM when the timed
+region starts.
 
 Prints ONE JSON line (rank 0, N=1).  The `roofline` object covers the
-dominant kernel (the split-K attention), timed live with HIP events on the
-library's stream; `cpu_baseline` times the CPU oracle on a bounded sample of
-the same workload.
+dominant kernel, k_step: its algorithmic bytes per launch over its mean
+duration, from HIP events on the library's stream around 64 back-to-back
+step launches without append (k_step alone, same workload, rotating over the
+layer instances); `traffic` is the HBM traffic per
+launch from the committed FETCH_SIZE/WRITE_SIZE counter summary, null once the
+kernel sources differ from those it was taken on.  `cpu_baseline` times the
+CPU oracle on a bounded sample of the same workload.  --fused 0 runs the four separate ABI calls instead (same
+results, for comparison).
 """
 from __future__ import annotations
 
@@ -31,6 +37,21 @@ import numpy as np  # noqa: E402
 HBM_PEAK_GBS = 8000.0
 
 
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "k_step_llama32k_traffic.json")
+KERNEL_SOURCES = ["block_sparse_top_score_amd/csrc/sd_kernels.hip",
+                  "block_sparse_top_score_amd/csrc/sd_internal.h",
+                  "block_sparse_top_score_amd/csrc/sd_runtime.hip"]
+
+
+def sources_sha256():
+    import hashlib
+    h = hashlib.sha256()
+    for f in KERNEL_SOURCES:
+        with open(os.path.join(ROOT, f), "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()
+
+
 def parse():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -42,7 +63,73 @@ def parse():
     ap.add_argument("--cpu-baseline", type=int, default=1)
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
     ap.add_argument("--trials", type=int, default=3)
+    ap.add_argument("--copy-calibration", action="store_true",
+                    help="run a plain 1 GiB device copy (counter calibration) and exit")
+    ap.add_argument("--traffic-summary", nargs=4, metavar=("FETCH", "WRITE", "CAL_FETCH", "CAL_WRITE"),
+                    help="rocprofv3 --pmc csv dirs of k_step and of the copy; write the "
+                         "per-launch traffic file and exit")
     return ap.parse_args()
+
+
+def copy_calibration(nbytes=1 << 30, reps=4):
+    """A plain device copy of known size, for scaling FETCH_SIZE/WRITE_SIZE."""
+    import torch
+    x = torch.ones(nbytes // 4, dtype=torch.float32, device="cuda")
+    y = torch.empty_like(x)
+    torch.cuda.synchronize()
+    for _ in range(reps):
+        y.copy_(x)
+    torch.cuda.synchronize()
+    print(json.dumps({"copy_bytes": nbytes, "reps": reps}), flush=True)
+
+
+def _pmc_avg_kib(d, name_part):
+    """Mean counter value (KiB) per dispatch of kernels whose name contains
+    name_part, from a rocprofv3 --pmc csv output directory."""
+    import csv
+    import glob
+    vals = {}
+    for f in glob.glob(os.path.join(d, "**", "*counter_collection.csv"), recursive=True):
+        with open(f) as fh:
+            for row in csv.DictReader(fh):
+                if name_part in row.get("Kernel_Name", ""):
+                    key = (row.get("Dispatch_Id"), row.get("Counter_Name"))
+                    vals[key] = vals.get(key, 0.0) + float(row["Counter_Value"])
+    if not vals:
+        raise SystemExit("no %s dispatches in %s" % (name_part, d))
+    return sum(vals.values()) / len(vals), len(vals)
+
+
+def traffic_summary(fetch_dir, write_dir, cal_fetch_dir, cal_write_dir):
+    f_kib, nf = _pmc_avg_kib(fetch_dir, "k_step")
+    w_kib, nw = _pmc_avg_kib(write_dir, "k_step")
+    cf_kib, ncf = _pmc_avg_kib(cal_fetch_dir, "copy")
+    cw_kib, ncw = _pmc_avg_kib(cal_write_dir, "copy")
+    copy_bytes = 1 << 30
+    f_scale = copy_bytes / (cf_kib * 1024.0)
+    w_scale = copy_bytes / (cw_kib * 1024.0)
+    out = {"kernel": "k_step (llama32k)",
+           "fetch_kib_per_dispatch": f_kib, "write_kib_per_dispatch": w_kib,
+           "dispatches": [nf, nw],
+           "copy_fetch_kib": cf_kib, "copy_write_kib": cw_kib, "copy_bytes": copy_bytes,
+           "fetch_scale": f_scale, "write_scale": w_scale,
+           "traffic_bytes_per_launch": f_kib * 1024.0 * f_scale + w_kib * 1024.0 * w_scale,
+           "source_sha256": sources_sha256()}
+    print(json.dumps(out), flush=True)
+    return out
+
+
+def measured_traffic():
+    """Per-launch HBM bytes of k_step from the committed counter summary, or
+    None when the kernel sources changed since it was taken."""
+    try:
+        with open(TRAFFIC_FILE) as fh:
+            t = json.load(fh)
+    except (OSError, ValueError):
+        return None
+    if t.get("source_sha256") != sources_sha256():
+        return None
+    return t.get("traffic_bytes_per_launch")
 
 
 def algorithmic_bytes(w, N, blk_cnt, blk_idx, with_maw=True):
@@ -71,6 +158,12 @@ def algorithmic_bytes(w, N, blk_cnt, blk_idx, with_maw=True):
 
 def main():
     args = parse()
+    if args.traffic_summary:
+        traffic_summary(*args.traffic_summary)
+        return
+    if args.copy_calibration:
+        copy_calibration()
+        return
     if args.gpus != 1:
         print("bench.py measures one GPU only (this build has no multi-GPU path); "
               "run with --gpus 1", file=sys.stderr)
@@ -112,29 +205,19 @@ def main():
     v_new = torch.randn(64, w.B, w.Hkv, w.d, generator=g, device=dev).to(torch.bfloat16)
     bufs = eng.alloc_step(w.B, device=dev)
 
-    def step(s, ev=None):
+    def step(s):
         layer = s % L
         kn, vn = k_new[s % 64], v_new[s % 64]
-        if args.fused and ev is None:
+        if args.fused:
             eng.decode_step(layer, seqs, qs[layer], bufs["blk_idx"], bufs["blk_cnt"],
                             bufs["o_part"], bufs["lse_part"], bufs["o"], bufs["lse"],
                             k_new=kn, v_new=vn)
             return
-        if ev is not None:
-            ev[0].record(stream)
         eng.append_kv(layer, seqs, [1] * w.B, kn, vn)
-        if ev is not None:
-            ev[1].record(stream)
         eng.select_topk(layer, seqs, qs[layer], bufs["blk_idx"], bufs["blk_cnt"])
-        if ev is not None:
-            ev[2].record(stream)
         eng.sparse_attend(layer, seqs, qs[layer], bufs["blk_idx"], bufs["blk_cnt"],
                           bufs["o_part"], bufs["lse_part"])
-        if ev is not None:
-            ev[3].record(stream)
         eng.fuse_lse(layer, seqs, bufs["o_part"], bufs["lse_part"], bufs["o"], bufs["lse"])
-        if ev is not None:
-            ev[4].record(stream)
 
     s_global = 0
     for _ in range(args.warmup):
@@ -157,17 +240,20 @@ def main():
         trial_ms.append(e0.elapsed_time(e1) / args.steps)
     ms = float(np.median(trial_ms))
 
-    # per-call timing with events on the library stream (same workload)
-    n_inst = max(16, min(args.steps, 64))
-    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(5)] for _ in range(n_inst)]
-    for i in range(n_inst):
-        step(s_global, evs[i])
-        s_global += 1
+    # k_step timed alone: n_inst back-to-back steps without append (so k_step
+    # is the only kernel) between two HIP events on the library's stream
+    n_inst = 64
+    ea = torch.cuda.Event(enable_timing=True)
+    eb = torch.cuda.Event(enable_timing=True)
     torch.cuda.synchronize()
-    t_app = np.mean([e[0].elapsed_time(e[1]) for e in evs])
-    t_sel = np.mean([e[1].elapsed_time(e[2]) for e in evs])
-    t_att = np.mean([e[2].elapsed_time(e[3]) for e in evs])
-    t_fus = np.mean([e[3].elapsed_time(e[4]) for e in evs])
+    ea.record(stream)
+    for i in range(n_inst):
+        layer = i % L  # rotate layers: the working set stays out of the LLC
+        eng.decode_step(layer, seqs, qs[layer], bufs["blk_idx"], bufs["blk_cnt"],
+                        bufs["o_part"], bufs["lse_part"], bufs["o"], bufs["lse"])
+    eb.record(stream)
+    torch.cuda.synchronize()
+    t_step = ea.elapsed_time(eb) / n_inst
 
     cnt = bufs["blk_cnt"].cpu().numpy()
     idx = bufs["blk_idx"].cpu().numpy()
@@ -176,7 +262,8 @@ def main():
     qheads = w.B * w.Hq
     value = qheads / (ms * 1e-3)
     step_gbs = ab["total"] / (ms * 1e-3) / 1e9
-    att_gbs = (ab["attend"] + w.B * w.Hq * 2 * w.d) / (t_att * 1e-3) / 1e9
+    kstep_bytes = ab["total"]  # k_step moves every algorithmic byte of the step
+    kstep_gbs = kstep_bytes / (t_step * 1e-3) / 1e9
 
     out = {
         "metric": "sparse-decode attn query-heads/s at Llama-3-8B 32K, 5% budget; % HBM peak",
@@ -198,11 +285,10 @@ def main():
         "step_hbm": {"algorithmic_bytes": ab["total"], "achieved_GBs": step_gbs,
                      "frac_of_8TBs": step_gbs / HBM_PEAK_GBS,
                      "breakdown_bytes": {k: ab[k] for k in ("summaries", "attend", "maw", "q_o_lse")}},
-        "per_call_ms": {"append_kv": t_app, "select_topk": t_sel, "sparse_attend": t_att,
-                        "fuse_lse": t_fus},
-        "roofline": {"kernel": "k_attend (sparse_attend)", "bound": "hbm",
-                     "achieved": att_gbs, "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                     "frac": att_gbs / HBM_PEAK_GBS, "traffic": None},
+        "kernel_ms": {"k_step": t_step, "timed_launches": n_inst},
+        "roofline": {"kernel": "k_step", "bound": "hbm", "achieved": kstep_gbs,
+                     "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": kstep_gbs / HBM_PEAK_GBS,
+                     "traffic": measured_traffic(), "algorithmic_bytes_per_launch": kstep_bytes},
         "trials_ms": trial_ms,
         "setup_s": setup_s,
     }
@@ -236,7 +322,7 @@ def cpu_baseline(w, K, V, q, budget_s):
     done = 0
     t0 = time.time()
     with cf.ThreadPoolExecutor(threads) as ex:
-        while time.time() - t0 < budget_s and done < 4 * len(units):
+        while time.time() - t0 < budget_s:
             batch = units[:]
             done += sum(ex.map(run, batch))
     dt = time.time() - t0

@@ -85,6 +85,8 @@ struct Scratch {
   int32_t *usel;     // [max_seqs][Hkv][kcap] selected block ids (attend copy)
   int32_t *ucnt;     // [max_seqs][Hkv] selected block count (attend copy)
   uint32_t *arrive;  // [max_seqs][Hkv][2] last-arriver counters (kept at 0)
+  uint32_t *ready;   // [max_seqs][Hkv] step number of the unit's published selection
+  uint32_t *err;     // [1] nonzero once a step kernel's wait ran out of time
 };
 
 // Everything a kernel needs about the context (passed by value).
@@ -109,14 +111,19 @@ hipError_t launch_select(const Ctx &c, const SeqBatch &b, int max_blocks,
                          int32_t k_cap, int dchunks_x, float *dense_o_part,
                          float *dense_lse_part, int32_t p_cap, hipStream_t st);
 
-// fused = false: one workgroup per partial slot (dense chunks at [0, pd),
-// selected chunks after; unused slots emptied).  fused = true: selected
-// chunks only; the last workgroup of each unit fuses and updates MAW.
+// One workgroup per partial slot (dense chunks at [0, pd), selected chunks
+// after; unused slots emptied).
 hipError_t launch_attend(const Ctx &c, const SeqBatch &b, const uint16_t *q,
                          const int32_t *blk_idx, const int32_t *blk_cnt,
                          int32_t k_cap, float *o_part, float *lse_part,
-                         int32_t p_cap, bool fused, int max_sel_chunks, float *o,
-                         float *lse, hipStream_t st);
+                         int32_t p_cap, hipStream_t st);
+
+// The whole step in one launch: scoring, top-k, dense and selected chunks,
+// fusion and MAW (epoch: a nonzero number that differs between launches).
+hipError_t launch_step(const Ctx &c, const SeqBatch &b, int max_blocks, const uint16_t *q,
+                       int32_t *blk_idx, int32_t *blk_cnt, int32_t k_cap, int dchunks_x,
+                       int schunks_x, float *o_part, float *lse_part, int32_t p_cap,
+                       float *o, float *lse, uint32_t epoch, hipStream_t st);
 
 // Fusion of the partials: with_maw = slots and MAW from the attend scratch
 // (layer call); otherwise every slot of p_cap is fused (layer -1).

@@ -79,6 +79,25 @@ __device__ __forceinline__ bool arrive_last(uint32_t *counter, unsigned expected
   return *flag != 0;
 }
 
+// Arrival on a unit's fusion counter.  The fusion waits for the unit's dense
+// chunks, its selected chunks and the top-k itself (nd + ns + 1 arrivals);
+// ns is known from the published count once the top-k has arrived, and before
+// that the count cannot reach nd + 1, so a stale count is never used.
+__device__ __forceinline__ bool arrive_fuse(uint32_t *counter, int nd, const int32_t *ucnt,
+                                            int CB, int *flag) {
+  wait_vmem();
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    const int prev = (int)__hip_atomic_fetch_add(counter, 1u, __ATOMIC_RELAXED,
+                                                 __HIP_MEMORY_SCOPE_AGENT);
+    bool last = false;
+    if (prev + 1 >= nd + 1) last = prev + 1 == nd + cdiv(ld_dev(ucnt), CB) + 1;
+    *flag = last;
+  }
+  __syncthreads();
+  return *flag != 0;
+}
+
 __device__ __forceinline__ float wave_max(float x) {
 #pragma unroll
   for (int o = 32; o >= 1; o >>= 1) x = fmaxf(x, __shfl_xor(x, o, 64));
@@ -843,7 +862,7 @@ __device__ void topk_unit(const Ctx &c, int i, int seq, int h, const HeadInfo &h
     const bool ch = v == 1u || v > kb_hi || ((dm >> lane) & 1ull);
     const unsigned long long mc = __ballot(ch);
     const int o = ob + lanes_below(mc);
-    if (ch && o < k_cap) dst[o] = r * 64 + lane;
+    if (ch && o < k_cap) st_dev(&dst[o], r * 64 + lane);
     ob += __popcll(mc);
   };
   {
@@ -855,7 +874,7 @@ __device__ void topk_unit(const Ctx &c, int i, int seq, int h, const HeadInfo &h
   }
   for (int r = kTopkRegRows; r < rows; ++r) emit_row(r, mem_ld(r * 64 + lane), dmask[r]);
   if (lane == 0) {
-    blk_cnt[(size_t)i * c.dm.Hkv + h] = kk;
+    st_dev(&blk_cnt[(size_t)i * c.dm.Hkv + h], kk);
     st_dev(&c.sc.unit_acc[2 * unit], 0u);  // cleared for the next step
     st_dev(&c.sc.unit_acc[2 * unit + 1], 0u);
   }
@@ -953,7 +972,7 @@ __device__ void attend_chunk(const Ctx &c, int i, int seq, int h, const HeadInfo
     if (p < npg) {
       const int jj = p / PPB, pp = p - jj * PPB;
       const int j = chunk * CB + jj;
-      const int blk = dense ? dense_block(g, j) : sel[j];
+      const int blk = dense ? dense_block(g, j) : ld_dev(&sel[j]);
       const unsigned long long m = block_mask(g, blk, dense);
       if (!dense && pp == 0) st_dev(&c.sc.usel[((size_t)seq * c.dm.Hkv + h) * c.dm.kcap + j], blk);
       my_mask = (int)((m >> (pp * kPage)) & 0xffffull);
@@ -1376,39 +1395,92 @@ __global__ __launch_bounds__(256) void k_attend_slots(Ctx c, SeqBatch b,
   }
 }
 
-// attend, fused form: selected chunks; the last workgroup of each unit fuses
-// the unit's partials (dense ones from the select launch) and updates MAW.
+// One decode step in one launch.  Workgroups by index: score tiles (the last
+// of a unit runs its top-k and publishes the selection), dense chunks, then
+// selected chunks, which wait for their unit's selection.  The last of a
+// unit's dense chunks, selected chunks and top-k to finish fuses the partials
+// and updates MAW.  Workgroups start in index order on each XCD, so every
+// score tile has started before any selected chunk waits, and no wait is on a
+// workgroup that cannot start; each wait is also bounded in time (after
+// kWaitTicks it gives up and raises the error flag).
+constexpr unsigned long long kWaitTicks = 20000000ull;  // 0.2 s of the 100 MHz clock
+
 template <int D, int G>
-__global__ __launch_bounds__(256) void k_attend_fuse(Ctx c, SeqBatch b, int chunks_x,
-                                                     const uint16_t *__restrict__ q,
-                                                     const int32_t *__restrict__ blk_idx,
-                                                     const int32_t *__restrict__ blk_cnt,
-                                                     int k_cap, float *__restrict__ o_part,
-                                                     float *__restrict__ lse_part, int p_cap,
-                                                     float *__restrict__ o,
-                                                     float *__restrict__ lse) {
-  constexpr size_t kBytes = sizeof(FuseSmem<G>) > sizeof(AttSmem<D, G>) ? sizeof(FuseSmem<G>)
-                                                                         : sizeof(AttSmem<D, G>);
-  __shared__ __align__(16) unsigned char smem_raw[kBytes];
-  FuseSmem<G> &smem_fuse = *reinterpret_cast<FuseSmem<G> *>(smem_raw);
+__global__ __launch_bounds__(256) void k_step(Ctx c, SeqBatch b, int tiles_x, int dchunks_x,
+                                              int schunks_x, int32_t *__restrict__ blk_idx,
+                                              int32_t *__restrict__ blk_cnt, int k_cap,
+                                              const uint16_t *__restrict__ q,
+                                              float *__restrict__ o_part,
+                                              float *__restrict__ lse_part, int p_cap,
+                                              float *__restrict__ o, float *__restrict__ lse,
+                                              int lrows_words, uint32_t epoch) {
+  // dynamic LDS: max(TopkSmem + top-k words and row masks, AttSmem, FuseSmem)
+  extern __shared__ __align__(16) unsigned char smem_raw[];
+  __shared__ int s_flag;
+  TopkSmem &smem_topk = *reinterpret_cast<TopkSmem *>(smem_raw);
   AttSmem<D, G> &smem_att = *reinterpret_cast<AttSmem<D, G> *>(smem_raw);
-  const int wg = blockIdx.x;
-  const int ch = wg % chunks_x, h = (wg / chunks_x) % c.dm.Hkv, i = wg / (chunks_x * c.dm.Hkv);
+  FuseSmem<G> &smem_fuse = *reinterpret_cast<FuseSmem<G> *>(smem_raw);
+  const int units = c.dm.Hkv * b.n;
+  const int n_score = tiles_x * units, n_dense = dchunks_x * units;
+  int wg = blockIdx.x, role, idx, u;
+  if (wg < n_score) {
+    role = 0; idx = wg % tiles_x; u = wg / tiles_x;
+  } else if (wg < n_score + n_dense) {
+    wg -= n_score; role = 1; idx = wg / units; u = wg % units;  // chunk-major
+  } else {
+    wg -= n_score + n_dense; role = 2; idx = wg / units; u = wg % units;
+  }
+  const int h = u % c.dm.Hkv, i = u / c.dm.Hkv;
   const HeadInfo hi = c.heads[h];
   const int seq = b.seq[i];
   const UG g = unit_geom(b.len[i], hi, c.dm);
-  const int cnt = min(min(max(blk_cnt[(size_t)i * c.dm.Hkv + h], 0), k_cap), hi.kcap);
-  const int n_active = max(1, cdiv(cnt, g.CB));
-  if (ch >= n_active) return;
-  if (ch == 0 && threadIdx.x == 0) st_dev(&c.sc.ucnt[(size_t)seq * c.dm.Hkv + h], cnt);
-  const int32_t *sel = blk_idx + ((size_t)i * c.dm.Hkv + h) * k_cap;
-  if (ch < cdiv(cnt, g.CB))
-    attend_chunk<D, G>(c, i, seq, h, hi, g, false, ch, cnt, sel, q, o_part, lse_part, p_cap,
+  const size_t unit = (size_t)seq * c.dm.Hkv + h;
+  const int nd = cdiv(g.n_dt, g.CB);
+  int32_t *sel = blk_idx + ((size_t)i * c.dm.Hkv + h) * k_cap;
+  if (role == 0) {
+    const int n_tiles = max(1, cdiv(g.n_blk, kScoreTile));
+    if (idx >= n_tiles) return;
+    score_tile<D, G>(c, i, seq, h, hi, g, idx, q, smem_topk.red);
+    uint32_t *ctr = &c.sc.arrive[unit * 2];
+    if (!arrive_last(ctr, (unsigned)n_tiles, &s_flag)) return;
+    uint32_t *lrows = reinterpret_cast<uint32_t *>(smem_raw + sizeof(TopkSmem));
+    topk_unit<D, G>(c, i, seq, h, hi, g, q, blk_idx, blk_cnt, k_cap, smem_topk, lrows,
+                    lrows_words, reinterpret_cast<unsigned long long *>(lrows + lrows_words));
+    if (threadIdx.x == 0) {
+      st_dev(ctr, 0u);
+      st_dev(&c.sc.ucnt[unit], min(min(g.kk, k_cap), hi.kcap));
+      wait_vmem();  // the selection and its count first
+      st_dev(&c.sc.ready[unit], epoch);
+    }
+  } else if (role == 1) {
+    if (idx >= nd) return;
+    attend_chunk<D, G>(c, i, seq, h, hi, g, true, idx, 0, nullptr, q, o_part, lse_part, p_cap,
                        smem_att);
-  uint32_t *ctr = &c.sc.arrive[((size_t)seq * c.dm.Hkv + h) * 2 + 1];
-  if (!arrive_last(ctr, (unsigned)n_active, &smem_fuse.last)) return;
+  } else {
+    if (threadIdx.x == 0) {
+      int ok = 1;
+      const unsigned long long t0 = wall_clock64();
+      while (ld_dev(&c.sc.ready[unit]) != epoch) {
+        if (wall_clock64() - t0 > kWaitTicks) {
+          ok = 0;
+          st_dev(&c.sc.err[0], 1u);
+          break;
+        }
+        __builtin_amdgcn_s_sleep(8);
+      }
+      s_flag = ok;
+    }
+    __syncthreads();
+    if (!s_flag) return;
+    const int cnt = min(ld_dev(&c.sc.ucnt[unit]), hi.kcap);
+    if (idx >= cdiv(cnt, g.CB)) return;
+    attend_chunk<D, G>(c, i, seq, h, hi, g, false, idx, cnt, sel, q, o_part, lse_part, p_cap,
+                       smem_att);
+  }
+  uint32_t *fctr = &c.sc.arrive[unit * 2 + 1];
+  if (!arrive_fuse(fctr, nd, &c.sc.ucnt[unit], g.CB, &s_flag)) return;
   fuse_unit<D, G>(c, i, seq, h, hi, g, true, false, o_part, lse_part, p_cap, o, lse, smem_fuse);
-  if (threadIdx.x == 0) st_dev(ctr, 0u);
+  if (threadIdx.x == 0) st_dev(fctr, 0u);
 }
 
 template <int D, int G>
@@ -1477,6 +1549,17 @@ hipError_t launch_append(const Ctx &c, const AppendBatch &b, int max_new,
   return hipGetLastError();
 }
 
+// top-k words past the register rows go to LDS while the launch stays within
+// 64 KiB of LDS per workgroup, else to the global scratch
+static int topk_lds(int max_blocks, size_t *bytes) {
+  const int rows = max(1, (max_blocks + 63) / 64);
+  const int extra = max(0, rows - kTopkRegRows) * 64;
+  const size_t fixed = sizeof(TopkSmem) + sizeof(unsigned long long) * (size_t)max(rows, kTopkRegRows);
+  const int lrows_words = fixed + sizeof(uint32_t) * (size_t)extra <= 65536 ? extra : 0;
+  *bytes = fixed + sizeof(uint32_t) * (size_t)lrows_words;
+  return lrows_words;
+}
+
 hipError_t launch_select(const Ctx &c, const SeqBatch &b, int max_blocks,
                          const uint16_t *q, int32_t *blk_idx, int32_t *blk_cnt,
                          int32_t k_cap, int dchunks_x, float *dense_o_part,
@@ -1485,16 +1568,11 @@ hipError_t launch_select(const Ctx &c, const SeqBatch &b, int max_blocks,
   const int tiles_x = max(1, (max_blocks + kScoreTile - 1) / kScoreTile);
   if (!dense_o_part) dchunks_x = 0;
   const int grid = tiles_x * c.dm.Hkv * b.n + dchunks_x * c.dm.Hkv * b.n;
-  // top-k words past the register rows go to LDS while the launch stays
-  // within 64 KiB of LDS per workgroup, else to the global scratch
-  const int rows = max(1, (max_blocks + 63) / 64);
-  const int extra = max(0, rows - kTopkRegRows) * 64;
-  const size_t fixed = sizeof(TopkSmem) + sizeof(unsigned long long) * (size_t)max(rows, kTopkRegRows);
-  if (fixed > 65536) return hipErrorInvalidValue;
-  const int lrows_words = fixed + sizeof(uint32_t) * (size_t)extra <= 65536 ? extra : 0;
+  size_t topk_bytes;
+  const int lrows_words = topk_lds(max_blocks, &topk_bytes);
+  if (topk_bytes > 65536) return hipErrorInvalidValue;
   SD_DISPATCH_DG(c.dm.d, c.dm.G, {
-    const size_t smem = std::max(sizeof(AttSmem<D_, G_>),
-                                 fixed + sizeof(uint32_t) * (size_t)lrows_words);
+    const size_t smem = std::max(sizeof(AttSmem<D_, G_>), topk_bytes);
     hipLaunchKernelGGL((k_select<D_, G_>), dim3(grid), dim3(256), smem, st, c, b, tiles_x,
                        max(dchunks_x, 1), blk_idx, blk_cnt, k_cap, q, dense_o_part,
                        dense_lse_part, p_cap, lrows_words);
@@ -1505,22 +1583,33 @@ hipError_t launch_select(const Ctx &c, const SeqBatch &b, int max_blocks,
 hipError_t launch_attend(const Ctx &c, const SeqBatch &b, const uint16_t *q,
                          const int32_t *blk_idx, const int32_t *blk_cnt,
                          int32_t k_cap, float *o_part, float *lse_part,
-                         int32_t p_cap, bool fused, int max_sel_chunks, float *o,
-                         float *lse, hipStream_t st) {
+                         int32_t p_cap, hipStream_t st) {
   if (b.n <= 0) return hipSuccess;
-  if (!fused) {
-    dim3 grid(p_cap, c.dm.Hkv, b.n);
-    SD_DISPATCH_DG(c.dm.d, c.dm.G,
-                   hipLaunchKernelGGL((k_attend_slots<D_, G_>), grid, dim3(256), 0, st, c, b,
-                                      q, blk_idx, blk_cnt, k_cap, o_part, lse_part, p_cap));
-  } else {
-    const int chunks_x = max(1, max_sel_chunks);
-    const int grid = chunks_x * c.dm.Hkv * b.n;
-    SD_DISPATCH_DG(c.dm.d, c.dm.G,
-                   hipLaunchKernelGGL((k_attend_fuse<D_, G_>), dim3(grid), dim3(256), 0, st,
-                                      c, b, chunks_x, q, blk_idx, blk_cnt, k_cap, o_part,
-                                      lse_part, p_cap, o, lse));
-  }
+  dim3 grid(p_cap, c.dm.Hkv, b.n);
+  SD_DISPATCH_DG(c.dm.d, c.dm.G,
+                 hipLaunchKernelGGL((k_attend_slots<D_, G_>), grid, dim3(256), 0, st, c, b,
+                                    q, blk_idx, blk_cnt, k_cap, o_part, lse_part, p_cap));
+  return hipGetLastError();
+}
+
+hipError_t launch_step(const Ctx &c, const SeqBatch &b, int max_blocks, const uint16_t *q,
+                       int32_t *blk_idx, int32_t *blk_cnt, int32_t k_cap, int dchunks_x,
+                       int schunks_x, float *o_part, float *lse_part, int32_t p_cap,
+                       float *o, float *lse, uint32_t epoch, hipStream_t st) {
+  if (b.n <= 0) return hipSuccess;
+  const int tiles_x = max(1, (max_blocks + kScoreTile - 1) / kScoreTile);
+  const int units = c.dm.Hkv * b.n;
+  const int grid = (tiles_x + dchunks_x + schunks_x) * units;
+  size_t topk_bytes;
+  const int lrows_words = topk_lds(max_blocks, &topk_bytes);
+  if (topk_bytes > 65536) return hipErrorInvalidValue;
+  SD_DISPATCH_DG(c.dm.d, c.dm.G, {
+    const size_t smem = std::max(std::max(sizeof(AttSmem<D_, G_>), sizeof(FuseSmem<G_>)),
+                                 topk_bytes);
+    hipLaunchKernelGGL((k_step<D_, G_>), dim3(grid), dim3(256), smem, st, c, b, tiles_x,
+                       dchunks_x, schunks_x, blk_idx, blk_cnt, k_cap, q, o_part, lse_part,
+                       p_cap, o, lse, lrows_words, epoch);
+  });
   return hipGetLastError();
 }
 

@@ -40,6 +40,7 @@ struct sd_ctx {
   Scratch sc{};
   std::vector<Layer> layers;
   int32_t k_cap = 0, p_cap = 0;
+  uint32_t epoch = 0;  // step launches so far (never 0 once used)
   // attend -> fuse hand-over state
   int pend_layer = -2;
   std::vector<int32_t> pend_seqs;
@@ -301,6 +302,10 @@ sd_status sparse_decode_init(const sd_config *cfg, sd_ctx **out) {
   if ((s = dev_alloc(c, &c->sc.arrive, (size_t)max_seqs * c->Hkv * 2)) != SD_OK) return s;
   SD_HIP(c, hipMemset(c->sc.ucnt, 0, sizeof(int32_t) * max_seqs * c->Hkv));
   SD_HIP(c, hipMemset(c->sc.arrive, 0, sizeof(uint32_t) * max_seqs * c->Hkv * 2));
+  if ((s = dev_alloc(c, &c->sc.ready, (size_t)max_seqs * c->Hkv)) != SD_OK) return s;
+  if ((s = dev_alloc(c, &c->sc.err, 1)) != SD_OK) return s;
+  SD_HIP(c, hipMemset(c->sc.ready, 0, sizeof(uint32_t) * max_seqs * c->Hkv));
+  SD_HIP(c, hipMemset(c->sc.err, 0, sizeof(uint32_t)));
 
   // layers
   c->layers.resize(cfg->num_layers);
@@ -360,6 +365,13 @@ const char *sd_last_error(const sd_ctx *c) {
 sd_status sd_sync(sd_ctx *c) {
   if (!c) return SD_EINVAL;
   SD_HIP(c, hipStreamSynchronize(c->stream));
+  uint32_t e = 0;
+  SD_HIP(c, hipMemcpy(&e, c->sc.err, sizeof e, hipMemcpyDeviceToHost));
+  if (e) {
+    SD_HIP(c, hipMemset(c->sc.err, 0, sizeof e));
+    return fail(c, SD_EHIP, "a decode step kernel timed out waiting for a unit's selection; "
+                "its outputs are invalid");
+  }
   return SD_OK;
 }
 
@@ -518,8 +530,7 @@ sd_status sparse_attend(sd_ctx *c, int32_t layer, int32_t n_seqs,
                             blk_idx + (size_t)base * c->Hkv * k_cap,
                             blk_cnt + (size_t)base * c->Hkv, k_cap,
                             o_part + (size_t)base * c->Hq * p_cap * c->D,
-                            lse_part + (size_t)base * c->Hq * p_cap, p_cap, false, 0, nullptr,
-                            nullptr, c->stream));
+                            lse_part + (size_t)base * c->Hq * p_cap, p_cap, c->stream));
   }
   c->pend_layer = layer;
   c->pend_seqs.assign(seq_ids, seq_ids + n_seqs);
@@ -620,10 +631,10 @@ sd_status sparse_decode_step(sd_ctx *c, int32_t layer, int32_t n_seqs,
     int32_t *bc = blk_cnt + (size_t)base * c->Hkv;
     float *op = o_part + (size_t)base * c->Hq * p_cap * c->D;
     float *lp = lse_part + (size_t)base * c->Hq * p_cap;
-    SD_HIP(c, launch_select(kc, b, mb, qb, bi, bc, k_cap, dchunks, op, lp, p_cap, c->stream));
-    SD_HIP(c, launch_attend(kc, b, qb, bi, bc, k_cap, op, lp, p_cap, true, schunks,
-                            o + (size_t)base * c->Hq * c->D, lse + (size_t)base * c->Hq,
-                            c->stream));
+    if (++c->epoch == 0) c->epoch = 1;
+    SD_HIP(c, launch_step(kc, b, mb, qb, bi, bc, k_cap, dchunks, schunks, op, lp, p_cap,
+                          o + (size_t)base * c->Hq * c->D, lse + (size_t)base * c->Hq,
+                          c->epoch, c->stream));
   }
   c->pend_layer = -2;
   return SD_OK;

@@ -197,6 +197,7 @@ sd_status sd_sync(sd_ctx *ctx);
 /* Text of the last error on this context (never NULL). */
 const char *sd_last_error(const sd_ctx *ctx);
 
+
 /* Debug/parity export of one sequence of one layer to host memory (waits for
  * the stream).  Layouts:
  *   SD_DEBUG_PAGE_TABLE  int32 [ceil(max_seq_len/16)] page ids (in use: the
