@@ -320,10 +320,12 @@ __device__ __forceinline__ float score_eps(float E, float A) {
   return 3.1e-5f * E + 1.2e-7f * fabsf(A) + 1e-30f;
 }
 
+// decay_maw: also write r*MAW for the tile's blocks (the fused step; the
+// fusion then adds (1-r)*a to the attended blocks only).
 template <int D, int G>
-__device__ void score_tile(const Ctx &c, int i, int seq, int h, const HeadInfo &hi,
+__device__ __attribute__((always_inline)) void score_tile(const Ctx &c, int i, int seq, int h, const HeadInfo &hi,
                            const UG &g, int tile, const uint16_t *__restrict__ q,
-                           uint32_t *red /* LDS [8] */) {
+                           uint32_t *red /* LDS [8] */, bool decay_maw) {
   constexpr int MM = D / 16;    // MFMAs per 16 blocks (k = 2d values, 32 per MFMA)
   constexpr int GPW = kScoreTile / 64;  // 16-block groups per wave
   constexpr int C4 = D / 4;
@@ -349,6 +351,15 @@ __device__ void score_tile(const Ctx &c, int i, int seq, int h, const HeadInfo &
 #pragma unroll
   for (int mm = 0; mm < MM; ++mm)
     qw[mm] = *reinterpret_cast<const uint2 *>(qrow + 4 * (4 * mm + lgrp));
+  // MAW of the lane's blocks (lanes of channel group 0 own the keys)
+  const bool need_maw = c.dm.maw_beta > 0.0f || decay_maw;
+  float *mwp = c.L.maw + hi.maw_off + (size_t)seq * hi.nbmax;
+  float mwv[GPW];
+#pragma unroll
+  for (int gi = 0; gi < GPW; ++gi) {
+    const int blk = base + gi * 16 + r16;
+    mwv[gi] = (need_maw && lgrp == 0 && blk < g.n_blk) ? mwp[blk] : 0.0f;
+  }
   __builtin_amdgcn_sched_barrier(0);
   // A operand: lane = head r16 (zero rows past G), channel quad 4*mm + lgrp,
   // pairs (q-, q+) matching the (min, max) pairs of the summaries
@@ -402,13 +413,13 @@ __device__ void score_tile(const Ctx &c, int i, int seq, int h, const HeadInfo &
       unsigned long long kv = cand ? order_key(A) : 0u;
       if (cand) emax = fmaxf(emax, score_eps(E, A));
       if (c.dm.maw_beta > 0.0f) {
-        const float mw = c.L.maw[hi.maw_off + (size_t)seq * hi.nbmax + blk];
-        if ((double)mw * (double)dense_count(g) > (double)c.dm.maw_beta * (double)hi.S) {
+        if ((double)mwv[gi] * (double)dense_count(g) > (double)c.dm.maw_beta * (double)hi.S) {
           kv |= 1ull << 32;
           n_flag += cand ? 1 : 0;
         }
       }
       st_dev(&c.sc.keyflag[ko], kv);
+      if (decay_maw) st_dev(&mwp[blk], __fmul_rn(c.dm.maw_decay, mwv[gi]));
     }
   }
   // the unit's largest error bound (non-negative floats order as their bits)
@@ -588,7 +599,7 @@ __device__ __forceinline__ uint32_t bisect_kth(uint32_t lo, uint32_t hi, int k, 
 }
 
 template <int D, int G>
-__device__ void topk_unit(const Ctx &c, int i, int seq, int h, const HeadInfo &hi,
+__device__ __attribute__((always_inline)) void topk_unit(const Ctx &c, int i, int seq, int h, const HeadInfo &hi,
                           const UG &g, const uint16_t *__restrict__ q,
                           int32_t *__restrict__ blk_idx, int32_t *__restrict__ blk_cnt,
                           int k_cap, TopkSmem &sm, uint32_t *lrows, int lrows_words,
@@ -939,7 +950,7 @@ __device__ __forceinline__ unsigned long long block_mask(const UG &g, int blk, b
 }
 
 template <int D, int G>
-__device__ void attend_chunk(const Ctx &c, int i, int seq, int h, const HeadInfo &hi,
+__device__ __attribute__((always_inline)) void attend_chunk(const Ctx &c, int i, int seq, int h, const HeadInfo &hi,
                              const UG &g, bool dense, int chunk, int cnt,
                              const int32_t *__restrict__ sel,
                              const uint16_t *__restrict__ q, float *__restrict__ o_part,
@@ -1168,13 +1179,21 @@ __device__ void attend_chunk(const Ctx &c, int i, int seq, int h, const HeadInfo
 
 // ---------------------------------------------------------------------------
 // fuse: exact LSE fusion of a unit's partials per query head ([HGCA] What
-// carries the argument, max-subtracted form) and, with MAW, the update of
-// every block: MAW <- r MAW + (1-r) a, a = group-mean softmax mass of the
-// block (0 if not attended) ([LFPS] decay r; [HGCA] MAW).  256 threads.
-// all_slots: fuse every slot of p_cap (lse = -inf ones drop out).
+// carries the argument, max-subtracted form) and the MAW update
+// MAW <- r MAW + (1-r) a, a = group-mean softmax mass of the block (0 if not
+// attended) ([LFPS] decay r; [HGCA] MAW).  256 threads.  Every load the
+// fusion needs is issued in one batch.  MAW: r*MAW is written for every
+// block, then (1-r)*a is added to each attended block with one device-scope
+// atomic add (the same operations, so the same rounding, in both modes):
+//   kMawFull: the decay is done here (separate calls);
+//   kMawAdd:  the score tiles already wrote r*MAW (fused step).
+// all_slots: fuse every slot of p_cap (lse = -inf ones drop out), no MAW.
+constexpr int kMawNone = 0, kMawFull = 1, kMawAdd = 2;
+constexpr int kFusePre = 16;  // partial slots whose O values are preloaded
+
 template <int D, int G>
-__device__ void fuse_unit(const Ctx &c, int i, int seq, int h, const HeadInfo &hi,
-                          const UG &g, bool with_maw, bool all_slots,
+__device__ __attribute__((always_inline)) void fuse_unit(const Ctx &c, int i, int seq, int h, const HeadInfo &hi,
+                          const UG &g, int maw_mode, bool all_slots, int cnt_in,
                           const float *__restrict__ o_part,
                           const float *__restrict__ lse_part, int p_cap,
                           float *__restrict__ o, float *__restrict__ lse,
@@ -1183,23 +1202,68 @@ __device__ void fuse_unit(const Ctx &c, int i, int seq, int h, const HeadInfo &h
   const int qh0 = h * G;
   int nd = 0, ns = 0, cnt = 0;
   if (!all_slots) {
-    cnt = min(ld_dev(&c.sc.ucnt[(size_t)seq * c.dm.Hkv + h]), hi.kcap);
+    cnt = min(cnt_in, hi.kcap);
     nd = cdiv(g.n_dt, g.CB);
     ns = cdiv(cnt, g.CB);
   }
   const int n_slots = min(all_slots ? p_cap : nd + ns, kFuseSlots);
   auto slot_of = [&](int u) { return (all_slots || u < nd) ? u : hi.pd + (u - nd); };
-  // per-head lse over the slots (wave gg handles heads gg, gg+4); the slot
-  // weights e^{lse_u - lse} go to LDS
+  const bool with_maw = maw_mode != kMawNone;
+  const int n_dt = with_maw ? min(g.n_dt, kFuseSlots) : 0;
+  const int n_sel = with_maw ? cnt : 0;
+  const int32_t *gsel = c.sc.usel + ((size_t)seq * c.dm.Hkv + h) * c.dm.kcap;
+  const bool sel_lds = n_sel <= kFuseSelLds;
+
+  // ---- one batch of loads ---------------------------------------------------
   constexpr int R = kFuseSlots / 64;
-  for (int gg = wv; gg < G; gg += 4) {
-    const float *lp = lse_part + ((size_t)i * c.dm.Hq + qh0 + gg) * p_cap;
+  float l0[R], l1[R];  // lse of heads wv and wv + 4
+#pragma unroll
+  for (int r = 0; r < R; ++r) {
+    const int u = lane + 64 * r;
+    const bool on = u < n_slots;
+    l0[r] = (on && wv < G) ? ld_dev(&lse_part[((size_t)i * c.dm.Hq + qh0 + wv) * p_cap + slot_of(u)])
+                           : -INFINITY;
+    l1[r] = (on && wv + 4 < G)
+                ? ld_dev(&lse_part[((size_t)i * c.dm.Hq + qh0 + wv + 4) * p_cap + slot_of(u)])
+                : -INFINITY;
+  }
+  constexpr int NP = (G * D + 255) / 256;
+  float ov[NP][kFusePre];
+#pragma unroll
+  for (int rr = 0; rr < NP; ++rr) {
+    const int x = tid + 256 * rr;
+    const int gg = x / D, ch = x - gg * D;
+    const size_t hb = ((size_t)i * c.dm.Hq + qh0 + min(gg, G - 1)) * p_cap;
+#pragma unroll
+    for (int u = 0; u < kFusePre; ++u)
+      ov[rr][u] = (x < G * D && u < n_slots) ? ld_dev(&o_part[(hb + slot_of(u)) * D + ch]) : 0.0f;
+  }
+  // attended entries of MAW: dense-touching blocks, then the selection
+  constexpr int ME = 4;  // entries per thread preloaded (more loop below)
+  float lmv[ME][G];
+  int selv[ME];
+#pragma unroll
+  for (int t = 0; t < ME; ++t) {
+    const int x = tid + 256 * t;
+    const bool dn = x < n_dt, sl = !dn && x < n_dt + n_sel;
+    const int u = dn ? x : x - n_dt;
+#pragma unroll
+    for (int gg = 0; gg < G; ++gg) {
+      const size_t row = (size_t)seq * c.dm.Hq + qh0 + gg;
+      lmv[t][gg] = dn ? ld_dev(&c.sc.lm_dense[row * c.dm.ndt_cap + u])
+                      : (sl ? ld_dev(&c.sc.lm_sel[row * c.dm.kcap + u]) : -INFINITY);
+    }
+    selv[t] = sl ? ld_dev(&gsel[u]) : 0;
+  }
+
+  // ---- per-head lse and slot weights ----------------------------------------
+#pragma unroll
+  for (int pass = 0; pass < 2; ++pass) {
+    const int gg = wv + 4 * pass;
+    if (gg >= G) continue;
     float l[R];
 #pragma unroll
-    for (int r = 0; r < R; ++r) {
-      const int u = lane + 64 * r;
-      l[r] = u < n_slots ? ld_dev(&lp[slot_of(u)]) : -INFINITY;
-    }
+    for (int r = 0; r < R; ++r) l[r] = pass ? l1[r] : l0[r];
     float m = l[0];
 #pragma unroll
     for (int r = 1; r < R; ++r) m = fmaxf(m, l[r]);
@@ -1218,8 +1282,7 @@ __device__ void fuse_unit(const Ctx &c, int i, int seq, int h, const HeadInfo &h
     }
   }
   __syncthreads();
-  // O = sum_u w_u O_u (loads issued unconditionally; zero weights select 0)
-  constexpr int NP = (G * D + 255) / 256;
+  // ---- O = sum_u w_u O_u (zero weights select 0) ------------------------------
 #pragma unroll
   for (int rr = 0; rr < NP; ++rr) {
     const int x = tid + 256 * rr;
@@ -1227,11 +1290,17 @@ __device__ void fuse_unit(const Ctx &c, int i, int seq, int h, const HeadInfo &h
       const int gg = x / D, ch = x - gg * D;
       const size_t hb = ((size_t)i * c.dm.Hq + qh0 + gg) * p_cap;
       float a = 0.0f;
-#pragma unroll 8
-      for (int u = 0; u < n_slots; ++u) {
+#pragma unroll
+      for (int u = 0; u < kFusePre; ++u) {
+        if (u < n_slots) {
+          const float wgt = sm.w[gg][u];
+          a = fmaf(wgt, wgt != 0.0f ? ov[rr][u] : 0.0f, a);
+        }
+      }
+      for (int u = kFusePre; u < n_slots; ++u) {
         const float wgt = sm.w[gg][u];
-        const float ov = ld_dev(&o_part[(hb + slot_of(u)) * D + ch]);
-        a = fmaf(wgt, wgt != 0.0f ? ov : 0.0f, a);
+        const float v = ld_dev(&o_part[(hb + slot_of(u)) * D + ch]);
+        a = fmaf(wgt, wgt != 0.0f ? v : 0.0f, a);
       }
       o[((size_t)i * c.dm.Hq + qh0 + gg) * D + ch] = a;
     }
@@ -1239,63 +1308,85 @@ __device__ void fuse_unit(const Ctx &c, int i, int seq, int h, const HeadInfo &h
   if (tid < G) lse[(size_t)i * c.dm.Hq + qh0 + tid] = sm.lse[tid];
   if (!with_maw) return;
 
-  // ---- MAW update of every block of the unit -------------------------------
-  // group-mean mass of the attended slots first (independent loads), then one
-  // streaming pass over the blocks.
-  const int n_dt = min(g.n_dt, kFuseSlots);
-  const int32_t *gsel = c.sc.usel + ((size_t)seq * c.dm.Hkv + h) * c.dm.kcap;
-  const bool sel_lds = cnt <= kFuseSelLds;
-  for (int x = tid; x < n_dt + cnt; x += 256) {
-    const bool dn = x < n_dt;
-    const int u = dn ? x : x - n_dt;
+  // ---- MAW -------------------------------------------------------------------
+  // group-mean mass of every attended entry, into LDS
+  auto mass = [&](const float (&lm)[G]) {
     float a = 0.0f;
 #pragma unroll
     for (int gg = 0; gg < G; ++gg) {
-      const size_t row = (size_t)seq * c.dm.Hq + qh0 + gg;
-      const float lm = dn ? ld_dev(&c.sc.lm_dense[row * c.dm.ndt_cap + u])
-                          : ld_dev(&c.sc.lm_sel[row * c.dm.kcap + u]);
       const float L = sm.lse[gg];
-      a += (L == -INFINITY || lm == -INFINITY) ? 0.0f : expf(lm - L);
+      a += (L == -INFINITY || lm[gg] == -INFINITY) ? 0.0f : expf(lm[gg] - L);
     }
-    a *= 1.0f / (float)G;
-    if (dn) {
-      sm.adense[u] = a;
+    return a * (1.0f / (float)G);
+  };
+  auto put = [&](int x, float a, int sv) {
+    if (x < n_dt) {
+      sm.adense[x] = a;
     } else if (sel_lds) {
-      sm.asel[u] = a;
-      sm.sel[u] = ld_dev(&gsel[u]);
+      sm.asel[x - n_dt] = a;
+      sm.sel[x - n_dt] = sv;
     }
+  };
+#pragma unroll
+  for (int t = 0; t < ME; ++t) {
+    const int x = tid + 256 * t;
+    if (x < n_dt + n_sel) put(x, mass(lmv[t]), selv[t]);
+  }
+  for (int x = tid + 256 * ME; x < n_dt + n_sel; x += 256) {
+    const bool dn = x < n_dt;
+    const int u = dn ? x : x - n_dt;
+    float lm[G];
+#pragma unroll
+    for (int gg = 0; gg < G; ++gg) {
+      const size_t row = (size_t)seq * c.dm.Hq + qh0 + gg;
+      lm[gg] = dn ? ld_dev(&c.sc.lm_dense[row * c.dm.ndt_cap + u])
+                  : ld_dev(&c.sc.lm_sel[row * c.dm.kcap + u]);
+    }
+    put(x, mass(lm), dn ? 0 : ld_dev(&gsel[u]));
   }
   __syncthreads();
-  const int n = g.n_blk;
   float *mw = c.L.maw + hi.maw_off + (size_t)seq * hi.nbmax;
-  const float r = c.dm.maw_decay;
-  for (int blk = tid; blk < n; blk += 256) {
-    const float old = mw[blk];
-    float a = 0.0f;
-    if (blk < g.hb) a += sm.adense[blk];
-    else if (blk >= g.tb) a += sm.adense[g.hb + (blk - g.tb)];
-    if (sel_lds) {
-      const int j = lower_bound(sm.sel, cnt, blk);
-      if (j < cnt && sm.sel[j] == blk) a += sm.asel[j];
-    } else {
-      // very large selections: search the global copy and recompute the mass
-      int lo = 0, hi2 = cnt;  // binary search over the published selection
-      while (lo < hi2) {
-        const int mid = (lo + hi2) >> 1;
-        if (ld_dev(&gsel[mid]) < blk) lo = mid + 1; else hi2 = mid;
-      }
-      const int j = lo;
-      if (j < cnt && ld_dev(&gsel[j]) == blk) {
-        float aa = 0.0f;
-        for (int gg = 0; gg < G; ++gg) {
-          const float lm = ld_dev(&c.sc.lm_sel[((size_t)seq * c.dm.Hq + qh0 + gg) * c.dm.kcap + j]);
-          const float L = sm.lse[gg];
-          aa += (L == -INFINITY || lm == -INFINITY) ? 0.0f : expf(lm - L);
-        }
-        a += aa * (1.0f / (float)G);
-      }
+  const float r = c.dm.maw_decay, omr = 1.0f - r;
+  // mass of a selected block from the global copy (selections beyond the LDS)
+  auto sel_mass_global = [&](int blk) -> float {
+    int lo = 0, hi2 = n_sel;
+    while (lo < hi2) {
+      const int mid = (lo + hi2) >> 1;
+      if (ld_dev(&gsel[mid]) < blk) lo = mid + 1; else hi2 = mid;
     }
-    mw[blk] = fmaf(r, old, (1.0f - r) * a);
+    if (lo >= n_sel || ld_dev(&gsel[lo]) != blk) return 0.0f;
+    float lm[G];
+#pragma unroll
+    for (int gg = 0; gg < G; ++gg)
+      lm[gg] = ld_dev(&c.sc.lm_sel[((size_t)seq * c.dm.Hq + qh0 + gg) * c.dm.kcap + lo]);
+    return mass(lm);
+  };
+  auto sel_mass = [&](int blk) -> float {
+    if (!sel_lds) return sel_mass_global(blk);
+    const int j = lower_bound(sm.sel, n_sel, blk);
+    return (j < n_sel && sm.sel[j] == blk) ? sm.asel[j] : 0.0f;
+  };
+  if (maw_mode == kMawFull) {  // decay here (the fused step's score tiles do it there)
+    for (int blk = tid; blk < g.n_blk; blk += 256) st_dev(&mw[blk], __fmul_rn(r, ld_dev(&mw[blk])));
+    wait_vmem();
+    __syncthreads();
+  }
+  // attended blocks: dense-touching ones (with their selected part, if any),
+  // then selected blocks that touch no dense token; one atomic add each, so
+  // both modes round identically
+  for (int x = tid; x < n_dt + n_sel; x += 256) {
+    int blk;
+    float a;
+    if (x < n_dt) {
+      blk = dense_block(g, x);
+      a = sm.adense[x] + sel_mass(blk);
+    } else {
+      const int j = x - n_dt;
+      blk = sel_lds ? sm.sel[j] : ld_dev(&gsel[j]);
+      if (blk < g.hb || blk >= g.tb) continue;  // counted with the dense entry
+      a = sel_lds ? sm.asel[j] : sel_mass_global(blk);
+    }
+    __hip_atomic_fetch_add(&mw[blk], __fmul_rn(omr, a), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
   }
 }
 
@@ -1349,7 +1440,7 @@ __global__ __launch_bounds__(256) void k_select(Ctx c, SeqBatch b, int tiles_x,
     const UG g = unit_geom(b.len[i], hi, c.dm);
     const int n_tiles = max(1, cdiv(g.n_blk, kScoreTile));
     if (tile >= n_tiles) return;
-    score_tile<D, G>(c, i, seq, h, hi, g, tile, q, smem_topk.red);
+    score_tile<D, G>(c, i, seq, h, hi, g, tile, q, smem_topk.red, false);
     // the last tile of the unit to arrive runs its top-k (one wave)
     uint32_t *ctr = &c.sc.arrive[((size_t)seq * c.dm.Hkv + h) * 2];
     if (!arrive_last(ctr, (unsigned)n_tiles, &smem_topk.last)) return;
@@ -1440,7 +1531,7 @@ __global__ __launch_bounds__(256) void k_step(Ctx c, SeqBatch b, int tiles_x, in
   if (role == 0) {
     const int n_tiles = max(1, cdiv(g.n_blk, kScoreTile));
     if (idx >= n_tiles) return;
-    score_tile<D, G>(c, i, seq, h, hi, g, idx, q, smem_topk.red);
+    score_tile<D, G>(c, i, seq, h, hi, g, idx, q, smem_topk.red, true);
     uint32_t *ctr = &c.sc.arrive[unit * 2];
     if (!arrive_last(ctr, (unsigned)n_tiles, &s_flag)) return;
     uint32_t *lrows = reinterpret_cast<uint32_t *>(smem_raw + sizeof(TopkSmem));
@@ -1479,7 +1570,8 @@ __global__ __launch_bounds__(256) void k_step(Ctx c, SeqBatch b, int tiles_x, in
   }
   uint32_t *fctr = &c.sc.arrive[unit * 2 + 1];
   if (!arrive_fuse(fctr, nd, &c.sc.ucnt[unit], g.CB, &s_flag)) return;
-  fuse_unit<D, G>(c, i, seq, h, hi, g, true, false, o_part, lse_part, p_cap, o, lse, smem_fuse);
+  fuse_unit<D, G>(c, i, seq, h, hi, g, kMawAdd, false, ld_dev(&c.sc.ucnt[unit]), o_part,
+                  lse_part, p_cap, o, lse, smem_fuse);
   if (threadIdx.x == 0) st_dev(fctr, 0u);
 }
 
@@ -1493,10 +1585,12 @@ __global__ __launch_bounds__(256) void k_fuse(Ctx c, SeqBatch b, int with_maw,
   const HeadInfo hi = c.heads[h];
   if (with_maw) {
     const UG g = unit_geom(b.len[i], hi, c.dm);
-    fuse_unit<D, G>(c, i, b.seq[i], h, hi, g, true, false, o_part, lse_part, p_cap, o, lse, sm);
+    fuse_unit<D, G>(c, i, b.seq[i], h, hi, g, kMawFull, false,
+                    ld_dev(&c.sc.ucnt[(size_t)b.seq[i] * c.dm.Hkv + h]), o_part, lse_part,
+                    p_cap, o, lse, sm);
   } else {
     UG g{};
-    fuse_unit<D, G>(c, i, 0, h, hi, g, false, true, o_part, lse_part, p_cap, o, lse, sm);
+    fuse_unit<D, G>(c, i, 0, h, hi, g, kMawNone, true, 0, o_part, lse_part, p_cap, o, lse, sm);
   }
 }
 
