@@ -17,6 +17,7 @@ constexpr int kChunkTokens = 256;    // token slots of one split-K chunk
 constexpr int kScoreTile = 256;      // blocks scored by one workgroup
 constexpr int kTopkRegRows = 20;     // top-k rows of 64 block words kept in registers
 constexpr int kTopkUnc = 512;        // uncertain blocks the top-k lists in LDS
+constexpr int kFastTiles = 8;        // score tiles per unit of the fast top-k, at most
 constexpr int kFuseSlots = 256;      // partial slots per query head, at most
 constexpr int kFuseSelLds = 2048;    // fusion keeps the selection in LDS up to this
 
@@ -85,6 +86,9 @@ struct Scratch {
   int32_t *usel;     // [max_seqs][Hkv][kcap] selected block ids (attend copy)
   int32_t *ucnt;     // [max_seqs][Hkv] selected block count (attend copy)
   uint32_t *arrive;  // [max_seqs][Hkv][2] last-arriver counters (kept at 0)
+  unsigned long long *cand;  // [max_seqs][Hkv][key_stride] per-tile candidate lists
+                             // (key << 32 | block), tile t's at [t*kScoreTile, ...)
+  uint32_t *tcnt;    // [max_seqs][Hkv][kFastTiles] entries of each tile's list
   uint32_t *ready;   // [max_seqs][Hkv] step number of the unit's published selection
   uint32_t *err;     // [1] nonzero once a step kernel's wait ran out of time
 };

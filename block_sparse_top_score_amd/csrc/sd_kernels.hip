@@ -179,6 +179,9 @@ __device__ __forceinline__ uint32_t order_key(float u) {
 struct TopkSmem {
   int32_t ulist[kTopkUnc];  // uncertain blocks of the top-k, in index order
   uint32_t ukey[kTopkUnc];  // their exact keys
+  int32_t upos[kTopkUnc];   // their list positions (fast top-k)
+  uint32_t tk[kScoreTile];  // keys of a score tile (fast top-k)
+  unsigned long long cm[kFastTiles];  // chosen uncertain entries (fast top-k)
   float qs[SD_MAX_GROUP * 128];
   double ud[16];
   uint32_t red[8];
@@ -296,6 +299,52 @@ __device__ void append_summ(const Ctx &c, const AppendBatch &b, int i, int h,
 }
 
 // ---------------------------------------------------------------------------
+// Wave-level helpers of the scoring and the top-k.
+__device__ __forceinline__ int lanes_below(unsigned long long m) {
+  return (int)__builtin_amdgcn_mbcnt_hi((uint32_t)(m >> 32),
+                                        __builtin_amdgcn_mbcnt_lo((uint32_t)m, 0u));
+}
+__device__ __forceinline__ int count_lanes(bool p) { return __popcll(__ballot(p)); }
+// Wave min / max of an unsigned value (uniform result): DPP inside rows of
+// 16 lanes, then the four row results.
+template <int CTRL>
+__device__ __forceinline__ uint32_t dppu(uint32_t x) {
+  return (uint32_t)__builtin_amdgcn_update_dpp(0, (int)x, CTRL, 0xF, 0xF, false);
+}
+__device__ __forceinline__ uint32_t wave_min_u(uint32_t v) {
+  v = min(v, dppu<0xB1>(v));   // quad_perm [1,0,3,2]
+  v = min(v, dppu<0x4E>(v));   // quad_perm [2,3,0,1]
+  v = min(v, dppu<0x141>(v));  // row_half_mirror
+  v = min(v, dppu<0x140>(v));  // row_mirror
+  const uint32_t a = min((uint32_t)__builtin_amdgcn_readlane((int)v, 0),
+                         (uint32_t)__builtin_amdgcn_readlane((int)v, 16));
+  const uint32_t b = min((uint32_t)__builtin_amdgcn_readlane((int)v, 32),
+                         (uint32_t)__builtin_amdgcn_readlane((int)v, 48));
+  return min(a, b);
+}
+__device__ __forceinline__ uint32_t wave_max_u(uint32_t v) {
+  v = max(v, dppu<0xB1>(v));
+  v = max(v, dppu<0x4E>(v));
+  v = max(v, dppu<0x141>(v));
+  v = max(v, dppu<0x140>(v));
+  const uint32_t a = max((uint32_t)__builtin_amdgcn_readlane((int)v, 0),
+                         (uint32_t)__builtin_amdgcn_readlane((int)v, 16));
+  const uint32_t b = max((uint32_t)__builtin_amdgcn_readlane((int)v, 32),
+                         (uint32_t)__builtin_amdgcn_readlane((int)v, 48));
+  return max(a, b);
+}
+// Largest t in [lo, hi] with count_ge(t) >= k, given count_ge(lo) >= k: the
+// k-th largest of the counted values.
+template <class CountF>
+__device__ __forceinline__ uint32_t bisect_kth(uint32_t lo, uint32_t hi, int k, CountF count_ge) {
+  while (lo < hi) {
+    const uint32_t mid = lo + ((hi - lo) >> 1) + 1u;  // lo < mid <= hi
+    if (count_ge(mid) >= k) lo = mid; else hi = mid - 1u;
+  }
+  return lo;
+}
+
+// ---------------------------------------------------------------------------
 // score, approximate pass ([LFPS] block-based Quest bound, R2):
 //   U_h(i) = sum_c max(q_hc m_ic, q_hc M_ic) = sum_c q-_hc m_ic + q+_hc M_ic
 // with q- = min(q,0), q+ = max(q,0) (exact in bf16), so the bound of 16
@@ -320,12 +369,66 @@ __device__ __forceinline__ float score_eps(float E, float A) {
   return 3.1e-5f * E + 1.2e-7f * fabsf(A) + 1e-30f;
 }
 
+// Candidate list of one score tile for the fast top-k (one wave; no MAW
+// flags, so every candidate is ranked and k = kk).  With C_t > kk candidates
+// in the tile, let L be the tile's kk-th largest approximate key and eps_t its
+// largest error bound.  A block with A < L - 2 eps_t has kk blocks in its own
+// tile whose exact scores are strictly larger (each at least L - eps_t >
+// A + eps_t), so it cannot be in the unit's top kk and is dropped.  Bisection
+// narrows [a, b] around L to within eps_t; the tile keeps the blocks with
+// A >= a - 2 eps_t, in ascending block order.
+__device__ __forceinline__ void tile_candidates(const Ctx &c, int seq, int h, const UG &g, int tile,
+                                                const uint32_t *tk /* LDS [kScoreTile] */,
+                                                double eps_t) {
+  const int lane = threadIdx.x & 63;
+  constexpr int TR = kScoreTile / 64;
+  const size_t unit = (size_t)seq * c.dm.Hkv + h;
+  const int kk = g.kk;
+  uint32_t x[TR], lo = 0xffffffffu, hi = 0u;
+  int ct = 0;
+#pragma unroll
+  for (int r = 0; r < TR; ++r) {
+    x[r] = tk[r * 64 + lane];
+    if (x[r] >= 2u) {
+      lo = min(lo, x[r]);
+      hi = max(hi, x[r]);
+    }
+    ct += count_lanes(x[r] >= 2u);
+  }
+  uint32_t dmin = kk > 0 ? 2u : 0xffffffffu;  // keys below dmin are dropped
+  if (kk > 0 && ct > kk) {
+    uint32_t a = wave_min_u(lo), b = wave_max_u(hi);
+    while (a < b && (double)key_to_float(b) - (double)key_to_float(a) > eps_t) {
+      const uint32_t mid = a + ((b - a) >> 1) + 1u;
+      int cm = 0;
+#pragma unroll
+      for (int r = 0; r < TR; ++r) cm += count_lanes(x[r] >= mid);
+      if (cm >= kk) a = mid; else b = mid - 1u;
+    }
+    dmin = order_key(__double2float_ru((double)key_to_float(a) - 2.0 * eps_t));
+  }
+  unsigned long long *dst = c.sc.cand + unit * c.dm.key_stride + (size_t)tile * kScoreTile;
+  int n = 0;
+#pragma unroll
+  for (int r = 0; r < TR; ++r) {
+    const bool in = x[r] >= 2u && x[r] >= dmin;
+    const unsigned long long m = __ballot(in);
+    if (in)
+      st_dev(&dst[n + lanes_below(m)],
+             ((unsigned long long)x[r] << 32) | (uint32_t)(tile * kScoreTile + r * 64 + lane));
+    n += __popcll(m);
+  }
+  if (lane == 0) st_dev(&c.sc.tcnt[unit * kFastTiles + tile], (uint32_t)n);
+}
+
 // decay_maw: also write r*MAW for the tile's blocks (the fused step; the
-// fusion then adds (1-r)*a to the attended blocks only).
+// fusion then adds (1-r)*a to the attended blocks only).  publish: also write
+// the tile's candidate list for the fast top-k (tile < kFastTiles).
 template <int D, int G>
 __device__ __attribute__((always_inline)) void score_tile(const Ctx &c, int i, int seq, int h, const HeadInfo &hi,
                            const UG &g, int tile, const uint16_t *__restrict__ q,
-                           uint32_t *red /* LDS [8] */, bool decay_maw) {
+                           TopkSmem &sm, bool decay_maw, bool publish) {
+  uint32_t *red = sm.red;
   constexpr int MM = D / 16;    // MFMAs per 16 blocks (k = 2d values, 32 per MFMA)
   constexpr int GPW = kScoreTile / 64;  // 16-block groups per wave
   constexpr int C4 = D / 4;
@@ -407,10 +510,11 @@ __device__ __attribute__((always_inline)) void score_tile(const Ctx &c, int i, i
       E = fmaxf(E, __shfl_xor(E, 16, 64));
     }
     const int blk = base + gi * 16 + r16;
+    unsigned long long kv = 0u;
     if (lgrp == 0 && blk < g.n_blk) {
       const size_t ko = ((size_t)seq * c.dm.Hkv + h) * c.dm.key_stride + blk;
       const bool cand = is_candidate(g, blk);
-      unsigned long long kv = cand ? order_key(A) : 0u;
+      kv = cand ? order_key(A) : 0u;
       if (cand) emax = fmaxf(emax, score_eps(E, A));
       if (c.dm.maw_beta > 0.0f) {
         if ((double)mwv[gi] * (double)dense_count(g) > (double)c.dm.maw_beta * (double)hi.S) {
@@ -421,6 +525,7 @@ __device__ __attribute__((always_inline)) void score_tile(const Ctx &c, int i, i
       st_dev(&c.sc.keyflag[ko], kv);
       if (decay_maw) st_dev(&mwp[blk], __fmul_rn(c.dm.maw_decay, mwv[gi]));
     }
+    if (publish && lgrp == 0) sm.tk[wv * 16 * GPW + gi * 16 + r16] = (uint32_t)kv;
   }
   // the unit's largest error bound (non-negative floats order as their bits)
   // and its flagged candidates, accumulated over the tiles
@@ -439,6 +544,10 @@ __device__ __attribute__((always_inline)) void score_tile(const Ctx &c, int i, i
                            __HIP_MEMORY_SCOPE_AGENT);
     const uint32_t f = red[4] + red[5] + red[6] + red[7];
     if (f) __hip_atomic_fetch_add(acc + 1, f, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  }
+  if (publish && wv == 0) {
+    const double eps_t = (double)__uint_as_float(max(max(red[0], red[1]), max(red[2], red[3])));
+    tile_candidates(c, seq, h, g, tile, sm.tk, eps_t);
   }
 }
 
@@ -554,50 +663,6 @@ __device__ double exact_score_quad(const Ctx &c, int seq, const HeadInfo &hi, in
 //      to the lower index), found by bisection; they are marked in an LDS
 //      bitmask of rows;
 //   4. ordered compaction with ballots: ascending block indices.
-__device__ __forceinline__ int lanes_below(unsigned long long m) {
-  return (int)__builtin_amdgcn_mbcnt_hi((uint32_t)(m >> 32),
-                                        __builtin_amdgcn_mbcnt_lo((uint32_t)m, 0u));
-}
-__device__ __forceinline__ int count_lanes(bool p) { return __popcll(__ballot(p)); }
-// Wave min / max of an unsigned value (uniform result): DPP inside rows of
-// 16 lanes, then the four row results.
-template <int CTRL>
-__device__ __forceinline__ uint32_t dppu(uint32_t x) {
-  return (uint32_t)__builtin_amdgcn_update_dpp(0, (int)x, CTRL, 0xF, 0xF, false);
-}
-__device__ __forceinline__ uint32_t wave_min_u(uint32_t v) {
-  v = min(v, dppu<0xB1>(v));   // quad_perm [1,0,3,2]
-  v = min(v, dppu<0x4E>(v));   // quad_perm [2,3,0,1]
-  v = min(v, dppu<0x141>(v));  // row_half_mirror
-  v = min(v, dppu<0x140>(v));  // row_mirror
-  const uint32_t a = min((uint32_t)__builtin_amdgcn_readlane((int)v, 0),
-                         (uint32_t)__builtin_amdgcn_readlane((int)v, 16));
-  const uint32_t b = min((uint32_t)__builtin_amdgcn_readlane((int)v, 32),
-                         (uint32_t)__builtin_amdgcn_readlane((int)v, 48));
-  return min(a, b);
-}
-__device__ __forceinline__ uint32_t wave_max_u(uint32_t v) {
-  v = max(v, dppu<0xB1>(v));
-  v = max(v, dppu<0x4E>(v));
-  v = max(v, dppu<0x141>(v));
-  v = max(v, dppu<0x140>(v));
-  const uint32_t a = max((uint32_t)__builtin_amdgcn_readlane((int)v, 0),
-                         (uint32_t)__builtin_amdgcn_readlane((int)v, 16));
-  const uint32_t b = max((uint32_t)__builtin_amdgcn_readlane((int)v, 32),
-                         (uint32_t)__builtin_amdgcn_readlane((int)v, 48));
-  return max(a, b);
-}
-// Largest t in [lo, hi] with count_ge(t) >= k, given count_ge(lo) >= k: the
-// k-th largest of the counted values.
-template <class CountF>
-__device__ __forceinline__ uint32_t bisect_kth(uint32_t lo, uint32_t hi, int k, CountF count_ge) {
-  while (lo < hi) {
-    const uint32_t mid = lo + ((hi - lo) >> 1) + 1u;  // lo < mid <= hi
-    if (count_ge(mid) >= k) lo = mid; else hi = mid - 1u;
-  }
-  return lo;
-}
-
 template <int D, int G>
 __device__ __attribute__((always_inline)) void topk_unit(const Ctx &c, int i, int seq, int h, const HeadInfo &hi,
                           const UG &g, const uint16_t *__restrict__ q,
@@ -889,6 +954,142 @@ __device__ __attribute__((always_inline)) void topk_unit(const Ctx &c, int i, in
     st_dev(&c.sc.unit_acc[2 * unit], 0u);  // cleared for the next step
     st_dev(&c.sc.unit_acc[2 * unit + 1], 0u);
   }
+}
+
+// Fast top-k of one unit from the score tiles' candidate lists (one wave; no
+// MAW flags).  At most 64 entries per tile are loaded in one batch; then the
+// steps of topk_unit run on those entries: the kk-th largest approximate key
+// by bisection to within eps, the band, exact re-scoring of the blocks in it
+// (ties to the lower index), and the ordered compaction.  The entries are in
+// ascending block order (tile by tile).  Returns false, before writing
+// anything, when a tile listed more than 64 entries or the band holds more
+// than 64 blocks; the caller then runs topk_unit on the full keys.
+template <int D, int G>
+__device__ __attribute__((always_inline)) bool topk_fast(const Ctx &c, int i, int seq, int h,
+                                                         const HeadInfo &hi, const UG &g,
+                                                         const uint16_t *__restrict__ q,
+                                                         int32_t *__restrict__ blk_idx,
+                                                         int32_t *__restrict__ blk_cnt, int k_cap,
+                                                         TopkSmem &sm) {
+  if (threadIdx.x >= 64) return true;
+  const int lane = threadIdx.x;
+  const size_t unit = (size_t)seq * c.dm.Hkv + h;
+  const int n_tiles = max(1, cdiv(g.n_blk, kScoreTile));
+  // one batch: entry counts, entries, error bound, the group's query
+  const unsigned long long *cl = c.sc.cand + unit * c.dm.key_stride;
+  uint32_t cntv[kFastTiles];
+  unsigned long long e[kFastTiles];
+#pragma unroll
+  for (int r = 0; r < kFastTiles; ++r) {
+    cntv[r] = ld_dev(&c.sc.tcnt[unit * kFastTiles + r]);
+    e[r] = ld_dev(&cl[(size_t)(r < n_tiles ? r : 0) * kScoreTile + lane]);
+  }
+  const uint32_t eps_bits = ld_dev(&c.sc.unit_acc[2 * unit]);
+  constexpr int QPL = (G * D + 63) / 64;
+  const uint16_t *qg = q + ((size_t)i * c.dm.Hq + (size_t)h * G) * D;
+  uint16_t qv[QPL];
+#pragma unroll
+  for (int r = 0; r < QPL; ++r) qv[r] = qg[min(r * 64 + lane, G * D - 1)];
+
+  bool ok = true;
+  uint32_t x[kFastTiles];
+  int bl[kFastTiles];
+#pragma unroll
+  for (int r = 0; r < kFastTiles; ++r) {
+    const uint32_t cr = r < n_tiles ? cntv[r] : 0u;
+    ok = ok && cr <= 64u;
+    x[r] = lane < (int)cr ? (uint32_t)(e[r] >> 32) : 0u;
+    bl[r] = (int)(uint32_t)e[r];
+  }
+  if (!ok) return false;
+#pragma unroll
+  for (int r = 0; r < QPL; ++r) {
+    const int xx = r * 64 + lane;
+    if (xx < G * D) sm.qs[xx] = __uint_as_float((uint32_t)qv[r] << 16);
+  }
+  if (lane < kFastTiles) sm.cm[lane] = 0ull;
+  const int kk = g.kk;
+  uint32_t kb_hi = 0xffffffffu;
+  if (kk > 0) {
+    const double eps = (double)__uint_as_float(eps_bits);
+    uint32_t lo = 0xffffffffu, hi_k = 0u;
+#pragma unroll
+    for (int r = 0; r < kFastTiles; ++r)
+      if (x[r] >= 2u) {
+        lo = min(lo, x[r]);
+        hi_k = max(hi_k, x[r]);
+      }
+    uint32_t a = wave_min_u(lo), b = wave_max_u(hi_k);
+    while (a < b && (double)key_to_float(b) - (double)key_to_float(a) > eps) {
+      const uint32_t mid = a + ((b - a) >> 1) + 1u;
+      int cm = 0;
+#pragma unroll
+      for (int r = 0; r < kFastTiles; ++r)
+        if (r < n_tiles) cm += count_lanes(x[r] >= mid);
+      if (cm >= kk) a = mid; else b = mid - 1u;
+    }
+    kb_hi = order_key(__double2float_rd((double)key_to_float(b) + 2.0 * eps));
+    const uint32_t kb_lo = order_key(__double2float_ru((double)key_to_float(a) - 2.0 * eps));
+    // uncertain entries in block order; sure ones counted
+    int n_in = 0, n_unc = 0;
+#pragma unroll
+    for (int r = 0; r < kFastTiles; ++r) {
+      const bool unc = x[r] >= kb_lo && x[r] <= kb_hi;
+      const unsigned long long m = __ballot(unc);
+      const int p = n_unc + lanes_below(m);
+      if (unc && p < kTopkUnc) {
+        sm.ulist[p] = bl[r];
+        sm.upos[p] = r * 64 + lane;
+      }
+      n_unc += __popcll(m);
+      n_in += count_lanes(x[r] > kb_hi);
+    }
+    if (n_unc > 64) return false;
+    const int kr2 = kk - n_in;  // >= 1: the kk-th entry is uncertain
+    // exact keys of the uncertain blocks, one lane quad per (block, head)
+    constexpr int BPR = 16 / G;
+    for (int u0 = 0; u0 < n_unc; u0 += BPR) {
+      const int pair = lane >> 2, uu = u0 + pair / G, gg = pair % G;
+      const bool on = pair < BPR * G && uu < n_unc;
+      const double U = exact_score_quad<D>(c, seq, hi, on ? sm.ulist[uu] : 0,
+                                           sm.qs + (on ? gg : 0) * D, on);
+      if ((lane & 3) == 0) sm.ud[pair] = U;
+      if (lane < BPR && u0 + lane < n_unc) {
+        double best = sm.ud[lane * G];
+        for (int xg = 1; xg < G; ++xg) best = sm.ud[lane * G + xg] > best ? sm.ud[lane * G + xg] : best;
+        sm.ukey[u0 + lane] = order_key((float)best);
+      }
+    }
+    // rank of each uncertain entry: larger exact keys, then equal keys listed
+    // earlier; the kr2 first are taken
+    const uint32_t ek = lane < n_unc ? sm.ukey[lane] : 0u;
+    int rank = 0;
+    for (int p = 0; p < n_unc; ++p) {
+      const uint32_t ep = (uint32_t)__builtin_amdgcn_readlane((int)ek, p);
+      rank += (ep > ek || (ep == ek && p < lane)) ? 1 : 0;
+    }
+    if (lane < n_unc && rank < kr2) {
+      const int pos = sm.upos[lane];
+      atomicOr(&sm.cm[pos >> 6], 1ull << (pos & 63));
+    }
+  }
+  // ordered compaction
+  int32_t *dst = blk_idx + ((size_t)i * c.dm.Hkv + h) * k_cap;
+  int ob = 0;
+#pragma unroll
+  for (int r = 0; r < kFastTiles; ++r) {
+    const bool ch = (x[r] >= 2u && x[r] > kb_hi) || ((sm.cm[r] >> lane) & 1ull);
+    const unsigned long long mc = __ballot(ch);
+    const int o = ob + lanes_below(mc);
+    if (ch && o < k_cap) st_dev(&dst[o], bl[r]);
+    ob += __popcll(mc);
+  }
+  if (lane == 0) {
+    st_dev(&blk_cnt[(size_t)i * c.dm.Hkv + h], kk);
+    st_dev(&c.sc.unit_acc[2 * unit], 0u);  // cleared for the next step
+    st_dev(&c.sc.unit_acc[2 * unit + 1], 0u);
+  }
+  return true;
 }
 
 // ---------------------------------------------------------------------------
@@ -1440,7 +1641,7 @@ __global__ __launch_bounds__(256) void k_select(Ctx c, SeqBatch b, int tiles_x,
     const UG g = unit_geom(b.len[i], hi, c.dm);
     const int n_tiles = max(1, cdiv(g.n_blk, kScoreTile));
     if (tile >= n_tiles) return;
-    score_tile<D, G>(c, i, seq, h, hi, g, tile, q, smem_topk.red, false);
+    score_tile<D, G>(c, i, seq, h, hi, g, tile, q, smem_topk, false, false);
     // the last tile of the unit to arrive runs its top-k (one wave)
     uint32_t *ctr = &c.sc.arrive[((size_t)seq * c.dm.Hkv + h) * 2];
     if (!arrive_last(ctr, (unsigned)n_tiles, &smem_topk.last)) return;
@@ -1531,12 +1732,15 @@ __global__ __launch_bounds__(256) void k_step(Ctx c, SeqBatch b, int tiles_x, in
   if (role == 0) {
     const int n_tiles = max(1, cdiv(g.n_blk, kScoreTile));
     if (idx >= n_tiles) return;
-    score_tile<D, G>(c, i, seq, h, hi, g, idx, q, smem_topk.red, true);
+    // without MAW flags each tile also lists its candidates for the fast top-k
+    const bool fast = c.dm.maw_beta <= 0.0f && n_tiles <= kFastTiles;
+    score_tile<D, G>(c, i, seq, h, hi, g, idx, q, smem_topk, true, fast);
     uint32_t *ctr = &c.sc.arrive[unit * 2];
     if (!arrive_last(ctr, (unsigned)n_tiles, &s_flag)) return;
     uint32_t *lrows = reinterpret_cast<uint32_t *>(smem_raw + sizeof(TopkSmem));
-    topk_unit<D, G>(c, i, seq, h, hi, g, q, blk_idx, blk_cnt, k_cap, smem_topk, lrows,
-                    lrows_words, reinterpret_cast<unsigned long long *>(lrows + lrows_words));
+    if (!fast || !topk_fast<D, G>(c, i, seq, h, hi, g, q, blk_idx, blk_cnt, k_cap, smem_topk))
+      topk_unit<D, G>(c, i, seq, h, hi, g, q, blk_idx, blk_cnt, k_cap, smem_topk, lrows,
+                      lrows_words, reinterpret_cast<unsigned long long *>(lrows + lrows_words));
     if (threadIdx.x == 0) {
       st_dev(ctr, 0u);
       st_dev(&c.sc.ucnt[unit], min(min(g.kk, k_cap), hi.kcap));
