@@ -13,13 +13,15 @@ namespace sd {
 
 constexpr int kPage = SD_PAGE_SIZE;  // tokens per KV page
 constexpr int kLaunchSeqs = 64;      // sequences per kernel launch
-constexpr int kChunkTokens = 256;    // token slots of one split-K chunk
+constexpr int kPartPages = 40;       // attended pages per attention workgroup (target)
 constexpr int kScoreTile = 256;      // blocks scored by one workgroup
 constexpr int kTopkRegRows = 20;     // top-k rows of 64 block words kept in registers
 constexpr int kTopkUnc = 512;        // uncertain blocks the top-k lists in LDS
 constexpr int kFastTiles = 8;        // score tiles per unit of the fast top-k, at most
+constexpr int kPtLds = 4096;         // page-table entries a selected chunk copies to LDS, at most
 constexpr int kFuseSlots = 256;      // partial slots per query head, at most
 constexpr int kFuseSelLds = 2048;    // fusion keeps the selection in LDS up to this
+constexpr int kFusePgLds = 2048;     // and the attended pages' masses up to this
 
 // Per-KV-head constants, resident in device memory for the context's life
 // (read with uniform addresses, so they come through the scalar cache).
@@ -27,9 +29,7 @@ struct HeadInfo {
   int32_t S;             // block size in tokens
   int32_t ppm;           // budget, parts per million of N
   int32_t nbmax;         // ceil(max_seq_len / S): blocks per sequence
-  int32_t chunk_blocks;  // kChunkTokens / S
   int32_t kcap;          // most blocks ever selected on this head
-  int32_t pd;            // partial slots reserved for dense chunks
   int64_t summ_off;      // uint16 offset of this head's summary region
   int64_t maw_off;       // float offset of this head's MAW region
 };
@@ -53,7 +53,7 @@ struct AppendBatch {
 // Device state of one layer.
 struct LayerDev {
   uint16_t *k;     // [num_pages][Hkv][16][d] bf16
-  uint16_t *v;     // [num_pages][Hkv][16][d] bf16
+  uint16_t *v;     // [num_pages][Hkv][d][16] bf16: V pages stored transposed
   int32_t *pt;     // [max_seqs][pages_per_seq]
   uint16_t *summ;  // per head h: [max_seqs][d/4][nbmax_h][8] bf16
   float *maw;      // per head h: [max_seqs][nbmax_h]
@@ -68,7 +68,8 @@ struct Dims {
   float maw_decay;
   float maw_beta;
   int32_t key_stride;  // uint32 keys per (seq, kv head) in scratch
-  int32_t ndt_cap;     // dense-touching block slots per (seq, kv head)
+  int32_t lm_sel0;     // log-mass slots of dense pages; selected pages follow
+  int32_t lm_cap;      // log-mass slots per (seq, query head)
   int32_t kcap;        // selected block slots per (seq, kv head)
 };
 
@@ -81,15 +82,17 @@ struct Scratch {
   uint32_t *ukeys;   // [max_seqs][Hkv][key_stride] their exact keys
   uint32_t *unit_acc;  // [max_seqs][Hkv][2] error bound (float bits, max) and
                        // flagged candidates (count) of the score tiles; 0 between steps
-  float *lm_dense;   // [max_seqs][Hq][ndt_cap] log-mass of dense block slots
-  float *lm_sel;     // [max_seqs][Hq][kcap] log-mass of selected block slots
+  float *lm_pg;      // [max_seqs][Hq][lm_cap] log softmax mass of each attended page
   int32_t *usel;     // [max_seqs][Hkv][kcap] selected block ids (attend copy)
   int32_t *ucnt;     // [max_seqs][Hkv] selected block count (attend copy)
   uint32_t *arrive;  // [max_seqs][Hkv][2] last-arriver counters (kept at 0)
   unsigned long long *cand;  // [max_seqs][Hkv][key_stride] per-tile candidate lists
                              // (key << 32 | block), tile t's at [t*kScoreTile, ...)
   uint32_t *tcnt;    // [max_seqs][Hkv][kFastTiles] entries of each tile's list
-  uint32_t *ready;   // [max_seqs][Hkv] step number of the unit's published selection
+  uint32_t *scored;  // [max_seqs][Hkv] step number once every score tile of the unit is done
+  unsigned long long *rtag;    // [max_seqs][Hkv] step << 32 | selected count, published
+                               // after the selection
+  unsigned long long *seltag;  // [max_seqs][Hkv][kcap] step << 32 | block of the selection
   uint32_t *err;     // [1] nonzero once a step kernel's wait ran out of time
 };
 
@@ -108,32 +111,29 @@ hipError_t launch_append(const Ctx &c, const AppendBatch &b, int max_new,
                          int max_touch_blocks, const uint16_t *k_new,
                          const uint16_t *v_new, hipStream_t st);
 
-// Score + top-k (last arriver per unit).  With dense_o_part set, the
-// dchunks_x dense sink/window chunks per unit are attended in the same launch.
-hipError_t launch_select(const Ctx &c, const SeqBatch &b, int max_blocks,
-                         const uint16_t *q, int32_t *blk_idx, int32_t *blk_cnt,
-                         int32_t k_cap, int dchunks_x, float *dense_o_part,
-                         float *dense_lse_part, int32_t p_cap, hipStream_t st);
+// Score + top-k (last arriver per unit).
+hipError_t launch_select(const Ctx &c, const SeqBatch &b, int max_blocks, const uint16_t *q,
+                         int32_t *blk_idx, int32_t *blk_cnt, int32_t k_cap, hipStream_t st);
 
-// One workgroup per partial slot (dense chunks at [0, pd), selected chunks
-// after; unused slots emptied).
-hipError_t launch_attend(const Ctx &c, const SeqBatch &b, const uint16_t *q,
-                         const int32_t *blk_idx, const int32_t *blk_cnt,
-                         int32_t k_cap, float *o_part, float *lse_part,
-                         int32_t p_cap, hipStream_t st);
+// Attention: P workgroups per unit, one partial slot each (slots [P, p_cap)
+// emptied); keeps a copy of the selection for the fusion call.
+hipError_t launch_attend(const Ctx &c, const SeqBatch &b, int P, const uint16_t *q,
+                         const int32_t *blk_idx, const int32_t *blk_cnt, int32_t k_cap,
+                         float *o_part, float *lse_part, int32_t p_cap, hipStream_t st);
 
-// The whole step in one launch: scoring, top-k, dense and selected chunks,
-// fusion and MAW (epoch: a nonzero number that differs between launches).
-hipError_t launch_step(const Ctx &c, const SeqBatch &b, int max_blocks, const uint16_t *q,
-                       int32_t *blk_idx, int32_t *blk_cnt, int32_t k_cap, int dchunks_x,
-                       int schunks_x, float *o_part, float *lse_part, int32_t p_cap,
-                       float *o, float *lse, uint32_t epoch, hipStream_t st);
+// The whole step in one launch: scoring, top-k, P attention parts per unit,
+// fusion and MAW (epoch: a nonzero number that differs between launches;
+// ptl_cap: page-table entries a part may copy to LDS, 0 for none).
+hipError_t launch_step(const Ctx &c, const SeqBatch &b, int max_blocks, int P, const uint16_t *q,
+                       int32_t *blk_idx, int32_t *blk_cnt, int32_t k_cap, float *o_part,
+                       float *lse_part, int32_t p_cap, float *o, float *lse, uint32_t epoch,
+                       int ptl_cap, hipStream_t st);
 
-// Fusion of the partials: with_maw = slots and MAW from the attend scratch
+// Fusion of the partials: with_maw = the P slots of the attend call and MAW
 // (layer call); otherwise every slot of p_cap is fused (layer -1).
-hipError_t launch_fuse(const Ctx &c, const SeqBatch &b, bool with_maw,
-                       const float *o_part, const float *lse_part,
-                       int32_t p_cap, float *o, float *lse, hipStream_t st);
+hipError_t launch_fuse(const Ctx &c, const SeqBatch &b, bool with_maw, int P,
+                       const float *o_part, const float *lse_part, int32_t p_cap,
+                       float *o, float *lse, hipStream_t st);
 
 hipError_t launch_fill_f32(float *p, size_t n, float v, hipStream_t st);
 

@@ -18,16 +18,16 @@
 //          carries the argument); block-based Quest (Extended reading notes).
 //
 // Work decomposition of one (sequence, KV head) "unit":
-//   * score tiles: 256 blocks per workgroup, one lane per block; the last
-//     tile to finish (atomic arrival counter) runs the unit's top-k;
-//   * dense chunks: the blocks touching the sinks or the recent window,
-//     attended over their dense tokens only;
-//   * selected chunks: the selected blocks, attended over their tokens that
-//     are not dense (so every token of T = D U selected is counted once);
-//   * fusion: partial slots [0, dense chunks) and [pd, pd + selected chunks)
-//     merged with the LSE identity, then the MAW update of every block.
+//   * score tiles: 256 blocks per workgroup; the last tile to finish (atomic
+//     arrival counter) runs the unit's top-k;
+//   * attention parts: P workgroups per unit share the unit's attended pages
+//     (the dense pages, then the pages of the selected blocks without their
+//     dense tokens, so every token of T = D U selected counts once); each
+//     streams its pages and writes one partial (O, lse);
+//   * fusion: the P partials merged with the LSE identity, then the MAW
+//     update of every block.
 // The fused step and the separate ABI calls run these same device functions
-// on the same slots, so their results are bitwise identical.
+// with the same P, so their results are bitwise identical.
 #include <algorithm>
 #include <cfloat>
 #include <cmath>
@@ -79,24 +79,8 @@ __device__ __forceinline__ bool arrive_last(uint32_t *counter, unsigned expected
   return *flag != 0;
 }
 
-// Arrival on a unit's fusion counter.  The fusion waits for the unit's dense
-// chunks, its selected chunks and the top-k itself (nd + ns + 1 arrivals);
-// ns is known from the published count once the top-k has arrived, and before
-// that the count cannot reach nd + 1, so a stale count is never used.
-__device__ __forceinline__ bool arrive_fuse(uint32_t *counter, int nd, const int32_t *ucnt,
-                                            int CB, int *flag) {
-  wait_vmem();
-  __syncthreads();
-  if (threadIdx.x == 0) {
-    const int prev = (int)__hip_atomic_fetch_add(counter, 1u, __ATOMIC_RELAXED,
-                                                 __HIP_MEMORY_SCOPE_AGENT);
-    bool last = false;
-    if (prev + 1 >= nd + 1) last = prev + 1 == nd + cdiv(ld_dev(ucnt), CB) + 1;
-    *flag = last;
-  }
-  __syncthreads();
-  return *flag != 0;
-}
+// Bound of every wait inside a launch.
+constexpr unsigned long long kWaitTicks = 20000000ull;  // 0.2 s of the 100 MHz clock
 
 __device__ __forceinline__ float wave_max(float x) {
 #pragma unroll
@@ -133,7 +117,7 @@ __device__ __forceinline__ int budget_blocks(int ppm, int N, int S) {
 // Geometry of one unit.  D = [0, ns) U [wlo, N) ([FLX] sinks, [HGCA] recent
 // window); blocks [0, hb) touch the sinks, blocks [tb, n_blk) the window.
 struct UG {
-  int N, S, n_blk, ns, wlo, hb, tb, n_dt, kk, CB;
+  int N, S, n_blk, ns, wlo, hb, tb, n_dt, kk;
 };
 __device__ __forceinline__ UG unit_geom(int N, const HeadInfo &hi, const Dims &dm) {
   UG g;
@@ -152,7 +136,6 @@ __device__ __forceinline__ UG unit_geom(int N, const HeadInfo &hi, const Dims &d
   g.n_dt = g.hb + (g.n_blk - g.tb);
   const int n_cand = g.ns < g.wlo ? cdiv(g.wlo, S) - g.ns / S : 0;
   g.kk = min(n_cand, budget_blocks(hi.ppm, N, S));
-  g.CB = hi.chunk_blocks;
   return g;
 }
 
@@ -176,26 +159,30 @@ __device__ __forceinline__ uint32_t order_key(float u) {
 
 // ---------------------------------------------------------------------------
 // Shared memory of the roles (one launch may host several roles).
+constexpr int kTileList = 64;  // blocks a score tile lists for the fast top-k, at most
 struct TopkSmem {
   int32_t ulist[kTopkUnc];  // uncertain blocks of the top-k, in index order
   uint32_t ukey[kTopkUnc];  // their exact keys
-  int32_t upos[kTopkUnc];   // their list positions (fast top-k)
   uint32_t tk[kScoreTile];  // keys of a score tile (fast top-k)
-  unsigned long long cm[kFastTiles];  // chosen uncertain entries (fast top-k)
+  int32_t tslot[kScoreTile];  // list slot of each block of a score tile, or -1
+  uint4 cs[kTileList][32];  // summaries of a score tile's listed blocks
+  double ue[kTileList * SD_MAX_GROUP];  // their exact scores, per head
+  unsigned long long bm[kFastTiles * kScoreTile / 64];  // chosen blocks (fast top-k)
+  unsigned long long srt[kFastTiles][kTileList];  // sorted lists (tile; fast top-k)
+  int rk[4][kTileList];  // partial ranks of a tile's list
   float qs[SD_MAX_GROUP * 128];
   double ud[16];
   uint32_t red[8];
+  int nlist;
   int last;
 };
 
 template <int G>
 struct FuseSmem {
-  float w[G][kFuseSlots];  // per-slot LSE weights
+  float w[G][kFuseSlots];   // per-slot LSE weights
   float lse[G];
-  float adense[kFuseSlots];
-  float asel[kFuseSelLds];
-  int32_t sel[kFuseSelLds];
-  int last;
+  int32_t sel[kFuseSelLds];  // the selection
+  float pm[kFusePgLds];      // softmax mass of each attended page, summed over heads
 };
 
 // ---------------------------------------------------------------------------
@@ -223,7 +210,13 @@ __device__ void append_scatter(const Ctx &c, const AppendBatch &b, int i,
     const int page = c.L.pt[(size_t)seq * c.dm.pages_per_seq + pos / kPage];
     const size_t dst = (((size_t)page * Hkv + h) * kPage + (pos % kPage)) * V8 + c8;
     reinterpret_cast<uint4 *>(c.L.k)[dst] = ks[idx];
-    reinterpret_cast<uint4 *>(c.L.v)[dst] = vs[idx];
+    // V page transposed: element (channel ch, token t) at ch * 16 + t
+    const uint4 vv = vs[idx];
+    const uint32_t w[4] = {vv.x, vv.y, vv.z, vv.w};
+    uint16_t *vt = c.L.v + ((size_t)page * Hkv + h) * D * kPage + (size_t)(8 * c8) * kPage +
+                   (pos % kPage);
+#pragma unroll
+    for (int e = 0; e < 8; ++e) vt[(size_t)e * kPage] = (uint16_t)(w[e >> 1] >> (16 * (e & 1)));
   }
 }
 
@@ -369,56 +362,160 @@ __device__ __forceinline__ float score_eps(float E, float A) {
   return 3.1e-5f * E + 1.2e-7f * fabsf(A) + 1e-30f;
 }
 
-// Candidate list of one score tile for the fast top-k (one wave; no MAW
-// flags, so every candidate is ranked and k = kk).  With C_t > kk candidates
-// in the tile, let L be the tile's kk-th largest approximate key and eps_t its
-// largest error bound.  A block with A < L - 2 eps_t has kk blocks in its own
-// tile whose exact scores are strictly larger (each at least L - eps_t >
-// A + eps_t), so it cannot be in the unit's top kk and is dropped.  Bisection
-// narrows [a, b] around L to within eps_t; the tile keeps the blocks with
-// A >= a - 2 eps_t, in ascending block order.
-__device__ __forceinline__ void tile_candidates(const Ctx &c, int seq, int h, const UG &g, int tile,
-                                                const uint32_t *tk /* LDS [kScoreTile] */,
-                                                double eps_t) {
-  const int lane = threadIdx.x & 63;
-  constexpr int TR = kScoreTile / 64;
+// Exact score of one block for one query head: sum_c max(q_c m_c, q_c M_c)
+// in double in channel order, the plain sequential double sum.  The larger
+// product is q_c M_c for q_c >= 0 and q_c m_c otherwise (m_c <= M_c; with
+// q_c = 0 both are zeros, which leave the sum unchanged), and a product of
+// two bf16 values is exact in double, so one fma per channel rounds as the
+// product-then-add of the definition.
+__device__ __forceinline__ float upper_term(float qv, uint32_t mm) {
+  return qv >= 0.0f ? bf16_hi(mm) : bf16_lo(mm);
+}
+// Exact list of one score tile for the fast top-k (no MAW flags, kk <= 64):
+// the tile's kk best blocks by exact score, as keys (exact order key << 32 |
+// ~block), descending, padded with zeros.  Wave 0 bounds the tile's kk-th
+// largest approximate key L from below by a few bisection steps (a <= L,
+// count(>= a) >= kk); every block with exact score among the tile's kk best
+// has an approximate score >= a - 2 eps_t (kk blocks have exact scores >=
+// a - eps_t), so only those are listed, at most kTileList.  All waves stage
+// the listed blocks' summaries in LDS, score them exactly (double, channel
+// order, as the oracle does), rank the keys and wave 0 publishes the list in
+// descending order.  A tile that
+// would list more publishes the count kTileOverflow instead (the top-k then
+// takes the full path).  Every thread of the workgroup calls it, after the
+// tile's keys are in sm.tk.
+constexpr int kTileSteps = 12;
+constexpr uint32_t kTileOverflow = 0xffffffffu;
+template <int D, int G>
+__device__ __forceinline__ void tile_exact_list(const Ctx &c, int i, int seq, int h,
+                                                const UG &g, int tile,
+                                                const uint16_t *__restrict__ q,
+                                                const uint4 (&kf)[kScoreTile / 64][D / 16],
+                                                double eps_t, TopkSmem &sm) {
+  const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
+  const int r16 = lane & 15, lgrp = lane >> 4;
+  constexpr int TR = kScoreTile / 64, MM = D / 16;
   const size_t unit = (size_t)seq * c.dm.Hkv + h;
   const int kk = g.kk;
-  uint32_t x[TR], lo = 0xffffffffu, hi = 0u;
-  int ct = 0;
+  if (wv == 0) {
+    uint32_t x[TR], lo = 0xffffffffu, hi_k = 0u;
+    int ct = 0;
 #pragma unroll
-  for (int r = 0; r < TR; ++r) {
-    x[r] = tk[r * 64 + lane];
-    if (x[r] >= 2u) {
-      lo = min(lo, x[r]);
-      hi = max(hi, x[r]);
+    for (int r = 0; r < TR; ++r) {
+      x[r] = sm.tk[r * 64 + lane];
+      if (x[r] >= 2u) {
+        lo = min(lo, x[r]);
+        hi_k = max(hi_k, x[r]);
+      }
+      ct += count_lanes(x[r] >= 2u);
     }
-    ct += count_lanes(x[r] >= 2u);
-  }
-  uint32_t dmin = kk > 0 ? 2u : 0xffffffffu;  // keys below dmin are dropped
-  if (kk > 0 && ct > kk) {
-    uint32_t a = wave_min_u(lo), b = wave_max_u(hi);
-    while (a < b && (double)key_to_float(b) - (double)key_to_float(a) > eps_t) {
-      const uint32_t mid = a + ((b - a) >> 1) + 1u;
-      int cm = 0;
+    uint32_t dmin = 2u;  // keys below dmin are not listed
+    if (kk > 0 && ct > kk) {
+      uint32_t a = wave_min_u(lo), b = wave_max_u(hi_k);
+      int ca = ct;  // count(>= a)
+      for (int it = 0; it < kTileSteps && a < b && ca > kTileList - 8; ++it) {
+        const uint32_t mid = a + ((b - a) >> 1) + 1u;
+        int cm = 0;
 #pragma unroll
-      for (int r = 0; r < TR; ++r) cm += count_lanes(x[r] >= mid);
-      if (cm >= kk) a = mid; else b = mid - 1u;
+        for (int r = 0; r < TR; ++r) cm += count_lanes(x[r] >= mid);
+        if (cm >= kk) {
+          a = mid;
+          ca = cm;
+        } else {
+          b = mid - 1u;
+        }
+      }
+      dmin = max(2u, order_key(__double2float_ru((double)key_to_float(a) - 2.0 * eps_t)));
     }
-    dmin = order_key(__double2float_ru((double)key_to_float(a) - 2.0 * eps_t));
-  }
-  unsigned long long *dst = c.sc.cand + unit * c.dm.key_stride + (size_t)tile * kScoreTile;
-  int n = 0;
+    int n = 0;
 #pragma unroll
-  for (int r = 0; r < TR; ++r) {
-    const bool in = x[r] >= 2u && x[r] >= dmin;
-    const unsigned long long m = __ballot(in);
-    if (in)
-      st_dev(&dst[n + lanes_below(m)],
-             ((unsigned long long)x[r] << 32) | (uint32_t)(tile * kScoreTile + r * 64 + lane));
-    n += __popcll(m);
+    for (int r = 0; r < TR; ++r) {
+      const bool in = kk > 0 && x[r] >= dmin;
+      const unsigned long long m = __ballot(in);
+      const int pos = n + lanes_below(m);
+      const bool put = in && pos < kTileList;
+      sm.tslot[r * 64 + lane] = put ? pos : -1;
+      if (put) sm.ulist[pos] = tile * kScoreTile + r * 64 + lane;
+      n += __popcll(m);
+    }
+    if (lane == 0) sm.nlist = n;
   }
-  if (lane == 0) st_dev(&c.sc.tcnt[unit * kFastTiles + tile], (uint32_t)n);
+  __syncthreads();
+  const int n = sm.nlist;
+  unsigned long long *dst = c.sc.cand + unit * c.dm.key_stride + (size_t)tile * kTileList;
+  if (n > kTileList) {
+    if (tid == 0) st_dev(&c.sc.tcnt[unit * kFastTiles + tile], kTileOverflow);
+    return;
+  }
+  // stage the listed blocks' summaries (lane (r16, lgrp) holds channel quads
+  // 4 mm + lgrp of block r16 of its groups) and the group's query
+#pragma unroll
+  for (int gi = 0; gi < TR; ++gi) {
+    const int sl = sm.tslot[wv * 64 + gi * 16 + r16];
+    if (sl >= 0) {
+#pragma unroll
+      for (int mm = 0; mm < MM; ++mm) sm.cs[sl][4 * mm + lgrp] = kf[gi][mm];
+    }
+  }
+  __syncthreads();
+  // exact score of (listed block, head) pairs: the plain sequential sum
+  // (LDS reads batched eight channel quads at a time)
+  for (int p = tid; p < n * G; p += 256) {
+    const int b = p / G, gg = p - b * G;
+    const float4 *qv = reinterpret_cast<const float4 *>(sm.qs + gg * D);
+    double acc = 0.0;
+#pragma unroll
+    for (int c8 = 0; c8 < D / 4; c8 += 8) {
+      uint4 w[8];
+      float4 qq[8];
+#pragma unroll
+      for (int t = 0; t < 8; ++t) {
+        w[t] = sm.cs[b][c8 + t];
+        qq[t] = qv[c8 + t];
+      }
+#pragma unroll
+      for (int t = 0; t < 8; ++t) {
+        const uint32_t ws[4] = {w[t].x, w[t].y, w[t].z, w[t].w};
+        const float qf[4] = {qq[t].x, qq[t].y, qq[t].z, qq[t].w};
+#pragma unroll
+        for (int j = 0; j < 4; ++j) acc = fma((double)qf[j], (double)upper_term(qf[j], ws[j]), acc);
+      }
+    }
+    sm.ue[p] = acc;
+  }
+  __syncthreads();
+  // keys (every wave, lane = list entry), then each wave counts the larger
+  // keys among 16 entries: the rank of an entry is its place in the sorted list
+  unsigned long long key = 0ull;
+  if (lane < n) {
+    double best = sm.ue[lane * G];
+#pragma unroll
+    for (int gg = 1; gg < G; ++gg) best = sm.ue[lane * G + gg] > best ? sm.ue[lane * G + gg] : best;
+    const int blk = sm.ulist[lane];  // listed in block order
+    key = ((unsigned long long)order_key((float)best) << 32) | (uint32_t)~(uint32_t)blk;
+  }
+  int rk = 0;
+#pragma unroll
+  for (int t = 0; t < 16; ++t) {
+    const int src = 16 * wv + t;
+    const unsigned long long o =
+        ((unsigned long long)(uint32_t)__builtin_amdgcn_readlane((int)(key >> 32), src) << 32) |
+        (uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)key, src);
+    rk += o > key ? 1 : 0;
+  }
+  sm.rk[wv][lane] = rk;
+  __syncthreads();
+  if (wv == 0) {
+    // entries past n are zeros; they keep their own places (every listed key
+    // is larger, so listed ranks are below n)
+    const int pos = lane < n ? sm.rk[0][lane] + sm.rk[1][lane] + sm.rk[2][lane] + sm.rk[3][lane]
+                             : lane;
+    sm.srt[0][pos] = key;
+    __builtin_amdgcn_s_waitcnt(0xc07f);
+    __builtin_amdgcn_wave_barrier();
+    st_dev(&dst[lane], sm.srt[0][lane]);
+    if (lane == 0) st_dev(&c.sc.tcnt[unit * kFastTiles + tile], (uint32_t)min(n, kk));
+  }
 }
 
 // decay_maw: also write r*MAW for the tile's blocks (the fused step; the
@@ -435,18 +532,17 @@ __device__ __attribute__((always_inline)) void score_tile(const Ctx &c, int i, i
   const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
   const int r16 = lane & 15, lgrp = lane >> 4;
   const int base = tile * kScoreTile + wv * 16 * GPW;
-  const bool active = base < g.n_blk;
   const uint4 *sp = reinterpret_cast<const uint4 *>(c.L.summ + hi.summ_off +
                                                     (size_t)seq * C4 * hi.nbmax * 8);
-  // every load of the tile is issued before any is used
+  // every load of the tile is issued before any is used (block indices are
+  // clamped, so the loads of a wave past the last block stay in bounds)
   uint4 kf[GPW][MM];
   const int nb_last = max(g.n_blk - 1, 0);
 #pragma unroll
   for (int gi = 0; gi < GPW; ++gi) {
     const int blk = min(base + gi * 16 + r16, nb_last);
 #pragma unroll
-    for (int mm = 0; mm < MM; ++mm)
-      kf[gi][mm] = active ? sp[(size_t)(4 * mm + lgrp) * hi.nbmax + blk] : make_uint4(0, 0, 0, 0);
+    for (int mm = 0; mm < MM; ++mm) kf[gi][mm] = sp[(size_t)(4 * mm + lgrp) * hi.nbmax + blk];
   }
   const int qh0 = h * G;
   const uint16_t *qrow = q + ((size_t)i * c.dm.Hq + qh0 + min(r16, G - 1)) * D;
@@ -480,6 +576,16 @@ __device__ __attribute__((always_inline)) void score_tile(const Ctx &c, int i, i
       o4[2 * t + 1] = hi_neg | (hi_pos << 16);
     }
     qa[mm] = r16 < G ? make_uint4(o4[0], o4[1], o4[2], o4[3]) : make_uint4(0, 0, 0, 0);
+  }
+  if (publish && wv == 0 && r16 < G) {  // the query as floats, for the exact list
+#pragma unroll
+    for (int mm = 0; mm < MM; ++mm) {
+      float *d4 = sm.qs + r16 * D + 4 * (4 * mm + lgrp);
+      d4[0] = bf16_lo(qw[mm].x);
+      d4[1] = bf16_hi(qw[mm].x);
+      d4[2] = bf16_lo(qw[mm].y);
+      d4[3] = bf16_hi(qw[mm].y);
+    }
   }
   const uint32_t absm = 0x7fff7fffu;
   float emax = 0.0f;
@@ -545,21 +651,12 @@ __device__ __attribute__((always_inline)) void score_tile(const Ctx &c, int i, i
     const uint32_t f = red[4] + red[5] + red[6] + red[7];
     if (f) __hip_atomic_fetch_add(acc + 1, f, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
   }
-  if (publish && wv == 0) {
+  if (publish) {
     const double eps_t = (double)__uint_as_float(max(max(red[0], red[1]), max(red[2], red[3])));
-    tile_candidates(c, seq, h, g, tile, sm.tk, eps_t);
+    tile_exact_list<D, G>(c, i, seq, h, g, tile, q, kf, eps_t, sm);
   }
 }
 
-// Exact score of one block for one query head: sum_c max(q_c m_c, q_c M_c)
-// in double in channel order, the plain sequential double sum.  The larger
-// product is q_c M_c for q_c >= 0 and q_c m_c otherwise (m_c <= M_c; with
-// q_c = 0 both are zeros, which leave the sum unchanged), and a product of
-// two bf16 values is exact in double, so one fma per channel rounds as the
-// product-then-add of the definition.
-__device__ __forceinline__ float upper_term(float qv, uint32_t mm) {
-  return qv >= 0.0f ? bf16_hi(mm) : bf16_lo(mm);
-}
 template <int D>
 __device__ double exact_score_seq(const Ctx &c, int seq, const HeadInfo &hi, int blk,
                                   const float *qs /* LDS [D] of this head */) {
@@ -668,7 +765,8 @@ __device__ __attribute__((always_inline)) void topk_unit(const Ctx &c, int i, in
                           const UG &g, const uint16_t *__restrict__ q,
                           int32_t *__restrict__ blk_idx, int32_t *__restrict__ blk_cnt,
                           int k_cap, TopkSmem &sm, uint32_t *lrows, int lrows_words,
-                          unsigned long long *dmask /* LDS, one word per row */) {
+                          unsigned long long *dmask /* LDS, one word per row */,
+                          unsigned long long *tagd = nullptr, uint32_t epoch = 0) {
   if (threadIdx.x >= 64) return;
   const int lane = threadIdx.x;
   const int n = g.n_blk, rows = cdiv(n, 64);
@@ -938,7 +1036,11 @@ __device__ __attribute__((always_inline)) void topk_unit(const Ctx &c, int i, in
     const bool ch = v == 1u || v > kb_hi || ((dm >> lane) & 1ull);
     const unsigned long long mc = __ballot(ch);
     const int o = ob + lanes_below(mc);
-    if (ch && o < k_cap) st_dev(&dst[o], r * 64 + lane);
+    if (ch && o < k_cap) {
+      st_dev(&dst[o], r * 64 + lane);
+      if (tagd && o < c.dm.kcap)
+        st_dev(&tagd[o], ((unsigned long long)epoch << 32) | (uint32_t)(r * 64 + lane));
+    }
     ob += __popcll(mc);
   };
   {
@@ -956,135 +1058,109 @@ __device__ __attribute__((always_inline)) void topk_unit(const Ctx &c, int i, in
   }
 }
 
-// Fast top-k of one unit from the score tiles' candidate lists (one wave; no
-// MAW flags).  At most 64 entries per tile are loaded in one batch; then the
-// steps of topk_unit run on those entries: the kk-th largest approximate key
-// by bisection to within eps, the band, exact re-scoring of the blocks in it
-// (ties to the lower index), and the ordered compaction.  The entries are in
-// ascending block order (tile by tile).  Returns false, before writing
-// anything, when a tile listed more than 64 entries or the band holds more
-// than 64 blocks; the caller then runs topk_unit on the full keys.
+// Fast top-k of one unit from the score tiles' exact lists (no MAW flags,
+// kk <= kTileList; every thread of the workgroup calls it and gets the same
+// result).  The unit's kk best blocks are among the kk best of their own
+// tiles.  The rank of entry p of tile r's descending list among all listed
+// keys is p plus, for every other tile, the number of its keys above (a
+// binary search of its list in LDS); the entries of rank below kk are the
+// unit's top kk in (exact score desc, index asc) order.  Each is written at
+// its place in ascending block order, read off an LDS bitmap of the chosen
+// blocks.  Returns false, before writing anything, when a tile overflowed
+// its list; the caller then runs topk_unit on the full keys.
 template <int D, int G>
 __device__ __attribute__((always_inline)) bool topk_fast(const Ctx &c, int i, int seq, int h,
                                                          const HeadInfo &hi, const UG &g,
-                                                         const uint16_t *__restrict__ q,
                                                          int32_t *__restrict__ blk_idx,
                                                          int32_t *__restrict__ blk_cnt, int k_cap,
-                                                         TopkSmem &sm) {
-  if (threadIdx.x >= 64) return true;
-  const int lane = threadIdx.x;
+                                                         TopkSmem &sm,
+                                                         unsigned long long *tagd = nullptr,
+                                                         uint32_t epoch = 0) {
+  const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
   const size_t unit = (size_t)seq * c.dm.Hkv + h;
   const int n_tiles = max(1, cdiv(g.n_blk, kScoreTile));
-  // one batch: entry counts, entries, error bound, the group's query
   const unsigned long long *cl = c.sc.cand + unit * c.dm.key_stride;
+  const int kk = g.kk;
+  const int nw = cdiv(g.n_blk, 64);
+  // wave w holds lists w and w + 4
+  constexpr int RW = kFastTiles / 4;
+  unsigned long long e[RW];
   uint32_t cntv[kFastTiles];
-  unsigned long long e[kFastTiles];
 #pragma unroll
-  for (int r = 0; r < kFastTiles; ++r) {
-    cntv[r] = ld_dev(&c.sc.tcnt[unit * kFastTiles + r]);
-    e[r] = ld_dev(&cl[(size_t)(r < n_tiles ? r : 0) * kScoreTile + lane]);
+  for (int rr = 0; rr < RW; ++rr) {
+    const int r = wv + 4 * rr;
+    e[rr] = r < n_tiles ? ld_dev(&cl[(size_t)r * kTileList + lane]) : 0ull;
   }
-  const uint32_t eps_bits = ld_dev(&c.sc.unit_acc[2 * unit]);
-  constexpr int QPL = (G * D + 63) / 64;
-  const uint16_t *qg = q + ((size_t)i * c.dm.Hq + (size_t)h * G) * D;
-  uint16_t qv[QPL];
 #pragma unroll
-  for (int r = 0; r < QPL; ++r) qv[r] = qg[min(r * 64 + lane, G * D - 1)];
-
+  for (int r = 0; r < kFastTiles; ++r)
+    cntv[r] = r < n_tiles ? ld_dev(&c.sc.tcnt[unit * kFastTiles + r]) : 0u;
   bool ok = true;
-  uint32_t x[kFastTiles];
-  int bl[kFastTiles];
 #pragma unroll
-  for (int r = 0; r < kFastTiles; ++r) {
-    const uint32_t cr = r < n_tiles ? cntv[r] : 0u;
-    ok = ok && cr <= 64u;
-    x[r] = lane < (int)cr ? (uint32_t)(e[r] >> 32) : 0u;
-    bl[r] = (int)(uint32_t)e[r];
-  }
+  for (int r = 0; r < kFastTiles; ++r) ok = ok && cntv[r] != kTileOverflow;
   if (!ok) return false;
 #pragma unroll
-  for (int r = 0; r < QPL; ++r) {
-    const int xx = r * 64 + lane;
-    if (xx < G * D) sm.qs[xx] = __uint_as_float((uint32_t)qv[r] << 16);
+  for (int rr = 0; rr < RW; ++rr) {
+    const int r = wv + 4 * rr;
+    if (r < n_tiles) sm.srt[r][lane] = e[rr];
   }
-  if (lane < kFastTiles) sm.cm[lane] = 0ull;
-  const int kk = g.kk;
-  uint32_t kb_hi = 0xffffffffu;
-  if (kk > 0) {
-    const double eps = (double)__uint_as_float(eps_bits);
-    uint32_t lo = 0xffffffffu, hi_k = 0u;
+  if (tid < nw) sm.bm[tid] = 0ull;
+  if (tid == 0) sm.nlist = 0;
+  __syncthreads();
+  int n_take = 0;
+  int myblk[RW];
 #pragma unroll
-    for (int r = 0; r < kFastTiles; ++r)
-      if (x[r] >= 2u) {
-        lo = min(lo, x[r]);
-        hi_k = max(hi_k, x[r]);
-      }
-    uint32_t a = wave_min_u(lo), b = wave_max_u(hi_k);
-    while (a < b && (double)key_to_float(b) - (double)key_to_float(a) > eps) {
-      const uint32_t mid = a + ((b - a) >> 1) + 1u;
-      int cm = 0;
+  for (int rr = 0; rr < RW; ++rr) {
+    const int r = wv + 4 * rr;
+    const unsigned long long v = e[rr];
+    bool take = false;
+    if (r < n_tiles && lane < kk && v != 0ull) {
+      // keys of each list above v: binary searches of all lists in lockstep
+      int pr[kFastTiles];
 #pragma unroll
-      for (int r = 0; r < kFastTiles; ++r)
-        if (r < n_tiles) cm += count_lanes(x[r] >= mid);
-      if (cm >= kk) a = mid; else b = mid - 1u;
-    }
-    kb_hi = order_key(__double2float_rd((double)key_to_float(b) + 2.0 * eps));
-    const uint32_t kb_lo = order_key(__double2float_ru((double)key_to_float(a) - 2.0 * eps));
-    // uncertain entries in block order; sure ones counted
-    int n_in = 0, n_unc = 0;
+      for (int r2 = 0; r2 < kFastTiles; ++r2) pr[r2] = 0;
 #pragma unroll
-    for (int r = 0; r < kFastTiles; ++r) {
-      const bool unc = x[r] >= kb_lo && x[r] <= kb_hi;
-      const unsigned long long m = __ballot(unc);
-      const int p = n_unc + lanes_below(m);
-      if (unc && p < kTopkUnc) {
-        sm.ulist[p] = bl[r];
-        sm.upos[p] = r * 64 + lane;
-      }
-      n_unc += __popcll(m);
-      n_in += count_lanes(x[r] > kb_hi);
+      for (int st = 32; st > 0; st >>= 1)
+#pragma unroll
+        for (int r2 = 0; r2 < kFastTiles; ++r2)
+          if (r2 < n_tiles && sm.srt[r2][pr[r2] + st - 1] > v) pr[r2] += st;
+      int rank = lane;
+#pragma unroll
+      for (int r2 = 0; r2 < kFastTiles; ++r2)
+        if (r2 < n_tiles && r2 != r) rank += pr[r2] + (sm.srt[r2][pr[r2]] > v ? 1 : 0);
+      take = rank < kk;
     }
-    if (n_unc > 64) return false;
-    const int kr2 = kk - n_in;  // >= 1: the kk-th entry is uncertain
-    // exact keys of the uncertain blocks, one lane quad per (block, head)
-    constexpr int BPR = 16 / G;
-    for (int u0 = 0; u0 < n_unc; u0 += BPR) {
-      const int pair = lane >> 2, uu = u0 + pair / G, gg = pair % G;
-      const bool on = pair < BPR * G && uu < n_unc;
-      const double U = exact_score_quad<D>(c, seq, hi, on ? sm.ulist[uu] : 0,
-                                           sm.qs + (on ? gg : 0) * D, on);
-      if ((lane & 3) == 0) sm.ud[pair] = U;
-      if (lane < BPR && u0 + lane < n_unc) {
-        double best = sm.ud[lane * G];
-        for (int xg = 1; xg < G; ++xg) best = sm.ud[lane * G + xg] > best ? sm.ud[lane * G + xg] : best;
-        sm.ukey[u0 + lane] = order_key((float)best);
-      }
-    }
-    // rank of each uncertain entry: larger exact keys, then equal keys listed
-    // earlier; the kr2 first are taken
-    const uint32_t ek = lane < n_unc ? sm.ukey[lane] : 0u;
-    int rank = 0;
-    for (int p = 0; p < n_unc; ++p) {
-      const uint32_t ep = (uint32_t)__builtin_amdgcn_readlane((int)ek, p);
-      rank += (ep > ek || (ep == ek && p < lane)) ? 1 : 0;
-    }
-    if (lane < n_unc && rank < kr2) {
-      const int pos = sm.upos[lane];
-      atomicOr(&sm.cm[pos >> 6], 1ull << (pos & 63));
-    }
+    myblk[rr] = take ? (int)~(uint32_t)v : -1;
+    if (take) atomicOr(&sm.bm[myblk[rr] >> 6], 1ull << (myblk[rr] & 63));
+    n_take += count_lanes(take);
   }
-  // ordered compaction
+  if (lane == 0 && n_take) atomicAdd(&sm.nlist, n_take);
+  __syncthreads();
+  if (sm.nlist != kk) return false;  // not expected: the lists are complete
+  // chosen blocks below each bitmap word: wave 0 scans the words' popcounts
+  if (wv == 0) {
+    const int cw = lane < nw ? __popcll(sm.bm[lane]) : 0;
+    int incl = cw;
+#pragma unroll
+    for (int off = 1; off < 64; off <<= 1) {
+      const int t = __shfl_up(incl, off, 64);
+      if (lane >= off) incl += t;
+    }
+    if (lane < nw) sm.rk[0][lane] = incl - cw;
+  }
+  __syncthreads();
   int32_t *dst = blk_idx + ((size_t)i * c.dm.Hkv + h) * k_cap;
-  int ob = 0;
 #pragma unroll
-  for (int r = 0; r < kFastTiles; ++r) {
-    const bool ch = (x[r] >= 2u && x[r] > kb_hi) || ((sm.cm[r] >> lane) & 1ull);
-    const unsigned long long mc = __ballot(ch);
-    const int o = ob + lanes_below(mc);
-    if (ch && o < k_cap) st_dev(&dst[o], bl[r]);
-    ob += __popcll(mc);
+  for (int rr = 0; rr < RW; ++rr) {
+    const int b = myblk[rr];
+    if (b >= 0) {
+      const int o = sm.rk[0][b >> 6] + __popcll(sm.bm[b >> 6] & ((1ull << (b & 63)) - 1ull));
+      if (o < k_cap) {
+        st_dev(&dst[o], b);
+        if (tagd && o < c.dm.kcap) st_dev(&tagd[o], ((unsigned long long)epoch << 32) | (uint32_t)b);
+      }
+    }
   }
-  if (lane == 0) {
+  if (tid == 0) {
     st_dev(&blk_cnt[(size_t)i * c.dm.Hkv + h], kk);
     st_dev(&c.sc.unit_acc[2 * unit], 0u);  // cleared for the next step
     st_dev(&c.sc.unit_acc[2 * unit + 1], 0u);
@@ -1114,237 +1190,380 @@ __device__ __forceinline__ float row_sum16(float x) {
   return x;
 }
 
-// attend: softmax attention of the G query heads of one KV head over one
-// chunk of its blocks ([HGCA] What carries the argument: dense window plus
-// selected entries, each part with its own normalisation statistics).  Each
-// wave owns 4 pages of the chunk end to end: page lookup, q.K with one
-// v_mfma_f32_16x16x32_bf16 tile per 16-token page (q rows padded to 16),
-// softmax over its tokens with DPP row reductions, p*V on fp32 VALU.  The
-// four waves meet once to merge their (max, sum, O) and write the chunk's
-// normalised O, its lse and the log softmax mass of each block (for MAW).
-template <int D, int G>
-struct AttSmem {
-  static constexpr int GP = G <= 4 ? 4 : 8;
-  static constexpr int PPW = kChunkTokens / kPage / 4;  // pages per wave
-  float p[4][PPW * kPage][GP];  // per-wave softmax weights of its token slots
-  float wo[4][G][D];            // per-wave unnormalised O
-  float wm[4][G];               // per-wave max (log2 units)
-  float wz[4][G];               // per-wave sum
-  float pmass[4 * PPW][G];      // per-page mass relative to its wave max
-};
-
 __device__ __forceinline__ unsigned long long bit_range(int a, int b) {
   if (b <= a) return 0ull;
   const unsigned long long hi = b >= 64 ? ~0ull : ((1ull << b) - 1ull);
   const unsigned long long lo = (1ull << a) - 1ull;  // a < b <= 64
   return hi & ~lo;
 }
-// Token mask of a block: its dense tokens (dense chunks) or its tokens outside
-// the dense set (selected chunks).
-__device__ __forceinline__ unsigned long long block_mask(const UG &g, int blk, bool dense) {
-  if (blk < 0 || blk >= g.n_blk) return 0ull;
-  const int lo = blk * g.S, cnt = min(g.S, g.N - lo);
-  const unsigned long long all = bit_range(0, cnt);
-  const unsigned long long dm = bit_range(0, min(max(g.ns - lo, 0), cnt)) |
-                                bit_range(min(max(g.wlo - lo, 0), cnt), cnt);
-  return dense ? dm : (all & ~dm);
+
+// ---------------------------------------------------------------------------
+// Page lists of the attention.  The attended set of a unit is T = D U the
+// selected blocks ([HGCA] What carries the argument: dense recent window plus
+// selected entries; union, so no token is counted twice), cut into 16-token
+// pages: first the pages holding dense tokens (sink pages [0, sp), then window
+// pages [wp, np)), each with its dense-token mask, then the pages of the
+// selected blocks in selection order, each with the mask of its tokens that
+// are not dense.  Position t of the unit's list is also the slot of the
+// page's log softmax mass (selected pages from lm_sel0 on).
+struct DenseList {
+  int sp, wp, np, n;
+};
+__device__ __forceinline__ DenseList dense_list(const UG &g) {
+  DenseList d;
+  d.np = cdiv(g.N, kPage);
+  d.sp = cdiv(g.ns, kPage);
+  d.wp = g.wlo < g.N ? max(d.sp, g.wlo / kPage) : d.np;
+  d.n = d.sp + (d.np - d.wp);
+  return d;
+}
+__device__ __forceinline__ int dense_page(const DenseList &d, int e) {
+  return e < d.sp ? e : d.wp + (e - d.sp);
+}
+// position of page pn in the dense list, or -1
+__device__ __forceinline__ int dense_pos(const DenseList &d, int pn) {
+  return pn < d.sp ? pn : ((pn >= d.wp && pn < d.np) ? d.sp + (pn - d.wp) : -1);
+}
+__device__ __forceinline__ int page_valid16(const UG &g, int pn) {
+  return (int)bit_range(0, min(max(g.N - pn * kPage, 0), kPage));
+}
+__device__ __forceinline__ int page_dense16(const UG &g, int pn) {
+  const int b = pn * kPage;
+  const int lo = min(max(g.wlo - b, 0), kPage), hi = min(max(g.N - b, 0), kPage);
+  return (int)(bit_range(0, min(max(g.ns - b, 0), kPage)) | bit_range(lo, hi));
 }
 
+// ---------------------------------------------------------------------------
+// Attention of one (unit, part): softmax attention of the G query heads of a
+// KV head over its share of the unit's pages ([HGCA] What carries the
+// argument: each partial carries its own normalisation statistics; split-K
+// decoding).  Wave w of part p takes list positions 4p + w + i * 4P.  Pages
+// stream through two register stages of two pages each: the loads of the
+// next stage are in flight while the current one computes.  Per stage:
+//   q.K: one v_mfma_f32_16x16x32_bf16 tile per page and 32 channels (rows =
+//        heads padded to 16, columns = the page's 16 tokens);
+//   softmax: online (running max and sum per head, O rescaled), DPP row
+//        reductions;
+//   p.V: the weights go through LDS into the MFMA A layout (row = head, 8
+//        tokens per lane), split into bf16 hi + lo parts; V pages are stored
+//        transposed ([channel][16 tokens]), so a lane's 8 tokens of one
+//        channel are one 16-byte load in the MFMA B layout; two MFMAs per
+//        16 output channels accumulate O in fp32.
+// The four waves merge their (max, sum, O) once at the end.
 template <int D, int G>
-__device__ __attribute__((always_inline)) void attend_chunk(const Ctx &c, int i, int seq, int h, const HeadInfo &hi,
-                             const UG &g, bool dense, int chunk, int cnt,
-                             const int32_t *__restrict__ sel,
-                             const uint16_t *__restrict__ q, float *__restrict__ o_part,
-                             float *__restrict__ lse_part, int p_cap,
-                             AttSmem<D, G> &sm) {
-  constexpr int GP = AttSmem<D, G>::GP;
-  constexpr int PPW = AttSmem<D, G>::PPW;
-  constexpr int KV4 = D / 32;                       // MFMA k-steps per page row
-  constexpr int LPR = D / 8, RPI = 64 / LPR, VIT = kPage / RPI;  // p*V layout
-  const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
-  const int S = g.S, CB = g.CB, PPB = S / kPage;
-  const int qh0 = h * G;
-  const int slot = dense ? chunk : hi.pd + chunk;
-  const int total = dense ? g.n_dt : cnt;
-  const int nb = min(CB, total - chunk * CB);
-  const size_t ohead = ((size_t)i * c.dm.Hq + qh0) * p_cap + slot;
-  if (nb <= 0) {  // empty slot: lse = -inf, O = 0
-    for (int x = tid; x < G * D; x += 256)
-      st_dev(&o_part[(ohead + (size_t)(x / D) * p_cap) * D + (x % D)], 0.0f);
-    if (tid < G) st_dev(&lse_part[ohead + (size_t)tid * p_cap], -INFINITY);
-    return;
-  }
-  const int npg = nb * PPB;
-  const int p0 = wv * PPW;
+struct AttLds {
+  float p[4][16][32];  // per wave: the stage's weights, [head row][token]
+  float wo[4][G][D];   // per wave: unnormalised O at the end
+  float wm[4][G];      // per wave: running max (log2 units)
+  float wz[4][G];      // per wave: running sum
+};
 
-  // ---- page lookup for this wave's pages (lanes 0..PPW-1), made uniform ----
-  int my_page = 0, my_mask = 0;
-  if (lane < PPW) {
-    const int p = p0 + lane;
-    if (p < npg) {
-      const int jj = p / PPB, pp = p - jj * PPB;
-      const int j = chunk * CB + jj;
-      const int blk = dense ? dense_block(g, j) : ld_dev(&sel[j]);
-      const unsigned long long m = block_mask(g, blk, dense);
-      if (!dense && pp == 0) st_dev(&c.sc.usel[((size_t)seq * c.dm.Hkv + h) * c.dm.kcap + j], blk);
-      my_mask = (int)((m >> (pp * kPage)) & 0xffffull);
-      if (my_mask)
-        my_page = c.L.pt[(size_t)seq * c.dm.pages_per_seq + (blk * S + pp * kPage) / kPage];
-    }
-  }
-  int pg[PPW], pmk[PPW];
-#pragma unroll
-  for (int pi = 0; pi < PPW; ++pi) {
-    pg[pi] = __builtin_amdgcn_readlane(my_page, pi);
-    pmk[pi] = __builtin_amdgcn_readlane(my_mask, pi);
-  }
+template <int D>
+struct KVStage {
+  uint4 k[2][D / 32];  // K of the two pages: lane = token r16, channels lgrp*D/4 + 8m
+  uint4 v[D / 16];     // V: lane = channel 16 nt + r16, tokens 8 lgrp .. 8 lgrp + 7
+};
 
-  // ---- loads: K rows in the MFMA B layout, V rows in the p*V layout -------
-  const int r16 = lane & 15, lgrp = lane >> 4;
-  const int cl = lane % LPR, lg = lane / LPR;
-  uint4 kf[PPW][KV4];
-  uint4 vf[PPW][VIT];
-#pragma unroll
-  for (int pi = 0; pi < PPW; ++pi) {
-    const size_t pbase = ((size_t)pg[pi] * c.dm.Hkv + h) * kPage;
-    const bool kon = (pmk[pi] >> r16) & 1;
-#pragma unroll
-    for (int m = 0; m < KV4; ++m)
-      kf[pi][m] = kon ? *reinterpret_cast<const uint4 *>(c.L.k + (pbase + r16) * D +
-                                                         lgrp * (D / 4) + 8 * m)
-                      : make_uint4(0, 0, 0, 0);
-  }
-#pragma unroll
-  for (int pi = 0; pi < PPW; ++pi) {
-    const size_t pbase = ((size_t)pg[pi] * c.dm.Hkv + h) * kPage;
-#pragma unroll
-    for (int it = 0; it < VIT; ++it) {
-      const int r = it * RPI + lg;
-      vf[pi][it] = ((pmk[pi] >> r) & 1)
-                       ? *reinterpret_cast<const uint4 *>(c.L.v + (pbase + r) * D + 8 * cl)
-                       : make_uint4(0, 0, 0, 0);
-    }
-  }
-  // q in the MFMA A layout: row r16 = head (zero past G), same channel order
-  uint4 qa[KV4];
-#pragma unroll
-  for (int m = 0; m < KV4; ++m)
-    qa[m] = r16 < G ? *reinterpret_cast<const uint4 *>(
-                          q + ((size_t)i * c.dm.Hq + qh0 + r16) * D + lgrp * (D / 4) + 8 * m)
-                    : make_uint4(0, 0, 0, 0);
+template <int D>
+struct AttWave {
+  float m[4], z[4];  // heads 4 lgrp + j: running max (log2 units), sum
+  f32x4 o[D / 16];   // unnormalised O: rows 4 lgrp + j, channel 16 nt + r16
+};
 
-  // ---- q.K: lane holds token r16 of page pi for heads 4*lgrp + jr --------
-  float sc[PPW][4];
+template <int D>
+__device__ __forceinline__ void load_stage(const Ctx &c, int h, int pg0, int pg1,
+                                           KVStage<D> &st) {
+  const int lane = threadIdx.x & 63, r16 = lane & 15, lgrp = lane >> 4;
 #pragma unroll
-  for (int pi = 0; pi < PPW; ++pi) {
+  for (int pi = 0; pi < 2; ++pi) {
+    const uint16_t *kp = c.L.k + ((((size_t)(pi ? pg1 : pg0) * c.dm.Hkv + h) * kPage + r16) * D +
+                                  lgrp * (D / 4));
+#pragma unroll
+    for (int m = 0; m < D / 32; ++m) st.k[pi][m] = *reinterpret_cast<const uint4 *>(kp + 8 * m);
+  }
+  const uint16_t *vp = c.L.v + (((size_t)(lgrp >= 2 ? pg1 : pg0) * c.dm.Hkv + h) * D + r16) * kPage +
+                       8 * (lgrp & 1);
+#pragma unroll
+  for (int nt = 0; nt < D / 16; ++nt)
+    st.v[nt] = *reinterpret_cast<const uint4 *>(vp + (size_t)nt * 16 * kPage);
+}
+
+__device__ __forceinline__ uint32_t bf16_rne_bits(float x) {
+  const uint32_t b = __float_as_uint(x);
+  return (b + 0x7fffu + ((b >> 16) & 1u)) >> 16;
+}
+
+// One stage of a wave: pages with token masks mk0, mk1 (uniform), log-mass
+// slots s0, s1 (-1: none).  lmb: log-mass rows of the unit's heads.  Rows of
+// padding heads (past G) carry finite values that are never stored.
+template <int D, int G>
+__device__ __forceinline__ void compute_stage(const Ctx &c, KVStage<D> &st, int mk0, int mk1,
+                                              int s0, int s1, const uint4 (&qa)[D / 32],
+                                              const uint4 &ones, AttWave<D> &W, float (*pl)[32],
+                                              float *lmb) {
+  const int lane = threadIdx.x & 63, r16 = lane & 15, lgrp = lane >> 4;
+  constexpr int NT = D / 16;
+  constexpr float kLn2 = 0.69314718055994530942f;
+  float sc[2][4];
+#pragma unroll
+  for (int pi = 0; pi < 2; ++pi) {
     f32x4 acc = {0.f, 0.f, 0.f, 0.f};
-    if (p0 + pi < npg) {
 #pragma unroll
-      for (int m = 0; m < KV4; ++m)
-        acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, qa[m]),
-                                                      __builtin_bit_cast(bf16x8, kf[pi][m]),
-                                                      acc, 0, 0, 0);
-    }
-    const bool on = (pmk[pi] >> r16) & 1;
+    for (int m = 0; m < D / 32; ++m)
+      acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, qa[m]),
+                                                    __builtin_bit_cast(bf16x8, st.k[pi][m]),
+                                                    acc, 0, 0, 0);
+    const bool on = (((pi ? mk1 : mk0) >> r16) & 1) != 0;
 #pragma unroll
-    for (int jr = 0; jr < 4; ++jr) sc[pi][jr] = on ? acc[jr] * c.dm.scale_log2 : -INFINITY;
+    for (int j = 0; j < 4; ++j) sc[pi][j] = on ? acc[j] * c.dm.scale_log2 : -INFINITY;
   }
-  // ---- softmax over the wave's tokens (per head = per (row, jr)) ----------
-  float wmax[4], wsum[4];
+  float al[4], mnv[4];
 #pragma unroll
-  for (int jr = 0; jr < 4; ++jr) {
-    float m = sc[0][jr];
+  for (int j = 0; j < 4; ++j) {
+    const float mn = fmaxf(W.m[j], row_max16(fmaxf(sc[0][j], sc[1][j])));
+    const bool none = mn == -INFINITY;
+    // exp2 of a non-positive argument (or -inf): the hardware v_exp_f32
+    al[j] = none ? 1.0f : __builtin_amdgcn_exp2f(W.m[j] - mn);
+    pl[4 * lgrp + j][r16] = none ? 0.0f : __builtin_amdgcn_exp2f(sc[0][j] - mn);
+    pl[4 * lgrp + j][16 + r16] = none ? 0.0f : __builtin_amdgcn_exp2f(sc[1][j] - mn);
+    W.m[j] = mn;
+    mnv[j] = mn;
 #pragma unroll
-    for (int pi = 1; pi < PPW; ++pi) m = fmaxf(m, sc[pi][jr]);
-    wmax[jr] = row_max16(m);
+    for (int nt = 0; nt < NT; ++nt) W.o[nt][j] *= al[j];
   }
-  float pmass_l[PPW][4];
-#pragma unroll
-  for (int jr = 0; jr < 4; ++jr) {
-    float z = 0.0f;
-#pragma unroll
-    for (int pi = 0; pi < PPW; ++pi) {
-      const float pr = (sc[pi][jr] == -INFINITY) ? 0.0f : exp2f(sc[pi][jr] - wmax[jr]);
-      sc[pi][jr] = pr;
-      pmass_l[pi][jr] = row_sum16(pr);
-      z += pmass_l[pi][jr];
-    }
-    wsum[jr] = z;
-  }
-  // weights to LDS (wave-private region), per-wave stats
-  if (lgrp * 4 < G) {
-#pragma unroll
-    for (int pi = 0; pi < PPW; ++pi)
-      *reinterpret_cast<float4 *>(&sm.p[wv][pi * kPage + r16][lgrp * 4]) =
-          make_float4(sc[pi][0], sc[pi][1], sc[pi][2], sc[pi][3]);
-    if (r16 == 0) {
-#pragma unroll
-      for (int jr = 0; jr < 4; ++jr) {
-        const int head = lgrp * 4 + jr;
-        if (head < G) {
-          sm.wm[wv][head] = wmax[jr];
-          sm.wz[wv][head] = wsum[jr];
-#pragma unroll
-          for (int pi = 0; pi < PPW; ++pi) sm.pmass[p0 + pi][head] = pmass_l[pi][jr];
-        }
-      }
-    }
-  }
-  __builtin_amdgcn_s_waitcnt(0xc07f);  // lgkmcnt(0): this wave's LDS writes are done
+  __builtin_amdgcn_s_waitcnt(0xc07f);  // lgkmcnt(0): the wave's LDS writes are done
   __builtin_amdgcn_wave_barrier();
+  // A operands: lane (head r16, tokens 8 lgrp .. 8 lgrp + 7); hi = weight
+  // truncated to bf16, lo = the exact remainder rounded to bf16
+  uint4 ahi, alo;
+  {
+    const float4 x0 = *reinterpret_cast<const float4 *>(&pl[r16][8 * lgrp]);
+    const float4 x1 = *reinterpret_cast<const float4 *>(&pl[r16][8 * lgrp + 4]);
+    const float f[8] = {x0.x, x0.y, x0.z, x0.w, x1.x, x1.y, x1.z, x1.w};
+    uint32_t hw[4], lw[4];
+#pragma unroll
+    for (int t = 0; t < 4; ++t) {
+      const uint32_t b0 = __float_as_uint(f[2 * t]) & 0xffff0000u;
+      const uint32_t b1 = __float_as_uint(f[2 * t + 1]) & 0xffff0000u;
+      hw[t] = (b0 >> 16) | b1;
+      lw[t] = bf16_rne_bits(f[2 * t] - __uint_as_float(b0)) |
+              (bf16_rne_bits(f[2 * t + 1] - __uint_as_float(b1)) << 16);
+    }
+    ahi = make_uint4(hw[0], hw[1], hw[2], hw[3]);
+    alo = make_uint4(lw[0], lw[1], lw[2], lw[3]);
+  }
+  // masked tokens have zero weight; their V is zeroed too, so that stale or
+  // unwritten slots cannot turn the products into NaN
+  if ((mk0 & mk1) != 0xffff) {
+    const int m8 = ((lgrp >= 2 ? mk1 : mk0) >> (8 * (lgrp & 1))) & 0xff;
+    uint32_t wm[4];
+#pragma unroll
+    for (int t = 0; t < 4; ++t)
+      wm[t] = (((m8 >> (2 * t)) & 1) ? 0x0000ffffu : 0u) | (((m8 >> (2 * t + 1)) & 1) ? 0xffff0000u : 0u);
+#pragma unroll
+    for (int nt = 0; nt < NT; ++nt) {
+      st.v[nt].x &= wm[0];
+      st.v[nt].y &= wm[1];
+      st.v[nt].z &= wm[2];
+      st.v[nt].w &= wm[3];
+    }
+  }
+#pragma unroll
+  for (int nt = 0; nt < NT; ++nt) {
+    W.o[nt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, ahi),
+                                                      __builtin_bit_cast(bf16x8, st.v[nt]),
+                                                      W.o[nt], 0, 0, 0);
+    W.o[nt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, alo),
+                                                      __builtin_bit_cast(bf16x8, st.v[nt]),
+                                                      W.o[nt], 0, 0, 0);
+  }
+  // sums of the same bf16 weights by MFMA against constant columns: column 0
+  // both pages, column 1 page 0, column 2 page 1
+  f32x4 zs = {0.f, 0.f, 0.f, 0.f};
+  zs = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, ahi),
+                                               __builtin_bit_cast(bf16x8, ones), zs, 0, 0, 0);
+  zs = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, alo),
+                                               __builtin_bit_cast(bf16x8, ones), zs, 0, 0, 0);
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    W.z[j] = fmaf(W.z[j], al[j], zs[j]);  // meaningful in lanes r16 == 0
+    const int hd = 4 * lgrp + j, sl = r16 == 1 ? s0 : s1;
+    if ((r16 == 1 || r16 == 2) && hd < G && sl >= 0) {
+      const float zp = zs[j];
+      st_dev(&lmb[(size_t)hd * c.dm.lm_cap + sl],
+             zp > 0.0f ? (mnv[j] + __builtin_amdgcn_logf(zp)) * kLn2 : -INFINITY);
+    }
+  }
+}
 
-  // ---- p*V on fp32 VALU ---------------------------------------------------
-  float o[G][8];
+// One wave over its positions of a page list of `total` entries: positions
+// gw + i NW.  resolve(t, pg, mk, sl) gives the page id, token mask and
+// log-mass slot of list position t; up to 64 positions are resolved at once,
+// one per lane.  gate (if set): streaming starts once it equals epoch (a
+// bounded wait that is not an error).
+template <int D, int G, class Resolve>
+__device__ __forceinline__ void wave_pages(const Ctx &c, int h, int gw, int NW, int total,
+                                           Resolve resolve, const uint32_t *gate, uint32_t epoch,
+                                           const uint4 (&qa)[D / 32], AttWave<D> &W,
+                                           float (*pl)[32], float *lmb) {
+  const int lane = threadIdx.x & 63;
+  const int nw = total > gw ? cdiv(total - gw, NW) : 0;
+  for (int b0 = 0; b0 < nw; b0 += 64) {
+    const int n = min(64, nw - b0);
+    int pg = 0, mk = 0, sl = -1;
+    if (lane < n) resolve(gw + (b0 + lane) * NW, pg, mk, sl);
+    if (gate && b0 == 0) {
+      const unsigned long long t0 = wall_clock64();
+      while (ld_dev(gate) != epoch && wall_clock64() - t0 < kWaitTicks) __builtin_amdgcn_s_sleep(4);
+    }
+    auto PG = [&](int t) { return __builtin_amdgcn_readlane(pg, min(t, n - 1)); };
+    auto MK = [&](int t) { return t < n ? __builtin_amdgcn_readlane(mk, t) : 0; };
+    auto SL = [&](int t) { return t < n ? __builtin_amdgcn_readlane(sl, t) : -1; };
+    const int ns = cdiv(n, 2);
+    // constant B columns of the weight sums: lane (column r16, tokens 8 lgrp ..)
+    const int r16 = lane & 15, lgrp = lane >> 4;
+    const uint32_t one2 = (r16 == 0 || (r16 == 1 && lgrp < 2) || (r16 == 2 && lgrp >= 2))
+                              ? 0x3f803f80u : 0u;
+    const uint4 ones = make_uint4(one2, one2, one2, one2);
+    KVStage<D> A, B;
+    load_stage<D>(c, h, PG(0), PG(1), A);
+    for (int s = 0;; s += 2) {
+      load_stage<D>(c, h, PG(2 * s + 2), PG(2 * s + 3), B);
+      compute_stage<D, G>(c, A, MK(2 * s), MK(2 * s + 1), SL(2 * s), SL(2 * s + 1), qa, ones, W,
+                          pl, lmb);
+      if (s + 1 >= ns) break;
+      load_stage<D>(c, h, PG(2 * s + 4), PG(2 * s + 5), A);
+      compute_stage<D, G>(c, B, MK(2 * s + 2), MK(2 * s + 3), SL(2 * s + 2), SL(2 * s + 3), qa,
+                          ones, W, pl, lmb);
+      if (s + 2 >= ns) break;
+    }
+  }
+}
+
+// Where a part finds the unit's selection.
+struct SelIn {
+  const int32_t *blk = nullptr;              // separate call: the caller's list
+  int cnt = 0;                               //   and its count
+  const unsigned long long *tag = nullptr;   // one-launch step: tagged entries
+  const unsigned long long *rtag = nullptr;  //   and the tagged count
+  const uint32_t *gate = nullptr;            //   dense pages wait for this
+  uint32_t epoch = 0;
+};
+
+template <int D, int G>
+__device__ __attribute__((always_inline)) void attend_part(const Ctx &c, int i, int seq, int h,
+                                                           const UG &g, int part, int P,
+                                                           const uint16_t *__restrict__ q,
+                                                           const SelIn &si,
+                                                           float *__restrict__ o_part,
+                                                           float *__restrict__ lse_part, int p_cap,
+                                                           AttLds<D, G> &sm,
+                                                           const int32_t *ptl /* LDS or null */,
+                                                           int *s_cnt) {
+  const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6, r16 = lane & 15, lgrp = lane >> 4;
+  constexpr int NT = D / 16;
+  const int qh0 = h * G, NW = 4 * P, gw = 4 * part + wv;
+  const int PPB = g.S / kPage;
+  const int32_t *pts = c.L.pt + (size_t)seq * c.dm.pages_per_seq;
+  uint4 qa[D / 32];
 #pragma unroll
-  for (int gg = 0; gg < G; ++gg)
+  for (int m = 0; m < D / 32; ++m)
+    qa[m] = r16 < G ? *reinterpret_cast<const uint4 *>(q + ((size_t)i * c.dm.Hq + qh0 + r16) * D +
+                                                       lgrp * (D / 4) + 8 * m)
+                    : make_uint4(0, 0, 0, 0);
+  AttWave<D> W;
 #pragma unroll
-    for (int e = 0; e < 8; ++e) o[gg][e] = 0.0f;
+  for (int j = 0; j < 4; ++j) {
+    W.m[j] = -INFINITY;
+    W.z[j] = 0.0f;
+  }
 #pragma unroll
-  for (int pi = 0; pi < PPW; ++pi) {
-    if (p0 + pi >= npg) continue;
-#pragma unroll
-    for (int it = 0; it < VIT; ++it) {
-      const int t = pi * kPage + it * RPI + lg;
-      float pw[GP];
-      {
-        const float4 x = *reinterpret_cast<const float4 *>(&sm.p[wv][t][0]);
-        pw[0] = x.x; pw[1] = x.y; pw[2] = x.z; pw[3] = x.w;
-        if constexpr (GP == 8) {
-          const float4 y = *reinterpret_cast<const float4 *>(&sm.p[wv][t][4]);
-          pw[4] = y.x; pw[5] = y.y; pw[6] = y.z; pw[7] = y.w;
+  for (int nt = 0; nt < NT; ++nt) W.o[nt] = f32x4{0.f, 0.f, 0.f, 0.f};
+  float(*pl)[32] = sm.p[wv];
+  float *lmb = c.sc.lm_pg + ((size_t)seq * c.dm.Hq + qh0) * c.dm.lm_cap;
+
+  // dense pages
+  const DenseList dl = dense_list(g);
+  wave_pages<D, G>(
+      c, h, gw, NW, dl.n,
+      [&](int t, int &pg, int &mk, int &sl) {
+        const int pn = dense_page(dl, t);
+        pg = pts[pn];
+        mk = page_dense16(g, pn);
+        sl = t;
+      },
+      si.gate, si.epoch, qa, W, pl, lmb);
+
+  // the selection
+  int cnt = si.cnt;
+  if (si.rtag) {
+    if (tid == 0) {
+      int n = -1;
+      const unsigned long long t0 = wall_clock64();
+      for (;;) {
+        const unsigned long long rt = ld_dev(si.rtag);
+        if ((uint32_t)(rt >> 32) == si.epoch) {
+          n = (int)(uint32_t)rt;
+          break;
         }
+        if (wall_clock64() - t0 > kWaitTicks) {
+          st_dev(&c.sc.err[0], 1u);
+          break;
+        }
+        __builtin_amdgcn_s_sleep(2);
       }
-      const uint32_t ws[4] = {vf[pi][it].x, vf[pi][it].y, vf[pi][it].z, vf[pi][it].w};
+      *s_cnt = n;
+    }
+    __syncthreads();
+    cnt = *s_cnt;
+  }
+  if (cnt > 0) {
+    wave_pages<D, G>(
+        c, h, gw, NW, cnt * PPB,
+        [&](int t, int &pg, int &mk, int &sl) {
+          const int j = t / PPB, pp = t - j * PPB;
+          int blk;
+          if (si.tag) {  // published before the count; the tag confirms it
+            unsigned long long e = ld_dev(&si.tag[j]);
+            const unsigned long long t0 = wall_clock64();
+            while ((uint32_t)(e >> 32) != si.epoch && wall_clock64() - t0 < kWaitTicks)
+              e = ld_dev(&si.tag[j]);
+            blk = (uint32_t)(e >> 32) == si.epoch ? (int)(uint32_t)e : 0;
+          } else {
+            blk = si.blk[j];
+          }
+          blk = min(max(blk, 0), max(g.n_blk - 1, 0));
+          const int pn = blk * PPB + pp;
+          const int pl_ = min(pn, dl.np - 1);  // pages past N are never read
+          pg = ptl ? ptl[pl_] : pts[pl_];
+          mk = page_valid16(g, pn) & ~page_dense16(g, pn);
+          sl = c.dm.lm_sel0 + t;
+        },
+        nullptr, 0u, qa, W, pl, lmb);
+  }
+
+  // merge the four waves into the part's partial
+  if (r16 == 0) {
 #pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        const float v0 = bf16_lo(ws[e]), v1 = bf16_hi(ws[e]);
-#pragma unroll
-        for (int gg = 0; gg < G; ++gg) {
-          o[gg][2 * e] = fmaf(pw[gg], v0, o[gg][2 * e]);
-          o[gg][2 * e + 1] = fmaf(pw[gg], v1, o[gg][2 * e + 1]);
-        }
+    for (int j = 0; j < 4; ++j) {
+      const int hd = 4 * lgrp + j;
+      if (hd < G) {
+        sm.wm[wv][hd] = W.m[j];
+        sm.wz[wv][hd] = W.z[j];
       }
     }
   }
 #pragma unroll
-  for (int gg = 0; gg < G; ++gg)
+  for (int j = 0; j < 4; ++j) {
+    const int hd = 4 * lgrp + j;
+    if (hd < G) {
 #pragma unroll
-    for (int e = 0; e < 8; ++e) {
-      float x = o[gg][e];
-#pragma unroll
-      for (int off = LPR; off < 64; off <<= 1) x += __shfl_xor(x, off, 64);
-      o[gg][e] = x;
+      for (int nt = 0; nt < NT; ++nt) sm.wo[wv][hd][16 * nt + r16] = W.o[nt][j];
     }
-  if (lg == 0) {
-#pragma unroll
-    for (int gg = 0; gg < G; ++gg)
-#pragma unroll
-      for (int e = 0; e < 8; ++e) sm.wo[wv][gg][8 * cl + e] = o[gg][e];
   }
   __syncthreads();
-
-  // ---- merge the four waves -----------------------------------------------
   constexpr float kLn2 = 0.69314718055994530942f;
+  const size_t ohead = ((size_t)i * c.dm.Hq + qh0) * p_cap + part;
   for (int x = tid; x < G * D; x += 256) {
     const int gg = x / D, ch = x - gg * D;
     const float M = fmaxf(fmaxf(sm.wm[0][gg], sm.wm[1][gg]), fmaxf(sm.wm[2][gg], sm.wm[3][gg]));
@@ -1360,60 +1579,69 @@ __device__ __attribute__((always_inline)) void attend_chunk(const Ctx &c, int i,
     if (ch == 0)
       st_dev(&lse_part[ohead + (size_t)gg * p_cap], Z > 0.0f ? (M + log2f(Z)) * kLn2 : -INFINITY);
   }
-  if (tid < nb * G) {  // log softmax mass of each block of the chunk (MAW)
-    const int jj = tid / G, gg = tid - jj * G;
-    const float M = fmaxf(fmaxf(sm.wm[0][gg], sm.wm[1][gg]), fmaxf(sm.wm[2][gg], sm.wm[3][gg]));
-    float z = 0.0f;
-    if (M != -INFINITY)
-      for (int pp = 0; pp < PPB; ++pp) {
-        const int p = jj * PPB + pp;
-        z = fmaf(exp2f(sm.wm[p / PPW][gg] - M), sm.pmass[p][gg], z);
-      }
-    const float lm = z > 0.0f ? (M + log2f(z)) * kLn2 : -INFINITY;
-    const int j = chunk * CB + jj;
-    if (dense)
-      st_dev(&c.sc.lm_dense[((size_t)seq * c.dm.Hq + qh0 + gg) * c.dm.ndt_cap + j], lm);
-    else
-      st_dev(&c.sc.lm_sel[((size_t)seq * c.dm.Hq + qh0 + gg) * c.dm.kcap + j], lm);
+}
+
+// Slots [P, p_cap) of a unit's partials are unused: lse = -inf, O = 0.
+template <int D, int G>
+__device__ __forceinline__ void empty_slots(const Ctx &c, int i, int h, int P, int p_cap,
+                                            float *__restrict__ o_part,
+                                            float *__restrict__ lse_part) {
+  const size_t hb = ((size_t)i * c.dm.Hq + (size_t)h * G) * p_cap;
+  const int n = p_cap - P;
+  for (int x = threadIdx.x; x < G * n * D; x += 256) {
+    const int gg = x / (n * D), r = x - gg * n * D, u = r / D, ch = r - u * D;
+    st_dev(&o_part[(hb + (size_t)gg * p_cap + P + u) * D + ch], 0.0f);
   }
+  for (int x = threadIdx.x; x < G * n; x += 256)
+    st_dev(&lse_part[hb + (size_t)(x / n) * p_cap + P + x % n], -INFINITY);
 }
 
 // ---------------------------------------------------------------------------
-// fuse: exact LSE fusion of a unit's partials per query head ([HGCA] What
-// carries the argument, max-subtracted form) and the MAW update
-// MAW <- r MAW + (1-r) a, a = group-mean softmax mass of the block (0 if not
-// attended) ([LFPS] decay r; [HGCA] MAW).  256 threads.  Every load the
-// fusion needs is issued in one batch.  MAW: r*MAW is written for every
-// block, then (1-r)*a is added to each attended block with one device-scope
-// atomic add (the same operations, so the same rounding, in both modes):
-//   kMawFull: the decay is done here (separate calls);
-//   kMawAdd:  the score tiles already wrote r*MAW (fused step).
-// all_slots: fuse every slot of p_cap (lse = -inf ones drop out), no MAW.
+// fusion + MAW ([HGCA] What carries the argument: the exact log-sum-exp merge
+// of partials; MAW as a decaying average of attention weights; [LFPS] decay
+// r = 0.95).  For each query head: lse = m + log sum_u exp(lse_u - m) with m
+// the largest partial lse (empty slots, lse = -inf, drop out), and O =
+// sum_u exp(lse_u - lse) O_u.  Then for every block, MAW <- r MAW + (1 - r) a
+// with a the group-mean softmax mass of the block's attended tokens, from the
+// log-mass of each attended page.
+//   kMawNone: fusion only.
+//   kMawFull: decay of every block here, then one add per attended block.
+//   kMawAdd:  the score tiles already wrote r*MAW (one-launch step).
 constexpr int kMawNone = 0, kMawFull = 1, kMawAdd = 2;
 constexpr int kFusePre = 16;  // partial slots whose O values are preloaded
+constexpr int kFusePgPre = 2;  // page-mass entries per thread preloaded
 
 template <int D, int G>
-__device__ __attribute__((always_inline)) void fuse_unit(const Ctx &c, int i, int seq, int h, const HeadInfo &hi,
-                          const UG &g, int maw_mode, bool all_slots, int cnt_in,
-                          const float *__restrict__ o_part,
-                          const float *__restrict__ lse_part, int p_cap,
-                          float *__restrict__ o, float *__restrict__ lse,
-                          FuseSmem<G> &sm) {
+__device__ __attribute__((always_inline)) void fuse_unit(const Ctx &c, int i, int seq, int h,
+                                                         const HeadInfo &hi, const UG &g,
+                                                         int maw_mode, int n_slots,
+                                                         const int32_t *__restrict__ selp, int cnt,
+                                                         const float *__restrict__ o_part,
+                                                         const float *__restrict__ lse_part,
+                                                         int p_cap, float *__restrict__ o,
+                                                         float *__restrict__ lse, FuseSmem<G> &sm,
+                                                         const unsigned long long *seltag = nullptr,
+                                                         uint32_t epoch = 0) {
   const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
   const int qh0 = h * G;
-  int nd = 0, ns = 0, cnt = 0;
-  if (!all_slots) {
-    cnt = min(cnt_in, hi.kcap);
-    nd = cdiv(g.n_dt, g.CB);
-    ns = cdiv(cnt, g.CB);
-  }
-  const int n_slots = min(all_slots ? p_cap : nd + ns, kFuseSlots);
-  auto slot_of = [&](int u) { return (all_slots || u < nd) ? u : hi.pd + (u - nd); };
+  n_slots = min(n_slots, kFuseSlots);
+  // selection entry j: from the tagged copy (waiting, bounded, for its tag)
+  // or the plain list
+  auto sel_ld = [&](int j) -> int {
+    if (!seltag) return ld_dev(&selp[j]);
+    unsigned long long e = ld_dev(&seltag[j]);
+    const unsigned long long t0 = wall_clock64();
+    while ((uint32_t)(e >> 32) != epoch && wall_clock64() - t0 < kWaitTicks) e = ld_dev(&seltag[j]);
+    return (uint32_t)(e >> 32) == epoch ? (int)(uint32_t)e : 0;
+  };
   const bool with_maw = maw_mode != kMawNone;
-  const int n_dt = with_maw ? min(g.n_dt, kFuseSlots) : 0;
-  const int n_sel = with_maw ? cnt : 0;
-  const int32_t *gsel = c.sc.usel + ((size_t)seq * c.dm.Hkv + h) * c.dm.kcap;
-  const bool sel_lds = n_sel <= kFuseSelLds;
+  const DenseList dl = with_maw ? dense_list(g) : DenseList{0, 0, 0, 0};
+  const int PPB = with_maw ? g.S / kPage : 1;
+  cnt = with_maw ? min(cnt, hi.kcap) : 0;
+  const int n_pg = dl.n + cnt * PPB;  // attended pages of the unit
+  const bool sel_lds = cnt <= kFuseSelLds;
+  const float *lmb = c.sc.lm_pg + ((size_t)seq * c.dm.Hq + qh0) * c.dm.lm_cap;
+  auto pg_slot = [&](int t) { return t < dl.n ? t : c.dm.lm_sel0 + (t - dl.n); };
 
   // ---- one batch of loads ---------------------------------------------------
   constexpr int R = kFuseSlots / 64;
@@ -1422,11 +1650,10 @@ __device__ __attribute__((always_inline)) void fuse_unit(const Ctx &c, int i, in
   for (int r = 0; r < R; ++r) {
     const int u = lane + 64 * r;
     const bool on = u < n_slots;
-    l0[r] = (on && wv < G) ? ld_dev(&lse_part[((size_t)i * c.dm.Hq + qh0 + wv) * p_cap + slot_of(u)])
+    l0[r] = (on && wv < G) ? ld_dev(&lse_part[((size_t)i * c.dm.Hq + qh0 + wv) * p_cap + u])
                            : -INFINITY;
-    l1[r] = (on && wv + 4 < G)
-                ? ld_dev(&lse_part[((size_t)i * c.dm.Hq + qh0 + wv + 4) * p_cap + slot_of(u)])
-                : -INFINITY;
+    l1[r] = (on && wv + 4 < G) ? ld_dev(&lse_part[((size_t)i * c.dm.Hq + qh0 + wv + 4) * p_cap + u])
+                               : -INFINITY;
   }
   constexpr int NP = (G * D + 255) / 256;
   float ov[NP][kFusePre];
@@ -1437,24 +1664,21 @@ __device__ __attribute__((always_inline)) void fuse_unit(const Ctx &c, int i, in
     const size_t hb = ((size_t)i * c.dm.Hq + qh0 + min(gg, G - 1)) * p_cap;
 #pragma unroll
     for (int u = 0; u < kFusePre; ++u)
-      ov[rr][u] = (x < G * D && u < n_slots) ? ld_dev(&o_part[(hb + slot_of(u)) * D + ch]) : 0.0f;
+      ov[rr][u] = (x < G * D && u < n_slots) ? ld_dev(&o_part[(hb + u) * D + ch]) : 0.0f;
   }
-  // attended entries of MAW: dense-touching blocks, then the selection
-  constexpr int ME = 4;  // entries per thread preloaded (more loop below)
-  float lmv[ME][G];
-  int selv[ME];
+  float lmv[kFusePgPre][G];
 #pragma unroll
-  for (int t = 0; t < ME; ++t) {
+  for (int t = 0; t < kFusePgPre; ++t) {
     const int x = tid + 256 * t;
-    const bool dn = x < n_dt, sl = !dn && x < n_dt + n_sel;
-    const int u = dn ? x : x - n_dt;
 #pragma unroll
-    for (int gg = 0; gg < G; ++gg) {
-      const size_t row = (size_t)seq * c.dm.Hq + qh0 + gg;
-      lmv[t][gg] = dn ? ld_dev(&c.sc.lm_dense[row * c.dm.ndt_cap + u])
-                      : (sl ? ld_dev(&c.sc.lm_sel[row * c.dm.kcap + u]) : -INFINITY);
-    }
-    selv[t] = sl ? ld_dev(&gsel[u]) : 0;
+    for (int gg = 0; gg < G; ++gg)
+      lmv[t][gg] = x < n_pg ? ld_dev(&lmb[(size_t)gg * c.dm.lm_cap + pg_slot(x)]) : -INFINITY;
+  }
+  int selv[kFuseSelLds / 256];
+#pragma unroll
+  for (int t = 0; t < kFuseSelLds / 256; ++t) {
+    const int x = tid + 256 * t;
+    selv[t] = (sel_lds && x < cnt) ? sel_ld(x) : 0;
   }
 
   // ---- per-head lse and slot weights ----------------------------------------
@@ -1482,6 +1706,11 @@ __device__ __attribute__((always_inline)) void fuse_unit(const Ctx &c, int i, in
       sm.w[gg][u] = (L == -INFINITY || l[r] == -INFINITY) ? 0.0f : expf(l[r] - L);
     }
   }
+#pragma unroll
+  for (int t = 0; t < kFuseSelLds / 256; ++t) {
+    const int x = tid + 256 * t;
+    if (sel_lds && x < cnt) sm.sel[x] = selv[t];
+  }
   __syncthreads();
   // ---- O = sum_u w_u O_u (zero weights select 0) ------------------------------
 #pragma unroll
@@ -1500,7 +1729,7 @@ __device__ __attribute__((always_inline)) void fuse_unit(const Ctx &c, int i, in
       }
       for (int u = kFusePre; u < n_slots; ++u) {
         const float wgt = sm.w[gg][u];
-        const float v = ld_dev(&o_part[(hb + slot_of(u)) * D + ch]);
+        const float v = ld_dev(&o_part[(hb + u) * D + ch]);
         a = fmaf(wgt, wgt != 0.0f ? v : 0.0f, a);
       }
       o[((size_t)i * c.dm.Hq + qh0 + gg) * D + ch] = a;
@@ -1510,84 +1739,75 @@ __device__ __attribute__((always_inline)) void fuse_unit(const Ctx &c, int i, in
   if (!with_maw) return;
 
   // ---- MAW -------------------------------------------------------------------
-  // group-mean mass of every attended entry, into LDS
-  auto mass = [&](const float (&lm)[G]) {
+  // softmax mass of every attended page summed over the heads, into LDS
+  auto page_mass = [&](const float (&lm)[G]) {
     float a = 0.0f;
 #pragma unroll
     for (int gg = 0; gg < G; ++gg) {
       const float L = sm.lse[gg];
       a += (L == -INFINITY || lm[gg] == -INFINITY) ? 0.0f : expf(lm[gg] - L);
     }
-    return a * (1.0f / (float)G);
+    return a;
   };
-  auto put = [&](int x, float a, int sv) {
-    if (x < n_dt) {
-      sm.adense[x] = a;
-    } else if (sel_lds) {
-      sm.asel[x - n_dt] = a;
-      sm.sel[x - n_dt] = sv;
-    }
-  };
-#pragma unroll
-  for (int t = 0; t < ME; ++t) {
-    const int x = tid + 256 * t;
-    if (x < n_dt + n_sel) put(x, mass(lmv[t]), selv[t]);
-  }
-  for (int x = tid + 256 * ME; x < n_dt + n_sel; x += 256) {
-    const bool dn = x < n_dt;
-    const int u = dn ? x : x - n_dt;
+  auto page_mass_at = [&](int t) {
     float lm[G];
 #pragma unroll
-    for (int gg = 0; gg < G; ++gg) {
-      const size_t row = (size_t)seq * c.dm.Hq + qh0 + gg;
-      lm[gg] = dn ? ld_dev(&c.sc.lm_dense[row * c.dm.ndt_cap + u])
-                  : ld_dev(&c.sc.lm_sel[row * c.dm.kcap + u]);
-    }
-    put(x, mass(lm), dn ? 0 : ld_dev(&gsel[u]));
+    for (int gg = 0; gg < G; ++gg) lm[gg] = ld_dev(&lmb[(size_t)gg * c.dm.lm_cap + pg_slot(t)]);
+    return page_mass(lm);
+  };
+  const int n_pg_lds = min(n_pg, kFusePgLds);
+#pragma unroll
+  for (int t = 0; t < kFusePgPre; ++t) {
+    const int x = tid + 256 * t;
+    if (x < n_pg_lds) sm.pm[x] = page_mass(lmv[t]);
   }
+  for (int x = tid + 256 * kFusePgPre; x < n_pg_lds; x += 256) sm.pm[x] = page_mass_at(x);
   __syncthreads();
-  float *mw = c.L.maw + hi.maw_off + (size_t)seq * hi.nbmax;
-  const float r = c.dm.maw_decay, omr = 1.0f - r;
-  // mass of a selected block from the global copy (selections beyond the LDS)
-  auto sel_mass_global = [&](int blk) -> float {
-    int lo = 0, hi2 = n_sel;
+  auto pm = [&](int t) { return t < n_pg_lds ? sm.pm[t] : page_mass_at(t); };
+  auto sel_at = [&](int j) { return sel_lds ? sm.sel[j] : sel_ld(j); };
+  auto sel_find = [&](int blk) {  // position of blk in the (ascending) selection, or -1
+    int lo = 0, hi2 = cnt;
     while (lo < hi2) {
       const int mid = (lo + hi2) >> 1;
-      if (ld_dev(&gsel[mid]) < blk) lo = mid + 1; else hi2 = mid;
+      if (sel_at(mid) < blk) lo = mid + 1; else hi2 = mid;
     }
-    if (lo >= n_sel || ld_dev(&gsel[lo]) != blk) return 0.0f;
-    float lm[G];
-#pragma unroll
-    for (int gg = 0; gg < G; ++gg)
-      lm[gg] = ld_dev(&c.sc.lm_sel[((size_t)seq * c.dm.Hq + qh0 + gg) * c.dm.kcap + lo]);
-    return mass(lm);
+    return (lo < cnt && sel_at(lo) == blk) ? lo : -1;
   };
-  auto sel_mass = [&](int blk) -> float {
-    if (!sel_lds) return sel_mass_global(blk);
-    const int j = lower_bound(sm.sel, n_sel, blk);
-    return (j < n_sel && sm.sel[j] == blk) ? sm.asel[j] : 0.0f;
+  auto sel_pages_mass = [&](int j) {
+    float a = 0.0f;
+    for (int pp = 0; pp < PPB; ++pp) a += pm(dl.n + j * PPB + pp);
+    return a;
   };
-  if (maw_mode == kMawFull) {  // decay here (the fused step's score tiles do it there)
+  float *mw = c.L.maw + hi.maw_off + (size_t)seq * hi.nbmax;
+  const float r = c.dm.maw_decay, omr = 1.0f - r;
+  if (maw_mode == kMawFull) {  // decay here (the one-launch step's score tiles do it there)
     for (int blk = tid; blk < g.n_blk; blk += 256) st_dev(&mw[blk], __fmul_rn(r, ld_dev(&mw[blk])));
     wait_vmem();
     __syncthreads();
   }
-  // attended blocks: dense-touching ones (with their selected part, if any),
+  // attended blocks: dense-touching ones (with their selected pages, if any),
   // then selected blocks that touch no dense token; one atomic add each, so
   // both modes round identically
-  for (int x = tid; x < n_dt + n_sel; x += 256) {
+  const float inv_g = 1.0f / (float)G;
+  for (int x = tid; x < g.n_dt + cnt; x += 256) {
     int blk;
-    float a;
-    if (x < n_dt) {
+    float a = 0.0f;
+    if (x < g.n_dt) {
       blk = dense_block(g, x);
-      a = sm.adense[x] + sel_mass(blk);
+      for (int pp = 0; pp < PPB; ++pp) {
+        const int t = dense_pos(dl, blk * PPB + pp);
+        if (t >= 0) a += pm(t);
+      }
+      const int j = sel_find(blk);
+      if (j >= 0) a += sel_pages_mass(j);
     } else {
-      const int j = x - n_dt;
-      blk = sel_lds ? sm.sel[j] : ld_dev(&gsel[j]);
+      const int j = x - g.n_dt;
+      blk = sel_at(j);
       if (blk < g.hb || blk >= g.tb) continue;  // counted with the dense entry
-      a = sel_lds ? sm.asel[j] : sel_mass_global(blk);
+      a = sel_pages_mass(j);
     }
-    __hip_atomic_fetch_add(&mw[blk], __fmul_rn(omr, a), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    __hip_atomic_fetch_add(&mw[blk], __fmul_rn(omr, a * inv_g), __ATOMIC_RELAXED,
+                           __HIP_MEMORY_SCOPE_AGENT);
   }
 }
 
@@ -1615,172 +1835,176 @@ __global__ __launch_bounds__(256) void k_prep(Ctx c, AppendBatch b, int tok_per_
   }
 }
 
-// select (+ dense chunks): score tiles with a last-arriver top-k per unit;
-// dense attention chunks, which do not depend on the selection, share the
-// launch.
+// select: score tiles; the last tile of a unit to arrive runs its top-k.
 template <int D, int G>
 __global__ __launch_bounds__(256) void k_select(Ctx c, SeqBatch b, int tiles_x,
-                                                int dchunks_x,
                                                 int32_t *__restrict__ blk_idx,
                                                 int32_t *__restrict__ blk_cnt, int k_cap,
                                                 const uint16_t *__restrict__ q,
-                                                float *__restrict__ o_part,
-                                                float *__restrict__ lse_part, int p_cap,
                                                 int lrows_words) {
-  // dynamic LDS: max(AttSmem, TopkSmem + lrows_words top-k words + one
-  // 64-bit mask per top-k row)
+  // dynamic LDS: TopkSmem + lrows_words top-k words + one 64-bit mask per row
   extern __shared__ __align__(16) unsigned char smem_raw[];
   TopkSmem &smem_topk = *reinterpret_cast<TopkSmem *>(smem_raw);
-  AttSmem<D, G> &smem_att = *reinterpret_cast<AttSmem<D, G> *>(smem_raw);
-  int wg = blockIdx.x;
-  const int n_score = tiles_x * c.dm.Hkv * b.n;
-  if (wg < n_score) {
-    const int tile = wg % tiles_x, h = (wg / tiles_x) % c.dm.Hkv, i = wg / (tiles_x * c.dm.Hkv);
-    const HeadInfo hi = c.heads[h];
-    const int seq = b.seq[i];
-    const UG g = unit_geom(b.len[i], hi, c.dm);
-    const int n_tiles = max(1, cdiv(g.n_blk, kScoreTile));
-    if (tile >= n_tiles) return;
-    score_tile<D, G>(c, i, seq, h, hi, g, tile, q, smem_topk, false, false);
-    // the last tile of the unit to arrive runs its top-k (one wave)
-    uint32_t *ctr = &c.sc.arrive[((size_t)seq * c.dm.Hkv + h) * 2];
-    if (!arrive_last(ctr, (unsigned)n_tiles, &smem_topk.last)) return;
-    uint32_t *lrows = reinterpret_cast<uint32_t *>(smem_raw + sizeof(TopkSmem));
-    topk_unit<D, G>(c, i, seq, h, hi, g, q, blk_idx, blk_cnt, k_cap, smem_topk, lrows,
-                    lrows_words, reinterpret_cast<unsigned long long *>(lrows + lrows_words));
-    if (threadIdx.x == 0) st_dev(ctr, 0u);
-    return;
-  }
-  wg -= n_score;
-  const int ch = wg % dchunks_x, h = (wg / dchunks_x) % c.dm.Hkv, i = wg / (dchunks_x * c.dm.Hkv);
-  if (i >= b.n) return;
-  const HeadInfo hi = c.heads[h];
-  const UG g = unit_geom(b.len[i], hi, c.dm);
-  if (ch >= cdiv(g.n_dt, g.CB)) return;
-  attend_chunk<D, G>(c, i, b.seq[i], h, hi, g, true, ch, 0, nullptr, q, o_part, lse_part,
-                     p_cap, smem_att);
-}
-
-// attend, separate-call form: one workgroup per partial slot of each unit
-// (dense chunks at [0, pd), selected chunks after), unused slots emptied.
-template <int D, int G>
-__global__ __launch_bounds__(256) void k_attend_slots(Ctx c, SeqBatch b,
-                                                      const uint16_t *__restrict__ q,
-                                                      const int32_t *__restrict__ blk_idx,
-                                                      const int32_t *__restrict__ blk_cnt,
-                                                      int k_cap, float *__restrict__ o_part,
-                                                      float *__restrict__ lse_part, int p_cap) {
-  __shared__ AttSmem<D, G> sm;
-  const int slot = blockIdx.x, h = blockIdx.y, i = blockIdx.z;
+  const int wg = blockIdx.x;
+  const int tile = wg % tiles_x, h = (wg / tiles_x) % c.dm.Hkv, i = wg / (tiles_x * c.dm.Hkv);
   const HeadInfo hi = c.heads[h];
   const int seq = b.seq[i];
   const UG g = unit_geom(b.len[i], hi, c.dm);
-  const int cnt = min(min(max(blk_cnt[(size_t)i * c.dm.Hkv + h], 0), k_cap), hi.kcap);
-  if (slot == 0 && threadIdx.x == 0) st_dev(&c.sc.ucnt[(size_t)seq * c.dm.Hkv + h], cnt);
-  const int32_t *sel = blk_idx + ((size_t)i * c.dm.Hkv + h) * k_cap;
-  if (slot < hi.pd) {
-    attend_chunk<D, G>(c, i, seq, h, hi, g, true, slot, cnt, sel, q, o_part, lse_part, p_cap, sm);
-  } else {
-    const int ch = slot - hi.pd;
-    // chunks past the selection write an empty slot
-    attend_chunk<D, G>(c, i, seq, h, hi, g, false, ch, cnt, sel, q, o_part, lse_part, p_cap, sm);
+  const int n_tiles = max(1, cdiv(g.n_blk, kScoreTile));
+  if (tile >= n_tiles) return;
+  score_tile<D, G>(c, i, seq, h, hi, g, tile, q, smem_topk, false, false);
+  uint32_t *ctr = &c.sc.arrive[((size_t)seq * c.dm.Hkv + h) * 2];
+  if (!arrive_last(ctr, (unsigned)n_tiles, &smem_topk.last)) return;
+  uint32_t *lrows = reinterpret_cast<uint32_t *>(smem_raw + sizeof(TopkSmem));
+  topk_unit<D, G>(c, i, seq, h, hi, g, q, blk_idx, blk_cnt, k_cap, smem_topk, lrows,
+                  lrows_words, reinterpret_cast<unsigned long long *>(lrows + lrows_words));
+  if (threadIdx.x == 0) st_dev(ctr, 0u);
+}
+
+// attend, separate-call form: P workgroups per unit, one partial each; part
+// 0 also keeps a copy of the selection for the fusion call and empties the
+// slots [P, p_cap).
+template <int D, int G>
+__global__ __launch_bounds__(256, 2) void k_attend(Ctx c, SeqBatch b, int P,
+                                                   const uint16_t *__restrict__ q,
+                                                   const int32_t *__restrict__ blk_idx,
+                                                   const int32_t *__restrict__ blk_cnt, int k_cap,
+                                                   float *__restrict__ o_part,
+                                                   float *__restrict__ lse_part, int p_cap) {
+  __shared__ AttLds<D, G> sm;
+  __shared__ int s_cnt;
+  const int part = blockIdx.x % P, u = blockIdx.x / P;
+  const int h = u % c.dm.Hkv, i = u / c.dm.Hkv;
+  const HeadInfo hi = c.heads[h];
+  const int seq = b.seq[i];
+  const UG g = unit_geom(b.len[i], hi, c.dm);
+  const size_t unit = (size_t)seq * c.dm.Hkv + h;
+  SelIn si;
+  si.blk = blk_idx + ((size_t)i * c.dm.Hkv + h) * k_cap;
+  si.cnt = min(min(max(blk_cnt[(size_t)i * c.dm.Hkv + h], 0), k_cap), hi.kcap);
+  if (part == 0) {
+    for (int j = threadIdx.x; j < si.cnt; j += 256) st_dev(&c.sc.usel[unit * c.dm.kcap + j], si.blk[j]);
+    if (threadIdx.x == 0) st_dev(&c.sc.ucnt[unit], si.cnt);
+    empty_slots<D, G>(c, i, h, P, p_cap, o_part, lse_part);
   }
+  attend_part<D, G>(c, i, seq, h, g, part, P, q, si, o_part, lse_part, p_cap, sm, nullptr,
+                    &s_cnt);
 }
 
 // One decode step in one launch.  Workgroups by index: score tiles (the last
-// of a unit runs its top-k and publishes the selection), dense chunks, then
-// selected chunks, which wait for their unit's selection.  The last of a
-// unit's dense chunks, selected chunks and top-k to finish fuses the partials
-// and updates MAW.  Workgroups start in index order on each XCD, so every
-// score tile has started before any selected chunk waits, and no wait is on a
+// of a unit runs its top-k and publishes the selection, tagged with the step
+// number), then P attention parts per unit.  A part streams its dense pages
+// once the unit's score tiles are done, then waits for the selection and
+// streams its selected pages; the last part of a unit to finish fuses the
+// partials and updates MAW.  Workgroups start in index order on each XCD and
+// every wait is on a score tile, which never waits, so no wait is on a
 // workgroup that cannot start; each wait is also bounded in time (after
 // kWaitTicks it gives up and raises the error flag).
-constexpr unsigned long long kWaitTicks = 20000000ull;  // 0.2 s of the 100 MHz clock
-
 template <int D, int G>
-__global__ __launch_bounds__(256) void k_step(Ctx c, SeqBatch b, int tiles_x, int dchunks_x,
-                                              int schunks_x, int32_t *__restrict__ blk_idx,
-                                              int32_t *__restrict__ blk_cnt, int k_cap,
-                                              const uint16_t *__restrict__ q,
-                                              float *__restrict__ o_part,
-                                              float *__restrict__ lse_part, int p_cap,
-                                              float *__restrict__ o, float *__restrict__ lse,
-                                              int lrows_words, uint32_t epoch) {
-  // dynamic LDS: max(TopkSmem + top-k words and row masks, AttSmem, FuseSmem)
+__global__ __launch_bounds__(256, 2) void k_step(Ctx c, SeqBatch b, int tiles_x, int P,
+                                                 int32_t *__restrict__ blk_idx,
+                                                 int32_t *__restrict__ blk_cnt, int k_cap,
+                                                 const uint16_t *__restrict__ q,
+                                                 float *__restrict__ o_part,
+                                                 float *__restrict__ lse_part, int p_cap,
+                                                 float *__restrict__ o, float *__restrict__ lse,
+                                                 int lrows_words, uint32_t epoch, int ptl_cap) {
+  // dynamic LDS: max(TopkSmem + top-k words and row masks, AttLds + ptl_cap
+  // page-table entries, FuseSmem)
   extern __shared__ __align__(16) unsigned char smem_raw[];
-  __shared__ int s_flag;
+  __shared__ int s_flag, s_cnt;
   TopkSmem &smem_topk = *reinterpret_cast<TopkSmem *>(smem_raw);
-  AttSmem<D, G> &smem_att = *reinterpret_cast<AttSmem<D, G> *>(smem_raw);
+  AttLds<D, G> &smem_att = *reinterpret_cast<AttLds<D, G> *>(smem_raw);
   FuseSmem<G> &smem_fuse = *reinterpret_cast<FuseSmem<G> *>(smem_raw);
   const int units = c.dm.Hkv * b.n;
-  const int n_score = tiles_x * units, n_dense = dchunks_x * units;
-  int wg = blockIdx.x, role, idx, u;
-  if (wg < n_score) {
-    role = 0; idx = wg % tiles_x; u = wg / tiles_x;
-  } else if (wg < n_score + n_dense) {
-    wg -= n_score; role = 1; idx = wg / units; u = wg % units;  // chunk-major
+  const int n_score = tiles_x * units;
+  int wg = blockIdx.x;
+  const bool score = wg < n_score;
+  int idx, u;
+  if (score) {
+    idx = wg % tiles_x;
+    u = wg / tiles_x;
   } else {
-    wg -= n_score + n_dense; role = 2; idx = wg / units; u = wg % units;
+    wg -= n_score;
+    idx = wg / units;  // part-major
+    u = wg % units;
   }
   const int h = u % c.dm.Hkv, i = u / c.dm.Hkv;
   const HeadInfo hi = c.heads[h];
   const int seq = b.seq[i];
   const UG g = unit_geom(b.len[i], hi, c.dm);
   const size_t unit = (size_t)seq * c.dm.Hkv + h;
-  const int nd = cdiv(g.n_dt, g.CB);
-  int32_t *sel = blk_idx + ((size_t)i * c.dm.Hkv + h) * k_cap;
-  if (role == 0) {
+  if (score) {
     const int n_tiles = max(1, cdiv(g.n_blk, kScoreTile));
     if (idx >= n_tiles) return;
+    // the score tiles, the top-k and the fusion are on every unit's critical
+    // path: their waves get issue priority over the attention parts'
+    __builtin_amdgcn_s_setprio(2);
     // without MAW flags each tile also lists its candidates for the fast top-k
-    const bool fast = c.dm.maw_beta <= 0.0f && n_tiles <= kFastTiles;
+    const bool fast = c.dm.maw_beta <= 0.0f && n_tiles <= kFastTiles && g.kk <= kTileList;
     score_tile<D, G>(c, i, seq, h, hi, g, idx, q, smem_topk, true, fast);
     uint32_t *ctr = &c.sc.arrive[unit * 2];
     if (!arrive_last(ctr, (unsigned)n_tiles, &s_flag)) return;
+    if (threadIdx.x == 0) st_dev(&c.sc.scored[unit], epoch);  // opens the dense pages
+    __builtin_amdgcn_s_setprio(3);
     uint32_t *lrows = reinterpret_cast<uint32_t *>(smem_raw + sizeof(TopkSmem));
-    if (!fast || !topk_fast<D, G>(c, i, seq, h, hi, g, q, blk_idx, blk_cnt, k_cap, smem_topk))
+    unsigned long long *tagd = c.sc.seltag + unit * c.dm.kcap;
+    if (!fast || !topk_fast<D, G>(c, i, seq, h, hi, g, blk_idx, blk_cnt, k_cap, smem_topk,
+                                  tagd, epoch))
       topk_unit<D, G>(c, i, seq, h, hi, g, q, blk_idx, blk_cnt, k_cap, smem_topk, lrows,
-                      lrows_words, reinterpret_cast<unsigned long long *>(lrows + lrows_words));
+                      lrows_words, reinterpret_cast<unsigned long long *>(lrows + lrows_words),
+                      tagd, epoch);
     if (threadIdx.x == 0) {
+      // the entries carry their own tags, so the count need not wait for them
+      const int cnt = min(min(g.kk, k_cap), hi.kcap);
       st_dev(ctr, 0u);
-      st_dev(&c.sc.ucnt[unit], min(min(g.kk, k_cap), hi.kcap));
-      wait_vmem();  // the selection and its count first
-      st_dev(&c.sc.ready[unit], epoch);
+      st_dev(&c.sc.rtag[unit], ((unsigned long long)epoch << 32) | (uint32_t)cnt);
     }
-  } else if (role == 1) {
-    if (idx >= nd) return;
-    attend_chunk<D, G>(c, i, seq, h, hi, g, true, idx, 0, nullptr, q, o_part, lse_part, p_cap,
-                       smem_att);
-  } else {
-    if (threadIdx.x == 0) {
-      int ok = 1;
-      const unsigned long long t0 = wall_clock64();
-      while (ld_dev(&c.sc.ready[unit]) != epoch) {
-        if (wall_clock64() - t0 > kWaitTicks) {
-          ok = 0;
-          st_dev(&c.sc.err[0], 1u);
-          break;
-        }
-        __builtin_amdgcn_s_sleep(8);
-      }
-      s_flag = ok;
-    }
-    __syncthreads();
-    if (!s_flag) return;
-    const int cnt = min(ld_dev(&c.sc.ucnt[unit]), hi.kcap);
-    if (idx >= cdiv(cnt, g.CB)) return;
-    attend_chunk<D, G>(c, i, seq, h, hi, g, false, idx, cnt, sel, q, o_part, lse_part, p_cap,
-                       smem_att);
+    return;
   }
+  // attention part idx of unit u; the sequence's page table is copied to LDS
+  // (one batch of loads) for the selected pages
+  const int32_t *ptl = nullptr;
+  const int np = cdiv(g.N, kPage);
+  if (np <= ptl_cap) {
+    int32_t *t = reinterpret_cast<int32_t *>(smem_raw + ((sizeof(AttLds<D, G>) + 15) & ~15));
+    constexpr int PER = (kPtLds + 255) / 256;
+    const int32_t *pts = c.L.pt + (size_t)seq * c.dm.pages_per_seq;
+    int32_t v[PER];
+#pragma unroll
+    for (int k = 0; k < PER; ++k) {
+      const int x = (int)threadIdx.x + 256 * k;
+      v[k] = x < np ? pts[x] : 0;
+    }
+#pragma unroll
+    for (int k = 0; k < PER; ++k) {
+      const int x = (int)threadIdx.x + 256 * k;
+      if (x < np) t[x] = v[k];
+    }
+    ptl = t;  // visible to all waves after the barrier of the selection wait
+  }
+  if (idx == 0) empty_slots<D, G>(c, i, h, P, p_cap, o_part, lse_part);
+  SelIn si;
+  si.tag = c.sc.seltag + unit * c.dm.kcap;
+  si.rtag = &c.sc.rtag[unit];
+  si.gate = &c.sc.scored[unit];
+  si.epoch = epoch;
+  attend_part<D, G>(c, i, seq, h, g, idx, P, q, si, o_part, lse_part, p_cap, smem_att, ptl,
+                    &s_cnt);
   uint32_t *fctr = &c.sc.arrive[unit * 2 + 1];
-  if (!arrive_fuse(fctr, nd, &c.sc.ucnt[unit], g.CB, &s_flag)) return;
-  fuse_unit<D, G>(c, i, seq, h, hi, g, kMawAdd, false, ld_dev(&c.sc.ucnt[unit]), o_part,
-                  lse_part, p_cap, o, lse, smem_fuse);
+  if (!arrive_last(fctr, (unsigned)P, &s_flag)) return;
+  __builtin_amdgcn_s_setprio(3);
+  const int cnt = (int)(uint32_t)ld_dev(&c.sc.rtag[unit]);  // this step's, seen by every part
+  fuse_unit<D, G>(c, i, seq, h, hi, g, kMawAdd, P, nullptr, cnt, o_part, lse_part, p_cap, o, lse,
+                  smem_fuse, c.sc.seltag + unit * c.dm.kcap, epoch);
   if (threadIdx.x == 0) st_dev(fctr, 0u);
 }
 
+// fuse, separate-call form: one workgroup per unit over P partial slots (layer
+// call: selection and page masses from the attend call) or over every slot
+// of p_cap (pure fusion).
 template <int D, int G>
-__global__ __launch_bounds__(256) void k_fuse(Ctx c, SeqBatch b, int with_maw,
+__global__ __launch_bounds__(256) void k_fuse(Ctx c, SeqBatch b, int with_maw, int P,
                                               const float *__restrict__ o_part,
                                               const float *__restrict__ lse_part, int p_cap,
                                               float *__restrict__ o, float *__restrict__ lse) {
@@ -1789,12 +2013,13 @@ __global__ __launch_bounds__(256) void k_fuse(Ctx c, SeqBatch b, int with_maw,
   const HeadInfo hi = c.heads[h];
   if (with_maw) {
     const UG g = unit_geom(b.len[i], hi, c.dm);
-    fuse_unit<D, G>(c, i, b.seq[i], h, hi, g, kMawFull, false,
-                    ld_dev(&c.sc.ucnt[(size_t)b.seq[i] * c.dm.Hkv + h]), o_part, lse_part,
-                    p_cap, o, lse, sm);
+    const size_t unit = (size_t)b.seq[i] * c.dm.Hkv + h;
+    fuse_unit<D, G>(c, i, b.seq[i], h, hi, g, kMawFull, P, c.sc.usel + unit * c.dm.kcap,
+                    ld_dev(&c.sc.ucnt[unit]), o_part, lse_part, p_cap, o, lse, sm);
   } else {
     UG g{};
-    fuse_unit<D, G>(c, i, 0, h, hi, g, kMawNone, true, 0, o_part, lse_part, p_cap, o, lse, sm);
+    fuse_unit<D, G>(c, i, 0, h, hi, g, kMawNone, p_cap, nullptr, 0, o_part, lse_part, p_cap, o,
+                    lse, sm);
   }
 }
 
@@ -1858,67 +2083,63 @@ static int topk_lds(int max_blocks, size_t *bytes) {
   return lrows_words;
 }
 
-hipError_t launch_select(const Ctx &c, const SeqBatch &b, int max_blocks,
-                         const uint16_t *q, int32_t *blk_idx, int32_t *blk_cnt,
-                         int32_t k_cap, int dchunks_x, float *dense_o_part,
-                         float *dense_lse_part, int32_t p_cap, hipStream_t st) {
+hipError_t launch_select(const Ctx &c, const SeqBatch &b, int max_blocks, const uint16_t *q,
+                         int32_t *blk_idx, int32_t *blk_cnt, int32_t k_cap, hipStream_t st) {
   if (b.n <= 0) return hipSuccess;
   const int tiles_x = max(1, (max_blocks + kScoreTile - 1) / kScoreTile);
-  if (!dense_o_part) dchunks_x = 0;
-  const int grid = tiles_x * c.dm.Hkv * b.n + dchunks_x * c.dm.Hkv * b.n;
+  const int grid = tiles_x * c.dm.Hkv * b.n;
   size_t topk_bytes;
   const int lrows_words = topk_lds(max_blocks, &topk_bytes);
   if (topk_bytes > 65536) return hipErrorInvalidValue;
   SD_DISPATCH_DG(c.dm.d, c.dm.G, {
-    const size_t smem = std::max(sizeof(AttSmem<D_, G_>), topk_bytes);
-    hipLaunchKernelGGL((k_select<D_, G_>), dim3(grid), dim3(256), smem, st, c, b, tiles_x,
-                       max(dchunks_x, 1), blk_idx, blk_cnt, k_cap, q, dense_o_part,
-                       dense_lse_part, p_cap, lrows_words);
+    hipLaunchKernelGGL((k_select<D_, G_>), dim3(grid), dim3(256), topk_bytes, st, c, b, tiles_x,
+                       blk_idx, blk_cnt, k_cap, q, lrows_words);
   });
   return hipGetLastError();
 }
 
-hipError_t launch_attend(const Ctx &c, const SeqBatch &b, const uint16_t *q,
-                         const int32_t *blk_idx, const int32_t *blk_cnt,
-                         int32_t k_cap, float *o_part, float *lse_part,
-                         int32_t p_cap, hipStream_t st) {
+hipError_t launch_attend(const Ctx &c, const SeqBatch &b, int P, const uint16_t *q,
+                         const int32_t *blk_idx, const int32_t *blk_cnt, int32_t k_cap,
+                         float *o_part, float *lse_part, int32_t p_cap, hipStream_t st) {
   if (b.n <= 0) return hipSuccess;
-  dim3 grid(p_cap, c.dm.Hkv, b.n);
+  if (P < 1 || P > p_cap) return hipErrorInvalidValue;
+  const int grid = P * c.dm.Hkv * b.n;
   SD_DISPATCH_DG(c.dm.d, c.dm.G,
-                 hipLaunchKernelGGL((k_attend_slots<D_, G_>), grid, dim3(256), 0, st, c, b,
+                 hipLaunchKernelGGL((k_attend<D_, G_>), dim3(grid), dim3(256), 0, st, c, b, P,
                                     q, blk_idx, blk_cnt, k_cap, o_part, lse_part, p_cap));
   return hipGetLastError();
 }
 
-hipError_t launch_step(const Ctx &c, const SeqBatch &b, int max_blocks, const uint16_t *q,
-                       int32_t *blk_idx, int32_t *blk_cnt, int32_t k_cap, int dchunks_x,
-                       int schunks_x, float *o_part, float *lse_part, int32_t p_cap,
-                       float *o, float *lse, uint32_t epoch, hipStream_t st) {
+hipError_t launch_step(const Ctx &c, const SeqBatch &b, int max_blocks, int P, const uint16_t *q,
+                       int32_t *blk_idx, int32_t *blk_cnt, int32_t k_cap, float *o_part,
+                       float *lse_part, int32_t p_cap, float *o, float *lse, uint32_t epoch,
+                       int ptl_cap, hipStream_t st) {
   if (b.n <= 0) return hipSuccess;
+  if (P < 1 || P > p_cap) return hipErrorInvalidValue;
   const int tiles_x = max(1, (max_blocks + kScoreTile - 1) / kScoreTile);
   const int units = c.dm.Hkv * b.n;
-  const int grid = (tiles_x + dchunks_x + schunks_x) * units;
+  const int grid = (tiles_x + P) * units;
   size_t topk_bytes;
   const int lrows_words = topk_lds(max_blocks, &topk_bytes);
   if (topk_bytes > 65536) return hipErrorInvalidValue;
   SD_DISPATCH_DG(c.dm.d, c.dm.G, {
-    const size_t smem = std::max(std::max(sizeof(AttSmem<D_, G_>), sizeof(FuseSmem<G_>)),
-                                 topk_bytes);
-    hipLaunchKernelGGL((k_step<D_, G_>), dim3(grid), dim3(256), smem, st, c, b, tiles_x,
-                       dchunks_x, schunks_x, blk_idx, blk_cnt, k_cap, q, o_part, lse_part,
-                       p_cap, o, lse, lrows_words, epoch);
+    const size_t att = ((sizeof(AttLds<D_, G_>) + 15) & ~size_t(15)) + sizeof(int32_t) * ptl_cap;
+    const size_t smem = std::max(std::max(att, sizeof(FuseSmem<G_>)), topk_bytes);
+    hipLaunchKernelGGL((k_step<D_, G_>), dim3(grid), dim3(256), smem, st, c, b, tiles_x, P,
+                       blk_idx, blk_cnt, k_cap, q, o_part, lse_part, p_cap, o, lse, lrows_words,
+                       epoch, ptl_cap);
   });
   return hipGetLastError();
 }
 
-hipError_t launch_fuse(const Ctx &c, const SeqBatch &b, bool with_maw,
+hipError_t launch_fuse(const Ctx &c, const SeqBatch &b, bool with_maw, int P,
                        const float *o_part, const float *lse_part, int32_t p_cap,
                        float *o, float *lse, hipStream_t st) {
   if (b.n <= 0) return hipSuccess;
   dim3 grid(c.dm.Hkv, b.n);
   SD_DISPATCH_DG(c.dm.d, c.dm.G,
                  hipLaunchKernelGGL((k_fuse<D_, G_>), grid, dim3(256), 0, st, c, b,
-                                    with_maw ? 1 : 0, o_part, lse_part, p_cap, o, lse));
+                                    with_maw ? 1 : 0, P, o_part, lse_part, p_cap, o, lse));
   return hipGetLastError();
 }
 

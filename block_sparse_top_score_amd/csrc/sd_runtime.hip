@@ -45,6 +45,7 @@ struct sd_ctx {
   int pend_layer = -2;
   std::vector<int32_t> pend_seqs;
   int32_t pend_pcap = 0;
+  std::vector<int> pend_parts;  // P of each launch of the attend call
   std::string err;
   std::vector<void *> dev_allocs;
 };
@@ -233,17 +234,18 @@ sd_status sparse_decode_init(const sd_config *cfg, sd_ctx **out) {
     return fail(c, SD_EHIP, "no HIP device");
 
   const int max_seqs = cfg->max_seqs;
-  // per-head geometry and capacities.  Partial slots of a unit: dense
-  // chunks at [0, pd), selected chunks at [pd, pd + ceil(kcap / CB)).
+  // per-head geometry and capacities.  The attended pages of a unit: at most
+  // lm_sel0 pages with dense tokens, then kcap * S / 16 pages of selected
+  // blocks; partial slots: one per attention workgroup, P <= p_cap.
   c->heads.resize(c->Hkv);
   int64_t summ_elems = 0, maw_elems = 0;
-  int key_stride = 1, ndt_cap = 1;
+  int key_stride = 1, sel_pages = 1;
+  const int lm_sel0 = (int)(cdiv(cfg->sink_tokens, kPage) + cdiv(cfg->recent_window, kPage) + 1);
   for (int h = 0; h < c->Hkv; ++h) {
     HeadInfo &hi = c->heads[h];
     hi.S = c->S[h];
     hi.ppm = c->ppm[h];
     hi.nbmax = (int)cdiv(cfg->max_seq_len, hi.S);
-    hi.chunk_blocks = kChunkTokens / hi.S;
     hi.summ_off = summ_elems;
     hi.maw_off = maw_elems;
     summ_elems += (int64_t)max_seqs * (c->D / 4) * hi.nbmax * 8;
@@ -253,12 +255,10 @@ sd_status sparse_decode_init(const sd_config *cfg, sd_ctx **out) {
     int64_t kc = std::min<int64_t>(cdiv((int64_t)hi.ppm * cfg->max_seq_len, 1000000LL * hi.S),
                                    hi.nbmax);
     hi.kcap = (int)std::max<int64_t>(kc, 1);
-    int64_t ndt = std::min<int64_t>(cdiv(cfg->sink_tokens, hi.S) +
-                                        cdiv(cfg->recent_window, hi.S) + 1, hi.nbmax);
-    ndt_cap = std::max<int>(ndt_cap, (int)ndt);
-    hi.pd = (int)cdiv(ndt, hi.chunk_blocks);
+    const int spg = hi.kcap * (hi.S / kPage);
+    sel_pages = std::max(sel_pages, spg);
     c->k_cap = std::max(c->k_cap, hi.kcap);
-    c->p_cap = std::max<int32_t>(c->p_cap, hi.pd + (int32_t)cdiv(hi.kcap, hi.chunk_blocks));
+    c->p_cap = std::max<int32_t>(c->p_cap, (int32_t)std::max<int64_t>(1, cdiv(lm_sel0 + spg, kPartPages)));
   }
 
   if (c->p_cap > kFuseSlots)
@@ -284,7 +284,8 @@ sd_status sparse_decode_init(const sd_config *cfg, sd_ctx **out) {
   c->dims.maw_beta = cfg->maw_beta;
   key_stride = (int)cdiv(key_stride, 64) * 64;  // whole top-k rows of 64 blocks
   c->dims.key_stride = key_stride;
-  c->dims.ndt_cap = ndt_cap;
+  c->dims.lm_sel0 = lm_sel0;
+  c->dims.lm_cap = lm_sel0 + sel_pages;
   c->dims.kcap = c->k_cap;
 
   // scratch
@@ -295,8 +296,7 @@ sd_status sparse_decode_init(const sd_config *cfg, sd_ctx **out) {
   if ((s = dev_alloc(c, &c->sc.ukeys, per_unit)) != SD_OK) return s;
   if ((s = dev_alloc(c, &c->sc.unit_acc, (size_t)max_seqs * c->Hkv * 2)) != SD_OK) return s;
   SD_HIP(c, hipMemset(c->sc.unit_acc, 0, sizeof(uint32_t) * max_seqs * c->Hkv * 2));
-  if ((s = dev_alloc(c, &c->sc.lm_dense, (size_t)max_seqs * c->Hq * ndt_cap)) != SD_OK) return s;
-  if ((s = dev_alloc(c, &c->sc.lm_sel, (size_t)max_seqs * c->Hq * c->k_cap)) != SD_OK) return s;
+  if ((s = dev_alloc(c, &c->sc.lm_pg, (size_t)max_seqs * c->Hq * c->dims.lm_cap)) != SD_OK) return s;
   if ((s = dev_alloc(c, &c->sc.usel, (size_t)max_seqs * c->Hkv * c->k_cap)) != SD_OK) return s;
   if ((s = dev_alloc(c, &c->sc.ucnt, (size_t)max_seqs * c->Hkv)) != SD_OK) return s;
   if ((s = dev_alloc(c, &c->sc.arrive, (size_t)max_seqs * c->Hkv * 2)) != SD_OK) return s;
@@ -304,9 +304,13 @@ sd_status sparse_decode_init(const sd_config *cfg, sd_ctx **out) {
   SD_HIP(c, hipMemset(c->sc.arrive, 0, sizeof(uint32_t) * max_seqs * c->Hkv * 2));
   if ((s = dev_alloc(c, &c->sc.cand, per_unit)) != SD_OK) return s;
   if ((s = dev_alloc(c, &c->sc.tcnt, (size_t)max_seqs * c->Hkv * kFastTiles)) != SD_OK) return s;
-  if ((s = dev_alloc(c, &c->sc.ready, (size_t)max_seqs * c->Hkv)) != SD_OK) return s;
+  if ((s = dev_alloc(c, &c->sc.scored, (size_t)max_seqs * c->Hkv)) != SD_OK) return s;
+  if ((s = dev_alloc(c, &c->sc.rtag, (size_t)max_seqs * c->Hkv)) != SD_OK) return s;
+  if ((s = dev_alloc(c, &c->sc.seltag, (size_t)max_seqs * c->Hkv * c->k_cap)) != SD_OK) return s;
   if ((s = dev_alloc(c, &c->sc.err, 1)) != SD_OK) return s;
-  SD_HIP(c, hipMemset(c->sc.ready, 0, sizeof(uint32_t) * max_seqs * c->Hkv));
+  SD_HIP(c, hipMemset(c->sc.scored, 0, sizeof(uint32_t) * max_seqs * c->Hkv));
+  SD_HIP(c, hipMemset(c->sc.rtag, 0, sizeof(unsigned long long) * max_seqs * c->Hkv));
+  SD_HIP(c, hipMemset(c->sc.seltag, 0, sizeof(unsigned long long) * max_seqs * c->Hkv * c->k_cap));
   SD_HIP(c, hipMemset(c->sc.err, 0, sizeof(uint32_t)));
 
   // layers
@@ -461,6 +465,27 @@ int64_t k_of_seq(const sd_ctx *c, int64_t N, int h) {
   return k_of(N, c->S[h], c->ppm[h], c->cfg.sink_tokens, c->cfg.recent_window);
 }
 
+// Pages holding dense tokens (sinks, recent window) of a sequence of N tokens.
+int64_t dense_pages(const sd_ctx *c, int64_t N) {
+  const int64_t np = cdiv(N, kPage);
+  const int64_t sp = cdiv(std::min<int64_t>(c->cfg.sink_tokens, N), kPage);
+  const int64_t wlo = std::max<int64_t>(0, N - c->cfg.recent_window);
+  const int64_t wp = wlo < N ? std::max<int64_t>(sp, wlo / kPage) : np;
+  return sp + (np - wp);
+}
+
+// Attention workgroups per unit of one launch: about kPartPages attended
+// pages each, for the unit with the most.
+int parts_of(const sd_ctx *c, const SeqBatch &b) {
+  int64_t P = 1;
+  for (int i = 0; i < b.n; ++i)
+    for (int h = 0; h < c->Hkv; ++h) {
+      const int64_t pages = dense_pages(c, b.len[i]) + k_of_seq(c, b.len[i], h) * (c->S[h] / kPage);
+      P = std::max<int64_t>(P, cdiv(pages, kPartPages));
+    }
+  return (int)std::min<int64_t>(P, c->p_cap);
+}
+
 sd_status check_kcap(sd_ctx *c, int layer, int n_seqs, const int32_t *seq_ids, int32_t k_cap) {
   const Layer &L = c->layers[layer];
   for (int i = 0; i < n_seqs; ++i)
@@ -503,8 +528,7 @@ sd_status select_topk(sd_ctx *c, int32_t layer, int32_t n_seqs,
     fill_batch(c, layer, seq_ids, base, std::min(kLaunchSeqs, n_seqs - base), &b, &mb);
     const uint16_t *qb = q + (size_t)base * c->Hq * c->D;
     SD_HIP(c, launch_select(kc, b, mb, qb, blk_idx + (size_t)base * c->Hkv * k_cap,
-                            blk_cnt + (size_t)base * c->Hkv, k_cap, 0, nullptr, nullptr, 0,
-                            c->stream));
+                            blk_cnt + (size_t)base * c->Hkv, k_cap, c->stream));
   }
   return SD_OK;
 }
@@ -525,10 +549,13 @@ sd_status sparse_attend(sd_ctx *c, int32_t layer, int32_t n_seqs,
     return fail(c, SD_EINVAL, "p_cap %d < %d partial slots per head (sd_caps)", p_cap, c->p_cap);
   const Ctx kc = kctx(c, layer);
   const uint16_t *q = static_cast<const uint16_t *>(q_bf16);
+  c->pend_parts.clear();
   for (int base = 0; base < n_seqs; base += kLaunchSeqs) {
     SeqBatch b;
     fill_batch(c, layer, seq_ids, base, std::min(kLaunchSeqs, n_seqs - base), &b, nullptr);
-    SD_HIP(c, launch_attend(kc, b, q + (size_t)base * c->Hq * c->D,
+    const int P = parts_of(c, b);
+    c->pend_parts.push_back(P);
+    SD_HIP(c, launch_attend(kc, b, P, q + (size_t)base * c->Hq * c->D,
                             blk_idx + (size_t)base * c->Hkv * k_cap,
                             blk_cnt + (size_t)base * c->Hkv, k_cap,
                             o_part + (size_t)base * c->Hq * p_cap * c->D,
@@ -570,7 +597,8 @@ sd_status fuse_lse(sd_ctx *c, int32_t layer, int32_t n_seqs,
       b.n = n;
       for (int i = 0; i < n; ++i) b.seq[i] = b.len[i] = 0;
     }
-    SD_HIP(c, launch_fuse(kc, b, with_maw, o_part + (size_t)base * c->Hq * p_cap * c->D,
+    const int P = with_maw ? c->pend_parts[base / kLaunchSeqs] : p_cap;
+    SD_HIP(c, launch_fuse(kc, b, with_maw, P, o_part + (size_t)base * c->Hq * p_cap * c->D,
                           lse_part + (size_t)base * c->Hq * p_cap, p_cap,
                           o + (size_t)base * c->Hq * c->D, lse + (size_t)base * c->Hq,
                           c->stream));
@@ -622,21 +650,15 @@ sd_status sparse_decode_step(sd_ctx *c, int32_t layer, int32_t n_seqs,
     const int n = std::min(kLaunchSeqs, n_seqs - base);
     fill_batch(c, layer, seq_ids, base, n, &b, &mb);
     const uint16_t *qb = q + (size_t)base * c->Hq * c->D;
-    int dchunks = 0, schunks = 0;
-    for (int i = 0; i < n; ++i)
-      for (int h = 0; h < c->Hkv; ++h) {
-        const HeadInfo &hi = c->heads[h];
-        dchunks = std::max(dchunks, hi.pd);
-        schunks = std::max<int>(schunks, (int)cdiv(k_of_seq(c, b.len[i], h), hi.chunk_blocks));
-      }
+    const int P = parts_of(c, b);
     int32_t *bi = blk_idx + (size_t)base * c->Hkv * k_cap;
     int32_t *bc = blk_cnt + (size_t)base * c->Hkv;
     float *op = o_part + (size_t)base * c->Hq * p_cap * c->D;
     float *lp = lse_part + (size_t)base * c->Hq * p_cap;
     if (++c->epoch == 0) c->epoch = 1;
-    SD_HIP(c, launch_step(kc, b, mb, qb, bi, bc, k_cap, dchunks, schunks, op, lp, p_cap,
+    SD_HIP(c, launch_step(kc, b, mb, P, qb, bi, bc, k_cap, op, lp, p_cap,
                           o + (size_t)base * c->Hq * c->D, lse + (size_t)base * c->Hq,
-                          c->epoch, c->stream));
+                          c->epoch, c->pps <= kPtLds ? c->pps : 0, c->stream));
   }
   c->pend_layer = -2;
   return SD_OK;
@@ -738,9 +760,13 @@ sd_status sd_debug_copy(sd_ctx *c, int32_t what, int32_t layer, int32_t seq,
       SD_HIP(c, hipMemcpy(page.data(), pool + (size_t)pid * page_elems,
                           page_elems * sizeof(uint16_t), hipMemcpyDeviceToHost));
       for (int r = 0; r < kPage && p * kPage + r < len; ++r)
-        for (int h = 0; h < c->Hkv; ++h)
-          memcpy(dst + (((size_t)(p * kPage + r)) * c->Hkv + h) * D,
-                 page.data() + ((size_t)h * kPage + r) * D, sizeof(uint16_t) * D);
+        for (int h = 0; h < c->Hkv; ++h) {
+          uint16_t *row = dst + (((size_t)(p * kPage + r)) * c->Hkv + h) * D;
+          if (what == SD_DEBUG_K)
+            memcpy(row, page.data() + ((size_t)h * kPage + r) * D, sizeof(uint16_t) * D);
+          else  // V pages are stored transposed: [Hkv][d][16]
+            for (int ch = 0; ch < D; ++ch) row[ch] = page[((size_t)h * D + ch) * kPage + r];
+        }
     }
   }
   return SD_OK;

@@ -257,7 +257,7 @@ def test_fuse_pure_identity():
 
 
 def test_error_paths():
-    w = _w(synth.tiny(), N=2000)
+    w = _w(synth.tiny(), N=2000, budget_ppm=[1000000])  # full budget: several partial slots
     log("case: error paths")
     eng = harness.make_engine(w, 2048)
     try:
@@ -279,8 +279,8 @@ def test_error_paths():
         big = torch.zeros(4096, 1, w.d, dtype=torch.bfloat16, device="cuda")
         assert eng.append_kv(0, [0], [4096], big, big, check=False) == -1  # > max_seq_len
         assert eng.seq_len(0, 0) == 2000
-        # 2000 tokens at 25%: 1 + 32 + 5 attended blocks -> 3 chunks needed
-        # p_cap too small
+        # p_cap too small (the engine needs more than one partial slot here)
+        assert eng.p_cap > 1
         tiny_part = torch.zeros(1, w.Hq, 1, w.d, device="cuda")
         tiny_lse = torch.zeros(1, w.Hq, 1, device="cuda")
         eng.select_topk(0, [0], q, bufs["blk_idx"], bufs["blk_cnt"])
