@@ -89,7 +89,6 @@ struct Scratch {
   unsigned long long *cand;  // [max_seqs][Hkv][key_stride] per-tile candidate lists
                              // (key << 32 | block), tile t's at [t*kScoreTile, ...)
   uint32_t *tcnt;    // [max_seqs][Hkv][kFastTiles] entries of each tile's list
-  uint32_t *scored;  // [max_seqs][Hkv] step number once every score tile of the unit is done
   unsigned long long *rtag;    // [max_seqs][Hkv] step << 32 | selected count, published
                                // after the selection
   unsigned long long *seltag;  // [max_seqs][Hkv][kcap] step << 32 | block of the selection

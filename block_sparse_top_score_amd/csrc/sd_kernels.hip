@@ -164,16 +164,14 @@ struct TopkSmem {
   int32_t ulist[kTopkUnc];  // uncertain blocks of the top-k, in index order
   uint32_t ukey[kTopkUnc];  // their exact keys
   uint32_t tk[kScoreTile];  // keys of a score tile (fast top-k)
-  int32_t tslot[kScoreTile];  // list slot of each block of a score tile, or -1
-  uint4 cs[kTileList][32];  // summaries of a score tile's listed blocks
-  double ue[kTileList * SD_MAX_GROUP];  // their exact scores, per head
+  double ue[kTileList * SD_MAX_GROUP];  // exact scores of the fast top-k's band, per head
   unsigned long long bm[kFastTiles * kScoreTile / 64];  // chosen blocks (fast top-k)
   unsigned long long srt[kFastTiles][kTileList];  // sorted lists (tile; fast top-k)
   int rk[4][kTileList];  // partial ranks of a tile's list
   float qs[SD_MAX_GROUP * 128];
   double ud[16];
   uint32_t red[8];
-  int nlist;
+  int nlist, nin, kr2, ok;
   int last;
 };
 
@@ -371,30 +369,23 @@ __device__ __forceinline__ float score_eps(float E, float A) {
 __device__ __forceinline__ float upper_term(float qv, uint32_t mm) {
   return qv >= 0.0f ? bf16_hi(mm) : bf16_lo(mm);
 }
-// Exact list of one score tile for the fast top-k (no MAW flags, kk <= 64):
-// the tile's kk best blocks by exact score, as keys (exact order key << 32 |
-// ~block), descending, padded with zeros.  Wave 0 bounds the tile's kk-th
-// largest approximate key L from below by a few bisection steps (a <= L,
-// count(>= a) >= kk); every block with exact score among the tile's kk best
-// has an approximate score >= a - 2 eps_t (kk blocks have exact scores >=
-// a - eps_t), so only those are listed, at most kTileList.  All waves stage
-// the listed blocks' summaries in LDS, score them exactly (double, channel
-// order, as the oracle does), rank the keys and wave 0 publishes the list in
-// descending order.  A tile that
-// would list more publishes the count kTileOverflow instead (the top-k then
-// takes the full path).  Every thread of the workgroup calls it, after the
-// tile's keys are in sm.tk.
+// List of one score tile for the fast top-k (no MAW flags, kk <= kTileList):
+// the blocks whose approximate score can still reach the unit's top kk, as
+// keys (approximate order key << 32 | ~block), descending, padded with
+// zeros.  Wave 0 bounds the tile's kk-th largest approximate key L from below
+// by a few bisection steps (a <= L, count(>= a) >= kk).  A block with A <
+// a - 2 eps_t has kk blocks in its own tile whose exact scores are larger
+// (each at least a - eps_t > A + eps_t), so only blocks with A >= a - 2 eps_t
+// are listed, at most kTileList.  The four waves rank the keys and wave 0
+// publishes them in order.  A tile that would list more publishes the count
+// kTileOverflow (the top-k then takes the full path).  Every thread of the
+// workgroup calls it, after the tile's keys are in sm.tk.
 constexpr int kTileSteps = 12;
 constexpr uint32_t kTileOverflow = 0xffffffffu;
-template <int D, int G>
-__device__ __forceinline__ void tile_exact_list(const Ctx &c, int i, int seq, int h,
-                                                const UG &g, int tile,
-                                                const uint16_t *__restrict__ q,
-                                                const uint4 (&kf)[kScoreTile / 64][D / 16],
-                                                double eps_t, TopkSmem &sm) {
+__device__ __forceinline__ void tile_list(const Ctx &c, int seq, int h, const UG &g, int tile,
+                                          double eps_t, TopkSmem &sm) {
   const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
-  const int r16 = lane & 15, lgrp = lane >> 4;
-  constexpr int TR = kScoreTile / 64, MM = D / 16;
+  constexpr int TR = kScoreTile / 64;
   const size_t unit = (size_t)seq * c.dm.Hkv + h;
   const int kk = g.kk;
   if (wv == 0) {
@@ -433,9 +424,9 @@ __device__ __forceinline__ void tile_exact_list(const Ctx &c, int i, int seq, in
       const bool in = kk > 0 && x[r] >= dmin;
       const unsigned long long m = __ballot(in);
       const int pos = n + lanes_below(m);
-      const bool put = in && pos < kTileList;
-      sm.tslot[r * 64 + lane] = put ? pos : -1;
-      if (put) sm.ulist[pos] = tile * kScoreTile + r * 64 + lane;
+      if (in && pos < kTileList)
+        sm.srt[0][pos] = ((unsigned long long)x[r] << 32) |
+                         (uint32_t)~(uint32_t)(tile * kScoreTile + r * 64 + lane);
       n += __popcll(m);
     }
     if (lane == 0) sm.nlist = n;
@@ -447,53 +438,8 @@ __device__ __forceinline__ void tile_exact_list(const Ctx &c, int i, int seq, in
     if (tid == 0) st_dev(&c.sc.tcnt[unit * kFastTiles + tile], kTileOverflow);
     return;
   }
-  // stage the listed blocks' summaries (lane (r16, lgrp) holds channel quads
-  // 4 mm + lgrp of block r16 of its groups) and the group's query
-#pragma unroll
-  for (int gi = 0; gi < TR; ++gi) {
-    const int sl = sm.tslot[wv * 64 + gi * 16 + r16];
-    if (sl >= 0) {
-#pragma unroll
-      for (int mm = 0; mm < MM; ++mm) sm.cs[sl][4 * mm + lgrp] = kf[gi][mm];
-    }
-  }
-  __syncthreads();
-  // exact score of (listed block, head) pairs: the plain sequential sum
-  // (LDS reads batched eight channel quads at a time)
-  for (int p = tid; p < n * G; p += 256) {
-    const int b = p / G, gg = p - b * G;
-    const float4 *qv = reinterpret_cast<const float4 *>(sm.qs + gg * D);
-    double acc = 0.0;
-#pragma unroll
-    for (int c8 = 0; c8 < D / 4; c8 += 8) {
-      uint4 w[8];
-      float4 qq[8];
-#pragma unroll
-      for (int t = 0; t < 8; ++t) {
-        w[t] = sm.cs[b][c8 + t];
-        qq[t] = qv[c8 + t];
-      }
-#pragma unroll
-      for (int t = 0; t < 8; ++t) {
-        const uint32_t ws[4] = {w[t].x, w[t].y, w[t].z, w[t].w};
-        const float qf[4] = {qq[t].x, qq[t].y, qq[t].z, qq[t].w};
-#pragma unroll
-        for (int j = 0; j < 4; ++j) acc = fma((double)qf[j], (double)upper_term(qf[j], ws[j]), acc);
-      }
-    }
-    sm.ue[p] = acc;
-  }
-  __syncthreads();
-  // keys (every wave, lane = list entry), then each wave counts the larger
-  // keys among 16 entries: the rank of an entry is its place in the sorted list
-  unsigned long long key = 0ull;
-  if (lane < n) {
-    double best = sm.ue[lane * G];
-#pragma unroll
-    for (int gg = 1; gg < G; ++gg) best = sm.ue[lane * G + gg] > best ? sm.ue[lane * G + gg] : best;
-    const int blk = sm.ulist[lane];  // listed in block order
-    key = ((unsigned long long)order_key((float)best) << 32) | (uint32_t)~(uint32_t)blk;
-  }
+  // rank of each listed key: each wave counts the larger keys among 16 of them
+  const unsigned long long key = lane < n ? sm.srt[0][lane] : 0ull;
   int rk = 0;
 #pragma unroll
   for (int t = 0; t < 16; ++t) {
@@ -510,11 +456,11 @@ __device__ __forceinline__ void tile_exact_list(const Ctx &c, int i, int seq, in
     // is larger, so listed ranks are below n)
     const int pos = lane < n ? sm.rk[0][lane] + sm.rk[1][lane] + sm.rk[2][lane] + sm.rk[3][lane]
                              : lane;
-    sm.srt[0][pos] = key;
+    sm.srt[1][pos] = key;
     __builtin_amdgcn_s_waitcnt(0xc07f);
     __builtin_amdgcn_wave_barrier();
-    st_dev(&dst[lane], sm.srt[0][lane]);
-    if (lane == 0) st_dev(&c.sc.tcnt[unit * kFastTiles + tile], (uint32_t)min(n, kk));
+    st_dev(&dst[lane], sm.srt[1][lane]);
+    if (lane == 0) st_dev(&c.sc.tcnt[unit * kFastTiles + tile], (uint32_t)n);
   }
 }
 
@@ -576,16 +522,6 @@ __device__ __attribute__((always_inline)) void score_tile(const Ctx &c, int i, i
       o4[2 * t + 1] = hi_neg | (hi_pos << 16);
     }
     qa[mm] = r16 < G ? make_uint4(o4[0], o4[1], o4[2], o4[3]) : make_uint4(0, 0, 0, 0);
-  }
-  if (publish && wv == 0 && r16 < G) {  // the query as floats, for the exact list
-#pragma unroll
-    for (int mm = 0; mm < MM; ++mm) {
-      float *d4 = sm.qs + r16 * D + 4 * (4 * mm + lgrp);
-      d4[0] = bf16_lo(qw[mm].x);
-      d4[1] = bf16_hi(qw[mm].x);
-      d4[2] = bf16_lo(qw[mm].y);
-      d4[3] = bf16_hi(qw[mm].y);
-    }
   }
   const uint32_t absm = 0x7fff7fffu;
   float emax = 0.0f;
@@ -653,7 +589,7 @@ __device__ __attribute__((always_inline)) void score_tile(const Ctx &c, int i, i
   }
   if (publish) {
     const double eps_t = (double)__uint_as_float(max(max(red[0], red[1]), max(red[2], red[3])));
-    tile_exact_list<D, G>(c, i, seq, h, g, tile, q, kf, eps_t, sm);
+    tile_list(c, seq, h, g, tile, eps_t, sm);
   }
 }
 
@@ -1058,19 +994,26 @@ __device__ __attribute__((always_inline)) void topk_unit(const Ctx &c, int i, in
   }
 }
 
-// Fast top-k of one unit from the score tiles' exact lists (no MAW flags,
-// kk <= kTileList; every thread of the workgroup calls it and gets the same
-// result).  The unit's kk best blocks are among the kk best of their own
-// tiles.  The rank of entry p of tile r's descending list among all listed
-// keys is p plus, for every other tile, the number of its keys above (a
-// binary search of its list in LDS); the entries of rank below kk are the
-// unit's top kk in (exact score desc, index asc) order.  Each is written at
-// its place in ascending block order, read off an LDS bitmap of the chosen
-// blocks.  Returns false, before writing anything, when a tile overflowed
-// its list; the caller then runs topk_unit on the full keys.
+// Fast top-k of one unit from the score tiles' lists (no MAW flags, kk <=
+// kTileList; every thread of the workgroup calls it and gets the same
+// result).  The steps of topk_unit run on the listed keys, which hold the
+// unit's top kk:
+//   1. bisection, inside the bracket [max over tiles of the kk-th listed key,
+//      max over tiles of the ceil(kk / tiles)-th] (some tile holds that many
+//      of the top kk), narrows [a, b] around the kk-th largest approximate
+//      key T to within the unit's error bound eps;
+//   2. band: keys above b + 2 eps are in, below a - 2 eps out; the blocks in
+//      between are re-scored exactly by the four waves, one lane quad per
+//      (block, head);
+//   3. the kk - (blocks in) best of them by (exact key desc, index asc);
+//   4. each chosen block is written at its place in ascending block order,
+//      read off an LDS bitmap of the chosen blocks.
+// Returns false, before writing anything, when a tile overflowed its list or
+// the band holds more than kTileList blocks; the caller then runs topk_unit.
 template <int D, int G>
 __device__ __attribute__((always_inline)) bool topk_fast(const Ctx &c, int i, int seq, int h,
                                                          const HeadInfo &hi, const UG &g,
+                                                         const uint16_t *__restrict__ q,
                                                          int32_t *__restrict__ blk_idx,
                                                          int32_t *__restrict__ blk_cnt, int k_cap,
                                                          TopkSmem &sm,
@@ -1082,88 +1025,142 @@ __device__ __attribute__((always_inline)) bool topk_fast(const Ctx &c, int i, in
   const unsigned long long *cl = c.sc.cand + unit * c.dm.key_stride;
   const int kk = g.kk;
   const int nw = cdiv(g.n_blk, 64);
-  // wave w holds lists w and w + 4
-  constexpr int RW = kFastTiles / 4;
-  unsigned long long e[RW];
+  // one batch of loads: lists and counts (wave 0), error bound, the query
+  unsigned long long e[kFastTiles];
   uint32_t cntv[kFastTiles];
 #pragma unroll
-  for (int rr = 0; rr < RW; ++rr) {
-    const int r = wv + 4 * rr;
-    e[rr] = r < n_tiles ? ld_dev(&cl[(size_t)r * kTileList + lane]) : 0ull;
+  for (int r = 0; r < kFastTiles; ++r) {
+    const bool on = wv == 0 && r < n_tiles;
+    e[r] = on ? ld_dev(&cl[(size_t)r * kTileList + lane]) : 0ull;
+    cntv[r] = on ? ld_dev(&c.sc.tcnt[unit * kFastTiles + r]) : 0u;
   }
+  const uint32_t eps_bits = ld_dev(&c.sc.unit_acc[2 * unit]);
+  const uint16_t *qg = q + ((size_t)i * c.dm.Hq + (size_t)h * G) * D;
+  constexpr int QT = (G * D + 255) / 256;
+  uint16_t qv[QT];
 #pragma unroll
-  for (int r = 0; r < kFastTiles; ++r)
-    cntv[r] = r < n_tiles ? ld_dev(&c.sc.tcnt[unit * kFastTiles + r]) : 0u;
-  bool ok = true;
+  for (int t = 0; t < QT; ++t) qv[t] = qg[min(tid + 256 * t, G * D - 1)];
 #pragma unroll
-  for (int r = 0; r < kFastTiles; ++r) ok = ok && cntv[r] != kTileOverflow;
-  if (!ok) return false;
-#pragma unroll
-  for (int rr = 0; rr < RW; ++rr) {
-    const int r = wv + 4 * rr;
-    if (r < n_tiles) sm.srt[r][lane] = e[rr];
-  }
-  if (tid < nw) sm.bm[tid] = 0ull;
-  if (tid == 0) sm.nlist = 0;
-  __syncthreads();
-  int n_take = 0;
-  int myblk[RW];
-#pragma unroll
-  for (int rr = 0; rr < RW; ++rr) {
-    const int r = wv + 4 * rr;
-    const unsigned long long v = e[rr];
-    bool take = false;
-    if (r < n_tiles && lane < kk && v != 0ull) {
-      // keys of each list above v: binary searches of all lists in lockstep
-      int pr[kFastTiles];
-#pragma unroll
-      for (int r2 = 0; r2 < kFastTiles; ++r2) pr[r2] = 0;
-#pragma unroll
-      for (int st = 32; st > 0; st >>= 1)
-#pragma unroll
-        for (int r2 = 0; r2 < kFastTiles; ++r2)
-          if (r2 < n_tiles && sm.srt[r2][pr[r2] + st - 1] > v) pr[r2] += st;
-      int rank = lane;
-#pragma unroll
-      for (int r2 = 0; r2 < kFastTiles; ++r2)
-        if (r2 < n_tiles && r2 != r) rank += pr[r2] + (sm.srt[r2][pr[r2]] > v ? 1 : 0);
-      take = rank < kk;
-    }
-    myblk[rr] = take ? (int)~(uint32_t)v : -1;
-    if (take) atomicOr(&sm.bm[myblk[rr] >> 6], 1ull << (myblk[rr] & 63));
-    n_take += count_lanes(take);
-  }
-  if (lane == 0 && n_take) atomicAdd(&sm.nlist, n_take);
-  __syncthreads();
-  if (sm.nlist != kk) return false;  // not expected: the lists are complete
-  // chosen blocks below each bitmap word: wave 0 scans the words' popcounts
+  for (int t = 0; t < QT; ++t)
+    if (tid + 256 * t < G * D) sm.qs[tid + 256 * t] = __uint_as_float((uint32_t)qv[t] << 16);
+
   if (wv == 0) {
-    const int cw = lane < nw ? __popcll(sm.bm[lane]) : 0;
+    bool ok = true;
+#pragma unroll
+    for (int r = 0; r < kFastTiles; ++r) ok = ok && cntv[r] != kTileOverflow;
+    int n_in = 0, n_unc = 0;
+    if (lane < nw) sm.bm[lane] = 0ull;
+    __builtin_amdgcn_s_waitcnt(0xc07f);
+    __builtin_amdgcn_wave_barrier();
+    if (ok && kk > 0) {
+      const double eps = (double)__uint_as_float(eps_bits);
+      auto key_of = [&](int r, int l) {  // listed key r, l (uniform)
+        return (uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)(e[r] >> 32), l);
+      };
+      const int cb = cdiv(kk, n_tiles);
+      uint32_t a = 0u, b = 0u;
+#pragma unroll
+      for (int r = 0; r < kFastTiles; ++r)
+        if (r < n_tiles) {
+          a = max(a, key_of(r, kk - 1));
+          b = max(b, key_of(r, cb - 1));
+        }
+      a = max(a, 2u);
+      while (a < b && (double)key_to_float(b) - (double)key_to_float(a) > eps) {
+        const uint32_t mid = a + ((b - a) >> 1) + 1u;
+        int cm = 0;
+#pragma unroll
+        for (int r = 0; r < kFastTiles; ++r)
+          if (r < n_tiles) cm += count_lanes((uint32_t)(e[r] >> 32) >= mid);
+        if (cm >= kk) a = mid; else b = mid - 1u;
+      }
+      const uint32_t kb_hi = order_key(__double2float_rd((double)key_to_float(b) + 2.0 * eps));
+      const uint32_t kb_lo = order_key(__double2float_ru((double)key_to_float(a) - 2.0 * eps));
+#pragma unroll
+      for (int r = 0; r < kFastTiles; ++r) {
+        if (r >= n_tiles) break;
+        const uint32_t kx = (uint32_t)(e[r] >> 32);
+        const int blk = (int)~(uint32_t)e[r];
+        const bool in = kx >= 2u && kx > kb_hi;
+        const bool unc = kx >= 2u && kx >= kb_lo && kx <= kb_hi;
+        if (in) atomicOr(&sm.bm[blk >> 6], 1ull << (blk & 63));
+        const unsigned long long mu = __ballot(unc);
+        const int pos = n_unc + lanes_below(mu);
+        if (unc && pos < kTileList) sm.ulist[pos] = blk;
+        n_unc += __popcll(mu);
+        n_in += count_lanes(in);
+      }
+      ok = n_unc <= kTileList && n_in <= kk && n_in + n_unc >= kk;
+    }
+    if (lane == 0) {
+      sm.ok = ok;
+      sm.nin = n_in;
+      sm.nlist = n_unc;
+    }
+  }
+  __syncthreads();
+  if (!sm.ok) return false;
+  const int n_unc = sm.nlist, kr2 = kk - sm.nin;
+  if (kr2 > 0) {
+    // exact keys of the band, one lane quad per (block, head), in passes of 64
+    for (int p0 = 0; p0 < n_unc * G; p0 += 64) {
+      const int pair = p0 + (tid >> 2);
+      const bool on = pair < n_unc * G;
+      const int u = on ? pair / G : 0, gg = on ? pair - u * G : 0;
+      const double U = exact_score_quad<D>(c, seq, hi, on ? sm.ulist[u] : 0, sm.qs + gg * D, on);
+      if (on && (tid & 3) == 0) sm.ue[pair] = U;
+    }
+    __syncthreads();
+    if (wv == 0) {
+      unsigned long long ek = 0ull;
+      if (lane < n_unc) {
+        double best = sm.ue[lane * G];
+#pragma unroll
+        for (int gg = 1; gg < G; ++gg) best = sm.ue[lane * G + gg] > best ? sm.ue[lane * G + gg] : best;
+        ek = ((unsigned long long)order_key((float)best) << 32) | (uint32_t)~(uint32_t)sm.ulist[lane];
+      }
+      int rank = 0;
+      for (int t = 0; t < n_unc; ++t) {
+        const unsigned long long o =
+            ((unsigned long long)(uint32_t)__builtin_amdgcn_readlane((int)(ek >> 32), t) << 32) |
+            (uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)ek, t);
+        rank += o > ek ? 1 : 0;
+      }
+      if (lane < n_unc && rank < kr2) {
+        const int blk = sm.ulist[lane];
+        atomicOr(&sm.bm[blk >> 6], 1ull << (blk & 63));
+      }
+    }
+  }
+  if (wv == 0) {
+    __builtin_amdgcn_s_waitcnt(0xc07f);
+    __builtin_amdgcn_wave_barrier();
+    // ascending order: exclusive prefix of the words' popcounts, then each
+    // lane writes the chosen blocks of its word
+    unsigned long long wbits = lane < nw ? sm.bm[lane] : 0ull;
+    const int cw = __popcll(wbits);
     int incl = cw;
 #pragma unroll
     for (int off = 1; off < 64; off <<= 1) {
       const int t = __shfl_up(incl, off, 64);
       if (lane >= off) incl += t;
     }
-    if (lane < nw) sm.rk[0][lane] = incl - cw;
-  }
-  __syncthreads();
-  int32_t *dst = blk_idx + ((size_t)i * c.dm.Hkv + h) * k_cap;
-#pragma unroll
-  for (int rr = 0; rr < RW; ++rr) {
-    const int b = myblk[rr];
-    if (b >= 0) {
-      const int o = sm.rk[0][b >> 6] + __popcll(sm.bm[b >> 6] & ((1ull << (b & 63)) - 1ull));
+    int o = incl - cw;
+    int32_t *dst = blk_idx + ((size_t)i * c.dm.Hkv + h) * k_cap;
+    while (wbits) {
+      const int bb = lane * 64 + (__ffsll((long long)wbits) - 1);
       if (o < k_cap) {
-        st_dev(&dst[o], b);
-        if (tagd && o < c.dm.kcap) st_dev(&tagd[o], ((unsigned long long)epoch << 32) | (uint32_t)b);
+        st_dev(&dst[o], bb);
+        if (tagd && o < c.dm.kcap) st_dev(&tagd[o], ((unsigned long long)epoch << 32) | (uint32_t)bb);
       }
+      ++o;
+      wbits &= wbits - 1ull;
     }
-  }
-  if (tid == 0) {
-    st_dev(&blk_cnt[(size_t)i * c.dm.Hkv + h], kk);
-    st_dev(&c.sc.unit_acc[2 * unit], 0u);  // cleared for the next step
-    st_dev(&c.sc.unit_acc[2 * unit + 1], 0u);
+    if (lane == 0) {
+      st_dev(&blk_cnt[(size_t)i * c.dm.Hkv + h], kk);
+      st_dev(&c.sc.unit_acc[2 * unit], 0u);  // cleared for the next step
+      st_dev(&c.sc.unit_acc[2 * unit + 1], 0u);
+    }
   }
   return true;
 }
@@ -1399,12 +1396,10 @@ __device__ __forceinline__ void compute_stage(const Ctx &c, KVStage<D> &st, int 
 // One wave over its positions of a page list of `total` entries: positions
 // gw + i NW.  resolve(t, pg, mk, sl) gives the page id, token mask and
 // log-mass slot of list position t; up to 64 positions are resolved at once,
-// one per lane.  gate (if set): streaming starts once it equals epoch (a
-// bounded wait that is not an error).
+// one per lane.
 template <int D, int G, class Resolve>
 __device__ __forceinline__ void wave_pages(const Ctx &c, int h, int gw, int NW, int total,
-                                           Resolve resolve, const uint32_t *gate, uint32_t epoch,
-                                           const uint4 (&qa)[D / 32], AttWave<D> &W,
+                                           Resolve resolve, const uint4 (&qa)[D / 32], AttWave<D> &W,
                                            float (*pl)[32], float *lmb) {
   const int lane = threadIdx.x & 63;
   const int nw = total > gw ? cdiv(total - gw, NW) : 0;
@@ -1412,10 +1407,6 @@ __device__ __forceinline__ void wave_pages(const Ctx &c, int h, int gw, int NW, 
     const int n = min(64, nw - b0);
     int pg = 0, mk = 0, sl = -1;
     if (lane < n) resolve(gw + (b0 + lane) * NW, pg, mk, sl);
-    if (gate && b0 == 0) {
-      const unsigned long long t0 = wall_clock64();
-      while (ld_dev(gate) != epoch && wall_clock64() - t0 < kWaitTicks) __builtin_amdgcn_s_sleep(4);
-    }
     auto PG = [&](int t) { return __builtin_amdgcn_readlane(pg, min(t, n - 1)); };
     auto MK = [&](int t) { return t < n ? __builtin_amdgcn_readlane(mk, t) : 0; };
     auto SL = [&](int t) { return t < n ? __builtin_amdgcn_readlane(sl, t) : -1; };
@@ -1446,7 +1437,6 @@ struct SelIn {
   int cnt = 0;                               //   and its count
   const unsigned long long *tag = nullptr;   // one-launch step: tagged entries
   const unsigned long long *rtag = nullptr;  //   and the tagged count
-  const uint32_t *gate = nullptr;            //   dense pages wait for this
   uint32_t epoch = 0;
 };
 
@@ -1492,7 +1482,7 @@ __device__ __attribute__((always_inline)) void attend_part(const Ctx &c, int i, 
         mk = page_dense16(g, pn);
         sl = t;
       },
-      si.gate, si.epoch, qa, W, pl, lmb);
+      qa, W, pl, lmb);
 
   // the selection
   int cnt = si.cnt;
@@ -1539,7 +1529,7 @@ __device__ __attribute__((always_inline)) void attend_part(const Ctx &c, int i, 
           mk = page_valid16(g, pn) & ~page_dense16(g, pn);
           sl = c.dm.lm_sel0 + t;
         },
-        nullptr, 0u, qa, W, pl, lmb);
+        qa, W, pl, lmb);
   }
 
   // merge the four waves into the part's partial
@@ -1945,11 +1935,10 @@ __global__ __launch_bounds__(256, 2) void k_step(Ctx c, SeqBatch b, int tiles_x,
     score_tile<D, G>(c, i, seq, h, hi, g, idx, q, smem_topk, true, fast);
     uint32_t *ctr = &c.sc.arrive[unit * 2];
     if (!arrive_last(ctr, (unsigned)n_tiles, &s_flag)) return;
-    if (threadIdx.x == 0) st_dev(&c.sc.scored[unit], epoch);  // opens the dense pages
     __builtin_amdgcn_s_setprio(3);
     uint32_t *lrows = reinterpret_cast<uint32_t *>(smem_raw + sizeof(TopkSmem));
     unsigned long long *tagd = c.sc.seltag + unit * c.dm.kcap;
-    if (!fast || !topk_fast<D, G>(c, i, seq, h, hi, g, blk_idx, blk_cnt, k_cap, smem_topk,
+    if (!fast || !topk_fast<D, G>(c, i, seq, h, hi, g, q, blk_idx, blk_cnt, k_cap, smem_topk,
                                   tagd, epoch))
       topk_unit<D, G>(c, i, seq, h, hi, g, q, blk_idx, blk_cnt, k_cap, smem_topk, lrows,
                       lrows_words, reinterpret_cast<unsigned long long *>(lrows + lrows_words),
@@ -1987,7 +1976,6 @@ __global__ __launch_bounds__(256, 2) void k_step(Ctx c, SeqBatch b, int tiles_x,
   SelIn si;
   si.tag = c.sc.seltag + unit * c.dm.kcap;
   si.rtag = &c.sc.rtag[unit];
-  si.gate = &c.sc.scored[unit];
   si.epoch = epoch;
   attend_part<D, G>(c, i, seq, h, g, idx, P, q, si, o_part, lse_part, p_cap, smem_att, ptl,
                     &s_cnt);
