@@ -22,6 +22,7 @@ constexpr int kPtLds = 4096;         // page-table entries a selected chunk copi
 constexpr int kFuseSlots = 256;      // partial slots per query head, at most
 constexpr int kFuseSelLds = 2048;    // fusion keeps the selection in LDS up to this
 constexpr int kFusePgLds = 2048;     // and the attended pages' masses up to this
+constexpr int kFuseDense = 256;      // and a map of the dense-touching blocks up to this
 
 // Per-KV-head constants, resident in device memory for the context's life
 // (read with uniform addresses, so they come through the scalar cache).

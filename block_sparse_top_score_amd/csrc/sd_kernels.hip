@@ -181,6 +181,7 @@ struct FuseSmem {
   float lse[G];
   int32_t sel[kFuseSelLds];  // the selection
   float pm[kFusePgLds];      // softmax mass of each attended page, summed over heads
+  int32_t dsel[kFuseDense];  // selection index of each dense-touching block, or -1
 };
 
 // ---------------------------------------------------------------------------
@@ -1066,13 +1067,16 @@ __device__ __attribute__((always_inline)) bool topk_fast(const Ctx &c, int i, in
           b = max(b, key_of(r, cb - 1));
         }
       a = max(a, 2u);
-      while (a < b && (double)key_to_float(b) - (double)key_to_float(a) > eps) {
-        const uint32_t mid = a + ((b - a) >> 1) + 1u;
+      auto count_ge = [&](uint32_t t) {
         int cm = 0;
 #pragma unroll
         for (int r = 0; r < kFastTiles; ++r)
-          if (r < n_tiles) cm += count_lanes((uint32_t)(e[r] >> 32) >= mid);
-        if (cm >= kk) a = mid; else b = mid - 1u;
+          if (r < n_tiles) cm += count_lanes((uint32_t)(e[r] >> 32) >= t);
+        return cm;
+      };
+      while (a < b && (double)key_to_float(b) - (double)key_to_float(a) > eps) {
+        const uint32_t mid = a + ((b - a) >> 1) + 1u;
+        if (count_ge(mid) >= kk) a = mid; else b = mid - 1u;
       }
       const uint32_t kb_hi = order_key(__double2float_rd((double)key_to_float(b) + 2.0 * eps));
       const uint32_t kb_lo = order_key(__double2float_ru((double)key_to_float(a) - 2.0 * eps));
@@ -1139,12 +1143,15 @@ __device__ __attribute__((always_inline)) bool topk_fast(const Ctx &c, int i, in
     // lane writes the chosen blocks of its word
     unsigned long long wbits = lane < nw ? sm.bm[lane] : 0ull;
     const int cw = __popcll(wbits);
+    // inclusive prefix: DPP shifts inside 16-lane rows, then the row totals
     int incl = cw;
-#pragma unroll
-    for (int off = 1; off < 64; off <<= 1) {
-      const int t = __shfl_up(incl, off, 64);
-      if (lane >= off) incl += t;
-    }
+    incl += __builtin_amdgcn_update_dpp(0, incl, 0x111, 0xF, 0xF, true);  // row_shr:1
+    incl += __builtin_amdgcn_update_dpp(0, incl, 0x112, 0xF, 0xF, true);  // row_shr:2
+    incl += __builtin_amdgcn_update_dpp(0, incl, 0x114, 0xF, 0xF, true);  // row_shr:4
+    incl += __builtin_amdgcn_update_dpp(0, incl, 0x118, 0xF, 0xF, true);  // row_shr:8
+    const int r0 = __builtin_amdgcn_readlane(incl, 15), r1 = __builtin_amdgcn_readlane(incl, 31),
+              r2 = __builtin_amdgcn_readlane(incl, 47);
+    incl += (lane >= 16 ? r0 : 0) + (lane >= 32 ? r1 : 0) + (lane >= 48 ? r2 : 0);
     int o = incl - cw;
     int32_t *dst = blk_idx + ((size_t)i * c.dm.Hkv + h) * k_cap;
     while (wbits) {
@@ -1701,6 +1708,9 @@ __device__ __attribute__((always_inline)) void fuse_unit(const Ctx &c, int i, in
     const int x = tid + 256 * t;
     if (sel_lds && x < cnt) sm.sel[x] = selv[t];
   }
+  const bool dsel_lds = with_maw && g.n_dt <= kFuseDense;
+  if (dsel_lds)
+    for (int x = tid; x < g.n_dt; x += 256) sm.dsel[x] = -1;
   __syncthreads();
   // ---- O = sum_u w_u O_u (zero weights select 0) ------------------------------
 #pragma unroll
@@ -1752,6 +1762,13 @@ __device__ __attribute__((always_inline)) void fuse_unit(const Ctx &c, int i, in
     if (x < n_pg_lds) sm.pm[x] = page_mass(lmv[t]);
   }
   for (int x = tid + 256 * kFusePgPre; x < n_pg_lds; x += 256) sm.pm[x] = page_mass_at(x);
+  // selection index of each selected block that touches dense tokens
+  if (dsel_lds && sel_lds)
+    for (int j = tid; j < cnt; j += 256) {
+      const int blk = sm.sel[j];
+      if (blk < g.hb) sm.dsel[blk] = j;
+      else if (blk >= g.tb && blk < g.n_blk) sm.dsel[g.hb + (blk - g.tb)] = j;
+    }
   __syncthreads();
   auto pm = [&](int t) { return t < n_pg_lds ? sm.pm[t] : page_mass_at(t); };
   auto sel_at = [&](int j) { return sel_lds ? sm.sel[j] : sel_ld(j); };
@@ -1788,7 +1805,7 @@ __device__ __attribute__((always_inline)) void fuse_unit(const Ctx &c, int i, in
         const int t = dense_pos(dl, blk * PPB + pp);
         if (t >= 0) a += pm(t);
       }
-      const int j = sel_find(blk);
+      const int j = (dsel_lds && sel_lds) ? sm.dsel[x] : sel_find(blk);
       if (j >= 0) a += sel_pages_mass(j);
     } else {
       const int j = x - g.n_dt;
