@@ -139,11 +139,12 @@ sd_status select_topk(sd_ctx *ctx, int32_t layer, int32_t n_seqs,
                       int32_t *blk_idx, int32_t *blk_cnt, int32_t k_cap);
 
 /* Split-K attention over T = D U tokens(selected blocks), a set ([HGCA] dense
- * window + sparse entries; flash-decoding split).  The attended blocks of a
- * (sequence, KV head) are cut into chunks; chunk p of query head h writes
- * o_part[n][h][p][:] (fp32, normalised within the chunk) and
- * lse_part[n][h][p] (natural log of the chunk's sum of exp(scaled logits));
- * unused slots get lse = -inf and O = 0.  blk_idx / blk_cnt are as written by
+ * window + sparse entries; flash-decoding split).  The attended tokens of a
+ * (sequence, KV head) are cut into 16-token pages that P parts share (P <=
+ * p_cap, about 40 pages per part); part p of query head h writes
+ * o_part[n][h][p][:] (fp32, normalised within the part) and
+ * lse_part[n][h][p] (natural log of the part's sum of exp(scaled logits));
+ * slots [P, p_cap) get lse = -inf and O = 0.  blk_idx / blk_cnt are as written by
  * select_topk (ascending, distinct); entries outside [0, n_blk) are ignored.
  * The per-block attention mass needed by fuse_lse is kept inside the context
  * for this layer. */
@@ -169,10 +170,10 @@ sd_status fuse_lse(sd_ctx *ctx, int32_t layer, int32_t n_seqs,
 /* Fused decode step of one layer: the optional append of one token per
  * sequence (k_new, v_new: dev [n_seqs][Hkv][d] bf16, both NULL to skip), then
  * select_topk + sparse_attend + fuse_lse with bitwise identical results, in
- * three launches: [append + query split], [block scoring with the top-k of
- * each (sequence, KV head) done by its last scoring workgroup, alongside the
- * dense sink/window chunks], [selected-block chunks with the LSE fusion and
- * MAW update done by the last chunk of each (sequence, KV head)].
+ * one launch per 64 sequences (after the append's): block scoring with the
+ * top-k of each (sequence, KV head) done by its last scoring workgroup, the
+ * attention parts, and the LSE fusion and MAW update done by the last part of
+ * each (sequence, KV head).
  * blk_idx/blk_cnt/o_part/lse_part are written as by the separate calls, except
  * that partial slots a unit does not use are left unspecified. */
 sd_status sparse_decode_step(sd_ctx *ctx, int32_t layer, int32_t n_seqs,
