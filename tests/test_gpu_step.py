@@ -1,0 +1,198 @@
+"""GPU parity of the one-launch decode step (the benchmarked path) against the
+CPU oracle, including the full-size multi-step workloads on sampled units.
+
+The one-launch step runs its own top-k (score tiles publish candidate lists
+that the last tile ranks) where the separate calls run the full top-k, so it
+is checked against the oracle directly, at the same bars as the separate calls
+(tests/harness.py).
+"""
+import dataclasses
+
+import numpy as np
+import pytest
+import torch
+
+import synth
+from tests import harness
+from tests.harness import log
+
+pytestmark = pytest.mark.gpu
+
+
+def _w(base, **over):
+    return dataclasses.replace(base, **over)
+
+
+@pytest.fixture(autouse=True)
+def _gpu():
+    if not torch.cuda.is_available():
+        pytest.skip("needs a GPU")
+    torch.cuda.set_device(0)
+    yield
+    torch.cuda.synchronize()
+
+
+def _check(st):
+    log("  ties=%d max|dO|=%.3g max rel=%.3g max|dlse|=%.3g" % (
+        st["ties"], st["max_abs"], st["max_rel"], st["max_dlse"]))
+    harness.assert_parity(st)
+
+
+@pytest.mark.parametrize("seed", range(4))
+def test_fused_tiny(seed):
+    log("case: fused tiny seed %d" % seed)
+    _check(harness.run_single_step(synth.tiny(), seed, fused=True))
+
+
+@pytest.mark.parametrize("N", [1, 17, 100, 1007, 2049, 4111])
+def test_fused_ragged(N):
+    log("case: fused tiny N=%d" % N)
+    _check(harness.run_single_step(_w(synth.tiny(), N=N), 3, fused=True))
+
+
+@pytest.mark.parametrize("G,Hkv,d,S", [(7, 4, 128, 16), (8, 2, 64, 64), (1, 2, 128, 32)])
+def test_fused_group_sizes(G, Hkv, d, S):
+    w = _w(synth.tiny(), Hq=G * Hkv, Hkv=Hkv, d=d, N=9000, block_size=[S] * Hkv,
+           budget_ppm=[40000] * Hkv)
+    log("case: fused G=%d Hkv=%d d=%d S=%d" % (G, Hkv, d, S))
+    _check(harness.run_single_step(w, 8, fused=True))
+
+
+@pytest.mark.parametrize("B,S,pct", [(1, 16, 2), (8, 32, 5), (64, 16, 10), (32, 64, 10)])
+def test_fused_sweep_points(B, S, pct):
+    log("case: fused sweep B=%d S=%d budget=%d%%" % (B, S, pct))
+    _check(harness.run_single_step(synth.sweep(B, S, pct), 22, fused=True))
+
+
+def test_fused_llama32k_full():
+    """The benchmarked workload at full size, every unit against the oracle."""
+    log("case: fused llama32k full")
+    st = harness.run_single_step(synth.llama32k(), 1, fused=True, shuffle_seed=12345)
+    _check(st)
+    assert len(st["units"]) == 64
+
+
+def test_fused_qwen128k_full():
+    w = synth.qwen128k(1)
+    log("case: fused qwen128k S=%s ppm=%s" % (w.block_size, w.budget_ppm))
+    _check(harness.run_single_step(w, 2, fused=True))
+
+
+def test_fused_equal_scores_tie_order():
+    """Blocks with bitwise equal summaries have equal scores: the one-launch
+    top-k must take them by index, as the oracle does."""
+    w = _w(synth.llama32k(), B=1, Hq=8, Hkv=2, N=16384)
+    log("case: fused equal-score ties")
+    x = synth.single_step(w, 4, N=w.N)
+    K, V, q = x["K"], x["V"], x["q"]
+    # block 40's keys scaled x4 (a bound well above the rest), copied over
+    # blocks 41..200 of KV head 0: 161 equal top scores
+    S = w.block_size[0]
+    src = (K[0, 40 * S:41 * S, 0].float() * 4.0).to(torch.bfloat16)
+    for blk in range(40, 201):
+        K[0, blk * S:(blk + 1) * S, 0] = src
+    eng = harness.make_engine(w, w.N + 64)
+    try:
+        harness.prefill(eng, 0, K.cuda(), V.cuda())
+        gpu = harness.run_gpu_step(eng, 0, [0], q.cuda(), fused=True)
+        Kb, Vb = synth.bits(K), synth.bits(V)
+        st = harness.check_units(w, eng, 0, [0], synth.bits(q), {0: Kb[0]}, {0: Vb[0]},
+                                 {0: w.N}, gpu)
+        _check(st)
+        assert st["ties"] == 0
+    finally:
+        eng.close()
+
+
+def test_qwen128k_drift_multistep_fused():
+    """qwen128k at full size: four planted sets, one per 64-step epoch; one
+    decode step (with its one-token append) in each epoch, every unit against
+    the oracle."""
+    w = synth.qwen128k(0)
+    log("case: qwen128k drift S=%s ppm=%s" % (w.block_size, w.budget_ppm))
+    seed, N0 = 5, w.N - 4
+    qe, dirs = synth.drift_setup(w, seed, 4, device="cuda")
+    K, V, _ = synth.prefill_with_directions(w, seed, 0, N0, dirs, device="cuda")
+    eng = harness.make_engine(w, w.N + 64)
+    try:
+        harness.prefill(eng, 0, K, V)
+        Kb, Vb = synth.bits(K), synth.bits(V)
+        del K, V
+        K_bits = {b: Kb[b] for b in range(w.B)}
+        V_bits = {b: Vb[b] for b in range(w.B)}
+        N = N0
+        for e in range(4):
+            step = 64 * e
+            kn, vn = synth.step_kv(w, seed, 0, step, device="cuda")
+            q = synth.drift_query(w, seed, step, qe, device="cuda")
+            bufs = eng.alloc_step(w.B)
+            eng.decode_step(0, list(range(w.B)), q, bufs["blk_idx"], bufs["blk_cnt"],
+                            bufs["o_part"], bufs["lse_part"], bufs["o"], bufs["lse"],
+                            k_new=kn.view(w.B, w.Hkv, w.d).contiguous(),
+                            v_new=vn.view(w.B, w.Hkv, w.d).contiguous())
+            eng.sync()
+            gpu = {k: v.cpu().numpy() for k, v in bufs.items()}
+            N += 1
+            knb, vnb = synth.bits(kn), synth.bits(vn)
+            for b in range(w.B):
+                K_bits[b] = np.concatenate([K_bits[b], knb[b]], 0)
+                V_bits[b] = np.concatenate([V_bits[b], vnb[b]], 0)
+            log("  epoch %d N=%d" % (e, N))
+            st = harness.check_units(w, eng, 0, list(range(w.B)), synth.bits(q), K_bits,
+                                     V_bits, {b: N for b in range(w.B)}, gpu,
+                                     check_summ=(e == 0))
+            _check(st)
+    finally:
+        eng.close()
+
+
+def test_loop32_full_size_sampled():
+    """The loop workload at its per-layer size (B=16, N=65536, MAW beta=1),
+    two layer instances, three decode steps each with the one-launch step;
+    sampled units are followed in lockstep by the oracle, MAW included."""
+    w = _w(synth.loop32(), layers=2, steps=3)
+    log("case: loop32 full size, sampled units")
+    seed = 7
+    N0 = w.N - 1
+    sample = {(0, 0), (5, 3), (15, 7), (9, 1)}
+    seqs = sorted({s for s, _ in sample})
+    eng = harness.make_engine(w, w.N + 64, layers=w.layers)
+    try:
+        K_bits, V_bits, dirs_l, maw_state = {}, {}, {}, {}
+        for layer in range(w.layers):
+            dirs = synth.directions(w, seed, layer, 1, device="cuda")
+            K, V, _ = synth.prefill_with_directions(w, seed, layer, N0, dirs, device="cuda")
+            harness.prefill(eng, layer, K, V)
+            K_bits[layer] = {s: synth.bits(K[s]) for s in seqs}
+            V_bits[layer] = {s: synth.bits(V[s]) for s in seqs}
+            del K, V
+            dirs_l[layer] = dirs
+            maw_state[layer] = {}
+        torch.cuda.empty_cache()
+        N = N0
+        for step in range(w.steps):
+            N += 1
+            for layer in range(w.layers):
+                kn, vn = synth.step_kv(w, seed, layer, step, device="cuda")
+                q = synth.loop_query(w, seed, layer, step, dirs_l[layer], device="cuda")
+                bufs = eng.alloc_step(w.B)
+                eng.decode_step(layer, list(range(w.B)), q, bufs["blk_idx"], bufs["blk_cnt"],
+                                bufs["o_part"], bufs["lse_part"], bufs["o"], bufs["lse"],
+                                k_new=kn.view(w.B, w.Hkv, w.d).contiguous(),
+                                v_new=vn.view(w.B, w.Hkv, w.d).contiguous())
+                eng.sync()
+                gpu = {k: v.cpu().numpy() for k, v in bufs.items()}
+                knb, vnb = synth.bits(kn), synth.bits(vn)
+                for s in seqs:
+                    K_bits[layer][s] = np.concatenate([K_bits[layer][s], knb[s]], 0)
+                    V_bits[layer][s] = np.concatenate([V_bits[layer][s], vnb[s]], 0)
+                st = harness.check_units(w, eng, layer, list(range(w.B)), synth.bits(q),
+                                         K_bits[layer], V_bits[layer],
+                                         {s: N for s in range(w.B)}, gpu,
+                                         maw_state=maw_state[layer], units=sample,
+                                         check_summ=False)
+                log("  step %d layer %d N=%d" % (step, layer, N))
+                _check(st)
+                assert len(st["units"]) == len(sample)
+    finally:
+        eng.close()
