@@ -129,6 +129,10 @@ hipError_t launch_step(const Ctx &c, const SeqBatch &b, int max_blocks, int P, c
                        float *lse_part, int32_t p_cap, float *o, float *lse, uint32_t epoch,
                        int ptl_cap, hipStream_t st);
 
+// Workgroups of the one-launch step that can be resident on the device at
+// once (0 if unknown).
+int step_capacity(const Ctx &c, int max_blocks, int ptl_cap);
+
 // Fusion of the partials: with_maw = the P slots of the attend call and MAW
 // (layer call); otherwise every slot of p_cap is fused (layer -1).
 hipError_t launch_fuse(const Ctx &c, const SeqBatch &b, bool with_maw, int P,

@@ -1074,7 +1074,14 @@ __device__ __attribute__((always_inline)) bool topk_fast(const Ctx &c, int i, in
           if (r < n_tiles) cm += count_lanes((uint32_t)(e[r] >> 32) >= t);
         return cm;
       };
-      while (a < b && (double)key_to_float(b) - (double)key_to_float(a) > eps) {
+      // stop once [a, b] spans at most eps: keys of positive floats are
+      // linear in the value within a binade, so w keys below the first
+      // bracket's top span at most w * ulp(top) (any [a, b] holding the kk-th
+      // key is correct; a wider one only widens the band)
+      const double top = fabs((double)key_to_float(b));
+      const double ulp_top = top > 0.0 ? ldexp(1.0, __builtin_amdgcn_frexp_exp(top) - 24) : 1.0;
+      const uint32_t wk = (uint32_t)min(eps / ulp_top, 4.0e9);
+      while (a < b && b - a > wk) {
         const uint32_t mid = a + ((b - a) >> 1) + 1u;
         if (count_ge(mid) >= kk) a = mid; else b = mid - 1u;
       }
@@ -2113,6 +2120,22 @@ hipError_t launch_attend(const Ctx &c, const SeqBatch &b, int P, const uint16_t 
                  hipLaunchKernelGGL((k_attend<D_, G_>), dim3(grid), dim3(256), 0, st, c, b, P,
                                     q, blk_idx, blk_cnt, k_cap, o_part, lse_part, p_cap));
   return hipGetLastError();
+}
+
+int step_capacity(const Ctx &c, int max_blocks, int ptl_cap) {
+  size_t topk_bytes;
+  topk_lds(max_blocks, &topk_bytes);
+  int dev = 0, cus = 0, per_cu = 0;
+  if (hipGetDevice(&dev) != hipSuccess ||
+      hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess)
+    return 0;
+  hipError_t e = hipSuccess;
+  SD_DISPATCH_DG(c.dm.d, c.dm.G, {
+    const size_t att = ((sizeof(AttLds<D_, G_>) + 15) & ~size_t(15)) + sizeof(int32_t) * ptl_cap;
+    const size_t smem = std::max(std::max(att, sizeof(FuseSmem<G_>)), topk_bytes);
+    e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, k_step<D_, G_>, 256, smem);
+  });
+  return e == hipSuccess ? per_cu * cus : 0;
 }
 
 hipError_t launch_step(const Ctx &c, const SeqBatch &b, int max_blocks, int P, const uint16_t *q,

@@ -9,6 +9,7 @@
 #include <cstdarg>
 #include <cstdio>
 #include <cstring>
+#include <map>
 #include <new>
 #include <string>
 #include <vector>
@@ -46,6 +47,7 @@ struct sd_ctx {
   std::vector<int32_t> pend_seqs;
   int32_t pend_pcap = 0;
   std::vector<int> pend_parts;  // P of each launch of the attend call
+  std::map<int, int> capacity;  // resident step workgroups by max_blocks
   std::string err;
   std::vector<void *> dev_allocs;
 };
@@ -473,14 +475,23 @@ int64_t dense_pages(const sd_ctx *c, int64_t N) {
 }
 
 // Attention workgroups per unit of one launch: about kPartPages attended
-// pages each, for the unit with the most.
-int parts_of(const sd_ctx *c, const SeqBatch &b) {
+// pages each, for the unit with the most; fewer if the one-launch step would
+// otherwise not fit on the device at once (a part that starts late finishes
+// late).  The separate calls use the same P, so both give the same bits.
+int parts_of(sd_ctx *c, int layer, const SeqBatch &b, int max_blocks) {
   int64_t P = 1;
   for (int i = 0; i < b.n; ++i)
     for (int h = 0; h < c->Hkv; ++h) {
       const int64_t pages = dense_pages(c, b.len[i]) + k_of_seq(c, b.len[i], h) * (c->S[h] / kPage);
       P = std::max<int64_t>(P, cdiv(pages, kPartPages));
     }
+  auto it = c->capacity.find(max_blocks);
+  if (it == c->capacity.end())
+    it = c->capacity.emplace(max_blocks, step_capacity(kctx(c, layer), max_blocks,
+                                                       c->pps <= kPtLds ? c->pps : 0)).first;
+  const int units = c->Hkv * b.n;
+  const int tiles = std::max(1, (max_blocks + kScoreTile - 1) / kScoreTile);
+  if (it->second > 0) P = std::min<int64_t>(P, std::max(1, it->second / units - tiles));
   return (int)std::min<int64_t>(P, c->p_cap);
 }
 
@@ -550,8 +561,9 @@ sd_status sparse_attend(sd_ctx *c, int32_t layer, int32_t n_seqs,
   c->pend_parts.clear();
   for (int base = 0; base < n_seqs; base += kLaunchSeqs) {
     SeqBatch b;
-    fill_batch(c, layer, seq_ids, base, std::min(kLaunchSeqs, n_seqs - base), &b, nullptr);
-    const int P = parts_of(c, b);
+    int mb = 0;
+    fill_batch(c, layer, seq_ids, base, std::min(kLaunchSeqs, n_seqs - base), &b, &mb);
+    const int P = parts_of(c, layer, b, mb);
     c->pend_parts.push_back(P);
     SD_HIP(c, launch_attend(kc, b, P, q + (size_t)base * c->Hq * c->D,
                             blk_idx + (size_t)base * c->Hkv * k_cap,
@@ -648,7 +660,7 @@ sd_status sparse_decode_step(sd_ctx *c, int32_t layer, int32_t n_seqs,
     const int n = std::min(kLaunchSeqs, n_seqs - base);
     fill_batch(c, layer, seq_ids, base, n, &b, &mb);
     const uint16_t *qb = q + (size_t)base * c->Hq * c->D;
-    const int P = parts_of(c, b);
+    const int P = parts_of(c, layer, b, mb);
     int32_t *bi = blk_idx + (size_t)base * c->Hkv * k_cap;
     int32_t *bc = blk_cnt + (size_t)base * c->Hkv;
     float *op = o_part + (size_t)base * c->Hq * p_cap * c->D;
