@@ -354,11 +354,14 @@ __device__ __forceinline__ float key_to_float(uint32_t k) {
   return __uint_as_float(key_to_bits(k));
 }
 
-// fp32 error bound of an MFMA sum of n <= 256 products of bf16 values with
-// total magnitude E: 2 * gamma_256 * E (gamma_n = n u / (1 - n u),
-// u = 2^-24), plus one float rounding of the exact score.
+// fp32 error bound of the approximate score: partial sums of 64 products of
+// bf16 values (one chain of two MFMAs each, error <= gamma_64 times their
+// magnitude) added in fp32 (at most 4 partials: gamma_4), with total
+// magnitude E: 2 * (gamma_64 + gamma_4) * E (gamma_n = n u / (1 - n u),
+// u = 2^-24, and a factor 2 of margin), plus one float rounding of the exact
+// score.
 __device__ __forceinline__ float score_eps(float E, float A) {
-  return 3.1e-5f * E + 1.2e-7f * fabsf(A) + 1e-30f;
+  return 8.2e-6f * E + 1.2e-7f * fabsf(A) + 1e-30f;
 }
 
 // Exact score of one block for one query head: sum_c max(q_c m_c, q_c M_c)
@@ -529,16 +532,24 @@ __device__ __attribute__((always_inline)) void score_tile(const Ctx &c, int i, i
   int n_flag = 0;
 #pragma unroll
   for (int gi = 0; gi < GPW; ++gi) {
+    // partial sums over 64 (min, max) values (two chained MFMAs), added in
+    // fp32: a tighter error bound than one chain over all 2d values
     f32x4 acc = {0.f, 0.f, 0.f, 0.f}, acce = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-    for (int mm = 0; mm < MM; ++mm) {
-      const uint4 a = qa[mm], b = kf[gi][mm];
-      acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, a),
-                                                    __builtin_bit_cast(bf16x8, b), acc, 0, 0, 0);
-      const uint4 aa = make_uint4(a.x & absm, a.y & absm, a.z & absm, a.w & absm);
-      const uint4 ba = make_uint4(b.x & absm, b.y & absm, b.z & absm, b.w & absm);
-      acce = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, aa),
-                                                     __builtin_bit_cast(bf16x8, ba), acce, 0, 0, 0);
+    for (int m2 = 0; m2 < MM; m2 += 2) {
+      f32x4 pa = {0.f, 0.f, 0.f, 0.f}, pe = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int mm = m2; mm < m2 + 2; ++mm) {
+        const uint4 a = qa[mm], b = kf[gi][mm];
+        pa = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, a),
+                                                     __builtin_bit_cast(bf16x8, b), pa, 0, 0, 0);
+        const uint4 aa = make_uint4(a.x & absm, a.y & absm, a.z & absm, a.w & absm);
+        const uint4 ba = make_uint4(b.x & absm, b.y & absm, b.z & absm, b.w & absm);
+        pe = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, aa),
+                                                     __builtin_bit_cast(bf16x8, ba), pe, 0, 0, 0);
+      }
+      acc += pa;
+      acce += pe;
     }
     // lane (r16, lgrp) holds block r16 for heads 4*lgrp + jr
     float A = -INFINITY, E = 0.0f;
@@ -1112,7 +1123,12 @@ __device__ __attribute__((always_inline)) bool topk_fast(const Ctx &c, int i, in
   __syncthreads();
   if (!sm.ok) return false;
   const int n_unc = sm.nlist, kr2 = kk - sm.nin;
-  if (kr2 > 0) {
+  if (kr2 > 0 && kr2 == n_unc) {  // every band block is taken: no exact keys needed
+    if (wv == 0 && lane < n_unc) {
+      const int blk = sm.ulist[lane];
+      atomicOr(&sm.bm[blk >> 6], 1ull << (blk & 63));
+    }
+  } else if (kr2 > 0) {
     // exact keys of the band, one lane quad per (block, head), in passes of 64
     for (int p0 = 0; p0 < n_unc * G; p0 += 64) {
       const int pair = p0 + (tid >> 2);
