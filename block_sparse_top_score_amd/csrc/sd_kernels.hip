@@ -1006,22 +1006,63 @@ __device__ __attribute__((always_inline)) void topk_unit(const Ctx &c, int i, in
   }
 }
 
+// Value of lane ^ J within the wave (J = 1, 2, 4, 8 by DPP inside 16-lane
+// rows; 16 and 32 through ds_bpermute).
+template <int J>
+__device__ __forceinline__ uint32_t lane_xor(uint32_t v) {
+  if constexpr (J == 1) {
+    return (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0xB1, 0xF, 0xF, false);  // quad_perm [1,0,3,2]
+  } else if constexpr (J == 2) {
+    return (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x4E, 0xF, 0xF, false);  // quad_perm [2,3,0,1]
+  } else if constexpr (J == 4) {
+    // row_ror:n gives lane l the value of lane l - n (mod 16)
+    const uint32_t lo = (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x124, 0xF, 0xF, false);  // row_ror:4
+    const uint32_t hi = (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x12C, 0xF, 0xF, false);  // row_ror:12
+    return (threadIdx.x & 4) ? lo : hi;
+  } else if constexpr (J == 8) {
+    return (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x128, 0xF, 0xF, false);  // row_ror:8
+  } else {
+    return (uint32_t)__shfl_xor((int)v, J, 64);
+  }
+}
+template <int J>
+__device__ __forceinline__ unsigned long long half_clean(unsigned long long v) {
+  const unsigned long long o =
+      ((unsigned long long)lane_xor<J>((uint32_t)(v >> 32)) << 32) | lane_xor<J>((uint32_t)v);
+  return (threadIdx.x & J) == 0 ? (v > o ? v : o) : (v < o ? v : o);
+}
+// The 64 largest of two descending lists of 64 keys (one per lane), in
+// descending order: max(a, b reversed) is bitonic and holds them; a cascade of
+// half-cleaners sorts it.
+__device__ __forceinline__ unsigned long long merge_top64(unsigned long long a, unsigned long long b) {
+  const int rev = 63 - (int)(threadIdx.x & 63);
+  const unsigned long long br = ((unsigned long long)(uint32_t)__shfl((int)(uint32_t)(b >> 32), rev, 64) << 32) |
+                                (uint32_t)__shfl((int)(uint32_t)b, rev, 64);
+  unsigned long long v = a > br ? a : br;
+  v = half_clean<32>(v);
+  v = half_clean<16>(v);
+  v = half_clean<8>(v);
+  v = half_clean<4>(v);
+  v = half_clean<2>(v);
+  v = half_clean<1>(v);
+  return v;
+}
+
 // Fast top-k of one unit from the score tiles' lists (no MAW flags, kk <=
 // kTileList; every thread of the workgroup calls it and gets the same
 // result).  The steps of topk_unit run on the listed keys, which hold the
 // unit's top kk:
-//   1. bisection, inside the bracket [max over tiles of the kk-th listed key,
-//      max over tiles of the ceil(kk / tiles)-th] (some tile holds that many
-//      of the top kk), narrows [a, b] around the kk-th largest approximate
-//      key T to within the unit's error bound eps;
-//   2. band: keys above b + 2 eps are in, below a - 2 eps out; the blocks in
-//      between are re-scored exactly by the four waves, one lane quad per
-//      (block, head);
+//   1. the lists, each descending, are merged pairwise keeping the 64
+//      largest keys (bitonic half-cleaners; DPP and ds_bpermute exchanges),
+//      which gives the kk-th largest approximate key T;
+//   2. band: keys above T + 2 eps are in, below T - 2 eps out (eps: the
+//      unit's error bound); the blocks in between are re-scored exactly by
+//      the four waves, one lane quad per (block, head);
 //   3. the kk - (blocks in) best of them by (exact key desc, index asc);
 //   4. each chosen block is written at its place in ascending block order,
 //      read off an LDS bitmap of the chosen blocks.
 // Returns false, before writing anything, when a tile overflowed its list or
-// the band holds more than kTileList blocks; the caller then runs topk_unit.
+// the band reaches past the 64 largest keys; the caller then runs topk_unit.
 template <int D, int G>
 __device__ __attribute__((always_inline)) bool topk_fast(const Ctx &c, int i, int seq, int h,
                                                          const HeadInfo &hi, const UG &g,
@@ -1069,50 +1110,30 @@ __device__ __attribute__((always_inline)) bool topk_fast(const Ctx &c, int i, in
       auto key_of = [&](int r, int l) {  // listed key r, l (uniform)
         return (uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)(e[r] >> 32), l);
       };
-      const int cb = cdiv(kk, n_tiles);
-      uint32_t a = 0u, b = 0u;
+      // the 64 largest listed keys, descending: pairwise merges of the lists
 #pragma unroll
-      for (int r = 0; r < kFastTiles; ++r)
-        if (r < n_tiles) {
-          a = max(a, key_of(r, kk - 1));
-          b = max(b, key_of(r, cb - 1));
-        }
-      a = max(a, 2u);
-      auto count_ge = [&](uint32_t t) {
-        int cm = 0;
+      for (int w = 1; w < kFastTiles; w <<= 1)
 #pragma unroll
-        for (int r = 0; r < kFastTiles; ++r)
-          if (r < n_tiles) cm += count_lanes((uint32_t)(e[r] >> 32) >= t);
-        return cm;
-      };
-      // stop once [a, b] spans at most eps: keys of positive floats are
-      // linear in the value within a binade, so w keys below the first
-      // bracket's top span at most w * ulp(top) (any [a, b] holding the kk-th
-      // key is correct; a wider one only widens the band)
-      const double top = fabs((double)key_to_float(b));
-      const double ulp_top = top > 0.0 ? ldexp(1.0, __builtin_amdgcn_frexp_exp(top) - 24) : 1.0;
-      const uint32_t wk = (uint32_t)min(eps / ulp_top, 4.0e9);
-      while (a < b && b - a > wk) {
-        const uint32_t mid = a + ((b - a) >> 1) + 1u;
-        if (count_ge(mid) >= kk) a = mid; else b = mid - 1u;
-      }
-      const uint32_t kb_hi = order_key(__double2float_rd((double)key_to_float(b) + 2.0 * eps));
-      const uint32_t kb_lo = order_key(__double2float_ru((double)key_to_float(a) - 2.0 * eps));
-#pragma unroll
-      for (int r = 0; r < kFastTiles; ++r) {
-        if (r >= n_tiles) break;
-        const uint32_t kx = (uint32_t)(e[r] >> 32);
-        const int blk = (int)~(uint32_t)e[r];
-        const bool in = kx >= 2u && kx > kb_hi;
-        const bool unc = kx >= 2u && kx >= kb_lo && kx <= kb_hi;
-        if (in) atomicOr(&sm.bm[blk >> 6], 1ull << (blk & 63));
-        const unsigned long long mu = __ballot(unc);
-        const int pos = n_unc + lanes_below(mu);
-        if (unc && pos < kTileList) sm.ulist[pos] = blk;
-        n_unc += __popcll(mu);
-        n_in += count_lanes(in);
-      }
-      ok = n_unc <= kTileList && n_in <= kk && n_in + n_unc >= kk;
+        for (int r = 0; r + w < kFastTiles; r += 2 * w)
+          if (r + w < n_tiles) e[r] = merge_top64(e[r], e[r + w]);
+      const unsigned long long m = e[0];
+      const uint32_t kx = (uint32_t)(m >> 32);
+      const uint32_t T = (uint32_t)__builtin_amdgcn_readlane((int)kx, kk - 1);
+      const uint32_t kb_hi = order_key(__double2float_rd((double)key_to_float(T) + 2.0 * eps));
+      const uint32_t kb_lo = order_key(__double2float_ru((double)key_to_float(T) - 2.0 * eps));
+      // a band reaching below the 64 kept keys could miss blocks
+      const uint32_t k63 = (uint32_t)__builtin_amdgcn_readlane((int)kx, 63);
+      const bool whole = k63 < 2u || k63 < kb_lo;
+      const int blk = (int)~(uint32_t)m;
+      const bool in = kx >= 2u && kx > kb_hi;
+      const bool unc = kx >= 2u && kx >= kb_lo && kx <= kb_hi;
+      if (in) atomicOr(&sm.bm[blk >> 6], 1ull << (blk & 63));
+      const unsigned long long mu = __ballot(unc);
+      if (unc) sm.ulist[lanes_below(mu)] = blk;
+      n_unc = __popcll(mu);
+      n_in = count_lanes(in);
+      ok = whole;
+      ok = ok && n_in <= kk && n_in + n_unc >= kk;
     }
     if (lane == 0) {
       sm.ok = ok;
