@@ -1973,8 +1973,11 @@ __global__ __launch_bounds__(256, 2) void k_step(Ctx c, SeqBatch b, int tiles_x,
   const bool score = wg < n_score;
   int idx, u;
   if (score) {
-    idx = wg % tiles_x;
-    u = wg / tiles_x;
+    // tile-major: consecutive workgroups (spread over the CUs first) are
+    // different units' tiles of the same index, so the summary loads spread
+    // evenly and the short last tiles of units are the ones dispatched last
+    idx = wg / units;
+    u = wg % units;
   } else {
     wg -= n_score;
     idx = wg / units;  // part-major
