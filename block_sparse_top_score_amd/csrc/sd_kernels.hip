@@ -48,6 +48,13 @@ __device__ __forceinline__ float bf16_hi(uint32_t w) {
   return __uint_as_float(w & 0xffff0000u);
 }
 __device__ __forceinline__ int cdiv(int a, int b) { return (a + b - 1) / b; }
+// x / m for x >= 0 and m in {1, 2, 3, 4} (pages per block): a shift, or a
+// multiply-high by ceil(2^33 / 3) for m = 3 (exact for every 32-bit x).
+__device__ __forceinline__ int div_m(int x, int m) {
+  return m == 3 ? (int)(__umulhi((uint32_t)x, 0xAAAAAAABu) >> 1) : (int)((uint32_t)x >> (m >> 1));
+}
+// x / S for x >= 0 and a block size S = 16 m.
+__device__ __forceinline__ int div_S(int x, int S) { return div_m((int)((uint32_t)x >> 4), S >> 4); }
 
 // Data that one workgroup publishes to the last-arriving workgroup of the same
 // unit inside one launch is written and read with relaxed device-scope atomic
@@ -124,17 +131,17 @@ __device__ __forceinline__ UG unit_geom(int N, const HeadInfo &hi, const Dims &d
   const int S = hi.S;
   g.N = N;
   g.S = S;
-  g.n_blk = cdiv(N, S);
+  g.n_blk = div_S(N + S - 1, S);
   g.ns = min(dm.n_sink, N);
   g.wlo = max(0, N - dm.window);
-  g.hb = cdiv(g.ns, S);
-  g.tb = (dm.window > 0 && N > 0) ? g.wlo / S : g.n_blk;
+  g.hb = div_S(g.ns + S - 1, S);
+  g.tb = (dm.window > 0 && N > 0) ? div_S(g.wlo, S) : g.n_blk;
   if (g.hb >= g.tb) {  // every block touches D
     g.hb = g.n_blk;
     g.tb = g.n_blk;
   }
   g.n_dt = g.hb + (g.n_blk - g.tb);
-  const int n_cand = g.ns < g.wlo ? cdiv(g.wlo, S) - g.ns / S : 0;
+  const int n_cand = g.ns < g.wlo ? div_S(g.wlo + S - 1, S) - div_S(g.ns, S) : 0;
   g.kk = min(n_cand, budget_blocks(hi.ppm, N, S));
   return g;
 }
@@ -472,9 +479,9 @@ __device__ __forceinline__ void tile_list(const Ctx &c, int seq, int h, const UG
 // fusion then adds (1-r)*a to the attended blocks only).  publish: also write
 // the tile's candidate list for the fast top-k (tile < kFastTiles).
 template <int D, int G>
-__device__ __attribute__((always_inline)) void score_tile(const Ctx &c, int i, int seq, int h, const HeadInfo &hi,
-                           const UG &g, int tile, const uint16_t *__restrict__ q,
-                           TopkSmem &sm, bool decay_maw, bool publish) {
+__device__ __attribute__((always_inline)) bool score_tile(const Ctx &c, int i, int seq, int h, const HeadInfo &hi,
+                           int N, int n_blk, int tile, const uint16_t *__restrict__ q,
+                           TopkSmem &sm, bool decay_maw, bool fast_ok, UG &g) {
   uint32_t *red = sm.red;
   constexpr int MM = D / 16;    // MFMAs per 16 blocks (k = 2d values, 32 per MFMA)
   constexpr int GPW = kScoreTile / 64;  // 16-block groups per wave
@@ -484,10 +491,11 @@ __device__ __attribute__((always_inline)) void score_tile(const Ctx &c, int i, i
   const int base = tile * kScoreTile + wv * 16 * GPW;
   const uint4 *sp = reinterpret_cast<const uint4 *>(c.L.summ + hi.summ_off +
                                                     (size_t)seq * C4 * hi.nbmax * 8);
-  // every load of the tile is issued before any is used (block indices are
-  // clamped, so the loads of a wave past the last block stay in bounds)
+  // every load of the tile is issued first, before any is used and before
+  // the rest of the unit's geometry is worked out (block indices are clamped,
+  // so the loads of a wave past the last block stay in bounds)
   uint4 kf[GPW][MM];
-  const int nb_last = max(g.n_blk - 1, 0);
+  const int nb_last = max(n_blk - 1, 0);
 #pragma unroll
   for (int gi = 0; gi < GPW; ++gi) {
     const int blk = min(base + gi * 16 + r16, nb_last);
@@ -507,9 +515,11 @@ __device__ __attribute__((always_inline)) void score_tile(const Ctx &c, int i, i
 #pragma unroll
   for (int gi = 0; gi < GPW; ++gi) {
     const int blk = base + gi * 16 + r16;
-    mwv[gi] = (need_maw && lgrp == 0 && blk < g.n_blk) ? mwp[blk] : 0.0f;
+    mwv[gi] = (need_maw && lgrp == 0 && blk < n_blk) ? mwp[blk] : 0.0f;
   }
   __builtin_amdgcn_sched_barrier(0);
+  g = unit_geom(N, hi, c.dm);
+  const bool publish = fast_ok && g.kk <= kTileList;
   // A operand: lane = head r16 (zero rows past G), channel quad 4*mm + lgrp,
   // pairs (q-, q+) matching the (min, max) pairs of the summaries
   uint4 qa[MM];
@@ -603,6 +613,7 @@ __device__ __attribute__((always_inline)) void score_tile(const Ctx &c, int i, i
     const double eps_t = (double)__uint_as_float(max(max(red[0], red[1]), max(red[2], red[3])));
     tile_list(c, seq, h, g, tile, eps_t, sm);
   }
+  return publish;
 }
 
 template <int D>
@@ -822,7 +833,7 @@ __device__ __attribute__((always_inline)) void topk_unit(const Ctx &c, int i, in
     const double eps = (double)__uint_as_float(eps_bits);
     uint32_t a = wave_min_u(lo), b = wave_max_u(hi_k);
     // invariant: #words >= a is cnt_a >= k_sub, #words > b is cnt_b1 < k_sub
-    const int n_cand = g.ns < g.wlo ? cdiv(g.wlo, g.S) - g.ns / g.S : 0;
+    const int n_cand = g.ns < g.wlo ? div_S(g.wlo + g.S - 1, g.S) - div_S(g.ns, g.S) : 0;
     int cnt_a = take_flagged ? n_cand - F : F, cnt_b1 = 0;
     // lower bound on T_a: the k_sub-th largest of the maxima of the row
     // groups (r mod NG; distinct blocks' keys), when there are enough of them
@@ -1107,9 +1118,6 @@ __device__ __attribute__((always_inline)) bool topk_fast(const Ctx &c, int i, in
     __builtin_amdgcn_wave_barrier();
     if (ok && kk > 0) {
       const double eps = (double)__uint_as_float(eps_bits);
-      auto key_of = [&](int r, int l) {  // listed key r, l (uniform)
-        return (uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)(e[r] >> 32), l);
-      };
       // the 64 largest listed keys, descending: pairwise merges of the lists
 #pragma unroll
       for (int w = 1; w < kFastTiles; w <<= 1)
@@ -1562,7 +1570,7 @@ __device__ __attribute__((always_inline)) void attend_part(const Ctx &c, int i, 
     wave_pages<D, G>(
         c, h, gw, NW, cnt * PPB,
         [&](int t, int &pg, int &mk, int &sl) {
-          const int j = t / PPB, pp = t - j * PPB;
+          const int j = div_m(t, PPB), pp = t - j * PPB;
           int blk;
           if (si.tag) {  // published before the count; the tag confirms it
             unsigned long long e = ld_dev(&si.tag[j]);
@@ -1899,11 +1907,12 @@ __global__ __launch_bounds__(256) void k_select(Ctx c, SeqBatch b, int tiles_x,
   const int wg = blockIdx.x;
   const int tile = wg % tiles_x, h = (wg / tiles_x) % c.dm.Hkv, i = wg / (tiles_x * c.dm.Hkv);
   const HeadInfo hi = c.heads[h];
-  const int seq = b.seq[i];
-  const UG g = unit_geom(b.len[i], hi, c.dm);
-  const int n_tiles = max(1, cdiv(g.n_blk, kScoreTile));
+  const int seq = b.seq[i], N = b.len[i];
+  const int n_blk = div_S(N + hi.S - 1, hi.S);
+  const int n_tiles = max(1, cdiv(n_blk, kScoreTile));
   if (tile >= n_tiles) return;
-  score_tile<D, G>(c, i, seq, h, hi, g, tile, q, smem_topk, false, false);
+  UG g;
+  score_tile<D, G>(c, i, seq, h, hi, N, n_blk, tile, q, smem_topk, false, false, g);
   uint32_t *ctr = &c.sc.arrive[((size_t)seq * c.dm.Hkv + h) * 2];
   if (!arrive_last(ctr, (unsigned)n_tiles, &smem_topk.last)) return;
   uint32_t *lrows = reinterpret_cast<uint32_t *>(smem_raw + sizeof(TopkSmem));
@@ -1967,36 +1976,29 @@ __global__ __launch_bounds__(256, 2) void k_step(Ctx c, SeqBatch b, int tiles_x,
   TopkSmem &smem_topk = *reinterpret_cast<TopkSmem *>(smem_raw);
   AttLds<D, G> &smem_att = *reinterpret_cast<AttLds<D, G> *>(smem_raw);
   FuseSmem<G> &smem_fuse = *reinterpret_cast<FuseSmem<G> *>(smem_raw);
-  const int units = c.dm.Hkv * b.n;
-  const int n_score = tiles_x * units;
-  int wg = blockIdx.x;
-  const bool score = wg < n_score;
-  int idx, u;
-  if (score) {
-    // tile-major: consecutive workgroups (spread over the CUs first) are
-    // different units' tiles of the same index, so the summary loads spread
-    // evenly and the short last tiles of units are the ones dispatched last
-    idx = wg / units;
-    u = wg % units;
-  } else {
-    wg -= n_score;
-    idx = wg / units;  // part-major
-    u = wg % units;
-  }
-  const int h = u % c.dm.Hkv, i = u / c.dm.Hkv;
+  // grid (KV head, sequence, role index): workgroups are dispatched with
+  // blockIdx.x fastest, so the flat order is role-major.  Score tiles come
+  // first, tile-major: consecutive workgroups (spread over the CUs first) are
+  // different units' tiles of the same index, so the summary loads spread
+  // evenly and the short last tiles of units are dispatched last.  The
+  // attention parts follow, part-major.
+  const int h = blockIdx.x, i = blockIdx.y;
+  const bool score = (int)blockIdx.z < tiles_x;
+  const int idx = score ? (int)blockIdx.z : (int)blockIdx.z - tiles_x;
   const HeadInfo hi = c.heads[h];
-  const int seq = b.seq[i];
-  const UG g = unit_geom(b.len[i], hi, c.dm);
+  const int seq = b.seq[i], N = b.len[i];
   const size_t unit = (size_t)seq * c.dm.Hkv + h;
   if (score) {
-    const int n_tiles = max(1, cdiv(g.n_blk, kScoreTile));
+    const int n_blk = div_S(N + hi.S - 1, hi.S);
+    const int n_tiles = max(1, cdiv(n_blk, kScoreTile));
     if (idx >= n_tiles) return;
     // the score tiles, the top-k and the fusion are on every unit's critical
     // path: their waves get issue priority over the attention parts'
     __builtin_amdgcn_s_setprio(2);
     // without MAW flags each tile also lists its candidates for the fast top-k
-    const bool fast = c.dm.maw_beta <= 0.0f && n_tiles <= kFastTiles && g.kk <= kTileList;
-    score_tile<D, G>(c, i, seq, h, hi, g, idx, q, smem_topk, true, fast);
+    UG g;
+    const bool fast = score_tile<D, G>(c, i, seq, h, hi, N, n_blk, idx, q, smem_topk, true,
+                                       c.dm.maw_beta <= 0.0f && n_tiles <= kFastTiles, g);
     uint32_t *ctr = &c.sc.arrive[unit * 2];
     if (!arrive_last(ctr, (unsigned)n_tiles, &s_flag)) return;
     __builtin_amdgcn_s_setprio(3);
@@ -2015,7 +2017,8 @@ __global__ __launch_bounds__(256, 2) void k_step(Ctx c, SeqBatch b, int tiles_x,
     }
     return;
   }
-  // attention part idx of unit u; the sequence's page table is copied to LDS
+  const UG g = unit_geom(N, hi, c.dm);
+  // attention part idx of the unit; the sequence's page table is copied to LDS
   // (one batch of loads) for the selected pages
   const int32_t *ptl = nullptr;
   const int np = cdiv(g.N, kPage);
@@ -2185,15 +2188,14 @@ hipError_t launch_step(const Ctx &c, const SeqBatch &b, int max_blocks, int P, c
   if (b.n <= 0) return hipSuccess;
   if (P < 1 || P > p_cap) return hipErrorInvalidValue;
   const int tiles_x = max(1, (max_blocks + kScoreTile - 1) / kScoreTile);
-  const int units = c.dm.Hkv * b.n;
-  const int grid = (tiles_x + P) * units;
+  const dim3 grid(c.dm.Hkv, b.n, tiles_x + P);
   size_t topk_bytes;
   const int lrows_words = topk_lds(max_blocks, &topk_bytes);
   if (topk_bytes > 65536) return hipErrorInvalidValue;
   SD_DISPATCH_DG(c.dm.d, c.dm.G, {
     const size_t att = ((sizeof(AttLds<D_, G_>) + 15) & ~size_t(15)) + sizeof(int32_t) * ptl_cap;
     const size_t smem = std::max(std::max(att, sizeof(FuseSmem<G_>)), topk_bytes);
-    hipLaunchKernelGGL((k_step<D_, G_>), dim3(grid), dim3(256), smem, st, c, b, tiles_x, P,
+    hipLaunchKernelGGL((k_step<D_, G_>), grid, dim3(256), smem, st, c, b, tiles_x, P,
                        blk_idx, blk_cnt, k_cap, q, o_part, lse_part, p_cap, o, lse, lrows_words,
                        epoch, ptl_cap);
   });
