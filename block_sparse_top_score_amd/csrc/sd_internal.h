@@ -87,9 +87,8 @@ struct Scratch {
   int32_t *usel;     // [max_seqs][Hkv][kcap] selected block ids (attend copy)
   int32_t *ucnt;     // [max_seqs][Hkv] selected block count (attend copy)
   uint32_t *arrive;  // [max_seqs][Hkv][2] last-arriver counters (kept at 0)
-  unsigned long long *cand;  // [max_seqs][Hkv][key_stride] per-tile candidate lists
-                             // (key << 32 | block), tile t's at [t*kScoreTile, ...)
-  uint32_t *tcnt;    // [max_seqs][Hkv][kFastTiles] entries of each tile's list
+  unsigned long long *cand;  // [max_seqs][Hkv][key_stride] per-tile lists of the 64
+                             // largest keys (key << 32 | ~block), tile t's at [64 t, 64 t + 64)
   unsigned long long *rtag;    // [max_seqs][Hkv] step << 32 | selected count, published
                                // after the selection
   unsigned long long *seltag;  // [max_seqs][Hkv][kcap] step << 32 | block of the selection

@@ -173,8 +173,7 @@ struct TopkSmem {
   uint32_t tk[kScoreTile];  // keys of a score tile (fast top-k)
   double ue[kTileList * SD_MAX_GROUP];  // exact scores of the fast top-k's band, per head
   unsigned long long bm[kFastTiles * kScoreTile / 64];  // chosen blocks (fast top-k)
-  unsigned long long srt[kFastTiles][kTileList];  // sorted lists (tile; fast top-k)
-  int rk[4][kTileList];  // partial ranks of a tile's list
+  unsigned long long srt[4][kTileList];  // the waves' sorted keys (tile list)
   float qs[SD_MAX_GROUP * 128];
   double ud[16];
   uint32_t red[8];
@@ -380,98 +379,105 @@ __device__ __forceinline__ float score_eps(float E, float A) {
 __device__ __forceinline__ float upper_term(float qv, uint32_t mm) {
   return qv >= 0.0f ? bf16_hi(mm) : bf16_lo(mm);
 }
+// Lane exchanges, bitonic sorting and merging of 64 keys held one per lane
+// (key = order key << 32 | ~block: unique, so no ties).
+template <int J>
+__device__ __forceinline__ uint32_t lane_xor(uint32_t v) {
+  if constexpr (J == 1) {
+    return (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0xB1, 0xF, 0xF, false);  // quad_perm [1,0,3,2]
+  } else if constexpr (J == 2) {
+    return (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x4E, 0xF, 0xF, false);  // quad_perm [2,3,0,1]
+  } else if constexpr (J == 4) {
+    // row_ror:n gives lane l the value of lane l - n (mod 16)
+    const uint32_t lo = (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x124, 0xF, 0xF, false);  // row_ror:4
+    const uint32_t hi = (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x12C, 0xF, 0xF, false);  // row_ror:12
+    return (threadIdx.x & 4) ? lo : hi;
+  } else if constexpr (J == 8) {
+    return (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x128, 0xF, 0xF, false);  // row_ror:8
+  } else {
+    return (uint32_t)__shfl_xor((int)v, J, 64);
+  }
+}
+template <int J>
+__device__ __forceinline__ unsigned long long half_clean(unsigned long long v) {
+  const unsigned long long o =
+      ((unsigned long long)lane_xor<J>((uint32_t)(v >> 32)) << 32) | lane_xor<J>((uint32_t)v);
+  return (threadIdx.x & J) == 0 ? (v > o ? v : o) : (v < o ? v : o);
+}
+// The 64 largest of two descending lists of 64 keys (one per lane), in
+// descending order: max(a, b reversed) is bitonic and holds them; a cascade of
+// half-cleaners sorts it.
+__device__ __forceinline__ unsigned long long merge_top64(unsigned long long a, unsigned long long b) {
+  const int rev = 63 - (int)(threadIdx.x & 63);
+  const unsigned long long br = ((unsigned long long)(uint32_t)__shfl((int)(uint32_t)(b >> 32), rev, 64) << 32) |
+                                (uint32_t)__shfl((int)(uint32_t)b, rev, 64);
+  unsigned long long v = a > br ? a : br;
+  v = half_clean<32>(v);
+  v = half_clean<16>(v);
+  v = half_clean<8>(v);
+  v = half_clean<4>(v);
+  v = half_clean<2>(v);
+  v = half_clean<1>(v);
+  return v;
+}
+// One compare-exchange step of a bitonic sort into descending order: lane l
+// and lane l ^ J compare; in a run of K lanes sorted descending (l & K = 0)
+// the lower lane keeps the larger key, in an ascending run the smaller.
+template <int K, int J>
+__device__ __forceinline__ unsigned long long bitonic_step(unsigned long long v) {
+  const unsigned long long o =
+      ((unsigned long long)lane_xor<J>((uint32_t)(v >> 32)) << 32) | lane_xor<J>((uint32_t)v);
+  const int l = threadIdx.x & 63;
+  const bool keep_max = ((l & J) == 0) == ((l & K) == 0);
+  return keep_max ? (v > o ? v : o) : (v < o ? v : o);
+}
+__device__ __forceinline__ unsigned long long sort64_desc(unsigned long long v) {
+  v = bitonic_step<2, 1>(v);
+  v = bitonic_step<4, 2>(v);
+  v = bitonic_step<4, 1>(v);
+  v = bitonic_step<8, 4>(v);
+  v = bitonic_step<8, 2>(v);
+  v = bitonic_step<8, 1>(v);
+  v = bitonic_step<16, 8>(v);
+  v = bitonic_step<16, 4>(v);
+  v = bitonic_step<16, 2>(v);
+  v = bitonic_step<16, 1>(v);
+  v = bitonic_step<32, 16>(v);
+  v = bitonic_step<32, 8>(v);
+  v = bitonic_step<32, 4>(v);
+  v = bitonic_step<32, 2>(v);
+  v = bitonic_step<32, 1>(v);
+  v = half_clean<32>(v);  // the final merge: a descending run of 64
+  v = half_clean<16>(v);
+  v = half_clean<8>(v);
+  v = half_clean<4>(v);
+  v = half_clean<2>(v);
+  v = half_clean<1>(v);
+  return v;
+}
+
 // List of one score tile for the fast top-k (no MAW flags, kk <= kTileList):
-// the blocks whose approximate score can still reach the unit's top kk, as
-// keys (approximate order key << 32 | ~block), descending, padded with
-// zeros.  Wave 0 bounds the tile's kk-th largest approximate key L from below
-// by a few bisection steps (a <= L, count(>= a) >= kk).  A block with A <
-// a - 2 eps_t has kk blocks in its own tile whose exact scores are larger
-// (each at least a - eps_t > A + eps_t), so only blocks with A >= a - 2 eps_t
-// are listed, at most kTileList.  The four waves rank the keys and wave 0
-// publishes them in order.  A tile that would list more publishes the count
-// kTileOverflow (the top-k then takes the full path).  Every thread of the
-// workgroup calls it, after the tile's keys are in sm.tk.
-constexpr int kTileSteps = 12;
-constexpr uint32_t kTileOverflow = 0xffffffffu;
-__device__ __forceinline__ void tile_list(const Ctx &c, int seq, int h, const UG &g, int tile,
-                                          double eps_t, TopkSmem &sm) {
-  const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
-  constexpr int TR = kScoreTile / 64;
+// the tile's 64 largest approximate keys, descending.  Blocks past the end of
+// the unit and blocks that are not candidates have order key 0 and sort
+// last.  Every block among the unit's 64 largest keys is among its own
+// tile's 64 largest, so merging the tiles' lists gives the unit's 64 largest.
+// Each wave sorts its 64 keys across its lanes; wave 0 merges the four
+// sorted lists and publishes the result.  Every thread of the workgroup calls
+// it, after a barrier that follows the tile's keys' writes to sm.tk.
+__device__ __forceinline__ void tile_list(const Ctx &c, int seq, int h, int tile, TopkSmem &sm) {
+  const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
   const size_t unit = (size_t)seq * c.dm.Hkv + h;
-  const int kk = g.kk;
-  if (wv == 0) {
-    uint32_t x[TR], lo = 0xffffffffu, hi_k = 0u;
-    int ct = 0;
-#pragma unroll
-    for (int r = 0; r < TR; ++r) {
-      x[r] = sm.tk[r * 64 + lane];
-      if (x[r] >= 2u) {
-        lo = min(lo, x[r]);
-        hi_k = max(hi_k, x[r]);
-      }
-      ct += count_lanes(x[r] >= 2u);
-    }
-    uint32_t dmin = 2u;  // keys below dmin are not listed
-    if (kk > 0 && ct > kk) {
-      uint32_t a = wave_min_u(lo), b = wave_max_u(hi_k);
-      int ca = ct;  // count(>= a)
-      for (int it = 0; it < kTileSteps && a < b && ca > kTileList - 8; ++it) {
-        const uint32_t mid = a + ((b - a) >> 1) + 1u;
-        int cm = 0;
-#pragma unroll
-        for (int r = 0; r < TR; ++r) cm += count_lanes(x[r] >= mid);
-        if (cm >= kk) {
-          a = mid;
-          ca = cm;
-        } else {
-          b = mid - 1u;
-        }
-      }
-      dmin = max(2u, order_key(__double2float_ru((double)key_to_float(a) - 2.0 * eps_t)));
-    }
-    int n = 0;
-#pragma unroll
-    for (int r = 0; r < TR; ++r) {
-      const bool in = kk > 0 && x[r] >= dmin;
-      const unsigned long long m = __ballot(in);
-      const int pos = n + lanes_below(m);
-      if (in && pos < kTileList)
-        sm.srt[0][pos] = ((unsigned long long)x[r] << 32) |
-                         (uint32_t)~(uint32_t)(tile * kScoreTile + r * 64 + lane);
-      n += __popcll(m);
-    }
-    if (lane == 0) sm.nlist = n;
-  }
-  __syncthreads();
-  const int n = sm.nlist;
-  unsigned long long *dst = c.sc.cand + unit * c.dm.key_stride + (size_t)tile * kTileList;
-  if (n > kTileList) {
-    if (tid == 0) st_dev(&c.sc.tcnt[unit * kFastTiles + tile], kTileOverflow);
-    return;
-  }
-  // rank of each listed key: each wave counts the larger keys among 16 of them
-  const unsigned long long key = lane < n ? sm.srt[0][lane] : 0ull;
-  int rk = 0;
-#pragma unroll
-  for (int t = 0; t < 16; ++t) {
-    const int src = 16 * wv + t;
-    const unsigned long long o =
-        ((unsigned long long)(uint32_t)__builtin_amdgcn_readlane((int)(key >> 32), src) << 32) |
-        (uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)key, src);
-    rk += o > key ? 1 : 0;
-  }
-  sm.rk[wv][lane] = rk;
+  const int b = wv * 64 + lane;  // block tile * kScoreTile + b
+  unsigned long long v =
+      ((unsigned long long)sm.tk[b] << 32) | (uint32_t)~(uint32_t)(tile * kScoreTile + b);
+  v = sort64_desc(v);
+  if (wv > 0) sm.srt[wv][lane] = v;
   __syncthreads();
   if (wv == 0) {
-    // entries past n are zeros; they keep their own places (every listed key
-    // is larger, so listed ranks are below n)
-    const int pos = lane < n ? sm.rk[0][lane] + sm.rk[1][lane] + sm.rk[2][lane] + sm.rk[3][lane]
-                             : lane;
-    sm.srt[1][pos] = key;
-    __builtin_amdgcn_s_waitcnt(0xc07f);
-    __builtin_amdgcn_wave_barrier();
-    st_dev(&dst[lane], sm.srt[1][lane]);
-    if (lane == 0) st_dev(&c.sc.tcnt[unit * kFastTiles + tile], (uint32_t)n);
+    const unsigned long long m01 = merge_top64(v, sm.srt[1][lane]);
+    const unsigned long long m23 = merge_top64(sm.srt[2][lane], sm.srt[3][lane]);
+    st_dev(&c.sc.cand[unit * c.dm.key_stride + (size_t)tile * kTileList + lane],
+           merge_top64(m01, m23));
   }
 }
 
@@ -609,10 +615,7 @@ __device__ __attribute__((always_inline)) bool score_tile(const Ctx &c, int i, i
     const uint32_t f = red[4] + red[5] + red[6] + red[7];
     if (f) __hip_atomic_fetch_add(acc + 1, f, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
   }
-  if (publish) {
-    const double eps_t = (double)__uint_as_float(max(max(red[0], red[1]), max(red[2], red[3])));
-    tile_list(c, seq, h, g, tile, eps_t, sm);
-  }
+  if (publish) tile_list(c, seq, h, tile, sm);
   return publish;
 }
 
@@ -1019,46 +1022,6 @@ __device__ __attribute__((always_inline)) void topk_unit(const Ctx &c, int i, in
 
 // Value of lane ^ J within the wave (J = 1, 2, 4, 8 by DPP inside 16-lane
 // rows; 16 and 32 through ds_bpermute).
-template <int J>
-__device__ __forceinline__ uint32_t lane_xor(uint32_t v) {
-  if constexpr (J == 1) {
-    return (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0xB1, 0xF, 0xF, false);  // quad_perm [1,0,3,2]
-  } else if constexpr (J == 2) {
-    return (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x4E, 0xF, 0xF, false);  // quad_perm [2,3,0,1]
-  } else if constexpr (J == 4) {
-    // row_ror:n gives lane l the value of lane l - n (mod 16)
-    const uint32_t lo = (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x124, 0xF, 0xF, false);  // row_ror:4
-    const uint32_t hi = (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x12C, 0xF, 0xF, false);  // row_ror:12
-    return (threadIdx.x & 4) ? lo : hi;
-  } else if constexpr (J == 8) {
-    return (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x128, 0xF, 0xF, false);  // row_ror:8
-  } else {
-    return (uint32_t)__shfl_xor((int)v, J, 64);
-  }
-}
-template <int J>
-__device__ __forceinline__ unsigned long long half_clean(unsigned long long v) {
-  const unsigned long long o =
-      ((unsigned long long)lane_xor<J>((uint32_t)(v >> 32)) << 32) | lane_xor<J>((uint32_t)v);
-  return (threadIdx.x & J) == 0 ? (v > o ? v : o) : (v < o ? v : o);
-}
-// The 64 largest of two descending lists of 64 keys (one per lane), in
-// descending order: max(a, b reversed) is bitonic and holds them; a cascade of
-// half-cleaners sorts it.
-__device__ __forceinline__ unsigned long long merge_top64(unsigned long long a, unsigned long long b) {
-  const int rev = 63 - (int)(threadIdx.x & 63);
-  const unsigned long long br = ((unsigned long long)(uint32_t)__shfl((int)(uint32_t)(b >> 32), rev, 64) << 32) |
-                                (uint32_t)__shfl((int)(uint32_t)b, rev, 64);
-  unsigned long long v = a > br ? a : br;
-  v = half_clean<32>(v);
-  v = half_clean<16>(v);
-  v = half_clean<8>(v);
-  v = half_clean<4>(v);
-  v = half_clean<2>(v);
-  v = half_clean<1>(v);
-  return v;
-}
-
 // Fast top-k of one unit from the score tiles' lists (no MAW flags, kk <=
 // kTileList; every thread of the workgroup calls it and gets the same
 // result).  The steps of topk_unit run on the listed keys, which hold the
@@ -1072,8 +1035,8 @@ __device__ __forceinline__ unsigned long long merge_top64(unsigned long long a, 
 //   3. the kk - (blocks in) best of them by (exact key desc, index asc);
 //   4. each chosen block is written at its place in ascending block order,
 //      read off an LDS bitmap of the chosen blocks.
-// Returns false, before writing anything, when a tile overflowed its list or
-// the band reaches past the 64 largest keys; the caller then runs topk_unit.
+// Returns false, before writing anything, when the band reaches past the 64
+// largest keys; the caller then runs topk_unit.
 template <int D, int G>
 __device__ __attribute__((always_inline)) bool topk_fast(const Ctx &c, int i, int seq, int h,
                                                          const HeadInfo &hi, const UG &g,
@@ -1091,13 +1054,9 @@ __device__ __attribute__((always_inline)) bool topk_fast(const Ctx &c, int i, in
   const int nw = cdiv(g.n_blk, 64);
   // one batch of loads: lists and counts (wave 0), error bound, the query
   unsigned long long e[kFastTiles];
-  uint32_t cntv[kFastTiles];
 #pragma unroll
-  for (int r = 0; r < kFastTiles; ++r) {
-    const bool on = wv == 0 && r < n_tiles;
-    e[r] = on ? ld_dev(&cl[(size_t)r * kTileList + lane]) : 0ull;
-    cntv[r] = on ? ld_dev(&c.sc.tcnt[unit * kFastTiles + r]) : 0u;
-  }
+  for (int r = 0; r < kFastTiles; ++r)
+    e[r] = (wv == 0 && r < n_tiles) ? ld_dev(&cl[(size_t)r * kTileList + lane]) : 0ull;
   const uint32_t eps_bits = ld_dev(&c.sc.unit_acc[2 * unit]);
   const uint16_t *qg = q + ((size_t)i * c.dm.Hq + (size_t)h * G) * D;
   constexpr int QT = (G * D + 255) / 256;
@@ -1110,8 +1069,6 @@ __device__ __attribute__((always_inline)) bool topk_fast(const Ctx &c, int i, in
 
   if (wv == 0) {
     bool ok = true;
-#pragma unroll
-    for (int r = 0; r < kFastTiles; ++r) ok = ok && cntv[r] != kTileOverflow;
     int n_in = 0, n_unc = 0;
     if (lane < nw) sm.bm[lane] = 0ull;
     __builtin_amdgcn_s_waitcnt(0xc07f);

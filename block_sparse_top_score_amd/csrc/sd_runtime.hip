@@ -305,7 +305,6 @@ sd_status sparse_decode_init(const sd_config *cfg, sd_ctx **out) {
   SD_HIP(c, hipMemset(c->sc.ucnt, 0, sizeof(int32_t) * max_seqs * c->Hkv));
   SD_HIP(c, hipMemset(c->sc.arrive, 0, sizeof(uint32_t) * max_seqs * c->Hkv * 2));
   if ((s = dev_alloc(c, &c->sc.cand, per_unit)) != SD_OK) return s;
-  if ((s = dev_alloc(c, &c->sc.tcnt, (size_t)max_seqs * c->Hkv * kFastTiles)) != SD_OK) return s;
   if ((s = dev_alloc(c, &c->sc.rtag, (size_t)max_seqs * c->Hkv)) != SD_OK) return s;
   if ((s = dev_alloc(c, &c->sc.seltag, (size_t)max_seqs * c->Hkv * c->k_cap)) != SD_OK) return s;
   if ((s = dev_alloc(c, &c->sc.err, 1)) != SD_OK) return s;
