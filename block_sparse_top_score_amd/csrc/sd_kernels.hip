@@ -381,36 +381,53 @@ __device__ __forceinline__ float upper_term(float qv, uint32_t mm) {
 }
 // Lane exchanges, bitonic sorting and merging of 64 keys held one per lane
 // (key = order key << 32 | ~block: unique, so no ties).
+// Lane l receives lane l ^ J's value.  J < 16: DPP inside 16-lane rows
+// (quad permutations; row_ror:n gives lane l the value of lane l - n mod 16,
+// so J = 4 takes row_ror:4 or row_ror:12 by lane).  J = 16, 32: the gfx950
+// permlane swaps, which with both operands v return, in every lane, the
+// values of the lower and the upper lane of the pair (l, l ^ J).
 template <int J>
 __device__ __forceinline__ uint32_t lane_xor(uint32_t v) {
   if constexpr (J == 1) {
-    return (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0xB1, 0xF, 0xF, false);  // quad_perm [1,0,3,2]
+    return (uint32_t)__builtin_amdgcn_mov_dpp((int)v, 0xB1, 0xF, 0xF, true);  // quad_perm [1,0,3,2]
   } else if constexpr (J == 2) {
-    return (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x4E, 0xF, 0xF, false);  // quad_perm [2,3,0,1]
+    return (uint32_t)__builtin_amdgcn_mov_dpp((int)v, 0x4E, 0xF, 0xF, true);  // quad_perm [2,3,0,1]
   } else if constexpr (J == 4) {
-    // row_ror:n gives lane l the value of lane l - n (mod 16)
-    const uint32_t lo = (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x124, 0xF, 0xF, false);  // row_ror:4
-    const uint32_t hi = (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x12C, 0xF, 0xF, false);  // row_ror:12
-    return (threadIdx.x & 4) ? lo : hi;
+    const uint32_t dn = (uint32_t)__builtin_amdgcn_mov_dpp((int)v, 0x124, 0xF, 0xF, true);  // row_ror:4
+    const uint32_t up = (uint32_t)__builtin_amdgcn_mov_dpp((int)v, 0x12C, 0xF, 0xF, true);  // row_ror:12
+    return (threadIdx.x & 4) ? dn : up;
   } else if constexpr (J == 8) {
-    return (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x128, 0xF, 0xF, false);  // row_ror:8
+    return (uint32_t)__builtin_amdgcn_mov_dpp((int)v, 0x128, 0xF, 0xF, true);  // row_ror:8
   } else {
-    return (uint32_t)__shfl_xor((int)v, J, 64);
+    static_assert(J == 16 || J == 32, "lane distance");
+    const auto r = J == 16 ? __builtin_amdgcn_permlane16_swap(v, v, false, false)
+                           : __builtin_amdgcn_permlane32_swap(v, v, false, false);
+    return (threadIdx.x & J) ? r[0] : r[1];
   }
 }
 template <int J>
+__device__ __forceinline__ unsigned long long key_xor(unsigned long long v) {
+  return ((unsigned long long)lane_xor<J>((uint32_t)(v >> 32)) << 32) | lane_xor<J>((uint32_t)v);
+}
+// Half-cleaner of a bitonic run of 64 into descending halves: the lower lane
+// of each pair (l, l ^ J) keeps the larger key (keys are unique).
+template <int J>
 __device__ __forceinline__ unsigned long long half_clean(unsigned long long v) {
-  const unsigned long long o =
-      ((unsigned long long)lane_xor<J>((uint32_t)(v >> 32)) << 32) | lane_xor<J>((uint32_t)v);
-  return (threadIdx.x & J) == 0 ? (v > o ? v : o) : (v < o ? v : o);
+  const unsigned long long o = key_xor<J>(v);
+  return (v > o) == ((threadIdx.x & J) == 0) ? v : o;
+}
+// Lane l receives lane 63 - l's key: row_mirror reverses each 16-lane row,
+// the swaps at distance 16 and 32 reverse the order of the rows.
+__device__ __forceinline__ uint32_t lane_rev(uint32_t v) {
+  v = (uint32_t)__builtin_amdgcn_mov_dpp((int)v, 0x140, 0xF, 0xF, true);  // row_mirror
+  return lane_xor<32>(lane_xor<16>(v));
 }
 // The 64 largest of two descending lists of 64 keys (one per lane), in
 // descending order: max(a, b reversed) is bitonic and holds them; a cascade of
 // half-cleaners sorts it.
 __device__ __forceinline__ unsigned long long merge_top64(unsigned long long a, unsigned long long b) {
-  const int rev = 63 - (int)(threadIdx.x & 63);
-  const unsigned long long br = ((unsigned long long)(uint32_t)__shfl((int)(uint32_t)(b >> 32), rev, 64) << 32) |
-                                (uint32_t)__shfl((int)(uint32_t)b, rev, 64);
+  const unsigned long long br =
+      ((unsigned long long)lane_rev((uint32_t)(b >> 32)) << 32) | lane_rev((uint32_t)b);
   unsigned long long v = a > br ? a : br;
   v = half_clean<32>(v);
   v = half_clean<16>(v);
@@ -425,11 +442,10 @@ __device__ __forceinline__ unsigned long long merge_top64(unsigned long long a, 
 // the lower lane keeps the larger key, in an ascending run the smaller.
 template <int K, int J>
 __device__ __forceinline__ unsigned long long bitonic_step(unsigned long long v) {
-  const unsigned long long o =
-      ((unsigned long long)lane_xor<J>((uint32_t)(v >> 32)) << 32) | lane_xor<J>((uint32_t)v);
+  const unsigned long long o = key_xor<J>(v);
   const int l = threadIdx.x & 63;
   const bool keep_max = ((l & J) == 0) == ((l & K) == 0);
-  return keep_max ? (v > o ? v : o) : (v < o ? v : o);
+  return (v > o) == keep_max ? v : o;
 }
 __device__ __forceinline__ unsigned long long sort64_desc(unsigned long long v) {
   v = bitonic_step<2, 1>(v);
