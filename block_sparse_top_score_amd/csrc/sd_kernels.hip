@@ -89,22 +89,6 @@ __device__ __forceinline__ bool arrive_last(uint32_t *counter, unsigned expected
 // Bound of every wait inside a launch.
 constexpr unsigned long long kWaitTicks = 20000000ull;  // 0.2 s of the 100 MHz clock
 
-__device__ __forceinline__ float wave_max(float x) {
-#pragma unroll
-  for (int o = 32; o >= 1; o >>= 1) x = fmaxf(x, __shfl_xor(x, o, 64));
-  return x;
-}
-__device__ __forceinline__ float wave_sum(float x) {
-#pragma unroll
-  for (int o = 32; o >= 1; o >>= 1) x += __shfl_xor(x, o, 64);
-  return x;
-}
-__device__ __forceinline__ int wave_sum_i(int x) {
-#pragma unroll
-  for (int o = 32; o >= 1; o >>= 1) x += __shfl_xor(x, o, 64);
-  return x;
-}
-
 __device__ __forceinline__ int lower_bound(const int32_t *a, int n, int v) {
   int lo = 0, hi = n;
   while (lo < hi) {
@@ -409,6 +393,54 @@ template <int J>
 __device__ __forceinline__ unsigned long long key_xor(unsigned long long v) {
   return ((unsigned long long)lane_xor<J>((uint32_t)(v >> 32)) << 32) | lane_xor<J>((uint32_t)v);
 }
+// DPP exchanges inside 16-lane rows (gfx9 encodings): every lane of a row
+// receives the row's max / sum.
+template <int CTRL>
+__device__ __forceinline__ float dppf(float x) {
+  return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), CTRL, 0xF, 0xF, false));
+}
+__device__ __forceinline__ float row_max16(float x) {
+  x = fmaxf(x, dppf<0xB1>(x));   // quad_perm [1,0,3,2]
+  x = fmaxf(x, dppf<0x4E>(x));   // quad_perm [2,3,0,1]
+  x = fmaxf(x, dppf<0x141>(x));  // row_half_mirror
+  x = fmaxf(x, dppf<0x140>(x));  // row_mirror
+  return x;
+}
+__device__ __forceinline__ float row_sum16(float x) {
+  x += dppf<0xB1>(x);
+  x += dppf<0x4E>(x);
+  x += dppf<0x141>(x);
+  x += dppf<0x140>(x);
+  return x;
+}
+// Whole-wave reductions (every lane receives the result): the row reduction,
+// then the rows combined by the swaps at distance 16 and 32.
+__device__ __forceinline__ float wave_max(float x) {
+  x = row_max16(x);
+  x = fmaxf(x, __uint_as_float(lane_xor<16>(__float_as_uint(x))));
+  return fmaxf(x, __uint_as_float(lane_xor<32>(__float_as_uint(x))));
+}
+__device__ __forceinline__ float wave_sum(float x) {
+  x = row_sum16(x);
+  x += __uint_as_float(lane_xor<16>(__float_as_uint(x)));
+  return x + __uint_as_float(lane_xor<32>(__float_as_uint(x)));
+}
+__device__ __forceinline__ uint32_t wave_max_u32(uint32_t x) {
+  x = max(x, lane_xor<1>(x));
+  x = max(x, lane_xor<2>(x));
+  x = max(x, lane_xor<4>(x));
+  x = max(x, lane_xor<8>(x));
+  x = max(x, lane_xor<16>(x));
+  return max(x, lane_xor<32>(x));
+}
+__device__ __forceinline__ int wave_sum_i(int x) {
+  x += (int)lane_xor<1>((uint32_t)x);
+  x += (int)lane_xor<2>((uint32_t)x);
+  x += (int)lane_xor<4>((uint32_t)x);
+  x += (int)lane_xor<8>((uint32_t)x);
+  x += (int)lane_xor<16>((uint32_t)x);
+  return x + (int)lane_xor<32>((uint32_t)x);
+}
 // Half-cleaner of a bitonic run of 64 into descending halves: the lower lane
 // of each pair (l, l ^ J) keeps the larger key (keys are unique).
 template <int J>
@@ -616,8 +648,7 @@ __device__ __attribute__((always_inline)) bool score_tile(const Ctx &c, int i, i
   // the unit's largest error bound (non-negative floats order as their bits)
   // and its flagged candidates, accumulated over the tiles
   uint32_t eb = __float_as_uint(emax);
-#pragma unroll
-  for (int o = 32; o >= 1; o >>= 1) eb = max(eb, (uint32_t)__shfl_xor((int)eb, o, 64));
+  eb = wave_max_u32(eb);
   const int nf = wave_sum_i(n_flag);
   if (lane == 0) {
     red[wv] = eb;
@@ -1198,26 +1229,6 @@ __device__ __attribute__((always_inline)) bool topk_fast(const Ctx &c, int i, in
 }
 
 // ---------------------------------------------------------------------------
-// DPP exchanges inside 16-lane rows (gfx9 encodings): every lane of a row
-// receives the row's max / sum.
-template <int CTRL>
-__device__ __forceinline__ float dppf(float x) {
-  return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), CTRL, 0xF, 0xF, false));
-}
-__device__ __forceinline__ float row_max16(float x) {
-  x = fmaxf(x, dppf<0xB1>(x));   // quad_perm [1,0,3,2]
-  x = fmaxf(x, dppf<0x4E>(x));   // quad_perm [2,3,0,1]
-  x = fmaxf(x, dppf<0x141>(x));  // row_half_mirror
-  x = fmaxf(x, dppf<0x140>(x));  // row_mirror
-  return x;
-}
-__device__ __forceinline__ float row_sum16(float x) {
-  x += dppf<0xB1>(x);
-  x += dppf<0x4E>(x);
-  x += dppf<0x141>(x);
-  x += dppf<0x140>(x);
-  return x;
-}
 
 __device__ __forceinline__ unsigned long long bit_range(int a, int b) {
   if (b <= a) return 0ull;
@@ -1630,6 +1641,15 @@ __device__ __forceinline__ void empty_slots(const Ctx &c, int i, int h, int P, i
 //   kMawFull: decay of every block here, then one add per attended block.
 //   kMawAdd:  the score tiles already wrote r*MAW (one-launch step).
 constexpr int kMawNone = 0, kMawFull = 1, kMawAdd = 2;
+// e^x and ln x from the hardware base-2 exponential and logarithm (about one
+// ulp each; the fp32 rounding of x log2(e) adds |x| 2^-24 relative, under
+// 1e-5 for the partial weights here)
+__device__ __forceinline__ float fast_exp(float x) {
+  return __builtin_amdgcn_exp2f(x * 1.44269504088896341f);
+}
+__device__ __forceinline__ float fast_log(float x) {
+  return __builtin_amdgcn_logf(x) * 0.69314718055994531f;
+}
 constexpr int kFusePre = 16;  // partial slots whose O values are preloaded
 constexpr int kFusePgPre = 2;  // page-mass entries per thread preloaded
 
@@ -1718,14 +1738,14 @@ __device__ __attribute__((always_inline)) void fuse_unit(const Ctx &c, int i, in
     float z = 0.0f;
     if (m != -INFINITY)
 #pragma unroll
-      for (int r = 0; r < R; ++r) z += l[r] == -INFINITY ? 0.0f : expf(l[r] - m);
+      for (int r = 0; r < R; ++r) z += l[r] == -INFINITY ? 0.0f : fast_exp(l[r] - m);
     z = wave_sum(z);
-    const float L = m == -INFINITY ? -INFINITY : m + logf(z);
+    const float L = m == -INFINITY ? -INFINITY : m + fast_log(z);
     if (lane == 0) sm.lse[gg] = L;
 #pragma unroll
     for (int r = 0; r < R; ++r) {
       const int u = lane + 64 * r;
-      sm.w[gg][u] = (L == -INFINITY || l[r] == -INFINITY) ? 0.0f : expf(l[r] - L);
+      sm.w[gg][u] = (L == -INFINITY || l[r] == -INFINITY) ? 0.0f : fast_exp(l[r] - L);
     }
   }
 #pragma unroll
@@ -1770,7 +1790,7 @@ __device__ __attribute__((always_inline)) void fuse_unit(const Ctx &c, int i, in
 #pragma unroll
     for (int gg = 0; gg < G; ++gg) {
       const float L = sm.lse[gg];
-      a += (L == -INFINITY || lm[gg] == -INFINITY) ? 0.0f : expf(lm[gg] - L);
+      a += (L == -INFINITY || lm[gg] == -INFINITY) ? 0.0f : fast_exp(lm[gg] - L);
     }
     return a;
   };
