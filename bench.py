@@ -23,6 +23,7 @@ results, for comparison).
 from __future__ import annotations
 
 import argparse
+import dataclasses
 import json
 import math
 import os
@@ -63,6 +64,9 @@ def parse():
     ap.add_argument("--cpu-baseline", type=int, default=1)
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
     ap.add_argument("--trials", type=int, default=3)
+    ap.add_argument("--streaming-heads", type=int, default=0,
+                    help="give the first K KV heads budget 0 (streaming heads: sinks and "
+                         "recent window only); a variant of the workload, not the headline")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="run a plain 1 GiB device copy (counter calibration) and exit")
     ap.add_argument("--traffic-summary", nargs=4, metavar=("FETCH", "WRITE", "CAL_FETCH", "CAL_WRITE"),
@@ -148,7 +152,7 @@ def algorithmic_bytes(w, N, blk_cnt, blk_idx, with_maw=True):
             inT[max(0, N - w.window):] = True
             for i in sel:
                 inT[i * S:min(N, (i + 1) * S)] = True
-            summ += nb * 2 * w.d * 2
+            summ += nb * 2 * w.d * 2 if w.budget_ppm[g] > 0 else 0  # streaming heads score nothing
             attend += int(inT.sum()) * 2 * w.d * 2
             maw += nb * 4 * 2 if with_maw else 0
     qol = w.B * w.Hq * (2 * w.d + 4 * w.d + 4)
@@ -175,6 +179,9 @@ def main():
     torch.cuda.set_device(0)
     dev = torch.device("cuda:0")
     w = synth.llama32k()
+    if args.streaming_heads:
+        K_s = min(args.streaming_heads, w.Hkv)
+        w = dataclasses.replace(w, budget_ppm=[0] * K_s + list(w.budget_ppm[K_s:]))
     N0 = w.N - 1                      # the first timed visit appends token N
     L = args.layers
     max_len = w.N + (args.steps + args.warmup) * (args.trials + 2) // L + 64
@@ -279,7 +286,9 @@ def main():
         "dtype": "bf16",
         "data": "synthetic",
         "config": {"workload": "llama32k: B=8, Hq=32, Hkv=8, d=128, N=32768 (+1 per visit), "
-                               "S=32, budget 5%%, 4 sinks + 512 recent, %d layer instances" % L,
+                               "S=32, budget 5%%, 4 sinks + 512 recent, %d layer instances" % L
+                               + ("; KV heads 0-%d streaming (budget 0)" % (args.streaming_heads - 1)
+                                  if args.streaming_heads else ""),
                    "global_batch": w.B, "seq_len": w.N, "parallelism": "none (1 GPU)",
                    "fused_step": bool(args.fused)},
         "step_hbm": {"algorithmic_bytes": ab["total"], "achieved_GBs": step_gbs,
@@ -288,7 +297,8 @@ def main():
         "kernel_ms": {"k_step": t_step, "timed_launches": n_inst},
         "roofline": {"kernel": "k_step", "bound": "hbm", "achieved": kstep_gbs,
                      "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": kstep_gbs / HBM_PEAK_GBS,
-                     "traffic": measured_traffic(), "algorithmic_bytes_per_launch": kstep_bytes},
+                     "traffic": None if args.streaming_heads else measured_traffic(),
+                     "algorithmic_bytes_per_launch": kstep_bytes},
         "trials_ms": trial_ms,
         "setup_s": setup_s,
     }

@@ -130,6 +130,14 @@ __device__ __forceinline__ UG unit_geom(int N, const HeadInfo &hi, const Dims &d
   return g;
 }
 
+// A unit selects nothing (k = 0) when its head's budget is 0 (a streaming
+// head, which attends to its sinks and recent window only; [FLX] streaming
+// heads) or when no block has a token outside the dense set.  Cheap: no
+// division, so the score tiles can decide before any work.
+__device__ __forceinline__ bool selects_nothing(const HeadInfo &hi, int N, const Dims &dm) {
+  return hi.ppm == 0 || min(dm.n_sink, N) >= max(0, N - dm.window);
+}
+
 __device__ __forceinline__ bool is_candidate(const UG &g, int i) {
   if (g.ns >= g.wlo) return false;
   const int lo = i * g.S, hi = min(lo + g.S, g.N);
@@ -1904,6 +1912,10 @@ __global__ __launch_bounds__(256) void k_select(Ctx c, SeqBatch b, int tiles_x,
   const int n_blk = div_S(N + hi.S - 1, hi.S);
   const int n_tiles = max(1, cdiv(n_blk, kScoreTile));
   if (tile >= n_tiles) return;
+  if (selects_nothing(hi, N, c.dm)) {  // no scoring: the count is 0
+    if (tile == 0 && threadIdx.x == 0) st_dev(&blk_cnt[(size_t)i * c.dm.Hkv + h], 0);
+    return;
+  }
   UG g;
   score_tile<D, G>(c, i, seq, h, hi, N, n_blk, tile, q, smem_topk, false, false, g);
   uint32_t *ctr = &c.sc.arrive[((size_t)seq * c.dm.Hkv + h) * 2];
@@ -1984,7 +1996,7 @@ __global__ __launch_bounds__(256, 2) void k_step(Ctx c, SeqBatch b, int tiles_x,
   if (score) {
     const int n_blk = div_S(N + hi.S - 1, hi.S);
     const int n_tiles = max(1, cdiv(n_blk, kScoreTile));
-    if (idx >= n_tiles) return;
+    if (idx >= n_tiles || selects_nothing(hi, N, c.dm)) return;  // (the parts cover k = 0)
     // the score tiles, the top-k and the fusion are on every unit's critical
     // path: their waves get issue priority over the attention parts'
     __builtin_amdgcn_s_setprio(2);
@@ -2033,18 +2045,24 @@ __global__ __launch_bounds__(256, 2) void k_step(Ctx c, SeqBatch b, int tiles_x,
     ptl = t;  // visible to all waves after the barrier of the selection wait
   }
   if (idx == 0) empty_slots<D, G>(c, i, h, P, p_cap, o_part, lse_part);
+  // a unit that selects nothing has no score tiles: its parts take the dense
+  // pages only, part 0 writes the count, the fusion decays every block's MAW
+  const bool no_sel = selects_nothing(hi, N, c.dm);
+  if (no_sel && idx == 0 && threadIdx.x == 0) st_dev(&blk_cnt[(size_t)i * c.dm.Hkv + h], 0);
   SelIn si;
-  si.tag = c.sc.seltag + unit * c.dm.kcap;
-  si.rtag = &c.sc.rtag[unit];
+  si.tag = no_sel ? nullptr : c.sc.seltag + unit * c.dm.kcap;
+  si.rtag = no_sel ? nullptr : &c.sc.rtag[unit];
+  si.cnt = 0;
   si.epoch = epoch;
   attend_part<D, G>(c, i, seq, h, g, idx, P, q, si, o_part, lse_part, p_cap, smem_att, ptl,
                     &s_cnt);
   uint32_t *fctr = &c.sc.arrive[unit * 2 + 1];
   if (!arrive_last(fctr, (unsigned)P, &s_flag)) return;
   __builtin_amdgcn_s_setprio(3);
-  const int cnt = (int)(uint32_t)ld_dev(&c.sc.rtag[unit]);  // this step's, seen by every part
-  fuse_unit<D, G>(c, i, seq, h, hi, g, kMawAdd, P, nullptr, cnt, o_part, lse_part, p_cap, o, lse,
-                  smem_fuse, c.sc.seltag + unit * c.dm.kcap, epoch);
+  // this step's count, seen by every part
+  const int cnt = no_sel ? 0 : (int)(uint32_t)ld_dev(&c.sc.rtag[unit]);
+  fuse_unit<D, G>(c, i, seq, h, hi, g, no_sel ? kMawFull : kMawAdd, P, nullptr, cnt, o_part,
+                  lse_part, p_cap, o, lse, smem_fuse, c.sc.seltag + unit * c.dm.kcap, epoch);
   if (threadIdx.x == 0) st_dev(fctr, 0u);
 }
 

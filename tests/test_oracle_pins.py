@@ -322,6 +322,30 @@ def test_everything_dense_when_short():
     np.testing.assert_allclose(a["lse"], lse, atol=1e-12, rtol=0)
 
 
+@pytest.mark.parametrize("N,S,n_s,W", [(2000, 32, 4, 512), (777, 16, 0, 64), (5000, 64, 16, 0)])
+def test_streaming_head_attends_dense_set_only(N, S, n_s, W):
+    """A head with budget 0 (a streaming head) selects nothing and attends to
+    its sinks and recent window only: the oracle's result equals a numpy
+    softmax over those tokens."""
+    G, d = 4, 64
+    K = rand_bits((N, d), seed=N + 11, scale=1.5)
+    V = rand_bits((N, d), seed=N + 12)
+    q = rand_bits((G, d), seed=N + 13)
+    mn, mx = oracle.summaries(K, S)
+    r = oracle.select(q, mn, mx, N, S, n_s, W, 0)
+    assert r["k"] == 0 and len(r["sel"]) == 0
+    a = oracle.attend(q, K, V, N, S, n_s, W, r["sel"])
+    tok = np.array(sorted(set(range(min(n_s, N))) | set(range(max(0, N - W), N))))
+    assert a["n_tok"] == len(tok)
+    s = f64(q) @ f64(K)[tok].T / math.sqrt(d)
+    m = s.max(axis=1, keepdims=True)
+    p = np.exp(s - m)
+    O = (p / p.sum(axis=1, keepdims=True)) @ f64(V)[tok]
+    lse = m[:, 0] + np.log(p.sum(axis=1))
+    np.testing.assert_allclose(a["O"], O, rtol=0, atol=1e-12)
+    np.testing.assert_allclose(a["lse"], lse, rtol=0, atol=1e-12)
+
+
 def test_single_token():
     d = 16
     K, V, q = rand_bits((1, d), 7), rand_bits((1, d), 8), rand_bits((2, d), 9)
