@@ -1088,8 +1088,11 @@ __device__ __attribute__((always_inline)) void topk_unit(const Ctx &c, int i, in
 //      unit's error bound); the blocks in between are re-scored exactly by
 //      the four waves, one lane quad per (block, head);
 //   3. the kk - (blocks in) best of them by (exact key desc, index asc);
-//   4. each chosen block is written at its place in ascending block order,
-//      read off an LDS bitmap of the chosen blocks.
+//   4. in the one-launch step, the tagged selection for the attention parts
+//      is written in key order as soon as it is known (the surely selected
+//      blocks at once, the band's picks after the re-score), then the count;
+//      the caller's list is written in ascending block order, read off an
+//      LDS bitmap of the chosen blocks.
 // Returns false, before writing anything, when the band reaches past the 64
 // largest keys; the caller then runs topk_unit.
 template <int D, int G>
@@ -1100,10 +1103,12 @@ __device__ __attribute__((always_inline)) bool topk_fast(const Ctx &c, int i, in
                                                          int32_t *__restrict__ blk_cnt, int k_cap,
                                                          TopkSmem &sm,
                                                          unsigned long long *tagd = nullptr,
+                                                         unsigned long long *rtag = nullptr,
                                                          uint32_t epoch = 0) {
   const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
   const size_t unit = (size_t)seq * c.dm.Hkv + h;
   const int n_tiles = max(1, cdiv(g.n_blk, kScoreTile));
+  const unsigned long long etag = (unsigned long long)epoch << 32;
   const unsigned long long *cl = c.sc.cand + unit * c.dm.key_stride;
   const int kk = g.kk;
   const int nw = cdiv(g.n_blk, 64);
@@ -1154,6 +1159,17 @@ __device__ __attribute__((always_inline)) bool topk_fast(const Ctx &c, int i, in
       n_in = count_lanes(in);
       ok = whole;
       ok = ok && n_in <= kk && n_in + n_unc >= kk;
+      if (ok && tagd) {
+        // the tagged selection goes out in key order: the surely selected
+        // blocks at once, with the band when it is taken whole; the count
+        // follows the last entry (the band's picks may come after the
+        // exact re-score)
+        const bool whole_band = n_in + n_unc == kk;
+        const unsigned long long mi = __ballot(in);
+        const int pos = in ? lanes_below(mi) : n_in + lanes_below(mu);
+        if ((in || (whole_band && unc)) && pos < c.dm.kcap) st_dev(&tagd[pos], etag | (uint32_t)blk);
+        if (lane == 0 && (whole_band || n_in == kk)) st_dev(rtag, etag | (uint32_t)kk);
+      }
     }
     if (lane == 0) {
       sm.ok = ok;
@@ -1197,7 +1213,9 @@ __device__ __attribute__((always_inline)) bool topk_fast(const Ctx &c, int i, in
       if (lane < n_unc && rank < kr2) {
         const int blk = sm.ulist[lane];
         atomicOr(&sm.bm[blk >> 6], 1ull << (blk & 63));
+        if (tagd && sm.nin + rank < c.dm.kcap) st_dev(&tagd[sm.nin + rank], etag | (uint32_t)blk);
       }
+      if (tagd && lane == 0) st_dev(rtag, etag | (uint32_t)kk);
     }
   }
   if (wv == 0) {
@@ -1220,10 +1238,7 @@ __device__ __attribute__((always_inline)) bool topk_fast(const Ctx &c, int i, in
     int32_t *dst = blk_idx + ((size_t)i * c.dm.Hkv + h) * k_cap;
     while (wbits) {
       const int bb = lane * 64 + (__ffsll((long long)wbits) - 1);
-      if (o < k_cap) {
-        st_dev(&dst[o], bb);
-        if (tagd && o < c.dm.kcap) st_dev(&tagd[o], ((unsigned long long)epoch << 32) | (uint32_t)bb);
-      }
+      if (o < k_cap) st_dev(&dst[o], bb);
       ++o;
       wbits &= wbits - 1ull;
     }
@@ -1825,7 +1840,14 @@ __device__ __attribute__((always_inline)) void fuse_unit(const Ctx &c, int i, in
   __syncthreads();
   auto pm = [&](int t) { return t < n_pg_lds ? sm.pm[t] : page_mass_at(t); };
   auto sel_at = [&](int j) { return sel_lds ? sm.sel[j] : sel_ld(j); };
-  auto sel_find = [&](int blk) {  // position of blk in the (ascending) selection, or -1
+  // position of blk in the selection, or -1: a scan of a short selection (the
+  // fast top-k's, in key order), else a binary search (ascending order)
+  auto sel_find = [&](int blk) {
+    if (cnt <= kTileList) {
+      for (int j = 0; j < cnt; ++j)
+        if (sel_at(j) == blk) return j;
+      return -1;
+    }
     int lo = 0, hi2 = cnt;
     while (lo < hi2) {
       const int mid = (lo + hi2) >> 1;
@@ -2009,16 +2031,19 @@ __global__ __launch_bounds__(256, 2) void k_step(Ctx c, SeqBatch b, int tiles_x,
     __builtin_amdgcn_s_setprio(3);
     uint32_t *lrows = reinterpret_cast<uint32_t *>(smem_raw + sizeof(TopkSmem));
     unsigned long long *tagd = c.sc.seltag + unit * c.dm.kcap;
-    if (!fast || !topk_fast<D, G>(c, i, seq, h, hi, g, q, blk_idx, blk_cnt, k_cap, smem_topk,
-                                  tagd, epoch))
+    // the fast top-k publishes the count itself, right after the entries
+    const bool fast_done = fast && topk_fast<D, G>(c, i, seq, h, hi, g, q, blk_idx, blk_cnt, k_cap,
+                                                   smem_topk, tagd, &c.sc.rtag[unit], epoch);
+    if (!fast_done)
       topk_unit<D, G>(c, i, seq, h, hi, g, q, blk_idx, blk_cnt, k_cap, smem_topk, lrows,
                       lrows_words, reinterpret_cast<unsigned long long *>(lrows + lrows_words),
                       tagd, epoch);
     if (threadIdx.x == 0) {
       // the entries carry their own tags, so the count need not wait for them
-      const int cnt = min(min(g.kk, k_cap), hi.kcap);
       st_dev(ctr, 0u);
-      st_dev(&c.sc.rtag[unit], ((unsigned long long)epoch << 32) | (uint32_t)cnt);
+      if (!fast_done || g.kk == 0)
+        st_dev(&c.sc.rtag[unit], ((unsigned long long)epoch << 32) |
+                                     (uint32_t)min(min(g.kk, k_cap), hi.kcap));
     }
     return;
   }
