@@ -490,7 +490,11 @@ int parts_of(sd_ctx *c, int layer, const SeqBatch &b, int max_blocks) {
                                                        c->pps <= kPtLds ? c->pps : 0)).first;
   const int units = c->Hkv * b.n;
   const int tiles = std::max(1, (max_blocks + kScoreTile - 1) / kScoreTile);
-  if (it->second > 0) P = std::min<int64_t>(P, std::max(1, it->second / units - tiles));
+  // fewer parts, so that the whole step stays resident, pays when it costs
+  // at most half of them; otherwise (long units, many tiles) the parts that do
+  // not fit start as score tiles finish
+  const int64_t resident = it->second > 0 ? it->second / units - tiles : P;
+  if (2 * resident >= P) P = std::min<int64_t>(P, std::max<int64_t>(1, resident));
   return (int)std::min<int64_t>(P, c->p_cap);
 }
 
