@@ -168,7 +168,7 @@ struct TopkSmem {
   unsigned long long srt[4][kTileList];  // the waves' sorted keys (tile list)
   float qs[SD_MAX_GROUP * 128];
   double ud[16];
-  uint32_t red[8];
+  uint32_t red[16];
   int nlist, nin, kr2, ok;
   int last;
 };
@@ -1075,6 +1075,249 @@ __device__ __attribute__((always_inline)) void topk_unit(const Ctx &c, int i, in
   }
 }
 
+// Workgroup helpers of the wide top-k (every thread calls them; red holds 8
+// words of LDS, used in two halves by alternate calls).
+__device__ __forceinline__ int wg_sum(int x, uint32_t *red, int &slot) {
+  const int wv = threadIdx.x >> 6;
+  x = wave_sum_i(x);
+  uint32_t *r = red + 4 * slot;
+  slot ^= 1;
+  if ((threadIdx.x & 63) == 0) r[wv] = (uint32_t)x;
+  __syncthreads();
+  return (int)(r[0] + r[1] + r[2] + r[3]);
+}
+// exclusive prefix of x over the threads in index order, and the total
+__device__ __forceinline__ int wg_scan(int x, uint32_t *red, int &slot, int &total) {
+  const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
+  int incl = x;
+  incl += __builtin_amdgcn_update_dpp(0, incl, 0x111, 0xF, 0xF, true);  // row_shr:1
+  incl += __builtin_amdgcn_update_dpp(0, incl, 0x112, 0xF, 0xF, true);  // row_shr:2
+  incl += __builtin_amdgcn_update_dpp(0, incl, 0x114, 0xF, 0xF, true);  // row_shr:4
+  incl += __builtin_amdgcn_update_dpp(0, incl, 0x118, 0xF, 0xF, true);  // row_shr:8
+  const int r0 = __builtin_amdgcn_readlane(incl, 15), r1 = __builtin_amdgcn_readlane(incl, 31),
+            r2 = __builtin_amdgcn_readlane(incl, 47);
+  incl += (lane >= 16 ? r0 : 0) + (lane >= 32 ? r1 : 0) + (lane >= 48 ? r2 : 0);
+  uint32_t *r = red + 4 * slot;
+  slot ^= 1;
+  if (lane == 63) r[wv] = (uint32_t)incl;
+  __syncthreads();
+  int before = 0;
+  for (int v = 0; v < wv; ++v) before += (int)r[v];
+  total = (int)(r[0] + r[1] + r[2] + r[3]);
+  return before + incl - x;
+}
+
+// Full top-k of a long unit by all four waves (the same order and result as
+// topk_unit): thread t holds the words of blocks [t m, t m + m), m =
+// ceil(n / 256) <= kWideM, in registers.  The k-th largest word is bracketed
+// by bisection with workgroup counts until the bracket is within eps; the
+// band is listed in index order by a workgroup scan, re-scored exactly (lane
+// quads of all waves) and ranked; the chosen blocks are written in ascending
+// order by a second scan.
+constexpr int kWideM = 40;  // blocks per thread: units up to 10240 blocks
+template <int D, int G>
+__device__ __attribute__((always_inline)) void topk_wide(const Ctx &c, int i, int seq, int h, const HeadInfo &hi,
+                          const UG &g, const uint16_t *__restrict__ q,
+                          int32_t *__restrict__ blk_idx, int32_t *__restrict__ blk_cnt,
+                          int k_cap, TopkSmem &sm,
+                          unsigned long long *dmask /* LDS, one word per row */,
+                          unsigned long long *tagd = nullptr, uint32_t epoch = 0) {
+  const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
+  const int n = g.n_blk, rows = cdiv(n, 64);
+  const int m = cdiv(n, 256), j0 = tid * m;
+  const size_t unit = (size_t)seq * c.dm.Hkv + h;
+  const size_t uo = unit * c.dm.key_stride;
+  const unsigned long long *gkf = c.sc.keyflag + uo;
+  int32_t *gul = c.sc.ulist + uo;
+  uint32_t *guk = c.sc.ukeys + uo;
+  auto ul_ld = [&](int p) -> int { return p < kTopkUnc ? sm.ulist[p] : ld_dev(&gul[p]); };
+  auto ul_st = [&](int p, int v) { if (p < kTopkUnc) sm.ulist[p] = v; else st_dev(&gul[p], v); };
+  auto uk_ld = [&](int p) -> uint32_t { return p < kTopkUnc ? sm.ukey[p] : ld_dev(&guk[p]); };
+  auto uk_st = [&](int p, uint32_t v) { if (p < kTopkUnc) sm.ukey[p] = v; else st_dev(&guk[p], v); };
+  uint32_t *red = sm.red;
+  int slot = 0;
+
+  // 0. one batch of loads: the accumulators, the thread's keys, the query
+  const uint32_t eps_bits = ld_dev(&c.sc.unit_acc[2 * unit]);
+  const uint32_t f_raw = ld_dev(&c.sc.unit_acc[2 * unit + 1]);
+  unsigned long long kv[kWideM];
+#pragma unroll
+  for (int x = 0; x < kWideM; ++x) kv[x] = (x < m && j0 + x < n) ? ld_dev(&gkf[j0 + x]) : 0ull;
+  constexpr int QT = (G * D + 255) / 256;
+  const uint16_t *qg = q + ((size_t)i * c.dm.Hq + (size_t)h * G) * D;
+  uint16_t qv[QT];
+#pragma unroll
+  for (int t = 0; t < QT; ++t) qv[t] = qg[min(tid + 256 * t, G * D - 1)];
+
+  const bool use_flag = c.dm.maw_beta > 0.0f;
+  const int F = use_flag ? (int)f_raw : 0;
+  const int kk = g.kk;
+  const bool take_flagged = F < kk;
+  const uint32_t want = take_flagged ? 0u : 1u;
+  const int k_sub = take_flagged ? kk - F : kk;
+  uint32_t w[kWideM];
+  uint32_t lo = 0xffffffffu, hi_k = 0u;
+#pragma unroll
+  for (int x = 0; x < kWideM; ++x) {
+    const uint32_t key = (uint32_t)kv[x];
+    const uint32_t fl = use_flag ? (uint32_t)(kv[x] >> 32) & 1u : 0u;
+    w[x] = key == 0u ? 0u : (fl == want ? key : (take_flagged ? 1u : 0u));
+    if (w[x] >= 2u) {
+      lo = min(lo, w[x]);
+      hi_k = max(hi_k, w[x]);
+    }
+  }
+  for (int r = tid; r < rows; r += 256) dmask[r] = 0ull;
+#pragma unroll
+  for (int t = 0; t < QT; ++t)
+    if (tid + 256 * t < G * D) sm.qs[tid + 256 * t] = __uint_as_float((uint32_t)qv[t] << 16);
+  auto count_ge = [&](uint32_t t) {
+    int cnt = 0;
+#pragma unroll
+    for (int x = 0; x < kWideM; ++x) cnt += w[x] >= t ? 1 : 0;
+    return wg_sum(cnt, red, slot);
+  };
+
+  uint32_t kb_lo = 0xffffffffu, kb_hi = 0xffffffffu;
+  if (k_sub > 0) {
+    // 1. bracket [a, b] of the k_sub-th largest word T_a: #(>= a) >= k_sub >
+    // #(> b), narrowed until within eps; the band edges as in topk_unit
+    const double eps = (double)__uint_as_float(eps_bits);
+    lo = wave_min_u(lo);
+    hi_k = wave_max_u(hi_k);
+    if (lane == 0) {
+      red[8 + wv] = lo;
+      red[12 + wv] = hi_k;
+    }
+    __syncthreads();
+    uint32_t a = min(min(red[8], red[9]), min(red[10], red[11]));
+    uint32_t b = max(max(red[12], red[13]), max(red[14], red[15]));
+    while (a < b && (double)key_to_float(b) - (double)key_to_float(a) > eps) {
+      const uint32_t mid = a + ((b - a) >> 1) + 1u;  // a < mid <= b
+      if (count_ge(mid) >= k_sub) a = mid; else b = mid - 1u;
+    }
+    kb_hi = order_key(__double2float_rd((double)key_to_float(b) + 2.0 * eps));
+    kb_lo = order_key(__double2float_ru((double)key_to_float(a) - 2.0 * eps));
+    // 2. the band in index order; the sure ones counted
+    int my_unc = 0, my_in = 0;
+#pragma unroll
+    for (int x = 0; x < kWideM; ++x) {
+      my_unc += (w[x] >= kb_lo && w[x] <= kb_hi) ? 1 : 0;
+      my_in += w[x] > kb_hi ? 1 : 0;
+    }
+    int n_unc = 0;
+    int p = wg_scan(my_unc, red, slot, n_unc);
+    const int n_in = wg_sum(my_in, red, slot);
+#pragma unroll
+    for (int x = 0; x < kWideM; ++x)
+      if (w[x] >= kb_lo && w[x] <= kb_hi) ul_st(p++, j0 + x);
+    wait_vmem();
+    __syncthreads();
+    const int kr2 = k_sub - n_in;  // >= 1: T_a's own block is in the band
+    // 3. exact keys of the band: one lane quad per (block, head), 64 / G
+    // whole blocks a pass; then the best head per block
+    constexpr int BPP = 64 / G;
+    for (int b0 = 0; b0 < n_unc; b0 += BPP) {
+      const int pair = tid >> 2, u = b0 + pair / G, gg = pair % G;
+      const bool on = pair < BPP * G && u < n_unc;
+      const double U = exact_score_quad<D>(c, seq, hi, on ? ul_ld(u) : 0, sm.qs + gg * D, on);
+      if (on && (tid & 3) == 0) sm.ue[pair] = U;
+      __syncthreads();
+      if (tid < BPP && b0 + tid < n_unc) {
+        double best = sm.ue[tid * G];
+        for (int x = 1; x < G; ++x) best = sm.ue[tid * G + x] > best ? sm.ue[tid * G + x] : best;
+        uk_st(b0 + tid, order_key((float)best));
+      }
+      __syncthreads();
+    }
+    wait_vmem();
+    __syncthreads();
+    // 4. the kr2 largest exact keys, ties to the lower index (list order)
+    if (wv == 0) {
+      if (n_unc <= 64) {
+        const uint32_t e = lane < n_unc ? uk_ld(lane) : 0u;
+        int rank = 0;
+        for (int q2 = 0; q2 < n_unc; ++q2) {
+          const uint32_t eq2 = (uint32_t)__builtin_amdgcn_readlane((int)e, q2);
+          rank += (eq2 > e || (eq2 == e && q2 < lane)) ? 1 : 0;
+        }
+        if (lane < n_unc && rank < kr2) {
+          const int j = ul_ld(lane);
+          atomicOr(&dmask[j >> 6], 1ull << (j & 63));
+        }
+      } else {
+        const int urows = cdiv(n_unc, 64);
+        uint32_t lo2 = 0xffffffffu, hi2 = 0u;
+        for (int r = 0; r < urows; ++r) {
+          const int pp = r * 64 + lane;
+          if (pp < n_unc) {
+            const uint32_t e = uk_ld(pp);
+            lo2 = min(lo2, e);
+            hi2 = max(hi2, e);
+          }
+        }
+        lo2 = wave_min_u(lo2);
+        hi2 = wave_max_u(hi2);
+        auto ucount_ge = [&](uint32_t t) -> int {
+          int cnt = 0;
+          for (int r = 0; r < urows; ++r) {
+            const int pp = r * 64 + lane;
+            cnt += count_lanes(pp < n_unc && uk_ld(pp) >= t);
+          }
+          return cnt;
+        };
+        const uint32_t T2 = bisect_kth(lo2, hi2, kr2, ucount_ge);
+        const int kr2_eq = kr2 - (T2 == 0xffffffffu ? 0 : ucount_ge(T2 + 1u));
+        int eqb = 0;
+        for (int r = 0; r < urows; ++r) {
+          const int pp = r * 64 + lane;
+          const uint32_t e = pp < n_unc ? uk_ld(pp) : 0u;
+          const bool eq = pp < n_unc && e == T2;
+          const unsigned long long me = __ballot(eq);
+          const bool take = (pp < n_unc && e > T2) || (eq && eqb + lanes_below(me) < kr2_eq);
+          eqb += __popcll(me);
+          if (take) {
+            const int j = ul_ld(pp);
+            atomicOr(&dmask[j >> 6], 1ull << (j & 63));
+          }
+        }
+      }
+    }
+  }
+  __syncthreads();
+
+  // 5. ordered compaction: the thread's chosen blocks at their places
+  int my_ch = 0;
+#pragma unroll
+  for (int x = 0; x < kWideM; ++x) {
+    const int j = j0 + x;
+    const bool ch = x < m && j < n &&
+                    (w[x] == 1u || w[x] > kb_hi || ((dmask[j >> 6] >> (j & 63)) & 1ull));
+    my_ch += ch ? 1 : 0;
+  }
+  int tot = 0;
+  int o = wg_scan(my_ch, red, slot, tot);
+  int32_t *dst = blk_idx + ((size_t)i * c.dm.Hkv + h) * k_cap;
+#pragma unroll
+  for (int x = 0; x < kWideM; ++x) {
+    const int j = j0 + x;
+    const bool ch = x < m && j < n &&
+                    (w[x] == 1u || w[x] > kb_hi || ((dmask[j >> 6] >> (j & 63)) & 1ull));
+    if (ch) {
+      if (o < k_cap) {
+        st_dev(&dst[o], j);
+        if (tagd && o < c.dm.kcap) st_dev(&tagd[o], ((unsigned long long)epoch << 32) | (uint32_t)j);
+      }
+      ++o;
+    }
+  }
+  if (tid == 0) {
+    st_dev(&blk_cnt[(size_t)i * c.dm.Hkv + h], kk);
+    st_dev(&c.sc.unit_acc[2 * unit], 0u);  // cleared for the next step
+    st_dev(&c.sc.unit_acc[2 * unit + 1], 0u);
+  }
+}
+
 // Value of lane ^ J within the wave (J = 1, 2, 4, 8 by DPP inside 16-lane
 // rows; 16 and 32 through ds_bpermute).
 // Fast top-k of one unit from the score tiles' lists (no MAW flags, kk <=
@@ -1943,8 +2186,12 @@ __global__ __launch_bounds__(256) void k_select(Ctx c, SeqBatch b, int tiles_x,
   uint32_t *ctr = &c.sc.arrive[((size_t)seq * c.dm.Hkv + h) * 2];
   if (!arrive_last(ctr, (unsigned)n_tiles, &smem_topk.last)) return;
   uint32_t *lrows = reinterpret_cast<uint32_t *>(smem_raw + sizeof(TopkSmem));
-  topk_unit<D, G>(c, i, seq, h, hi, g, q, blk_idx, blk_cnt, k_cap, smem_topk, lrows,
-                  lrows_words, reinterpret_cast<unsigned long long *>(lrows + lrows_words));
+  unsigned long long *dmask = reinterpret_cast<unsigned long long *>(lrows + lrows_words);
+  if (g.n_blk > kTopkRegRows * 64 && g.n_blk <= 256 * kWideM)
+    topk_wide<D, G>(c, i, seq, h, hi, g, q, blk_idx, blk_cnt, k_cap, smem_topk, dmask);
+  else
+    topk_unit<D, G>(c, i, seq, h, hi, g, q, blk_idx, blk_cnt, k_cap, smem_topk, lrows,
+                    lrows_words, dmask);
   if (threadIdx.x == 0) st_dev(ctr, 0u);
 }
 
@@ -2034,10 +2281,15 @@ __global__ __launch_bounds__(256, 2) void k_step(Ctx c, SeqBatch b, int tiles_x,
     // the fast top-k publishes the count itself, right after the entries
     const bool fast_done = fast && topk_fast<D, G>(c, i, seq, h, hi, g, q, blk_idx, blk_cnt, k_cap,
                                                    smem_topk, tagd, &c.sc.rtag[unit], epoch);
-    if (!fast_done)
-      topk_unit<D, G>(c, i, seq, h, hi, g, q, blk_idx, blk_cnt, k_cap, smem_topk, lrows,
-                      lrows_words, reinterpret_cast<unsigned long long *>(lrows + lrows_words),
-                      tagd, epoch);
+    if (!fast_done) {
+      unsigned long long *dmask = reinterpret_cast<unsigned long long *>(lrows + lrows_words);
+      if (g.n_blk > kTopkRegRows * 64 && g.n_blk <= 256 * kWideM)
+        topk_wide<D, G>(c, i, seq, h, hi, g, q, blk_idx, blk_cnt, k_cap, smem_topk, dmask, tagd,
+                        epoch);
+      else
+        topk_unit<D, G>(c, i, seq, h, hi, g, q, blk_idx, blk_cnt, k_cap, smem_topk, lrows,
+                        lrows_words, dmask, tagd, epoch);
+    }
     if (threadIdx.x == 0) {
       // the entries carry their own tags, so the count need not wait for them
       st_dev(ctr, 0u);

@@ -176,21 +176,23 @@ def test_group_sizes(G, Hkv, d):
     harness.assert_parity(harness.run_single_step(w, 13))
 
 
-def test_tied_scores_resolved_exactly():
+@pytest.mark.parametrize("N,fused", [(4096, False), (40000, False), (40000, True)])
+def test_tied_scores_resolved_exactly(N, fused):
     """Coarse integer keys make many block scores exactly equal: every tie at
-    the k-th key goes through the exact re-scoring and the index tie-break."""
-    w = _w(synth.tiny(), N=4096, n_plant=0)
-    log("case: tied scores")
-    x = synth.single_step(w, 3, N=4096)
+    the k-th key goes through the exact re-scoring and the index tie-break
+    (N = 40000: 2500 blocks, the four-wave top-k of long units)."""
+    w = _w(synth.tiny(), N=N, n_plant=0)
+    log("case: tied scores N=%d fused=%s" % (N, fused))
+    x = synth.single_step(w, 3, N=N)
     g = torch.Generator().manual_seed(3)
     K = torch.randint(-1, 2, x["K"].shape, generator=g).to(torch.bfloat16)
-    eng = harness.make_engine(w, 4160)
+    eng = harness.make_engine(w, N + 64)
     try:
         harness.prefill(eng, 0, K.cuda(), x["V"].cuda())
-        gpu = harness.run_gpu_step(eng, 0, [0], x["q"].cuda())
+        gpu = harness.run_gpu_step(eng, 0, [0], x["q"].cuda(), fused=fused)
         Kb, Vb = synth.bits(K), synth.bits(x["V"])
         st = harness.check_units(w, eng, 0, [0], synth.bits(x["q"]), {0: Kb[0]}, {0: Vb[0]},
-                                 {0: 4096}, gpu)
+                                 {0: N}, gpu)
         harness.assert_parity(st)
         assert st["ties"] == 0
     finally:
@@ -316,34 +318,36 @@ def test_pool_exhaustion_enomem():
         eng.close()
 
 
-def test_maw_flag_selection():
+@pytest.mark.parametrize("N,fused", [(8000, False), (48000, False), (48000, True)])
+def test_maw_flag_selection(N, fused):
     """MAW threshold flags rank blocks first (values set through the debug
-    hook; the oracle reads the same fp32 values widened to double)."""
-    w = _w(synth.llama32k(), B=2, N=8000, maw_beta=1.0)
-    log("case: MAW flag selection")
-    x = synth.single_step(w, 3, N=8000)
+    hook; the oracle reads the same fp32 values widened to double).  N =
+    48000: 1500 blocks, the four-wave top-k of long units."""
+    w = _w(synth.llama32k(), B=2, N=N, maw_beta=1.0)
+    log("case: MAW flag selection N=%d fused=%s" % (N, fused))
+    x = synth.single_step(w, 3, N=N)
     K, V, q = x["K"].cuda(), x["V"].cuda(), x["q"].cuda()
-    eng = harness.make_engine(w, 8064)
+    eng = harness.make_engine(w, N + 64)
     try:
         harness.prefill(eng, 0, K, V)
-        nb = 8000 // 32
+        nb = N // 32
         rng = np.random.default_rng(0)
         maw_set, vals_by = {}, {}
         for s in range(2):
             vals = np.zeros(w.Hkv * nb, np.float32)
             # threshold beta*S/|D| = 32/516; put some blocks far above it
             for g in range(w.Hkv):
-                hot = rng.choice(np.arange(1, 230), size=12, replace=False)
+                hot = rng.choice(np.arange(1, nb - 20), size=12, replace=False)
                 vals[g * nb + hot] = 0.5
-                vals[g * nb + rng.choice(np.arange(1, 230), size=5)] = 0.01
+                vals[g * nb + rng.choice(np.arange(1, nb - 20), size=5)] = 0.01
             eng.set_maw(0, s, vals)
             for g in range(w.Hkv):
                 maw_set[(s, g)] = vals[g * nb:(g + 1) * nb].astype(np.float64)
                 vals_by[(s, g)] = maw_set[(s, g)].copy()
-        gpu = harness.run_gpu_step(eng, 0, [0, 1], q)
+        gpu = harness.run_gpu_step(eng, 0, [0, 1], q, fused=fused)
         Kb, Vb = synth.bits(K), synth.bits(V)
         st = harness.check_units(w, eng, 0, [0, 1], synth.bits(q), {0: Kb[0], 1: Kb[1]},
-                                 {0: Vb[0], 1: Vb[1]}, {0: 8000, 1: 8000}, gpu,
+                                 {0: Vb[0], 1: Vb[1]}, {0: N, 1: N}, gpu,
                                  maw_state=maw_set)
         harness.assert_parity(st)
         for s in range(2):
