@@ -2038,10 +2038,16 @@ __device__ __attribute__((always_inline)) void fuse_unit(const Ctx &c, int i, in
           a = fmaf(wgt, wgt != 0.0f ? ov[rr][u] : 0.0f, a);
         }
       }
-      for (int u = kFusePre; u < n_slots; ++u) {
-        const float wgt = sm.w[gg][u];
-        const float v = ld_dev(&o_part[(hb + u) * D + ch]);
-        a = fmaf(wgt, wgt != 0.0f ? v : 0.0f, a);
+      for (int u0 = kFusePre; u0 < n_slots; u0 += 8) {  // the rest, 8 loads in flight
+        float v[8];
+#pragma unroll
+        for (int t = 0; t < 8; ++t) v[t] = u0 + t < n_slots ? ld_dev(&o_part[(hb + u0 + t) * D + ch]) : 0.0f;
+#pragma unroll
+        for (int t = 0; t < 8; ++t)
+          if (u0 + t < n_slots) {
+            const float wgt = sm.w[gg][u0 + t];
+            a = fmaf(wgt, wgt != 0.0f ? v[t] : 0.0f, a);
+          }
       }
       o[((size_t)i * c.dm.Hq + qh0 + gg) * D + ch] = a;
     }
