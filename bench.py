@@ -64,6 +64,9 @@ def parse():
     ap.add_argument("--cpu-baseline", type=int, default=1)
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
     ap.add_argument("--trials", type=int, default=3)
+    ap.add_argument("--workload", choices=["llama32k", "qwen128k", "loop32"], default="llama32k",
+                    help="llama32k: the headline step; qwen128k (per-head budgets and block "
+                         "sizes, N=131072) and loop32 (B=16, N=65536, MAW flags on) are variants")
     ap.add_argument("--streaming-heads", type=int, default=0,
                     help="give the first K KV heads budget 0 (streaming heads: sinks and "
                          "recent window only); a variant of the workload, not the headline")
@@ -178,7 +181,9 @@ def main():
 
     torch.cuda.set_device(0)
     dev = torch.device("cuda:0")
-    w = synth.llama32k()
+    w = {"llama32k": synth.llama32k, "qwen128k": lambda: synth.qwen128k(0),
+         "loop32": synth.loop32}[args.workload]()
+    maw_beta = w.maw_beta  # MAW flags on for loop32 only
     if args.streaming_heads:
         K_s = min(args.streaming_heads, w.Hkv)
         w = dataclasses.replace(w, budget_ppm=[0] * K_s + list(w.budget_ppm[K_s:]))
@@ -191,13 +196,18 @@ def main():
                        num_pages=w.B * ((max_len + 15) // 16), max_seq_len=max_len,
                        sink_tokens=w.n_sink, recent_window=w.window,
                        block_size=w.block_size, budget_ppm=w.budget_ppm,
-                       maw_decay=0.95, maw_beta=0.0,
+                       maw_decay=0.95, maw_beta=maw_beta,
                        page_shuffle_seed=12345, stream=stream)
     seqs = list(range(w.B))
     qs = []
     t0 = time.time()
     for layer in range(L):
-        x = synth.single_step(w, args.seed * 100 + layer, device=dev, N=w.N)
+        if args.workload == "loop32":  # a planted direction per (layer, seq, KV head)
+            dirs = synth.directions(w, args.seed, layer, 1, device=dev)
+            Kf, Vf, _ = synth.prefill_with_directions(w, args.seed, layer, w.N, dirs, device=dev)
+            x = {"K": Kf, "V": Vf, "q": synth.loop_query(w, args.seed, layer, 0, dirs, device=dev)}
+        else:
+            x = synth.single_step(w, args.seed * 100 + layer, device=dev, N=w.N)
         K, V = x["K"][:, :N0].contiguous(), x["V"][:, :N0].contiguous()
         eng.append_kv(layer, seqs, [N0] * w.B, K.view(-1, w.Hkv, w.d), V.view(-1, w.Hkv, w.d))
         qs.append(x["q"].contiguous())
@@ -205,6 +215,7 @@ def main():
             K0 = x["K"]
             V0 = x["V"]
         del x, K, V
+        torch.cuda.empty_cache()
     torch.cuda.synchronize()
     setup_s = time.time() - t0
     g = torch.Generator(device=dev).manual_seed(args.seed)
@@ -285,8 +296,10 @@ def main():
         "vs_baseline": None,
         "dtype": "bf16",
         "data": "synthetic",
-        "config": {"workload": "llama32k: B=8, Hq=32, Hkv=8, d=128, N=32768 (+1 per visit), "
-                               "S=32, budget 5%%, 4 sinks + 512 recent, %d layer instances" % L
+        "config": {"workload": "%s: B=%d, Hq=%d, Hkv=%d, d=%d, N=%d (+1 per visit), S=%s, "
+                               "budget ppm %s, %d sinks + %d recent, MAW flags %s, %d layer instances"
+                               % (w.name, w.B, w.Hq, w.Hkv, w.d, w.N, w.block_size, w.budget_ppm,
+                                  w.n_sink, w.window, "on" if maw_beta > 0 else "off", L)
                                + ("; KV heads 0-%d streaming (budget 0)" % (args.streaming_heads - 1)
                                   if args.streaming_heads else ""),
                    "global_batch": w.B, "seq_len": w.N, "parallelism": "none (1 GPU)",
@@ -297,7 +310,9 @@ def main():
         "kernel_ms": {"k_step": t_step, "timed_launches": n_inst},
         "roofline": {"kernel": "k_step", "bound": "hbm", "achieved": kstep_gbs,
                      "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": kstep_gbs / HBM_PEAK_GBS,
-                     "traffic": None if args.streaming_heads else measured_traffic(),
+                     # the committed counter summary is the headline workload's
+                     "traffic": measured_traffic() if args.workload == "llama32k"
+                     and not args.streaming_heads else None,
                      "algorithmic_bytes_per_launch": kstep_bytes},
         "trials_ms": trial_ms,
         "setup_s": setup_s,
@@ -311,8 +326,8 @@ def main():
 
 def cpu_baseline(w, K, V, q, budget_s):
     """The CPU oracle (unchanged) on a bounded sample of the same workload:
-    whole (sequence, KV head) units of one decode step at N=32767, run one
-    per thread until about budget_s seconds have passed."""
+    whole (sequence, KV head) units of one decode step at N - 1 tokens, run
+    one per thread until about budget_s seconds have passed."""
     import concurrent.futures as cf
     import synth
     import oracle
@@ -326,7 +341,9 @@ def cpu_baseline(w, K, V, q, budget_s):
         b, g = u
         oracle.unit_step(qb[b, g * G:(g + 1) * G], np.ascontiguousarray(Kb[b, :, g]),
                          np.ascontiguousarray(Vb[b, :, g]), N, w.block_size[g], w.n_sink,
-                         w.window, w.budget_ppm[g])
+                         w.window, w.budget_ppm[g],
+                         maw=np.zeros((N + w.block_size[g] - 1) // w.block_size[g]) if w.maw_beta > 0 else None,
+                         beta=w.maw_beta)
         return 1
 
     done = 0
@@ -339,8 +356,8 @@ def cpu_baseline(w, K, V, q, budget_s):
     qheads = done * G
     return {"value": qheads / dt, "unit": "query-heads/s", "cores": threads,
             "kind": "oracle",
-            "sample": "%d (sequence, KV head) units of the llama32k step (N=%d, G=%d), "
-                      "summaries+select+attend per unit, %.1f s" % (done, N, G, dt)}
+            "sample": "%d (sequence, KV head) units of the %s step (N=%d, G=%d), "
+                      "summaries+select+attend per unit, %.1f s" % (done, w.name, N, G, dt)}
 
 
 if __name__ == "__main__":
