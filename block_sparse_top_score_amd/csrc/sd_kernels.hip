@@ -159,6 +159,21 @@ __device__ __forceinline__ uint32_t order_key(float u) {
 // ---------------------------------------------------------------------------
 // Shared memory of the roles (one launch may host several roles).
 constexpr int kTileList = 64;  // blocks a score tile lists for the fast top-k, at most
+// The four-wave top-k ranks units of (kTopkRegRows * 64, 256 * kWideM]
+// blocks; its thread t holds blocks [t m, t m + m), m = ceil(n / 256).
+constexpr int kWideM = 40;  // blocks per thread: units up to 10240 blocks
+static_assert(kWideM <= 64, "a thread's blocks span at most two mask words");
+__device__ __forceinline__ bool wide_unit(int n_blk) {
+  return n_blk > kTopkRegRows * 64 && n_blk <= 256 * kWideM;
+}
+// Slot of block blk's key in its unit's key array: the block index, except
+// in units the four-wave top-k ranks, where thread t's blocks sit at t,
+// t + 256, ..., so that its loads are coalesced.
+__device__ __forceinline__ int key_slot(int blk, int n_blk) {
+  if (!wide_unit(n_blk)) return blk;
+  const int m = cdiv(n_blk, 256), t = blk / m;
+  return (blk - t * m) * 256 + t;
+}
 struct TopkSmem {
   int32_t ulist[kTopkUnc];  // uncertain blocks of the top-k, in index order
   uint32_t ukey[kTopkUnc];  // their exact keys
@@ -638,7 +653,7 @@ __device__ __attribute__((always_inline)) bool score_tile(const Ctx &c, int i, i
     const int blk = base + gi * 16 + r16;
     unsigned long long kv = 0u;
     if (lgrp == 0 && blk < g.n_blk) {
-      const size_t ko = ((size_t)seq * c.dm.Hkv + h) * c.dm.key_stride + blk;
+      const size_t ko = ((size_t)seq * c.dm.Hkv + h) * c.dm.key_stride + key_slot(blk, g.n_blk);
       const bool cand = is_candidate(g, blk);
       kv = cand ? order_key(A) : 0u;
       if (cand) emax = fmaxf(emax, score_eps(E, A));
@@ -1112,15 +1127,16 @@ __device__ __forceinline__ int wg_scan(int x, uint32_t *red, int &slot, int &tot
 // ceil(n / 256) <= kWideM, in registers.  The k-th largest word is bracketed
 // by bisection with workgroup counts until the bracket is within eps; the
 // band is listed in index order by a workgroup scan, re-scored exactly (lane
-// quads of all waves) and ranked; the chosen blocks are written in ascending
-// order by a second scan.
-constexpr int kWideM = 40;  // blocks per thread: units up to 10240 blocks
+// quads of all waves) and ranked; the chosen blocks are put in ascending
+// order by a second scan, through LDS when they fit so that the stores are
+// coalesced.
 template <int D, int G>
 __device__ __attribute__((always_inline)) void topk_wide(const Ctx &c, int i, int seq, int h, const HeadInfo &hi,
                           const UG &g, const uint16_t *__restrict__ q,
                           int32_t *__restrict__ blk_idx, int32_t *__restrict__ blk_cnt,
                           int k_cap, TopkSmem &sm,
                           unsigned long long *dmask /* LDS, one word per row */,
+                          int32_t *stage /* LDS, stage_words entries */, int stage_words,
                           unsigned long long *tagd = nullptr, uint32_t epoch = 0) {
   const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
   const int n = g.n_blk, rows = cdiv(n, 64);
@@ -1142,7 +1158,7 @@ __device__ __attribute__((always_inline)) void topk_wide(const Ctx &c, int i, in
   const uint32_t f_raw = ld_dev(&c.sc.unit_acc[2 * unit + 1]);
   unsigned long long kv[kWideM];
 #pragma unroll
-  for (int x = 0; x < kWideM; ++x) kv[x] = (x < m && j0 + x < n) ? ld_dev(&gkf[j0 + x]) : 0ull;
+  for (int x = 0; x < kWideM; ++x) kv[x] = (x < m && j0 + x < n) ? ld_dev(&gkf[x * 256 + tid]) : 0ull;
   constexpr int QT = (G * D + 255) / 256;
   const uint16_t *qg = q + ((size_t)i * c.dm.Hq + (size_t)h * G) * D;
   uint16_t qv[QT];
@@ -1155,13 +1171,19 @@ __device__ __attribute__((always_inline)) void topk_wide(const Ctx &c, int i, in
   const bool take_flagged = F < kk;
   const uint32_t want = take_flagged ? 0u : 1u;
   const int k_sub = take_flagged ? kk - F : kk;
+  // the thread's blocks as bit masks (bit x: block j0 + x), so that the
+  // single passes below are short loops over set bits rather than unrolled
+  // code over all kWideM words: onem = always chosen (word 1), gtm = above
+  // the band, bandm = in the band
   uint32_t w[kWideM];
   uint32_t lo = 0xffffffffu, hi_k = 0u;
+  unsigned long long onem = 0ull, gtm = 0ull, bandm = 0ull;
 #pragma unroll
   for (int x = 0; x < kWideM; ++x) {
     const uint32_t key = (uint32_t)kv[x];
     const uint32_t fl = use_flag ? (uint32_t)(kv[x] >> 32) & 1u : 0u;
     w[x] = key == 0u ? 0u : (fl == want ? key : (take_flagged ? 1u : 0u));
+    onem |= w[x] == 1u ? (1ull << x) : 0ull;
     if (w[x] >= 2u) {
       lo = min(lo, w[x]);
       hi_k = max(hi_k, w[x]);
@@ -1199,18 +1221,16 @@ __device__ __attribute__((always_inline)) void topk_wide(const Ctx &c, int i, in
     kb_hi = order_key(__double2float_rd((double)key_to_float(b) + 2.0 * eps));
     kb_lo = order_key(__double2float_ru((double)key_to_float(a) - 2.0 * eps));
     // 2. the band in index order; the sure ones counted
-    int my_unc = 0, my_in = 0;
 #pragma unroll
     for (int x = 0; x < kWideM; ++x) {
-      my_unc += (w[x] >= kb_lo && w[x] <= kb_hi) ? 1 : 0;
-      my_in += w[x] > kb_hi ? 1 : 0;
+      bandm |= (w[x] >= kb_lo && w[x] <= kb_hi) ? (1ull << x) : 0ull;
+      gtm |= w[x] > kb_hi ? (1ull << x) : 0ull;
     }
     int n_unc = 0;
-    int p = wg_scan(my_unc, red, slot, n_unc);
-    const int n_in = wg_sum(my_in, red, slot);
-#pragma unroll
-    for (int x = 0; x < kWideM; ++x)
-      if (w[x] >= kb_lo && w[x] <= kb_hi) ul_st(p++, j0 + x);
+    int p = wg_scan(__popcll(bandm), red, slot, n_unc);
+    const int n_in = wg_sum(__popcll(gtm), red, slot);
+    for (unsigned long long bm = bandm; bm != 0ull; bm &= bm - 1ull)
+      ul_st(p++, j0 + (int)__builtin_ctzll(bm));
     wait_vmem();
     __syncthreads();
     const int kr2 = k_sub - n_in;  // >= 1: T_a's own block is in the band
@@ -1286,29 +1306,36 @@ __device__ __attribute__((always_inline)) void topk_wide(const Ctx &c, int i, in
   }
   __syncthreads();
 
-  // 5. ordered compaction: the thread's chosen blocks at their places
-  int my_ch = 0;
-#pragma unroll
-  for (int x = 0; x < kWideM; ++x) {
-    const int j = j0 + x;
-    const bool ch = x < m && j < n &&
-                    (w[x] == 1u || w[x] > kb_hi || ((dmask[j >> 6] >> (j & 63)) & 1ull));
-    my_ch += ch ? 1 : 0;
-  }
+  // 5. ordered compaction: the thread's chosen blocks at their places.  Its
+  // m <= 64 blocks touch at most two words of the band's mask, read once.
+  const int r0 = j0 >> 6, sh = j0 & 63;
+  const unsigned long long dm0 = r0 < rows ? dmask[r0] : 0ull;
+  const unsigned long long dm1 = r0 + 1 < rows ? dmask[r0 + 1] : 0ull;
+  const unsigned long long dmb = sh == 0 ? dm0 : ((dm0 >> sh) | (dm1 << (64 - sh)));
+  const int nv = max(0, min(m, n - j0));  // the thread's blocks that exist
+  const unsigned long long validm = nv >= 64 ? ~0ull : ((1ull << nv) - 1ull);
+  const unsigned long long chm = (onem | gtm | dmb) & validm;  // bit x: block j0 + x chosen
+  const int my_ch = __popcll(chm);
   int tot = 0;
   int o = wg_scan(my_ch, red, slot, tot);
   int32_t *dst = blk_idx + ((size_t)i * c.dm.Hkv + h) * k_cap;
-#pragma unroll
-  for (int x = 0; x < kWideM; ++x) {
-    const int j = j0 + x;
-    const bool ch = x < m && j < n &&
-                    (w[x] == 1u || w[x] > kb_hi || ((dmask[j >> 6] >> (j & 63)) & 1ull));
-    if (ch) {
-      if (o < k_cap) {
-        st_dev(&dst[o], j);
-        if (tagd && o < c.dm.kcap) st_dev(&tagd[o], ((unsigned long long)epoch << 32) | (uint32_t)j);
-      }
-      ++o;
+  const bool staged = tot <= stage_words;  // the same for every thread
+  for (unsigned long long cm = chm; cm != 0ull; cm &= cm - 1ull) {
+    const int j = j0 + (int)__builtin_ctzll(cm);
+    if (staged) {
+      stage[o] = j;
+    } else if (o < k_cap) {
+      st_dev(&dst[o], j);
+      if (tagd && o < c.dm.kcap) st_dev(&tagd[o], ((unsigned long long)epoch << 32) | (uint32_t)j);
+    }
+    ++o;
+  }
+  if (staged) {
+    __syncthreads();
+    for (int p = tid; p < tot; p += 256) {
+      const int j = stage[p];
+      if (p < k_cap) st_dev(&dst[p], j);
+      if (tagd && p < c.dm.kcap) st_dev(&tagd[p], ((unsigned long long)epoch << 32) | (uint32_t)j);
     }
   }
   if (tid == 0) {
@@ -1522,6 +1549,15 @@ __device__ __forceinline__ DenseList dense_list(const UG &g) {
   d.wp = g.wlo < g.N ? max(d.sp, g.wlo / kPage) : d.np;
   d.n = d.sp + (d.np - d.wp);
   return d;
+}
+// Attention parts a unit uses out of a launch's P: one per about kPartPages
+// of its attended pages (dense pages, then k blocks' pages), at least one.
+// Both call forms take the same number, so they give the same bits; a unit
+// with fewer pages than the launch's longest does not hold workgroups that
+// have nothing to do.
+__device__ __forceinline__ int unit_parts(const UG &g, int P) {
+  const int pages = dense_list(g).n + g.kk * (g.S / kPage);
+  return min(P, max(1, cdiv(pages, kPartPages)));
 }
 __device__ __forceinline__ int dense_page(const DenseList &d, int e) {
   return e < d.sp ? e : d.wp + (e - d.sp);
@@ -1916,7 +1952,7 @@ __device__ __forceinline__ float fast_exp(float x) {
 __device__ __forceinline__ float fast_log(float x) {
   return __builtin_amdgcn_logf(x) * 0.69314718055994531f;
 }
-constexpr int kFusePre = 16;  // partial slots whose O values are preloaded
+constexpr int kFusePre = 8;  // partial slots whose O values are preloaded
 constexpr int kFusePgPre = 2;  // page-mass entries per thread preloaded
 
 template <int D, int G>
@@ -1963,17 +1999,23 @@ __device__ __attribute__((always_inline)) void fuse_unit(const Ctx &c, int i, in
     l1[r] = (on && wv + 4 < G) ? ld_dev(&lse_part[((size_t)i * c.dm.Hq + qh0 + wv + 4) * p_cap + u])
                                : -INFINITY;
   }
-  constexpr int NP = (G * D + 255) / 256;
-  float ov[NP][kFusePre];
+  // O: thread tid < G D / 4 sums 4 channels of one head, each slot's read as
+  // two 8-byte loads (the partials are 16-byte aligned)
+  constexpr int NO = G * D / 4;
+  static_assert(NO <= 256, "one thread per 4 output channels");
+  const bool o_on = tid < NO;
+  const int ogg = (4 * min(tid, NO - 1)) / D, och = 4 * min(tid, NO - 1) - ogg * D;
+  const unsigned long long *op2 = reinterpret_cast<const unsigned long long *>(
+      o_part + ((size_t)i * c.dm.Hq + qh0 + ogg) * p_cap * D + och);
+  auto ld_o = [&](int u, bool on) -> float4 {
+    if (!on) return make_float4(0.0f, 0.0f, 0.0f, 0.0f);
+    const unsigned long long a = ld_dev(op2 + (size_t)u * (D / 2)), b = ld_dev(op2 + (size_t)u * (D / 2) + 1);
+    return make_float4(__uint_as_float((uint32_t)a), __uint_as_float((uint32_t)(a >> 32)),
+                       __uint_as_float((uint32_t)b), __uint_as_float((uint32_t)(b >> 32)));
+  };
+  float4 ov[kFusePre];
 #pragma unroll
-  for (int rr = 0; rr < NP; ++rr) {
-    const int x = tid + 256 * rr;
-    const int gg = x / D, ch = x - gg * D;
-    const size_t hb = ((size_t)i * c.dm.Hq + qh0 + min(gg, G - 1)) * p_cap;
-#pragma unroll
-    for (int u = 0; u < kFusePre; ++u)
-      ov[rr][u] = (x < G * D && u < n_slots) ? ld_dev(&o_part[(hb + u) * D + ch]) : 0.0f;
-  }
+  for (int u = 0; u < kFusePre; ++u) ov[u] = ld_o(u, o_on && u < n_slots);
   float lmv[kFusePgPre][G];
 #pragma unroll
   for (int t = 0; t < kFusePgPre; ++t) {
@@ -1982,11 +2024,13 @@ __device__ __attribute__((always_inline)) void fuse_unit(const Ctx &c, int i, in
     for (int gg = 0; gg < G; ++gg)
       lmv[t][gg] = x < n_pg ? ld_dev(&lmb[(size_t)gg * c.dm.lm_cap + pg_slot(x)]) : -INFINITY;
   }
+  // the selection: a plain list here; a tagged one (whose reads wait for
+  // their tags) only its first 256 entries here, the rest after the O sums
   int selv[kFuseSelLds / 256];
 #pragma unroll
   for (int t = 0; t < kFuseSelLds / 256; ++t) {
     const int x = tid + 256 * t;
-    selv[t] = (sel_lds && x < cnt) ? sel_ld(x) : 0;
+    selv[t] = (sel_lds && x < cnt && (t == 0 || !seltag)) ? sel_ld(x) : 0;
   }
 
   // ---- per-head lse and slot weights ----------------------------------------
@@ -2017,43 +2061,59 @@ __device__ __attribute__((always_inline)) void fuse_unit(const Ctx &c, int i, in
 #pragma unroll
   for (int t = 0; t < kFuseSelLds / 256; ++t) {
     const int x = tid + 256 * t;
-    if (sel_lds && x < cnt) sm.sel[x] = selv[t];
+    if (sel_lds && x < cnt && (t == 0 || !seltag)) sm.sel[x] = selv[t];
   }
   const bool dsel_lds = with_maw && g.n_dt <= kFuseDense;
   if (dsel_lds)
     for (int x = tid; x < g.n_dt; x += 256) sm.dsel[x] = -1;
   __syncthreads();
-  // ---- O = sum_u w_u O_u (zero weights select 0) ------------------------------
+  // ---- O = sum_u w_u O_u (zero weights select 0), each channel in slot order
+  float4 acc = make_float4(0.0f, 0.0f, 0.0f, 0.0f);
+  auto add_slot = [&](int u, const float4 &v) {
+    const float wgt = sm.w[ogg][u];
+    const bool z = wgt == 0.0f;
+    acc.x = fmaf(wgt, z ? 0.0f : v.x, acc.x);
+    acc.y = fmaf(wgt, z ? 0.0f : v.y, acc.y);
+    acc.z = fmaf(wgt, z ? 0.0f : v.z, acc.z);
+    acc.w = fmaf(wgt, z ? 0.0f : v.w, acc.w);
+  };
 #pragma unroll
-  for (int rr = 0; rr < NP; ++rr) {
-    const int x = tid + 256 * rr;
-    if (x < G * D) {
-      const int gg = x / D, ch = x - gg * D;
-      const size_t hb = ((size_t)i * c.dm.Hq + qh0 + gg) * p_cap;
-      float a = 0.0f;
+  for (int u = 0; u < kFusePre; ++u)
+    if (u < n_slots) add_slot(u, ov[u]);
+  for (int u0 = kFusePre; u0 < n_slots; u0 += 8) {  // the rest, 8 slots in flight
+    float4 v[8];
 #pragma unroll
-      for (int u = 0; u < kFusePre; ++u) {
-        if (u < n_slots) {
-          const float wgt = sm.w[gg][u];
-          a = fmaf(wgt, wgt != 0.0f ? ov[rr][u] : 0.0f, a);
-        }
-      }
-      for (int u0 = kFusePre; u0 < n_slots; u0 += 8) {  // the rest, 8 loads in flight
-        float v[8];
+    for (int t = 0; t < 8; ++t) v[t] = ld_o(u0 + t, o_on && u0 + t < n_slots);
 #pragma unroll
-        for (int t = 0; t < 8; ++t) v[t] = u0 + t < n_slots ? ld_dev(&o_part[(hb + u0 + t) * D + ch]) : 0.0f;
-#pragma unroll
-        for (int t = 0; t < 8; ++t)
-          if (u0 + t < n_slots) {
-            const float wgt = sm.w[gg][u0 + t];
-            a = fmaf(wgt, wgt != 0.0f ? v[t] : 0.0f, a);
-          }
-      }
-      o[((size_t)i * c.dm.Hq + qh0 + gg) * D + ch] = a;
-    }
+    for (int t = 0; t < 8; ++t)
+      if (u0 + t < n_slots) add_slot(u0 + t, v[t]);
+  }
+  if (o_on) {
+    float *od = o + ((size_t)i * c.dm.Hq + qh0 + ogg) * D + och;
+    od[0] = acc.x;
+    od[1] = acc.y;
+    od[2] = acc.z;
+    od[3] = acc.w;
   }
   if (tid < G) lse[(size_t)i * c.dm.Hq + qh0 + tid] = sm.lse[tid];
   if (!with_maw) return;
+  // the rest of a tagged selection: every load in flight at once, then a
+  // bounded re-read of any entry whose tag is not yet this step's (each
+  // thread reads back only the entries it writes until the barrier below)
+  if (seltag && sel_lds)
+    for (int x0 = tid + 256; x0 < cnt; x0 += 4 * 256) {
+      unsigned long long e[4];
+#pragma unroll
+      for (int t = 0; t < 4; ++t) {
+        const int x = x0 + 256 * t;
+        e[t] = x < cnt ? ld_dev(&seltag[x]) : ((unsigned long long)epoch << 32);
+      }
+#pragma unroll
+      for (int t = 0; t < 4; ++t) {
+        const int x = x0 + 256 * t;
+        if (x < cnt) sm.sel[x] = (uint32_t)(e[t] >> 32) == epoch ? (int)(uint32_t)e[t] : sel_ld(x);
+      }
+    }
 
   // ---- MAW -------------------------------------------------------------------
   // softmax mass of every attended page summed over the heads, into LDS
@@ -2078,7 +2138,19 @@ __device__ __attribute__((always_inline)) void fuse_unit(const Ctx &c, int i, in
     const int x = tid + 256 * t;
     if (x < n_pg_lds) sm.pm[x] = page_mass(lmv[t]);
   }
-  for (int x = tid + 256 * kFusePgPre; x < n_pg_lds; x += 256) sm.pm[x] = page_mass_at(x);
+  for (int x0 = tid + 256 * kFusePgPre; x0 < n_pg_lds; x0 += 2 * 256) {
+    float lm[2][G];
+#pragma unroll
+    for (int u = 0; u < 2; ++u) {
+      const int x = x0 + 256 * u;
+#pragma unroll
+      for (int gg = 0; gg < G; ++gg)
+        lm[u][gg] = x < n_pg_lds ? ld_dev(&lmb[(size_t)gg * c.dm.lm_cap + pg_slot(x)]) : -INFINITY;
+    }
+#pragma unroll
+    for (int u = 0; u < 2; ++u)
+      if (x0 + 256 * u < n_pg_lds) sm.pm[x0 + 256 * u] = page_mass(lm[u]);
+  }
   // selection index of each selected block that touches dense tokens
   if (dsel_lds && sel_lds)
     for (int j = tid; j < cnt; j += 256) {
@@ -2193,17 +2265,18 @@ __global__ __launch_bounds__(256) void k_select(Ctx c, SeqBatch b, int tiles_x,
   if (!arrive_last(ctr, (unsigned)n_tiles, &smem_topk.last)) return;
   uint32_t *lrows = reinterpret_cast<uint32_t *>(smem_raw + sizeof(TopkSmem));
   unsigned long long *dmask = reinterpret_cast<unsigned long long *>(lrows + lrows_words);
-  if (g.n_blk > kTopkRegRows * 64 && g.n_blk <= 256 * kWideM)
-    topk_wide<D, G>(c, i, seq, h, hi, g, q, blk_idx, blk_cnt, k_cap, smem_topk, dmask);
+  if (wide_unit(g.n_blk))
+    topk_wide<D, G>(c, i, seq, h, hi, g, q, blk_idx, blk_cnt, k_cap, smem_topk, dmask,
+                    reinterpret_cast<int32_t *>(lrows), lrows_words);
   else
     topk_unit<D, G>(c, i, seq, h, hi, g, q, blk_idx, blk_cnt, k_cap, smem_topk, lrows,
                     lrows_words, dmask);
   if (threadIdx.x == 0) st_dev(ctr, 0u);
 }
 
-// attend, separate-call form: P workgroups per unit, one partial each; part
-// 0 also keeps a copy of the selection for the fusion call and empties the
-// slots [P, p_cap).
+// attend, separate-call form: P workgroups per unit, of which the unit's
+// parts (unit_parts) write one partial each; part 0 also keeps a copy of the
+// selection for the fusion call and empties the other slots up to p_cap.
 template <int D, int G>
 __global__ __launch_bounds__(256, 2) void k_attend(Ctx c, SeqBatch b, int P,
                                                    const uint16_t *__restrict__ q,
@@ -2218,6 +2291,8 @@ __global__ __launch_bounds__(256, 2) void k_attend(Ctx c, SeqBatch b, int P,
   const HeadInfo hi = c.heads[h];
   const int seq = b.seq[i];
   const UG g = unit_geom(b.len[i], hi, c.dm);
+  const int PU = unit_parts(g, P);
+  if (part >= PU) return;
   const size_t unit = (size_t)seq * c.dm.Hkv + h;
   SelIn si;
   si.blk = blk_idx + ((size_t)i * c.dm.Hkv + h) * k_cap;
@@ -2225,18 +2300,19 @@ __global__ __launch_bounds__(256, 2) void k_attend(Ctx c, SeqBatch b, int P,
   if (part == 0) {
     for (int j = threadIdx.x; j < si.cnt; j += 256) st_dev(&c.sc.usel[unit * c.dm.kcap + j], si.blk[j]);
     if (threadIdx.x == 0) st_dev(&c.sc.ucnt[unit], si.cnt);
-    empty_slots<D, G>(c, i, h, P, p_cap, o_part, lse_part);
+    empty_slots<D, G>(c, i, h, PU, p_cap, o_part, lse_part);
   }
-  attend_part<D, G>(c, i, seq, h, g, part, P, q, si, o_part, lse_part, p_cap, sm, nullptr,
+  attend_part<D, G>(c, i, seq, h, g, part, PU, q, si, o_part, lse_part, p_cap, sm, nullptr,
                     &s_cnt);
 }
 
 // One decode step in one launch.  Workgroups by index: score tiles (the last
 // of a unit runs its top-k and publishes the selection, tagged with the step
-// number), then P attention parts per unit.  A part streams its dense pages
-// once the unit's score tiles are done, then waits for the selection and
-// streams its selected pages; the last part of a unit to finish fuses the
-// partials and updates MAW.  Workgroups start in index order on each XCD and
+// number), then P attention parts per unit (a unit uses unit_parts of them,
+// the rest exit at once).  A part streams its dense pages once the unit's
+// score tiles are done, then waits for the selection and streams its
+// selected pages; the last part of a unit to finish fuses the partials and
+// updates MAW.  Workgroups start in index order on each XCD and
 // every wait is on a score tile, which never waits, so no wait is on a
 // workgroup that cannot start; each wait is also bounded in time (after
 // kWaitTicks it gives up and raises the error flag).
@@ -2289,9 +2365,9 @@ __global__ __launch_bounds__(256, 2) void k_step(Ctx c, SeqBatch b, int tiles_x,
                                                    smem_topk, tagd, &c.sc.rtag[unit], epoch);
     if (!fast_done) {
       unsigned long long *dmask = reinterpret_cast<unsigned long long *>(lrows + lrows_words);
-      if (g.n_blk > kTopkRegRows * 64 && g.n_blk <= 256 * kWideM)
-        topk_wide<D, G>(c, i, seq, h, hi, g, q, blk_idx, blk_cnt, k_cap, smem_topk, dmask, tagd,
-                        epoch);
+      if (wide_unit(g.n_blk))
+        topk_wide<D, G>(c, i, seq, h, hi, g, q, blk_idx, blk_cnt, k_cap, smem_topk, dmask,
+                        reinterpret_cast<int32_t *>(lrows), lrows_words, tagd, epoch);
       else
         topk_unit<D, G>(c, i, seq, h, hi, g, q, blk_idx, blk_cnt, k_cap, smem_topk, lrows,
                         lrows_words, dmask, tagd, epoch);
@@ -2306,6 +2382,8 @@ __global__ __launch_bounds__(256, 2) void k_step(Ctx c, SeqBatch b, int tiles_x,
     return;
   }
   const UG g = unit_geom(N, hi, c.dm);
+  const int PU = unit_parts(g, P);
+  if (idx >= PU) return;
   // attention part idx of the unit; the sequence's page table is copied to LDS
   // (one batch of loads) for the selected pages
   const int32_t *ptl = nullptr;
@@ -2327,7 +2405,7 @@ __global__ __launch_bounds__(256, 2) void k_step(Ctx c, SeqBatch b, int tiles_x,
     }
     ptl = t;  // visible to all waves after the barrier of the selection wait
   }
-  if (idx == 0) empty_slots<D, G>(c, i, h, P, p_cap, o_part, lse_part);
+  if (idx == 0) empty_slots<D, G>(c, i, h, PU, p_cap, o_part, lse_part);
   // a unit that selects nothing has no score tiles: its parts take the dense
   // pages only, part 0 writes the count, the fusion decays every block's MAW
   const bool no_sel = selects_nothing(hi, N, c.dm);
@@ -2337,21 +2415,21 @@ __global__ __launch_bounds__(256, 2) void k_step(Ctx c, SeqBatch b, int tiles_x,
   si.rtag = no_sel ? nullptr : &c.sc.rtag[unit];
   si.cnt = 0;
   si.epoch = epoch;
-  attend_part<D, G>(c, i, seq, h, g, idx, P, q, si, o_part, lse_part, p_cap, smem_att, ptl,
+  attend_part<D, G>(c, i, seq, h, g, idx, PU, q, si, o_part, lse_part, p_cap, smem_att, ptl,
                     &s_cnt);
   uint32_t *fctr = &c.sc.arrive[unit * 2 + 1];
-  if (!arrive_last(fctr, (unsigned)P, &s_flag)) return;
+  if (!arrive_last(fctr, (unsigned)PU, &s_flag)) return;
   __builtin_amdgcn_s_setprio(3);
   // this step's count, seen by every part
   const int cnt = no_sel ? 0 : (int)(uint32_t)ld_dev(&c.sc.rtag[unit]);
-  fuse_unit<D, G>(c, i, seq, h, hi, g, no_sel ? kMawFull : kMawAdd, P, nullptr, cnt, o_part,
+  fuse_unit<D, G>(c, i, seq, h, hi, g, no_sel ? kMawFull : kMawAdd, PU, nullptr, cnt, o_part,
                   lse_part, p_cap, o, lse, smem_fuse, c.sc.seltag + unit * c.dm.kcap, epoch);
   if (threadIdx.x == 0) st_dev(fctr, 0u);
 }
 
-// fuse, separate-call form: one workgroup per unit over P partial slots (layer
-// call: selection and page masses from the attend call) or over every slot
-// of p_cap (pure fusion).
+// fuse, separate-call form: one workgroup per unit over the partial slots of
+// its parts out of the attend call's P (layer call: selection and page masses
+// from the attend call) or over every slot of p_cap (pure fusion).
 template <int D, int G>
 __global__ __launch_bounds__(256) void k_fuse(Ctx c, SeqBatch b, int with_maw, int P,
                                               const float *__restrict__ o_part,
@@ -2363,7 +2441,7 @@ __global__ __launch_bounds__(256) void k_fuse(Ctx c, SeqBatch b, int with_maw, i
   if (with_maw) {
     const UG g = unit_geom(b.len[i], hi, c.dm);
     const size_t unit = (size_t)b.seq[i] * c.dm.Hkv + h;
-    fuse_unit<D, G>(c, i, b.seq[i], h, hi, g, kMawFull, P, c.sc.usel + unit * c.dm.kcap,
+    fuse_unit<D, G>(c, i, b.seq[i], h, hi, g, kMawFull, unit_parts(g, P), c.sc.usel + unit * c.dm.kcap,
                     ld_dev(&c.sc.ucnt[unit]), o_part, lse_part, p_cap, o, lse, sm);
   } else {
     UG g{};

@@ -7,6 +7,7 @@
 #include <algorithm>
 #include <cmath>
 #include <cstdarg>
+#include <cstdint>
 #include <cstdio>
 #include <cstring>
 #include <map>
@@ -284,7 +285,9 @@ sd_status sparse_decode_init(const sd_config *cfg, sd_ctx **out) {
   c->dims.scale_log2 = (float)((double)scale * 1.4426950408889634);
   c->dims.maw_decay = cfg->maw_decay > 0.0f ? cfg->maw_decay : 0.95f;
   c->dims.maw_beta = cfg->maw_beta;
-  key_stride = (int)cdiv(key_stride, 64) * 64;  // whole top-k rows of 64 blocks
+  // whole groups of 256 blocks: the keys of a unit that the four-wave top-k
+  // ranks are stored 256 apart (thread-transposed)
+  key_stride = (int)cdiv(key_stride, 256) * 256;
   c->dims.key_stride = key_stride;
   c->dims.lm_sel0 = lm_sel0;
   c->dims.lm_cap = lm_sel0 + sel_pages;
@@ -589,6 +592,8 @@ sd_status fuse_lse(sd_ctx *c, int32_t layer, int32_t n_seqs,
   if (!o_part || !lse_part || !o || !lse)
     return fail(c, SD_EINVAL, "a device pointer is NULL");
   if (p_cap < 1) return fail(c, SD_EINVAL, "p_cap %d < 1", p_cap);
+  if (reinterpret_cast<uintptr_t>(o_part) % 16 != 0)
+    return fail(c, SD_EINVAL, "o_part must be 16-byte aligned");
   const bool with_maw = layer >= 0;
   if (layer < -1) return fail(c, SD_EINVAL, "layer %d < -1", layer);
   if (with_maw) {
@@ -633,6 +638,8 @@ sd_status sparse_decode_step(sd_ctx *c, int32_t layer, int32_t n_seqs,
     return fail(c, SD_EINVAL, "a device pointer is NULL");
   if ((k_new == nullptr) != (v_new == nullptr))
     return fail(c, SD_EINVAL, "k_new and v_new must both be given or both be NULL");
+  if (reinterpret_cast<uintptr_t>(o_part) % 16 != 0)
+    return fail(c, SD_EINVAL, "o_part must be 16-byte aligned");
   if (p_cap < c->p_cap)
     return fail(c, SD_EINVAL, "p_cap %d < %d partial slots per head (sd_caps)", p_cap, c->p_cap);
   // k after the optional one-token append

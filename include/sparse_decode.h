@@ -162,7 +162,8 @@ sd_status sparse_attend(sd_ctx *ctx, int32_t layer, int32_t n_seqs,
  * MAW of every block of each (sequence, KV head) is then updated as
  * MAW <- r*MAW + (1-r)*a with a the group-mean softmax mass of the block
  * (0 if not attended) ([LFPS] decay; [HGCA] MAW).
- * layer == -1: pure fusion of n_seqs*Hq heads, no MAW (seq_ids may be NULL). */
+ * layer == -1: pure fusion of n_seqs*Hq heads, no MAW (seq_ids may be NULL).
+ * o_part must be 16-byte aligned (SD_EINVAL otherwise). */
 sd_status fuse_lse(sd_ctx *ctx, int32_t layer, int32_t n_seqs,
                    const int32_t *seq_ids, const float *o_part,
                    const float *lse_part, int32_t p_cap, float *o, float *lse);
@@ -175,7 +176,8 @@ sd_status fuse_lse(sd_ctx *ctx, int32_t layer, int32_t n_seqs,
  * attention parts, and the LSE fusion and MAW update done by the last part of
  * each (sequence, KV head).
  * blk_idx/blk_cnt/o_part/lse_part are written as by the separate calls, except
- * that partial slots a unit does not use are left unspecified. */
+ * that partial slots a unit does not use are left unspecified.  o_part must be
+ * 16-byte aligned (SD_EINVAL otherwise). */
 sd_status sparse_decode_step(sd_ctx *ctx, int32_t layer, int32_t n_seqs,
                              const int32_t *seq_ids, const void *k_new,
                              const void *v_new, const void *q_bf16,

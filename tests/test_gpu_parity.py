@@ -294,6 +294,14 @@ def test_error_paths():
         eng.select_topk(0, [0], q, bufs["blk_idx"], bufs["blk_cnt"])
         assert eng.sparse_attend(0, [0], q, bufs["blk_idx"], bufs["blk_cnt"], tiny_part,
                                  tiny_lse, check=False) == -1
+        # o_part not 16-byte aligned: both calls that read it refuse it
+        flat = torch.zeros(bufs["o_part"].numel() + 4, device="cuda")
+        skew = flat[1:1 + bufs["o_part"].numel()].view(bufs["o_part"].shape)
+        assert eng.fuse_lse(-1, None, skew, bufs["lse_part"], bufs["o"], bufs["lse"],
+                            check=False) == -1
+        assert eng.decode_step(0, [0], q, bufs["blk_idx"], bufs["blk_cnt"], skew,
+                               bufs["lse_part"], bufs["o"], bufs["lse"], check=False) == -1
+        assert eng.seq_len(0, 0) == 2000
         eng.sync()
     finally:
         eng.close()
