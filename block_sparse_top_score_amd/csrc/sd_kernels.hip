@@ -1193,17 +1193,39 @@ __device__ __attribute__((always_inline)) void topk_wide(const Ctx &c, int i, in
 #pragma unroll
   for (int t = 0; t < QT; ++t)
     if (tid + 256 * t < G * D) sm.qs[tid + 256 * t] = __uint_as_float((uint32_t)qv[t] << 16);
-  auto count_ge = [&](uint32_t t) {
-    int cnt = 0;
+  // workgroup counts of the words >= t1, t2, t3 (t1 <= t2 <= t3 > 1): the
+  // first two packed in 16-bit halves (at most 10240 each), over the first
+  // MM >= m words of each thread; LDS words red[8 s3 .. 8 s3 + 7], alternate
+  // calls alternating
+  int s3 = 0;
+  auto count3 = [&](auto MMc, uint32_t t1, uint32_t t2, uint32_t t3, int &c1, int &c2, int &c3) {
+    constexpr int MM = decltype(MMc)::value;
+    int x12 = 0, x3 = 0;
 #pragma unroll
-    for (int x = 0; x < kWideM; ++x) cnt += w[x] >= t ? 1 : 0;
-    return wg_sum(cnt, red, slot);
+    for (int x = 0; x < MM; ++x) {
+      x12 += (w[x] >= t1 ? 1 : 0) + (w[x] >= t2 ? 0x10000 : 0);
+      x3 += w[x] >= t3 ? 1 : 0;
+    }
+    x12 = wave_sum_i(x12);
+    x3 = wave_sum_i(x3);
+    uint32_t *r = red + 8 * s3;
+    s3 ^= 1;
+    if (lane == 0) {
+      r[wv] = (uint32_t)x12;
+      r[4 + wv] = (uint32_t)x3;
+    }
+    __syncthreads();
+    const uint32_t s12 = r[0] + r[1] + r[2] + r[3];
+    c1 = (int)(s12 & 0xffffu);
+    c2 = (int)(s12 >> 16);
+    c3 = (int)(r[4] + r[5] + r[6] + r[7]);
   };
 
   uint32_t kb_lo = 0xffffffffu, kb_hi = 0xffffffffu;
   if (k_sub > 0) {
     // 1. bracket [a, b] of the k_sub-th largest word T_a: #(>= a) >= k_sub >
-    // #(> b), narrowed until within eps; the band edges as in topk_unit
+    // #(> b), narrowed until within eps by a four-way search (three counts a
+    // step); the band edges as in topk_unit
     const double eps = (double)__uint_as_float(eps_bits);
     lo = wave_min_u(lo);
     hi_k = wave_max_u(hi_k);
@@ -1215,9 +1237,31 @@ __device__ __attribute__((always_inline)) void topk_wide(const Ctx &c, int i, in
     uint32_t a = min(min(red[8], red[9]), min(red[10], red[11]));
     uint32_t b = max(max(red[12], red[13]), max(red[14], red[15]));
     while (a < b && (double)key_to_float(b) - (double)key_to_float(a) > eps) {
-      const uint32_t mid = a + ((b - a) >> 1) + 1u;  // a < mid <= b
-      if (count_ge(mid) >= k_sub) a = mid; else b = mid - 1u;
+      // a < t1 <= t2 <= t3 <= b at about the quarters of [a, b]
+      const uint64_t span = (uint64_t)(b - a);
+      const uint32_t t1 = a + (uint32_t)((span + 3u) / 4u);
+      const uint32_t t2 = a + (uint32_t)((2u * span + 3u) / 4u);
+      const uint32_t t3 = a + (uint32_t)((3u * span + 3u) / 4u);
+      int c1, c2, c3;
+      if (m <= 8)
+        count3(std::integral_constant<int, 8>(), t1, t2, t3, c1, c2, c3);
+      else if (m <= 16)
+        count3(std::integral_constant<int, 16>(), t1, t2, t3, c1, c2, c3);
+      else
+        count3(std::integral_constant<int, kWideM>(), t1, t2, t3, c1, c2, c3);
+      if (c3 >= k_sub) {
+        a = t3;
+      } else if (c2 >= k_sub) {
+        a = t2;
+        b = t3 - 1u;
+      } else if (c1 >= k_sub) {
+        a = t1;
+        b = t2 - 1u;
+      } else {
+        b = t1 - 1u;
+      }
     }
+    __syncthreads();  // the counts' LDS words are free again
     kb_hi = order_key(__double2float_rd((double)key_to_float(b) + 2.0 * eps));
     kb_lo = order_key(__double2float_ru((double)key_to_float(a) - 2.0 * eps));
     // 2. the band in index order; the sure ones counted
