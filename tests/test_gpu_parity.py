@@ -120,13 +120,20 @@ def test_fused_step_equals_separate_calls():
     np.testing.assert_allclose(b["gpu"]["lse"], a["gpu"]["lse"], rtol=0, atol=1e-5)
 
 
-def test_fused_step_with_append_equals_separate_calls():
+@pytest.mark.parametrize("shape", ["llama", "qwen"])
+def test_fused_step_with_append_equals_separate_calls(shape):
     """sparse_decode_step with the one-token append equals append_kv +
-    select_topk + sparse_attend + fuse_lse, over several steps (MAW on)."""
-    w = _w(synth.llama32k(), B=3, N=3000, maw_beta=1.0)
-    log("case: fused step with append")
-    x = synth.single_step(w, 6, N=3000)
-    engs = [harness.make_engine(w, 3064) for _ in range(2)]
+    select_topk + sparse_attend + fuse_lse, over several steps (MAW on).
+    qwen: per-head block sizes and budgets, so the units of one launch use
+    different numbers of attention parts, and the 1500-block units take the
+    four-wave top-k."""
+    if shape == "llama":
+        w = _w(synth.llama32k(), B=3, N=3000, maw_beta=1.0)
+    else:
+        w = _w(synth.qwen128k(0), B=3, N=24000, maw_beta=1.0)
+    log("case: fused step with append (%s) S=%s ppm=%s" % (shape, w.block_size, w.budget_ppm))
+    x = synth.single_step(w, 6, N=w.N)
+    engs = [harness.make_engine(w, w.N + 64) for _ in range(2)]
     try:
         for e in engs:
             harness.prefill(e, 0, x["K"].cuda(), x["V"].cuda())
