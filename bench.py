@@ -17,7 +17,8 @@ step launches without append (k_step alone, same workload, rotating over the
 layer instances); `traffic` is the HBM traffic per
 launch from the committed FETCH_SIZE/WRITE_SIZE counter summary, null once the
 kernel sources differ from those it was taken on.  `cpu_baseline` times the
-CPU oracle on a bounded sample of the same workload.  --fused 0 runs the four separate ABI calls instead (same
+CPU oracle on a bounded sample of the same workload.  `read_ceiling` is a
+plain streaming read of the same byte count on the same GPU, for context.  --fused 0 runs the four separate ABI calls instead (same
 results, for comparison).
 """
 from __future__ import annotations
@@ -318,10 +319,49 @@ def main():
         "setup_s": setup_s,
     }
 
+    out["read_ceiling"] = read_ceiling(kstep_bytes, kstep_gbs)
     if args.cpu_baseline:
         out["cpu_baseline"] = cpu_baseline(w, K0, V0, qs[0], args.cpu_seconds)
     print(json.dumps(out), flush=True)
     eng.close()
+
+
+def read_ceiling(nbytes, kstep_gbs, n_buf=8, reps=64, wgs=8192):
+    """A plain streaming read on the same GPU, for context: the library's read
+    probe (each 16-byte word once, coalesced, 8192 workgroups) over n_buf
+    rotating buffers of the step's algorithmic size (8 x ~106 MB, so the reads
+    are not served from the 256 MB last-level cache), timed with events on
+    torch's stream.  `k_step_frac` is k_step's rate over this one."""
+    import ctypes
+    import torch
+    from block_sparse_top_score_amd import _abi
+    L = _abi.load()
+    n = nbytes // 16 * 16
+    bufs = [torch.randint(0, 255, (n,), device="cuda", dtype=torch.uint8) for _ in range(n_buf)]
+    sink = torch.zeros(wgs, device="cuda", dtype=torch.int32)
+    stream = ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
+
+    def launch(b):
+        st = L.sd_read_probe(ctypes.c_void_p(b.data_ptr()), n, ctypes.c_void_p(sink.data_ptr()),
+                             wgs, stream)
+        if st != 0:
+            raise RuntimeError("sd_read_probe failed: %d" % st)
+
+    for b in bufs:  # warm-up
+        launch(b)
+    ea, eb = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    ea.record()
+    for r in range(reps):
+        launch(bufs[r % n_buf])
+    eb.record()
+    torch.cuda.synchronize()
+    t_ms = ea.elapsed_time(eb) / reps
+    gbs = n / (t_ms * 1e-3) / 1e9
+    del bufs
+    return {"kind": "k_read_probe, %d rotating buffers, %d workgroups" % (n_buf, wgs), "bytes": n,
+            "ms": t_ms, "achieved_GBs": gbs, "frac_of_8TBs": gbs / HBM_PEAK_GBS,
+            "k_step_frac": kstep_gbs / gbs}
 
 
 def cpu_baseline(w, K, V, q, budget_s):

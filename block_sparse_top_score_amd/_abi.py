@@ -25,6 +25,7 @@ EXPORTS = [
     "sd_caps", "append_kv", "select_topk", "sparse_attend", "fuse_lse",
     "sparse_decode_step", "sd_release_seq", "sd_seq_len", "sd_sync",
     "sd_last_error", "sd_debug_bytes", "sd_debug_copy", "sd_debug_set_maw",
+    "sd_read_probe",
 ]
 
 
@@ -88,6 +89,7 @@ def load(path: str = LIB_PATH):
         "sd_debug_bytes": (i32, [P, i32, i32, i32, ctypes.POINTER(sz)]),
         "sd_debug_copy": (i32, [P, i32, i32, i32, P, sz]),
         "sd_debug_set_maw": (i32, [P, i32, i32, P, sz]),
+        "sd_read_probe": (i32, [P, sz, P, i32, P]),
     }
     for name, (res, args) in sig.items():
         f = getattr(L, name)

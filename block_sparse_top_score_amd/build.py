@@ -9,7 +9,7 @@ HERE = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(HERE)
 CSRC = os.path.join(HERE, "csrc")
 LIB = os.path.join(HERE, "libsparse_decode.so")
-SOURCES = ["sd_kernels.hip", "sd_runtime.hip"]
+SOURCES = ["sd_kernels.hip", "sd_runtime.hip", "sd_probe.hip"]
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 
 FLAGS = [

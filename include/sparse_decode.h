@@ -225,6 +225,19 @@ sd_status sd_debug_copy(sd_ctx *ctx, int32_t what, int32_t layer,
 sd_status sd_debug_set_maw(sd_ctx *ctx, int32_t layer, int32_t seq_id,
                            const float *host_src, size_t bytes);
 
+/* Streaming-read probe, for measurement only (no part of the decode path):
+ * the HBM read rate a plain kernel reaches on this GPU, against which the
+ * decode step's own rate can be read.  Reads `bytes` bytes at `src` once
+ * (device memory, 16-byte aligned, bytes > 0 and a multiple of 16) with
+ * `sink_words` workgroups of 256 threads, each thread reading 16-byte words
+ * grid-stride, four in flight; writes the XOR of each workgroup's words to
+ * sink[0 .. sink_words) (device, caller-owned).  Needs no context;
+ * stream-ordered and asynchronous on `stream` (hipStream_t, NULL = the null
+ * stream).  Returns SD_EINVAL (nothing launched) for a NULL pointer, a
+ * misaligned src, a bad size or sink_words < 1; SD_EHIP if the launch fails. */
+sd_status sd_read_probe(const void *src, size_t bytes, uint32_t *sink, int32_t sink_words,
+                        void *stream);
+
 #ifdef __cplusplus
 }
 #endif

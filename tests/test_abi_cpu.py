@@ -91,3 +91,17 @@ def test_product_path_does_not_import_oracle():
                 txt = open(os.path.join(dp, fn)).read()
                 assert "import oracle" not in txt and "from oracle" not in txt, fn
                 assert "oracle.h" not in txt, fn
+
+
+def test_read_probe_rejects_bad_arguments_before_any_launch():
+    """Argument checks of the streaming-read probe run on the host, so they
+    return SD_EINVAL here without a device."""
+    import ctypes
+    L = bsts.load()
+    dummy = ctypes.c_void_p(16)  # never dereferenced: every call below is rejected
+    assert L.sd_read_probe(None, 16, dummy, 1, None) == -1
+    assert L.sd_read_probe(dummy, 16, None, 1, None) == -1
+    assert L.sd_read_probe(dummy, 0, dummy, 1, None) == -1
+    assert L.sd_read_probe(dummy, 24, dummy, 1, None) == -1
+    assert L.sd_read_probe(ctypes.c_void_p(8), 16, dummy, 1, None) == -1
+    assert L.sd_read_probe(dummy, 16, dummy, 0, None) == -1
