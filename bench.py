@@ -65,9 +65,13 @@ def parse():
     ap.add_argument("--cpu-baseline", type=int, default=1)
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
     ap.add_argument("--trials", type=int, default=3)
-    ap.add_argument("--workload", choices=["llama32k", "qwen128k", "loop32"], default="llama32k",
+    ap.add_argument("--workload", choices=["llama32k", "qwen128k", "loop32", "sweep"],
+                    default="llama32k",
                     help="llama32k: the headline step; qwen128k (per-head budgets and block "
-                         "sizes, N=131072) and loop32 (B=16, N=65536, MAW flags on) are variants")
+                         "sizes, N=131072), loop32 (B=16, N=65536, MAW flags on) and sweep "
+                         "(the 4-query-head, d=64 geometry at N=32768, see --sweep) are variants")
+    ap.add_argument("--sweep", type=int, nargs=3, default=[64, 16, 10], metavar=("B", "S", "PCT"),
+                    help="sweep point: batch, block size, budget in percent of tokens")
     ap.add_argument("--streaming-heads", type=int, default=0,
                     help="give the first K KV heads budget 0 (streaming heads: sinks and "
                          "recent window only); a variant of the workload, not the headline")
@@ -183,7 +187,7 @@ def main():
     torch.cuda.set_device(0)
     dev = torch.device("cuda:0")
     w = {"llama32k": synth.llama32k, "qwen128k": lambda: synth.qwen128k(0),
-         "loop32": synth.loop32}[args.workload]()
+         "loop32": synth.loop32, "sweep": lambda: synth.sweep(*args.sweep)}[args.workload]()
     maw_beta = w.maw_beta  # MAW flags on for loop32 only
     if args.streaming_heads:
         K_s = min(args.streaming_heads, w.Hkv)
