@@ -58,7 +58,8 @@ def test_fused_group_sizes(G, Hkv, d, S):
     _check(harness.run_single_step(w, 8, fused=True))
 
 
-@pytest.mark.parametrize("B,S,pct", [(1, 16, 2), (8, 32, 5), (64, 16, 10), (32, 64, 10)])
+@pytest.mark.parametrize("B,S,pct", [(1, 16, 2), (8, 32, 5), (64, 16, 10), (32, 64, 10),
+                                     (64, 32, 10)])
 def test_fused_sweep_points(B, S, pct):
     log("case: fused sweep B=%d S=%d budget=%d%%" % (B, S, pct))
     _check(harness.run_single_step(synth.sweep(B, S, pct), 22, fused=True))
