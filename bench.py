@@ -72,6 +72,8 @@ def parse():
                          "(the 4-query-head, d=64 geometry at N=32768, see --sweep) are variants")
     ap.add_argument("--sweep", type=int, nargs=3, default=[64, 16, 10], metavar=("B", "S", "PCT"),
                     help="sweep point: batch, block size, budget in percent of tokens")
+    ap.add_argument("--sweep-n", type=int, default=32768,
+                    help="cached tokens of a sweep point (32768 in the sweep workload)")
     ap.add_argument("--streaming-heads", type=int, default=0,
                     help="give the first K KV heads budget 0 (streaming heads: sinks and "
                          "recent window only); a variant of the workload, not the headline")
@@ -187,7 +189,7 @@ def main():
     torch.cuda.set_device(0)
     dev = torch.device("cuda:0")
     w = {"llama32k": synth.llama32k, "qwen128k": lambda: synth.qwen128k(0),
-         "loop32": synth.loop32, "sweep": lambda: synth.sweep(*args.sweep)}[args.workload]()
+         "loop32": synth.loop32, "sweep": lambda: dataclasses.replace(synth.sweep(*args.sweep), N=args.sweep_n)}[args.workload]()
     maw_beta = w.maw_beta  # MAW flags on for loop32 only
     if args.streaming_heads:
         K_s = min(args.streaming_heads, w.Hkv)
