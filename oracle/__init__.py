@@ -11,7 +11,10 @@ their raw 16-bit patterns (``numpy.uint16``).  All arithmetic is in
 
 Parity status: see the header comment of ``oracle.c``.  The group max (R1),
 block-level MAW (R8), the beta/|D| flag scale (R9) and the flag-then-score
-order (R11) are "parity unpinned" by the pages.
+order (R11) are readings the pages do not fix; pins tie the oracle to them.
+
+``ORACLE_LIB`` in the environment names another build of ``oracle.c`` to load
+instead (used only by the mutation sweep in ``tests/``).
 """
 from __future__ import annotations
 
@@ -41,9 +44,10 @@ def build(force: bool = True) -> str:
 def lib():
     global _lib
     if _lib is None:
-        if not os.path.exists(_LIB_PATH):
+        path = os.environ.get("ORACLE_LIB") or _LIB_PATH
+        if path == _LIB_PATH and not os.path.exists(_LIB_PATH):
             build(force=True)
-        L = ctypes.CDLL(_LIB_PATH)
+        L = ctypes.CDLL(path)
         i32, i64, dbl = ctypes.c_int32, ctypes.c_int64, ctypes.c_double
         P = ctypes.c_void_p
         L.oracle_num_blocks.restype = i64
@@ -70,13 +74,18 @@ def lib():
                                            dbl, P, P, P]
         L.oracle_attend.restype = i64
         L.oracle_attend.argtypes = [P, i32, i32, P, i64, P, i64, i64, i32, i32,
-                                    i32, P, i64, dbl, P, P, P]
+                                    i32, P, i64, dbl, P, P]
+        L.oracle_dense_mass.restype = None
+        L.oracle_dense_mass.argtypes = [P, i32, i32, P, i64, i64, i32, i32, i32,
+                                        dbl, P]
         L.oracle_dense.restype = None
         L.oracle_dense.argtypes = [P, i32, i32, P, i64, P, i64, i64, dbl, P, P]
         L.oracle_fuse.restype = None
         L.oracle_fuse.argtypes = [i64, i32, P, P, P, P]
         L.oracle_maw_update.restype = None
         L.oracle_maw_update.argtypes = [P, P, i64, dbl]
+        L.oracle_maw_step.restype = None
+        L.oracle_maw_step.argtypes = [P, P, i64, i32, i32, i32, dbl]
         _lib = L
     return _lib
 
@@ -180,24 +189,32 @@ def attend_tokens(q, K, V, tok, scale=None, want_p=False):
     return O, lse
 
 
-def attend(q, K, V, N, S, n_s, W, sel, scale=None, want_mass=False):
+def attend(q, K, V, N, S, n_s, W, sel, scale=None):
     """Attention over D U blocks(sel).  K, V: [>=N, d] (row j = token j)."""
     q, K, V = _u16(q), _u16(K), _u16(V)
     G, d = q.shape
     sel = np.ascontiguousarray(sel, dtype=np.int32)
     if scale is None:
         scale = 1.0 / np.sqrt(d)
-    nb = num_blocks(N, S)
     O = np.zeros((G, d), np.float64)
     lse = np.zeros(G, np.float64)
-    a = np.zeros(max(nb, 1), np.float64) if want_mass else None
     nt = lib().oracle_attend(_p(q), G, d, _p(K), K.shape[1], _p(V), V.shape[1],
                              N, S, n_s, W, _p(sel), sel.shape[0], float(scale),
-                             _p(O), _p(lse), _p(a))
-    out = dict(O=O, lse=lse, n_tok=int(nt))
-    if want_mass:
-        out["a"] = a[:nb]
-    return out
+                             _p(O), _p(lse))
+    return dict(O=O, lse=lse, n_tok=int(nt))
+
+
+def dense_mass(q, K, N, S, n_s, W, scale=None):
+    """MAW input per block: group-mean mass under the softmax over D alone."""
+    q, K = _u16(q), _u16(K)
+    G, d = q.shape
+    if scale is None:
+        scale = 1.0 / np.sqrt(d)
+    nb = num_blocks(N, S)
+    a = np.zeros(max(nb, 1), np.float64)
+    lib().oracle_dense_mass(_p(q), G, d, _p(K), K.shape[1], N, S, n_s, W,
+                            float(scale), _p(a))
+    return a[:nb]
 
 
 def dense(q, K, V, N, scale=None):
@@ -231,10 +248,20 @@ def maw_update(maw, a, r=0.95):
     return m
 
 
+def maw_step(maw, a, N, S, n_s, W, r=0.95):
+    """One MAW step of a unit (blocks touching D only); the updated copy."""
+    m = np.array(maw, dtype=np.float64, copy=True)
+    a = np.ascontiguousarray(a, dtype=np.float64)
+    assert a.shape == m.shape == (num_blocks(N, S),)
+    lib().oracle_maw_step(_p(m), _p(a), N, S, n_s, W, float(r))
+    return m
+
+
 def unit_step(q, K, V, N, S, n_s, W, budget_ppm, maw=None, beta=0.0,
               r=0.95, scale=None, sel_override=None):
     """One decode step of one (sequence, KV head) unit, in the pages' order:
-    summaries -> scores and selection -> attention over D U Sel -> MAW.
+    summaries -> scores and selection -> attention over D U Sel -> MAW (fed
+    by the dense partial's per-block mass; blocks outside D keep theirs).
 
     sel_override lets a lockstep test continue from another legal selection
     (a tie inside the stated band).  Returns a dict with sel, O, lse, U, u,
@@ -251,11 +278,13 @@ def unit_step(q, K, V, N, S, n_s, W, budget_ppm, maw=None, beta=0.0,
     sres = select(q, mn, mx, N, S, n_s, W, budget_ppm, maw=m, beta=beta)
     sel = sres["sel"] if sel_override is None else np.asarray(sel_override,
                                                                np.int32)
-    ares = attend(q, K, V, N, S, n_s, W, sel, scale=scale, want_mass=True)
+    ares = attend(q, K, V, N, S, n_s, W, sel, scale=scale)
     out = dict(sres)
-    out.update(sel=sel, O=ares["O"], lse=ares["lse"], a=ares["a"], mn=mn,
-               mx=mx, n_tok=ares["n_tok"], oracle_sel=sres["sel"])
+    out.update(sel=sel, O=ares["O"], lse=ares["lse"], mn=mn, mx=mx,
+               n_tok=ares["n_tok"], oracle_sel=sres["sel"])
     if m is not None:
+        a = dense_mass(q, K, N, S, n_s, W, scale=scale)
+        out["a"] = a
         out["maw_before"] = m
-        out["maw"] = maw_update(m, ares["a"], r)
+        out["maw"] = maw_step(m, a, N, S, n_s, W, r)
     return out

@@ -16,9 +16,20 @@
  *                         identity
  *   oracle_fuse           pinned: LSE identity over random partitions
  *   oracle_maw_update     pinned: closed forms of the decay-0.95 average
- *   group max (R1), per-block MAW (R8), the beta/|D| flag scale (R9) and the
- *   lexicographic flag-then-score order (R11): parity unpinned by the pages
- *   (fixed only by the stated readings; checked for internal consistency).
+ *   oracle_dense_mass     pinned: numpy softmax over the dense set per head,
+ *                         summed per block and averaged over unequal heads;
+ *                         mass conservation over D
+ *   oracle_maw_step       pinned: hand fixture (blocks outside D keep MAW,
+ *                         blocks touching D take the average)
+ *   oracle_maw_flag       pinned: hand fixture at S = 32 and a selection hand
+ *                         case at S = 2 on either side of beta*S/|D|
+ *   The readings themselves - group max (R1), per-block MAW (R8), the
+ *   beta/|D| flag scale (R9) and the lexicographic flag-then-score order
+ *   (R11) - are not fixed by the pages; the pins above fix the oracle to
+ *   those readings, not the readings to the pages.
+ * A committed mutation sweep (tests/test_oracle_mutants.py) plants one
+ * plausible mistake at a time in a copy of this file and checks that some
+ * pin fails for each.
  */
 #include "oracle.h"
 
@@ -239,13 +250,12 @@ void oracle_attend_tokens(const uint16_t *q, int32_t G, int32_t d,
 
 /* Attention over T = D U tokens(Sel) (R4), the split-K partial that the pages
  * merge ([HGCA] "What carries the argument": dense recent window plus sparse
- * selected entries).  a_blk: group-mean mass per block (R8). */
+ * selected entries). */
 int64_t oracle_attend(const uint16_t *q, int32_t G, int32_t d,
                       const uint16_t *K, int64_t ldk, const uint16_t *V,
                       int64_t ldv, int64_t N, int32_t S, int32_t n_s,
                       int32_t W, const int32_t *sel, int64_t k, double scale,
-                      double *O, double *lse, double *a_blk) {
-  int64_t n_blk = oracle_num_blocks(N, S);
+                      double *O, double *lse) {
   int8_t *inT = (int8_t *)calloc(N > 0 ? N : 1, 1);
   for (int64_t j = 0; j < N; ++j) inT[j] = (int8_t)oracle_in_dense(j, N, n_s, W);
   for (int64_t t = 0; t < k; ++t)
@@ -257,18 +267,44 @@ int64_t oracle_attend(const uint16_t *q, int32_t G, int32_t d,
   int64_t t = 0;
   for (int64_t j = 0; j < N; ++j)
     if (inT[j]) tok[t++] = j;
-  double *p = (double *)malloc(sizeof(double) * (size_t)G * (n_tok > 0 ? n_tok : 1));
-  oracle_attend_tokens(q, G, d, K, ldk, V, ldv, tok, n_tok, scale, O, lse, p);
-  if (a_blk) {
-    for (int64_t i = 0; i < n_blk; ++i) a_blk[i] = 0.0;
-    for (int32_t h = 0; h < G; ++h)
-      for (int64_t tt = 0; tt < n_tok; ++tt)
-        a_blk[tok[tt] / S] += p[(int64_t)h * n_tok + tt] / (double)G;
-  }
-  free(p);
+  oracle_attend_tokens(q, G, d, K, ldk, V, ldv, tok, n_tok, scale, O, lse, NULL);
   free(tok);
   free(inT);
   return n_tok;
+}
+
+/* The MAW input of one step (R8, and R10 as read from HGCA): HGCA's moving
+ * average is fed only by the attention weights of the GPU-side partial, the
+ * dense recent window, normalised over that window alone ([HGCA] "What
+ * carries the argument": the threshold is beta over the number of GPU-side
+ * entries; referee report on section 3.2.2 / Algorithm 1: the average is
+ * updated from the window's weights only).  Here the GPU-side entries are D:
+ * per query head h the softmax over D, p_hj = e^{s_hj - lse_D,h}; per block
+ * a_i = (1/G) sum_h sum_{j in D, j in block i} p_hj.  a_i = 0 for blocks
+ * with no token in D; sum_i a_i = 1 when D is not empty. */
+void oracle_dense_mass(const uint16_t *q, int32_t G, int32_t d,
+                       const uint16_t *K, int64_t ldk, int64_t N, int32_t S,
+                       int32_t n_s, int32_t W, double scale, double *a_blk) {
+  int64_t n_blk = oracle_num_blocks(N, S);
+  for (int64_t i = 0; i < n_blk; ++i) a_blk[i] = 0.0;
+  int64_t nD = oracle_dense_count(N, n_s, W);
+  if (nD == 0) return;
+  int64_t *tok = (int64_t *)malloc(sizeof(int64_t) * nD);
+  int64_t t = 0;
+  for (int64_t j = 0; j < N; ++j)
+    if (oracle_in_dense(j, N, n_s, W)) tok[t++] = j;
+  double *O = (double *)malloc(sizeof(double) * (size_t)G * d);
+  double *lse = (double *)malloc(sizeof(double) * (size_t)G);
+  double *p = (double *)malloc(sizeof(double) * (size_t)G * nD);
+  /* attend_tokens reads V only to form O, which is not used here */
+  oracle_attend_tokens(q, G, d, K, ldk, K, ldk, tok, nD, scale, O, lse, p);
+  for (int32_t h = 0; h < G; ++h)
+    for (int64_t tt = 0; tt < nD; ++tt)
+      a_blk[tok[tt] / S] += p[(int64_t)h * nD + tt] / (double)G;
+  free(p);
+  free(lse);
+  free(O);
+  free(tok);
 }
 
 /* Independent textbook softmax over every token: weights e^{s_j - max}
@@ -329,7 +365,23 @@ void oracle_fuse(int64_t P, int32_t d, const double *O_parts,
 
 /* Moving average with decay r ([LFPS] "What carries the argument" and
  * "Assumptions & free parameters": decay factor r = 0.95; [HGCA] MAW, whose
- * own factor is not reported).  R10: applied to every block every step. */
+ * own factor is not reported): MAW <- r MAW + (1 - r) a for every entry
+ * given. */
 void oracle_maw_update(double *maw, const double *a, int64_t n_blk, double r) {
   for (int64_t i = 0; i < n_blk; ++i) maw[i] = r * maw[i] + (1.0 - r) * a[i];
+}
+
+/* One MAW step of a unit (R10): blocks with a token in D take the average of
+ * their dense-partial mass a (oracle_dense_mass); a block with no token in D
+ * keeps its value ([HGCA] referee report on section 3.2.2 / Algorithm 1: the
+ * average of an entry that has left the GPU-side window is frozen). */
+void oracle_maw_step(double *maw, const double *a, int64_t N, int32_t S,
+                     int32_t n_s, int32_t W, double r) {
+  int64_t n_blk = oracle_num_blocks(N, S);
+  for (int64_t i = 0; i < n_blk; ++i) {
+    int touches = 0;
+    for (int64_t j = i * S; j < (i + 1) * S && j < N; ++j)
+      if (oracle_in_dense(j, N, n_s, W)) touches = 1;
+    if (touches) maw[i] = r * maw[i] + (1.0 - r) * a[i];
+  }
 }

@@ -35,10 +35,12 @@
  *   R4  the attended set is the union of the dense set and the selected
  *       blocks (a token is counted once).
  *   R5  selection order is (flag desc, fp32 score desc, block index asc).
- *   R8-R10  the moving average of attention weight (MAW) is kept per block,
- *       holds the group-mean softmax mass of the block, and is updated for
- *       every block as MAW <- r*MAW + (1-r)*a; a block is flagged when
- *       MAW * |D| > beta * S.
+ *   R8-R10  the moving average of attention weight (MAW) is kept per block.
+ *       Its input a is the group-mean softmax mass of the block's dense
+ *       tokens under the dense partial alone (softmax over D, HGCA's
+ *       GPU-side window); blocks with a token in D take
+ *       MAW <- r*MAW + (1-r)*a, the others keep their value (frozen once
+ *       they leave D); a block is flagged when MAW * |D| > beta * S.
  *   R18 scale 1/sqrt(d) unless given; lse is a natural log of scaled logits.
  */
 #ifndef BSTS_ORACLE_H
@@ -103,14 +105,19 @@ void oracle_attend_tokens(const uint16_t *q, int32_t G, int32_t d,
                           double scale, double *O /* [G][d] */,
                           double *lse /* [G] */, double *p /* or NULL */);
 
-/* Attention over T = D U tokens(sel) (a set).  a_blk (optional, [n_blk]):
- * group-mean softmax mass per block, (1/G) sum_h sum_{j in T, blk} p_hj.
- * Returns |T|. */
+/* Attention over T = D U tokens(sel) (a set).  Returns |T|. */
 int64_t oracle_attend(const uint16_t *q, int32_t G, int32_t d,
                       const uint16_t *K, int64_t ldk, const uint16_t *V,
                       int64_t ldv, int64_t N, int32_t S, int32_t n_s,
                       int32_t W, const int32_t *sel, int64_t k, double scale,
-                      double *O, double *lse, double *a_blk);
+                      double *O, double *lse);
+
+/* MAW input: a_blk[i] = (1/G) sum_h sum_{j in D, j in block i} p_hj with p_h
+ * the softmax of head h over the dense set D alone (0 for blocks with no
+ * token in D).  a_blk: [n_blk]. */
+void oracle_dense_mass(const uint16_t *q, int32_t G, int32_t d,
+                       const uint16_t *K, int64_t ldk, int64_t N, int32_t S,
+                       int32_t n_s, int32_t W, double scale, double *a_blk);
 
 /* Independent naive dense softmax attention over all tokens [0, N). */
 void oracle_dense(const uint16_t *q, int32_t G, int32_t d, const uint16_t *K,
@@ -124,8 +131,13 @@ void oracle_dense(const uint16_t *q, int32_t G, int32_t d, const uint16_t *K,
 void oracle_fuse(int64_t P, int32_t d, const double *O_parts /* [P][d] */,
                  const double *lse_parts /* [P] */, double *O, double *lse);
 
-/* MAW update for every block: maw[i] <- r * maw[i] + (1 - r) * a[i]. */
+/* MAW update for every entry: maw[i] <- r * maw[i] + (1 - r) * a[i]. */
 void oracle_maw_update(double *maw, const double *a, int64_t n_blk, double r);
+
+/* One MAW step of a unit of N tokens: blocks with a token in D take
+ * maw[i] <- r * maw[i] + (1 - r) * a[i]; the others keep maw[i]. */
+void oracle_maw_step(double *maw, const double *a, int64_t N, int32_t S,
+                     int32_t n_s, int32_t W, double r);
 
 #ifdef __cplusplus
 }
