@@ -249,7 +249,7 @@ def maw_update(maw, a, r=0.95):
 
 
 def maw_step(maw, a, N, S, n_s, W, r=0.95):
-    """One MAW step of a unit (blocks touching D only); the updated copy."""
+    """One MAW step of a unit (blocks wholly inside D only); the updated copy."""
     m = np.array(maw, dtype=np.float64, copy=True)
     a = np.ascontiguousarray(a, dtype=np.float64)
     assert a.shape == m.shape == (num_blocks(N, S),)
@@ -261,7 +261,8 @@ def unit_step(q, K, V, N, S, n_s, W, budget_ppm, maw=None, beta=0.0,
               r=0.95, scale=None, sel_override=None):
     """One decode step of one (sequence, KV head) unit, in the pages' order:
     summaries -> scores and selection -> attention over D U Sel -> MAW (fed
-    by the dense partial's per-block mass; blocks outside D keep theirs).
+    by the dense partial's per-block mass; blocks not wholly inside D keep
+    theirs).
 
     sel_override lets a lockstep test continue from another legal selection
     (a tie inside the stated band).  Returns a dict with sel, O, lse, U, u,

@@ -19,8 +19,8 @@
  *   oracle_dense_mass     pinned: numpy softmax over the dense set per head,
  *                         summed per block and averaged over unequal heads;
  *                         mass conservation over D
- *   oracle_maw_step       pinned: hand fixture (blocks outside D keep MAW,
- *                         blocks touching D take the average)
+ *   oracle_maw_step       pinned: hand fixture (blocks with a token outside D
+ *                         keep MAW, blocks inside D take the average)
  *   oracle_maw_flag       pinned: hand fixture at S = 32 and a selection hand
  *                         case at S = 2 on either side of beta*S/|D|
  *   The readings themselves - group max (R1), per-block MAW (R8), the
@@ -371,17 +371,20 @@ void oracle_maw_update(double *maw, const double *a, int64_t n_blk, double r) {
   for (int64_t i = 0; i < n_blk; ++i) maw[i] = r * maw[i] + (1.0 - r) * a[i];
 }
 
-/* One MAW step of a unit (R10): blocks with a token in D take the average of
- * their dense-partial mass a (oracle_dense_mass); a block with no token in D
- * keeps its value ([HGCA] referee report on section 3.2.2 / Algorithm 1: the
- * average of an entry that has left the GPU-side window is frozen). */
+/* One MAW step of a unit (R10): a block all of whose tokens lie in D takes
+ * the average of its dense-partial mass a (oracle_dense_mass); every other
+ * block keeps its value.  [HGCA] keeps the newest KV blocks in a GPU-side
+ * circular buffer and evicts old blocks whole ("What carries the argument"),
+ * and the average of an entry that has left the GPU side is frozen (referee
+ * report on section 3.2.2 / Algorithm 1): a block leaves the GPU side when
+ * its oldest token leaves D. */
 void oracle_maw_step(double *maw, const double *a, int64_t N, int32_t S,
                      int32_t n_s, int32_t W, double r) {
   int64_t n_blk = oracle_num_blocks(N, S);
   for (int64_t i = 0; i < n_blk; ++i) {
-    int touches = 0;
+    int inside = 1;
     for (int64_t j = i * S; j < (i + 1) * S && j < N; ++j)
-      if (oracle_in_dense(j, N, n_s, W)) touches = 1;
-    if (touches) maw[i] = r * maw[i] + (1.0 - r) * a[i];
+      if (!oracle_in_dense(j, N, n_s, W)) inside = 0;
+    if (inside) maw[i] = r * maw[i] + (1.0 - r) * a[i];
   }
 }

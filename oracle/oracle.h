@@ -38,9 +38,10 @@
  *   R8-R10  the moving average of attention weight (MAW) is kept per block.
  *       Its input a is the group-mean softmax mass of the block's dense
  *       tokens under the dense partial alone (softmax over D, HGCA's
- *       GPU-side window); blocks with a token in D take
- *       MAW <- r*MAW + (1-r)*a, the others keep their value (frozen once
- *       they leave D); a block is flagged when MAW * |D| > beta * S.
+ *       GPU-side window); blocks whose tokens all lie in D take
+ *       MAW <- r*MAW + (1-r)*a, the others keep their value (frozen from the
+ *       step their oldest token leaves D); a block is flagged when
+ *       MAW * |D| > beta * S.
  *   R18 scale 1/sqrt(d) unless given; lse is a natural log of scaled logits.
  */
 #ifndef BSTS_ORACLE_H
@@ -134,7 +135,7 @@ void oracle_fuse(int64_t P, int32_t d, const double *O_parts /* [P][d] */,
 /* MAW update for every entry: maw[i] <- r * maw[i] + (1 - r) * a[i]. */
 void oracle_maw_update(double *maw, const double *a, int64_t n_blk, double r);
 
-/* One MAW step of a unit of N tokens: blocks with a token in D take
+/* One MAW step of a unit of N tokens: blocks whose tokens all lie in D take
  * maw[i] <- r * maw[i] + (1 - r) * a[i]; the others keep maw[i]. */
 void oracle_maw_step(double *maw, const double *a, int64_t N, int32_t S,
                      int32_t n_s, int32_t W, double r);

@@ -52,11 +52,14 @@ MUTANTS = [
      "double w = exp(lse_parts[i] - m);"),
     ("decay_swapped", "maw[i] = r * maw[i] + (1.0 - r) * a[i];\n}\n\n/* One MAW step",
      "maw[i] = (1.0 - r) * maw[i] + r * a[i];\n}\n\n/* One MAW step"),
-    ("maw_step_updates_every_block", "if (touches) maw[i] = r * maw[i] + (1.0 - r) * a[i];",
+    ("maw_step_updates_every_block", "if (inside) maw[i] = r * maw[i] + (1.0 - r) * a[i];",
      "maw[i] = r * maw[i] + (1.0 - r) * a[i];"),
     ("maw_step_decays_outside_dense",
-     "if (touches) maw[i] = r * maw[i] + (1.0 - r) * a[i];",
-     "maw[i] = touches ? r * maw[i] + (1.0 - r) * a[i] : r * maw[i];"),
+     "if (inside) maw[i] = r * maw[i] + (1.0 - r) * a[i];",
+     "maw[i] = inside ? r * maw[i] + (1.0 - r) * a[i] : r * maw[i];"),
+    ("maw_step_updates_blocks_touching_dense",
+     "if (!oracle_in_dense(j, N, n_s, W)) inside = 0;",
+     "if (oracle_in_dense(j, N, n_s, W)) inside = 2;\n    inside = inside == 2;"),
     ("dense_mass_head0_only", "a_blk[tok[tt] / S] += p[(int64_t)h * nD + tt] / (double)G;",
      "a_blk[tok[tt] / S] += p[tt] / (double)G;"),
     ("dense_mass_not_averaged", "a_blk[tok[tt] / S] += p[(int64_t)h * nD + tt] / (double)G;",

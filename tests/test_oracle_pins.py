@@ -426,7 +426,8 @@ def test_dense_mass_matches_numpy_unequal_heads(N, S, n_s, W):
 
 def test_maw_step_keeps_blocks_outside_dense():
     """R10: over several steps with the window moving, a block keeps its MAW
-    once it has no token in D, and blocks in D follow the closed form."""
+    from the step its oldest token leaves D, and blocks wholly inside D
+    follow the update."""
     S, n_s, W, r = 16, 4, 64, 0.95
     N0 = 400
     m = np.zeros(oracle.num_blocks(N0, S))
@@ -439,8 +440,8 @@ def test_maw_step_keeps_blocks_outside_dense():
         new = oracle.maw_step(m, a, N, S, n_s, W, r)
         for i in range(nb):
             lo, hi = i * S, min(N, (i + 1) * S)
-            touches = lo < n_s or hi > N - W
-            want = r * m[i] + (1 - r) * a[i] if touches else m[i]
+            inside = all(j < n_s or j >= N - W for j in range(lo, hi))
+            want = r * m[i] + (1 - r) * a[i] if inside else m[i]
             assert new[i] == want
         m = new
 
