@@ -20,9 +20,7 @@ constexpr int kTopkUnc = 512;        // uncertain blocks the top-k lists in LDS
 constexpr int kFastTiles = 8;        // score tiles per unit of the fast top-k, at most
 constexpr int kPtLds = 4096;         // page-table entries a selected chunk copies to LDS, at most
 constexpr int kFuseSlots = 256;      // partial slots per query head, at most
-constexpr int kFuseSelLds = 2048;    // fusion keeps the selection in LDS up to this
-constexpr int kFusePgLds = 2048;     // and the attended pages' masses up to this
-constexpr int kFuseDense = 256;      // and a map of the dense-touching blocks up to this
+constexpr int kFuseDenseLds = 2048;  // dense pages (sinks + window) per unit, at most
 
 // Per-KV-head constants, resident in device memory for the context's life
 // (read with uniform addresses, so they come through the scalar cache).
@@ -84,8 +82,6 @@ struct Scratch {
   uint32_t *unit_acc;  // [max_seqs][Hkv][2] error bound (float bits, max) and
                        // flagged candidates (count) of the score tiles; 0 between steps
   float *lm_pg;      // [max_seqs][Hq][lm_cap] log softmax mass of each attended page
-  int32_t *usel;     // [max_seqs][Hkv][kcap] selected block ids (attend copy)
-  int32_t *ucnt;     // [max_seqs][Hkv] selected block count (attend copy)
   uint32_t *arrive;  // [max_seqs][Hkv][2] last-arriver counters (kept at 0)
   unsigned long long *cand;  // [max_seqs][Hkv][key_stride] per-tile lists of the 64
                              // largest keys (key << 32 | ~block), tile t's at [64 t, 64 t + 64)
@@ -115,7 +111,7 @@ hipError_t launch_select(const Ctx &c, const SeqBatch &b, int max_blocks, const 
                          int32_t *blk_idx, int32_t *blk_cnt, int32_t k_cap, hipStream_t st);
 
 // Attention: P workgroups per unit, one partial slot each (slots [P, p_cap)
-// emptied); keeps a copy of the selection for the fusion call.
+// emptied); keeps the dense pages' log-masses for the fusion call.
 hipError_t launch_attend(const Ctx &c, const SeqBatch &b, int P, const uint16_t *q,
                          const int32_t *blk_idx, const int32_t *blk_cnt, int32_t k_cap,
                          float *o_part, float *lse_part, int32_t p_cap, hipStream_t st);
@@ -133,7 +129,7 @@ hipError_t launch_step(const Ctx &c, const SeqBatch &b, int max_blocks, int P, c
 int step_capacity(const Ctx &c, int max_blocks, int ptl_cap);
 
 // Fusion of the partials: with_maw = the P slots of the attend call and MAW
-// (layer call); otherwise every slot of p_cap is fused (layer -1).
+// (layer call); otherwise every slot of p_cap <= kFuseSlots is fused (layer -1).
 hipError_t launch_fuse(const Ctx &c, const SeqBatch &b, bool with_maw, int P,
                        const float *o_part, const float *lse_part, int32_t p_cap,
                        float *o, float *lse, hipStream_t st);

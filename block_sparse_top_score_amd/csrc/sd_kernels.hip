@@ -192,9 +192,8 @@ template <int G>
 struct FuseSmem {
   float w[G][kFuseSlots];   // per-slot LSE weights
   float lse[G];
-  int32_t sel[kFuseSelLds];  // the selection
-  float pm[kFusePgLds];      // softmax mass of each attended page, summed over heads
-  int32_t dsel[kFuseDense];  // selection index of each dense-touching block, or -1
+  float dm[4][G], dz[4][G];  // per wave: running max and sum of the dense log-masses
+  float pm[kFuseDenseLds];   // mass of each dense page under the dense partial, summed over heads
 };
 
 // ---------------------------------------------------------------------------
@@ -552,13 +551,12 @@ __device__ __forceinline__ void tile_list(const Ctx &c, int seq, int h, int tile
   }
 }
 
-// decay_maw: also write r*MAW for the tile's blocks (the fused step; the
-// fusion then adds (1-r)*a to the attended blocks only).  publish: also write
-// the tile's candidate list for the fast top-k (tile < kFastTiles).
+// fast_ok: also write the tile's candidate list for the fast top-k (tile <
+// kFastTiles).
 template <int D, int G>
 __device__ __attribute__((always_inline)) bool score_tile(const Ctx &c, int i, int seq, int h, const HeadInfo &hi,
                            int N, int n_blk, int tile, const uint16_t *__restrict__ q,
-                           TopkSmem &sm, bool decay_maw, bool fast_ok, UG &g) {
+                           TopkSmem &sm, bool fast_ok, UG &g) {
   uint32_t *red = sm.red;
   constexpr int MM = D / 16;    // MFMAs per 16 blocks (k = 2d values, 32 per MFMA)
   constexpr int GPW = kScoreTile / 64;  // 16-block groups per wave
@@ -585,9 +583,10 @@ __device__ __attribute__((always_inline)) bool score_tile(const Ctx &c, int i, i
 #pragma unroll
   for (int mm = 0; mm < MM; ++mm)
     qw[mm] = *reinterpret_cast<const uint2 *>(qrow + 4 * (4 * mm + lgrp));
-  // MAW of the lane's blocks (lanes of channel group 0 own the keys)
-  const bool need_maw = c.dm.maw_beta > 0.0f || decay_maw;
-  float *mwp = c.L.maw + hi.maw_off + (size_t)seq * hi.nbmax;
+  // MAW of the lane's blocks, for the flag (lanes of channel group 0 own the
+  // keys)
+  const bool need_maw = c.dm.maw_beta > 0.0f;
+  const float *mwp = c.L.maw + hi.maw_off + (size_t)seq * hi.nbmax;
   float mwv[GPW];
 #pragma unroll
   for (int gi = 0; gi < GPW; ++gi) {
@@ -664,7 +663,6 @@ __device__ __attribute__((always_inline)) bool score_tile(const Ctx &c, int i, i
         }
       }
       st_dev(&c.sc.keyflag[ko], kv);
-      if (decay_maw) st_dev(&mwp[blk], __fmul_rn(c.dm.maw_decay, mwv[gi]));
     }
     if (publish && lgrp == 0) sm.tk[wv * 16 * GPW + gi * 16 + r16] = (uint32_t)kv;
   }
@@ -1896,7 +1894,7 @@ __device__ __attribute__((always_inline)) void attend_part(const Ctx &c, int i, 
     __syncthreads();
     cnt = *s_cnt;
   }
-  if (cnt > 0) {
+  if (cnt > 0 && g.N > 0) {
     wave_pages<D, G>(
         c, h, gw, NW, cnt * PPB,
         [&](int t, int &pg, int &mk, int &sl) {
@@ -1907,15 +1905,22 @@ __device__ __attribute__((always_inline)) void attend_part(const Ctx &c, int i, 
             const unsigned long long t0 = wall_clock64();
             while ((uint32_t)(e >> 32) != si.epoch && wall_clock64() - t0 < kWaitTicks)
               e = ld_dev(&si.tag[j]);
-            blk = (uint32_t)(e >> 32) == si.epoch ? (int)(uint32_t)e : 0;
+            if ((uint32_t)(e >> 32) == si.epoch) {
+              blk = (int)(uint32_t)e;
+            } else {  // gave up: the step's outputs are invalid
+              blk = -1;
+              st_dev(&c.sc.err[0], 1u);
+            }
           } else {
             blk = si.blk[j];
           }
-          blk = min(max(blk, 0), max(g.n_blk - 1, 0));
-          const int pn = blk * PPB + pp;
+          // an entry outside [0, n_blk) attends nothing (its pages' masks are
+          // empty; the page read is a valid one of the sequence)
+          const bool in_range = blk >= 0 && blk < g.n_blk;
+          const int pn = in_range ? blk * PPB + pp : 0;
           const int pl_ = min(pn, dl.np - 1);  // pages past N are never read
           pg = ptl ? ptl[pl_] : pts[pl_];
-          mk = page_valid16(g, pn) & ~page_dense16(g, pn);
+          mk = in_range ? page_valid16(g, pn) & ~page_dense16(g, pn) : 0;
           sl = c.dm.lm_sel0 + t;
         },
         qa, W, pl, lmb);
@@ -1977,16 +1982,19 @@ __device__ __forceinline__ void empty_slots(const Ctx &c, int i, int h, int P, i
 
 // ---------------------------------------------------------------------------
 // fusion + MAW ([HGCA] What carries the argument: the exact log-sum-exp merge
-// of partials; MAW as a decaying average of attention weights; [LFPS] decay
+// of partials; MAW as a moving average of attention weights; [LFPS] decay
 // r = 0.95).  For each query head: lse = m + log sum_u exp(lse_u - m) with m
 // the largest partial lse (empty slots, lse = -inf, drop out), and O =
-// sum_u exp(lse_u - lse) O_u.  Then for every block, MAW <- r MAW + (1 - r) a
-// with a the group-mean softmax mass of the block's attended tokens, from the
-// log-mass of each attended page.
-//   kMawNone: fusion only.
-//   kMawFull: decay of every block here, then one add per attended block.
-//   kMawAdd:  the score tiles already wrote r*MAW (one-launch step).
-constexpr int kMawNone = 0, kMawFull = 1, kMawAdd = 2;
+// sum_u exp(lse_u - lse) O_u.
+// MAW (a layer call) is fed by the dense partial alone ([HGCA] referee report
+// on section 3.2.2 / Algorithm 1: the average is updated from the GPU-side
+// window's attention weights, and an entry's average is frozen once it has
+// left the window; blocks leave the GPU side whole): per head, lse_D = log
+// sum of exp(log-mass) over the dense pages; each block whose tokens all lie
+// in D - a block that is not a candidate - takes MAW <- r MAW + (1 - r) a,
+// a = (1/G) sum_h sum of exp(log-mass - lse_D) over the block's pages; every
+// other block keeps its value.  Candidates are the only blocks the score
+// tiles read MAW of, and these are never written here.
 // e^x and ln x from the hardware base-2 exponential and logarithm (about one
 // ulp each; the fp32 rounding of x log2(e) adds |x| 2^-24 relative, under
 // 1e-5 for the partial weights here)
@@ -1997,39 +2005,20 @@ __device__ __forceinline__ float fast_log(float x) {
   return __builtin_amdgcn_logf(x) * 0.69314718055994531f;
 }
 constexpr int kFusePre = 8;  // partial slots whose O values are preloaded
-constexpr int kFusePgPre = 2;  // page-mass entries per thread preloaded
 
 template <int D, int G>
 __device__ __attribute__((always_inline)) void fuse_unit(const Ctx &c, int i, int seq, int h,
                                                          const HeadInfo &hi, const UG &g,
-                                                         int maw_mode, int n_slots,
-                                                         const int32_t *__restrict__ selp, int cnt,
+                                                         bool with_maw, int n_slots,
                                                          const float *__restrict__ o_part,
                                                          const float *__restrict__ lse_part,
                                                          int p_cap, float *__restrict__ o,
-                                                         float *__restrict__ lse, FuseSmem<G> &sm,
-                                                         const unsigned long long *seltag = nullptr,
-                                                         uint32_t epoch = 0) {
+                                                         float *__restrict__ lse, FuseSmem<G> &sm) {
   const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
   const int qh0 = h * G;
-  n_slots = min(n_slots, kFuseSlots);
-  // selection entry j: from the tagged copy (waiting, bounded, for its tag)
-  // or the plain list
-  auto sel_ld = [&](int j) -> int {
-    if (!seltag) return ld_dev(&selp[j]);
-    unsigned long long e = ld_dev(&seltag[j]);
-    const unsigned long long t0 = wall_clock64();
-    while ((uint32_t)(e >> 32) != epoch && wall_clock64() - t0 < kWaitTicks) e = ld_dev(&seltag[j]);
-    return (uint32_t)(e >> 32) == epoch ? (int)(uint32_t)e : 0;
-  };
-  const bool with_maw = maw_mode != kMawNone;
+  n_slots = min(n_slots, kFuseSlots);  // (the host keeps every call within it)
   const DenseList dl = with_maw ? dense_list(g) : DenseList{0, 0, 0, 0};
-  const int PPB = with_maw ? g.S / kPage : 1;
-  cnt = with_maw ? min(cnt, hi.kcap) : 0;
-  const int n_pg = dl.n + cnt * PPB;  // attended pages of the unit
-  const bool sel_lds = cnt <= kFuseSelLds;
   const float *lmb = c.sc.lm_pg + ((size_t)seq * c.dm.Hq + qh0) * c.dm.lm_cap;
-  auto pg_slot = [&](int t) { return t < dl.n ? t : c.dm.lm_sel0 + (t - dl.n); };
 
   // ---- one batch of loads ---------------------------------------------------
   constexpr int R = kFuseSlots / 64;
@@ -2060,22 +2049,12 @@ __device__ __attribute__((always_inline)) void fuse_unit(const Ctx &c, int i, in
   float4 ov[kFusePre];
 #pragma unroll
   for (int u = 0; u < kFusePre; ++u) ov[u] = ld_o(u, o_on && u < n_slots);
-  float lmv[kFusePgPre][G];
+  // log-masses of the dense pages (list positions [0, dl.n)): one per thread
+  // here, the rest (windows of more than 4096 tokens) after the O sums
+  float lmv[G];
 #pragma unroll
-  for (int t = 0; t < kFusePgPre; ++t) {
-    const int x = tid + 256 * t;
-#pragma unroll
-    for (int gg = 0; gg < G; ++gg)
-      lmv[t][gg] = x < n_pg ? ld_dev(&lmb[(size_t)gg * c.dm.lm_cap + pg_slot(x)]) : -INFINITY;
-  }
-  // the selection: a plain list here; a tagged one (whose reads wait for
-  // their tags) only its first 256 entries here, the rest after the O sums
-  int selv[kFuseSelLds / 256];
-#pragma unroll
-  for (int t = 0; t < kFuseSelLds / 256; ++t) {
-    const int x = tid + 256 * t;
-    selv[t] = (sel_lds && x < cnt && (t == 0 || !seltag)) ? sel_ld(x) : 0;
-  }
+  for (int gg = 0; gg < G; ++gg)
+    lmv[gg] = tid < dl.n ? ld_dev(&lmb[(size_t)gg * c.dm.lm_cap + tid]) : -INFINITY;
 
   // ---- per-head lse and slot weights ----------------------------------------
 #pragma unroll
@@ -2102,14 +2081,6 @@ __device__ __attribute__((always_inline)) void fuse_unit(const Ctx &c, int i, in
       sm.w[gg][u] = (L == -INFINITY || l[r] == -INFINITY) ? 0.0f : fast_exp(l[r] - L);
     }
   }
-#pragma unroll
-  for (int t = 0; t < kFuseSelLds / 256; ++t) {
-    const int x = tid + 256 * t;
-    if (sel_lds && x < cnt && (t == 0 || !seltag)) sm.sel[x] = selv[t];
-  }
-  const bool dsel_lds = with_maw && g.n_dt <= kFuseDense;
-  if (dsel_lds)
-    for (int x = tid; x < g.n_dt; x += 256) sm.dsel[x] = -1;
   __syncthreads();
   // ---- O = sum_u w_u O_u (zero weights select 0), each channel in slot order
   float4 acc = make_float4(0.0f, 0.0f, 0.0f, 0.0f);
@@ -2140,121 +2111,74 @@ __device__ __attribute__((always_inline)) void fuse_unit(const Ctx &c, int i, in
     od[3] = acc.w;
   }
   if (tid < G) lse[(size_t)i * c.dm.Hq + qh0 + tid] = sm.lse[tid];
-  if (!with_maw) return;
-  // the rest of a tagged selection: every load in flight at once, then a
-  // bounded re-read of any entry whose tag is not yet this step's (each
-  // thread reads back only the entries it writes until the barrier below)
-  if (seltag && sel_lds)
-    for (int x0 = tid + 256; x0 < cnt; x0 += 4 * 256) {
-      unsigned long long e[4];
-#pragma unroll
-      for (int t = 0; t < 4; ++t) {
-        const int x = x0 + 256 * t;
-        e[t] = x < cnt ? ld_dev(&seltag[x]) : ((unsigned long long)epoch << 32);
-      }
-#pragma unroll
-      for (int t = 0; t < 4; ++t) {
-        const int x = x0 + 256 * t;
-        if (x < cnt) sm.sel[x] = (uint32_t)(e[t] >> 32) == epoch ? (int)(uint32_t)e[t] : sel_ld(x);
-      }
-    }
+  if (!with_maw || g.n_dt == 0) return;
 
   // ---- MAW -------------------------------------------------------------------
-  // softmax mass of every attended page summed over the heads, into LDS
-  auto page_mass = [&](const float (&lm)[G]) {
+  // per head, lse_D of the dense partial: each thread folds its pages into a
+  // running (max, sum), then the waves', then the workgroup's
+  float mt[G], zt[G];
+#pragma unroll
+  for (int gg = 0; gg < G; ++gg) {
+    mt[gg] = lmv[gg];
+    zt[gg] = lmv[gg] == -INFINITY ? 0.0f : 1.0f;
+  }
+  auto fold = [&](int gg, float x) {
+    if (x == -INFINITY) return;
+    if (x > mt[gg]) {
+      zt[gg] = zt[gg] * fast_exp(mt[gg] - x) + 1.0f;  // (exp(-inf) = 0)
+      mt[gg] = x;
+    } else {
+      zt[gg] += fast_exp(x - mt[gg]);
+    }
+  };
+  for (int t = tid + 256; t < dl.n; t += 256)
+#pragma unroll
+    for (int gg = 0; gg < G; ++gg) fold(gg, ld_dev(&lmb[(size_t)gg * c.dm.lm_cap + t]));
+#pragma unroll
+  for (int gg = 0; gg < G; ++gg) {
+    const float M = wave_max(mt[gg]);
+    const float z = wave_sum(M == -INFINITY || mt[gg] == -INFINITY ? 0.0f
+                                                                   : zt[gg] * fast_exp(mt[gg] - M));
+    if (lane == 0) {
+      sm.dm[wv][gg] = M;
+      sm.dz[wv][gg] = z;
+    }
+  }
+  __syncthreads();
+  float lse_d[G];
+#pragma unroll
+  for (int gg = 0; gg < G; ++gg) {
+    const float M = fmaxf(fmaxf(sm.dm[0][gg], sm.dm[1][gg]), fmaxf(sm.dm[2][gg], sm.dm[3][gg]));
+    float z = 0.0f;
+    if (M != -INFINITY)
+#pragma unroll
+      for (int w = 0; w < 4; ++w)
+        z += sm.dm[w][gg] == -INFINITY ? 0.0f : sm.dz[w][gg] * fast_exp(sm.dm[w][gg] - M);
+    lse_d[gg] = M == -INFINITY ? -INFINITY : M + fast_log(z);
+  }
+  // mass of each dense page under the dense partial, summed over the heads
+  for (int t = tid; t < dl.n; t += 256) {
     float a = 0.0f;
 #pragma unroll
     for (int gg = 0; gg < G; ++gg) {
-      const float L = sm.lse[gg];
-      a += (L == -INFINITY || lm[gg] == -INFINITY) ? 0.0f : fast_exp(lm[gg] - L);
+      const float x = t < 256 ? lmv[gg] : ld_dev(&lmb[(size_t)gg * c.dm.lm_cap + t]);
+      a += (x == -INFINITY || lse_d[gg] == -INFINITY) ? 0.0f : fast_exp(x - lse_d[gg]);
     }
-    return a;
-  };
-  auto page_mass_at = [&](int t) {
-    float lm[G];
-#pragma unroll
-    for (int gg = 0; gg < G; ++gg) lm[gg] = ld_dev(&lmb[(size_t)gg * c.dm.lm_cap + pg_slot(t)]);
-    return page_mass(lm);
-  };
-  const int n_pg_lds = min(n_pg, kFusePgLds);
-#pragma unroll
-  for (int t = 0; t < kFusePgPre; ++t) {
-    const int x = tid + 256 * t;
-    if (x < n_pg_lds) sm.pm[x] = page_mass(lmv[t]);
+    sm.pm[t] = a;
   }
-  for (int x0 = tid + 256 * kFusePgPre; x0 < n_pg_lds; x0 += 2 * 256) {
-    float lm[2][G];
-#pragma unroll
-    for (int u = 0; u < 2; ++u) {
-      const int x = x0 + 256 * u;
-#pragma unroll
-      for (int gg = 0; gg < G; ++gg)
-        lm[u][gg] = x < n_pg_lds ? ld_dev(&lmb[(size_t)gg * c.dm.lm_cap + pg_slot(x)]) : -INFINITY;
-    }
-#pragma unroll
-    for (int u = 0; u < 2; ++u)
-      if (x0 + 256 * u < n_pg_lds) sm.pm[x0 + 256 * u] = page_mass(lm[u]);
-  }
-  // selection index of each selected block that touches dense tokens
-  if (dsel_lds && sel_lds)
-    for (int j = tid; j < cnt; j += 256) {
-      const int blk = sm.sel[j];
-      if (blk < g.hb) sm.dsel[blk] = j;
-      else if (blk >= g.tb && blk < g.n_blk) sm.dsel[g.hb + (blk - g.tb)] = j;
-    }
   __syncthreads();
-  auto pm = [&](int t) { return t < n_pg_lds ? sm.pm[t] : page_mass_at(t); };
-  auto sel_at = [&](int j) { return sel_lds ? sm.sel[j] : sel_ld(j); };
-  // position of blk in the selection, or -1: a scan of a short selection (the
-  // fast top-k's, in key order), else a binary search (ascending order)
-  auto sel_find = [&](int blk) {
-    if (cnt <= kTileList) {
-      for (int j = 0; j < cnt; ++j)
-        if (sel_at(j) == blk) return j;
-      return -1;
-    }
-    int lo = 0, hi2 = cnt;
-    while (lo < hi2) {
-      const int mid = (lo + hi2) >> 1;
-      if (sel_at(mid) < blk) lo = mid + 1; else hi2 = mid;
-    }
-    return (lo < cnt && sel_at(lo) == blk) ? lo : -1;
-  };
-  auto sel_pages_mass = [&](int j) {
-    float a = 0.0f;
-    for (int pp = 0; pp < PPB; ++pp) a += pm(dl.n + j * PPB + pp);
-    return a;
-  };
   float *mw = c.L.maw + hi.maw_off + (size_t)seq * hi.nbmax;
-  const float r = c.dm.maw_decay, omr = 1.0f - r;
-  if (maw_mode == kMawFull) {  // decay here (the one-launch step's score tiles do it there)
-    for (int blk = tid; blk < g.n_blk; blk += 256) st_dev(&mw[blk], __fmul_rn(r, ld_dev(&mw[blk])));
-    wait_vmem();
-    __syncthreads();
-  }
-  // attended blocks: dense-touching ones (with their selected pages, if any),
-  // then selected blocks that touch no dense token; one atomic add each, so
-  // both modes round identically
-  const float inv_g = 1.0f / (float)G;
-  for (int x = tid; x < g.n_dt + cnt; x += 256) {
-    int blk;
+  const float r = c.dm.maw_decay, omr = 1.0f - r, inv_g = 1.0f / (float)G;
+  const int PPB = g.S / kPage;
+  for (int x = tid; x < g.n_dt; x += 256) {
+    const int blk = dense_block(g, x);
+    if (is_candidate(g, blk)) continue;  // a token outside D: frozen
     float a = 0.0f;
-    if (x < g.n_dt) {
-      blk = dense_block(g, x);
-      for (int pp = 0; pp < PPB; ++pp) {
-        const int t = dense_pos(dl, blk * PPB + pp);
-        if (t >= 0) a += pm(t);
-      }
-      const int j = (dsel_lds && sel_lds) ? sm.dsel[x] : sel_find(blk);
-      if (j >= 0) a += sel_pages_mass(j);
-    } else {
-      const int j = x - g.n_dt;
-      blk = sel_at(j);
-      if (blk < g.hb || blk >= g.tb) continue;  // counted with the dense entry
-      a = sel_pages_mass(j);
+    for (int pp = 0; pp < PPB; ++pp) {
+      const int t = dense_pos(dl, blk * PPB + pp);
+      if (t >= 0) a += sm.pm[t];
     }
-    __hip_atomic_fetch_add(&mw[blk], __fmul_rn(omr, a * inv_g), __ATOMIC_RELAXED,
-                           __HIP_MEMORY_SCOPE_AGENT);
+    mw[blk] = __fadd_rn(__fmul_rn(r, mw[blk]), __fmul_rn(omr, a * inv_g));
   }
 }
 
@@ -2304,7 +2228,7 @@ __global__ __launch_bounds__(256) void k_select(Ctx c, SeqBatch b, int tiles_x,
     return;
   }
   UG g;
-  score_tile<D, G>(c, i, seq, h, hi, N, n_blk, tile, q, smem_topk, false, false, g);
+  score_tile<D, G>(c, i, seq, h, hi, N, n_blk, tile, q, smem_topk, false, g);
   uint32_t *ctr = &c.sc.arrive[((size_t)seq * c.dm.Hkv + h) * 2];
   if (!arrive_last(ctr, (unsigned)n_tiles, &smem_topk.last)) return;
   uint32_t *lrows = reinterpret_cast<uint32_t *>(smem_raw + sizeof(TopkSmem));
@@ -2319,8 +2243,8 @@ __global__ __launch_bounds__(256) void k_select(Ctx c, SeqBatch b, int tiles_x,
 }
 
 // attend, separate-call form: P workgroups per unit, of which the unit's
-// parts (unit_parts) write one partial each; part 0 also keeps a copy of the
-// selection for the fusion call and empties the other slots up to p_cap.
+// parts (unit_parts) write one partial each; part 0 also empties the other
+// slots up to p_cap.
 template <int D, int G>
 __global__ __launch_bounds__(256, 2) void k_attend(Ctx c, SeqBatch b, int P,
                                                    const uint16_t *__restrict__ q,
@@ -2337,15 +2261,10 @@ __global__ __launch_bounds__(256, 2) void k_attend(Ctx c, SeqBatch b, int P,
   const UG g = unit_geom(b.len[i], hi, c.dm);
   const int PU = unit_parts(g, P);
   if (part >= PU) return;
-  const size_t unit = (size_t)seq * c.dm.Hkv + h;
   SelIn si;
   si.blk = blk_idx + ((size_t)i * c.dm.Hkv + h) * k_cap;
   si.cnt = min(min(max(blk_cnt[(size_t)i * c.dm.Hkv + h], 0), k_cap), hi.kcap);
-  if (part == 0) {
-    for (int j = threadIdx.x; j < si.cnt; j += 256) st_dev(&c.sc.usel[unit * c.dm.kcap + j], si.blk[j]);
-    if (threadIdx.x == 0) st_dev(&c.sc.ucnt[unit], si.cnt);
-    empty_slots<D, G>(c, i, h, PU, p_cap, o_part, lse_part);
-  }
+  if (part == 0) empty_slots<D, G>(c, i, h, PU, p_cap, o_part, lse_part);
   attend_part<D, G>(c, i, seq, h, g, part, PU, q, si, o_part, lse_part, p_cap, sm, nullptr,
                     &s_cnt);
 }
@@ -2353,10 +2272,9 @@ __global__ __launch_bounds__(256, 2) void k_attend(Ctx c, SeqBatch b, int P,
 // One decode step in one launch.  Workgroups by index: score tiles (the last
 // of a unit runs its top-k and publishes the selection, tagged with the step
 // number), then P attention parts per unit (a unit uses unit_parts of them,
-// the rest exit at once).  A part streams its dense pages once the unit's
-// score tiles are done, then waits for the selection and streams its
-// selected pages; the last part of a unit to finish fuses the partials and
-// updates MAW.  Workgroups start in index order on each XCD and
+// the rest exit at once).  A part streams its dense pages from the start,
+// then waits for the selection and streams its selected pages; the last part
+// of a unit to finish fuses the partials and updates MAW.  Workgroups start in index order on each XCD and
 // every wait is on a score tile, which never waits, so no wait is on a
 // workgroup that cannot start; each wait is also bounded in time (after
 // kWaitTicks it gives up and raises the error flag).
@@ -2397,7 +2315,7 @@ __global__ __launch_bounds__(256, 2) void k_step(Ctx c, SeqBatch b, int tiles_x,
     __builtin_amdgcn_s_setprio(2);
     // without MAW flags each tile also lists its candidates for the fast top-k
     UG g;
-    const bool fast = score_tile<D, G>(c, i, seq, h, hi, N, n_blk, idx, q, smem_topk, true,
+    const bool fast = score_tile<D, G>(c, i, seq, h, hi, N, n_blk, idx, q, smem_topk,
                                        c.dm.maw_beta <= 0.0f && n_tiles <= kFastTiles, g);
     uint32_t *ctr = &c.sc.arrive[unit * 2];
     if (!arrive_last(ctr, (unsigned)n_tiles, &s_flag)) return;
@@ -2451,7 +2369,7 @@ __global__ __launch_bounds__(256, 2) void k_step(Ctx c, SeqBatch b, int tiles_x,
   }
   if (idx == 0) empty_slots<D, G>(c, i, h, PU, p_cap, o_part, lse_part);
   // a unit that selects nothing has no score tiles: its parts take the dense
-  // pages only, part 0 writes the count, the fusion decays every block's MAW
+  // pages only and part 0 writes the count
   const bool no_sel = selects_nothing(hi, N, c.dm);
   if (no_sel && idx == 0 && threadIdx.x == 0) st_dev(&blk_cnt[(size_t)i * c.dm.Hkv + h], 0);
   SelIn si;
@@ -2464,15 +2382,12 @@ __global__ __launch_bounds__(256, 2) void k_step(Ctx c, SeqBatch b, int tiles_x,
   uint32_t *fctr = &c.sc.arrive[unit * 2 + 1];
   if (!arrive_last(fctr, (unsigned)PU, &s_flag)) return;
   __builtin_amdgcn_s_setprio(3);
-  // this step's count, seen by every part
-  const int cnt = no_sel ? 0 : (int)(uint32_t)ld_dev(&c.sc.rtag[unit]);
-  fuse_unit<D, G>(c, i, seq, h, hi, g, no_sel ? kMawFull : kMawAdd, PU, nullptr, cnt, o_part,
-                  lse_part, p_cap, o, lse, smem_fuse, c.sc.seltag + unit * c.dm.kcap, epoch);
+  fuse_unit<D, G>(c, i, seq, h, hi, g, true, PU, o_part, lse_part, p_cap, o, lse, smem_fuse);
   if (threadIdx.x == 0) st_dev(fctr, 0u);
 }
 
 // fuse, separate-call form: one workgroup per unit over the partial slots of
-// its parts out of the attend call's P (layer call: selection and page masses
+// its parts out of the attend call's P (layer call: the dense pages' masses
 // from the attend call) or over every slot of p_cap (pure fusion).
 template <int D, int G>
 __global__ __launch_bounds__(256) void k_fuse(Ctx c, SeqBatch b, int with_maw, int P,
@@ -2484,13 +2399,11 @@ __global__ __launch_bounds__(256) void k_fuse(Ctx c, SeqBatch b, int with_maw, i
   const HeadInfo hi = c.heads[h];
   if (with_maw) {
     const UG g = unit_geom(b.len[i], hi, c.dm);
-    const size_t unit = (size_t)b.seq[i] * c.dm.Hkv + h;
-    fuse_unit<D, G>(c, i, b.seq[i], h, hi, g, kMawFull, unit_parts(g, P), c.sc.usel + unit * c.dm.kcap,
-                    ld_dev(&c.sc.ucnt[unit]), o_part, lse_part, p_cap, o, lse, sm);
+    fuse_unit<D, G>(c, i, b.seq[i], h, hi, g, true, unit_parts(g, P), o_part, lse_part, p_cap, o,
+                    lse, sm);
   } else {
     UG g{};
-    fuse_unit<D, G>(c, i, 0, h, hi, g, kMawNone, p_cap, nullptr, 0, o_part, lse_part, p_cap, o,
-                    lse, sm);
+    fuse_unit<D, G>(c, i, 0, h, hi, g, false, p_cap, o_part, lse_part, p_cap, o, lse, sm);
   }
 }
 

@@ -268,6 +268,10 @@ sd_status sparse_decode_init(const sd_config *cfg, sd_ctx **out) {
     return fail(c, SD_EUNSUPPORTED,
                 "%d partial slots per head exceed the fusion limit %d (lower the budget "
                 "or max_seq_len, or raise the block size)", c->p_cap, kFuseSlots);
+  if (lm_sel0 > kFuseDenseLds)
+    return fail(c, SD_EUNSUPPORTED,
+                "sinks %d + recent window %d span up to %d pages, more than the %d the fusion "
+                "holds", cfg->sink_tokens, cfg->recent_window, lm_sel0, kFuseDenseLds);
   sd_status s;
   if ((s = dev_alloc(c, &c->d_heads, c->Hkv)) != SD_OK) return s;
   SD_HIP(c, hipMemcpy(c->d_heads, c->heads.data(), sizeof(HeadInfo) * c->Hkv,
@@ -302,10 +306,7 @@ sd_status sparse_decode_init(const sd_config *cfg, sd_ctx **out) {
   if ((s = dev_alloc(c, &c->sc.unit_acc, (size_t)max_seqs * c->Hkv * 2)) != SD_OK) return s;
   SD_HIP(c, hipMemset(c->sc.unit_acc, 0, sizeof(uint32_t) * max_seqs * c->Hkv * 2));
   if ((s = dev_alloc(c, &c->sc.lm_pg, (size_t)max_seqs * c->Hq * c->dims.lm_cap)) != SD_OK) return s;
-  if ((s = dev_alloc(c, &c->sc.usel, (size_t)max_seqs * c->Hkv * c->k_cap)) != SD_OK) return s;
-  if ((s = dev_alloc(c, &c->sc.ucnt, (size_t)max_seqs * c->Hkv)) != SD_OK) return s;
   if ((s = dev_alloc(c, &c->sc.arrive, (size_t)max_seqs * c->Hkv * 2)) != SD_OK) return s;
-  SD_HIP(c, hipMemset(c->sc.ucnt, 0, sizeof(int32_t) * max_seqs * c->Hkv));
   SD_HIP(c, hipMemset(c->sc.arrive, 0, sizeof(uint32_t) * max_seqs * c->Hkv * 2));
   if ((s = dev_alloc(c, &c->sc.cand, per_unit)) != SD_OK) return s;
   if ((s = dev_alloc(c, &c->sc.rtag, (size_t)max_seqs * c->Hkv)) != SD_OK) return s;
@@ -596,6 +597,9 @@ sd_status fuse_lse(sd_ctx *c, int32_t layer, int32_t n_seqs,
     return fail(c, SD_EINVAL, "o_part must be 16-byte aligned");
   const bool with_maw = layer >= 0;
   if (layer < -1) return fail(c, SD_EINVAL, "layer %d < -1", layer);
+  if (!with_maw && p_cap > kFuseSlots)
+    return fail(c, SD_EUNSUPPORTED, "pure fusion of p_cap %d > %d partial slots per head",
+                p_cap, kFuseSlots);
   if (with_maw) {
     sd_status s = check_seqs(c, layer, n_seqs, seq_ids);
     if (s != SD_OK) return s;

@@ -101,7 +101,10 @@ sd_status sd_validate_config(const sd_config *cfg, char *err, size_t err_len);
 
 /* Create a context on the current HIP device: allocates the per-layer KV
  * pools [num_pages][Hkv][16][d] bf16 (K and V), page tables, block summaries,
- * MAW tables and scratch.  All sequences start empty. */
+ * MAW tables and scratch.  All sequences start empty.  SD_EUNSUPPORTED if a
+ * unit could need more than 256 partial slots per query head (budget x
+ * max_seq_len too large for the block size) or if the sinks and the recent
+ * window span more than 2048 pages. */
 sd_status sparse_decode_init(const sd_config *cfg, sd_ctx **out);
 
 /* Synchronise the stream and free every device buffer of the context. */
@@ -145,8 +148,9 @@ sd_status select_topk(sd_ctx *ctx, int32_t layer, int32_t n_seqs,
  * o_part[n][h][p][:] (fp32, normalised within the part) and
  * lse_part[n][h][p] (natural log of the part's sum of exp(scaled logits));
  * slots [P, p_cap) get lse = -inf and O = 0.  blk_idx / blk_cnt are as written by
- * select_topk (ascending, distinct); entries outside [0, n_blk) are ignored.
- * The per-block attention mass needed by fuse_lse is kept inside the context
+ * select_topk (ascending, distinct; a repeated entry would count its tokens
+ * twice); entries outside [0, n_blk) attend nothing.  The log softmax mass of
+ * each dense page, which fuse_lse needs for MAW, is kept inside the context
  * for this layer. */
 sd_status sparse_attend(sd_ctx *ctx, int32_t layer, int32_t n_seqs,
                         const int32_t *seq_ids, const void *q_bf16,
@@ -158,26 +162,38 @@ sd_status sparse_attend(sd_ctx *ctx, int32_t layer, int32_t n_seqs,
  * max-subtracted form): lse = m + log sum_p e^{lse_p - m}, O = sum_p
  * e^{lse_p - lse} O_p; parts with lse = -inf drop out.  o: dev [n_seqs][Hq][d]
  * fp32, lse: dev [n_seqs][Hq] fp32.
- * layer >= 0: must follow sparse_attend of the same layer and sequences; the
- * MAW of every block of each (sequence, KV head) is then updated as
- * MAW <- r*MAW + (1-r)*a with a the group-mean softmax mass of the block
- * (0 if not attended) ([LFPS] decay; [HGCA] MAW).
- * layer == -1: pure fusion of n_seqs*Hq heads, no MAW (seq_ids may be NULL).
+ * layer >= 0: must follow sparse_attend of the same layer and sequences
+ * (SD_ESTATE otherwise); MAW of each (sequence, KV head) is then updated
+ * from the dense partial alone ([HGCA] What carries the argument and the
+ * referee report on section 3.2.2 / Algorithm 1: the moving average is fed by
+ * the GPU-side window's weights, normalised over that window, and frozen once
+ * an entry has left it; [LFPS] decay r): every block whose tokens all lie in
+ * D takes MAW <- r*MAW + (1-r)*a, a = the group-mean mass of the block under
+ * the softmax over D alone; every other block keeps its MAW.
+ * layer == -1: pure fusion of n_seqs*Hq heads over all p_cap slots, no MAW
+ * (seq_ids may be NULL); p_cap <= 256 (SD_EUNSUPPORTED otherwise).
  * o_part must be 16-byte aligned (SD_EINVAL otherwise). */
 sd_status fuse_lse(sd_ctx *ctx, int32_t layer, int32_t n_seqs,
                    const int32_t *seq_ids, const float *o_part,
                    const float *lse_part, int32_t p_cap, float *o, float *lse);
 
-/* Fused decode step of one layer: the optional append of one token per
- * sequence (k_new, v_new: dev [n_seqs][Hkv][d] bf16, both NULL to skip), then
- * select_topk + sparse_attend + fuse_lse with bitwise identical results, in
- * one launch per 64 sequences (after the append's): block scoring with the
- * top-k of each (sequence, KV head) done by its last scoring workgroup, the
- * attention parts, and the LSE fusion and MAW update done by the last part of
- * each (sequence, KV head).
+/* Fused decode step of one layer ([HGCA] Figure 2: the append process, then
+ * the decode process; [SPIN] Figure 3: select, then attend; [HGCA] What
+ * carries the argument: partials merged by the exact LSE identity): the
+ * optional append of one token per sequence (k_new, v_new: dev
+ * [n_seqs][Hkv][d] bf16, both NULL to skip), then select_topk +
+ * sparse_attend + fuse_lse, in one launch per 64 sequences (after the
+ * append's): block scoring with the top-k of each (sequence, KV head) done by
+ * its last scoring workgroup, the attention parts, and the LSE fusion and MAW
+ * update done by the last part of each (sequence, KV head).  The selection
+ * and MAW equal the separate calls' bit for bit; O and lse equal them to fp32
+ * rounding (the step visits the selected pages in key order, the separate
+ * attend call in ascending order).
  * blk_idx/blk_cnt/o_part/lse_part are written as by the separate calls, except
  * that partial slots a unit does not use are left unspecified.  o_part must be
- * 16-byte aligned (SD_EINVAL otherwise). */
+ * 16-byte aligned (SD_EINVAL otherwise).  A selection wait that runs out of
+ * time (it cannot in a correct launch) makes the next sd_sync return
+ * SD_EHIP. */
 sd_status sparse_decode_step(sd_ctx *ctx, int32_t layer, int32_t n_seqs,
                              const int32_t *seq_ids, const void *k_new,
                              const void *v_new, const void *q_bf16,

@@ -145,12 +145,13 @@ int32_t oracle_maw_flag(double maw, int64_t n_dense, double beta, int32_t S) {
   return maw * (double)n_dense > beta * (double)S;
 }
 
-/* Ordering context for qsort (the oracle is single-threaded by design). */
+/* Ordering context for qsort, one per thread (the oracle's functions may be
+ * called from several threads at once, one unit each). */
 typedef struct {
   const float *u;
   const int8_t *flag;
 } order_ctx;
-static order_ctx g_order;
+static _Thread_local order_ctx g_order;
 
 /* R5/R11: (flag desc, score desc, index asc) - a total order. */
 static int cmp_blocks(const void *pa, const void *pb) {

@@ -138,63 +138,91 @@ def compare_outputs(O_gpu, lse_gpu, O_ref, lse_ref):
     return max_abs, max_rel, max_dlse
 
 
-def check_units(w, eng, layer, seq_ids, q_bits, K_bits, V_bits, N_of, gpu,
-                maw_state=None, units=None, check_summ=True):
-    """Oracle each (sequence, KV head) unit and compare with the GPU result.
-    K_bits/V_bits: dict seq -> [N, Hkv, d] uint16.  maw_state: dict
-    (seq, g) -> oracle MAW (updated in place) or None.  Returns stats."""
+def _check_unit(w, seq, bi, g, N, q_bits, K_bits, V_bits, gpu, summ, maw_gpu, maw_state):
+    """Oracle one (sequence, KV head) unit and compare it with the GPU's."""
     G = w.G
-    stats = dict(units=[], ties=0, max_abs=0.0, max_rel=0.0, max_dlse=0.0,
-                 max_dmaw=0.0)
+    S, ppm = w.block_size[g], w.budget_ppm[g]
+    beta = w.maw_beta if maw_state is not None else 0.0
+    qg = q_bits[bi, g * G:(g + 1) * G]
+    Kg = np.ascontiguousarray(K_bits[seq][:N, g])
+    Vg = np.ascontiguousarray(V_bits[seq][:N, g])
+    mb = None if maw_state is None else maw_state.get((seq, g), np.zeros(0))
+    ores = oracle.unit_step(qg, Kg, Vg, N, S, w.n_sink, w.window, ppm,
+                            maw=mb, beta=beta, r=w.maw_decay)
+    cnt = int(gpu["blk_cnt"][bi, g])
+    assert cnt == ores["k"], "k differs: gpu %d oracle %d (seq %d head %d)" % (
+        cnt, ores["k"], seq, g)
+    gsel = gpu["blk_idx"][bi, g, :cnt]
+    assert np.all(np.diff(gsel) > 0), "GPU selection not ascending"
+    nd = oracle.dense_count(N, w.n_sink, w.window)
+    ties = adjudicate(gsel, ores, cnt, ores.get("maw_before"), nd, beta, S)
+    flagged = int(ores["flag"][ores["sel"]].sum()) if ores["k"] else 0
+    if ties:
+        ores = oracle.unit_step(qg, Kg, Vg, N, S, w.n_sink, w.window, ppm,
+                                maw=mb, beta=beta, r=w.maw_decay, sel_override=gsel)
+    r = dict(ties=ties, flagged=flagged)
+    O_gpu = gpu["o"][bi, g * G:(g + 1) * G]
+    lse_gpu = gpu["lse"][bi, g * G:(g + 1) * G]
+    r["max_abs"], r["max_rel"], r["max_dlse"] = compare_outputs(O_gpu, lse_gpu, ores["O"],
+                                                                ores["lse"])
+    if summ is not None:
+        mn, mx = summ[g]
+        f = lambda a: synth.from_bits(a).float().numpy()
+        assert np.array_equal(f(mn), f(ores["mn"])), "min summaries differ"
+        assert np.array_equal(f(mx), f(ores["mx"])), "max summaries differ"
+    r["max_dmaw"] = 0.0
+    if maw_state is not None:
+        ref = ores["maw"]
+        got = maw_gpu[g]
+        assert got.shape == ref.shape
+        dm = np.abs(got - ref)
+        assert np.all(dm <= MAW_ABS + MAW_REL * np.abs(ref)), (
+            "MAW differs: max %g" % dm.max())
+        r["max_dmaw"] = float(dm.max()) if dm.size else 0.0
+        r["maw"] = ref
+    return r
+
+
+def check_units(w, eng, layer, seq_ids, q_bits, K_bits, V_bits, N_of, gpu,
+                maw_state=None, units=None, check_summ=True, workers=1):
+    """Oracle each (sequence, KV head) unit and compare with the GPU result.
+    K_bits/V_bits: dict seq -> [>=N, Hkv, d] uint16.  maw_state: dict
+    (seq, g) -> oracle MAW (updated in place) or None.  workers > 1 runs the
+    units' oracles in threads (the C oracle releases the GIL).  Returns stats;
+    "flagged" counts selected blocks that the oracle's MAW flag ranked first."""
+    jobs = []
     for bi, seq in enumerate(seq_ids):
+        if units is not None and not any((seq, g) in units for g in range(w.Hkv)):
+            continue
         N = N_of[seq]
         summ = summaries_by_head(eng, layer, seq, w, N) if check_summ else None
         maw_gpu = maw_by_head(eng, layer, seq, w, N) if maw_state is not None else None
         for g in range(w.Hkv):
             if units is not None and (seq, g) not in units:
                 continue
-            S, ppm = w.block_size[g], w.budget_ppm[g]
-            qg = q_bits[bi, g * G:(g + 1) * G]
-            Kg = np.ascontiguousarray(K_bits[seq][:N, g])
-            Vg = np.ascontiguousarray(V_bits[seq][:N, g])
-            mb = None if maw_state is None else maw_state.get((seq, g), np.zeros(0))
-            ores = oracle.unit_step(qg, Kg, Vg, N, S, w.n_sink, w.window, ppm,
-                                    maw=mb, beta=w.maw_beta if maw_state is not None else 0.0,
-                                    r=w.maw_decay)
-            cnt = int(gpu["blk_cnt"][bi, g])
-            assert cnt == ores["k"], "k differs: gpu %d oracle %d (seq %d head %d)" % (
-                cnt, ores["k"], seq, g)
-            gsel = gpu["blk_idx"][bi, g, :cnt]
-            assert np.all(np.diff(gsel) > 0), "GPU selection not ascending"
-            nd = oracle.dense_count(N, w.n_sink, w.window)
-            ties = adjudicate(gsel, ores, cnt, ores.get("maw_before"), nd,
-                              w.maw_beta if maw_state is not None else 0.0, S)
-            if ties:
-                ores = oracle.unit_step(qg, Kg, Vg, N, S, w.n_sink, w.window, ppm,
-                                        maw=mb, beta=w.maw_beta if maw_state is not None else 0.0,
-                                        r=w.maw_decay, sel_override=gsel)
-            stats["ties"] += ties
-            O_gpu = gpu["o"][bi, g * G:(g + 1) * G]
-            lse_gpu = gpu["lse"][bi, g * G:(g + 1) * G]
-            ma, mr, ml = compare_outputs(O_gpu, lse_gpu, ores["O"], ores["lse"])
-            stats["max_abs"] = max(stats["max_abs"], ma)
-            stats["max_rel"] = max(stats["max_rel"], mr)
-            stats["max_dlse"] = max(stats["max_dlse"], ml)
-            if check_summ:
-                mn, mx = summ[g]
-                f = lambda a: synth.from_bits(a).float().numpy()
-                assert np.array_equal(f(mn), f(ores["mn"])), "min summaries differ"
-                assert np.array_equal(f(mx), f(ores["mx"])), "max summaries differ"
-            if maw_state is not None:
-                ref = ores["maw"]
-                got = maw_gpu[g]
-                assert got.shape == ref.shape
-                dm = np.abs(got - ref)
-                assert np.all(dm <= MAW_ABS + MAW_REL * np.abs(ref)), (
-                    "MAW differs: max %g" % dm.max())
-                stats["max_dmaw"] = max(stats["max_dmaw"], float(dm.max()) if dm.size else 0.0)
-                maw_state[(seq, g)] = ref
-            stats["units"].append((seq, g))
+            jobs.append((seq, bi, g, N, summ, maw_gpu))
+
+    def run(j):
+        seq, bi, g, N, summ, maw_gpu = j
+        return _check_unit(w, seq, bi, g, N, q_bits, K_bits, V_bits, gpu, summ, maw_gpu,
+                           maw_state)
+
+    if workers > 1 and len(jobs) > 1:
+        import concurrent.futures as cf
+        with cf.ThreadPoolExecutor(min(workers, len(jobs))) as ex:
+            res = list(ex.map(run, jobs))
+    else:
+        res = [run(j) for j in jobs]
+    stats = dict(units=[], ties=0, flagged=0, max_abs=0.0, max_rel=0.0, max_dlse=0.0,
+                 max_dmaw=0.0)
+    for (seq, bi, g, N, _, _), r in zip(jobs, res):
+        for k in ("ties", "flagged"):
+            stats[k] += r[k]
+        for k in ("max_abs", "max_rel", "max_dlse", "max_dmaw"):
+            stats[k] = max(stats[k], r[k])
+        if maw_state is not None:
+            maw_state[(seq, g)] = r["maw"]
+        stats["units"].append((seq, g))
     return stats
 
 

@@ -14,6 +14,7 @@ import oracle
 import synth
 from tests import harness
 from tests.harness import log
+from block_sparse_top_score_amd._abi import SDError
 
 pytestmark = pytest.mark.gpu
 
@@ -309,7 +310,55 @@ def test_error_paths():
         assert eng.decode_step(0, [0], q, bufs["blk_idx"], bufs["blk_cnt"], skew,
                                bufs["lse_part"], bufs["o"], bufs["lse"], check=False) == -1
         assert eng.seq_len(0, 0) == 2000
+        # pure fusion over more slots than the fusion holds: refused, nothing runs
+        wide_part = torch.zeros(1, w.Hq, 300, w.d, device="cuda")
+        wide_lse = torch.full((1, w.Hq, 300), -float("inf"), device="cuda")
+        assert eng.fuse_lse(-1, None, wide_part, wide_lse, bufs["o"], bufs["lse"], n_seqs=1,
+                            check=False) == -4
         eng.sync()
+    finally:
+        eng.close()
+    # sinks + window beyond the pages the fusion holds: refused at init
+    with pytest.raises(SDError) as e:
+        harness.make_engine(_w(synth.tiny(), window=40000), 41000)
+    assert e.value.status == -4
+
+
+def test_out_of_range_selection_entries_attend_nothing():
+    """sparse_attend skips blk_idx entries outside [0, n_blk): O and lse equal
+    the oracle's attention over the in-range entries, and MAW (fed by the
+    dense pages only) equals the oracle's."""
+    w = _w(synth.tiny(), N=1000)
+    log("case: out-of-range selection entries")
+    x = synth.single_step(w, 1, N=1000)
+    K, V, q = x["K"].cuda(), x["V"].cuda(), x["q"].cuda()
+    eng = harness.make_engine(w, 1064)
+    try:
+        harness.prefill(eng, 0, K, V)
+        bufs = eng.alloc_step(1)
+        eng.select_topk(0, [0], q, bufs["blk_idx"], bufs["blk_cnt"])
+        eng.sync()
+        cnt = int(bufs["blk_cnt"][0, 0])
+        nb = -(-1000 // 16)
+        assert cnt >= 3
+        bufs["blk_idx"][0, 0, 0] = -3
+        bufs["blk_idx"][0, 0, cnt - 1] = nb + 5
+        eng.sparse_attend(0, [0], q, bufs["blk_idx"], bufs["blk_cnt"], bufs["o_part"],
+                          bufs["lse_part"])
+        eng.fuse_lse(0, [0], bufs["o_part"], bufs["lse_part"], bufs["o"], bufs["lse"])
+        eng.sync()
+        sel = bufs["blk_idx"][0, 0, :cnt].cpu().numpy()
+        sel = sel[(sel >= 0) & (sel < nb)]
+        assert len(sel) == cnt - 2
+        Kb, Vb, qb = synth.bits(K[0, :, 0]), synth.bits(V[0, :, 0]), synth.bits(q[0])
+        ref = oracle.attend(qb, Kb, Vb, 1000, 16, w.n_sink, w.window, sel)
+        ma, mr, ml = harness.compare_outputs(bufs["o"][0].cpu().numpy(),
+                                             bufs["lse"][0].cpu().numpy(), ref["O"], ref["lse"])
+        harness.assert_parity(dict(max_abs=ma, max_rel=mr, max_dlse=ml))
+        a = oracle.dense_mass(qb, Kb, 1000, 16, w.n_sink, w.window)
+        want = oracle.maw_step(np.zeros(nb), a, 1000, 16, w.n_sink, w.window, w.maw_decay)
+        got = harness.maw_by_head(eng, 0, 0, w, 1000)[0]
+        assert np.all(np.abs(got - want) <= harness.MAW_ABS + harness.MAW_REL * np.abs(want))
     finally:
         eng.close()
 

@@ -197,3 +197,121 @@ def test_loop32_full_size_sampled():
                 assert len(st["units"]) == len(sample)
     finally:
         eng.close()
+
+
+def test_loop32_256_steps_flags_fire():
+    """The loop workload over its whole horizon on one layer at full per-layer
+    size (B=16, N=65536 -> 65791, MAW beta=1): 256 one-launch steps with their
+    appends, four sampled units in lockstep with the oracle at every step, MAW
+    tables included.  The MAW flag fires on its own: blocks that leave the
+    window with above-average mass keep a frozen MAW above beta*S/|D| and are
+    ranked into the selection first; the run must see such selections."""
+    w = _w(synth.loop32(), layers=1, steps=256)
+    log("case: loop32 one layer, 256 steps, sampled units")
+    seed = 7
+    N0 = w.N - 1
+    sample = {(0, 0), (5, 3), (9, 1), (15, 7)}
+    seqs = sorted({s for s, _ in sample})
+    eng = harness.make_engine(w, N0 + w.steps + 64)
+    try:
+        dirs = synth.directions(w, seed, 0, 1, device="cuda")
+        K, V, _ = synth.prefill_with_directions(w, seed, 0, N0, dirs, device="cuda")
+        harness.prefill(eng, 0, K, V)
+        n_max = N0 + w.steps
+        K_bits, V_bits = {}, {}
+        for s in seqs:
+            K_bits[s] = np.zeros((n_max, w.Hkv, w.d), np.uint16)
+            V_bits[s] = np.zeros((n_max, w.Hkv, w.d), np.uint16)
+            K_bits[s][:N0] = synth.bits(K[s])
+            V_bits[s][:N0] = synth.bits(V[s])
+        del K, V
+        torch.cuda.empty_cache()
+        maw_state = {}
+        flagged = ties = 0
+        max_dmaw = 0.0
+        bufs = eng.alloc_step(w.B)
+        N = N0
+        for step in range(w.steps):
+            kn, vn = synth.step_kv(w, seed, 0, step, device="cuda")
+            q = synth.loop_query(w, seed, 0, step, dirs, device="cuda")
+            eng.decode_step(0, list(range(w.B)), q, bufs["blk_idx"], bufs["blk_cnt"],
+                            bufs["o_part"], bufs["lse_part"], bufs["o"], bufs["lse"],
+                            k_new=kn.view(w.B, w.Hkv, w.d).contiguous(),
+                            v_new=vn.view(w.B, w.Hkv, w.d).contiguous())
+            eng.sync()
+            gpu = {k: v.cpu().numpy() for k, v in bufs.items()}
+            knb, vnb = synth.bits(kn), synth.bits(vn)
+            for s in seqs:
+                K_bits[s][N] = knb[s, 0]
+                V_bits[s][N] = vnb[s, 0]
+            N += 1
+            st = harness.check_units(w, eng, 0, list(range(w.B)), synth.bits(q), K_bits,
+                                     V_bits, {s: N for s in range(w.B)}, gpu,
+                                     maw_state=maw_state, units=sample,
+                                     check_summ=(step % 64 == 0), workers=4)
+            harness.assert_parity(st)
+            flagged += st["flagged"]
+            ties += st["ties"]
+            max_dmaw = max(max_dmaw, st["max_dmaw"])
+            if step % 32 == 0 or step == w.steps - 1:
+                log("  step %d N=%d flagged selections so far %d ties %d max|dMAW| %.2e "
+                    "max|dO| %.2e" % (step, N, flagged, ties, max_dmaw, st["max_abs"]))
+        assert flagged > 0, "no selection was decided by a MAW flag"
+    finally:
+        eng.close()
+
+
+def test_loop32_all_layers_short_horizon():
+    """All 32 layers of the loop workload at full per-layer size (B=16,
+    N=65536: about 138 GB of KV resident), four decode steps through every
+    layer with the one-launch step; one sampled unit per layer in lockstep
+    with the oracle, MAW included."""
+    w = _w(synth.loop32(), steps=4)
+    log("case: loop32 all %d layers, %d steps" % (w.layers, w.steps))
+    seed = 11
+    N0 = w.N - 1
+    eng = harness.make_engine(w, N0 + w.steps + 64, layers=w.layers)
+    try:
+        sample, K_bits, V_bits, dirs_l, maw_state = {}, {}, {}, {}, {}
+        n_max = N0 + w.steps
+        for layer in range(w.layers):
+            dirs = synth.directions(w, seed, layer, 1, device="cuda")
+            K, V, _ = synth.prefill_with_directions(w, seed, layer, N0, dirs, device="cuda")
+            harness.prefill(eng, layer, K, V)
+            s, g = (3 * layer + 1) % w.B, layer % w.Hkv
+            sample[layer] = {(s, g)}
+            kb = np.zeros((n_max, w.Hkv, w.d), np.uint16)
+            vb = np.zeros((n_max, w.Hkv, w.d), np.uint16)
+            kb[:N0] = synth.bits(K[s])
+            vb[:N0] = synth.bits(V[s])
+            K_bits[layer], V_bits[layer] = {s: kb}, {s: vb}
+            dirs_l[layer] = dirs
+            maw_state[layer] = {}
+            del K, V
+            torch.cuda.empty_cache()
+        log("  prefilled %d layers" % w.layers)
+        bufs = eng.alloc_step(w.B)
+        N = N0
+        for step in range(w.steps):
+            for layer in range(w.layers):
+                kn, vn = synth.step_kv(w, seed, layer, step, device="cuda")
+                q = synth.loop_query(w, seed, layer, step, dirs_l[layer], device="cuda")
+                eng.decode_step(layer, list(range(w.B)), q, bufs["blk_idx"], bufs["blk_cnt"],
+                                bufs["o_part"], bufs["lse_part"], bufs["o"], bufs["lse"],
+                                k_new=kn.view(w.B, w.Hkv, w.d).contiguous(),
+                                v_new=vn.view(w.B, w.Hkv, w.d).contiguous())
+                eng.sync()
+                gpu = {k: v.cpu().numpy() for k, v in bufs.items()}
+                (s, g), = sample[layer]
+                K_bits[layer][s][N] = synth.bits(kn)[s, 0]
+                V_bits[layer][s][N] = synth.bits(vn)[s, 0]
+                st = harness.check_units(w, eng, layer, list(range(w.B)), synth.bits(q),
+                                         K_bits[layer], V_bits[layer],
+                                         {x: N + 1 for x in range(w.B)}, gpu,
+                                         maw_state=maw_state[layer], units=sample[layer],
+                                         check_summ=(step == 0))
+                harness.assert_parity(st)
+            N += 1
+            log("  step %d done (N=%d)" % (step, N))
+    finally:
+        eng.close()
