@@ -23,7 +23,8 @@ SD_DEBUG_PAGE_TABLE, SD_DEBUG_SUMMARY, SD_DEBUG_MAW, SD_DEBUG_K, SD_DEBUG_V = ra
 EXPORTS = [
     "sd_validate_config", "sparse_decode_init", "sparse_decode_destroy",
     "sd_caps", "append_kv", "select_topk", "sparse_attend", "fuse_lse",
-    "sparse_decode_step", "sd_release_seq", "sd_seq_len", "sd_sync",
+    "sparse_decode_step", "sparse_decode_step_noalloc", "sd_release_seq", "sd_seq_len",
+    "sd_sync",
     "sd_last_error", "sd_debug_bytes", "sd_debug_copy", "sd_debug_set_maw",
     "sd_read_probe",
 ]
@@ -82,6 +83,7 @@ def load(path: str = LIB_PATH):
         "sparse_attend": (i32, [P, i32, i32, P, P, P, P, i32, P, P, i32]),
         "fuse_lse": (i32, [P, i32, i32, P, P, P, i32, P, P]),
         "sparse_decode_step": (i32, [P, i32, i32, P, P, P, P, P, P, i32, P, P, i32, P, P]),
+        "sparse_decode_step_noalloc": (i32, [P, i32, i32, P, P, P, P, P, P, i32, P, P, i32, P, P]),
         "sd_release_seq": (i32, [P, i32]),
         "sd_seq_len": (i32, [P, i32, i32, ctypes.POINTER(i32)]),
         "sd_sync": (i32, [P]),
@@ -235,6 +237,20 @@ class SparseDecode:
                                        _ptr(blk_idx), _ptr(blk_cnt), blk_idx.shape[-1],
                                        _ptr(o_part), _ptr(lse_part), lse_part.shape[-1],
                                        _ptr(o), _ptr(lse))
+        if check:
+            self._check(st)
+        return st
+
+    def decode_step_noalloc(self, layer, seq_ids, q, blk_idx, blk_cnt, o_part, lse_part, o,
+                            lse, k_new=None, v_new=None, check=True):
+        """sparse_decode_step_noalloc: the fused step with its scratch in the
+        library's static device array (allocates nothing)."""
+        s, sp = _i32arr(seq_ids)
+        st = self.L.sparse_decode_step_noalloc(self.ctx, layer, len(s), sp, _ptr(k_new),
+                                               _ptr(v_new), _ptr(q),
+                                               _ptr(blk_idx), _ptr(blk_cnt), blk_idx.shape[-1],
+                                               _ptr(o_part), _ptr(lse_part), lse_part.shape[-1],
+                                               _ptr(o), _ptr(lse))
         if check:
             self._check(st)
         return st

@@ -135,5 +135,6 @@ hipError_t launch_fuse(const Ctx &c, const SeqBatch &b, bool with_maw, int P,
                        float *o, float *lse, hipStream_t st);
 
 hipError_t launch_fill_f32(float *p, size_t n, float v, hipStream_t st);
+hipError_t launch_fill_u32(uint32_t *p, size_t n, uint32_t v, hipStream_t st);
 
 }  // namespace sd

@@ -2411,6 +2411,10 @@ __global__ void k_fill_f32(float *p, size_t n, float v) {
   size_t idx = (size_t)blockIdx.x * blockDim.x + threadIdx.x;
   for (; idx < n; idx += (size_t)gridDim.x * blockDim.x) p[idx] = v;
 }
+__global__ void k_fill_u32(uint32_t *p, size_t n, uint32_t v) {
+  size_t idx = (size_t)blockIdx.x * blockDim.x + threadIdx.x;
+  for (; idx < n; idx += (size_t)gridDim.x * blockDim.x) p[idx] = v;
+}
 
 }  // namespace
 
@@ -2539,6 +2543,14 @@ hipError_t launch_fuse(const Ctx &c, const SeqBatch &b, bool with_maw, int P,
   SD_DISPATCH_DG(c.dm.d, c.dm.G,
                  hipLaunchKernelGGL((k_fuse<D_, G_>), grid, dim3(256), 0, st, c, b,
                                     with_maw ? 1 : 0, P, o_part, lse_part, p_cap, o, lse));
+  return hipGetLastError();
+}
+
+hipError_t launch_fill_u32(uint32_t *p, size_t n, uint32_t v, hipStream_t st) {
+  if (n == 0) return hipSuccess;
+  size_t blocks = (n + 255) / 256;
+  if (blocks > 4096) blocks = 4096;
+  hipLaunchKernelGGL(k_fill_u32, dim3((unsigned)blocks), dim3(256), 0, st, p, n, v);
   return hipGetLastError();
 }
 

@@ -10,16 +10,38 @@
 #include <cstdint>
 #include <cstdio>
 #include <cstring>
-#include <map>
+#include <mutex>
 #include <new>
-#include <string>
 #include <vector>
 
 #include "sd_internal.h"
 
 using namespace sd;
 
+// Scratch of the allocation-free step (sparse_decode_step_noalloc): one
+// array per GPU, in the code object's device memory for as long as the
+// process runs.  Host code never passes `scratch` itself to a kernel (its
+// host-side name is a stand-in, not a device address): the device address is
+// resolved once per device with hipGetSymbolAddress at context set-up and
+// kept in g_scratch_dev.
+static __device__ __align__(256) unsigned char scratch[SD_STATIC_SCRATCH_BYTES];
+
 namespace {
+
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void *g_scratch_dev[kMaxDevices];    // device address of `scratch`, per device
+hipError_t g_scratch_err[kMaxDevices];  // result of resolving it (hipSuccess once done)
+bool g_scratch_tried[kMaxDevices];
+
+// Where the allocation-free step keeps each scratch array inside `scratch`
+// (byte offsets, 256-aligned).  The arrays that must start each call at zero
+// (arrival counters, score accumulators, selection hand-off tags) come first,
+// so one fill clears them.
+struct StaticLayout {
+  size_t arrive, unit_acc, rtag, seltag, clear_bytes;
+  size_t keyflag, cand, keys, ulist, ukeys, lm_pg, total;
+};
 
 struct Layer {
   LayerDev dev{};
@@ -48,8 +70,13 @@ struct sd_ctx {
   std::vector<int32_t> pend_seqs;
   int32_t pend_pcap = 0;
   std::vector<int> pend_parts;  // P of each launch of the attend call
-  std::map<int, int> capacity;  // resident step workgroups by max_blocks
-  std::string err;
+  // resident step workgroups by max_blocks (a fixed table: no allocation
+  // after init)
+  int cap_key[16] = {}, cap_val[16] = {}, n_cap = 0;
+  std::vector<uint8_t> seen;     // [max_seqs] duplicate-id check, all 0 between calls
+  void *static_scratch = nullptr;  // device address of `scratch` on this device
+  StaticLayout slayout{};
+  char err[512] = {};
   std::vector<void *> dev_allocs;
 };
 
@@ -61,7 +88,7 @@ sd_status fail(sd_ctx *c, sd_status st, const char *fmt, ...) {
   va_start(ap, fmt);
   vsnprintf(buf, sizeof buf, fmt, ap);
   va_end(ap);
-  if (c) c->err = buf;
+  if (c) snprintf(c->err, sizeof c->err, "%s", buf);
   return st;
 }
 
@@ -128,16 +155,23 @@ sd_status check_seqs(sd_ctx *c, int32_t layer, int32_t n_seqs,
                 c->cfg.num_layers);
   if (n_seqs < 0) return fail(c, SD_EINVAL, "n_seqs %d < 0", n_seqs);
   if (n_seqs > 0 && !seq_ids) return fail(c, SD_EINVAL, "seq_ids is NULL");
-  std::vector<char> seen(c->cfg.max_seqs, 0);
-  for (int i = 0; i < n_seqs; ++i) {
+  // c->seen is all zero between calls; the ids marked here are cleared again
+  sd_status st = SD_OK;
+  int i = 0;
+  for (; i < n_seqs; ++i) {
     int s = seq_ids[i];
-    if (s < 0 || s >= c->cfg.max_seqs)
-      return fail(c, SD_EINVAL, "seq_ids[%d]=%d out of range [0,%d)", i, s,
-                  c->cfg.max_seqs);
-    if (seen[s]) return fail(c, SD_EINVAL, "seq id %d repeated in one call", s);
-    seen[s] = 1;
+    if (s < 0 || s >= c->cfg.max_seqs) {
+      st = fail(c, SD_EINVAL, "seq_ids[%d]=%d out of range [0,%d)", i, s, c->cfg.max_seqs);
+      break;
+    }
+    if (c->seen[s]) {
+      st = fail(c, SD_EINVAL, "seq id %d repeated in one call", s);
+      break;
+    }
+    c->seen[s] = 1;
   }
-  return SD_OK;
+  for (int j = 0; j < i; ++j) c->seen[seq_ids[j]] = 0;
+  return st;
 }
 
 void fill_batch(const sd_ctx *c, int layer, const int32_t *seq_ids, int base,
@@ -217,7 +251,7 @@ sd_status sparse_decode_init(const sd_config *cfg, sd_ctx **out) {
   sd_ctx *c = new (std::nothrow) sd_ctx();
   if (!c) return SD_ENOMEM;
   if (st != SD_OK) {
-    c->err = msg;
+    snprintf(c->err, sizeof c->err, "%s", msg);
     *out = c;  // caller can read the message, then destroy
     return st;
   }
@@ -316,6 +350,44 @@ sd_status sparse_decode_init(const sd_config *cfg, sd_ctx **out) {
   SD_HIP(c, hipMemset(c->sc.seltag, 0, sizeof(unsigned long long) * max_seqs * c->Hkv * c->k_cap));
   SD_HIP(c, hipMemset(c->sc.err, 0, sizeof(uint32_t)));
 
+  c->seen.assign(max_seqs, 0);
+
+  // layout of the allocation-free step's scratch inside `scratch`, and the
+  // array's device address on this device (resolved once per device)
+  {
+    const size_t units = (size_t)max_seqs * c->Hkv;
+    size_t off = 0;
+    auto take = [&off](size_t bytes) {
+      const size_t at = off;
+      off = (off + bytes + 255) & ~size_t(255);
+      return at;
+    };
+    StaticLayout &sl = c->slayout;
+    sl.arrive = take(sizeof(uint32_t) * units * 2);
+    sl.unit_acc = take(sizeof(uint32_t) * units * 2);
+    sl.rtag = take(sizeof(unsigned long long) * units);
+    sl.seltag = take(sizeof(unsigned long long) * units * c->k_cap);
+    sl.clear_bytes = off;
+    sl.keyflag = take(sizeof(unsigned long long) * per_unit);
+    sl.cand = take(sizeof(unsigned long long) * per_unit);
+    sl.keys = take(sizeof(uint32_t) * per_unit);
+    sl.ulist = take(sizeof(int32_t) * per_unit);
+    sl.ukeys = take(sizeof(uint32_t) * per_unit);
+    sl.lm_pg = take(sizeof(float) * (size_t)max_seqs * c->Hq * c->dims.lm_cap);
+    sl.total = off;
+    if (c->device >= 0 && c->device < kMaxDevices) {
+      std::lock_guard<std::mutex> lock(g_scratch_mu);
+      if (!g_scratch_tried[c->device]) {
+        void *ptr = nullptr;
+        g_scratch_err[c->device] = hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch));
+        if (g_scratch_err[c->device] != hipSuccess) (void)hipGetLastError();
+        g_scratch_dev[c->device] = g_scratch_err[c->device] == hipSuccess ? ptr : nullptr;
+        g_scratch_tried[c->device] = true;
+      }
+      c->static_scratch = g_scratch_dev[c->device];
+    }
+  }
+
   // layers
   c->layers.resize(cfg->num_layers);
   const size_t pool = (size_t)cfg->num_pages * c->Hkv * kPage * c->D;
@@ -368,7 +440,7 @@ sd_status sd_caps(const sd_ctx *c, int32_t *k_cap, int32_t *p_cap) {
 
 const char *sd_last_error(const sd_ctx *c) {
   if (!c) return "null context";
-  return c->err.c_str();
+  return c->err;
 }
 
 sd_status sd_sync(sd_ctx *c) {
@@ -404,18 +476,19 @@ Ctx kctx(const sd_ctx *c, int layer) {
 }
 
 // Host-side append: validate, take pages, push the touched page-table span,
-// launch the append kernel (optionally carrying the q split for the step).
+// launch the append kernel.  n_new == NULL: one token per sequence.
 sd_status do_append(sd_ctx *c, int32_t layer, int32_t n_seqs, const int32_t *seq_ids,
-                    const int32_t *n_new, const void *k_bf16, const void *v_bf16) {
+                    const int32_t *n_new_arr, const void *k_bf16, const void *v_bf16) {
   Layer &L = c->layers[layer];
+  auto n_new = [n_new_arr](int i) { return n_new_arr ? n_new_arr[i] : 1; };
   int64_t total = 0, pages_needed = 0;
   for (int i = 0; i < n_seqs; ++i) {
-    if (n_new[i] < 0) return fail(c, SD_EINVAL, "n_new[%d]=%d < 0", i, n_new[i]);
-    int64_t nl = (int64_t)L.len[seq_ids[i]] + n_new[i];
+    if (n_new(i) < 0) return fail(c, SD_EINVAL, "n_new[%d]=%d < 0", i, n_new(i));
+    int64_t nl = (int64_t)L.len[seq_ids[i]] + n_new(i);
     if (nl > c->cfg.max_seq_len)
       return fail(c, SD_EINVAL, "sequence %d would hold %lld tokens > max_seq_len %d",
                   seq_ids[i], (long long)nl, c->cfg.max_seq_len);
-    total += n_new[i];
+    total += n_new(i);
     pages_needed += cdiv(nl, kPage) - cdiv(L.len[seq_ids[i]], kPage);
   }
   if (total > 0 && (!k_bf16 || !v_bf16)) return fail(c, SD_EINVAL, "k/v pointers are NULL");
@@ -425,7 +498,7 @@ sd_status do_append(sd_ctx *c, int32_t layer, int32_t n_seqs, const int32_t *seq
   int64_t lo = INT64_MAX, hi = -1;
   for (int i = 0; i < n_seqs; ++i) {
     int seq = seq_ids[i];
-    int64_t p0 = cdiv(L.len[seq], kPage), p1 = cdiv((int64_t)L.len[seq] + n_new[i], kPage);
+    int64_t p0 = cdiv(L.len[seq], kPage), p1 = cdiv((int64_t)L.len[seq] + n_new(i), kPage);
     for (int64_t p = p0; p < p1; ++p) {
       L.h_pt[(size_t)seq * c->pps + p] = L.free_pages.back();
       L.free_pages.pop_back();
@@ -446,9 +519,9 @@ sd_status do_append(sd_ctx *c, int32_t layer, int32_t n_seqs, const int32_t *seq
       int seq = seq_ids[base + i];
       b.seq[i] = seq;
       b.old_len[i] = L.len[seq];
-      b.n_new[i] = n_new[base + i];
+      b.n_new[i] = n_new(base + i);
       b.src_row[i] = row;
-      row += n_new[base + i];
+      row += n_new(base + i);
       max_new = std::max(max_new, b.n_new[i]);
       if (b.n_new[i] > 0)
         for (int h = 0; h < c->Hkv; ++h) {
@@ -460,7 +533,7 @@ sd_status do_append(sd_ctx *c, int32_t layer, int32_t n_seqs, const int32_t *seq
     SD_HIP(c, launch_append(kc, b, max_new, max_touch, static_cast<const uint16_t *>(k_bf16),
                             static_cast<const uint16_t *>(v_bf16), c->stream));
   }
-  for (int i = 0; i < n_seqs; ++i) L.len[seq_ids[i]] += n_new[i];
+  for (int i = 0; i < n_seqs; ++i) L.len[seq_ids[i]] += n_new(i);
   return SD_OK;
 }
 
@@ -488,16 +561,22 @@ int parts_of(sd_ctx *c, int layer, const SeqBatch &b, int max_blocks) {
       const int64_t pages = dense_pages(c, b.len[i]) + k_of_seq(c, b.len[i], h) * (c->S[h] / kPage);
       P = std::max<int64_t>(P, cdiv(pages, kPartPages));
     }
-  auto it = c->capacity.find(max_blocks);
-  if (it == c->capacity.end())
-    it = c->capacity.emplace(max_blocks, step_capacity(kctx(c, layer), max_blocks,
-                                                       c->pps <= kPtLds ? c->pps : 0)).first;
+  int cap = -1;
+  for (int t = 0; t < c->n_cap; ++t)
+    if (c->cap_key[t] == max_blocks) cap = c->cap_val[t];
+  if (cap < 0) {
+    cap = step_capacity(kctx(c, layer), max_blocks, c->pps <= kPtLds ? c->pps : 0);
+    if (c->n_cap < 16) {
+      c->cap_key[c->n_cap] = max_blocks;
+      c->cap_val[c->n_cap++] = cap;
+    }
+  }
   const int units = c->Hkv * b.n;
   const int tiles = std::max(1, (max_blocks + kScoreTile - 1) / kScoreTile);
   // fewer parts, so that the whole step stays resident, pays when it costs
   // at most half of them; otherwise (long units, many tiles) the parts that do
   // not fit start as score tiles finish
-  const int64_t resident = it->second > 0 ? it->second / units - tiles : P;
+  const int64_t resident = cap > 0 ? cap / units - tiles : P;
   if (2 * resident >= P) P = std::min<int64_t>(P, std::max<int64_t>(1, resident));
   return (int)std::min<int64_t>(P, c->p_cap);
 }
@@ -629,12 +708,19 @@ sd_status fuse_lse(sd_ctx *c, int32_t layer, int32_t n_seqs,
   return SD_OK;
 }
 
-sd_status sparse_decode_step(sd_ctx *c, int32_t layer, int32_t n_seqs,
-                             const int32_t *seq_ids, const void *k_new,
-                             const void *v_new, const void *q_bf16, int32_t *blk_idx,
-                             int32_t *blk_cnt, int32_t k_cap, float *o_part,
-                             float *lse_part, int32_t p_cap, float *o, float *lse) {
-  if (!c) return SD_EINVAL;
+}  // extern "C"
+
+namespace {
+
+// The one-launch step of both entry points: sc is the scratch its kernels
+// use (the context's own, or the static array's); clear_first zeroes the
+// arrays that must start at zero (the static array keeps whatever the last
+// call on the GPU left in it).
+sd_status decode_step_impl(sd_ctx *c, int32_t layer, int32_t n_seqs, const int32_t *seq_ids,
+                           const void *k_new, const void *v_new, const void *q_bf16,
+                           int32_t *blk_idx, int32_t *blk_cnt, int32_t k_cap, float *o_part,
+                           float *lse_part, int32_t p_cap, float *o, float *lse,
+                           const Scratch &sc, uint32_t *clear, size_t clear_words) {
   sd_status s = check_seqs(c, layer, n_seqs, seq_ids);
   if (s != SD_OK) return s;
   if (n_seqs == 0) return SD_OK;
@@ -662,12 +748,11 @@ sd_status sparse_decode_step(sd_ctx *c, int32_t layer, int32_t n_seqs,
     }
   }
   const uint16_t *q = static_cast<const uint16_t *>(q_bf16);
-  if (k_new) {
-    std::vector<int32_t> ones(n_seqs, 1);
-    if ((s = do_append(c, layer, n_seqs, seq_ids, ones.data(), k_new, v_new)) != SD_OK)
-      return s;
-  }
-  const Ctx kc = kctx(c, layer);
+  if (clear) SD_HIP(c, launch_fill_u32(clear, clear_words, 0u, c->stream));
+  if (k_new && (s = do_append(c, layer, n_seqs, seq_ids, nullptr, k_new, v_new)) != SD_OK)
+    return s;
+  Ctx kc = kctx(c, layer);
+  kc.sc = sc;
   for (int base = 0; base < n_seqs; base += kLaunchSeqs) {
     SeqBatch b;
     int mb = 0;
@@ -686,6 +771,55 @@ sd_status sparse_decode_step(sd_ctx *c, int32_t layer, int32_t n_seqs,
   }
   c->pend_layer = -2;
   return SD_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+sd_status sparse_decode_step(sd_ctx *c, int32_t layer, int32_t n_seqs,
+                             const int32_t *seq_ids, const void *k_new,
+                             const void *v_new, const void *q_bf16, int32_t *blk_idx,
+                             int32_t *blk_cnt, int32_t k_cap, float *o_part,
+                             float *lse_part, int32_t p_cap, float *o, float *lse) {
+  if (!c) return SD_EINVAL;
+  return decode_step_impl(c, layer, n_seqs, seq_ids, k_new, v_new, q_bf16, blk_idx, blk_cnt,
+                          k_cap, o_part, lse_part, p_cap, o, lse, c->sc, nullptr, 0);
+}
+
+sd_status sparse_decode_step_noalloc(sd_ctx *c, int32_t layer, int32_t n_seqs,
+                                     const int32_t *seq_ids, const void *k_new,
+                                     const void *v_new, const void *q_bf16, int32_t *blk_idx,
+                                     int32_t *blk_cnt, int32_t k_cap, float *o_part,
+                                     float *lse_part, int32_t p_cap, float *o, float *lse) {
+  if (!c) return SD_EINVAL;
+  if (!c->static_scratch) {
+    const hipError_t e = (c->device >= 0 && c->device < kMaxDevices) ? g_scratch_err[c->device]
+                                                                      : hipErrorInvalidDevice;
+    return fail(c, SD_EHIP, "the static scratch array has no device address on device %d (%s)",
+                c->device, hipGetErrorString(e));
+  }
+  const StaticLayout &sl = c->slayout;
+  if (sl.total > (size_t)SD_STATIC_SCRATCH_BYTES)
+    return fail(c, SD_EUNSUPPORTED,
+                "this context's step needs %zu bytes of scratch, more than the %zu of the "
+                "static array (fewer max_seqs or a shorter max_seq_len)",
+                sl.total, (size_t)SD_STATIC_SCRATCH_BYTES);
+  unsigned char *base = static_cast<unsigned char *>(c->static_scratch);
+  Scratch sc = c->sc;  // err stays the context's own
+  sc.arrive = reinterpret_cast<uint32_t *>(base + sl.arrive);
+  sc.unit_acc = reinterpret_cast<uint32_t *>(base + sl.unit_acc);
+  sc.rtag = reinterpret_cast<unsigned long long *>(base + sl.rtag);
+  sc.seltag = reinterpret_cast<unsigned long long *>(base + sl.seltag);
+  sc.keyflag = reinterpret_cast<unsigned long long *>(base + sl.keyflag);
+  sc.cand = reinterpret_cast<unsigned long long *>(base + sl.cand);
+  sc.keys = reinterpret_cast<uint32_t *>(base + sl.keys);
+  sc.ulist = reinterpret_cast<int32_t *>(base + sl.ulist);
+  sc.ukeys = reinterpret_cast<uint32_t *>(base + sl.ukeys);
+  sc.lm_pg = reinterpret_cast<float *>(base + sl.lm_pg);
+  return decode_step_impl(c, layer, n_seqs, seq_ids, k_new, v_new, q_bf16, blk_idx, blk_cnt,
+                          k_cap, o_part, lse_part, p_cap, o, lse, sc,
+                          reinterpret_cast<uint32_t *>(base), sl.clear_bytes / 4);
 }
 
 sd_status sd_release_seq(sd_ctx *c, int32_t seq) {

@@ -201,6 +201,30 @@ sd_status sparse_decode_step(sd_ctx *ctx, int32_t layer, int32_t n_seqs,
                              float *o_part, float *lse_part, int32_t p_cap,
                              float *o, float *lse);
 
+/* sparse_decode_step for callers that cannot allocate: code under HIP graph
+ * capture, tight serving loops, harnesses that forbid allocation.  Same
+ * arguments, results and errors as sparse_decode_step, but the step's
+ * scratch (per-block keys, score-tile candidate lists, top-k spill arrays,
+ * selection hand-off tags, arrival counters, page log-masses) lives in one
+ * library-wide static device array of SD_STATIC_SCRATCH_BYTES per GPU (held
+ * from the library's first context on that GPU until the process ends)
+ * instead of the context's own buffers.  The call allocates nothing: no
+ * hipMalloc/hipFree and no host allocation.  It first clears, with a fill
+ * kernel on the context's stream, the part of the array that must start at
+ * zero.  SD_EUNSUPPORTED if the context's scratch (about max_seqs * Hkv *
+ * (28 * ceil(max_seq_len / (256 * min block size)) * 256 + 16 + 8 * k_cap)
+ * bytes, plus the page log-masses) exceeds the array; SD_EHIP if the array's
+ * device address could not be resolved.  Every call on one GPU, from any
+ * context or stream, shares the array: calls that overlap in time race and
+ * give wrong results, so callers must order them (one stream, or events). */
+#define SD_STATIC_SCRATCH_BYTES (32u << 20)
+sd_status sparse_decode_step_noalloc(sd_ctx *ctx, int32_t layer, int32_t n_seqs,
+                                     const int32_t *seq_ids, const void *k_new,
+                                     const void *v_new, const void *q_bf16,
+                                     int32_t *blk_idx, int32_t *blk_cnt, int32_t k_cap,
+                                     float *o_part, float *lse_part, int32_t p_cap,
+                                     float *o, float *lse);
+
 /* Return a sequence slot to empty in every layer: its pages go back to the
  * free lists, its length becomes 0 and its MAW table is cleared.  Waits for
  * the stream first. */
