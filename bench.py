@@ -17,9 +17,13 @@ step launches without append (k_step alone, same workload, rotating over the
 layer instances); `traffic` is the HBM traffic per
 launch from the committed FETCH_SIZE/WRITE_SIZE counter summary, null once the
 kernel sources differ from those it was taken on.  `cpu_baseline` times the
-CPU oracle on a bounded sample of the same workload.  `read_ceiling` is a
-plain streaming read of the same byte count on the same GPU, for context.  --fused 0 runs the four separate ABI calls instead (same
-results, for comparison).
+CPU oracle (select + attend on precomputed summaries) on the last timed step's
+inputs, on all host threads and on one; `parity` compares that step's GPU
+outputs with those oracle results (every unit), and a failure exits non-zero.
+`read_ceiling` is a plain streaming read of the same byte count on the same
+GPU, for context.  --fused 0 runs the four separate ABI calls instead (same
+selection and MAW, O and lse to fp32 rounding, for comparison).  Each timed
+step draws a fresh query; a selection wait that runs out of time fails the run.
 """
 from __future__ import annotations
 
@@ -64,7 +68,9 @@ def parse():
     ap.add_argument("--fused", type=int, default=1, help="use sparse_decode_step")
     ap.add_argument("--cpu-baseline", type=int, default=1)
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
-    ap.add_argument("--trials", type=int, default=3)
+    ap.add_argument("--trials", type=int, default=5)
+    ap.add_argument("--parity", type=int, default=1,
+                    help="check the last timed step against the CPU oracle (every unit)")
     ap.add_argument("--workload", choices=["llama32k", "qwen128k", "loop32", "sweep"],
                     default="llama32k",
                     help="llama32k: the headline step; qwen128k (per-head budgets and block "
@@ -148,23 +154,27 @@ def measured_traffic():
 
 def algorithmic_bytes(w, N, blk_cnt, blk_idx, with_maw=True):
     """Per-step algorithmic HBM bytes (each term counted once):
-    summaries n_blk*2*d*2 per (seq, kv head); K+V of the distinct attended
-    tokens |T|*2*d*2; MAW read+write n_blk*4*2; q 2d, O 4d, lse 4 per query
-    head.  Scratch and page tables are excluded."""
+    summaries n_blk*2*d*2 per (seq, kv head) that selects; K+V of the distinct
+    attended tokens |T|*2*d*2; MAW: the flag's read of every block, n_blk*4,
+    when the flag is on (with_maw), plus the update of the blocks wholly inside
+    the dense set, 4*2 each; q 2d, O 4d, lse 4 per query head.  Scratch and
+    page tables are excluded."""
     summ = attend = maw = 0
     for b in range(w.B):
         for g in range(w.Hkv):
             S = w.block_size[g]
             nb = (N + S - 1) // S
             sel = blk_idx[b, g, :blk_cnt[b, g]]
-            inT = np.zeros(N, bool)
-            inT[:min(w.n_sink, N)] = True
-            inT[max(0, N - w.window):] = True
+            inD = np.zeros(N, bool)
+            inD[:min(w.n_sink, N)] = True
+            inD[max(0, N - w.window):] = True
+            inT = inD.copy()
             for i in sel:
                 inT[i * S:min(N, (i + 1) * S)] = True
             summ += nb * 2 * w.d * 2 if w.budget_ppm[g] > 0 else 0  # streaming heads score nothing
             attend += int(inT.sum()) * 2 * w.d * 2
-            maw += nb * 4 * 2 if with_maw else 0
+            inside = sum(1 for i in range(nb) if inD[i * S:min(N, (i + 1) * S)].all())
+            maw += (nb * 4 if with_maw and w.budget_ppm[g] > 0 else 0) + inside * 4 * 2
     qol = w.B * w.Hq * (2 * w.d + 4 * w.d + 4)
     return dict(summaries=summ, attend=attend, maw=maw, q_o_lse=qol,
                 total=summ + attend + maw + qol)
@@ -206,41 +216,53 @@ def main():
                        maw_decay=0.95, maw_beta=maw_beta,
                        page_shuffle_seed=12345, stream=stream)
     seqs = list(range(w.B))
-    qs = []
+    dirs_l = {}
     t0 = time.time()
-    for layer in range(L):
+
+    def layer_inputs(layer):
+        """The prefill K, V [B, w.N, Hkv, d] of a layer instance, from its seed
+        (the same call again gives the same bits)."""
         if args.workload == "loop32":  # a planted direction per (layer, seq, KV head)
             dirs = synth.directions(w, args.seed, layer, 1, device=dev)
-            Kf, Vf, _ = synth.prefill_with_directions(w, args.seed, layer, w.N, dirs, device=dev)
-            x = {"K": Kf, "V": Vf, "q": synth.loop_query(w, args.seed, layer, 0, dirs, device=dev)}
-        else:
-            x = synth.single_step(w, args.seed * 100 + layer, device=dev, N=w.N)
-        K, V = x["K"][:, :N0].contiguous(), x["V"][:, :N0].contiguous()
+            dirs_l[layer] = dirs
+            K, V, _ = synth.prefill_with_directions(w, args.seed, layer, w.N, dirs, device=dev)
+            return K, V
+        x = synth.single_step(w, args.seed * 100 + layer, device=dev, N=w.N)
+        return x["K"], x["V"]
+
+    for layer in range(L):
+        K, V = layer_inputs(layer)
+        K, V = K[:, :N0].contiguous(), V[:, :N0].contiguous()
         eng.append_kv(layer, seqs, [N0] * w.B, K.view(-1, w.Hkv, w.d), V.view(-1, w.Hkv, w.d))
-        qs.append(x["q"].contiguous())
-        if layer == 0:
-            K0 = x["K"]
-            V0 = x["V"]
-        del x, K, V
+        del K, V
         torch.cuda.empty_cache()
     torch.cuda.synchronize()
     setup_s = time.time() - t0
     g = torch.Generator(device=dev).manual_seed(args.seed)
     k_new = torch.randn(64, w.B, w.Hkv, w.d, generator=g, device=dev).to(torch.bfloat16)
     v_new = torch.randn(64, w.B, w.Hkv, w.d, generator=g, device=dev).to(torch.bfloat16)
+    # a fresh query every step, drawn before timing from the workload's query
+    # distribution (loop32: N(0,1) + 3u of the layer's directions; else N(0,1))
+    n_total = args.warmup + args.trials * args.steps
+    if args.workload == "loop32":
+        q_pool = torch.stack([synth.loop_query(w, args.seed, s_ % L, s_, dirs_l[s_ % L], device=dev)
+                              for s_ in range(n_total)])
+    else:
+        q_pool = torch.randn(n_total, w.B, w.Hq, w.d, generator=g, device=dev).to(torch.bfloat16)
     bufs = eng.alloc_step(w.B, device=dev)
 
     def step(s):
         layer = s % L
         kn, vn = k_new[s % 64], v_new[s % 64]
+        q = q_pool[s]
         if args.fused:
-            eng.decode_step(layer, seqs, qs[layer], bufs["blk_idx"], bufs["blk_cnt"],
+            eng.decode_step(layer, seqs, q, bufs["blk_idx"], bufs["blk_cnt"],
                             bufs["o_part"], bufs["lse_part"], bufs["o"], bufs["lse"],
                             k_new=kn, v_new=vn)
             return
         eng.append_kv(layer, seqs, [1] * w.B, kn, vn)
-        eng.select_topk(layer, seqs, qs[layer], bufs["blk_idx"], bufs["blk_cnt"])
-        eng.sparse_attend(layer, seqs, qs[layer], bufs["blk_idx"], bufs["blk_cnt"],
+        eng.select_topk(layer, seqs, q, bufs["blk_idx"], bufs["blk_cnt"])
+        eng.sparse_attend(layer, seqs, q, bufs["blk_idx"], bufs["blk_cnt"],
                           bufs["o_part"], bufs["lse_part"])
         eng.fuse_lse(layer, seqs, bufs["o_part"], bufs["lse_part"], bufs["o"], bufs["lse"])
 
@@ -248,7 +270,7 @@ def main():
     for _ in range(args.warmup):
         step(s_global)
         s_global += 1
-    torch.cuda.synchronize()
+    eng.sync()
 
     # timed trials: exactly --steps steps each, median reported
     trial_ms = []
@@ -263,7 +285,17 @@ def main():
         e1.record(stream)
         torch.cuda.synchronize()
         trial_ms.append(e0.elapsed_time(e1) / args.steps)
+    eng.sync()  # a selection wait that ran out of time fails the run here
     ms = float(np.median(trial_ms))
+
+    # outputs of the last timed step, and what it ran on (rebuilt from the
+    # seeds: the layer's prefill, then the token appended at each of its
+    # visits), for the parity check of the CPU-baseline leg
+    s_last = s_global - 1
+    l_last = s_last % L
+    last = {k: v.cpu().numpy() for k, v in bufs.items() if k in ("blk_idx", "blk_cnt", "o", "lse")}
+    N_now = eng.seq_len(l_last, 0)
+    cnt, idx = last["blk_cnt"], last["blk_idx"]
 
     # k_step timed alone: n_inst back-to-back steps without append (so k_step
     # is the only kernel) between two HIP events on the library's stream
@@ -274,16 +306,14 @@ def main():
     ea.record(stream)
     for i in range(n_inst):
         layer = i % L  # rotate layers: the working set stays out of the LLC
-        eng.decode_step(layer, seqs, qs[layer], bufs["blk_idx"], bufs["blk_cnt"],
+        eng.decode_step(layer, seqs, q_pool[i], bufs["blk_idx"], bufs["blk_cnt"],
                         bufs["o_part"], bufs["lse_part"], bufs["o"], bufs["lse"])
     eb.record(stream)
     torch.cuda.synchronize()
+    eng.sync()
     t_step = ea.elapsed_time(eb) / n_inst
 
-    cnt = bufs["blk_cnt"].cpu().numpy()
-    idx = bufs["blk_idx"].cpu().numpy()
-    N_now = eng.seq_len((s_global - 1) % L, 0)
-    ab = algorithmic_bytes(w, N_now, cnt, idx)
+    ab = algorithmic_bytes(w, N_now, cnt, idx, with_maw=maw_beta > 0)
     qheads = w.B * w.Hq
     value = qheads / (ms * 1e-3)
     step_gbs = ab["total"] / (ms * 1e-3) / 1e9
@@ -326,10 +356,27 @@ def main():
     }
 
     out["read_ceiling"] = read_ceiling(kstep_bytes, kstep_gbs)
+    parity_ok = True
     if args.cpu_baseline:
-        out["cpu_baseline"] = cpu_baseline(w, K0, V0, qs[0], args.cpu_seconds)
+        K, V = layer_inputs(l_last)
+        visits = [s_ for s_ in range(s_global) if s_ % L == l_last]
+        assert N_now == N0 + len(visits)
+        Kb = np.concatenate([synth.bits(K[:, :N0])] +
+                            [synth.bits(k_new[s_ % 64])[:, None] for s_ in visits], 1)
+        Vb = np.concatenate([synth.bits(V[:, :N0])] +
+                            [synth.bits(v_new[s_ % 64])[:, None] for s_ in visits], 1)
+        del K, V
+        torch.cuda.empty_cache()
+        out["cpu_baseline"], out["parity"] = cpu_baseline_and_parity(
+            w, Kb, Vb, synth.bits(q_pool[s_last]), N_now, last, args.cpu_seconds,
+            check=bool(args.parity) and maw_beta <= 0.0, step_index=s_last)
+        parity_ok = out["parity"].get("pass", True)
     print(json.dumps(out), flush=True)
     eng.close()
+    if not parity_ok:
+        print("parity of the last timed step FAILED: %s" % json.dumps(out["parity"]),
+              file=sys.stderr)
+        sys.exit(1)
 
 
 def read_ceiling(nbytes, kstep_gbs, n_buf=8, reps=64, wgs=8192):
@@ -370,40 +417,107 @@ def read_ceiling(nbytes, kstep_gbs, n_buf=8, reps=64, wgs=8192):
             "k_step_frac": kstep_gbs / gbs}
 
 
-def cpu_baseline(w, K, V, q, budget_s):
-    """The CPU oracle (unchanged) on a bounded sample of the same workload:
-    whole (sequence, KV head) units of one decode step at N - 1 tokens, run
-    one per thread until about budget_s seconds have passed."""
+def cpu_model():
+    try:
+        with open("/proc/cpuinfo") as fh:
+            for line in fh:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
+
+
+def cpu_baseline_and_parity(w, Kb, Vb, qb, N, gpu, budget_s, check=True, step_index=-1):
+    """The CPU-baseline leg: the CPU oracle (unchanged) on the inputs of the
+    last timed step (every (sequence, KV head) unit; bf16 bits rebuilt from the
+    seeds, none read back from the GPU).  Summaries are computed first, outside
+    the timing, as the GPU path keeps them incrementally; oracle select +
+    attend are then timed per unit, one unit per task, on all the host threads
+    the box gives one GPU (16) and on one thread, each for about budget_s / 2
+    seconds.  The oracle's results of the first pass over the units also serve
+    the parity check of the GPU's outputs of that step (check=True): selection
+    bit-exact except ties inside the 1e-6 relative score band, max |dO| <=
+    2e-3, max relative dO <= 1e-2 where |O| >= 0.1, |dlse| <= 1e-4."""
     import concurrent.futures as cf
-    import synth
     import oracle
-    Kb, Vb, qb = synth.bits(K[:, :w.N - 1]), synth.bits(V[:, :w.N - 1]), synth.bits(q)
-    N = w.N - 1
-    units = [(b, g) for b in range(w.B) for g in range(w.Hkv)]
-    threads = max(1, min(16, os.cpu_count() or 1))
     G = w.G
+    units = [(b, g) for b in range(w.B) for g in range(w.Hkv)]
+    Kg = {u: np.ascontiguousarray(Kb[u[0], :N, u[1]]) for u in units}
+    Vg = {u: np.ascontiguousarray(Vb[u[0], :N, u[1]]) for u in units}
+    summ = {u: oracle.summaries(Kg[u], w.block_size[u[1]]) for u in units}
 
     def run(u):
         b, g = u
-        oracle.unit_step(qb[b, g * G:(g + 1) * G], np.ascontiguousarray(Kb[b, :, g]),
-                         np.ascontiguousarray(Vb[b, :, g]), N, w.block_size[g], w.n_sink,
-                         w.window, w.budget_ppm[g],
-                         maw=np.zeros((N + w.block_size[g] - 1) // w.block_size[g]) if w.maw_beta > 0 else None,
-                         beta=w.maw_beta)
-        return 1
+        S, qg = w.block_size[g], qb[b, g * G:(g + 1) * G]
+        r = oracle.select(qg, summ[u][0], summ[u][1], N, S, w.n_sink, w.window, w.budget_ppm[g])
+        a = oracle.attend(qg, Kg[u], Vg[u], N, S, w.n_sink, w.window, r["sel"])
+        return u, r, a
 
-    done = 0
-    t0 = time.time()
-    with cf.ThreadPoolExecutor(threads) as ex:
-        while time.time() - t0 < budget_s:
-            batch = units[:]
-            done += sum(ex.map(run, batch))
-    dt = time.time() - t0
-    qheads = done * G
-    return {"value": qheads / dt, "unit": "query-heads/s", "cores": threads,
-            "kind": "oracle",
-            "sample": "%d (sequence, KV head) units of the %s step (N=%d, G=%d), "
-                      "summaries+select+attend per unit, %.1f s" % (done, w.name, N, G, dt)}
+    def timed(threads):
+        done, t0, results = 0, time.time(), None
+        with cf.ThreadPoolExecutor(threads) as ex:
+            while True:
+                res = list(ex.map(run, units))
+                done += len(units)
+                results = results or res
+                if time.time() - t0 >= budget_s / 2:
+                    break
+        return done, time.time() - t0, results
+
+    threads = max(1, min(16, os.cpu_count() or 1))
+    done, dt, results = timed(threads)
+    done1, dt1, _ = timed(1)
+    base = {"value": done * G / dt, "unit": "query-heads/s", "cores": threads, "kind": "oracle",
+            "sample": "%d (sequence, KV head) units (%d full steps) of the %s step at N=%d, "
+                      "oracle select + attend on precomputed summaries, %d threads, %.1f s"
+                      % (done, done // len(units), w.name, N, threads, dt),
+            "ms_per_step": dt / (done / len(units)) * 1e3,
+            "t1": {"value": done1 * G / dt1, "cores": 1,
+                   "ms_per_step": dt1 / (done1 / len(units)) * 1e3,
+                   "sample": "%d units, one thread, %.1f s" % (done1, dt1)},
+            "cpu_model": cpu_model(), "os_cpu_count": os.cpu_count()}
+    if not check:
+        return base, {"checked": False,
+                      "reason": "MAW flags depend on the layer's whole history (the lockstep "
+                                "tests cover them)" if w.maw_beta > 0 else "disabled"}
+    ties = 0
+    ma = mr = ml = 0.0
+    fails = []
+    for (b, g), r, a in results:
+        cnt = int(gpu["blk_cnt"][b, g])
+        gsel = set(gpu["blk_idx"][b, g, :cnt].tolist())
+        osel = set(r["sel"].tolist())
+        if cnt != r["k"]:
+            fails.append("unit (%d,%d): k %d vs %d" % (b, g, cnt, r["k"]))
+            continue
+        if gsel != osel:
+            kth = min(r["U"][i] for i in osel)
+            band = all(abs(r["U"][i] - kth) <= 1e-6 * max(abs(r["U"][i]), abs(kth), 1e-30)
+                       for i in gsel ^ osel)
+            if not band:
+                fails.append("unit (%d,%d): selection differs outside the tie band" % (b, g))
+                continue
+            ties += len(gsel ^ osel) // 2
+            a = oracle.attend(qb[b, g * G:(g + 1) * G], Kg[(b, g)], Vg[(b, g)], N,
+                              w.block_size[g], w.n_sink, w.window,
+                              np.array(sorted(gsel), np.int32))
+        Og = gpu["o"][b, g * G:(g + 1) * G].astype(np.float64)
+        dO = np.abs(Og - a["O"])
+        ma = max(ma, float(dO.max()))
+        big = np.abs(a["O"]) >= 0.1
+        if big.any():
+            mr = max(mr, float((dO[big] / np.abs(a["O"][big])).max()))
+        ml = max(ml, float(np.abs(gpu["lse"][b, g * G:(g + 1) * G] - a["lse"]).max()))
+    ok = not fails and ma <= 2e-3 and mr <= 1e-2 and ml <= 1e-4
+    par = {"checked": True, "step": step_index, "units": len(results), "ties": ties,
+           "max_abs": ma, "max_rel": mr, "max_dlse": ml,
+           "gates": {"max_abs": 2e-3, "max_rel": 1e-2, "rel_floor": 0.1, "max_dlse": 1e-4,
+                     "tie_band": 1e-6},
+           "pass": ok}
+    if fails:
+        par["failures"] = fails[:8]
+    return base, par
 
 
 if __name__ == "__main__":

@@ -118,11 +118,16 @@ hipError_t launch_attend(const Ctx &c, const SeqBatch &b, int P, const uint16_t 
 
 // The whole step in one launch: scoring, top-k, P attention parts per unit,
 // fusion and MAW (epoch: a nonzero number that differs between launches;
-// ptl_cap: page-table entries a part may copy to LDS, 0 for none).
+// ptl_cap: page-table entries a part may copy to LDS, 0 for none).  k_new,
+// v_new ([n][Hkv][d], or null): the token each sequence has just been given
+// (its page and length already set on the host); the attention reads it
+// from these rows and the fusion writes it into the pool and the summaries.
+// Only for a token whose block lies wholly in the recent window.
 hipError_t launch_step(const Ctx &c, const SeqBatch &b, int max_blocks, int P, const uint16_t *q,
                        int32_t *blk_idx, int32_t *blk_cnt, int32_t k_cap, float *o_part,
                        float *lse_part, int32_t p_cap, float *o, float *lse, uint32_t epoch,
-                       int ptl_cap, hipStream_t st);
+                       int ptl_cap, const uint16_t *k_new, const uint16_t *v_new,
+                       hipStream_t st);
 
 // Workgroups of the one-launch step that can be resident on the device at
 // once (0 if unknown).

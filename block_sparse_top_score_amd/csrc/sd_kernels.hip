@@ -1634,6 +1634,16 @@ __device__ __forceinline__ int page_dense16(const UG &g, int pn) {
 //        channel are one 16-byte load in the MFMA B layout; two MFMAs per
 //        16 output channels accumulate O in fp32.
 // The four waves merge their (max, sum, O) once at the end.
+// The step's new token of one unit when its append runs inside the step
+// launch (the block holding it lies wholly in the recent window, so no score
+// depends on it): the attention takes its K and V from the caller's rows, and
+// the unit's fusion, which runs after every part, writes it into its page and
+// folds it into the block summary.  pg < 0: no such token.
+struct NewTok {
+  int pg = -1, slot = 0;                      // physical page, place in the page
+  const uint16_t *k = nullptr, *v = nullptr;  // rows [D] of this (sequence, KV head)
+};
+
 template <int D, int G>
 struct AttLds {
   float p[4][16][32];  // per wave: the stage's weights, [head row][token]
@@ -1656,12 +1666,16 @@ struct AttWave {
 
 template <int D>
 __device__ __forceinline__ void load_stage(const Ctx &c, int h, int pg0, int pg1,
-                                           KVStage<D> &st) {
+                                           KVStage<D> &st, const NewTok &tok) {
   const int lane = threadIdx.x & 63, r16 = lane & 15, lgrp = lane >> 4;
 #pragma unroll
   for (int pi = 0; pi < 2; ++pi) {
-    const uint16_t *kp = c.L.k + ((((size_t)(pi ? pg1 : pg0) * c.dm.Hkv + h) * kPage + r16) * D +
-                                  lgrp * (D / 4));
+    const int pg = pi ? pg1 : pg0;
+    // the lane of the step's new token reads its K from the caller's row
+    const uint16_t *kp = (pg == tok.pg && r16 == tok.slot)
+                             ? tok.k + lgrp * (D / 4)
+                             : c.L.k + ((((size_t)pg * c.dm.Hkv + h) * kPage + r16) * D +
+                                        lgrp * (D / 4));
 #pragma unroll
     for (int m = 0; m < D / 32; ++m) st.k[pi][m] = *reinterpret_cast<const uint4 *>(kp + 8 * m);
   }
@@ -1684,7 +1698,7 @@ template <int D, int G>
 __device__ __forceinline__ void compute_stage(const Ctx &c, KVStage<D> &st, int mk0, int mk1,
                                               int s0, int s1, const uint4 (&qa)[D / 32],
                                               const uint4 &ones, AttWave<D> &W, float (*pl)[32],
-                                              float *lmb) {
+                                              float *lmb, int newp, const NewTok &tok) {
   const int lane = threadIdx.x & 63, r16 = lane & 15, lgrp = lane >> 4;
   constexpr int NT = D / 16;
   constexpr float kLn2 = 0.69314718055994530942f;
@@ -1735,6 +1749,22 @@ __device__ __forceinline__ void compute_stage(const Ctx &c, KVStage<D> &st, int 
     }
     ahi = make_uint4(hw[0], hw[1], hw[2], hw[3]);
     alo = make_uint4(lw[0], lw[1], lw[2], lw[3]);
+  }
+  // page newp (0 or 1, uniform) of the stage holds the step's new token: the
+  // lanes whose 8 tokens include it take its V from the caller's row (one
+  // stage per unit)
+  if (newp >= 0 && (lgrp >= 2 ? 1 : 0) == newp && (lgrp & 1) == (tok.slot >> 3)) {
+    const int e = tok.slot & 7, sh = 16 * (e & 1);
+    const uint32_t keep = ~(0xffffu << sh);
+#pragma unroll
+    for (int nt = 0; nt < NT; ++nt) {
+      const uint32_t x = (uint32_t)tok.v[16 * nt + r16] << sh;
+      uint4 &vv = st.v[nt];
+      vv.x = (e >> 1) == 0 ? (vv.x & keep) | x : vv.x;
+      vv.y = (e >> 1) == 1 ? (vv.y & keep) | x : vv.y;
+      vv.z = (e >> 1) == 2 ? (vv.z & keep) | x : vv.z;
+      vv.w = (e >> 1) == 3 ? (vv.w & keep) | x : vv.w;
+    }
   }
   // masked tokens have zero weight; their V is zeroed too, so that stale or
   // unwritten slots cannot turn the products into NaN
@@ -1787,7 +1817,7 @@ __device__ __forceinline__ void compute_stage(const Ctx &c, KVStage<D> &st, int 
 template <int D, int G, class Resolve>
 __device__ __forceinline__ void wave_pages(const Ctx &c, int h, int gw, int NW, int total,
                                            Resolve resolve, const uint4 (&qa)[D / 32], AttWave<D> &W,
-                                           float (*pl)[32], float *lmb) {
+                                           float (*pl)[32], float *lmb, const NewTok &tok) {
   const int lane = threadIdx.x & 63;
   const int nw = total > gw ? cdiv(total - gw, NW) : 0;
   for (int b0 = 0; b0 < nw; b0 += 64) {
@@ -1803,16 +1833,18 @@ __device__ __forceinline__ void wave_pages(const Ctx &c, int h, int gw, int NW, 
     const uint32_t one2 = (r16 == 0 || (r16 == 1 && lgrp < 2) || (r16 == 2 && lgrp >= 2))
                               ? 0x3f803f80u : 0u;
     const uint4 ones = make_uint4(one2, one2, one2, one2);
+    // which page of stage t (pages 2t, 2t + 1) holds the step's new token
+    auto NP = [&](int t) { return PG(2 * t) == tok.pg ? 0 : (PG(2 * t + 1) == tok.pg ? 1 : -1); };
     KVStage<D> A, B;
-    load_stage<D>(c, h, PG(0), PG(1), A);
+    load_stage<D>(c, h, PG(0), PG(1), A, tok);
     for (int s = 0;; s += 2) {
-      load_stage<D>(c, h, PG(2 * s + 2), PG(2 * s + 3), B);
+      load_stage<D>(c, h, PG(2 * s + 2), PG(2 * s + 3), B, tok);
       compute_stage<D, G>(c, A, MK(2 * s), MK(2 * s + 1), SL(2 * s), SL(2 * s + 1), qa, ones, W,
-                          pl, lmb);
+                          pl, lmb, NP(s), tok);
       if (s + 1 >= ns) break;
-      load_stage<D>(c, h, PG(2 * s + 4), PG(2 * s + 5), A);
+      load_stage<D>(c, h, PG(2 * s + 4), PG(2 * s + 5), A, tok);
       compute_stage<D, G>(c, B, MK(2 * s + 2), MK(2 * s + 3), SL(2 * s + 2), SL(2 * s + 3), qa,
-                          ones, W, pl, lmb);
+                          ones, W, pl, lmb, NP(s + 1), tok);
       if (s + 2 >= ns) break;
     }
   }
@@ -1836,7 +1868,7 @@ __device__ __attribute__((always_inline)) void attend_part(const Ctx &c, int i, 
                                                            float *__restrict__ lse_part, int p_cap,
                                                            AttLds<D, G> &sm,
                                                            const int32_t *ptl /* LDS or null */,
-                                                           int *s_cnt) {
+                                                           int *s_cnt, const NewTok &tok) {
   const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6, r16 = lane & 15, lgrp = lane >> 4;
   constexpr int NT = D / 16;
   const int qh0 = h * G, NW = 4 * P, gw = 4 * part + wv;
@@ -1869,7 +1901,7 @@ __device__ __attribute__((always_inline)) void attend_part(const Ctx &c, int i, 
         mk = page_dense16(g, pn);
         sl = t;
       },
-      qa, W, pl, lmb);
+      qa, W, pl, lmb, tok);
 
   // the selection
   int cnt = si.cnt;
@@ -1923,7 +1955,7 @@ __device__ __attribute__((always_inline)) void attend_part(const Ctx &c, int i, 
           mk = in_range ? page_valid16(g, pn) & ~page_dense16(g, pn) : 0;
           sl = c.dm.lm_sel0 + t;
         },
-        qa, W, pl, lmb);
+        qa, W, pl, lmb, tok);
   }
 
   // merge the four waves into the part's partial
@@ -2013,10 +2045,31 @@ __device__ __attribute__((always_inline)) void fuse_unit(const Ctx &c, int i, in
                                                          const float *__restrict__ o_part,
                                                          const float *__restrict__ lse_part,
                                                          int p_cap, float *__restrict__ o,
-                                                         float *__restrict__ lse, FuseSmem<G> &sm) {
+                                                         float *__restrict__ lse, FuseSmem<G> &sm,
+                                                         const NewTok &tok = NewTok()) {
   const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
   const int qh0 = h * G;
   n_slots = min(n_slots, kFuseSlots);  // (the host keeps every call within it)
+  // the step's new token (its append folded into the step): its K/V row
+  // chunks and, for a block that already held tokens, the block's summary
+  // chunks, loaded with the rest
+  constexpr int C4 = D / 4;
+  const bool app = tok.k != nullptr;
+  const int pos = g.N - 1, blk_new = app ? div_S(pos, g.S) : 0;
+  const bool had = app && pos > blk_new * g.S;  // the block held tokens before
+  uint16_t *sp_new = c.L.summ + hi.summ_off + (size_t)seq * C4 * hi.nbmax * 8 +
+                     ((size_t)tid * hi.nbmax + blk_new) * 8;
+  uint4 k8 = make_uint4(0, 0, 0, 0), s_old = make_uint4(0, 0, 0, 0);
+  uint2 k4 = make_uint2(0, 0);
+  uint16_t v1 = 0;
+  if (app) {
+    if (tid < D / 8) k8 = reinterpret_cast<const uint4 *>(tok.k)[tid];
+    if (tid < D) v1 = tok.v[tid];
+    if (tid < C4) {
+      k4 = reinterpret_cast<const uint2 *>(tok.k)[tid];
+      if (had) s_old = *reinterpret_cast<const uint4 *>(sp_new);
+    }
+  }
   const DenseList dl = with_maw ? dense_list(g) : DenseList{0, 0, 0, 0};
   const float *lmb = c.sc.lm_pg + ((size_t)seq * c.dm.Hq + qh0) * c.dm.lm_cap;
 
@@ -2111,6 +2164,30 @@ __device__ __attribute__((always_inline)) void fuse_unit(const Ctx &c, int i, in
     od[3] = acc.w;
   }
   if (tid < G) lse[(size_t)i * c.dm.Hq + qh0 + tid] = sm.lse[tid];
+  if (app) {
+    // the new token into its page (V transposed) and its block's summary:
+    // min/max folded in logical order, as the append kernel does
+    const size_t pk = (((size_t)tok.pg * c.dm.Hkv + h) * kPage + tok.slot) * D;
+    if (tid < D / 8) reinterpret_cast<uint4 *>(c.L.k + pk)[tid] = k8;
+    if (tid < D) c.L.v[(((size_t)tok.pg * c.dm.Hkv + h) * D + tid) * kPage + tok.slot] = v1;
+    if (tid < C4) {
+      const uint32_t kw[2] = {k4.x, k4.y}, ow[4] = {s_old.x, s_old.y, s_old.z, s_old.w};
+      uint32_t nw[4];
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const uint32_t x = (kw[j >> 1] >> (16 * (j & 1))) & 0xffffu;
+        uint32_t mn = x, mx = x;
+        if (had) {
+          const uint32_t omn = ow[j] & 0xffffu, omx = ow[j] >> 16;
+          const float fx = __uint_as_float(x << 16);
+          mn = fx < __uint_as_float(omn << 16) ? x : omn;
+          mx = fx > __uint_as_float(omx << 16) ? x : omx;
+        }
+        nw[j] = mn | (mx << 16);
+      }
+      *reinterpret_cast<uint4 *>(sp_new) = make_uint4(nw[0], nw[1], nw[2], nw[3]);
+    }
+  }
   if (!with_maw || g.n_dt == 0) return;
 
   // ---- MAW -------------------------------------------------------------------
@@ -2266,7 +2343,7 @@ __global__ __launch_bounds__(256, 2) void k_attend(Ctx c, SeqBatch b, int P,
   si.cnt = min(min(max(blk_cnt[(size_t)i * c.dm.Hkv + h], 0), k_cap), hi.kcap);
   if (part == 0) empty_slots<D, G>(c, i, h, PU, p_cap, o_part, lse_part);
   attend_part<D, G>(c, i, seq, h, g, part, PU, q, si, o_part, lse_part, p_cap, sm, nullptr,
-                    &s_cnt);
+                    &s_cnt, NewTok());
 }
 
 // One decode step in one launch.  Workgroups by index: score tiles (the last
@@ -2286,7 +2363,9 @@ __global__ __launch_bounds__(256, 2) void k_step(Ctx c, SeqBatch b, int tiles_x,
                                                  float *__restrict__ o_part,
                                                  float *__restrict__ lse_part, int p_cap,
                                                  float *__restrict__ o, float *__restrict__ lse,
-                                                 int lrows_words, uint32_t epoch, int ptl_cap) {
+                                                 int lrows_words, uint32_t epoch, int ptl_cap,
+                                                 const uint16_t *__restrict__ k_new,
+                                                 const uint16_t *__restrict__ v_new) {
   // dynamic LDS: max(TopkSmem + top-k words and row masks, AttLds + ptl_cap
   // page-table entries, FuseSmem)
   extern __shared__ __align__(16) unsigned char smem_raw[];
@@ -2377,12 +2456,21 @@ __global__ __launch_bounds__(256, 2) void k_step(Ctx c, SeqBatch b, int tiles_x,
   si.rtag = no_sel ? nullptr : &c.sc.rtag[unit];
   si.cnt = 0;
   si.epoch = epoch;
+  // the step's appended token, if its append runs in this launch (N >= 1)
+  NewTok tok;
+  if (k_new) {
+    tok.k = k_new + ((size_t)i * c.dm.Hkv + h) * D;
+    tok.v = v_new + ((size_t)i * c.dm.Hkv + h) * D;
+    tok.slot = (N - 1) & (kPage - 1);
+    tok.pg = c.L.pt[(size_t)seq * c.dm.pages_per_seq + ((N - 1) >> 4)];
+  }
   attend_part<D, G>(c, i, seq, h, g, idx, PU, q, si, o_part, lse_part, p_cap, smem_att, ptl,
-                    &s_cnt);
+                    &s_cnt, tok);
   uint32_t *fctr = &c.sc.arrive[unit * 2 + 1];
   if (!arrive_last(fctr, (unsigned)PU, &s_flag)) return;
   __builtin_amdgcn_s_setprio(3);
-  fuse_unit<D, G>(c, i, seq, h, hi, g, true, PU, o_part, lse_part, p_cap, o, lse, smem_fuse);
+  fuse_unit<D, G>(c, i, seq, h, hi, g, true, PU, o_part, lse_part, p_cap, o, lse, smem_fuse,
+                  tok);
   if (threadIdx.x == 0) st_dev(fctr, 0u);
 }
 
@@ -2517,7 +2605,8 @@ int step_capacity(const Ctx &c, int max_blocks, int ptl_cap) {
 hipError_t launch_step(const Ctx &c, const SeqBatch &b, int max_blocks, int P, const uint16_t *q,
                        int32_t *blk_idx, int32_t *blk_cnt, int32_t k_cap, float *o_part,
                        float *lse_part, int32_t p_cap, float *o, float *lse, uint32_t epoch,
-                       int ptl_cap, hipStream_t st) {
+                       int ptl_cap, const uint16_t *k_new, const uint16_t *v_new,
+                       hipStream_t st) {
   if (b.n <= 0) return hipSuccess;
   if (P < 1 || P > p_cap) return hipErrorInvalidValue;
   const int tiles_x = max(1, (max_blocks + kScoreTile - 1) / kScoreTile);
@@ -2530,7 +2619,7 @@ hipError_t launch_step(const Ctx &c, const SeqBatch &b, int max_blocks, int P, c
     const size_t smem = std::max(std::max(att, sizeof(FuseSmem<G_>)), topk_bytes);
     hipLaunchKernelGGL((k_step<D_, G_>), grid, dim3(256), smem, st, c, b, tiles_x, P,
                        blk_idx, blk_cnt, k_cap, q, o_part, lse_part, p_cap, o, lse, lrows_words,
-                       epoch, ptl_cap);
+                       epoch, ptl_cap, k_new, v_new);
   });
   return hipGetLastError();
 }

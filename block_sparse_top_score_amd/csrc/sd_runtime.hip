@@ -55,7 +55,7 @@ struct Layer {
 struct sd_ctx {
   sd_config cfg{};
   std::vector<int32_t> S, ppm;
-  int D = 0, Hq = 0, Hkv = 0, G = 0, pps = 0;
+  int D = 0, Hq = 0, Hkv = 0, G = 0, pps = 0, max_S = 0;
   hipStream_t stream = nullptr;
   int device = 0;
   std::vector<HeadInfo> heads;
@@ -262,6 +262,7 @@ sd_status sparse_decode_init(const sd_config *cfg, sd_ctx **out) {
   c->D = cfg->head_dim;
   c->pps = (int)cdiv(cfg->max_seq_len, kPage);
   c->S.assign(cfg->block_size, cfg->block_size + c->Hkv);
+  c->max_S = *std::max_element(c->S.begin(), c->S.end());
   c->ppm.assign(cfg->budget_ppm, cfg->budget_ppm + c->Hkv);
   c->cfg.block_size = nullptr;
   c->cfg.budget_ppm = nullptr;
@@ -476,9 +477,11 @@ Ctx kctx(const sd_ctx *c, int layer) {
 }
 
 // Host-side append: validate, take pages, push the touched page-table span,
-// launch the append kernel.  n_new == NULL: one token per sequence.
+// then (launch) the append kernel.  n_new == NULL: one token per sequence.
+// Without launch the caller's step kernel writes the tokens and summaries.
 sd_status do_append(sd_ctx *c, int32_t layer, int32_t n_seqs, const int32_t *seq_ids,
-                    const int32_t *n_new_arr, const void *k_bf16, const void *v_bf16) {
+                    const int32_t *n_new_arr, const void *k_bf16, const void *v_bf16,
+                    bool launch = true) {
   Layer &L = c->layers[layer];
   auto n_new = [n_new_arr](int i) { return n_new_arr ? n_new_arr[i] : 1; };
   int64_t total = 0, pages_needed = 0;
@@ -492,6 +495,9 @@ sd_status do_append(sd_ctx *c, int32_t layer, int32_t n_seqs, const int32_t *seq
     pages_needed += cdiv(nl, kPage) - cdiv(L.len[seq_ids[i]], kPage);
   }
   if (total > 0 && (!k_bf16 || !v_bf16)) return fail(c, SD_EINVAL, "k/v pointers are NULL");
+  if (total > 0 && (reinterpret_cast<uintptr_t>(k_bf16) % 16 != 0 ||
+                    reinterpret_cast<uintptr_t>(v_bf16) % 16 != 0))
+    return fail(c, SD_EINVAL, "k/v rows must be 16-byte aligned");
   if (pages_needed > (int64_t)L.free_pages.size())
     return fail(c, SD_ENOMEM, "page pool of layer %d exhausted: need %lld pages, %zu free",
                 layer, (long long)pages_needed, L.free_pages.size());
@@ -511,7 +517,7 @@ sd_status do_append(sd_ctx *c, int32_t layer, int32_t n_seqs, const int32_t *seq
                              hipMemcpyHostToDevice, c->stream));
   const Ctx kc = kctx(c, layer);
   int row = 0;
-  for (int base = 0; base < n_seqs; base += kLaunchSeqs) {
+  for (int base = 0; launch && base < n_seqs; base += kLaunchSeqs) {
     AppendBatch b{};
     b.n = std::min(kLaunchSeqs, n_seqs - base);
     int max_new = 0, max_touch = 0;
@@ -748,9 +754,15 @@ sd_status decode_step_impl(sd_ctx *c, int32_t layer, int32_t n_seqs, const int32
     }
   }
   const uint16_t *q = static_cast<const uint16_t *>(q_bf16);
+  // the append runs inside the step launch when the new token's block lies
+  // wholly in the recent window for every head (W >= S): no score then
+  // depends on it; otherwise the append kernel runs first
+  const bool fold = k_new && c->cfg.recent_window >= c->max_S;
   if (clear) SD_HIP(c, launch_fill_u32(clear, clear_words, 0u, c->stream));
-  if (k_new && (s = do_append(c, layer, n_seqs, seq_ids, nullptr, k_new, v_new)) != SD_OK)
+  if (k_new && (s = do_append(c, layer, n_seqs, seq_ids, nullptr, k_new, v_new, !fold)) != SD_OK)
     return s;
+  const uint16_t *kn = fold ? static_cast<const uint16_t *>(k_new) : nullptr;
+  const uint16_t *vn = fold ? static_cast<const uint16_t *>(v_new) : nullptr;
   Ctx kc = kctx(c, layer);
   kc.sc = sc;
   for (int base = 0; base < n_seqs; base += kLaunchSeqs) {
@@ -765,9 +777,11 @@ sd_status decode_step_impl(sd_ctx *c, int32_t layer, int32_t n_seqs, const int32
     float *op = o_part + (size_t)base * c->Hq * p_cap * c->D;
     float *lp = lse_part + (size_t)base * c->Hq * p_cap;
     if (++c->epoch == 0) c->epoch = 1;
+    const size_t row0 = (size_t)base * c->Hkv * c->D;
     SD_HIP(c, launch_step(kc, b, mb, P, qb, bi, bc, k_cap, op, lp, p_cap,
                           o + (size_t)base * c->Hq * c->D, lse + (size_t)base * c->Hq,
-                          c->epoch, c->pps <= kPtLds ? c->pps : 0, c->stream));
+                          c->epoch, c->pps <= kPtLds ? c->pps : 0, kn ? kn + row0 : nullptr,
+                          vn ? vn + row0 : nullptr, c->stream));
   }
   c->pend_layer = -2;
   return SD_OK;

@@ -315,3 +315,37 @@ def test_loop32_all_layers_short_horizon():
             log("  step %d done (N=%d)" % (step, N))
     finally:
         eng.close()
+
+
+@pytest.mark.parametrize("window,S", [(0, 16), (8, 16), (16, 16), (32, 64), (64, 64)])
+def test_fused_append_window_against_block_size(window, S):
+    """The one-launch step with its one-token append, four steps in a row,
+    every unit against the oracle (summaries included).  With W >= S the
+    append runs inside the step (the new token's block lies wholly in the
+    window); with W < S that block can be a candidate, so the append kernel
+    runs first."""
+    w = _w(synth.tiny(), B=3, N=3000, window=window, block_size=[S], budget_ppm=[100000])
+    log("case: fused append, W=%d S=%d" % (window, S))
+    x = synth.single_step(w, 4, device="cuda", N=w.N)
+    N0 = w.N - 4
+    eng = harness.make_engine(w, w.N + 64)
+    try:
+        harness.prefill(eng, 0, x["K"][:, :N0].contiguous(), x["V"][:, :N0].contiguous())
+        Kb, Vb = synth.bits(x["K"]), synth.bits(x["V"])
+        bufs = eng.alloc_step(w.B)
+        for t in range(4):
+            N = N0 + t + 1
+            kn = x["K"][:, N - 1].contiguous()
+            vn = x["V"][:, N - 1].contiguous()
+            q = synth.single_step(w, 100 + t, device="cuda", N=16)["q"]
+            eng.decode_step(0, list(range(w.B)), q, bufs["blk_idx"], bufs["blk_cnt"],
+                            bufs["o_part"], bufs["lse_part"], bufs["o"], bufs["lse"],
+                            k_new=kn, v_new=vn)
+            eng.sync()
+            gpu = {k: v.cpu().numpy() for k, v in bufs.items()}
+            st = harness.check_units(w, eng, 0, list(range(w.B)), synth.bits(q),
+                                     {b: Kb[b] for b in range(w.B)}, {b: Vb[b] for b in range(w.B)},
+                                     {b: N for b in range(w.B)}, gpu, check_summ=True)
+            _check(st)
+    finally:
+        eng.close()
