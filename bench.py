@@ -83,6 +83,10 @@ def parse():
     ap.add_argument("--streaming-heads", type=int, default=0,
                     help="give the first K KV heads budget 0 (streaming heads: sinks and "
                          "recent window only); a variant of the workload, not the headline")
+    ap.add_argument("--timeline", type=int, default=0, metavar="STEPS",
+                    help="measurement build only (build.py --timeline): record the per-phase "
+                         "timestamps of STEPS one-launch steps after the warm-up, print their "
+                         "per-role medians and exit")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="run a plain 1 GiB device copy (counter calibration) and exit")
     ap.add_argument("--traffic-summary", nargs=4, metavar=("FETCH", "WRITE", "CAL_FETCH", "CAL_WRITE"),
@@ -194,7 +198,9 @@ def main():
         sys.exit(2)
     import torch
     import synth
-    from block_sparse_top_score_amd import SparseDecode
+    from block_sparse_top_score_amd import SparseDecode, _abi
+    if args.timeline:
+        _abi.load(_abi.LIB_TIMELINE_PATH)
 
     torch.cuda.set_device(0)
     dev = torch.device("cuda:0")
@@ -271,6 +277,10 @@ def main():
         step(s_global)
         s_global += 1
     eng.sync()
+    if args.timeline:
+        timeline(args, w, eng, step, s_global, L)
+        eng.close()
+        return
 
     # timed trials: exactly --steps steps each, median reported
     trial_ms = []
@@ -377,6 +387,81 @@ def main():
         print("parity of the last timed step FAILED: %s" % json.dumps(out["parity"]),
               file=sys.stderr)
         sys.exit(1)
+
+
+def timeline(args, w, eng, step, s0, L):
+    """Per-phase timestamps of --timeline one-launch steps (the measurement
+    build): for each step, every workgroup's phase times in microseconds from
+    the step's first workgroup start; printed as medians and 10th/90th
+    percentiles per role and phase over all workgroups and steps, plus the
+    per-step time of the last event (the end of the critical path)."""
+    import torch
+    from block_sparse_top_score_amd import _abi
+    # score tiles per unit in the launch: blocks that can hold a candidate,
+    # ceil((N - W) / S), in tiles of 256 (N about the current length)
+    n_now = eng.seq_len(s0 % L, 0) + 1
+    tiles = -(-max(-(-max(0, n_now - w.window) // S) for S in w.block_size) // 256)
+    n_wg = w.Hkv * w.B * 64
+    names = {"score": ["start", "keys written", "tile list published", "arrived",
+                       "top-k done", "MAW updated (by the top-k)"],
+             "part": ["start", "dense pages done (wave 0)", "selection count seen",
+                      "selected pages done (wave 0)", "partial written, arrived",
+                      "fusion done", "(unused)", "MAW updated (by a part)"]}
+    acc = {r: {k: [] for k in range(len(v))} for r, v in names.items()}
+    # durations inside the last-arriver roles, per workgroup (us)
+    spans = {"top-k (last tile: arrived -> done)": ("score", 3, 4),
+             "fusion (last part: arrived -> done)": ("part", 4, 5),
+             "MAW by the top-k (top-k done -> MAW done)": ("score", 4, 5),
+             "MAW by a part (dense done -> MAW done)": ("part", 1, 7),
+             "tile: keys -> list published": ("score", 1, 2),
+             "tile: list published -> arrived": ("score", 2, 3),
+             "part: selected pages done -> partial written, arrived": ("part", 3, 4)}
+    dur = {k: [] for k in spans}
+    ends = []
+    _abi.timeline_read(n_wg)  # clear
+    for t in range(args.timeline):
+        step(s0 + t)
+        torch.cuda.synchronize()
+        tl = _abi.timeline_read(n_wg).astype(np.int64)
+        used = tl[:, 0] > 0
+        t0 = tl[used, 0].min()
+        us = (tl - t0) / 100.0  # 100 MHz ticks -> us
+        for wg in np.nonzero(used)[0]:
+            z = wg // (w.Hkv * w.B)
+            role = "score" if z < tiles else "part"
+            for k in range(len(names[role])):
+                if tl[wg, k] > 0:
+                    acc[role][k].append(us[wg, k])
+            for name, (r_, a_, b_) in spans.items():
+                if r_ == role and tl[wg, a_] > 0 and tl[wg, b_] > 0:
+                    dur[name].append(us[wg, b_] - us[wg, a_])
+        ends.append(float(us[used].max()))
+    out = {"workload": w.name, "steps": args.timeline, "tiles_per_unit": tiles,
+           "last_event_us": {"median": float(np.median(ends)), "min": float(np.min(ends)),
+                             "max": float(np.max(ends))}}
+    for role, ph in names.items():
+        rows = []
+        for k, name in enumerate(ph):
+            v = np.array(acc[role][k])
+            if v.size:
+                rows.append({"phase": name, "n": int(v.size), "p10": float(np.percentile(v, 10)),
+                             "median": float(np.median(v)), "p90": float(np.percentile(v, 90)),
+                             "max": float(v.max())})
+        out[role] = rows
+    out["durations"] = [{"span": k, "n": len(v), "median": float(np.median(v)),
+                         "p90": float(np.percentile(v, 90))} for k, v in dur.items() if v]
+    print(json.dumps(out), flush=True)
+    for role in names:
+        print("%s:" % role)
+        for r in out[role]:
+            print("  %-30s n=%6d  p10 %6.2f  median %6.2f  p90 %6.2f  max %6.2f us"
+                  % (r["phase"], r["n"], r["p10"], r["median"], r["p90"], r["max"]))
+    print("durations:")
+    for r in out["durations"]:
+        print("  %-62s n=%5d  median %5.2f  p90 %5.2f us" % (r["span"], r["n"], r["median"], r["p90"]))
+    print("last event per step: median %.2f us (min %.2f, max %.2f)"
+          % (out["last_event_us"]["median"], out["last_event_us"]["min"],
+             out["last_event_us"]["max"]), flush=True)
 
 
 def read_ceiling(nbytes, kstep_gbs, n_buf=8, reps=64, wgs=8192):

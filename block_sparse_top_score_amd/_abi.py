@@ -15,6 +15,8 @@ import numpy as np
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_HERE, "libsparse_decode.so")
+# the measurement build with per-phase timestamps (build.py --timeline)
+LIB_TIMELINE_PATH = os.path.join(_HERE, "libsparse_decode_timeline.so")
 
 SD_OK, SD_EINVAL, SD_ENOMEM, SD_EHIP, SD_EUNSUPPORTED, SD_ESTATE = 0, -1, -2, -3, -4, -5
 SD_DEBUG_PAGE_TABLE, SD_DEBUG_SUMMARY, SD_DEBUG_MAW, SD_DEBUG_K, SD_DEBUG_V = range(5)
@@ -292,3 +294,22 @@ class SparseDecode:
         lse = t.empty((n_seqs, self.Hq), dtype=t.float32, device=device)
         return dict(blk_idx=blk_idx, blk_cnt=blk_cnt, o_part=o_part, lse_part=lse_part,
                     o=o, lse=lse)
+
+
+def timeline_read(n_wg):
+    """Timestamps of the last steps from the measurement build (loaded with
+    load(LIB_TIMELINE_PATH)): uint64 [n_wg][slots]; the table is then zeroed."""
+    L = load()
+    if not hasattr(L, "sd_timeline_read"):
+        raise RuntimeError("the loaded library is not the timeline build")
+    L.sd_timeline_read.restype = ctypes.c_int32
+    L.sd_timeline_read.argtypes = [ctypes.c_void_p, ctypes.c_size_t,
+                                   ctypes.POINTER(ctypes.c_int32), ctypes.POINTER(ctypes.c_int32)]
+    slots, max_wg = ctypes.c_int32(), ctypes.c_int32()
+    L.sd_timeline_read(None, 0, ctypes.byref(slots), ctypes.byref(max_wg))
+    n_wg = min(n_wg, max_wg.value)
+    out = np.zeros((n_wg, slots.value), np.uint64)
+    st = L.sd_timeline_read(out.ctypes.data_as(ctypes.c_void_p), out.nbytes, None, None)
+    if st != SD_OK:
+        raise SDError(st, "sd_timeline_read")
+    return out

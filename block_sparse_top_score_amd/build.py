@@ -21,17 +21,23 @@ FLAGS = [
 ]
 
 
-def build(verbose: bool = False) -> str:
-    tmp = LIB + ".tmp%d" % os.getpid()
-    cmd = [HIPCC] + FLAGS + [os.path.join(CSRC, s) for s in SOURCES] + ["-o", tmp]
+LIB_TIMELINE = os.path.join(HERE, "libsparse_decode_timeline.so")
+
+
+def build(verbose: bool = False, timeline: bool = False) -> str:
+    """Compile the library; timeline=True builds the measurement variant
+    (per-phase timestamps of the one-launch step, SD_TIMELINE) instead."""
+    out = LIB_TIMELINE if timeline else LIB
+    tmp = out + ".tmp%d" % os.getpid()
+    cmd = ([HIPCC] + FLAGS + (["-DSD_TIMELINE"] if timeline else []) +
+           [os.path.join(CSRC, s) for s in SOURCES] + ["-o", tmp])
     if verbose:
         print(" ".join(cmd), flush=True)
     subprocess.check_call(cmd)
-    os.replace(tmp, LIB)
-    return LIB
+    os.replace(tmp, out)
+    return out
 
 
 if __name__ == "__main__":
-    build(verbose=True)
-    print(LIB)
+    print(build(verbose=True, timeline="--timeline" in sys.argv[1:]))
     sys.exit(0)

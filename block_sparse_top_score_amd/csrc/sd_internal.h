@@ -33,11 +33,13 @@ struct HeadInfo {
   int64_t maw_off;       // float offset of this head's MAW region
 };
 
-// Sequences of one launch: slot id and current token count.
+// Sequences of one launch: slot id and current token count; max_scored =
+// the most blocks any of its units scores (blocks that can hold a candidate).
 struct SeqBatch {
   int32_t n;
   int32_t seq[kLaunchSeqs];
   int32_t len[kLaunchSeqs];
+  int32_t max_scored;
 };
 
 // Per-launch append plan (host-computed).
@@ -82,7 +84,8 @@ struct Scratch {
   uint32_t *unit_acc;  // [max_seqs][Hkv][2] error bound (float bits, max) and
                        // flagged candidates (count) of the score tiles; 0 between steps
   float *lm_pg;      // [max_seqs][Hq][lm_cap] log softmax mass of each attended page
-  uint32_t *arrive;  // [max_seqs][Hkv][2] last-arriver counters (kept at 0)
+  uint32_t *arrive;  // [max_seqs][Hkv][4] last-arriver counters (kept at 0): score
+                     // tiles, attention parts, dense pages done (+ the top-k), spare
   unsigned long long *cand;  // [max_seqs][Hkv][key_stride] per-tile lists of the 64
                              // largest keys (key << 32 | ~block), tile t's at [64 t, 64 t + 64)
   unsigned long long *rtag;    // [max_seqs][Hkv] step << 32 | selected count, published

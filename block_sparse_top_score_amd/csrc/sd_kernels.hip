@@ -89,6 +89,32 @@ __device__ __forceinline__ bool arrive_last(uint32_t *counter, unsigned expected
 // Bound of every wait inside a launch.
 constexpr unsigned long long kWaitTicks = 20000000ull;  // 0.2 s of the 100 MHz clock
 
+}  // namespace
+
+// Per-phase timestamps of the one-launch step, built only with SD_TIMELINE
+// (a measurement build; the product library has none of this): thread 0 of
+// each workgroup stores wall_clock64(), a 100 MHz counter common to the whole
+// device, at the phase boundaries of its role, indexed by its flat workgroup
+// number.  sd_timeline_read copies them out.
+#ifdef SD_TIMELINE
+constexpr int kTlSlots = 8;
+constexpr int kTlMaxWG = 16384;
+__device__ unsigned long long sd_tl_buf[kTlMaxWG * kTlSlots];
+#define SD_TL(slot)                                                                  \
+  do {                                                                               \
+    if (threadIdx.x == 0) {                                                          \
+      const unsigned wg_ = blockIdx.x + gridDim.x * (blockIdx.y + gridDim.y * blockIdx.z); \
+      if (wg_ < (unsigned)kTlMaxWG) sd_tl_buf[wg_ * kTlSlots + (slot)] = wall_clock64(); \
+    }                                                                                \
+  } while (0)
+#else
+#define SD_TL(slot) \
+  do {              \
+  } while (0)
+#endif
+
+namespace {
+
 __device__ __forceinline__ int lower_bound(const int32_t *a, int n, int v) {
   int lo = 0, hi = n;
   while (lo < hi) {
@@ -107,9 +133,17 @@ __device__ __forceinline__ int budget_blocks(int ppm, int N, int S) {
 
 // Geometry of one unit.  D = [0, ns) U [wlo, N) ([FLX] sinks, [HGCA] recent
 // window); blocks [0, hb) touch the sinks, blocks [tb, n_blk) the window.
+// Candidates lie in [0, n_sc): a block from n_sc on lies wholly in the
+// window; only [0, n_sc) is scored and ranked.
 struct UG {
-  int N, S, n_blk, ns, wlo, hb, tb, n_dt, kk;
+  int N, S, n_blk, ns, wlo, hb, tb, n_dt, kk, n_sc;
 };
+// Blocks that can hold a candidate: [0, ceil(wlo / S)) with a window, else
+// all of them.
+__device__ __forceinline__ int scored_blocks(int N, int S, const Dims &dm) {
+  const int n_blk = div_S(N + S - 1, S);
+  return (dm.window > 0 && N > 0) ? min(n_blk, div_S(max(0, N - dm.window) + S - 1, S)) : n_blk;
+}
 __device__ __forceinline__ UG unit_geom(int N, const HeadInfo &hi, const Dims &dm) {
   UG g;
   const int S = hi.S;
@@ -125,6 +159,7 @@ __device__ __forceinline__ UG unit_geom(int N, const HeadInfo &hi, const Dims &d
     g.tb = g.n_blk;
   }
   g.n_dt = g.hb + (g.n_blk - g.tb);
+  g.n_sc = scored_blocks(N, S, dm);
   const int n_cand = g.ns < g.wlo ? div_S(g.wlo + S - 1, S) - div_S(g.ns, S) : 0;
   g.kk = min(n_cand, budget_blocks(hi.ppm, N, S));
   return g;
@@ -192,8 +227,8 @@ template <int G>
 struct FuseSmem {
   float w[G][kFuseSlots];   // per-slot LSE weights
   float lse[G];
-  float dm[4][G], dz[4][G];  // per wave: running max and sum of the dense log-masses
-  float pm[kFuseDenseLds];   // mass of each dense page under the dense partial, summed over heads
+  float dm[4 * G], dz[4 * G];  // MAW: per wave, running max and sum of the dense log-masses
+  float pm[kFuseDenseLds];     // MAW: mass of each dense page under the dense partial
 };
 
 // ---------------------------------------------------------------------------
@@ -651,8 +686,8 @@ __device__ __attribute__((always_inline)) bool score_tile(const Ctx &c, int i, i
     }
     const int blk = base + gi * 16 + r16;
     unsigned long long kv = 0u;
-    if (lgrp == 0 && blk < g.n_blk) {
-      const size_t ko = ((size_t)seq * c.dm.Hkv + h) * c.dm.key_stride + key_slot(blk, g.n_blk);
+    if (lgrp == 0 && blk < g.n_sc) {
+      const size_t ko = ((size_t)seq * c.dm.Hkv + h) * c.dm.key_stride + key_slot(blk, g.n_sc);
       const bool cand = is_candidate(g, blk);
       kv = cand ? order_key(A) : 0u;
       if (cand) emax = fmaxf(emax, score_eps(E, A));
@@ -683,6 +718,7 @@ __device__ __attribute__((always_inline)) bool score_tile(const Ctx &c, int i, i
     const uint32_t f = red[4] + red[5] + red[6] + red[7];
     if (f) __hip_atomic_fetch_add(acc + 1, f, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
   }
+  SD_TL(1);  // keys written
   if (publish) tile_list(c, seq, h, tile, sm);
   return publish;
 }
@@ -799,7 +835,7 @@ __device__ __attribute__((always_inline)) void topk_unit(const Ctx &c, int i, in
                           unsigned long long *tagd = nullptr, uint32_t epoch = 0) {
   if (threadIdx.x >= 64) return;
   const int lane = threadIdx.x;
-  const int n = g.n_blk, rows = cdiv(n, 64);
+  const int n = g.n_sc, rows = cdiv(n, 64);
   const size_t unit = (size_t)seq * c.dm.Hkv + h;
   const size_t uo = unit * c.dm.key_stride;
   const unsigned long long *gkf = c.sc.keyflag + uo;
@@ -1137,7 +1173,7 @@ __device__ __attribute__((always_inline)) void topk_wide(const Ctx &c, int i, in
                           int32_t *stage /* LDS, stage_words entries */, int stage_words,
                           unsigned long long *tagd = nullptr, uint32_t epoch = 0) {
   const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
-  const int n = g.n_blk, rows = cdiv(n, 64);
+  const int n = g.n_sc, rows = cdiv(n, 64);
   const int m = cdiv(n, 256), j0 = tid * m;
   const size_t unit = (size_t)seq * c.dm.Hkv + h;
   const size_t uo = unit * c.dm.key_stride;
@@ -1419,11 +1455,11 @@ __device__ __attribute__((always_inline)) bool topk_fast(const Ctx &c, int i, in
                                                          uint32_t epoch = 0) {
   const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
   const size_t unit = (size_t)seq * c.dm.Hkv + h;
-  const int n_tiles = max(1, cdiv(g.n_blk, kScoreTile));
+  const int n_tiles = max(1, cdiv(g.n_sc, kScoreTile));
   const unsigned long long etag = (unsigned long long)epoch << 32;
   const unsigned long long *cl = c.sc.cand + unit * c.dm.key_stride;
   const int kk = g.kk;
-  const int nw = cdiv(g.n_blk, 64);
+  const int nw = cdiv(g.n_sc, 64);
   // one batch of loads: lists and counts (wave 0), error bound, the query
   unsigned long long e[kFastTiles];
 #pragma unroll
@@ -1868,7 +1904,11 @@ __device__ __attribute__((always_inline)) void attend_part(const Ctx &c, int i, 
                                                            float *__restrict__ lse_part, int p_cap,
                                                            AttLds<D, G> &sm,
                                                            const int32_t *ptl /* LDS or null */,
-                                                           int *s_cnt, const NewTok &tok) {
+                                                           int *s_cnt, const NewTok &tok,
+                                                           const HeadInfo &hi,
+                                                           uint32_t *dctr = nullptr,
+                                                           unsigned d_expected = 0,
+                                                           int *s_dflag = nullptr) {
   const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6, r16 = lane & 15, lgrp = lane >> 4;
   constexpr int NT = D / 16;
   const int qh0 = h * G, NW = 4 * P, gw = 4 * part + wv;
@@ -1903,6 +1943,19 @@ __device__ __attribute__((always_inline)) void attend_part(const Ctx &c, int i, 
       },
       qa, W, pl, lmb, tok);
 
+  SD_TL(1);  // dense pages done (wave 0)
+  // one-launch step: every part, and the unit's top-k, arrive here once the
+  // dense pages' log-masses are written; the last to arrive updates MAW (and
+  // writes the folded append's token), off the unit's critical path
+  // (its own LDS flag: thread 0 rewrites *s_cnt below while other waves may
+  // still be reading the arrival's result)
+  if (dctr) {
+    if (arrive_last(dctr, d_expected, s_dflag)) {
+      dense_maw<D, G>(c, seq, h, hi, g, tok, &sm.p[0][0][0], &sm.wm[0][0], &sm.wz[0][0]);
+      if (threadIdx.x == 0) st_dev(dctr, 0u);
+      SD_TL(7);  // MAW updated here
+    }
+  }
   // the selection
   int cnt = si.cnt;
   if (si.rtag) {
@@ -1926,6 +1979,7 @@ __device__ __attribute__((always_inline)) void attend_part(const Ctx &c, int i, 
     __syncthreads();
     cnt = *s_cnt;
   }
+  SD_TL(2);  // selection count seen
   if (cnt > 0 && g.N > 0) {
     wave_pages<D, G>(
         c, h, gw, NW, cnt * PPB,
@@ -1958,6 +2012,7 @@ __device__ __attribute__((always_inline)) void attend_part(const Ctx &c, int i, 
         qa, W, pl, lmb, tok);
   }
 
+  SD_TL(3);  // selected pages done (wave 0)
   // merge the four waves into the part's partial
   if (r16 == 0) {
 #pragma unroll
@@ -2013,20 +2068,11 @@ __device__ __forceinline__ void empty_slots(const Ctx &c, int i, int h, int P, i
 }
 
 // ---------------------------------------------------------------------------
-// fusion + MAW ([HGCA] What carries the argument: the exact log-sum-exp merge
-// of partials; MAW as a moving average of attention weights; [LFPS] decay
-// r = 0.95).  For each query head: lse = m + log sum_u exp(lse_u - m) with m
-// the largest partial lse (empty slots, lse = -inf, drop out), and O =
-// sum_u exp(lse_u - lse) O_u.
-// MAW (a layer call) is fed by the dense partial alone ([HGCA] referee report
-// on section 3.2.2 / Algorithm 1: the average is updated from the GPU-side
-// window's attention weights, and an entry's average is frozen once it has
-// left the window; blocks leave the GPU side whole): per head, lse_D = log
-// sum of exp(log-mass) over the dense pages; each block whose tokens all lie
-// in D - a block that is not a candidate - takes MAW <- r MAW + (1 - r) a,
-// a = (1/G) sum_h sum of exp(log-mass - lse_D) over the block's pages; every
-// other block keeps its value.  Candidates are the only blocks the score
-// tiles read MAW of, and these are never written here.
+// fusion ([HGCA] What carries the argument: the exact log-sum-exp merge of
+// partials, with the maximum subtracted as the referee's minor comment on
+// section 3.3 asks): for each query head, lse = m + log sum_u exp(lse_u - m)
+// with m the largest partial lse (empty slots, lse = -inf, drop out), and
+// O = sum_u exp(lse_u - lse) O_u.
 // e^x and ln x from the hardware base-2 exponential and logarithm (about one
 // ulp each; the fp32 rounding of x log2(e) adds |x| 2^-24 relative, under
 // 1e-5 for the partial weights here)
@@ -2039,40 +2085,14 @@ __device__ __forceinline__ float fast_log(float x) {
 constexpr int kFusePre = 8;  // partial slots whose O values are preloaded
 
 template <int D, int G>
-__device__ __attribute__((always_inline)) void fuse_unit(const Ctx &c, int i, int seq, int h,
-                                                         const HeadInfo &hi, const UG &g,
-                                                         bool with_maw, int n_slots,
+__device__ __attribute__((always_inline)) void fuse_unit(const Ctx &c, int i, int h, int n_slots,
                                                          const float *__restrict__ o_part,
                                                          const float *__restrict__ lse_part,
                                                          int p_cap, float *__restrict__ o,
-                                                         float *__restrict__ lse, FuseSmem<G> &sm,
-                                                         const NewTok &tok = NewTok()) {
+                                                         float *__restrict__ lse, FuseSmem<G> &sm) {
   const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
   const int qh0 = h * G;
   n_slots = min(n_slots, kFuseSlots);  // (the host keeps every call within it)
-  // the step's new token (its append folded into the step): its K/V row
-  // chunks and, for a block that already held tokens, the block's summary
-  // chunks, loaded with the rest
-  constexpr int C4 = D / 4;
-  const bool app = tok.k != nullptr;
-  const int pos = g.N - 1, blk_new = app ? div_S(pos, g.S) : 0;
-  const bool had = app && pos > blk_new * g.S;  // the block held tokens before
-  uint16_t *sp_new = c.L.summ + hi.summ_off + (size_t)seq * C4 * hi.nbmax * 8 +
-                     ((size_t)tid * hi.nbmax + blk_new) * 8;
-  uint4 k8 = make_uint4(0, 0, 0, 0), s_old = make_uint4(0, 0, 0, 0);
-  uint2 k4 = make_uint2(0, 0);
-  uint16_t v1 = 0;
-  if (app) {
-    if (tid < D / 8) k8 = reinterpret_cast<const uint4 *>(tok.k)[tid];
-    if (tid < D) v1 = tok.v[tid];
-    if (tid < C4) {
-      k4 = reinterpret_cast<const uint2 *>(tok.k)[tid];
-      if (had) s_old = *reinterpret_cast<const uint4 *>(sp_new);
-    }
-  }
-  const DenseList dl = with_maw ? dense_list(g) : DenseList{0, 0, 0, 0};
-  const float *lmb = c.sc.lm_pg + ((size_t)seq * c.dm.Hq + qh0) * c.dm.lm_cap;
-
   // ---- one batch of loads ---------------------------------------------------
   constexpr int R = kFuseSlots / 64;
   float l0[R], l1[R];  // lse of heads wv and wv + 4
@@ -2102,12 +2122,6 @@ __device__ __attribute__((always_inline)) void fuse_unit(const Ctx &c, int i, in
   float4 ov[kFusePre];
 #pragma unroll
   for (int u = 0; u < kFusePre; ++u) ov[u] = ld_o(u, o_on && u < n_slots);
-  // log-masses of the dense pages (list positions [0, dl.n)): one per thread
-  // here, the rest (windows of more than 4096 tokens) after the O sums
-  float lmv[G];
-#pragma unroll
-  for (int gg = 0; gg < G; ++gg)
-    lmv[gg] = tid < dl.n ? ld_dev(&lmb[(size_t)gg * c.dm.lm_cap + tid]) : -INFINITY;
 
   // ---- per-head lse and slot weights ----------------------------------------
 #pragma unroll
@@ -2164,9 +2178,128 @@ __device__ __attribute__((always_inline)) void fuse_unit(const Ctx &c, int i, in
     od[3] = acc.w;
   }
   if (tid < G) lse[(size_t)i * c.dm.Hq + qh0 + tid] = sm.lse[tid];
+}
+
+// MAW update of one unit ([HGCA] What carries the argument: MAW, a moving
+// average of attention weights, against beta over the GPU-side entries;
+// referee report on section 3.2.2 / Algorithm 1: the average is fed by the
+// GPU-side window's attention weights alone and an entry's average is frozen
+// once it has left the window, blocks leaving whole; [LFPS] decay r = 0.95):
+// per head, lse_D = log sum of exp(log-mass) over the dense pages (the dense
+// partial's own normaliser); each block whose tokens all lie in D - a block
+// that is not a candidate - takes MAW <- r MAW + (1 - r) a, a = (1/G)
+// sum_h sum of exp(log-mass - lse_D) over the block's pages; every other
+// block keeps its value.  Candidates are the only blocks whose MAW the score
+// tiles read, and these are never written here, so this may run at any time
+// after every part of the unit has written its dense pages' log-masses.
+// With tok (the step's append folded into the launch, after every part has
+// read the dense pages) it also writes the new token into its page (V
+// transposed) and folds it into its block's summary (min/max in logical
+// order, as the append kernel does).  LDS: pm [kFuseDenseLds], dm and dz
+// [4 G] floats.  Every thread of the workgroup calls it.
+template <int D, int G>
+__device__ __attribute__((always_inline)) void dense_maw(const Ctx &c, int seq, int h,
+                                                         const HeadInfo &hi, const UG &g,
+                                                         const NewTok &tok, float *pm, float *dm,
+                                                         float *dz) {
+  const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
+  const DenseList dl = dense_list(g);
+  const float *lmb = c.sc.lm_pg + ((size_t)seq * c.dm.Hq + (size_t)h * G) * c.dm.lm_cap;
+  float *mw = c.L.maw + hi.maw_off + (size_t)seq * hi.nbmax;
+  constexpr int C4 = D / 4;
+  // ---- one batch of loads: the dense pages' log-masses (one page per
+  // thread; windows of more than 4096 tokens load the rest below), the MAW of
+  // the block of dense slot tid, the new token and its block's summary
+  float lmv[G];
+#pragma unroll
+  for (int gg = 0; gg < G; ++gg)
+    lmv[gg] = tid < dl.n ? ld_dev(&lmb[(size_t)gg * c.dm.lm_cap + tid]) : -INFINITY;
+  const int blk0 = tid < g.n_dt ? dense_block(g, tid) : 0;
+  const bool upd0 = tid < g.n_dt && !is_candidate(g, blk0);
+  const float mw0 = upd0 ? mw[blk0] : 0.0f;
+  const bool app = tok.k != nullptr;
+  const int pos = g.N - 1, blk_new = app ? div_S(pos, g.S) : 0;
+  const bool had = app && pos > blk_new * g.S;  // the block held tokens before
+  uint16_t *sp_new = c.L.summ + hi.summ_off + (size_t)seq * C4 * hi.nbmax * 8 +
+                     ((size_t)min(tid, C4 - 1) * hi.nbmax + blk_new) * 8;
+  uint4 k8 = make_uint4(0, 0, 0, 0), s_old = make_uint4(0, 0, 0, 0);
+  uint2 k4 = make_uint2(0, 0);
+  uint16_t v1 = 0;
   if (app) {
-    // the new token into its page (V transposed) and its block's summary:
-    // min/max folded in logical order, as the append kernel does
+    if (tid < D / 8) k8 = reinterpret_cast<const uint4 *>(tok.k)[tid];
+    if (tid < D) v1 = tok.v[tid];
+    if (tid < C4) {
+      k4 = reinterpret_cast<const uint2 *>(tok.k)[tid];
+      if (had) s_old = *reinterpret_cast<const uint4 *>(sp_new);
+    }
+  }
+  // ---- per head, lse_D: each thread folds its pages into a running (max,
+  // sum), then the waves', then the workgroup's
+  float mt[G], zt[G];
+#pragma unroll
+  for (int gg = 0; gg < G; ++gg) {
+    mt[gg] = lmv[gg];
+    zt[gg] = lmv[gg] == -INFINITY ? 0.0f : 1.0f;
+  }
+  for (int t = tid + 256; t < dl.n; t += 256)
+#pragma unroll
+    for (int gg = 0; gg < G; ++gg) {
+      const float x = ld_dev(&lmb[(size_t)gg * c.dm.lm_cap + t]);
+      if (x == -INFINITY) continue;
+      if (x > mt[gg]) {
+        zt[gg] = zt[gg] * fast_exp(mt[gg] - x) + 1.0f;  // (exp(-inf) = 0)
+        mt[gg] = x;
+      } else {
+        zt[gg] += fast_exp(x - mt[gg]);
+      }
+    }
+#pragma unroll
+  for (int gg = 0; gg < G; ++gg) {
+    const float M = wave_max(mt[gg]);
+    const float z = wave_sum(M == -INFINITY || mt[gg] == -INFINITY ? 0.0f
+                                                                   : zt[gg] * fast_exp(mt[gg] - M));
+    if (lane == 0) {
+      dm[wv * G + gg] = M;
+      dz[wv * G + gg] = z;
+    }
+  }
+  __syncthreads();
+  float lse_d[G];
+#pragma unroll
+  for (int gg = 0; gg < G; ++gg) {
+    const float M = fmaxf(fmaxf(dm[gg], dm[G + gg]), fmaxf(dm[2 * G + gg], dm[3 * G + gg]));
+    float z = 0.0f;
+    if (M != -INFINITY)
+#pragma unroll
+      for (int w = 0; w < 4; ++w)
+        z += dm[w * G + gg] == -INFINITY ? 0.0f : dz[w * G + gg] * fast_exp(dm[w * G + gg] - M);
+    lse_d[gg] = M == -INFINITY ? -INFINITY : M + fast_log(z);
+  }
+  // mass of each dense page under the dense partial, summed over the heads
+  for (int t = tid; t < dl.n; t += 256) {
+    float a = 0.0f;
+#pragma unroll
+    for (int gg = 0; gg < G; ++gg) {
+      const float x = t < 256 ? lmv[gg] : ld_dev(&lmb[(size_t)gg * c.dm.lm_cap + t]);
+      a += (x == -INFINITY || lse_d[gg] == -INFINITY) ? 0.0f : fast_exp(x - lse_d[gg]);
+    }
+    pm[t] = a;
+  }
+  __syncthreads();
+  const float r = c.dm.maw_decay, omr = 1.0f - r, inv_g = 1.0f / (float)G;
+  const int PPB = g.S / kPage;
+  for (int x = tid; x < g.n_dt; x += 256) {
+    const int blk = x == tid ? blk0 : dense_block(g, x);
+    if (is_candidate(g, blk)) continue;  // a token outside D: frozen
+    float a = 0.0f;
+    for (int pp = 0; pp < PPB; ++pp) {
+      const int t = dense_pos(dl, blk * PPB + pp);
+      if (t >= 0) a += pm[t];
+    }
+    const float m_old = x == tid ? mw0 : mw[blk];
+    mw[blk] = __fadd_rn(__fmul_rn(r, m_old), __fmul_rn(omr, a * inv_g));
+  }
+  if (app) {
     const size_t pk = (((size_t)tok.pg * c.dm.Hkv + h) * kPage + tok.slot) * D;
     if (tid < D / 8) reinterpret_cast<uint4 *>(c.L.k + pk)[tid] = k8;
     if (tid < D) c.L.v[(((size_t)tok.pg * c.dm.Hkv + h) * D + tid) * kPage + tok.slot] = v1;
@@ -2187,75 +2320,6 @@ __device__ __attribute__((always_inline)) void fuse_unit(const Ctx &c, int i, in
       }
       *reinterpret_cast<uint4 *>(sp_new) = make_uint4(nw[0], nw[1], nw[2], nw[3]);
     }
-  }
-  if (!with_maw || g.n_dt == 0) return;
-
-  // ---- MAW -------------------------------------------------------------------
-  // per head, lse_D of the dense partial: each thread folds its pages into a
-  // running (max, sum), then the waves', then the workgroup's
-  float mt[G], zt[G];
-#pragma unroll
-  for (int gg = 0; gg < G; ++gg) {
-    mt[gg] = lmv[gg];
-    zt[gg] = lmv[gg] == -INFINITY ? 0.0f : 1.0f;
-  }
-  auto fold = [&](int gg, float x) {
-    if (x == -INFINITY) return;
-    if (x > mt[gg]) {
-      zt[gg] = zt[gg] * fast_exp(mt[gg] - x) + 1.0f;  // (exp(-inf) = 0)
-      mt[gg] = x;
-    } else {
-      zt[gg] += fast_exp(x - mt[gg]);
-    }
-  };
-  for (int t = tid + 256; t < dl.n; t += 256)
-#pragma unroll
-    for (int gg = 0; gg < G; ++gg) fold(gg, ld_dev(&lmb[(size_t)gg * c.dm.lm_cap + t]));
-#pragma unroll
-  for (int gg = 0; gg < G; ++gg) {
-    const float M = wave_max(mt[gg]);
-    const float z = wave_sum(M == -INFINITY || mt[gg] == -INFINITY ? 0.0f
-                                                                   : zt[gg] * fast_exp(mt[gg] - M));
-    if (lane == 0) {
-      sm.dm[wv][gg] = M;
-      sm.dz[wv][gg] = z;
-    }
-  }
-  __syncthreads();
-  float lse_d[G];
-#pragma unroll
-  for (int gg = 0; gg < G; ++gg) {
-    const float M = fmaxf(fmaxf(sm.dm[0][gg], sm.dm[1][gg]), fmaxf(sm.dm[2][gg], sm.dm[3][gg]));
-    float z = 0.0f;
-    if (M != -INFINITY)
-#pragma unroll
-      for (int w = 0; w < 4; ++w)
-        z += sm.dm[w][gg] == -INFINITY ? 0.0f : sm.dz[w][gg] * fast_exp(sm.dm[w][gg] - M);
-    lse_d[gg] = M == -INFINITY ? -INFINITY : M + fast_log(z);
-  }
-  // mass of each dense page under the dense partial, summed over the heads
-  for (int t = tid; t < dl.n; t += 256) {
-    float a = 0.0f;
-#pragma unroll
-    for (int gg = 0; gg < G; ++gg) {
-      const float x = t < 256 ? lmv[gg] : ld_dev(&lmb[(size_t)gg * c.dm.lm_cap + t]);
-      a += (x == -INFINITY || lse_d[gg] == -INFINITY) ? 0.0f : fast_exp(x - lse_d[gg]);
-    }
-    sm.pm[t] = a;
-  }
-  __syncthreads();
-  float *mw = c.L.maw + hi.maw_off + (size_t)seq * hi.nbmax;
-  const float r = c.dm.maw_decay, omr = 1.0f - r, inv_g = 1.0f / (float)G;
-  const int PPB = g.S / kPage;
-  for (int x = tid; x < g.n_dt; x += 256) {
-    const int blk = dense_block(g, x);
-    if (is_candidate(g, blk)) continue;  // a token outside D: frozen
-    float a = 0.0f;
-    for (int pp = 0; pp < PPB; ++pp) {
-      const int t = dense_pos(dl, blk * PPB + pp);
-      if (t >= 0) a += sm.pm[t];
-    }
-    mw[blk] = __fadd_rn(__fmul_rn(r, mw[blk]), __fmul_rn(omr, a * inv_g));
   }
 }
 
@@ -2298,7 +2362,7 @@ __global__ __launch_bounds__(256) void k_select(Ctx c, SeqBatch b, int tiles_x,
   const HeadInfo hi = c.heads[h];
   const int seq = b.seq[i], N = b.len[i];
   const int n_blk = div_S(N + hi.S - 1, hi.S);
-  const int n_tiles = max(1, cdiv(n_blk, kScoreTile));
+  const int n_tiles = max(1, cdiv(scored_blocks(N, hi.S, c.dm), kScoreTile));
   if (tile >= n_tiles) return;
   if (selects_nothing(hi, N, c.dm)) {  // no scoring: the count is 0
     if (tile == 0 && threadIdx.x == 0) st_dev(&blk_cnt[(size_t)i * c.dm.Hkv + h], 0);
@@ -2306,11 +2370,11 @@ __global__ __launch_bounds__(256) void k_select(Ctx c, SeqBatch b, int tiles_x,
   }
   UG g;
   score_tile<D, G>(c, i, seq, h, hi, N, n_blk, tile, q, smem_topk, false, g);
-  uint32_t *ctr = &c.sc.arrive[((size_t)seq * c.dm.Hkv + h) * 2];
+  uint32_t *ctr = &c.sc.arrive[((size_t)seq * c.dm.Hkv + h) * 4];
   if (!arrive_last(ctr, (unsigned)n_tiles, &smem_topk.last)) return;
   uint32_t *lrows = reinterpret_cast<uint32_t *>(smem_raw + sizeof(TopkSmem));
   unsigned long long *dmask = reinterpret_cast<unsigned long long *>(lrows + lrows_words);
-  if (wide_unit(g.n_blk))
+  if (wide_unit(g.n_sc))
     topk_wide<D, G>(c, i, seq, h, hi, g, q, blk_idx, blk_cnt, k_cap, smem_topk, dmask,
                     reinterpret_cast<int32_t *>(lrows), lrows_words);
   else
@@ -2343,7 +2407,7 @@ __global__ __launch_bounds__(256, 2) void k_attend(Ctx c, SeqBatch b, int P,
   si.cnt = min(min(max(blk_cnt[(size_t)i * c.dm.Hkv + h], 0), k_cap), hi.kcap);
   if (part == 0) empty_slots<D, G>(c, i, h, PU, p_cap, o_part, lse_part);
   attend_part<D, G>(c, i, seq, h, g, part, PU, q, si, o_part, lse_part, p_cap, sm, nullptr,
-                    &s_cnt, NewTok());
+                    &s_cnt, NewTok(), hi);
 }
 
 // One decode step in one launch.  Workgroups by index: score tiles (the last
@@ -2385,19 +2449,35 @@ __global__ __launch_bounds__(256, 2) void k_step(Ctx c, SeqBatch b, int tiles_x,
   const HeadInfo hi = c.heads[h];
   const int seq = b.seq[i], N = b.len[i];
   const size_t unit = (size_t)seq * c.dm.Hkv + h;
+  // the step's appended token of this unit, if its append runs in this
+  // launch (then N >= 1)
+  auto new_tok = [&](int n) {
+    NewTok t;
+    if (k_new) {
+      t.k = k_new + ((size_t)i * c.dm.Hkv + h) * D;
+      t.v = v_new + ((size_t)i * c.dm.Hkv + h) * D;
+      t.slot = (n - 1) & (kPage - 1);
+      t.pg = c.L.pt[(size_t)seq * c.dm.pages_per_seq + ((n - 1) >> 4)];
+    }
+    return t;
+  };
   if (score) {
     const int n_blk = div_S(N + hi.S - 1, hi.S);
-    const int n_tiles = max(1, cdiv(n_blk, kScoreTile));
+    const int n_tiles = max(1, cdiv(scored_blocks(N, hi.S, c.dm), kScoreTile));
     if (idx >= n_tiles || selects_nothing(hi, N, c.dm)) return;  // (the parts cover k = 0)
     // the score tiles, the top-k and the fusion are on every unit's critical
     // path: their waves get issue priority over the attention parts'
     __builtin_amdgcn_s_setprio(2);
+    SD_TL(0);
     // without MAW flags each tile also lists its candidates for the fast top-k
     UG g;
     const bool fast = score_tile<D, G>(c, i, seq, h, hi, N, n_blk, idx, q, smem_topk,
                                        c.dm.maw_beta <= 0.0f && n_tiles <= kFastTiles, g);
-    uint32_t *ctr = &c.sc.arrive[unit * 2];
-    if (!arrive_last(ctr, (unsigned)n_tiles, &s_flag)) return;
+    SD_TL(2);  // tile list published
+    uint32_t *ctr = &c.sc.arrive[unit * 4];
+    const bool last_tile = arrive_last(ctr, (unsigned)n_tiles, &s_flag);
+    SD_TL(3);  // arrived
+    if (!last_tile) return;
     __builtin_amdgcn_s_setprio(3);
     uint32_t *lrows = reinterpret_cast<uint32_t *>(smem_raw + sizeof(TopkSmem));
     unsigned long long *tagd = c.sc.seltag + unit * c.dm.kcap;
@@ -2406,13 +2486,14 @@ __global__ __launch_bounds__(256, 2) void k_step(Ctx c, SeqBatch b, int tiles_x,
                                                    smem_topk, tagd, &c.sc.rtag[unit], epoch);
     if (!fast_done) {
       unsigned long long *dmask = reinterpret_cast<unsigned long long *>(lrows + lrows_words);
-      if (wide_unit(g.n_blk))
+      if (wide_unit(g.n_sc))
         topk_wide<D, G>(c, i, seq, h, hi, g, q, blk_idx, blk_cnt, k_cap, smem_topk, dmask,
                         reinterpret_cast<int32_t *>(lrows), lrows_words, tagd, epoch);
       else
         topk_unit<D, G>(c, i, seq, h, hi, g, q, blk_idx, blk_cnt, k_cap, smem_topk, lrows,
                         lrows_words, dmask, tagd, epoch);
     }
+    SD_TL(4);  // top-k done
     if (threadIdx.x == 0) {
       // the entries carry their own tags, so the count need not wait for them
       st_dev(ctr, 0u);
@@ -2420,11 +2501,24 @@ __global__ __launch_bounds__(256, 2) void k_step(Ctx c, SeqBatch b, int tiles_x,
         st_dev(&c.sc.rtag[unit], ((unsigned long long)epoch << 32) |
                                      (uint32_t)min(min(g.kk, k_cap), hi.kcap));
     }
+    // the unit's MAW update (and the folded append's writes) once every part
+    // has written its dense pages' log-masses: the last of the parts and this
+    // top-k to arrive does it; here that is usually this workgroup, which has
+    // nothing else left to do
+    uint32_t *dctr = &c.sc.arrive[unit * 4 + 2];
+    if (arrive_last(dctr, (unsigned)unit_parts(g, P) + 1u, &s_flag)) {
+      float *pm = reinterpret_cast<float *>(smem_raw);
+      dense_maw<D, G>(c, seq, h, hi, g, new_tok(N), pm, pm + kFuseDenseLds,
+                      pm + kFuseDenseLds + 4 * G);
+      if (threadIdx.x == 0) st_dev(dctr, 0u);
+      SD_TL(5);  // MAW updated here
+    }
     return;
   }
   const UG g = unit_geom(N, hi, c.dm);
   const int PU = unit_parts(g, P);
   if (idx >= PU) return;
+  SD_TL(0);
   // attention part idx of the unit; the sequence's page table is copied to LDS
   // (one batch of loads) for the selected pages
   const int32_t *ptl = nullptr;
@@ -2456,21 +2550,16 @@ __global__ __launch_bounds__(256, 2) void k_step(Ctx c, SeqBatch b, int tiles_x,
   si.rtag = no_sel ? nullptr : &c.sc.rtag[unit];
   si.cnt = 0;
   si.epoch = epoch;
-  // the step's appended token, if its append runs in this launch (N >= 1)
-  NewTok tok;
-  if (k_new) {
-    tok.k = k_new + ((size_t)i * c.dm.Hkv + h) * D;
-    tok.v = v_new + ((size_t)i * c.dm.Hkv + h) * D;
-    tok.slot = (N - 1) & (kPage - 1);
-    tok.pg = c.L.pt[(size_t)seq * c.dm.pages_per_seq + ((N - 1) >> 4)];
-  }
   attend_part<D, G>(c, i, seq, h, g, idx, PU, q, si, o_part, lse_part, p_cap, smem_att, ptl,
-                    &s_cnt, tok);
-  uint32_t *fctr = &c.sc.arrive[unit * 2 + 1];
-  if (!arrive_last(fctr, (unsigned)PU, &s_flag)) return;
+                    &s_cnt, new_tok(N), hi, &c.sc.arrive[unit * 4 + 2],
+                    (unsigned)PU + (no_sel ? 0u : 1u), &s_flag);
+  uint32_t *fctr = &c.sc.arrive[unit * 4 + 1];
+  const bool last_part = arrive_last(fctr, (unsigned)PU, &s_flag);
+  SD_TL(4);  // partial written, arrived
+  if (!last_part) return;
   __builtin_amdgcn_s_setprio(3);
-  fuse_unit<D, G>(c, i, seq, h, hi, g, true, PU, o_part, lse_part, p_cap, o, lse, smem_fuse,
-                  tok);
+  fuse_unit<D, G>(c, i, h, PU, o_part, lse_part, p_cap, o, lse, smem_fuse);
+  SD_TL(5);  // fused
   if (threadIdx.x == 0) st_dev(fctr, 0u);
 }
 
@@ -2487,11 +2576,10 @@ __global__ __launch_bounds__(256) void k_fuse(Ctx c, SeqBatch b, int with_maw, i
   const HeadInfo hi = c.heads[h];
   if (with_maw) {
     const UG g = unit_geom(b.len[i], hi, c.dm);
-    fuse_unit<D, G>(c, i, b.seq[i], h, hi, g, true, unit_parts(g, P), o_part, lse_part, p_cap, o,
-                    lse, sm);
+    fuse_unit<D, G>(c, i, h, unit_parts(g, P), o_part, lse_part, p_cap, o, lse, sm);
+    dense_maw<D, G>(c, b.seq[i], h, hi, g, NewTok(), sm.pm, sm.dm, sm.dz);
   } else {
-    UG g{};
-    fuse_unit<D, G>(c, i, 0, h, hi, g, false, p_cap, o_part, lse_part, p_cap, o, lse, sm);
+    fuse_unit<D, G>(c, i, h, p_cap, o_part, lse_part, p_cap, o, lse, sm);
   }
 }
 
@@ -2562,7 +2650,7 @@ static int topk_lds(int max_blocks, size_t *bytes) {
 hipError_t launch_select(const Ctx &c, const SeqBatch &b, int max_blocks, const uint16_t *q,
                          int32_t *blk_idx, int32_t *blk_cnt, int32_t k_cap, hipStream_t st) {
   if (b.n <= 0) return hipSuccess;
-  const int tiles_x = max(1, (max_blocks + kScoreTile - 1) / kScoreTile);
+  const int tiles_x = max(1, (b.max_scored + kScoreTile - 1) / kScoreTile);
   const int grid = tiles_x * c.dm.Hkv * b.n;
   size_t topk_bytes;
   const int lrows_words = topk_lds(max_blocks, &topk_bytes);
@@ -2609,7 +2697,7 @@ hipError_t launch_step(const Ctx &c, const SeqBatch &b, int max_blocks, int P, c
                        hipStream_t st) {
   if (b.n <= 0) return hipSuccess;
   if (P < 1 || P > p_cap) return hipErrorInvalidValue;
-  const int tiles_x = max(1, (max_blocks + kScoreTile - 1) / kScoreTile);
+  const int tiles_x = max(1, (b.max_scored + kScoreTile - 1) / kScoreTile);
   const dim3 grid(c.dm.Hkv, b.n, tiles_x + P);
   size_t topk_bytes;
   const int lrows_words = topk_lds(max_blocks, &topk_bytes);
@@ -2652,3 +2740,24 @@ hipError_t launch_fill_f32(float *p, size_t n, float v, hipStream_t st) {
 }
 
 }  // namespace sd
+
+#ifdef SD_TIMELINE
+// Copy of the step timeline (bytes <= kTlMaxWG * kTlSlots * 8) to host memory,
+// then zeroed.  Declared in include/sparse_decode_timeline.h.
+extern "C" int32_t sd_timeline_read(void *host_dst, size_t bytes, int32_t *slots,
+                                    int32_t *max_wg) {
+  if (slots) *slots = sd::kTlSlots;
+  if (max_wg) *max_wg = sd::kTlMaxWG;
+  const size_t all = sizeof(unsigned long long) * sd::kTlSlots * sd::kTlMaxWG;
+  if (!host_dst || bytes > all) return SD_EINVAL;
+  if (hipDeviceSynchronize() != hipSuccess ||
+      hipMemcpyFromSymbol(host_dst, HIP_SYMBOL(sd::sd_tl_buf), bytes) != hipSuccess)
+    return SD_EHIP;
+  static unsigned long long zeros[sd::kTlSlots * 1024];
+  for (size_t off = 0; off < all; off += sizeof zeros)
+    if (hipMemcpyToSymbol(HIP_SYMBOL(sd::sd_tl_buf), zeros, std::min(sizeof zeros, all - off), off) !=
+        hipSuccess)
+      return SD_EHIP;
+  return SD_OK;
+}
+#endif

@@ -177,13 +177,22 @@ sd_status check_seqs(sd_ctx *c, int32_t layer, int32_t n_seqs,
 void fill_batch(const sd_ctx *c, int layer, const int32_t *seq_ids, int base,
                 int n, SeqBatch *b, int *max_blocks) {
   b->n = n;
-  int mb = 0;
+  int mb = 0, ms = 0;
+  const int W = c->cfg.recent_window;
   for (int i = 0; i < n; ++i) {
     b->seq[i] = seq_ids[base + i];
     b->len[i] = c->layers[layer].len[seq_ids[base + i]];
-    for (int h = 0; h < c->Hkv; ++h)
-      mb = std::max<int>(mb, (int)cdiv(b->len[i], c->S[h]));
+    for (int h = 0; h < c->Hkv; ++h) {
+      const int nb = (int)cdiv(b->len[i], c->S[h]);
+      mb = std::max(mb, nb);
+      // blocks from ceil((N - W) / S) on lie wholly in the recent window
+      const int sc = (W > 0 && b->len[i] > 0)
+                         ? std::min<int>(nb, (int)cdiv(std::max(0, b->len[i] - W), c->S[h]))
+                         : nb;
+      ms = std::max(ms, sc);
+    }
   }
+  b->max_scored = ms;
   if (max_blocks) *max_blocks = mb;
 }
 
@@ -341,8 +350,8 @@ sd_status sparse_decode_init(const sd_config *cfg, sd_ctx **out) {
   if ((s = dev_alloc(c, &c->sc.unit_acc, (size_t)max_seqs * c->Hkv * 2)) != SD_OK) return s;
   SD_HIP(c, hipMemset(c->sc.unit_acc, 0, sizeof(uint32_t) * max_seqs * c->Hkv * 2));
   if ((s = dev_alloc(c, &c->sc.lm_pg, (size_t)max_seqs * c->Hq * c->dims.lm_cap)) != SD_OK) return s;
-  if ((s = dev_alloc(c, &c->sc.arrive, (size_t)max_seqs * c->Hkv * 2)) != SD_OK) return s;
-  SD_HIP(c, hipMemset(c->sc.arrive, 0, sizeof(uint32_t) * max_seqs * c->Hkv * 2));
+  if ((s = dev_alloc(c, &c->sc.arrive, (size_t)max_seqs * c->Hkv * 4)) != SD_OK) return s;
+  SD_HIP(c, hipMemset(c->sc.arrive, 0, sizeof(uint32_t) * max_seqs * c->Hkv * 4));
   if ((s = dev_alloc(c, &c->sc.cand, per_unit)) != SD_OK) return s;
   if ((s = dev_alloc(c, &c->sc.rtag, (size_t)max_seqs * c->Hkv)) != SD_OK) return s;
   if ((s = dev_alloc(c, &c->sc.seltag, (size_t)max_seqs * c->Hkv * c->k_cap)) != SD_OK) return s;
@@ -364,7 +373,7 @@ sd_status sparse_decode_init(const sd_config *cfg, sd_ctx **out) {
       return at;
     };
     StaticLayout &sl = c->slayout;
-    sl.arrive = take(sizeof(uint32_t) * units * 2);
+    sl.arrive = take(sizeof(uint32_t) * units * 4);
     sl.unit_acc = take(sizeof(uint32_t) * units * 2);
     sl.rtag = take(sizeof(unsigned long long) * units);
     sl.seltag = take(sizeof(unsigned long long) * units * c->k_cap);
@@ -578,7 +587,7 @@ int parts_of(sd_ctx *c, int layer, const SeqBatch &b, int max_blocks) {
     }
   }
   const int units = c->Hkv * b.n;
-  const int tiles = std::max(1, (max_blocks + kScoreTile - 1) / kScoreTile);
+  const int tiles = std::max(1, (b.max_scored + kScoreTile - 1) / kScoreTile);
   // fewer parts, so that the whole step stays resident, pays when it costs
   // at most half of them; otherwise (long units, many tiles) the parts that do
   // not fit start as score tiles finish
@@ -702,6 +711,7 @@ sd_status fuse_lse(sd_ctx *c, int32_t layer, int32_t n_seqs,
       fill_batch(c, layer, seq_ids, base, n, &b, nullptr);
     } else {
       b.n = n;
+      b.max_scored = 0;
       for (int i = 0; i < n; ++i) b.seq[i] = b.len[i] = 0;
     }
     const int P = with_maw ? c->pend_parts[base / kLaunchSeqs] : p_cap;
