@@ -105,3 +105,15 @@ def test_read_probe_rejects_bad_arguments_before_any_launch():
     assert L.sd_read_probe(dummy, 24, dummy, 1, None) == -1
     assert L.sd_read_probe(ctypes.c_void_p(8), 16, dummy, 1, None) == -1
     assert L.sd_read_probe(dummy, 16, dummy, 0, None) == -1
+
+
+def test_timeline_export_only_in_the_measurement_build():
+    """sd_timeline_read (include/sparse_decode_timeline.h) belongs to the
+    SD_TIMELINE measurement build only; the product library does not export
+    it."""
+    L = bsts.load()
+    assert not hasattr(L, "sd_timeline_read")
+    if not os.path.exists(_abi.LIB_TIMELINE_PATH):
+        pytest.skip("measurement build not present")
+    T = ctypes.CDLL(_abi.LIB_TIMELINE_PATH)
+    assert hasattr(T, "sd_timeline_read")
