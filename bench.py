@@ -402,9 +402,10 @@ def timeline(args, w, eng, step, s0, L):
     n_now = eng.seq_len(s0 % L, 0) + 1
     tiles = -(-max(-(-max(0, n_now - w.window) // S) for S in w.block_size) // 256)
     n_wg = w.Hkv * w.B * 64
-    names = {"score": ["start", "keys written", "tile list published", "arrived",
-                       "top-k done", "MAW updated (by the top-k)"],
-             "part": ["start", "dense pages done (wave 0)", "selection count seen",
+    names = {"score": ["first instruction", "keys written", "tile list published", "arrived",
+                       "top-k done", "MAW updated (by the top-k)",
+                       "fast top-k gave up (full top-k runs)", "band re-score started"],
+             "part": ["first instruction", "dense pages done (wave 0)", "selection count seen",
                       "selected pages done (wave 0)", "partial written, arrived",
                       "fusion done", "(unused)", "MAW updated (by a part)"]}
     acc = {r: {k: [] for k in range(len(v))} for r, v in names.items()}
@@ -413,6 +414,8 @@ def timeline(args, w, eng, step, s0, L):
              "fusion (last part: arrived -> done)": ("part", 4, 5),
              "MAW by the top-k (top-k done -> MAW done)": ("score", 4, 5),
              "MAW by a part (dense done -> MAW done)": ("part", 1, 7),
+             "top-k with the band re-score (arrived -> done)": ("score", 7, 4),
+             "top-k after the fast one gave up (gave up -> done)": ("score", 6, 4),
              "tile: keys -> list published": ("score", 1, 2),
              "tile: list published -> arrived": ("score", 2, 3),
              "part: selected pages done -> partial written, arrived": ("part", 3, 4)}

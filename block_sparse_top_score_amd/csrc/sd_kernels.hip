@@ -1526,7 +1526,10 @@ __device__ __attribute__((always_inline)) bool topk_fast(const Ctx &c, int i, in
     }
   }
   __syncthreads();
-  if (!sm.ok) return false;
+  if (!sm.ok) {
+    SD_TL(6);  // the fast top-k gave up: the full top-k runs
+    return false;
+  }
   const int n_unc = sm.nlist, kr2 = kk - sm.nin;
   if (kr2 > 0 && kr2 == n_unc) {  // every band block is taken: no exact keys needed
     if (wv == 0 && lane < n_unc) {
@@ -1534,6 +1537,7 @@ __device__ __attribute__((always_inline)) bool topk_fast(const Ctx &c, int i, in
       atomicOr(&sm.bm[blk >> 6], 1ull << (blk & 63));
     }
   } else if (kr2 > 0) {
+    SD_TL(7);  // the band's exact re-score starts
     // exact keys of the band, one lane quad per (block, head), in passes of 64
     for (int p0 = 0; p0 < n_unc * G; p0 += 64) {
       const int pair = p0 + (tid >> 2);
@@ -2437,6 +2441,7 @@ __global__ __launch_bounds__(256, 2) void k_step(Ctx c, SeqBatch b, int tiles_x,
   TopkSmem &smem_topk = *reinterpret_cast<TopkSmem *>(smem_raw);
   AttLds<D, G> &smem_att = *reinterpret_cast<AttLds<D, G> *>(smem_raw);
   FuseSmem<G> &smem_fuse = *reinterpret_cast<FuseSmem<G> *>(smem_raw);
+  SD_TL(0);  // first instruction
   // grid (KV head, sequence, role index): workgroups are dispatched with
   // blockIdx.x fastest, so the flat order is role-major.  Score tiles come
   // first, tile-major: consecutive workgroups (spread over the CUs first) are
@@ -2468,7 +2473,6 @@ __global__ __launch_bounds__(256, 2) void k_step(Ctx c, SeqBatch b, int tiles_x,
     // the score tiles, the top-k and the fusion are on every unit's critical
     // path: their waves get issue priority over the attention parts'
     __builtin_amdgcn_s_setprio(2);
-    SD_TL(0);
     // without MAW flags each tile also lists its candidates for the fast top-k
     UG g;
     const bool fast = score_tile<D, G>(c, i, seq, h, hi, N, n_blk, idx, q, smem_topk,
@@ -2518,7 +2522,6 @@ __global__ __launch_bounds__(256, 2) void k_step(Ctx c, SeqBatch b, int tiles_x,
   const UG g = unit_geom(N, hi, c.dm);
   const int PU = unit_parts(g, P);
   if (idx >= PU) return;
-  SD_TL(0);
   // attention part idx of the unit; the sequence's page table is copied to LDS
   // (one batch of loads) for the selected pages
   const int32_t *ptl = nullptr;
