@@ -139,6 +139,9 @@ def traffic_summary(fetch_dir, write_dir, cal_fetch_dir, cal_write_dir):
            "fetch_scale": f_scale, "write_scale": w_scale,
            "traffic_bytes_per_launch": f_kib * 1024.0 * f_scale + w_kib * 1024.0 * w_scale,
            "source_sha256": sources_sha256()}
+    with open(TRAFFIC_FILE, "w") as fh:
+        json.dump(out, fh)
+        fh.write("\n")
     print(json.dumps(out), flush=True)
     return out
 
