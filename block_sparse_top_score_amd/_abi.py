@@ -19,7 +19,7 @@ LIB_PATH = os.path.join(_HERE, "libsparse_decode.so")
 LIB_TIMELINE_PATH = os.path.join(_HERE, "libsparse_decode_timeline.so")
 
 SD_OK, SD_EINVAL, SD_ENOMEM, SD_EHIP, SD_EUNSUPPORTED, SD_ESTATE = 0, -1, -2, -3, -4, -5
-SD_DEBUG_PAGE_TABLE, SD_DEBUG_SUMMARY, SD_DEBUG_MAW, SD_DEBUG_K, SD_DEBUG_V = range(5)
+SD_DEBUG_PAGE_TABLE, SD_DEBUG_SUMMARY, SD_DEBUG_MAW, SD_DEBUG_K, SD_DEBUG_V, SD_DEBUG_SCORES = range(6)
 
 # every symbol declared in include/sparse_decode.h
 EXPORTS = [
@@ -272,7 +272,8 @@ class SparseDecode:
         """Host numpy copy of a debug export (see sd_debug_copy)."""
         nb = ctypes.c_size_t()
         self._check(self.L.sd_debug_bytes(self.ctx, what, layer, seq, ctypes.byref(nb)))
-        dt = {SD_DEBUG_PAGE_TABLE: np.int32, SD_DEBUG_MAW: np.float32}.get(what, np.uint16)
+        dt = {SD_DEBUG_PAGE_TABLE: np.int32, SD_DEBUG_MAW: np.float32,
+              SD_DEBUG_SCORES: np.float32}.get(what, np.uint16)
         out = np.zeros(nb.value // np.dtype(dt).itemsize, dt)
         self._check(self.L.sd_debug_copy(self.ctx, what, layer, seq,
                                          out.ctypes.data_as(ctypes.c_void_p), nb.value))

@@ -21,6 +21,21 @@ constexpr int kFastTiles = 8;        // score tiles per unit of the fast top-k, 
 constexpr int kPtLds = 4096;         // page-table entries a selected chunk copies to LDS, at most
 constexpr int kFuseSlots = 256;      // partial slots per query head, at most
 constexpr int kFuseDenseLds = 2048;  // dense pages (sinks + window) per unit, at most
+constexpr int kWideM = 40;           // blocks per thread of the four-wave top-k: units up to 10240 blocks
+
+// Units the four-wave top-k ranks (more blocks than the one-wave top-k keeps
+// in registers).
+__host__ __device__ inline bool wide_unit(int n_blk) {
+  return n_blk > kTopkRegRows * 64 && n_blk <= 256 * kWideM;
+}
+// Slot of block blk's key in its unit's key array: the block index, except
+// in units the four-wave top-k ranks, where thread t's blocks sit at t,
+// t + 256, ..., so that its loads are coalesced.
+__host__ __device__ inline int key_slot(int blk, int n_blk) {
+  if (!wide_unit(n_blk)) return blk;
+  const int m = (n_blk + 255) / 256, t = blk / m;
+  return (blk - t * m) * 256 + t;
+}
 
 // Per-KV-head constants, resident in device memory for the context's life
 // (read with uniform addresses, so they come through the scalar cache).
@@ -81,8 +96,9 @@ struct Scratch {
   uint32_t *keys;    // [max_seqs][Hkv][key_stride] top-k words past LDS (long units)
   int32_t *ulist;    // [max_seqs][Hkv][key_stride] uncertain blocks past LDS
   uint32_t *ukeys;   // [max_seqs][Hkv][key_stride] their exact keys
-  uint32_t *unit_acc;  // [max_seqs][Hkv][2] error bound (float bits, max) and
-                       // flagged candidates (count) of the score tiles; 0 between steps
+  uint32_t *unit_acc;  // [max_seqs][Hkv][4] error bound (float bits, max) and
+                       // flagged candidates (count) of the score tiles, 0 between
+                       // steps; the bound the unit's last selection used; spare
   float *lm_pg;      // [max_seqs][Hq][lm_cap] log softmax mass of each attended page
   uint32_t *arrive;  // [max_seqs][Hkv][4] last-arriver counters (kept at 0): score
                      // tiles, attention parts, dense pages done (+ the top-k), spare

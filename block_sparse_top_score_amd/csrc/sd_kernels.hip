@@ -196,19 +196,7 @@ __device__ __forceinline__ uint32_t order_key(float u) {
 constexpr int kTileList = 64;  // blocks a score tile lists for the fast top-k, at most
 // The four-wave top-k ranks units of (kTopkRegRows * 64, 256 * kWideM]
 // blocks; its thread t holds blocks [t m, t m + m), m = ceil(n / 256).
-constexpr int kWideM = 40;  // blocks per thread: units up to 10240 blocks
 static_assert(kWideM <= 64, "a thread's blocks span at most two mask words");
-__device__ __forceinline__ bool wide_unit(int n_blk) {
-  return n_blk > kTopkRegRows * 64 && n_blk <= 256 * kWideM;
-}
-// Slot of block blk's key in its unit's key array: the block index, except
-// in units the four-wave top-k ranks, where thread t's blocks sit at t,
-// t + 256, ..., so that its loads are coalesced.
-__device__ __forceinline__ int key_slot(int blk, int n_blk) {
-  if (!wide_unit(n_blk)) return blk;
-  const int m = cdiv(n_blk, 256), t = blk / m;
-  return (blk - t * m) * 256 + t;
-}
 struct TopkSmem {
   int32_t ulist[kTopkUnc];  // uncertain blocks of the top-k, in index order
   uint32_t ukey[kTopkUnc];  // their exact keys
@@ -712,7 +700,7 @@ __device__ __attribute__((always_inline)) bool score_tile(const Ctx &c, int i, i
   }
   __syncthreads();
   if (threadIdx.x == 0) {
-    uint32_t *acc = &c.sc.unit_acc[2 * ((size_t)seq * c.dm.Hkv + h)];
+    uint32_t *acc = &c.sc.unit_acc[4 * ((size_t)seq * c.dm.Hkv + h)];
     __hip_atomic_fetch_max(acc, max(max(red[0], red[1]), max(red[2], red[3])), __ATOMIC_RELAXED,
                            __HIP_MEMORY_SCOPE_AGENT);
     const uint32_t f = red[4] + red[5] + red[6] + red[7];
@@ -857,8 +845,8 @@ __device__ __attribute__((always_inline)) void topk_unit(const Ctx &c, int i, in
 
   // 0. every load in flight together: the score tiles' accumulators (error
   // bound, flagged candidates), the register rows, the group's query
-  const uint32_t eps_bits = ld_dev(&c.sc.unit_acc[2 * unit]);
-  const uint32_t f_raw = ld_dev(&c.sc.unit_acc[2 * unit + 1]);
+  const uint32_t eps_bits = ld_dev(&c.sc.unit_acc[4 * unit]);
+  const uint32_t f_raw = ld_dev(&c.sc.unit_acc[4 * unit + 1]);
   const int jl = max(n - 1, 0);
   unsigned long long kv[kTopkRegRows];
 #pragma unroll
@@ -1119,8 +1107,9 @@ __device__ __attribute__((always_inline)) void topk_unit(const Ctx &c, int i, in
   for (int r = kTopkRegRows; r < rows; ++r) emit_row(r, mem_ld(r * 64 + lane), dmask[r]);
   if (lane == 0) {
     st_dev(&blk_cnt[(size_t)i * c.dm.Hkv + h], kk);
-    st_dev(&c.sc.unit_acc[2 * unit], 0u);  // cleared for the next step
-    st_dev(&c.sc.unit_acc[2 * unit + 1], 0u);
+    st_dev(&c.sc.unit_acc[4 * unit], 0u);  // cleared for the next step
+    st_dev(&c.sc.unit_acc[4 * unit + 1], 0u);
+    st_dev(&c.sc.unit_acc[4 * unit + 2], eps_bits);  // the bound this selection used
   }
 }
 
@@ -1188,8 +1177,8 @@ __device__ __attribute__((always_inline)) void topk_wide(const Ctx &c, int i, in
   int slot = 0;
 
   // 0. one batch of loads: the accumulators, the thread's keys, the query
-  const uint32_t eps_bits = ld_dev(&c.sc.unit_acc[2 * unit]);
-  const uint32_t f_raw = ld_dev(&c.sc.unit_acc[2 * unit + 1]);
+  const uint32_t eps_bits = ld_dev(&c.sc.unit_acc[4 * unit]);
+  const uint32_t f_raw = ld_dev(&c.sc.unit_acc[4 * unit + 1]);
   unsigned long long kv[kWideM];
 #pragma unroll
   for (int x = 0; x < kWideM; ++x) kv[x] = (x < m && j0 + x < n) ? ld_dev(&gkf[x * 256 + tid]) : 0ull;
@@ -1418,8 +1407,9 @@ __device__ __attribute__((always_inline)) void topk_wide(const Ctx &c, int i, in
   }
   if (tid == 0) {
     st_dev(&blk_cnt[(size_t)i * c.dm.Hkv + h], kk);
-    st_dev(&c.sc.unit_acc[2 * unit], 0u);  // cleared for the next step
-    st_dev(&c.sc.unit_acc[2 * unit + 1], 0u);
+    st_dev(&c.sc.unit_acc[4 * unit], 0u);  // cleared for the next step
+    st_dev(&c.sc.unit_acc[4 * unit + 1], 0u);
+    st_dev(&c.sc.unit_acc[4 * unit + 2], eps_bits);  // the bound this selection used
   }
 }
 
@@ -1465,7 +1455,7 @@ __device__ __attribute__((always_inline)) bool topk_fast(const Ctx &c, int i, in
 #pragma unroll
   for (int r = 0; r < kFastTiles; ++r)
     e[r] = (wv == 0 && r < n_tiles) ? ld_dev(&cl[(size_t)r * kTileList + lane]) : 0ull;
-  const uint32_t eps_bits = ld_dev(&c.sc.unit_acc[2 * unit]);
+  const uint32_t eps_bits = ld_dev(&c.sc.unit_acc[4 * unit]);
   const uint16_t *qg = q + ((size_t)i * c.dm.Hq + (size_t)h * G) * D;
   constexpr int QT = (G * D + 255) / 256;
   uint16_t qv[QT];
@@ -1596,8 +1586,9 @@ __device__ __attribute__((always_inline)) bool topk_fast(const Ctx &c, int i, in
     }
     if (lane == 0) {
       st_dev(&blk_cnt[(size_t)i * c.dm.Hkv + h], kk);
-      st_dev(&c.sc.unit_acc[2 * unit], 0u);  // cleared for the next step
-      st_dev(&c.sc.unit_acc[2 * unit + 1], 0u);
+      st_dev(&c.sc.unit_acc[4 * unit], 0u);  // cleared for the next step
+      st_dev(&c.sc.unit_acc[4 * unit + 1], 0u);
+      st_dev(&c.sc.unit_acc[4 * unit + 2], eps_bits);  // the bound this selection used
     }
   }
   return true;

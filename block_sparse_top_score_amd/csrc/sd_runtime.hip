@@ -10,6 +10,7 @@
 #include <cstdint>
 #include <cstdio>
 #include <cstring>
+#include <limits>
 #include <mutex>
 #include <new>
 #include <vector>
@@ -347,8 +348,8 @@ sd_status sparse_decode_init(const sd_config *cfg, sd_ctx **out) {
   if ((s = dev_alloc(c, &c->sc.keyflag, per_unit)) != SD_OK) return s;
   if ((s = dev_alloc(c, &c->sc.ulist, per_unit)) != SD_OK) return s;
   if ((s = dev_alloc(c, &c->sc.ukeys, per_unit)) != SD_OK) return s;
-  if ((s = dev_alloc(c, &c->sc.unit_acc, (size_t)max_seqs * c->Hkv * 2)) != SD_OK) return s;
-  SD_HIP(c, hipMemset(c->sc.unit_acc, 0, sizeof(uint32_t) * max_seqs * c->Hkv * 2));
+  if ((s = dev_alloc(c, &c->sc.unit_acc, (size_t)max_seqs * c->Hkv * 4)) != SD_OK) return s;
+  SD_HIP(c, hipMemset(c->sc.unit_acc, 0, sizeof(uint32_t) * max_seqs * c->Hkv * 4));
   if ((s = dev_alloc(c, &c->sc.lm_pg, (size_t)max_seqs * c->Hq * c->dims.lm_cap)) != SD_OK) return s;
   if ((s = dev_alloc(c, &c->sc.arrive, (size_t)max_seqs * c->Hkv * 4)) != SD_OK) return s;
   SD_HIP(c, hipMemset(c->sc.arrive, 0, sizeof(uint32_t) * max_seqs * c->Hkv * 4));
@@ -374,7 +375,7 @@ sd_status sparse_decode_init(const sd_config *cfg, sd_ctx **out) {
     };
     StaticLayout &sl = c->slayout;
     sl.arrive = take(sizeof(uint32_t) * units * 4);
-    sl.unit_acc = take(sizeof(uint32_t) * units * 2);
+    sl.unit_acc = take(sizeof(uint32_t) * units * 4);
     sl.rtag = take(sizeof(unsigned long long) * units);
     sl.seltag = take(sizeof(unsigned long long) * units * c->k_cap);
     sl.clear_bytes = off;
@@ -886,6 +887,9 @@ sd_status sd_debug_bytes(const sd_ctx *c, int32_t what, int32_t layer,
       break;
     case SD_DEBUG_K:
     case SD_DEBUG_V: b = sizeof(uint16_t) * len * c->Hkv * c->D; break;
+    case SD_DEBUG_SCORES:
+      for (int h = 0; h < c->Hkv; ++h) b += sizeof(float) * (1 + cdiv(len, c->S[h]));
+      break;
     default: return SD_EINVAL;
   }
   *bytes = b;
@@ -931,6 +935,39 @@ sd_status sd_debug_copy(sd_ctx *c, int32_t what, int32_t layer, int32_t seq,
         SD_HIP(c, hipMemcpy(dst, L.dev.maw + hi.maw_off + (size_t)seq * hi.nbmax,
                             sizeof(float) * nb, hipMemcpyDeviceToHost));
       dst += nb;
+    }
+  } else if (what == SD_DEBUG_SCORES) {
+    // the unit's keys as its score tiles wrote them (order key of the fp32
+    // group score; 0 for a block that is not a candidate) and the bound its
+    // top-k kept
+    float *dst = static_cast<float *>(host_dst);
+    const int64_t ks = c->dims.key_stride;
+    std::vector<unsigned long long> kf((size_t)ks);
+    const int64_t W = c->dims.window, ns = c->dims.n_sink;
+    for (int h = 0; h < c->Hkv; ++h) {
+      const HeadInfo &hi = c->heads[h];
+      const int64_t nb = cdiv(len, hi.S);
+      const size_t unit = (size_t)seq * c->Hkv + h;
+      const bool none = hi.ppm == 0 || std::min(ns, len) >= std::max<int64_t>(0, len - W);
+      const int64_t n_sc = (W > 0 && len > 0) ? std::min(nb, cdiv(std::max<int64_t>(0, len - W), hi.S))
+                                              : nb;
+      const float nan = std::numeric_limits<float>::quiet_NaN();
+      for (int64_t b = 0; b <= nb; ++b) dst[b] = nan;
+      if (!none && nb) {
+        uint32_t eb = 0;
+        SD_HIP(c, hipMemcpy(&eb, c->sc.unit_acc + 4 * unit + 2, sizeof(uint32_t),
+                            hipMemcpyDeviceToHost));
+        memcpy(&dst[0], &eb, sizeof(float));
+        SD_HIP(c, hipMemcpy(kf.data(), c->sc.keyflag + unit * ks, sizeof(unsigned long long) * ks,
+                            hipMemcpyDeviceToHost));
+        for (int64_t b = 0; b < n_sc; ++b) {
+          const uint32_t k = (uint32_t)kf[(size_t)key_slot((int)b, (int)n_sc)];
+          if (k == 0u) continue;
+          const uint32_t bits = (k & 0x80000000u) ? (k & 0x7fffffffu) : ~k;
+          memcpy(&dst[1 + b], &bits, sizeof(float));
+        }
+      }
+      dst += 1 + nb;
     }
   } else {
     const uint16_t *pool = what == SD_DEBUG_K ? L.dev.k : L.dev.v;

@@ -249,12 +249,26 @@ const char *sd_last_error(const sd_ctx *ctx);
  *                        [ceil(len/S_h)][d][2] = (min, max)
  *   SD_DEBUG_MAW         for each KV head h in order: fp32 [ceil(len/S_h)]
  *   SD_DEBUG_K / _V      bf16 [len][Hkv][d], gathered through the page table
+ *   SD_DEBUG_SCORES      for each KV head h in order: fp32 [1 + ceil(len/S_h)]:
+ *                        element 0 the error bound eps the head's last
+ *                        selection used, then per block the approximate group
+ *                        score that selection ranked (the fp32 value of its
+ *                        order key); NaN for blocks that were not scored as
+ *                        candidates, and everywhere on a head that selects
+ *                        nothing.  Every scored block's exact score lies
+ *                        within eps of its approximate one ([LFPS] Core claim:
+ *                        the selection is the exact top-k; blocks within the
+ *                        band of the k-th are re-scored exactly).  Valid right
+ *                        after select_topk or sparse_decode_step of this layer
+ *                        and sequence (the scratch it reads is shared by every
+ *                        layer; the allocation-free step keeps its own).
  * bytes must equal the size reported by sd_debug_bytes. */
 #define SD_DEBUG_PAGE_TABLE 0
 #define SD_DEBUG_SUMMARY 1
 #define SD_DEBUG_MAW 2
 #define SD_DEBUG_K 3
 #define SD_DEBUG_V 4
+#define SD_DEBUG_SCORES 5
 sd_status sd_debug_bytes(const sd_ctx *ctx, int32_t what, int32_t layer,
                          int32_t seq_id, size_t *bytes);
 sd_status sd_debug_copy(sd_ctx *ctx, int32_t what, int32_t layer,

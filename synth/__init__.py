@@ -279,3 +279,53 @@ def step_kv(w: Workload, seed: int, layer: int, step: int, device="cpu"):
     K = randn((w.B, 1, w.Hkv, w.d), seed, 500000 + layer * 4096 + 2 * step, device)
     V = randn((w.B, 1, w.Hkv, w.d), seed, 500001 + layer * 4096 + 2 * step, device)
     return K, V
+
+
+# ----------------------------------------------------------------------------
+# adversarial inputs for the approximate block score's error bound
+# ----------------------------------------------------------------------------
+
+ADVERSARIAL_KINDS = ("spread", "cancel", "denormal")
+
+
+def adversarial(kind: str, B: int, Hkv: int, G: int, d: int, N: int, S: int, seed: int):
+    """Keys and queries that stress an fp32 score bound (no method arithmetic
+    here: only how the values are drawn).
+
+      spread    every (sequence, KV head, block of S tokens) draws a scale
+                2^e, e uniform in [-40, 40]; key elements are
+                +-2^(e + f) (1 + u), f uniform in [-3, 3], u in [0, 1);
+                queries N(0, 1).
+      cancel    query channels come in equal pairs (2j, 2j+1); every token
+                of a block is the same vector; in 97% of the blocks (chosen
+                at random) channel 2j+1 is the negation of channel 2j, so
+                their exact scores are 0 and a 5% budget ends among exact
+                ties; the rest are drawn as in `spread`.
+      denormal  keys as in `spread`; queries N(0, 1) * 2^-124, so that a part
+                of their elements fall below the smallest normal bf16.
+    Returns dict(q [B][G*Hkv][d], K, V [B][N][Hkv][d]) as bf16 tensors.
+    """
+    if kind not in ADVERSARIAL_KINDS:
+        raise ValueError(kind)
+    nb = n_blocks(N, S)
+    g = _gen(seed, 900, "cpu")
+    e_blk = torch.randint(-40, 41, (B, nb, Hkv), generator=g).to(torch.float32)
+    e_tok = e_blk.repeat_interleave(S, dim=1)[:, :N]                       # [B][N][Hkv]
+    f = torch.randint(-3, 4, (B, N, Hkv, d), generator=g).to(torch.float32)
+    u = torch.rand(B, N, Hkv, d, generator=g)
+    sgn = torch.where(torch.rand(B, N, Hkv, d, generator=g) < 0.5, -1.0, 1.0)
+    K = sgn * torch.exp2(e_tok[..., None] + f) * (1.0 + u)
+    q = torch.randn(B, Hkv * G, d, generator=g)
+    if kind == "cancel":
+        first = torch.arange(nb).repeat_interleave(S)[:N] * S              # first token of its block
+        K = K[:, first]                                                     # one vector per block
+        zero = torch.rand(B, nb, Hkv, generator=g) < 0.97
+        zt = zero.repeat_interleave(S, dim=1)[:, :N]
+        paired = K.clone()
+        paired[..., 1::2] = -K[..., 0::2]
+        K = torch.where(zt[..., None], paired, K)
+        q[..., 1::2] = q[..., 0::2]
+    elif kind == "denormal":
+        q = q * 2.0 ** -124
+    V = torch.randn(B, N, Hkv, d, generator=_gen(seed, 901, "cpu"))
+    return dict(q=q.to(torch.bfloat16), K=K.to(torch.bfloat16), V=V.to(torch.bfloat16))
