@@ -69,6 +69,12 @@ def lib():
         L.oracle_select.restype = i64
         L.oracle_select.argtypes = [P, i32, i32, P, P, i64, i32, i32, i32, i64,
                                     P, dbl, P, P, P, P]
+        L.oracle_select_heads.restype = i64
+        L.oracle_select_heads.argtypes = [P, i32, i32, P, P, i64, i32, i32, i32, i64,
+                                          P, dbl, P, i64]
+        L.oracle_attend_heads.restype = None
+        L.oracle_attend_heads.argtypes = [P, i32, i32, P, i64, P, i64, i64, i32, i32,
+                                          i32, P, i64, P, dbl, P, P]
         L.oracle_attend_tokens.restype = None
         L.oracle_attend_tokens.argtypes = [P, i32, i32, P, i64, P, i64, P, i64,
                                            dbl, P, P, P]
@@ -169,6 +175,44 @@ def select(q, mn, mx, N, S, n_s, W, budget_ppm, maw=None, beta=0.0):
                             _p(U), _p(u), _p(flag))
     return dict(sel=sel[:k].copy(), U=U[:nb], u=u[:nb],
                 flag=flag[:nb].astype(bool), k=int(k))
+
+
+def select_heads(q, mn, mx, N, S, n_s, W, budget_ppm, maw=None, beta=0.0):
+    """Per-query-head selection: list of G ascending int32 arrays."""
+    q, mn, mx = _u16(q), _u16(mn), _u16(mx)
+    G, d = q.shape
+    nb = num_blocks(N, S)
+    assert mn.shape == (nb, d) and mx.shape == (nb, d)
+    ld = max(nb, 1)
+    sel = np.zeros((G, ld), np.int32)
+    mw = None
+    if maw is not None:
+        mw = np.ascontiguousarray(maw, dtype=np.float64)
+        assert mw.shape[0] >= nb
+    k = lib().oracle_select_heads(_p(q), G, d, _p(mn), _p(mx), N, S, n_s, W,
+                                  int(budget_ppm), _p(mw), float(beta), _p(sel), ld)
+    return [sel[h, :k].copy() for h in range(G)]
+
+
+def attend_heads(q, K, V, N, S, n_s, W, sels, scale=None):
+    """Per-query-head attention: head h over D U blocks(sels[h])."""
+    q, K, V = _u16(q), _u16(K), _u16(V)
+    G, d = q.shape
+    assert len(sels) == G
+    ld = max([1] + [len(s) for s in sels])
+    sel = np.zeros((G, ld), np.int32)
+    k = np.zeros(G, np.int64)
+    for h, s in enumerate(sels):
+        sel[h, :len(s)] = s
+        k[h] = len(s)
+    if scale is None:
+        scale = 1.0 / np.sqrt(d)
+    O = np.zeros((G, d), np.float64)
+    lse = np.zeros(G, np.float64)
+    lib().oracle_attend_heads(_p(q), G, d, _p(K), K.shape[1], _p(V), V.shape[1],
+                              N, S, n_s, W, _p(sel), ld, _p(k), float(scale),
+                              _p(O), _p(lse))
+    return O, lse
 
 
 def attend_tokens(q, K, V, tok, scale=None, want_p=False):

@@ -23,6 +23,12 @@
  *                         keep MAW, blocks inside D take the average)
  *   oracle_maw_flag       pinned: hand fixture at S = 32 and a selection hand
  *                         case at S = 2 on either side of beta*S/|D|
+ *   oracle_select_heads   pinned: brute force over all k-subsets per head at
+ *                         G = 3, independence of the heads, equal rows give
+ *                         the group selection
+ *   oracle_attend_heads   pinned: each head over its own token list by
+ *                         oracle_attend_tokens; full budget equals the
+ *                         independent dense softmax for every head
  *   The readings themselves - group max (R1), per-block MAW (R8), the
  *   beta/|D| flag scale (R9) and the lexicographic flag-then-score order
  *   (R11) - are not fixed by the pages; the pins above fix the oracle to
@@ -214,6 +220,26 @@ int64_t oracle_select(const uint16_t *q, int32_t G, int32_t d,
   return k;
 }
 
+/* Per-query-head selection, the literal per-head reading: the pages count
+ * and budget attention heads one query head at a time ([FLX] Figure 4: the
+ * output deviation of each of Llama-3.1-8B's 32 heads; Figure 5: a minimum
+ * budget per head for the 32 heads of a layer; [HGCA] What carries the
+ * argument: the sparse set is chosen per head).  Under grouped-query
+ * attention the G query heads of a KV head read the same blocks, so each
+ * head's set is oracle_select over a group of that one head: its own bound,
+ * the KV head's k, MAW flags and order. */
+int64_t oracle_select_heads(const uint16_t *q, int32_t G, int32_t d,
+                            const uint16_t *mn, const uint16_t *mx, int64_t N,
+                            int32_t S, int32_t n_s, int32_t W,
+                            int64_t budget_ppm, const double *maw, double beta,
+                            int32_t *sel, int64_t ld_sel) {
+  int64_t k = 0;
+  for (int32_t h = 0; h < G; ++h)
+    k = oracle_select(q + (int64_t)h * d, 1, d, mn, mx, N, S, n_s, W, budget_ppm, maw, beta,
+                      sel + (int64_t)h * ld_sel, NULL, NULL, NULL);
+  return k;
+}
+
 /* Softmax attention of each query head over a token list, in the max-shifted
  * form ([HGCA] referee minor comment on section 3.3: subtract the maximum
  * before exponentiating).  R18: natural-log lse of scaled logits. */
@@ -272,6 +298,19 @@ int64_t oracle_attend(const uint16_t *q, int32_t G, int32_t d,
   free(tok);
   free(inT);
   return n_tok;
+}
+
+/* Per-query-head attention: head h attends T_h = D U tokens(sel_h), its own
+ * selection (a group of one head in oracle_attend). */
+void oracle_attend_heads(const uint16_t *q, int32_t G, int32_t d,
+                         const uint16_t *K, int64_t ldk, const uint16_t *V,
+                         int64_t ldv, int64_t N, int32_t S, int32_t n_s,
+                         int32_t W, const int32_t *sel, int64_t ld_sel,
+                         const int64_t *k, double scale, double *O,
+                         double *lse) {
+  for (int32_t h = 0; h < G; ++h)
+    oracle_attend(q + (int64_t)h * d, 1, d, K, ldk, V, ldv, N, S, n_s, W,
+                  sel + (int64_t)h * ld_sel, k[h], scale, O + (int64_t)h * d, lse + h);
 }
 
 /* The MAW input of one step (R8, and R10 as read from HGCA): HGCA's moving

@@ -96,6 +96,16 @@ int64_t oracle_select(const uint16_t *q, int32_t G, int32_t d,
                       const double *maw, double beta, int32_t *sel,
                       double *U, float *u, int8_t *flag);
 
+/* Per-query-head selection: each of the G query heads of a KV head ranks the
+ * candidate blocks by its own bound U_h alone, with the k, MAW flags and
+ * order of oracle_select (a group of one head).  sel: [G][ld_sel], row h
+ * holds head h's k entries ascending (ld_sel >= n_blk).  Returns k. */
+int64_t oracle_select_heads(const uint16_t *q, int32_t G, int32_t d,
+                            const uint16_t *mn, const uint16_t *mx, int64_t N,
+                            int32_t S, int32_t n_s, int32_t W,
+                            int64_t budget_ppm, const double *maw, double beta,
+                            int32_t *sel, int64_t ld_sel);
+
 /* Softmax attention of G heads over an explicit list of distinct tokens.
  * s_j = scale * q_h . k_j;  lse_h = log sum_j e^{s_j};
  * O_h = sum_j e^{s_j - lse_h} v_j.  An empty list gives lse = -inf, O = 0.
@@ -112,6 +122,16 @@ int64_t oracle_attend(const uint16_t *q, int32_t G, int32_t d,
                       int64_t ldv, int64_t N, int32_t S, int32_t n_s,
                       int32_t W, const int32_t *sel, int64_t k, double scale,
                       double *O, double *lse);
+
+/* Per-query-head attention: head h attends T_h = D U tokens(its own
+ * selection), row h of sel [G][ld_sel] with k[h] entries.  O: [G][d],
+ * lse: [G]. */
+void oracle_attend_heads(const uint16_t *q, int32_t G, int32_t d,
+                         const uint16_t *K, int64_t ldk, const uint16_t *V,
+                         int64_t ldv, int64_t N, int32_t S, int32_t n_s,
+                         int32_t W, const int32_t *sel, int64_t ld_sel,
+                         const int64_t *k, double scale, double *O,
+                         double *lse);
 
 /* MAW input: a_blk[i] = (1/G) sum_h sum_{j in D, j in block i} p_hj with p_h
  * the softmax of head h over the dense set D alone (0 for blocks with no

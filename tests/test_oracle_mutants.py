@@ -66,6 +66,12 @@ MUTANTS = [
      "a_blk[tok[tt] / S] += p[(int64_t)h * nD + tt];"),
     ("dense_mass_block_index", "a_blk[tok[tt] / S] += p[(int64_t)h * nD + tt] / (double)G;",
      "a_blk[tt / S] += p[(int64_t)h * nD + tt] / (double)G;"),
+    ("select_heads_group_of_all", "k = oracle_select(q + (int64_t)h * d, 1, d,",
+     "k = oracle_select(q, G, d,"),
+    ("select_heads_first_head_only", "k = oracle_select(q + (int64_t)h * d, 1, d,",
+     "k = oracle_select(q, 1, d,"),
+    ("attend_heads_first_selection", "sel + (int64_t)h * ld_sel, k[h], scale,",
+     "sel, k[0], scale,"),
     ("selected_block_last_token_dropped",
      "for (int64_t j = (int64_t)sel[t] * S; j < ((int64_t)sel[t] + 1) * S && j < N; ++j)",
      "for (int64_t j = (int64_t)sel[t] * S; j < ((int64_t)sel[t] + 1) * S - 1 && j < N; ++j)"),
