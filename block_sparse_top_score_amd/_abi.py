@@ -49,7 +49,7 @@ class SDConfig(ctypes.Structure):
         ("budget_ppm", ctypes.POINTER(ctypes.c_int32)),
         ("softmax_scale", ctypes.c_float), ("maw_decay", ctypes.c_float),
         ("maw_beta", ctypes.c_float), ("page_shuffle_seed", ctypes.c_uint64),
-        ("stream", ctypes.c_void_p),
+        ("stream", ctypes.c_void_p), ("select_per_query_head", ctypes.c_int32),
     ]
 
 
@@ -107,7 +107,8 @@ def make_config(*, max_seqs, num_layers, num_q_heads, num_kv_heads, head_dim,
                 num_pages, max_seq_len, sink_tokens, recent_window,
                 block_size: Sequence[int], budget_ppm: Sequence[int],
                 softmax_scale=0.0, maw_decay=0.95, maw_beta=0.0,
-                page_shuffle_seed=0, stream=None, page_size=16):
+                page_shuffle_seed=0, stream=None, page_size=16,
+                select_per_query_head=0):
     bs = (ctypes.c_int32 * len(block_size))(*block_size)
     bp = (ctypes.c_int32 * len(budget_ppm))(*budget_ppm)
     cfg = SDConfig(max_seqs, num_layers, num_q_heads, num_kv_heads, head_dim,
@@ -115,7 +116,7 @@ def make_config(*, max_seqs, num_layers, num_q_heads, num_kv_heads, head_dim,
                    recent_window, ctypes.cast(bs, ctypes.POINTER(ctypes.c_int32)),
                    ctypes.cast(bp, ctypes.POINTER(ctypes.c_int32)),
                    float(softmax_scale), float(maw_decay), float(maw_beta),
-                   int(page_shuffle_seed), stream)
+                   int(page_shuffle_seed), stream, int(select_per_query_head))
     cfg._keep = (bs, bp)  # keep the arrays alive with the struct
     return cfg
 
@@ -159,6 +160,8 @@ class SparseDecode:
             raise SDError(st, msg)
         self.Hq = self.cfg.num_q_heads
         self.Hkv = self.cfg.num_kv_heads
+        self.pqh = bool(self.cfg.select_per_query_head)
+        self.sel_heads = self.Hq if self.pqh else self.Hkv  # rows of blk_idx per sequence
         self.d = self.cfg.head_dim
         k, p = ctypes.c_int32(), ctypes.c_int32()
         self.L.sd_caps(self.ctx, ctypes.byref(k), ctypes.byref(p))
@@ -287,8 +290,8 @@ class SparseDecode:
     # -- allocation helpers (torch device memory) ---------------------------
     def alloc_step(self, n_seqs, device="cuda"):
         t = self.torch
-        blk_idx = t.full((n_seqs, self.Hkv, self.k_cap), -1, dtype=t.int32, device=device)
-        blk_cnt = t.zeros((n_seqs, self.Hkv), dtype=t.int32, device=device)
+        blk_idx = t.full((n_seqs, self.sel_heads, self.k_cap), -1, dtype=t.int32, device=device)
+        blk_cnt = t.zeros((n_seqs, self.sel_heads), dtype=t.int32, device=device)
         o_part = t.empty((n_seqs, self.Hq, self.p_cap, self.d), dtype=t.float32, device=device)
         lse_part = t.empty((n_seqs, self.Hq, self.p_cap), dtype=t.float32, device=device)
         o = t.empty((n_seqs, self.Hq, self.d), dtype=t.float32, device=device)

@@ -87,11 +87,16 @@ struct Dims {
   int32_t lm_sel0;     // log-mass slots of dense pages; selected pages follow
   int32_t lm_cap;      // log-mass slots per (seq, query head)
   int32_t kcap;        // selected block slots per (seq, kv head)
+  int32_t pqh;         // 1: one selection per query head (unit arrays of the
+                       // selection are per query head), 0: per KV head
+  int32_t ucap;        // entries of a KV head's union of its query heads' sets
 };
 
 // Scratch owned by the context.  Per-unit arrays have key_stride entries, a
 // multiple of 64.
 struct Scratch {
+  // (per-query-head selection: [max_seqs][Hq] in place of [max_seqs][Hkv]
+  // in keyflag, keys, ulist, ukeys and unit_acc)
   unsigned long long *keyflag;  // [max_seqs][Hkv][key_stride] key | MAW flag << 32
   uint32_t *keys;    // [max_seqs][Hkv][key_stride] top-k words past LDS (long units)
   int32_t *ulist;    // [max_seqs][Hkv][key_stride] uncertain blocks past LDS
@@ -108,6 +113,9 @@ struct Scratch {
                                // after the selection
   unsigned long long *seltag;  // [max_seqs][Hkv][kcap] step << 32 | block of the selection
   uint32_t *err;     // [1] nonzero once a step kernel's wait ran out of time
+  int32_t *uni;      // per-query-head selection: [max_seqs][Hkv][ucap] the union of
+                     // the group's sets, ascending, block | head mask << 24
+  int32_t *ucnt;     //   and its size, [max_seqs][Hkv]
 };
 
 // Everything a kernel needs about the context (passed by value).
@@ -128,6 +136,12 @@ hipError_t launch_append(const Ctx &c, const AppendBatch &b, int max_new,
 // Score + top-k (last arriver per unit).
 hipError_t launch_select(const Ctx &c, const SeqBatch &b, int max_blocks, const uint16_t *q,
                          int32_t *blk_idx, int32_t *blk_cnt, int32_t k_cap, hipStream_t st);
+
+// Per-query-head selection: the union of each KV head's query-head sets
+// (blk_idx [n][Hq][k_cap], blk_cnt [n][Hq]) into the context's scratch, for
+// the attention.
+hipError_t launch_union(const Ctx &c, const SeqBatch &b, const int32_t *blk_idx,
+                        const int32_t *blk_cnt, int32_t k_cap, hipStream_t st);
 
 // Attention: P workgroups per unit, one partial slot each (slots [P, p_cap)
 // emptied); keeps the dense pages' log-masses for the fusion call.

@@ -575,8 +575,10 @@ __device__ __forceinline__ void tile_list(const Ctx &c, int seq, int h, int tile
 }
 
 // fast_ok: also write the tile's candidate list for the fast top-k (tile <
-// kFastTiles).
-template <int D, int G>
+// kFastTiles).  PQH: one key per query head (each head ranks its own bounds;
+// the keys, bounds and flag counts of query head j of the unit sit at unit
+// index unit * G + j), no list.
+template <int D, int G, bool PQH = false>
 __device__ __attribute__((always_inline)) bool score_tile(const Ctx &c, int i, int seq, int h, const HeadInfo &hi,
                            int N, int n_blk, int tile, const uint16_t *__restrict__ q,
                            TopkSmem &sm, bool fast_ok, UG &g) {
@@ -614,11 +616,11 @@ __device__ __attribute__((always_inline)) bool score_tile(const Ctx &c, int i, i
 #pragma unroll
   for (int gi = 0; gi < GPW; ++gi) {
     const int blk = base + gi * 16 + r16;
-    mwv[gi] = (need_maw && lgrp == 0 && blk < n_blk) ? mwp[blk] : 0.0f;
+    mwv[gi] = (need_maw && (lgrp == 0 || PQH) && blk < n_blk) ? mwp[blk] : 0.0f;
   }
   __builtin_amdgcn_sched_barrier(0);
   g = unit_geom(N, hi, c.dm);
-  const bool publish = fast_ok && g.kk <= kTileList;
+  const bool publish = !PQH && fast_ok && g.kk <= kTileList;
   // A operand: lane = head r16 (zero rows past G), channel quad 4*mm + lgrp,
   // pairs (q-, q+) matching the (min, max) pairs of the summaries
   uint4 qa[MM];
@@ -638,6 +640,7 @@ __device__ __attribute__((always_inline)) bool score_tile(const Ctx &c, int i, i
   }
   const uint32_t absm = 0x7fff7fffu;
   float emax = 0.0f;
+  float eh[4] = {0.0f, 0.0f, 0.0f, 0.0f};  // PQH: bounds of heads 4 lgrp + jr
   int n_flag = 0;
 #pragma unroll
   for (int gi = 0; gi < GPW; ++gi) {
@@ -661,6 +664,27 @@ __device__ __attribute__((always_inline)) bool score_tile(const Ctx &c, int i, i
       acce += pe;
     }
     // lane (r16, lgrp) holds block r16 for heads 4*lgrp + jr
+    if constexpr (PQH) {
+      const int blk = base + gi * 16 + r16;
+      if (blk < g.n_sc) {
+        const bool cand = is_candidate(g, blk);
+        const bool fl = c.dm.maw_beta > 0.0f &&
+                        (double)mwv[gi] * (double)dense_count(g) > (double)c.dm.maw_beta * (double)hi.S;
+        n_flag += (fl && cand && lgrp == 0) ? 1 : 0;
+        const int slot = key_slot(blk, g.n_sc);
+#pragma unroll
+        for (int jr = 0; jr < 4; ++jr) {
+          const int hd = 4 * lgrp + jr;
+          if (hd < G) {
+            unsigned long long kv = cand ? order_key(acc[jr]) : 0u;
+            if (fl) kv |= 1ull << 32;
+            if (cand) eh[jr] = fmaxf(eh[jr], score_eps(acce[jr], acc[jr]));
+            st_dev(&c.sc.keyflag[(((size_t)seq * c.dm.Hkv + h) * G + hd) * c.dm.key_stride + slot], kv);
+          }
+        }
+      }
+      continue;
+    }
     float A = -INFINITY, E = 0.0f;
 #pragma unroll
     for (int jr = 0; jr < 4; ++jr)
@@ -688,6 +712,27 @@ __device__ __attribute__((always_inline)) bool score_tile(const Ctx &c, int i, i
       st_dev(&c.sc.keyflag[ko], kv);
     }
     if (publish && lgrp == 0) sm.tk[wv * 16 * GPW + gi * 16 + r16] = (uint32_t)kv;
+  }
+  if constexpr (PQH) {
+    // per query head: the largest bound over the tile (rows of 16 lanes share
+    // lgrp, so a row maximum gathers one head's blocks), then over the waves
+    const int nf = wave_sum_i(n_flag);
+#pragma unroll
+    for (int jr = 0; jr < 4; ++jr) {
+      const float e = row_max16(eh[jr]);
+      if (r16 == 0 && 4 * lgrp + jr < G) sm.ukey[wv * 8 + 4 * lgrp + jr] = __float_as_uint(e);
+    }
+    if (lane == 0) red[4 + wv] = (uint32_t)nf;
+    __syncthreads();
+    if (threadIdx.x < G) {
+      const int hd = threadIdx.x;
+      uint32_t *acc = &c.sc.unit_acc[4 * (((size_t)seq * c.dm.Hkv + h) * G + hd)];
+      const uint32_t e = max(max(sm.ukey[hd], sm.ukey[8 + hd]), max(sm.ukey[16 + hd], sm.ukey[24 + hd]));
+      __hip_atomic_fetch_max(acc, e, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      const uint32_t f = red[4] + red[5] + red[6] + red[7];
+      if (f) __hip_atomic_fetch_add(acc + 1, f, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    }
+    return false;
   }
   // the unit's largest error bound (non-negative floats order as their bits)
   // and its flagged candidates, accumulated over the tiles
@@ -815,7 +860,8 @@ __device__ double exact_score_quad(const Ctx &c, int seq, const HeadInfo &hi, in
 //      bitmask of rows;
 //   4. ordered compaction with ballots: ascending block indices.
 template <int D, int G>
-__device__ __attribute__((always_inline)) void topk_unit(const Ctx &c, int i, int seq, int h, const HeadInfo &hi,
+__device__ __attribute__((always_inline)) void topk_unit(const Ctx &c, int seq, size_t unit, size_t out,
+                          const HeadInfo &hi,
                           const UG &g, const uint16_t *__restrict__ q,
                           int32_t *__restrict__ blk_idx, int32_t *__restrict__ blk_cnt,
                           int k_cap, TopkSmem &sm, uint32_t *lrows, int lrows_words,
@@ -824,7 +870,6 @@ __device__ __attribute__((always_inline)) void topk_unit(const Ctx &c, int i, in
   if (threadIdx.x >= 64) return;
   const int lane = threadIdx.x;
   const int n = g.n_sc, rows = cdiv(n, 64);
-  const size_t unit = (size_t)seq * c.dm.Hkv + h;
   const size_t uo = unit * c.dm.key_stride;
   const unsigned long long *gkf = c.sc.keyflag + uo;
   constexpr int kRegWords = kTopkRegRows * 64;
@@ -852,7 +897,7 @@ __device__ __attribute__((always_inline)) void topk_unit(const Ctx &c, int i, in
 #pragma unroll
   for (int r = 0; r < kTopkRegRows; ++r) kv[r] = ld_dev(&gkf[min(r * 64 + lane, jl)]);
   constexpr int QPL = (G * D + 63) / 64;
-  const uint16_t *qg = q + ((size_t)i * c.dm.Hq + (size_t)h * G) * D;
+  const uint16_t *qg = q + out * G * D;
   uint16_t qv[QPL];
 #pragma unroll
   for (int r = 0; r < QPL; ++r) qv[r] = qg[min(r * 64 + lane, G * D - 1)];
@@ -1084,7 +1129,7 @@ __device__ __attribute__((always_inline)) void topk_unit(const Ctx &c, int i, in
   }
 
   // 4. ordered compaction
-  int32_t *dst = blk_idx + ((size_t)i * c.dm.Hkv + h) * k_cap;
+  int32_t *dst = blk_idx + out * k_cap;
   int ob = 0;
   auto emit_row = [&](int r, uint32_t v, unsigned long long dm) {
     const bool ch = v == 1u || v > kb_hi || ((dm >> lane) & 1ull);
@@ -1106,7 +1151,7 @@ __device__ __attribute__((always_inline)) void topk_unit(const Ctx &c, int i, in
   }
   for (int r = kTopkRegRows; r < rows; ++r) emit_row(r, mem_ld(r * 64 + lane), dmask[r]);
   if (lane == 0) {
-    st_dev(&blk_cnt[(size_t)i * c.dm.Hkv + h], kk);
+    st_dev(&blk_cnt[out], kk);
     st_dev(&c.sc.unit_acc[4 * unit], 0u);  // cleared for the next step
     st_dev(&c.sc.unit_acc[4 * unit + 1], 0u);
     st_dev(&c.sc.unit_acc[4 * unit + 2], eps_bits);  // the bound this selection used
@@ -1154,7 +1199,8 @@ __device__ __forceinline__ int wg_scan(int x, uint32_t *red, int &slot, int &tot
 // order by a second scan, through LDS when they fit so that the stores are
 // coalesced.
 template <int D, int G>
-__device__ __attribute__((always_inline)) void topk_wide(const Ctx &c, int i, int seq, int h, const HeadInfo &hi,
+__device__ __attribute__((always_inline)) void topk_wide(const Ctx &c, int seq, size_t unit, size_t out,
+                          const HeadInfo &hi,
                           const UG &g, const uint16_t *__restrict__ q,
                           int32_t *__restrict__ blk_idx, int32_t *__restrict__ blk_cnt,
                           int k_cap, TopkSmem &sm,
@@ -1164,7 +1210,6 @@ __device__ __attribute__((always_inline)) void topk_wide(const Ctx &c, int i, in
   const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
   const int n = g.n_sc, rows = cdiv(n, 64);
   const int m = cdiv(n, 256), j0 = tid * m;
-  const size_t unit = (size_t)seq * c.dm.Hkv + h;
   const size_t uo = unit * c.dm.key_stride;
   const unsigned long long *gkf = c.sc.keyflag + uo;
   int32_t *gul = c.sc.ulist + uo;
@@ -1183,7 +1228,7 @@ __device__ __attribute__((always_inline)) void topk_wide(const Ctx &c, int i, in
 #pragma unroll
   for (int x = 0; x < kWideM; ++x) kv[x] = (x < m && j0 + x < n) ? ld_dev(&gkf[x * 256 + tid]) : 0ull;
   constexpr int QT = (G * D + 255) / 256;
-  const uint16_t *qg = q + ((size_t)i * c.dm.Hq + (size_t)h * G) * D;
+  const uint16_t *qg = q + out * G * D;
   uint16_t qv[QT];
 #pragma unroll
   for (int t = 0; t < QT; ++t) qv[t] = qg[min(tid + 256 * t, G * D - 1)];
@@ -1385,7 +1430,7 @@ __device__ __attribute__((always_inline)) void topk_wide(const Ctx &c, int i, in
   const int my_ch = __popcll(chm);
   int tot = 0;
   int o = wg_scan(my_ch, red, slot, tot);
-  int32_t *dst = blk_idx + ((size_t)i * c.dm.Hkv + h) * k_cap;
+  int32_t *dst = blk_idx + out * k_cap;
   const bool staged = tot <= stage_words;  // the same for every thread
   for (unsigned long long cm = chm; cm != 0ull; cm &= cm - 1ull) {
     const int j = j0 + (int)__builtin_ctzll(cm);
@@ -1406,7 +1451,7 @@ __device__ __attribute__((always_inline)) void topk_wide(const Ctx &c, int i, in
     }
   }
   if (tid == 0) {
-    st_dev(&blk_cnt[(size_t)i * c.dm.Hkv + h], kk);
+    st_dev(&blk_cnt[out], kk);
     st_dev(&c.sc.unit_acc[4 * unit], 0u);  // cleared for the next step
     st_dev(&c.sc.unit_acc[4 * unit + 1], 0u);
     st_dev(&c.sc.unit_acc[4 * unit + 2], eps_bits);  // the bound this selection used
@@ -1420,7 +1465,7 @@ __device__ __attribute__((always_inline)) void topk_wide(const Ctx &c, int i, in
 // result).  The steps of topk_unit run on the listed keys, which hold the
 // unit's top kk:
 //   1. the lists, each descending, are merged pairwise keeping the 64
-//      largest keys (bitonic half-cleaners; DPP and ds_bpermute exchanges),
+//      largest keys (bitonic half-cleaners; DPP and permlane exchanges),
 //      which gives the kk-th largest approximate key T;
 //   2. band: keys above T + 2 eps are in, below T - 2 eps out (eps: the
 //      unit's error bound); the blocks in between are re-scored exactly by
@@ -1434,8 +1479,8 @@ __device__ __attribute__((always_inline)) void topk_wide(const Ctx &c, int i, in
 // Returns false, before writing anything, when the band reaches past the 64
 // largest keys; the caller then runs topk_unit.
 template <int D, int G>
-__device__ __attribute__((always_inline)) bool topk_fast(const Ctx &c, int i, int seq, int h,
-                                                         const HeadInfo &hi, const UG &g,
+__device__ __attribute__((always_inline)) bool topk_fast(const Ctx &c, int seq, size_t unit,
+                                                         size_t out, const HeadInfo &hi, const UG &g,
                                                          const uint16_t *__restrict__ q,
                                                          int32_t *__restrict__ blk_idx,
                                                          int32_t *__restrict__ blk_cnt, int k_cap,
@@ -1444,7 +1489,6 @@ __device__ __attribute__((always_inline)) bool topk_fast(const Ctx &c, int i, in
                                                          unsigned long long *rtag = nullptr,
                                                          uint32_t epoch = 0) {
   const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
-  const size_t unit = (size_t)seq * c.dm.Hkv + h;
   const int n_tiles = max(1, cdiv(g.n_sc, kScoreTile));
   const unsigned long long etag = (unsigned long long)epoch << 32;
   const unsigned long long *cl = c.sc.cand + unit * c.dm.key_stride;
@@ -1456,7 +1500,7 @@ __device__ __attribute__((always_inline)) bool topk_fast(const Ctx &c, int i, in
   for (int r = 0; r < kFastTiles; ++r)
     e[r] = (wv == 0 && r < n_tiles) ? ld_dev(&cl[(size_t)r * kTileList + lane]) : 0ull;
   const uint32_t eps_bits = ld_dev(&c.sc.unit_acc[4 * unit]);
-  const uint16_t *qg = q + ((size_t)i * c.dm.Hq + (size_t)h * G) * D;
+  const uint16_t *qg = q + out * G * D;
   constexpr int QT = (G * D + 255) / 256;
   uint16_t qv[QT];
 #pragma unroll
@@ -1577,7 +1621,7 @@ __device__ __attribute__((always_inline)) bool topk_fast(const Ctx &c, int i, in
               r2 = __builtin_amdgcn_readlane(incl, 47);
     incl += (lane >= 16 ? r0 : 0) + (lane >= 32 ? r1 : 0) + (lane >= 48 ? r2 : 0);
     int o = incl - cw;
-    int32_t *dst = blk_idx + ((size_t)i * c.dm.Hkv + h) * k_cap;
+    int32_t *dst = blk_idx + out * k_cap;
     while (wbits) {
       const int bb = lane * 64 + (__ffsll((long long)wbits) - 1);
       if (o < k_cap) st_dev(&dst[o], bb);
@@ -1585,7 +1629,7 @@ __device__ __attribute__((always_inline)) bool topk_fast(const Ctx &c, int i, in
       wbits &= wbits - 1ull;
     }
     if (lane == 0) {
-      st_dev(&blk_cnt[(size_t)i * c.dm.Hkv + h], kk);
+      st_dev(&blk_cnt[out], kk);
       st_dev(&c.sc.unit_acc[4 * unit], 0u);  // cleared for the next step
       st_dev(&c.sc.unit_acc[4 * unit + 1], 0u);
       st_dev(&c.sc.unit_acc[4 * unit + 2], eps_bits);  // the bound this selection used
@@ -1628,8 +1672,15 @@ __device__ __forceinline__ DenseList dense_list(const UG &g) {
 // Both call forms take the same number, so they give the same bits; a unit
 // with fewer pages than the launch's longest does not hold workgroups that
 // have nothing to do.
-__device__ __forceinline__ int unit_parts(const UG &g, int P) {
-  const int pages = dense_list(g).n + g.kk * (g.S / kPage);
+// Blocks the attention visits at most: k, or with one set per query head
+// the union of the G sets, min(candidates, G k).
+__device__ __forceinline__ int union_blocks(const UG &g, const Dims &dm) {
+  if (!dm.pqh) return g.kk;
+  const int n_cand = g.ns < g.wlo ? div_S(g.wlo + g.S - 1, g.S) - div_S(g.ns, g.S) : 0;
+  return min(n_cand, dm.G * g.kk);
+}
+__device__ __forceinline__ int unit_parts(const UG &g, int P, const Dims &dm) {
+  const int pages = dense_list(g).n + union_blocks(g, dm) * (g.S / kPage);
   return min(P, max(1, cdiv(pages, kPartPages)));
 }
 __device__ __forceinline__ int dense_page(const DenseList &d, int e) {
@@ -1722,8 +1773,10 @@ __device__ __forceinline__ uint32_t bf16_rne_bits(float x) {
   return (b + 0x7fffu + ((b >> 16) & 1u)) >> 16;
 }
 
-// One stage of a wave: pages with token masks mk0, mk1 (uniform), log-mass
-// slots s0, s1 (-1: none).  lmb: log-mass rows of the unit's heads.  Rows of
+// One stage of a wave: pages with token masks mk0, mk1 (uniform; bits 0-15
+// the page's tokens, bit 16 + h set when query head h attends none of them,
+// which only a per-query-head selection does), log-mass slots s0, s1 (-1:
+// none).  lmb: log-mass rows of the unit's heads.  Rows of
 // padding heads (past G) carry finite values that are never stored.
 template <int D, int G>
 __device__ __forceinline__ void compute_stage(const Ctx &c, KVStage<D> &st, int mk0, int mk1,
@@ -1742,9 +1795,11 @@ __device__ __forceinline__ void compute_stage(const Ctx &c, KVStage<D> &st, int 
       acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, qa[m]),
                                                     __builtin_bit_cast(bf16x8, st.k[pi][m]),
                                                     acc, 0, 0, 0);
-    const bool on = (((pi ? mk1 : mk0) >> r16) & 1) != 0;
+    const int mk = pi ? mk1 : mk0;
+    const bool on = ((mk >> r16) & 1) != 0;
 #pragma unroll
-    for (int j = 0; j < 4; ++j) sc[pi][j] = on ? acc[j] * c.dm.scale_log2 : -INFINITY;
+    for (int j = 0; j < 4; ++j)
+      sc[pi][j] = (on && !((mk >> (16 + 4 * lgrp + j)) & 1)) ? acc[j] * c.dm.scale_log2 : -INFINITY;
   }
   float al[4], mnv[4];
 #pragma unroll
@@ -1980,7 +2035,7 @@ __device__ __attribute__((always_inline)) void attend_part(const Ctx &c, int i, 
         c, h, gw, NW, cnt * PPB,
         [&](int t, int &pg, int &mk, int &sl) {
           const int j = div_m(t, PPB), pp = t - j * PPB;
-          int blk;
+          int blk, hx = 0;
           if (si.tag) {  // published before the count; the tag confirms it
             unsigned long long e = ld_dev(&si.tag[j]);
             const unsigned long long t0 = wall_clock64();
@@ -1992,6 +2047,10 @@ __device__ __attribute__((always_inline)) void attend_part(const Ctx &c, int i, 
               blk = -1;
               st_dev(&c.sc.err[0], 1u);
             }
+          } else if (c.dm.pqh) {  // the group's union: block | head mask << 24
+            const int e = si.blk[j];
+            blk = e & 0xffffff;
+            hx = ~(e >> 24) & 0xff;  // query heads that did not select it
           } else {
             blk = si.blk[j];
           }
@@ -2001,8 +2060,8 @@ __device__ __attribute__((always_inline)) void attend_part(const Ctx &c, int i, 
           const int pn = in_range ? blk * PPB + pp : 0;
           const int pl_ = min(pn, dl.np - 1);  // pages past N are never read
           pg = ptl ? ptl[pl_] : pts[pl_];
-          mk = in_range ? page_valid16(g, pn) & ~page_dense16(g, pn) : 0;
-          sl = c.dm.lm_sel0 + t;
+          mk = in_range ? (page_valid16(g, pn) & ~page_dense16(g, pn)) | (hx << 16) : 0;
+          sl = -1;  // (only the dense pages' masses feed MAW)
         },
         qa, W, pl, lmb, tok);
   }
@@ -2359,23 +2418,89 @@ __global__ __launch_bounds__(256) void k_select(Ctx c, SeqBatch b, int tiles_x,
   const int n_blk = div_S(N + hi.S - 1, hi.S);
   const int n_tiles = max(1, cdiv(scored_blocks(N, hi.S, c.dm), kScoreTile));
   if (tile >= n_tiles) return;
+  const int rows_h = c.dm.pqh ? G : 1;  // selections per KV head
   if (selects_nothing(hi, N, c.dm)) {  // no scoring: the count is 0
-    if (tile == 0 && threadIdx.x == 0) st_dev(&blk_cnt[(size_t)i * c.dm.Hkv + h], 0);
+    if (tile == 0 && threadIdx.x < rows_h)
+      st_dev(&blk_cnt[((size_t)i * c.dm.Hkv + h) * rows_h + threadIdx.x], 0);
     return;
   }
   UG g;
-  score_tile<D, G>(c, i, seq, h, hi, N, n_blk, tile, q, smem_topk, false, g);
+  if (c.dm.pqh)
+    score_tile<D, G, true>(c, i, seq, h, hi, N, n_blk, tile, q, smem_topk, false, g);
+  else
+    score_tile<D, G>(c, i, seq, h, hi, N, n_blk, tile, q, smem_topk, false, g);
   uint32_t *ctr = &c.sc.arrive[((size_t)seq * c.dm.Hkv + h) * 4];
   if (!arrive_last(ctr, (unsigned)n_tiles, &smem_topk.last)) return;
   uint32_t *lrows = reinterpret_cast<uint32_t *>(smem_raw + sizeof(TopkSmem));
   unsigned long long *dmask = reinterpret_cast<unsigned long long *>(lrows + lrows_words);
-  if (wide_unit(g.n_sc))
-    topk_wide<D, G>(c, i, seq, h, hi, g, q, blk_idx, blk_cnt, k_cap, smem_topk, dmask,
+  const size_t unit = (size_t)seq * c.dm.Hkv + h, out = (size_t)i * c.dm.Hkv + h;
+  if (c.dm.pqh) {
+    // one top-k per query head of the group, each over that head's own keys
+    // and exact scores (a group of one head)
+    for (int j = 0; j < G; ++j) {
+      if (wide_unit(g.n_sc))
+        topk_wide<D, 1>(c, seq, unit * G + j, out * G + j, hi, g, q, blk_idx, blk_cnt, k_cap,
+                        smem_topk, dmask, reinterpret_cast<int32_t *>(lrows), lrows_words);
+      else
+        topk_unit<D, 1>(c, seq, unit * G + j, out * G + j, hi, g, q, blk_idx, blk_cnt, k_cap,
+                        smem_topk, lrows, lrows_words, dmask);
+      __syncthreads();
+    }
+  } else if (wide_unit(g.n_sc)) {
+    topk_wide<D, G>(c, seq, unit, out, hi, g, q, blk_idx, blk_cnt, k_cap, smem_topk, dmask,
                     reinterpret_cast<int32_t *>(lrows), lrows_words);
-  else
-    topk_unit<D, G>(c, i, seq, h, hi, g, q, blk_idx, blk_cnt, k_cap, smem_topk, lrows,
+  } else {
+    topk_unit<D, G>(c, seq, unit, out, hi, g, q, blk_idx, blk_cnt, k_cap, smem_topk, lrows,
                     lrows_words, dmask);
+  }
   if (threadIdx.x == 0) st_dev(ctr, 0u);
+}
+
+// Union of a KV head's per-query-head selections (one workgroup per
+// (KV head, sequence)): a byte of head bits per scored block in LDS, set from
+// the G lists, then compacted in block order into block | mask << 24 entries
+// with a workgroup scan.  Entries outside the scored blocks are dropped (a
+// block past them lies wholly in the window: it has no token outside D).
+template <int G>
+__global__ __launch_bounds__(256) void k_union(Ctx c, SeqBatch b, const int32_t *__restrict__ blk_idx,
+                                               const int32_t *__restrict__ blk_cnt, int k_cap) {
+  extern __shared__ __align__(16) uint32_t hb[];  // ceil(max_scored / 4) words
+  __shared__ uint32_t red[8];
+  const int tid = threadIdx.x;
+  const int h = blockIdx.x, i = blockIdx.y;
+  const HeadInfo hi = c.heads[h];
+  const int seq = b.seq[i], N = b.len[i];
+  const int n_sc = min(scored_blocks(N, hi.S, c.dm), b.max_scored);
+  const int words = (n_sc + 3) >> 2;
+  for (int w = tid; w < words; w += 256) hb[w] = 0u;
+  __syncthreads();
+  for (int j = 0; j < G; ++j) {
+    const size_t row = ((size_t)i * c.dm.Hkv + h) * G + j;
+    const int cnt = min(max(blk_cnt[row], 0), k_cap);
+    for (int e = tid; e < cnt; e += 256) {
+      const int blk = blk_idx[row * k_cap + e];
+      if (blk >= 0 && blk < n_sc) atomicOr(&hb[blk >> 2], 1u << (8 * (blk & 3) + j));
+    }
+  }
+  __syncthreads();
+  const int m = (n_sc + 255) >> 8, j0 = tid * m;
+  auto mask_of = [&](int blk) -> uint32_t { return (hb[blk >> 2] >> (8 * (blk & 3))) & 0xffu; };
+  int mine = 0;
+  for (int x = 0; x < m; ++x)
+    if (j0 + x < n_sc && mask_of(j0 + x)) ++mine;
+  int slot = 0, total = 0;
+  int o = wg_scan(mine, red, slot, total);
+  const size_t unit = (size_t)seq * c.dm.Hkv + h;
+  int32_t *dst = c.sc.uni + unit * c.dm.ucap;
+  for (int x = 0; x < m; ++x) {
+    const int blk = j0 + x;
+    const uint32_t mk = blk < n_sc ? mask_of(blk) : 0u;
+    if (mk) {
+      if (o < c.dm.ucap) st_dev(&dst[o], (int32_t)((uint32_t)blk | (mk << 24)));
+      ++o;
+    }
+  }
+  if (tid == 0) st_dev(&c.sc.ucnt[unit], min(total, c.dm.ucap));
 }
 
 // attend, separate-call form: P workgroups per unit, of which the unit's
@@ -2395,11 +2520,17 @@ __global__ __launch_bounds__(256, 2) void k_attend(Ctx c, SeqBatch b, int P,
   const HeadInfo hi = c.heads[h];
   const int seq = b.seq[i];
   const UG g = unit_geom(b.len[i], hi, c.dm);
-  const int PU = unit_parts(g, P);
+  const int PU = unit_parts(g, P, c.dm);
   if (part >= PU) return;
   SelIn si;
-  si.blk = blk_idx + ((size_t)i * c.dm.Hkv + h) * k_cap;
-  si.cnt = min(min(max(blk_cnt[(size_t)i * c.dm.Hkv + h], 0), k_cap), hi.kcap);
+  if (c.dm.pqh) {  // the union of the group's sets (k_union)
+    const size_t unit = (size_t)seq * c.dm.Hkv + h;
+    si.blk = c.sc.uni + unit * c.dm.ucap;
+    si.cnt = min(max(c.sc.ucnt[unit], 0), union_blocks(g, c.dm));
+  } else {
+    si.blk = blk_idx + ((size_t)i * c.dm.Hkv + h) * k_cap;
+    si.cnt = min(min(max(blk_cnt[(size_t)i * c.dm.Hkv + h], 0), k_cap), hi.kcap);
+  }
   if (part == 0) empty_slots<D, G>(c, i, h, PU, p_cap, o_part, lse_part);
   attend_part<D, G>(c, i, seq, h, g, part, PU, q, si, o_part, lse_part, p_cap, sm, nullptr,
                     &s_cnt, NewTok(), hi);
@@ -2477,15 +2608,16 @@ __global__ __launch_bounds__(256, 2) void k_step(Ctx c, SeqBatch b, int tiles_x,
     uint32_t *lrows = reinterpret_cast<uint32_t *>(smem_raw + sizeof(TopkSmem));
     unsigned long long *tagd = c.sc.seltag + unit * c.dm.kcap;
     // the fast top-k publishes the count itself, right after the entries
-    const bool fast_done = fast && topk_fast<D, G>(c, i, seq, h, hi, g, q, blk_idx, blk_cnt, k_cap,
+    const size_t out = (size_t)i * c.dm.Hkv + h;
+    const bool fast_done = fast && topk_fast<D, G>(c, seq, unit, out, hi, g, q, blk_idx, blk_cnt, k_cap,
                                                    smem_topk, tagd, &c.sc.rtag[unit], epoch);
     if (!fast_done) {
       unsigned long long *dmask = reinterpret_cast<unsigned long long *>(lrows + lrows_words);
       if (wide_unit(g.n_sc))
-        topk_wide<D, G>(c, i, seq, h, hi, g, q, blk_idx, blk_cnt, k_cap, smem_topk, dmask,
+        topk_wide<D, G>(c, seq, unit, out, hi, g, q, blk_idx, blk_cnt, k_cap, smem_topk, dmask,
                         reinterpret_cast<int32_t *>(lrows), lrows_words, tagd, epoch);
       else
-        topk_unit<D, G>(c, i, seq, h, hi, g, q, blk_idx, blk_cnt, k_cap, smem_topk, lrows,
+        topk_unit<D, G>(c, seq, unit, out, hi, g, q, blk_idx, blk_cnt, k_cap, smem_topk, lrows,
                         lrows_words, dmask, tagd, epoch);
     }
     SD_TL(4);  // top-k done
@@ -2501,7 +2633,7 @@ __global__ __launch_bounds__(256, 2) void k_step(Ctx c, SeqBatch b, int tiles_x,
     // top-k to arrive does it; here that is usually this workgroup, which has
     // nothing else left to do
     uint32_t *dctr = &c.sc.arrive[unit * 4 + 2];
-    if (arrive_last(dctr, (unsigned)unit_parts(g, P) + 1u, &s_flag)) {
+    if (arrive_last(dctr, (unsigned)unit_parts(g, P, c.dm) + 1u, &s_flag)) {
       float *pm = reinterpret_cast<float *>(smem_raw);
       dense_maw<D, G>(c, seq, h, hi, g, new_tok(N), pm, pm + kFuseDenseLds,
                       pm + kFuseDenseLds + 4 * G);
@@ -2511,7 +2643,7 @@ __global__ __launch_bounds__(256, 2) void k_step(Ctx c, SeqBatch b, int tiles_x,
     return;
   }
   const UG g = unit_geom(N, hi, c.dm);
-  const int PU = unit_parts(g, P);
+  const int PU = unit_parts(g, P, c.dm);
   if (idx >= PU) return;
   // attention part idx of the unit; the sequence's page table is copied to LDS
   // (one batch of loads) for the selected pages
@@ -2570,7 +2702,7 @@ __global__ __launch_bounds__(256) void k_fuse(Ctx c, SeqBatch b, int with_maw, i
   const HeadInfo hi = c.heads[h];
   if (with_maw) {
     const UG g = unit_geom(b.len[i], hi, c.dm);
-    fuse_unit<D, G>(c, i, h, unit_parts(g, P), o_part, lse_part, p_cap, o, lse, sm);
+    fuse_unit<D, G>(c, i, h, unit_parts(g, P, c.dm), o_part, lse_part, p_cap, o, lse, sm);
     dense_maw<D, G>(c, b.seq[i], h, hi, g, NewTok(), sm.pm, sm.dm, sm.dz);
   } else {
     fuse_unit<D, G>(c, i, h, p_cap, o_part, lse_part, p_cap, o, lse, sm);
@@ -2653,6 +2785,17 @@ hipError_t launch_select(const Ctx &c, const SeqBatch &b, int max_blocks, const 
     hipLaunchKernelGGL((k_select<D_, G_>), dim3(grid), dim3(256), topk_bytes, st, c, b, tiles_x,
                        blk_idx, blk_cnt, k_cap, q, lrows_words);
   });
+  return hipGetLastError();
+}
+
+hipError_t launch_union(const Ctx &c, const SeqBatch &b, const int32_t *blk_idx,
+                        const int32_t *blk_cnt, int32_t k_cap, hipStream_t st) {
+  if (b.n <= 0) return hipSuccess;
+  const size_t lds = sizeof(uint32_t) * (size_t)max(1, (b.max_scored + 3) / 4);
+  if (lds > 65536) return hipErrorInvalidValue;
+  dim3 grid(c.dm.Hkv, b.n);
+  SD_DISPATCH_G(c.dm.G, hipLaunchKernelGGL((k_union<G_>), grid, dim3(256), lds, st, c, b,
+                                           blk_idx, blk_cnt, k_cap));
   return hipGetLastError();
 }
 

@@ -57,6 +57,8 @@ struct sd_ctx {
   sd_config cfg{};
   std::vector<int32_t> S, ppm;
   int D = 0, Hq = 0, Hkv = 0, G = 0, pps = 0, max_S = 0;
+  bool pqh = false;  // one selection per query head
+  int sel_rows = 0;  // selections per sequence: Hq with pqh, else Hkv
   hipStream_t stream = nullptr;
   int device = 0;
   std::vector<HeadInfo> heads;
@@ -248,6 +250,8 @@ sd_status sd_validate_config(const sd_config *cfg, char *err, size_t err_len) {
     return bad("maw_decay %g outside [0,1)", (double)cfg->maw_decay);
   if (std::isnan(cfg->maw_beta) || std::isinf(cfg->maw_beta))
     return bad("maw_beta must be finite");
+  if (cfg->select_per_query_head != 0 && cfg->select_per_query_head != 1)
+    return bad("select_per_query_head %d not in {0,1}", cfg->select_per_query_head);
   if (err && err_len) err[0] = 0;
   return SD_OK;
 #undef bad
@@ -269,6 +273,8 @@ sd_status sparse_decode_init(const sd_config *cfg, sd_ctx **out) {
   c->Hq = cfg->num_q_heads;
   c->Hkv = cfg->num_kv_heads;
   c->G = c->Hq / c->Hkv;
+  c->pqh = cfg->select_per_query_head == 1;
+  c->sel_rows = c->pqh ? c->Hq : c->Hkv;
   c->D = cfg->head_dim;
   c->pps = (int)cdiv(cfg->max_seq_len, kPage);
   c->S.assign(cfg->block_size, cfg->block_size + c->Hkv);
@@ -288,6 +294,7 @@ sd_status sparse_decode_init(const sd_config *cfg, sd_ctx **out) {
   c->heads.resize(c->Hkv);
   int64_t summ_elems = 0, maw_elems = 0;
   int key_stride = 1, sel_pages = 1;
+  int64_t ucap = 1;
   const int lm_sel0 = (int)(cdiv(cfg->sink_tokens, kPage) + cdiv(cfg->recent_window, kPage) + 1);
   for (int h = 0; h < c->Hkv; ++h) {
     HeadInfo &hi = c->heads[h];
@@ -303,7 +310,10 @@ sd_status sparse_decode_init(const sd_config *cfg, sd_ctx **out) {
     int64_t kc = std::min<int64_t>(cdiv((int64_t)hi.ppm * cfg->max_seq_len, 1000000LL * hi.S),
                                    hi.nbmax);
     hi.kcap = (int)std::max<int64_t>(kc, 1);
-    const int spg = hi.kcap * (hi.S / kPage);
+    // with one set per query head the attention reads the group's union
+    const int64_t ku = c->pqh ? std::min<int64_t>((int64_t)c->G * hi.kcap, hi.nbmax) : hi.kcap;
+    ucap = std::max<int64_t>(ucap, ku);
+    const int spg = (int)ku * (hi.S / kPage);
     sel_pages = std::max(sel_pages, spg);
     c->k_cap = std::max(c->k_cap, hi.kcap);
     c->p_cap = std::max<int32_t>(c->p_cap, (int32_t)std::max<int64_t>(1, cdiv(lm_sel0 + spg, kPartPages)));
@@ -339,17 +349,25 @@ sd_status sparse_decode_init(const sd_config *cfg, sd_ctx **out) {
   key_stride = (int)cdiv(key_stride, 256) * 256;
   c->dims.key_stride = key_stride;
   c->dims.lm_sel0 = lm_sel0;
-  c->dims.lm_cap = lm_sel0 + sel_pages;
+  c->dims.lm_cap = lm_sel0;  // the dense pages' log-masses (MAW's input)
   c->dims.kcap = c->k_cap;
+  c->dims.pqh = c->pqh ? 1 : 0;
+  c->dims.ucap = (int32_t)ucap;
 
-  // scratch
+  // scratch (the selection's per-unit arrays are per query head with one
+  // set per query head)
   const size_t per_unit = (size_t)max_seqs * c->Hkv * key_stride;
-  if ((s = dev_alloc(c, &c->sc.keys, per_unit)) != SD_OK) return s;
-  if ((s = dev_alloc(c, &c->sc.keyflag, per_unit)) != SD_OK) return s;
-  if ((s = dev_alloc(c, &c->sc.ulist, per_unit)) != SD_OK) return s;
-  if ((s = dev_alloc(c, &c->sc.ukeys, per_unit)) != SD_OK) return s;
-  if ((s = dev_alloc(c, &c->sc.unit_acc, (size_t)max_seqs * c->Hkv * 4)) != SD_OK) return s;
-  SD_HIP(c, hipMemset(c->sc.unit_acc, 0, sizeof(uint32_t) * max_seqs * c->Hkv * 4));
+  const size_t per_sel = (size_t)max_seqs * c->sel_rows * key_stride;
+  if ((s = dev_alloc(c, &c->sc.keys, per_sel)) != SD_OK) return s;
+  if ((s = dev_alloc(c, &c->sc.keyflag, per_sel)) != SD_OK) return s;
+  if ((s = dev_alloc(c, &c->sc.ulist, per_sel)) != SD_OK) return s;
+  if ((s = dev_alloc(c, &c->sc.ukeys, per_sel)) != SD_OK) return s;
+  if ((s = dev_alloc(c, &c->sc.unit_acc, (size_t)max_seqs * c->sel_rows * 4)) != SD_OK) return s;
+  SD_HIP(c, hipMemset(c->sc.unit_acc, 0, sizeof(uint32_t) * max_seqs * c->sel_rows * 4));
+  if (c->pqh) {
+    if ((s = dev_alloc(c, &c->sc.uni, (size_t)max_seqs * c->Hkv * ucap)) != SD_OK) return s;
+    if ((s = dev_alloc(c, &c->sc.ucnt, (size_t)max_seqs * c->Hkv)) != SD_OK) return s;
+  }
   if ((s = dev_alloc(c, &c->sc.lm_pg, (size_t)max_seqs * c->Hq * c->dims.lm_cap)) != SD_OK) return s;
   if ((s = dev_alloc(c, &c->sc.arrive, (size_t)max_seqs * c->Hkv * 4)) != SD_OK) return s;
   SD_HIP(c, hipMemset(c->sc.arrive, 0, sizeof(uint32_t) * max_seqs * c->Hkv * 4));
@@ -574,7 +592,11 @@ int parts_of(sd_ctx *c, int layer, const SeqBatch &b, int max_blocks) {
   int64_t P = 1;
   for (int i = 0; i < b.n; ++i)
     for (int h = 0; h < c->Hkv; ++h) {
-      const int64_t pages = dense_pages(c, b.len[i]) + k_of_seq(c, b.len[i], h) * (c->S[h] / kPage);
+      int64_t kb = k_of_seq(c, b.len[i], h);
+      if (c->pqh)  // the union of the group's sets
+        kb = std::min<int64_t>(kb * c->G, n_candidates(b.len[i], c->S[h], c->cfg.sink_tokens,
+                                                       c->cfg.recent_window));
+      const int64_t pages = dense_pages(c, b.len[i]) + kb * (c->S[h] / kPage);
       P = std::max<int64_t>(P, cdiv(pages, kPartPages));
     }
   int cap = -1;
@@ -638,8 +660,8 @@ sd_status select_topk(sd_ctx *c, int32_t layer, int32_t n_seqs,
     int mb = 0;
     fill_batch(c, layer, seq_ids, base, std::min(kLaunchSeqs, n_seqs - base), &b, &mb);
     const uint16_t *qb = q + (size_t)base * c->Hq * c->D;
-    SD_HIP(c, launch_select(kc, b, mb, qb, blk_idx + (size_t)base * c->Hkv * k_cap,
-                            blk_cnt + (size_t)base * c->Hkv, k_cap, c->stream));
+    SD_HIP(c, launch_select(kc, b, mb, qb, blk_idx + (size_t)base * c->sel_rows * k_cap,
+                            blk_cnt + (size_t)base * c->sel_rows, k_cap, c->stream));
   }
   return SD_OK;
 }
@@ -667,9 +689,12 @@ sd_status sparse_attend(sd_ctx *c, int32_t layer, int32_t n_seqs,
     fill_batch(c, layer, seq_ids, base, std::min(kLaunchSeqs, n_seqs - base), &b, &mb);
     const int P = parts_of(c, layer, b, mb);
     c->pend_parts.push_back(P);
+    if (c->pqh)
+      SD_HIP(c, launch_union(kc, b, blk_idx + (size_t)base * c->sel_rows * k_cap,
+                             blk_cnt + (size_t)base * c->sel_rows, k_cap, c->stream));
     SD_HIP(c, launch_attend(kc, b, P, q + (size_t)base * c->Hq * c->D,
-                            blk_idx + (size_t)base * c->Hkv * k_cap,
-                            blk_cnt + (size_t)base * c->Hkv, k_cap,
+                            blk_idx + (size_t)base * c->sel_rows * k_cap,
+                            blk_cnt + (size_t)base * c->sel_rows, k_cap,
                             o_part + (size_t)base * c->Hq * p_cap * c->D,
                             lse_part + (size_t)base * c->Hq * p_cap, p_cap, c->stream));
   }
@@ -740,6 +765,10 @@ sd_status decode_step_impl(sd_ctx *c, int32_t layer, int32_t n_seqs, const int32
                            const Scratch &sc, uint32_t *clear, size_t clear_words) {
   sd_status s = check_seqs(c, layer, n_seqs, seq_ids);
   if (s != SD_OK) return s;
+  if (c->pqh)
+    return fail(c, SD_EUNSUPPORTED,
+                "the one-launch step selects per KV head; with select_per_query_head use "
+                "select_topk, sparse_attend and fuse_lse");
   if (n_seqs == 0) return SD_OK;
   if (!q_bf16 || !blk_idx || !blk_cnt || !o_part || !lse_part || !o || !lse)
     return fail(c, SD_EINVAL, "a device pointer is NULL");
@@ -888,6 +917,7 @@ sd_status sd_debug_bytes(const sd_ctx *c, int32_t what, int32_t layer,
     case SD_DEBUG_K:
     case SD_DEBUG_V: b = sizeof(uint16_t) * len * c->Hkv * c->D; break;
     case SD_DEBUG_SCORES:
+      if (c->pqh) return SD_EUNSUPPORTED;  // (the keys are per query head)
       for (int h = 0; h < c->Hkv; ++h) b += sizeof(float) * (1 + cdiv(len, c->S[h]));
       break;
     default: return SD_EINVAL;

@@ -93,6 +93,17 @@ typedef struct {
   uint64_t page_shuffle_seed; /* 0: pages handed out in order; else a seeded
                                  random permutation of the free list         */
   void *stream;           /* hipStream_t; NULL = the default stream          */
+  int32_t select_per_query_head; /* 0: one block set per KV head, ranked by
+                                    the group's largest bound; 1: one set per
+                                    query head, ranked by its own bound
+                                    ([FLX] Figures 4 and 5: heads counted and
+                                    budgeted one query head at a time).  With
+                                    1, select_topk writes and sparse_attend
+                                    reads blk_idx [n][Hq][k_cap] and blk_cnt
+                                    [n][Hq]; the pages of the union of a KV
+                                    head's sets are read once, each query head
+                                    attends D and its own blocks; the
+                                    one-launch step returns SD_EUNSUPPORTED */
 } sd_config;
 
 /* Host-only check of a configuration (no device is touched).  err may be NULL;
@@ -136,7 +147,10 @@ sd_status append_kv(sd_ctx *ctx, int32_t layer, int32_t n_seqs,
  * MAW*|D| > beta*S is ranked before all others ([HGCA] threshold).  Order:
  * (flag desc, score desc, index asc); the first k are written ascending.
  * q_bf16: dev [n_seqs][Hq][d].  blk_idx: dev [n_seqs][Hkv][k_cap] int32
- * (entries past the count are left untouched).  blk_cnt: dev [n_seqs][Hkv]. */
+ * (entries past the count are left untouched).  blk_cnt: dev [n_seqs][Hkv].
+ * With select_per_query_head each query head h ranks by its own U_h (the
+ * same k, flags and order) and blk_idx / blk_cnt are [n_seqs][Hq][k_cap] /
+ * [n_seqs][Hq]. */
 sd_status select_topk(sd_ctx *ctx, int32_t layer, int32_t n_seqs,
                       const int32_t *seq_ids, const void *q_bf16,
                       int32_t *blk_idx, int32_t *blk_cnt, int32_t k_cap);
@@ -151,7 +165,12 @@ sd_status select_topk(sd_ctx *ctx, int32_t layer, int32_t n_seqs,
  * select_topk (ascending, distinct; a repeated entry would count its tokens
  * twice); entries outside [0, n_blk) attend nothing.  The log softmax mass of
  * each dense page, which fuse_lse needs for MAW, is kept inside the context
- * for this layer. */
+ * for this layer.
+ * With select_per_query_head, blk_idx / blk_cnt are per query head (as
+ * select_topk writes them): query head h attends D U tokens(its own
+ * entries); the union of a KV head's sets is formed first (entries outside
+ * the blocks that can hold a candidate are dropped, repeats count once) and
+ * its pages are read once for the whole group. */
 sd_status sparse_attend(sd_ctx *ctx, int32_t layer, int32_t n_seqs,
                         const int32_t *seq_ids, const void *q_bf16,
                         const int32_t *blk_idx, const int32_t *blk_cnt,
@@ -255,7 +274,8 @@ const char *sd_last_error(const sd_ctx *ctx);
  *                        score that selection ranked (the fp32 value of its
  *                        order key); NaN for blocks that were not scored as
  *                        candidates, and everywhere on a head that selects
- *                        nothing.  Every scored block's exact score lies
+ *                        nothing (SD_EUNSUPPORTED with one selection per
+ *                        query head).  Every scored block's exact score lies
  *                        within eps of its approximate one ([LFPS] Core claim:
  *                        the selection is the exact top-k; blocks within the
  *                        band of the k-th are re-scored exactly).  Valid right

@@ -42,7 +42,7 @@ def log(msg):
 
 
 def make_engine(w: synth.Workload, N_max: int, *, layers=1, shuffle_seed=0,
-                max_seqs=None, extra_pages=0, maw_beta=None):
+                max_seqs=None, extra_pages=0, maw_beta=None, per_query_head=False):
     pages = w.B * ((N_max + 15) // 16) + extra_pages
     return SparseDecode(max_seqs=max_seqs or w.B, num_layers=layers,
                         num_q_heads=w.Hq, num_kv_heads=w.Hkv, head_dim=w.d,
@@ -51,7 +51,8 @@ def make_engine(w: synth.Workload, N_max: int, *, layers=1, shuffle_seed=0,
                         block_size=w.block_size, budget_ppm=w.budget_ppm,
                         maw_decay=w.maw_decay,
                         maw_beta=w.maw_beta if maw_beta is None else maw_beta,
-                        page_shuffle_seed=shuffle_seed)
+                        page_shuffle_seed=shuffle_seed,
+                        select_per_query_head=1 if per_query_head else 0)
 
 
 def prefill(eng, layer, K, V, seq_ids=None, chunks=1):
