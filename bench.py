@@ -83,6 +83,10 @@ def parse():
     ap.add_argument("--streaming-heads", type=int, default=0,
                     help="give the first K KV heads budget 0 (streaming heads: sinks and "
                          "recent window only); a variant of the workload, not the headline")
+    ap.add_argument("--per-query-head", action="store_true",
+                    help="one block set per query head (select_per_query_head): the separate "
+                         "calls select_topk, sparse_attend (with the union of each KV head's "
+                         "sets) and fuse_lse; the kernel split is timed per call")
     ap.add_argument("--timeline", type=int, default=0, metavar="STEPS",
                     help="measurement build only (build.py --timeline): record the per-phase "
                          "timestamps of STEPS one-launch steps after the warm-up, print their "
@@ -162,7 +166,9 @@ def measured_traffic():
 def algorithmic_bytes(w, N, blk_cnt, blk_idx, with_maw=True):
     """Per-step algorithmic HBM bytes (each term counted once):
     summaries n_blk*2*d*2 per (seq, kv head) that selects; K+V of the distinct
-    attended tokens |T|*2*d*2; MAW: the flag's read of every block, n_blk*4,
+    attended tokens |T|*2*d*2 (with one set per query head, T = D U the union
+    of the group's sets: a KV page is read once for the whole group); MAW: the
+    flag's read of every block, n_blk*4,
     when the flag is on (with_maw), plus the update of the blocks wholly inside
     the dense set, 4*2 each; q 2d, O 4d, lse 4 per query head.  Scratch and
     page tables are excluded."""
@@ -171,7 +177,12 @@ def algorithmic_bytes(w, N, blk_cnt, blk_idx, with_maw=True):
         for g in range(w.Hkv):
             S = w.block_size[g]
             nb = (N + S - 1) // S
-            sel = blk_idx[b, g, :blk_cnt[b, g]]
+            if blk_idx.shape[1] == w.Hq:  # one set per query head: their union
+                G = w.G
+                sel = np.unique(np.concatenate(
+                    [blk_idx[b, g * G + j, :blk_cnt[b, g * G + j]] for j in range(G)]))
+            else:
+                sel = blk_idx[b, g, :blk_cnt[b, g]]
             inD = np.zeros(N, bool)
             inD[:min(w.n_sink, N)] = True
             inD[max(0, N - w.window):] = True
@@ -210,6 +221,8 @@ def main():
     w = {"llama32k": synth.llama32k, "qwen128k": lambda: synth.qwen128k(0),
          "loop32": synth.loop32, "sweep": lambda: dataclasses.replace(synth.sweep(*args.sweep), N=args.sweep_n)}[args.workload]()
     maw_beta = w.maw_beta  # MAW flags on for loop32 only
+    if args.per_query_head:
+        args.fused = 0  # the one-launch step selects per KV head
     if args.streaming_heads:
         K_s = min(args.streaming_heads, w.Hkv)
         w = dataclasses.replace(w, budget_ppm=[0] * K_s + list(w.budget_ppm[K_s:]))
@@ -223,7 +236,8 @@ def main():
                        sink_tokens=w.n_sink, recent_window=w.window,
                        block_size=w.block_size, budget_ppm=w.budget_ppm,
                        maw_decay=0.95, maw_beta=maw_beta,
-                       page_shuffle_seed=12345, stream=stream)
+                       page_shuffle_seed=12345, stream=stream,
+                       select_per_query_head=1 if args.per_query_head else 0)
     seqs = list(range(w.B))
     dirs_l = {}
     t0 = time.time()
@@ -310,28 +324,55 @@ def main():
     N_now = eng.seq_len(l_last, 0)
     cnt, idx = last["blk_cnt"], last["blk_idx"]
 
-    # k_step timed alone: n_inst back-to-back steps without append (so k_step
-    # is the only kernel) between two HIP events on the library's stream
+    # the dominant kernel timed alone: n_inst back-to-back launches between two
+    # HIP events on the library's stream, rotating layers so that the working
+    # set stays out of the last-level cache
     n_inst = 64
-    ea = torch.cuda.Event(enable_timing=True)
-    eb = torch.cuda.Event(enable_timing=True)
-    torch.cuda.synchronize()
-    ea.record(stream)
-    for i in range(n_inst):
-        layer = i % L  # rotate layers: the working set stays out of the LLC
-        eng.decode_step(layer, seqs, q_pool[i], bufs["blk_idx"], bufs["blk_cnt"],
-                        bufs["o_part"], bufs["lse_part"], bufs["o"], bufs["lse"])
-    eb.record(stream)
-    torch.cuda.synchronize()
-    eng.sync()
-    t_step = ea.elapsed_time(eb) / n_inst
+
+    def timed_loop(fn):
+        ea = torch.cuda.Event(enable_timing=True)
+        eb = torch.cuda.Event(enable_timing=True)
+        torch.cuda.synchronize()
+        ea.record(stream)
+        for i in range(n_inst):
+            fn(i)
+        eb.record(stream)
+        torch.cuda.synchronize()
+        eng.sync()
+        return ea.elapsed_time(eb) / n_inst
 
     ab = algorithmic_bytes(w, N_now, cnt, idx, with_maw=maw_beta > 0)
+    if args.per_query_head:
+        # select_topk alone, then sparse_attend (union + attention) alone on
+        # each layer's own selection (no append in between)
+        sel_bufs = [eng.alloc_step(w.B, device=dev) for _ in range(L)]
+        t_sel = timed_loop(lambda i: eng.select_topk(i % L, seqs, q_pool[i % L],
+                                                     sel_bufs[i % L]["blk_idx"],
+                                                     sel_bufs[i % L]["blk_cnt"]))
+        t_att = timed_loop(lambda i: eng.sparse_attend(i % L, seqs, q_pool[i % L],
+                                                       sel_bufs[i % L]["blk_idx"],
+                                                       sel_bufs[i % L]["blk_cnt"],
+                                                       bufs["o_part"], bufs["lse_part"]))
+        l_att = (n_inst - 1) % L
+        eng.fuse_lse(l_att, seqs, bufs["o_part"], bufs["lse_part"], bufs["o"], bufs["lse"])
+        eng.sync()
+        kernel_ms = {"select_topk": t_sel, "sparse_attend (k_union + k_attend)": t_att,
+                     "timed_launches": n_inst}
+        dom_name, t_dom = "k_union + k_attend", t_att
+        kstep_bytes = ab["attend"]  # the attention's K+V of the union's tokens
+        sel_gbs = ab["summaries"] / (t_sel * 1e-3) / 1e9
+    else:
+        # k_step: steps without append, so that it is the only kernel
+        t_step = timed_loop(lambda i: eng.decode_step(i % L, seqs, q_pool[i], bufs["blk_idx"],
+                                                      bufs["blk_cnt"], bufs["o_part"],
+                                                      bufs["lse_part"], bufs["o"], bufs["lse"]))
+        kernel_ms = {"k_step": t_step, "timed_launches": n_inst}
+        dom_name, t_dom = "k_step", t_step
+        kstep_bytes = ab["total"]  # k_step moves every algorithmic byte of the step
     qheads = w.B * w.Hq
     value = qheads / (ms * 1e-3)
     step_gbs = ab["total"] / (ms * 1e-3) / 1e9
-    kstep_bytes = ab["total"]  # k_step moves every algorithmic byte of the step
-    kstep_gbs = kstep_bytes / (t_step * 1e-3) / 1e9
+    kstep_gbs = kstep_bytes / (t_dom * 1e-3) / 1e9
 
     out = {
         "metric": "sparse-decode attn query-heads/s at Llama-3-8B 32K, 5% budget; % HBM peak",
@@ -353,21 +394,28 @@ def main():
                                + ("; KV heads 0-%d streaming (budget 0)" % (args.streaming_heads - 1)
                                   if args.streaming_heads else ""),
                    "global_batch": w.B, "seq_len": w.N, "parallelism": "none (1 GPU)",
-                   "fused_step": bool(args.fused)},
+                   "fused_step": bool(args.fused),
+                   "selection": "per query head" if args.per_query_head else "per KV head"},
         "step_hbm": {"algorithmic_bytes": ab["total"], "achieved_GBs": step_gbs,
                      "frac_of_8TBs": step_gbs / HBM_PEAK_GBS,
                      "breakdown_bytes": {k: ab[k] for k in ("summaries", "attend", "maw", "q_o_lse")}},
-        "kernel_ms": {"k_step": t_step, "timed_launches": n_inst},
-        "roofline": {"kernel": "k_step", "bound": "hbm", "achieved": kstep_gbs,
+        "kernel_ms": kernel_ms,
+        "roofline": {"kernel": dom_name, "bound": "hbm", "achieved": kstep_gbs,
                      "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": kstep_gbs / HBM_PEAK_GBS,
                      # the committed counter summary is the headline workload's
                      "traffic": measured_traffic() if args.workload == "llama32k"
-                     and not args.streaming_heads else None,
+                     and not args.streaming_heads and not args.per_query_head else None,
                      "algorithmic_bytes_per_launch": kstep_bytes},
         "trials_ms": trial_ms,
         "setup_s": setup_s,
     }
 
+    if args.per_query_head:
+        out["select_topk_GBs"] = sel_gbs
+        out["union_vs_group"] = {
+            "attended_bytes_per_query_head_set": ab["attend"],
+            "note": "K+V bytes of D U the union of each KV head's query-head sets; "
+                    "the per-KV-head selection of the same step reads D U k blocks"}
     out["read_ceiling"] = read_ceiling(kstep_bytes, kstep_gbs)
     parity_ok = True
     if args.cpu_baseline:
@@ -382,7 +430,8 @@ def main():
         torch.cuda.empty_cache()
         out["cpu_baseline"], out["parity"] = cpu_baseline_and_parity(
             w, Kb, Vb, synth.bits(q_pool[s_last]), N_now, last, args.cpu_seconds,
-            check=bool(args.parity) and maw_beta <= 0.0, step_index=s_last)
+            check=bool(args.parity) and maw_beta <= 0.0, step_index=s_last,
+            per_query_head=args.per_query_head)
         parity_ok = out["parity"].get("pass", True)
     print(json.dumps(out), flush=True)
     eng.close()
@@ -519,7 +568,8 @@ def cpu_model():
     return "unknown"
 
 
-def cpu_baseline_and_parity(w, Kb, Vb, qb, N, gpu, budget_s, check=True, step_index=-1):
+def cpu_baseline_and_parity(w, Kb, Vb, qb, N, gpu, budget_s, check=True, step_index=-1,
+                            per_query_head=False):
     """The CPU-baseline leg: the CPU oracle (unchanged) on the inputs of the
     last timed step (every (sequence, KV head) unit; bf16 bits rebuilt from the
     seeds, none read back from the GPU).  Summaries are computed first, outside
@@ -529,7 +579,9 @@ def cpu_baseline_and_parity(w, Kb, Vb, qb, N, gpu, budget_s, check=True, step_in
     seconds.  The oracle's results of the first pass over the units also serve
     the parity check of the GPU's outputs of that step (check=True): selection
     bit-exact except ties inside the 1e-6 relative score band, max |dO| <=
-    2e-3, max relative dO <= 1e-2 where |O| >= 0.1, |dlse| <= 1e-4."""
+    2e-3, max relative dO <= 1e-2 where |O| >= 0.1, |dlse| <= 1e-4.
+    per_query_head: the oracle's per-query-head selection and attention, and
+    the same check per query head."""
     import concurrent.futures as cf
     import oracle
     G = w.G
@@ -541,6 +593,11 @@ def cpu_baseline_and_parity(w, Kb, Vb, qb, N, gpu, budget_s, check=True, step_in
     def run(u):
         b, g = u
         S, qg = w.block_size[g], qb[b, g * G:(g + 1) * G]
+        if per_query_head:
+            sels = oracle.select_heads(qg, summ[u][0], summ[u][1], N, S, w.n_sink, w.window,
+                                       w.budget_ppm[g])
+            O, lse = oracle.attend_heads(qg, Kg[u], Vg[u], N, S, w.n_sink, w.window, sels)
+            return u, dict(sels=sels), dict(O=O, lse=lse)
         r = oracle.select(qg, summ[u][0], summ[u][1], N, S, w.n_sink, w.window, w.budget_ppm[g])
         a = oracle.attend(qg, Kg[u], Vg[u], N, S, w.n_sink, w.window, r["sel"])
         return u, r, a
@@ -561,8 +618,9 @@ def cpu_baseline_and_parity(w, Kb, Vb, qb, N, gpu, budget_s, check=True, step_in
     done1, dt1, _ = timed(1)
     base = {"value": done * G / dt, "unit": "query-heads/s", "cores": threads, "kind": "oracle",
             "sample": "%d (sequence, KV head) units (%d full steps) of the %s step at N=%d, "
-                      "oracle select + attend on precomputed summaries, %d threads, %.1f s"
-                      % (done, done // len(units), w.name, N, threads, dt),
+                      "oracle select + attend%s on precomputed summaries, %d threads, %.1f s"
+                      % (done, done // len(units), w.name, N,
+                         " per query head" if per_query_head else "", threads, dt),
             "ms_per_step": dt / (done / len(units)) * 1e3,
             "t1": {"value": done1 * G / dt1, "cores": 1,
                    "ms_per_step": dt1 / (done1 / len(units)) * 1e3,
@@ -575,24 +633,48 @@ def cpu_baseline_and_parity(w, Kb, Vb, qb, N, gpu, budget_s, check=True, step_in
     ties = 0
     ma = mr = ml = 0.0
     fails = []
+    if per_query_head:
+        # one row per query head: (selection, oracle result) pairs
+        flat = []
+        for (b, g), r, a in results:
+            S, qg = w.block_size[g], qb[b, g * G:(g + 1) * G]
+            Uh, _, _ = oracle.score(qg, summ[(b, g)][0], summ[(b, g)][1])
+            gs = []
+            for j in range(G):
+                cnt = int(gpu["blk_cnt"][b, g * G + j])
+                gsel, osel = set(gpu["blk_idx"][b, g * G + j, :cnt].tolist()), set(r["sels"][j].tolist())
+                if cnt != len(osel):
+                    fails.append("head (%d,%d): k %d vs %d" % (b, g * G + j, cnt, len(osel)))
+                elif gsel != osel:
+                    kth = min(Uh[j][i] for i in osel)
+                    if not all(abs(Uh[j][i] - kth) <= 1e-6 * max(abs(Uh[j][i]), abs(kth), 1e-30)
+                               for i in gsel ^ osel):
+                        fails.append("head (%d,%d): selection differs outside the tie band"
+                                     % (b, g * G + j))
+                    ties += len(gsel ^ osel) // 2
+                gs.append(np.array(sorted(gsel), np.int32))
+            O, lse = oracle.attend_heads(qg, Kg[(b, g)], Vg[(b, g)], N, S, w.n_sink, w.window, gs)
+            flat.append(((b, g), dict(O=O, lse=lse)))
+        results = [(u, None, a) for u, a in flat]
     for (b, g), r, a in results:
-        cnt = int(gpu["blk_cnt"][b, g])
-        gsel = set(gpu["blk_idx"][b, g, :cnt].tolist())
-        osel = set(r["sel"].tolist())
-        if cnt != r["k"]:
-            fails.append("unit (%d,%d): k %d vs %d" % (b, g, cnt, r["k"]))
-            continue
-        if gsel != osel:
-            kth = min(r["U"][i] for i in osel)
-            band = all(abs(r["U"][i] - kth) <= 1e-6 * max(abs(r["U"][i]), abs(kth), 1e-30)
-                       for i in gsel ^ osel)
-            if not band:
-                fails.append("unit (%d,%d): selection differs outside the tie band" % (b, g))
+        if not per_query_head:
+            cnt = int(gpu["blk_cnt"][b, g])
+            gsel = set(gpu["blk_idx"][b, g, :cnt].tolist())
+            osel = set(r["sel"].tolist())
+            if cnt != r["k"]:
+                fails.append("unit (%d,%d): k %d vs %d" % (b, g, cnt, r["k"]))
                 continue
-            ties += len(gsel ^ osel) // 2
-            a = oracle.attend(qb[b, g * G:(g + 1) * G], Kg[(b, g)], Vg[(b, g)], N,
-                              w.block_size[g], w.n_sink, w.window,
-                              np.array(sorted(gsel), np.int32))
+            if gsel != osel:
+                kth = min(r["U"][i] for i in osel)
+                band = all(abs(r["U"][i] - kth) <= 1e-6 * max(abs(r["U"][i]), abs(kth), 1e-30)
+                           for i in gsel ^ osel)
+                if not band:
+                    fails.append("unit (%d,%d): selection differs outside the tie band" % (b, g))
+                    continue
+                ties += len(gsel ^ osel) // 2
+                a = oracle.attend(qb[b, g * G:(g + 1) * G], Kg[(b, g)], Vg[(b, g)], N,
+                                  w.block_size[g], w.n_sink, w.window,
+                                  np.array(sorted(gsel), np.int32))
         Og = gpu["o"][b, g * G:(g + 1) * G].astype(np.float64)
         dO = np.abs(Og - a["O"])
         ma = max(ma, float(dO.max()))

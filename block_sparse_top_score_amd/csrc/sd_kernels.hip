@@ -2425,28 +2425,17 @@ __global__ __launch_bounds__(256) void k_select(Ctx c, SeqBatch b, int tiles_x,
     return;
   }
   UG g;
-  if (c.dm.pqh)
+  if (c.dm.pqh) {  // the query heads' top-ks run in the next launch (k_topk_heads)
     score_tile<D, G, true>(c, i, seq, h, hi, N, n_blk, tile, q, smem_topk, false, g);
-  else
-    score_tile<D, G>(c, i, seq, h, hi, N, n_blk, tile, q, smem_topk, false, g);
+    return;
+  }
+  score_tile<D, G>(c, i, seq, h, hi, N, n_blk, tile, q, smem_topk, false, g);
   uint32_t *ctr = &c.sc.arrive[((size_t)seq * c.dm.Hkv + h) * 4];
   if (!arrive_last(ctr, (unsigned)n_tiles, &smem_topk.last)) return;
   uint32_t *lrows = reinterpret_cast<uint32_t *>(smem_raw + sizeof(TopkSmem));
   unsigned long long *dmask = reinterpret_cast<unsigned long long *>(lrows + lrows_words);
   const size_t unit = (size_t)seq * c.dm.Hkv + h, out = (size_t)i * c.dm.Hkv + h;
-  if (c.dm.pqh) {
-    // one top-k per query head of the group, each over that head's own keys
-    // and exact scores (a group of one head)
-    for (int j = 0; j < G; ++j) {
-      if (wide_unit(g.n_sc))
-        topk_wide<D, 1>(c, seq, unit * G + j, out * G + j, hi, g, q, blk_idx, blk_cnt, k_cap,
-                        smem_topk, dmask, reinterpret_cast<int32_t *>(lrows), lrows_words);
-      else
-        topk_unit<D, 1>(c, seq, unit * G + j, out * G + j, hi, g, q, blk_idx, blk_cnt, k_cap,
-                        smem_topk, lrows, lrows_words, dmask);
-      __syncthreads();
-    }
-  } else if (wide_unit(g.n_sc)) {
+  if (wide_unit(g.n_sc)) {
     topk_wide<D, G>(c, seq, unit, out, hi, g, q, blk_idx, blk_cnt, k_cap, smem_topk, dmask,
                     reinterpret_cast<int32_t *>(lrows), lrows_words);
   } else {
@@ -2454,6 +2443,32 @@ __global__ __launch_bounds__(256) void k_select(Ctx c, SeqBatch b, int tiles_x,
                     lrows_words, dmask);
   }
   if (threadIdx.x == 0) st_dev(ctr, 0u);
+}
+
+// Top-k of one query head with one selection per query head (grid: G query
+// heads x KV heads x sequences, after k_select has scored every block per
+// query head): that head's own keys, bound and exact scores, a group of one.
+template <int D, int G>
+__global__ __launch_bounds__(256) void k_topk_heads(Ctx c, SeqBatch b, int32_t *__restrict__ blk_idx,
+                                                    int32_t *__restrict__ blk_cnt, int k_cap,
+                                                    const uint16_t *__restrict__ q,
+                                                    int lrows_words) {
+  extern __shared__ __align__(16) unsigned char smem_raw[];
+  TopkSmem &smem_topk = *reinterpret_cast<TopkSmem *>(smem_raw);
+  const int j = blockIdx.x % G, h = (blockIdx.x / G) % c.dm.Hkv, i = blockIdx.x / (G * c.dm.Hkv);
+  const HeadInfo hi = c.heads[h];
+  const int seq = b.seq[i], N = b.len[i];
+  if (selects_nothing(hi, N, c.dm)) return;  // (k_select wrote the count 0)
+  const UG g = unit_geom(N, hi, c.dm);
+  const size_t unit = ((size_t)seq * c.dm.Hkv + h) * G + j, out = ((size_t)i * c.dm.Hkv + h) * G + j;
+  uint32_t *lrows = reinterpret_cast<uint32_t *>(smem_raw + sizeof(TopkSmem));
+  unsigned long long *dmask = reinterpret_cast<unsigned long long *>(lrows + lrows_words);
+  if (wide_unit(g.n_sc))
+    topk_wide<D, 1>(c, seq, unit, out, hi, g, q, blk_idx, blk_cnt, k_cap, smem_topk, dmask,
+                    reinterpret_cast<int32_t *>(lrows), lrows_words);
+  else
+    topk_unit<D, 1>(c, seq, unit, out, hi, g, q, blk_idx, blk_cnt, k_cap, smem_topk, lrows,
+                    lrows_words, dmask);
 }
 
 // Union of a KV head's per-query-head selections (one workgroup per
@@ -2784,6 +2799,9 @@ hipError_t launch_select(const Ctx &c, const SeqBatch &b, int max_blocks, const 
   SD_DISPATCH_DG(c.dm.d, c.dm.G, {
     hipLaunchKernelGGL((k_select<D_, G_>), dim3(grid), dim3(256), topk_bytes, st, c, b, tiles_x,
                        blk_idx, blk_cnt, k_cap, q, lrows_words);
+    if (c.dm.pqh)
+      hipLaunchKernelGGL((k_topk_heads<D_, G_>), dim3(G_ * c.dm.Hkv * b.n), dim3(256), topk_bytes,
+                         st, c, b, blk_idx, blk_cnt, k_cap, q, lrows_words);
   });
   return hipGetLastError();
 }
