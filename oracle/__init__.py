@@ -75,6 +75,18 @@ def lib():
         L.oracle_attend_heads.restype = None
         L.oracle_attend_heads.argtypes = [P, i32, i32, P, i64, P, i64, i64, i32, i32,
                                           i32, P, i64, P, dbl, P, P]
+        L.oracle_lfps_candidates.restype = i64
+        L.oracle_lfps_candidates.argtypes = [P, P, i64, i32, i32, i32, dbl, P]
+        L.oracle_lfps_select.restype = i64
+        L.oracle_lfps_select.argtypes = [P, i32, i32, P, P, i64, i32, i32, i32, i64,
+                                         P, P, dbl, P, P, P]
+        L.oracle_attend_mass.restype = None
+        L.oracle_attend_mass.argtypes = [P, i32, i32, P, i64, i64, i32, i32, i32, P, i64,
+                                         dbl, P]
+        L.oracle_lfps_update.restype = None
+        L.oracle_lfps_update.argtypes = [P, P, P, i64, dbl]
+        L.oracle_lfps_init.restype = None
+        L.oracle_lfps_init.argtypes = [P, i32, i32, i32, P, i64, i64, i32, dbl, dbl, P, P]
         L.oracle_attend_tokens.restype = None
         L.oracle_attend_tokens.argtypes = [P, i32, i32, P, i64, P, i64, P, i64,
                                            dbl, P, P, P]
@@ -213,6 +225,73 @@ def attend_heads(q, K, V, N, S, n_s, W, sels, scale=None):
                               N, S, n_s, W, _p(sel), ld, _p(k), float(scale),
                               _p(O), _p(lse))
     return O, lse
+
+
+def _f64(a, n):
+    a = np.ascontiguousarray(a, dtype=np.float64)
+    assert a.shape[0] >= n
+    return a
+
+
+def lfps_candidates(phi_v, phi_s, N, S, n_s, W, a=0.2):
+    """Block mask of the table candidates C and |C|."""
+    nb = num_blocks(N, S)
+    pv, ps = _f64(phi_v, nb), _f64(phi_s, nb)
+    inC = np.zeros(max(nb, 1), np.int8)
+    n = lib().oracle_lfps_candidates(_p(pv), _p(ps), N, S, n_s, W, float(a), _p(inC))
+    return inC[:nb].astype(bool), int(n)
+
+
+def lfps_select(q, mn, mx, N, S, n_s, W, budget_ppm, phi_v, phi_s, a=0.2):
+    """Selection among the table candidates: dict(sel, U, u, k)."""
+    q, mn, mx = _u16(q), _u16(mn), _u16(mx)
+    G, d = q.shape
+    nb = num_blocks(N, S)
+    assert mn.shape == (nb, d) and mx.shape == (nb, d)
+    pv, ps = _f64(phi_v, nb), _f64(phi_s, nb)
+    sel = np.zeros(max(nb, 1), np.int32)
+    U = np.zeros(max(nb, 1), np.float64)
+    u = np.zeros(max(nb, 1), np.float32)
+    k = lib().oracle_lfps_select(_p(q), G, d, _p(mn), _p(mx), N, S, n_s, W, int(budget_ppm),
+                                 _p(pv), _p(ps), float(a), _p(sel), _p(U), _p(u))
+    return dict(sel=sel[:k].copy(), U=U[:nb], u=u[:nb], k=int(k))
+
+
+def attend_mass(q, K, N, S, n_s, W, sel, scale=None):
+    """Per-block mass under the softmax over D U blocks(sel), group mean."""
+    q, K = _u16(q), _u16(K)
+    G, d = q.shape
+    sel = np.ascontiguousarray(sel, dtype=np.int32)
+    if scale is None:
+        scale = 1.0 / np.sqrt(d)
+    nb = num_blocks(N, S)
+    a = np.zeros(max(nb, 1), np.float64)
+    lib().oracle_attend_mass(_p(q), G, d, _p(K), K.shape[1], N, S, n_s, W, _p(sel),
+                             sel.shape[0], float(scale), _p(a))
+    return a[:nb]
+
+
+def lfps_update(phi_v, phi_s, a_blk, r=0.95):
+    """Copies of the tables after one step's update (n_blk = len(a_blk))."""
+    nb = len(a_blk)
+    pv, ps = _f64(phi_v, nb).copy(), _f64(phi_s, nb).copy()
+    a = np.ascontiguousarray(a_blk, dtype=np.float64)
+    lib().oracle_lfps_update(_p(pv), _p(ps), _p(a), nb, float(r))
+    return pv, ps
+
+
+def lfps_init(q_prefill, K, N, S, r=0.95, scale=None):
+    """Tables [n_blk] from the last s prefill positions (q_prefill: [s][G][d])."""
+    q, K = _u16(q_prefill), _u16(K)
+    s_, G, d = q.shape
+    if scale is None:
+        scale = 1.0 / np.sqrt(d)
+    nb = num_blocks(N, S)
+    pv = np.zeros(max(nb, 1), np.float64)
+    ps = np.zeros(max(nb, 1), np.float64)
+    lib().oracle_lfps_init(_p(q), s_, G, d, _p(K), K.shape[1], N, S, float(scale), float(r),
+                           _p(pv), _p(ps))
+    return pv[:nb], ps[:nb]
 
 
 def attend_tokens(q, K, V, tok, scale=None, want_p=False):

@@ -26,6 +26,16 @@
  *   oracle_select_heads   pinned: brute force over all k-subsets per head at
  *                         G = 3, independence of the heads, equal rows give
  *                         the group selection
+ *   oracle_lfps_candidates pinned: hand fixture (thresholds, growth by the
+ *                         offsets, the mean filter, slash offsets, candidates)
+ *   oracle_lfps_select    pinned: brute force over all k-subsets of C; equals
+ *                         oracle_select when C holds that selection
+ *   oracle_attend_mass    pinned: numpy softmax over T summed per block;
+ *                         mass conservation
+ *   oracle_lfps_update /
+ *   oracle_lfps_init      pinned: closed forms of the decay, slash offsets of
+ *                         an impulse, init of one and two prefill positions
+ *                         against numpy softmax masses
  *   oracle_attend_heads   pinned: each head over its own token list by
  *                         oracle_attend_tokens; full budget equals the
  *                         independent dense softmax for every head
@@ -311,6 +321,167 @@ void oracle_attend_heads(const uint16_t *q, int32_t G, int32_t d,
   for (int32_t h = 0; h < G; ++h)
     oracle_attend(q + (int64_t)h * d, 1, d, K, ldk, V, ldv, N, S, n_s, W,
                   sel + (int64_t)h * ld_sel, k[h], scale, O + (int64_t)h * d, lse + h);
+}
+
+/* Learn from the past ([LFPS] What carries the argument: a vertical table per
+ * absolute position and a slash table per relative position, decayed by r =
+ * 0.95 after every step; Figure 4: thresholds and means of the two tables,
+ * initial candidates above the thresholds, grown by the offsets {-1, 0, 1, 2},
+ * keeping the grown indices whose scores exceed the means; Assumptions & free
+ * parameters: a = 0.2 sets the threshold).  Readings: positions are blocks of
+ * S tokens and the slash offset is counted from the newest token's block; the
+ * threshold's kurtosis estimator is not given, so tau interpolates between the
+ * table's mean and maximum by a; a kept block must also hold a token outside
+ * D (the dense tokens are attended anyway). */
+static void lfps_stats(const double *phi, int64_t n, double *mu, double *mx) {
+  double sum = 0.0, m = -INFINITY;
+  for (int64_t i = 0; i < n; ++i) {
+    sum += phi[i];
+    if (phi[i] > m) m = phi[i];
+  }
+  *mu = n > 0 ? sum / (double)n : 0.0;
+  *mx = n > 0 ? m : 0.0;
+}
+
+int64_t oracle_lfps_candidates(const double *phi_v, const double *phi_s, int64_t N,
+                               int32_t S, int32_t n_s, int32_t W, double a,
+                               int8_t *inC) {
+  int64_t n_blk = oracle_num_blocks(N, S);
+  if (n_blk == 0) return 0;
+  int64_t b = n_blk - 1;
+  double mu_v, mx_v, mu_s, mx_s;
+  lfps_stats(phi_v, b + 1, &mu_v, &mx_v);
+  lfps_stats(phi_s, b + 1, &mu_s, &mx_s);
+  double tau_v = mu_v + a * (mx_v - mu_v), tau_s = mu_s + a * (mx_s - mu_s);
+  int8_t *c0 = (int8_t *)calloc(n_blk, 1);
+  int8_t *cand = (int8_t *)malloc(n_blk);
+  for (int64_t i = 0; i <= b; ++i) c0[i] = (int8_t)(phi_v[i] > tau_v || phi_s[b - i] > tau_s);
+  oracle_candidates(N, S, n_s, W, cand);
+  int64_t n = 0;
+  for (int64_t i = 0; i < n_blk; ++i) {
+    int grown = 0;
+    for (int e = -1; e <= 2; ++e) {  /* i = c + e for some c in C0 */
+      int64_t c = i - e;
+      if (c >= 0 && c <= b && c0[c]) grown = 1;
+    }
+    int above = phi_v[i] > mu_v || phi_s[b - i] > mu_s;
+    inC[i] = (int8_t)(grown && above && cand[i]);
+    n += inC[i];
+  }
+  free(c0);
+  free(cand);
+  return n;
+}
+
+int64_t oracle_lfps_select(const uint16_t *q, int32_t G, int32_t d,
+                           const uint16_t *mn, const uint16_t *mx, int64_t N,
+                           int32_t S, int32_t n_s, int32_t W, int64_t budget_ppm,
+                           const double *phi_v, const double *phi_s, double a,
+                           int32_t *sel, double *U, float *u) {
+  int64_t n_blk = oracle_num_blocks(N, S);
+  if (n_blk == 0) return 0;
+  double *U_ = (double *)malloc(sizeof(double) * n_blk);
+  float *u_ = (float *)malloc(sizeof(float) * n_blk);
+  int8_t *f_ = (int8_t *)calloc(n_blk, 1);
+  int8_t *inC = (int8_t *)malloc(n_blk);
+  int32_t *order = (int32_t *)malloc(sizeof(int32_t) * n_blk);
+  oracle_score(q, G, d, mn, mx, n_blk, NULL, U_, u_);
+  for (int64_t i = 0; i < n_blk; ++i)
+    if (u_[i] == 0.0f) u_[i] = 0.0f;
+  int64_t nC = oracle_lfps_candidates(phi_v, phi_s, N, S, n_s, W, a, inC);
+  int64_t k = oracle_num_selected(N, S, budget_ppm, nC);
+  int64_t m = 0;
+  for (int64_t i = 0; i < n_blk; ++i)
+    if (inC[i]) order[m++] = (int32_t)i;
+  g_order.u = u_;
+  g_order.flag = f_;
+  qsort(order, (size_t)m, sizeof(int32_t), cmp_blocks);
+  for (int64_t t = 0; t < k; ++t) sel[t] = order[t];
+  qsort(sel, (size_t)k, sizeof(int32_t), cmp_int32);
+  if (U) memcpy(U, U_, sizeof(double) * n_blk);
+  if (u) memcpy(u, u_, sizeof(float) * n_blk);
+  free(U_);
+  free(u_);
+  free(f_);
+  free(inC);
+  free(order);
+  return k;
+}
+
+/* The mass each block receives under the softmax over the attended set
+ * ([LFPS] the tables aggregate the step's attention weights; reading of their
+ * "half-normalised" weights: normalised over the tokens the step attends,
+ * averaged over the group's query heads). */
+void oracle_attend_mass(const uint16_t *q, int32_t G, int32_t d, const uint16_t *K,
+                        int64_t ldk, int64_t N, int32_t S, int32_t n_s, int32_t W,
+                        const int32_t *sel, int64_t k, double scale, double *a_blk) {
+  int64_t n_blk = oracle_num_blocks(N, S);
+  for (int64_t i = 0; i < n_blk; ++i) a_blk[i] = 0.0;
+  int8_t *inT = (int8_t *)calloc(N > 0 ? N : 1, 1);
+  for (int64_t j = 0; j < N; ++j) inT[j] = (int8_t)oracle_in_dense(j, N, n_s, W);
+  for (int64_t t = 0; t < k; ++t)
+    for (int64_t j = (int64_t)sel[t] * S; j < ((int64_t)sel[t] + 1) * S && j < N; ++j)
+      inT[j] = 1;
+  int64_t nT = 0;
+  for (int64_t j = 0; j < N; ++j) nT += inT[j];
+  if (nT > 0) {
+    int64_t *tok = (int64_t *)malloc(sizeof(int64_t) * nT);
+    int64_t t = 0;
+    for (int64_t j = 0; j < N; ++j)
+      if (inT[j]) tok[t++] = j;
+    double *O = (double *)malloc(sizeof(double) * G * d);
+    double *lse = (double *)malloc(sizeof(double) * G);
+    double *p = (double *)malloc(sizeof(double) * G * nT);
+    oracle_attend_tokens(q, G, d, K, ldk, K, ldk, tok, nT, scale, O, lse, p);
+    for (int32_t h = 0; h < G; ++h)
+      for (int64_t tt = 0; tt < nT; ++tt) a_blk[tok[tt] / S] += p[(int64_t)h * nT + tt] / (double)G;
+    free(p);
+    free(lse);
+    free(O);
+    free(tok);
+  }
+  free(inT);
+}
+
+/* [LFPS] What carries the argument: both tables decay by r after every step
+ * and take the step's weights (Eq. (10) read as the convex update, as MAW). */
+void oracle_lfps_update(double *phi_v, double *phi_s, const double *a_blk,
+                        int64_t n_blk, double r) {
+  int64_t b = n_blk - 1;
+  for (int64_t i = 0; i <= b; ++i) phi_v[i] = r * phi_v[i] + (1.0 - r) * a_blk[i];
+  for (int64_t o = 0; o <= b; ++o) phi_s[o] = r * phi_s[o] + (1.0 - r) * a_blk[b - o];
+}
+
+/* [LFPS] Assumptions & free parameters: the tables start from the last s = 32
+ * prefill steps (Eq. (4)); each such step attends causally to every earlier
+ * token (the prefill is dense). */
+void oracle_lfps_init(const uint16_t *q, int32_t s, int32_t G, int32_t d,
+                      const uint16_t *K, int64_t ldk, int64_t N, int32_t S,
+                      double scale, double r, double *phi_v, double *phi_s) {
+  int64_t n_blk = oracle_num_blocks(N, S);
+  for (int64_t i = 0; i < n_blk; ++i) phi_v[i] = phi_s[i] = 0.0;
+  double *a = (double *)malloc(sizeof(double) * (n_blk > 0 ? n_blk : 1));
+  int64_t *tok = (int64_t *)malloc(sizeof(int64_t) * (N > 0 ? N : 1));
+  double *O = (double *)malloc(sizeof(double) * G * d);
+  double *lse = (double *)malloc(sizeof(double) * G);
+  double *p = (double *)malloc(sizeof(double) * G * (N > 0 ? N : 1));
+  for (int32_t u = 0; u < s; ++u) {
+    int64_t pos = N - s + u;
+    if (pos < 0) continue;
+    int64_t nb = pos / S + 1;
+    for (int64_t j = 0; j <= pos; ++j) tok[j] = j;
+    oracle_attend_tokens(q + (int64_t)u * G * d, G, d, K, ldk, K, ldk, tok, pos + 1, scale, O,
+                         lse, p);
+    for (int64_t i = 0; i < nb; ++i) a[i] = 0.0;
+    for (int32_t h = 0; h < G; ++h)
+      for (int64_t j = 0; j <= pos; ++j) a[j / S] += p[(int64_t)h * (pos + 1) + j] / (double)G;
+    oracle_lfps_update(phi_v, phi_s, a, nb, r);
+  }
+  free(p);
+  free(lse);
+  free(O);
+  free(tok);
+  free(a);
 }
 
 /* The MAW input of one step (R8, and R10 as read from HGCA): HGCA's moving

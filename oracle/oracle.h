@@ -133,6 +133,48 @@ void oracle_attend_heads(const uint16_t *q, int32_t G, int32_t d,
                          const int64_t *k, double scale, double *O,
                          double *lse);
 
+/* Learn-from-the-past tables at block granularity: phi_v[i] for block i
+ * (vertical: a fixed absolute position), phi_s[o] for block offset o from the
+ * block of the newest token, b = floor((N-1)/S) (slash: a fixed relative
+ * position); both [n_blk] and 0 at the start.
+ * Candidates: over the entries [0, b] of each table, mean mu and maximum M,
+ * threshold tau = mu + a (M - mu); C0 = blocks i <= b with phi_v[i] > tau_v
+ * or phi_s[b - i] > tau_s; C0 grows by the offsets {-1, 0, 1, 2}; a grown
+ * block is kept when one of its two scores exceeds that table's mean and it
+ * holds a token outside D.  inC: [n_blk].  Returns |C|. */
+int64_t oracle_lfps_candidates(const double *phi_v, const double *phi_s, int64_t N,
+                               int32_t S, int32_t n_s, int32_t W, double a,
+                               int8_t *inC);
+
+/* Selection among the table candidates C: the k = min(|C|, ceil(budget*N/S))
+ * best of C by (u desc, index asc), u as oracle_score; written ascending to
+ * sel.  Returns k.  U, u optional as oracle_select. */
+int64_t oracle_lfps_select(const uint16_t *q, int32_t G, int32_t d,
+                           const uint16_t *mn, const uint16_t *mx, int64_t N,
+                           int32_t S, int32_t n_s, int32_t W, int64_t budget_ppm,
+                           const double *phi_v, const double *phi_s, double a,
+                           int32_t *sel, double *U, float *u);
+
+/* Attention mass per block under the softmax over the attended set T = D U
+ * tokens(sel): a_blk[i] = (1/G) sum_h sum_{j in T, j in block i} p_hj. */
+void oracle_attend_mass(const uint16_t *q, int32_t G, int32_t d, const uint16_t *K,
+                        int64_t ldk, int64_t N, int32_t S, int32_t n_s, int32_t W,
+                        const int32_t *sel, int64_t k, double scale, double *a_blk);
+
+/* Table update after a step with n_blk blocks (b = n_blk - 1):
+ * phi_v[i] <- r phi_v[i] + (1-r) a[i] and phi_s[o] <- r phi_s[o] + (1-r) a[b-o]
+ * for i, o in [0, b]. */
+void oracle_lfps_update(double *phi_v, double *phi_s, const double *a_blk,
+                        int64_t n_blk, double r);
+
+/* Tables from the last s prefill positions: zeroed on [0, n_blk(N)), then for
+ * u = 0 .. s-1 in order, the query of position p = N - s + u (q: [s][G][d])
+ * attends to [0, p] (causal, dense) and its block masses update the tables
+ * with n_blk = floor(p/S) + 1. */
+void oracle_lfps_init(const uint16_t *q, int32_t s, int32_t G, int32_t d,
+                      const uint16_t *K, int64_t ldk, int64_t N, int32_t S,
+                      double scale, double r, double *phi_v, double *phi_s);
+
 /* MAW input: a_blk[i] = (1/G) sum_h sum_{j in D, j in block i} p_hj with p_h
  * the softmax of head h over the dense set D alone (0 for blocks with no
  * token in D).  a_blk: [n_blk]. */

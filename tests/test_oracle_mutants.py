@@ -72,9 +72,27 @@ MUTANTS = [
      "k = oracle_select(q, 1, d,"),
     ("attend_heads_first_selection", "sel + (int64_t)h * ld_sel, k[h], scale,",
      "sel, k[0], scale,"),
+    ("lfps_growth_offsets_mirrored", "int64_t c = i - e;", "int64_t c = i + e;"),
+    ("lfps_mean_filter_dropped", "inC[i] = (int8_t)(grown && above && cand[i]);",
+     "inC[i] = (int8_t)(grown && cand[i]);"),
+    ("lfps_slash_offset_from_start",
+     "for (int64_t i = 0; i <= b; ++i) c0[i] = (int8_t)(phi_v[i] > tau_v || phi_s[b - i] > tau_s);",
+     "for (int64_t i = 0; i <= b; ++i) c0[i] = (int8_t)(phi_v[i] > tau_v || phi_s[i] > tau_s);"),
+    ("lfps_threshold_at_max", "double tau_v = mu_v + a * (mx_v - mu_v), tau_s = mu_s + a * (mx_s - mu_s);",
+     "double tau_v = mx_v, tau_s = mx_s;"),
+    ("lfps_slash_update_unmirrored",
+     "for (int64_t o = 0; o <= b; ++o) phi_s[o] = r * phi_s[o] + (1.0 - r) * a_blk[b - o];",
+     "for (int64_t o = 0; o <= b; ++o) phi_s[o] = r * phi_s[o] + (1.0 - r) * a_blk[o];"),
+    ("lfps_init_not_causal", "for (int64_t j = 0; j <= pos; ++j) tok[j] = j;\n    oracle_attend_tokens(q + (int64_t)u * G * d, G, d, K, ldk, K, ldk, tok, pos + 1,",
+     "for (int64_t j = 0; j <= pos; ++j) tok[j] = j;\n    oracle_attend_tokens(q + (int64_t)u * G * d, G, d, K, ldk, K, ldk, tok, pos,"),
+    ("attend_mass_first_head_only", "for (int64_t tt = 0; tt < nT; ++tt) a_blk[tok[tt] / S] += p[(int64_t)h * nT + tt] / (double)G;",
+     "for (int64_t tt = 0; tt < nT; ++tt) a_blk[tok[tt] / S] += p[tt] / (double)G;"),
     ("selected_block_last_token_dropped",
-     "for (int64_t j = (int64_t)sel[t] * S; j < ((int64_t)sel[t] + 1) * S && j < N; ++j)",
-     "for (int64_t j = (int64_t)sel[t] * S; j < ((int64_t)sel[t] + 1) * S - 1 && j < N; ++j)"),
+     "for (int64_t j = (int64_t)sel[t] * S; j < ((int64_t)sel[t] + 1) * S && j < N; ++j)\n      inT[j] = 1;\n  int64_t n_tok = 0;",
+     "for (int64_t j = (int64_t)sel[t] * S; j < ((int64_t)sel[t] + 1) * S - 1 && j < N; ++j)\n      inT[j] = 1;\n  int64_t n_tok = 0;"),
+    ("attend_mass_selected_block_last_token_dropped",
+     "for (int64_t j = (int64_t)sel[t] * S; j < ((int64_t)sel[t] + 1) * S && j < N; ++j)\n      inT[j] = 1;\n  int64_t nT = 0;",
+     "for (int64_t j = (int64_t)sel[t] * S; j < ((int64_t)sel[t] + 1) * S - 1 && j < N; ++j)\n      inT[j] = 1;\n  int64_t nT = 0;"),
 ]
 
 

@@ -573,3 +573,124 @@ def test_attend_heads_over_own_token_lists():
     Od, ld = oracle.dense(q, K, V, N)
     np.testing.assert_allclose(O, Od, rtol=0, atol=1e-12)
     np.testing.assert_allclose(lse, ld, rtol=0, atol=1e-12)
+
+
+# ------------------------------------------ learn-from-the-past tables (blocks)
+
+@pytest.mark.parametrize("case", ["lfps_candidates", "lfps_candidates_slash"])
+def test_lfps_candidates_hand_case(case):
+    c = GOLD[case]
+    inC, n = oracle.lfps_candidates(c["phi_v"], c["phi_s"], c["N"], c["S"], c["n_s"], c["W"],
+                                    c["a"])
+    assert np.flatnonzero(inC).tolist() == c["want_C"] and n == len(c["want_C"])
+
+
+def _lfps_case(seed, N, S, n_s, W, G=2, d=8):
+    rng = np.random.default_rng(seed)
+    nb = oracle.num_blocks(N, S)
+    K = rand_bits((N, d), seed=600 + seed)
+    q = rand_bits((G, d), seed=700 + seed)
+    phi_v = rng.random(nb) * (rng.random(nb) < 0.5)
+    phi_s = rng.random(nb) * (rng.random(nb) < 0.3)
+    return K, q, phi_v, phi_s
+
+
+@pytest.mark.parametrize("seed", range(8))
+def test_lfps_select_bruteforce_tiny(seed):
+    """The selection is the lexicographic optimum of (u desc, index asc) over
+    all k-subsets of the table candidates."""
+    rng = np.random.default_rng(800 + seed)
+    S = int(rng.choice([1, 2, 4]))
+    n_s, W = int(rng.integers(0, 3)), int(rng.integers(0, 2 * S + 1))
+    N = int(rng.integers(n_s + W + 1, n_s + W + 12 * S + 1))
+    K, q, phi_v, phi_s = _lfps_case(seed, N, S, n_s, W, d=4)
+    mn, mx = oracle.summaries(K, S)
+    inC, nC = oracle.lfps_candidates(phi_v, phi_s, N, S, n_s, W)
+    if nC == 0 or nC > 10:
+        pytest.skip("candidate count outside brute-force range")
+    ppm = int(rng.integers(1, 1_000_001))
+    r = oracle.lfps_select(q, mn, mx, N, S, n_s, W, ppm, phi_v, phi_s)
+    k = oracle.num_selected(N, S, ppm, nC)
+    assert r["k"] == k == len(r["sel"])
+    keys = {i: (0, float(r["u"][i]) + 0.0, -i) for i in range(len(inC))}
+    assert r["sel"].tolist() == _bruteforce_best(keys, np.flatnonzero(inC).tolist(), k)
+
+
+def test_lfps_select_equals_block_topk_when_candidates_cover_it():
+    """When C holds the plain top-k of all candidates, restricting the ranking
+    to C changes nothing."""
+    N, S, n_s, W, d, G = 2000, 16, 4, 64, 16, 2
+    K = rand_bits((N, d), seed=61)
+    q = rand_bits((G, d), seed=62)
+    mn, mx = oracle.summaries(K, S)
+    nb = oracle.num_blocks(N, S)
+    ref = oracle.select(q, mn, mx, N, S, n_s, W, 50000)
+    phi_v = np.zeros(nb)
+    phi_v[ref["sel"]] = 1.0             # every selected block far above the threshold
+    phi_v[(ref["sel"][0] + 5) % nb] = 1.0  # and some other block
+    r = oracle.lfps_select(q, mn, mx, N, S, n_s, W, 50000, phi_v, np.zeros(nb))
+    np.testing.assert_array_equal(r["sel"], ref["sel"])
+    inC, _ = oracle.lfps_candidates(phi_v, np.zeros(nb), N, S, n_s, W)
+    assert inC.sum() < oracle.candidates(N, S, n_s, W)[1]
+
+
+def test_attend_mass_is_the_block_sum_of_the_softmax():
+    N, S, n_s, W, d, G = 300, 16, 4, 40, 8, 3
+    K, q = rand_bits((N, d), 71), rand_bits((G, d), 72)
+    sel = np.array([2, 9], np.int32)
+    a = oracle.attend_mass(q, K, N, S, n_s, W, sel)
+    toks = sorted(set(range(n_s)) | set(range(N - W, N)) | set(range(32, 48)) | set(range(144, 160)))
+    s = f64(q) @ f64(K)[toks].T / math.sqrt(d)
+    p = np.exp(s - s.max(1, keepdims=True))
+    p /= p.sum(1, keepdims=True)
+    want = np.zeros(oracle.num_blocks(N, S))
+    np.add.at(want, np.array(toks) // S, p.mean(0))
+    np.testing.assert_allclose(a, want, rtol=0, atol=1e-14)
+    assert abs(a.sum() - 1.0) < 1e-12
+
+
+def test_lfps_update_closed_forms():
+    r, nb = 0.95, 6
+    a = np.array([0.1, 0.0, 0.5, 0.0, 0.0, 0.4])
+    pv, ps = np.zeros(nb), np.zeros(nb)
+    for t in range(1, 40):
+        pv, ps = oracle.lfps_update(pv, ps, a, r)
+        np.testing.assert_allclose(pv, a * (1 - r ** t), rtol=1e-12, atol=1e-15)
+        np.testing.assert_allclose(ps, a[::-1] * (1 - r ** t), rtol=1e-12, atol=1e-15)
+    # an impulse on block 2 with newest block 5 lands on offset 3
+    pv, ps = oracle.lfps_update(np.zeros(nb), np.zeros(nb), np.eye(nb)[2], r)
+    assert ps.tolist() == [0.0, 0.0, 0.0, (1 - r), 0.0, 0.0]
+    # a shorter step (3 blocks) leaves the later entries alone
+    pv2, ps2 = oracle.lfps_update(np.ones(nb), np.ones(nb), np.array([0.2, 0.3, 0.5]), r)
+    np.testing.assert_allclose(pv2, [r + (1 - r) * 0.2, r + (1 - r) * 0.3, r + (1 - r) * 0.5, 1, 1, 1])
+    np.testing.assert_allclose(ps2, [r + (1 - r) * 0.5, r + (1 - r) * 0.3, r + (1 - r) * 0.2, 1, 1, 1])
+
+
+def test_lfps_init_one_and_two_prefill_positions():
+    """Init from the last s prefill positions: each attends causally to every
+    earlier token; the masses enter with the decay in order."""
+    N, S, d, G, r = 97, 16, 8, 2, 0.95  # the two positions 95, 96 lie in blocks 5 and 6
+    K = rand_bits((N, d), 81)
+    qp = rand_bits((2, G, d), 82).reshape(2, G, d)
+    nb = oracle.num_blocks(N, S)
+
+    def mass(qq, pos):
+        s = f64(qq) @ f64(K)[:pos + 1].T / math.sqrt(d)
+        p = np.exp(s - s.max(1, keepdims=True))
+        p /= p.sum(1, keepdims=True)
+        out = np.zeros(nb)
+        np.add.at(out, np.arange(pos + 1) // S, p.mean(0))
+        return out
+
+    pv, ps = oracle.lfps_init(qp[1:], K, N, S, r)
+    a1 = mass(qp[1], N - 1)
+    np.testing.assert_allclose(pv, (1 - r) * a1, rtol=0, atol=1e-14)
+    np.testing.assert_allclose(ps[:nb], (1 - r) * a1[::-1], rtol=0, atol=1e-14)
+    pv, ps = oracle.lfps_init(qp, K, N, S, r)
+    a0 = mass(qp[0], N - 2)
+    np.testing.assert_allclose(pv, r * (1 - r) * a0 + (1 - r) * a1, rtol=0, atol=1e-14)
+    b0, b1 = (N - 2) // S, (N - 1) // S
+    want_s = np.zeros(nb)
+    want_s[:b0 + 1] += r * (1 - r) * a0[:b0 + 1][::-1]
+    want_s[:b1 + 1] += (1 - r) * a1[:b1 + 1][::-1]
+    np.testing.assert_allclose(ps, want_s, rtol=0, atol=1e-14)
