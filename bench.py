@@ -87,6 +87,10 @@ def parse():
                     help="one block set per query head (select_per_query_head): the separate "
                          "calls select_topk, sparse_attend (with the union of each KV head's "
                          "sets) and fuse_lse; the kernel split is timed per call")
+    ap.add_argument("--lfps", action="store_true",
+                    help="selection among the learn-from-the-past table candidates "
+                         "(lfps_select): tables filled from 32 prefill positions per layer, then "
+                         "the separate calls; the kernel split is timed per call")
     ap.add_argument("--timeline", type=int, default=0, metavar="STEPS",
                     help="measurement build only (build.py --timeline): record the per-phase "
                          "timestamps of STEPS one-launch steps after the warm-up, print their "
@@ -163,7 +167,7 @@ def measured_traffic():
     return t.get("traffic_bytes_per_launch")
 
 
-def algorithmic_bytes(w, N, blk_cnt, blk_idx, with_maw=True):
+def algorithmic_bytes(w, N, blk_cnt, blk_idx, with_maw=True, lfps_cand=None):
     """Per-step algorithmic HBM bytes (each term counted once):
     summaries n_blk*2*d*2 per (seq, kv head) that selects; K+V of the distinct
     attended tokens |T|*2*d*2 (with one set per query head, T = D U the union
@@ -189,7 +193,11 @@ def algorithmic_bytes(w, N, blk_cnt, blk_idx, with_maw=True):
             inT = inD.copy()
             for i in sel:
                 inT[i * S:min(N, (i + 1) * S)] = True
-            summ += nb * 2 * w.d * 2 if w.budget_ppm[g] > 0 else 0  # streaming heads score nothing
+            if lfps_cand is not None:  # only the table candidates are scored; the two
+                # tables are read by the selection and read and written by the update
+                summ += int(lfps_cand[b][g]) * 2 * w.d * 2 + nb * 4 * 2 * 3
+            else:
+                summ += nb * 2 * w.d * 2 if w.budget_ppm[g] > 0 else 0  # streaming heads score nothing
             attend += int(inT.sum()) * 2 * w.d * 2
             inside = sum(1 for i in range(nb) if inD[i * S:min(N, (i + 1) * S)].all())
             maw += (nb * 4 if with_maw and w.budget_ppm[g] > 0 else 0) + inside * 4 * 2
@@ -221,8 +229,10 @@ def main():
     w = {"llama32k": synth.llama32k, "qwen128k": lambda: synth.qwen128k(0),
          "loop32": synth.loop32, "sweep": lambda: dataclasses.replace(synth.sweep(*args.sweep), N=args.sweep_n)}[args.workload]()
     maw_beta = w.maw_beta  # MAW flags on for loop32 only
-    if args.per_query_head:
-        args.fused = 0  # the one-launch step selects per KV head
+    if args.per_query_head or args.lfps:
+        args.fused = 0  # the one-launch step ranks every block per KV head
+    if args.lfps:
+        args.cpu_baseline = 0  # (the lockstep tests check this mode against the oracle)
     if args.streaming_heads:
         K_s = min(args.streaming_heads, w.Hkv)
         w = dataclasses.replace(w, budget_ppm=[0] * K_s + list(w.budget_ppm[K_s:]))
@@ -237,7 +247,8 @@ def main():
                        block_size=w.block_size, budget_ppm=w.budget_ppm,
                        maw_decay=0.95, maw_beta=maw_beta,
                        page_shuffle_seed=12345, stream=stream,
-                       select_per_query_head=1 if args.per_query_head else 0)
+                       select_per_query_head=1 if args.per_query_head else 0,
+                       lfps_select=1 if args.lfps else 0, lfps_a=0.2)
     seqs = list(range(w.B))
     dirs_l = {}
     t0 = time.time()
@@ -260,6 +271,17 @@ def main():
         del K, V
         torch.cuda.empty_cache()
     torch.cuda.synchronize()
+    lfps_init_ms = None
+    if args.lfps:  # the tables from the last 32 prefill positions of every layer
+        g0 = torch.Generator(device=dev).manual_seed(args.seed + 7)
+        ei, ej = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        ei.record(stream)
+        for layer in range(L):
+            qp = torch.randn(w.B, 32, w.Hq, w.d, generator=g0, device=dev).to(torch.bfloat16)
+            eng.lfps_init(layer, seqs, qp)
+        ej.record(stream)
+        torch.cuda.synchronize()
+        lfps_init_ms = ei.elapsed_time(ej) / L
     setup_s = time.time() - t0
     g = torch.Generator(device=dev).manual_seed(args.seed)
     k_new = torch.randn(64, w.B, w.Hkv, w.d, generator=g, device=dev).to(torch.bfloat16)
@@ -341,8 +363,11 @@ def main():
         eng.sync()
         return ea.elapsed_time(eb) / n_inst
 
-    ab = algorithmic_bytes(w, N_now, cnt, idx, with_maw=maw_beta > 0)
-    if args.per_query_head:
+    lfps_cand = None
+    if args.lfps:
+        lfps_cand = [eng.debug(_abi.SD_DEBUG_LFPS_CAND, l_last, b).tolist() for b in range(w.B)]
+    ab = algorithmic_bytes(w, N_now, cnt, idx, with_maw=maw_beta > 0, lfps_cand=lfps_cand)
+    if args.per_query_head or args.lfps:
         # select_topk alone, then sparse_attend (union + attention) alone on
         # each layer's own selection (no append in between)
         sel_bufs = [eng.alloc_step(w.B, device=dev) for _ in range(L)]
@@ -356,9 +381,11 @@ def main():
         l_att = (n_inst - 1) % L
         eng.fuse_lse(l_att, seqs, bufs["o_part"], bufs["lse_part"], bufs["o"], bufs["lse"])
         eng.sync()
-        kernel_ms = {"select_topk": t_sel, "sparse_attend (k_union + k_attend)": t_att,
+        kernel_ms = {"select_topk": t_sel,
+                     ("sparse_attend (k_union + k_attend)" if args.per_query_head
+                      else "sparse_attend"): t_att,
                      "timed_launches": n_inst}
-        dom_name, t_dom = "k_union + k_attend", t_att
+        dom_name, t_dom = ("k_union + k_attend" if args.per_query_head else "k_attend"), t_att
         kstep_bytes = ab["attend"]  # the attention's K+V of the union's tokens
         sel_gbs = ab["summaries"] / (t_sel * 1e-3) / 1e9
     else:
@@ -395,7 +422,8 @@ def main():
                                   if args.streaming_heads else ""),
                    "global_batch": w.B, "seq_len": w.N, "parallelism": "none (1 GPU)",
                    "fused_step": bool(args.fused),
-                   "selection": "per query head" if args.per_query_head else "per KV head"},
+                   "selection": "per query head" if args.per_query_head else
+                   ("learn-from-the-past table candidates, a = 0.2" if args.lfps else "per KV head")},
         "step_hbm": {"algorithmic_bytes": ab["total"], "achieved_GBs": step_gbs,
                      "frac_of_8TBs": step_gbs / HBM_PEAK_GBS,
                      "breakdown_bytes": {k: ab[k] for k in ("summaries", "attend", "maw", "q_o_lse")}},
@@ -404,12 +432,20 @@ def main():
                      "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": kstep_gbs / HBM_PEAK_GBS,
                      # the committed counter summary is the headline workload's
                      "traffic": measured_traffic() if args.workload == "llama32k"
-                     and not args.streaming_heads and not args.per_query_head else None,
+                     and not args.streaming_heads and not args.per_query_head
+                     and not args.lfps else None,
                      "algorithmic_bytes_per_launch": kstep_bytes},
         "trials_ms": trial_ms,
         "setup_s": setup_s,
     }
 
+    if args.lfps:
+        out["select_topk_GBs"] = sel_gbs
+        out["lfps"] = {"init_ms_per_layer": lfps_init_ms,
+                       "candidates_per_unit": lfps_cand,
+                       "note": "only the table candidates' summaries are read (the summaries "
+                               "term), plus the two tables: read by the selection, read and "
+                               "written by the update"}
     if args.per_query_head:
         out["select_topk_GBs"] = sel_gbs
         out["union_vs_group"] = {

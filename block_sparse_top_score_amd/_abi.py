@@ -19,7 +19,8 @@ LIB_PATH = os.path.join(_HERE, "libsparse_decode.so")
 LIB_TIMELINE_PATH = os.path.join(_HERE, "libsparse_decode_timeline.so")
 
 SD_OK, SD_EINVAL, SD_ENOMEM, SD_EHIP, SD_EUNSUPPORTED, SD_ESTATE = 0, -1, -2, -3, -4, -5
-SD_DEBUG_PAGE_TABLE, SD_DEBUG_SUMMARY, SD_DEBUG_MAW, SD_DEBUG_K, SD_DEBUG_V, SD_DEBUG_SCORES = range(6)
+(SD_DEBUG_PAGE_TABLE, SD_DEBUG_SUMMARY, SD_DEBUG_MAW, SD_DEBUG_K, SD_DEBUG_V, SD_DEBUG_SCORES,
+ SD_DEBUG_LFPS, SD_DEBUG_LFPS_CAND) = range(8)
 
 # every symbol declared in include/sparse_decode.h
 EXPORTS = [
@@ -28,7 +29,7 @@ EXPORTS = [
     "sparse_decode_step", "sparse_decode_step_noalloc", "sd_release_seq", "sd_seq_len",
     "sd_sync",
     "sd_last_error", "sd_debug_bytes", "sd_debug_copy", "sd_debug_set_maw",
-    "sd_read_probe",
+    "sd_debug_set_lfps", "sd_lfps_init", "sd_read_probe",
 ]
 
 
@@ -50,6 +51,7 @@ class SDConfig(ctypes.Structure):
         ("softmax_scale", ctypes.c_float), ("maw_decay", ctypes.c_float),
         ("maw_beta", ctypes.c_float), ("page_shuffle_seed", ctypes.c_uint64),
         ("stream", ctypes.c_void_p), ("select_per_query_head", ctypes.c_int32),
+        ("lfps_select", ctypes.c_int32), ("lfps_a", ctypes.c_float),
     ]
 
 
@@ -93,6 +95,8 @@ def load(path: str = LIB_PATH):
         "sd_debug_bytes": (i32, [P, i32, i32, i32, ctypes.POINTER(sz)]),
         "sd_debug_copy": (i32, [P, i32, i32, i32, P, sz]),
         "sd_debug_set_maw": (i32, [P, i32, i32, P, sz]),
+        "sd_debug_set_lfps": (i32, [P, i32, i32, P, sz]),
+        "sd_lfps_init": (i32, [P, i32, i32, P, P, i32]),
         "sd_read_probe": (i32, [P, sz, P, i32, P]),
     }
     for name, (res, args) in sig.items():
@@ -108,7 +112,7 @@ def make_config(*, max_seqs, num_layers, num_q_heads, num_kv_heads, head_dim,
                 block_size: Sequence[int], budget_ppm: Sequence[int],
                 softmax_scale=0.0, maw_decay=0.95, maw_beta=0.0,
                 page_shuffle_seed=0, stream=None, page_size=16,
-                select_per_query_head=0):
+                select_per_query_head=0, lfps_select=0, lfps_a=0.2):
     bs = (ctypes.c_int32 * len(block_size))(*block_size)
     bp = (ctypes.c_int32 * len(budget_ppm))(*budget_ppm)
     cfg = SDConfig(max_seqs, num_layers, num_q_heads, num_kv_heads, head_dim,
@@ -116,7 +120,8 @@ def make_config(*, max_seqs, num_layers, num_q_heads, num_kv_heads, head_dim,
                    recent_window, ctypes.cast(bs, ctypes.POINTER(ctypes.c_int32)),
                    ctypes.cast(bp, ctypes.POINTER(ctypes.c_int32)),
                    float(softmax_scale), float(maw_decay), float(maw_beta),
-                   int(page_shuffle_seed), stream, int(select_per_query_head))
+                   int(page_shuffle_seed), stream, int(select_per_query_head),
+                   int(lfps_select), float(lfps_a))
     cfg._keep = (bs, bp)  # keep the arrays alive with the struct
     return cfg
 
@@ -276,11 +281,26 @@ class SparseDecode:
         nb = ctypes.c_size_t()
         self._check(self.L.sd_debug_bytes(self.ctx, what, layer, seq, ctypes.byref(nb)))
         dt = {SD_DEBUG_PAGE_TABLE: np.int32, SD_DEBUG_MAW: np.float32,
-              SD_DEBUG_SCORES: np.float32}.get(what, np.uint16)
+              SD_DEBUG_SCORES: np.float32, SD_DEBUG_LFPS: np.float32,
+              SD_DEBUG_LFPS_CAND: np.int32}.get(what, np.uint16)
         out = np.zeros(nb.value // np.dtype(dt).itemsize, dt)
         self._check(self.L.sd_debug_copy(self.ctx, what, layer, seq,
                                          out.ctypes.data_as(ctypes.c_void_p), nb.value))
         return out
+
+    def set_lfps(self, layer, seq, values):
+        """Overwrite the tables of one (layer, sequence), laid out as SD_DEBUG_LFPS."""
+        a = np.ascontiguousarray(values, dtype=np.float32)
+        self._check(self.L.sd_debug_set_lfps(self.ctx, layer, seq,
+                                             a.ctypes.data_as(ctypes.c_void_p), a.nbytes))
+
+    def lfps_init(self, layer, seq_ids, q_prefill, check=True):
+        """sd_lfps_init: q_prefill [n][s][Hq][d] bf16 (device)."""
+        s, sp = _i32arr(seq_ids)
+        st = self.L.sd_lfps_init(self.ctx, layer, len(s), sp, _ptr(q_prefill), q_prefill.shape[1])
+        if check:
+            self._check(st)
+        return st
 
     def set_maw(self, layer, seq, values):
         a = np.ascontiguousarray(values, dtype=np.float32)

@@ -73,6 +73,8 @@ struct LayerDev {
   int32_t *pt;     // [max_seqs][pages_per_seq]
   uint16_t *summ;  // per head h: [max_seqs][d/4][nbmax_h][8] bf16
   float *maw;      // per head h: [max_seqs][nbmax_h]
+  float *phi;      // learn-from-the-past tables, per head h: [max_seqs][2][nbmax_h]
+                   // (vertical by block, then slash by block offset); NULL unless on
 };
 
 // Problem constants common to every kernel of a context.
@@ -90,6 +92,8 @@ struct Dims {
   int32_t pqh;         // 1: one selection per query head (unit arrays of the
                        // selection are per query head), 0: per KV head
   int32_t ucap;        // entries of a KV head's union of its query heads' sets
+  int32_t lfps;        // 1: selection among the learn-from-the-past table candidates
+  float lfps_a;        // its threshold parameter a
 };
 
 // Scratch owned by the context.  Per-unit arrays have key_stride entries, a
@@ -103,7 +107,8 @@ struct Scratch {
   uint32_t *ukeys;   // [max_seqs][Hkv][key_stride] their exact keys
   uint32_t *unit_acc;  // [max_seqs][Hkv][4] error bound (float bits, max) and
                        // flagged candidates (count) of the score tiles, 0 between
-                       // steps; the bound the unit's last selection used; spare
+                       // steps; the bound the unit's last selection used; the
+                       // table candidates of its last learn-from-the-past selection
   float *lm_pg;      // [max_seqs][Hq][lm_cap] log softmax mass of each attended page
   uint32_t *arrive;  // [max_seqs][Hkv][4] last-arriver counters (kept at 0): score
                      // tiles, attention parts, dense pages done (+ the top-k), spare
@@ -137,6 +142,17 @@ hipError_t launch_append(const Ctx &c, const AppendBatch &b, int max_new,
 hipError_t launch_select(const Ctx &c, const SeqBatch &b, int max_blocks, const uint16_t *q,
                          int32_t *blk_idx, int32_t *blk_cnt, int32_t k_cap, hipStream_t st);
 
+// Selection among the learn-from-the-past table candidates (one workgroup
+// per (sequence, KV head)); max_blocks: the most blocks of a unit.
+hipError_t launch_lfps_select(const Ctx &c, const SeqBatch &b, int max_blocks, const uint16_t *q,
+                              int32_t *blk_idx, int32_t *blk_cnt, int32_t k_cap, hipStream_t st);
+
+// The tables from the last s_steps prefill positions (q_prefill:
+// [n][s_steps][Hq][d] bf16); A: scratch [n][Hkv][s_steps][key_stride] floats
+// for the block masses.
+hipError_t launch_lfps_init(const Ctx &c, const SeqBatch &b, int max_blocks, const uint16_t *q_prefill,
+                            int s_steps, float *A, hipStream_t st);
+
 // Per-query-head selection: the union of each KV head's query-head sets
 // (blk_idx [n][Hq][k_cap], blk_cnt [n][Hq]) into the context's scratch, for
 // the attention.
@@ -168,9 +184,12 @@ int step_capacity(const Ctx &c, int max_blocks, int ptl_cap);
 
 // Fusion of the partials: with_maw = the P slots of the attend call and MAW
 // (layer call); otherwise every slot of p_cap <= kFuseSlots is fused (layer -1).
+// (with the learn-from-the-past tables on, sel_idx / sel_cnt / k_cap are the
+// selection the attention call took, and max_blocks the most blocks of a unit)
 hipError_t launch_fuse(const Ctx &c, const SeqBatch &b, bool with_maw, int P,
                        const float *o_part, const float *lse_part, int32_t p_cap,
-                       float *o, float *lse, hipStream_t st);
+                       float *o, float *lse, const int32_t *sel_idx, const int32_t *sel_cnt,
+                       int32_t k_cap, int max_blocks, hipStream_t st);
 
 hipError_t launch_fill_f32(float *p, size_t n, float v, hipStream_t st);
 hipError_t launch_fill_u32(uint32_t *p, size_t n, uint32_t v, hipStream_t st);

@@ -2061,7 +2061,9 @@ __device__ __attribute__((always_inline)) void attend_part(const Ctx &c, int i, 
           const int pl_ = min(pn, dl.np - 1);  // pages past N are never read
           pg = ptl ? ptl[pl_] : pts[pl_];
           mk = in_range ? (page_valid16(g, pn) & ~page_dense16(g, pn)) | (hx << 16) : 0;
-          sl = -1;  // (only the dense pages' masses feed MAW)
+          // (the learn-from-the-past tables take every attended page's
+          // mass; MAW only the dense pages')
+          sl = c.dm.lfps ? c.dm.lm_sel0 + t : -1;
         },
         qa, W, pl, lmb, tok);
   }
@@ -2471,6 +2473,319 @@ __global__ __launch_bounds__(256) void k_topk_heads(Ctx c, SeqBatch b, int32_t *
                     lrows_words, dmask);
 }
 
+// ---------------------------------------------------------------------------
+// Learn-from-the-past selection ([LFPS] What carries the argument and Figure 4;
+// at block granularity): per (sequence, KV head) a vertical table pv over
+// blocks and a slash table ps over block offsets from the newest block b.
+// Candidates C: blocks above the threshold tau = mean + a (max - mean) of
+// either table, grown by the offsets {-1, 0, 1, 2}, kept when above a table's
+// mean and holding a token outside D.  Only the blocks of C are scored, each
+// exactly (fp64 in channel order, the plain sum where the products' exponents
+// could make the quad's order round differently); the k = min(|C|, budget)
+// best by (score desc, index asc) are written ascending.  One workgroup per
+// unit.
+constexpr int kLfpsLds = 6144;  // table candidates a workgroup keeps in LDS
+struct LfpsSmem {
+  int32_t list[kLfpsLds];  // C, ascending (global scratch past kLfpsLds)
+  uint32_t key[kLfpsLds];  // order keys of their exact group scores
+  float qs[SD_MAX_GROUP * 128];
+  double rd[8];
+  float rf[8];
+  uint32_t red[16];
+};
+
+__device__ __forceinline__ double wg_sum_f64(double x, double *rd) {
+  for (int o = 32; o >= 1; o >>= 1) x += __shfl_xor(x, o, 64);
+  __syncthreads();
+  if ((threadIdx.x & 63) == 0) rd[threadIdx.x >> 6] = x;
+  __syncthreads();
+  return (rd[0] + rd[1]) + (rd[2] + rd[3]);
+}
+__device__ __forceinline__ float wg_max_f32(float x, float *rf) {
+  x = wave_max(x);
+  __syncthreads();
+  if ((threadIdx.x & 63) == 0) rf[threadIdx.x >> 6] = x;
+  __syncthreads();
+  return fmaxf(fmaxf(rf[0], rf[1]), fmaxf(rf[2], rf[3]));
+}
+
+template <int D, int G>
+__global__ __launch_bounds__(256) void k_lfps_select(Ctx c, SeqBatch b, int32_t *__restrict__ blk_idx,
+                                                     int32_t *__restrict__ blk_cnt, int k_cap,
+                                                     const uint16_t *__restrict__ q) {
+  extern __shared__ __align__(16) unsigned char smem_raw[];
+  LfpsSmem &sm = *reinterpret_cast<LfpsSmem *>(smem_raw);
+  uint32_t *c0w = reinterpret_cast<uint32_t *>(smem_raw + sizeof(LfpsSmem));  // C0 bits
+  const int tid = threadIdx.x;
+  const int h = blockIdx.x % c.dm.Hkv, i = blockIdx.x / c.dm.Hkv;
+  const HeadInfo hi = c.heads[h];
+  const int seq = b.seq[i], N = b.len[i];
+  const size_t unit = (size_t)seq * c.dm.Hkv + h, out = (size_t)i * c.dm.Hkv + h;
+  if (selects_nothing(hi, N, c.dm)) {
+    if (tid == 0) st_dev(&blk_cnt[out], 0);
+    return;
+  }
+  const UG g = unit_geom(N, hi, c.dm);
+  const int nb = g.n_blk, bb = nb - 1;
+  const float *pv = c.L.phi + 2 * hi.maw_off + (size_t)seq * 2 * hi.nbmax;
+  const float *ps = pv + hi.nbmax;
+  int32_t *gl = c.sc.ulist + unit * c.dm.key_stride;
+  uint32_t *gk = c.sc.ukeys + unit * c.dm.key_stride;
+  auto lst_ld = [&](int p) -> int { return p < kLfpsLds ? sm.list[p] : ld_dev(&gl[p]); };
+  auto lst_st = [&](int p, int v) { if (p < kLfpsLds) sm.list[p] = v; else st_dev(&gl[p], v); };
+  auto key_ld = [&](int p) -> uint32_t { return p < kLfpsLds ? sm.key[p] : ld_dev(&gk[p]); };
+  auto key_st = [&](int p, uint32_t v) { if (p < kLfpsLds) sm.key[p] = v; else st_dev(&gk[p], v); };
+  const uint16_t *qg = q + out * G * D;
+  for (int x = tid; x < G * D; x += 256) sm.qs[x] = __uint_as_float((uint32_t)qg[x] << 16);
+  // 1. mean and maximum of each table over [0, b]
+  double sv = 0.0, ss = 0.0;
+  float mv = -INFINITY, ms = -INFINITY;
+  for (int t = tid; t <= bb; t += 256) {
+    const float a = pv[t], e = ps[t];
+    sv += (double)a;
+    ss += (double)e;
+    mv = fmaxf(mv, a);
+    ms = fmaxf(ms, e);
+  }
+  sv = wg_sum_f64(sv, sm.rd);
+  ss = wg_sum_f64(ss, sm.rd + 4);
+  mv = wg_max_f32(mv, sm.rf);
+  ms = wg_max_f32(ms, sm.rf + 4);
+  const double mu_v = sv / (double)nb, mu_s = ss / (double)nb;
+  const double a = (double)c.dm.lfps_a;
+  const double tau_v = mu_v + a * ((double)mv - mu_v), tau_s = mu_s + a * ((double)ms - mu_s);
+  // 2. C0 over [0, b], as bits
+  const int words = (nb + 31) >> 5;
+  for (int w = tid; w < words; w += 256) c0w[w] = 0u;
+  __syncthreads();
+  for (int t = tid; t <= bb; t += 256)
+    if ((double)pv[t] > tau_v || (double)ps[bb - t] > tau_s) atomicOr(&c0w[t >> 5], 1u << (t & 31));
+  __syncthreads();
+  auto c0 = [&](int x) -> bool { return x >= 0 && x <= bb && ((c0w[x >> 5] >> (x & 31)) & 1u); };
+  auto in_c = [&](int x) -> bool {
+    if (!is_candidate(g, x) || !(c0(x + 1) || c0(x) || c0(x - 1) || c0(x - 2))) return false;
+    return (double)pv[x] > mu_v || (double)ps[bb - x] > mu_s;
+  };
+  // 3. C in block order: thread t takes blocks [t m, t m + m) of the scored ones
+  const int n_sc = g.n_sc, m = cdiv(n_sc, 256), j0 = tid * m;
+  int mine = 0;
+  for (int x = j0; x < min(j0 + m, n_sc); ++x) mine += in_c(x) ? 1 : 0;
+  int slot = 0, nC = 0;
+  int o = wg_scan(mine, sm.red, slot, nC);
+  for (int x = j0; x < min(j0 + m, n_sc); ++x)
+    if (in_c(x)) lst_st(o++, x);
+  __syncthreads();
+  if (tid == 0) st_dev(&c.sc.unit_acc[4 * unit + 3], (uint32_t)nC);  // |C|, for inspection
+  const int kq = min(g.kk, nC);
+  if (kq == 0) {
+    if (tid == 0) st_dev(&blk_cnt[out], 0);
+    return;
+  }
+  // 4. exact group scores: one lane quad per block, the heads in turn
+  for (int p0 = 0; p0 < nC; p0 += 64) {
+    const int p = p0 + (tid >> 2);
+    const bool on = p < nC;
+    const int blk = on ? lst_ld(p) : 0;
+    double best = -INFINITY;
+#pragma unroll 1
+    for (int hh = 0; hh < G; ++hh)
+      best = fmax(best, exact_score_quad<D>(c, seq, hi, blk, sm.qs + hh * D, on));
+    if (on && (tid & 3) == 0) key_st(p, order_key((float)best));
+  }
+  __syncthreads();
+  // 5. the kq-th largest key T: keys above T are in, of the keys equal to T
+  // the lowest blocks (first in the list) fill the rest
+  const int mm = cdiv(nC, 256), q0 = tid * mm, q1 = min(q0 + mm, nC);
+  auto count_ge = [&](uint32_t t) {
+    int n = 0;
+    for (int p = q0; p < q1; ++p) n += key_ld(p) >= t ? 1 : 0;
+    return wg_sum(n, sm.red, slot);
+  };
+  uint32_t lo = 0u, hi_k = 0xffffffffu;  // count_ge(lo) >= kq > count_ge(hi_k + 1)
+  while (lo < hi_k) {
+    const uint32_t mid = lo + ((hi_k - lo) >> 1) + 1u;
+    if (count_ge(mid) >= kq) lo = mid; else hi_k = mid - 1u;
+  }
+  const uint32_t T = lo;
+  const int n_gt = T == 0xffffffffu ? 0 : count_ge(T + 1u);
+  const int need = kq - n_gt;  // keys equal to T to take, by block order
+  int eq = 0, gt = 0;
+  for (int p = q0; p < q1; ++p) {
+    const uint32_t k = key_ld(p);
+    eq += k == T ? 1 : 0;
+    gt += k > T ? 1 : 0;
+  }
+  int eq_tot = 0;
+  const int eq_before = wg_scan(eq, sm.red, slot, eq_tot);
+  const int take_eq = max(0, min(eq, need - eq_before));
+  int tot = 0;
+  int pos = wg_scan(gt + take_eq, sm.red, slot, tot);
+  int32_t *dst = blk_idx + out * k_cap;
+  int e_seen = eq_before;
+  for (int p = q0; p < q1; ++p) {
+    const uint32_t k = key_ld(p);
+    bool take = k > T;
+    if (k == T) take = e_seen++ < need;
+    if (take) {
+      if (pos < k_cap) st_dev(&dst[pos], lst_ld(p));
+      ++pos;
+    }
+  }
+  if (tid == 0) st_dev(&blk_cnt[out], kq);
+}
+
+// The tables' update after a step's fusion ([LFPS] What carries the argument:
+// both tables decay by r and take the step's attention weights): the mass
+// each block received under the softmax over the attended set, averaged over
+// the group's query heads, from the log-masses of the dense pages and of the
+// selected pages (sel: the selection the attention call took) and each head's
+// lse; then pv[x] <- r pv[x] + (1 - r) a[x], ps[o] <- r ps[o] + (1 - r) a[b - o]
+// over [0, b].  ablk: LDS, one float per block.
+template <int D, int G>
+__device__ void lfps_update_unit(const Ctx &c, int seq, int h, const HeadInfo &hi, const UG &g,
+                                 const int32_t *sel, int cnt, const float *lse_h, float *ablk) {
+  const int tid = threadIdx.x, nb = g.n_blk, bb = nb - 1, PPB = g.S / kPage;
+  const float *lmb = c.sc.lm_pg + ((size_t)seq * c.dm.Hq + (size_t)h * G) * c.dm.lm_cap;
+  float *pv = c.L.phi + 2 * hi.maw_off + (size_t)seq * 2 * hi.nbmax;
+  float *ps = pv + hi.nbmax;
+  for (int x = tid; x < nb; x += 256) ablk[x] = 0.0f;
+  __syncthreads();
+  const DenseList dl = dense_list(g);
+  const float inv_g = 1.0f / (float)G;
+  auto mass = [&](int slot_) {
+    float a = 0.0f;
+#pragma unroll
+    for (int gg = 0; gg < G; ++gg) {
+      const float x = ld_dev(&lmb[(size_t)gg * c.dm.lm_cap + slot_]);
+      a += (x == -INFINITY || lse_h[gg] == -INFINITY) ? 0.0f : fast_exp(x - lse_h[gg]);
+    }
+    return a * inv_g;
+  };
+  for (int t = tid; t < dl.n; t += 256) {
+    const int blk = div_S(dense_page(dl, t) * kPage, g.S);
+    atomicAdd(&ablk[blk], mass(t));
+  }
+  for (int t = tid; t < cnt * PPB; t += 256) {
+    const int blk = sel[t / PPB];
+    if (blk >= 0 && blk < nb) atomicAdd(&ablk[blk], mass(c.dm.lm_sel0 + t));
+  }
+  __syncthreads();
+  const float r = c.dm.maw_decay, omr = 1.0f - r;
+  for (int x = tid; x <= bb; x += 256) {
+    pv[x] = __fadd_rn(__fmul_rn(r, pv[x]), __fmul_rn(omr, ablk[x]));
+    ps[x] = __fadd_rn(__fmul_rn(r, ps[x]), __fmul_rn(omr, ablk[bb - x]));
+  }
+}
+
+// Table init from the last s prefill positions ([LFPS] Assumptions & free
+// parameters, s = 32, Eq. (4)): position p_u = N - s + u attends causally to
+// [0, p_u] (dense); k_lfps_init_mass writes its block masses (group mean)
+// to scratch A, then k_lfps_init_tables applies the s updates in order.
+// Grid of the first: (s, Hkv, sequences); two passes over the tokens: the
+// heads' max and sum, then the masses.
+template <int D, int G>
+__global__ __launch_bounds__(256) void k_lfps_init_mass(Ctx c, SeqBatch b, const uint16_t *__restrict__ qp,
+                                                        int s_steps, float *__restrict__ A) {
+  extern __shared__ __align__(16) float ablk[];
+  __shared__ float qs[G * D];
+  __shared__ float rf[8];
+  const int tid = threadIdx.x;
+  const int u = blockIdx.x, h = blockIdx.y, i = blockIdx.z;
+  const HeadInfo hi = c.heads[h];
+  const int seq = b.seq[i], N = b.len[i];
+  const int pos = N - s_steps + u;
+  const size_t arow = (((size_t)i * c.dm.Hkv + h) * s_steps + u) * c.dm.key_stride;
+  if (pos < 0) return;
+  const int nb = div_S(pos, hi.S) + 1;
+  for (int x = tid; x < G * D; x += 256)
+    qs[x] = __uint_as_float(
+        (uint32_t)qp[(((size_t)i * s_steps + u) * c.dm.Hq + (size_t)h * G) * D + x] << 16);
+  for (int x = tid; x < nb; x += 256) ablk[x] = 0.0f;
+  __syncthreads();
+  const int32_t *pts = c.L.pt + (size_t)seq * c.dm.pages_per_seq;
+  auto logits = [&](int j, float (&sc)[G]) {
+    const uint16_t *kr = c.L.k + (((size_t)pts[j >> 4] * c.dm.Hkv + h) * kPage + (j & 15)) * D;
+#pragma unroll
+    for (int gg = 0; gg < G; ++gg) sc[gg] = 0.0f;
+    for (int ch = 0; ch < D; ch += 8) {
+      const uint4 w = *reinterpret_cast<const uint4 *>(kr + ch);
+      const uint32_t ws[4] = {w.x, w.y, w.z, w.w};
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const float k0 = bf16_lo(ws[e]), k1 = bf16_hi(ws[e]);
+#pragma unroll
+        for (int gg = 0; gg < G; ++gg)
+          sc[gg] = fmaf(qs[gg * D + ch + 2 * e + 1], k1, fmaf(qs[gg * D + ch + 2 * e], k0, sc[gg]));
+      }
+    }
+#pragma unroll
+    for (int gg = 0; gg < G; ++gg) sc[gg] *= c.dm.scale_log2;  // log2 units
+  };
+  float mx[G], z[G];
+#pragma unroll
+  for (int gg = 0; gg < G; ++gg) mx[gg] = -INFINITY, z[gg] = 0.0f;
+  for (int j = tid; j <= pos; j += 256) {
+    float sc[G];
+    logits(j, sc);
+#pragma unroll
+    for (int gg = 0; gg < G; ++gg) {
+      if (sc[gg] > mx[gg]) {
+        z[gg] = z[gg] * exp2f(mx[gg] - sc[gg]) + 1.0f;
+        mx[gg] = sc[gg];
+      } else {
+        z[gg] += exp2f(sc[gg] - mx[gg]);
+      }
+    }
+  }
+  float lse[G];  // log2 units
+#pragma unroll
+  for (int gg = 0; gg < G; ++gg) {
+    const float M = wg_max_f32(mx[gg], rf);
+    float zz = mx[gg] == -INFINITY ? 0.0f : z[gg] * exp2f(mx[gg] - M);
+    zz = wave_sum(zz);
+    __syncthreads();
+    if ((tid & 63) == 0) rf[4 + (tid >> 6)] = zz;
+    __syncthreads();
+    lse[gg] = M + log2f((rf[4] + rf[5]) + (rf[6] + rf[7]));
+  }
+  const float inv_g = 1.0f / (float)G;
+  for (int j = tid; j <= pos; j += 256) {
+    float sc[G];
+    logits(j, sc);
+    float a = 0.0f;
+#pragma unroll
+    for (int gg = 0; gg < G; ++gg) a += exp2f(sc[gg] - lse[gg]);
+    atomicAdd(&ablk[div_S(j, hi.S)], a * inv_g);
+  }
+  __syncthreads();
+  for (int x = tid; x < nb; x += 256) A[arow + x] = ablk[x];
+}
+
+// The s updates in order (grid: Hkv, sequences).
+__global__ __launch_bounds__(256) void k_lfps_init_tables(Ctx c, SeqBatch b, int s_steps,
+                                                          const float *__restrict__ A) {
+  const int h = blockIdx.x, i = blockIdx.y;
+  const HeadInfo hi = c.heads[h];
+  const int seq = b.seq[i], N = b.len[i];
+  float *pv = c.L.phi + 2 * hi.maw_off + (size_t)seq * 2 * hi.nbmax;
+  float *ps = pv + hi.nbmax;
+  const int nb_all = div_S(N + hi.S - 1, hi.S);
+  const float r = c.dm.maw_decay, omr = 1.0f - r;
+  for (int x = threadIdx.x; x < hi.nbmax; x += 256) pv[x] = ps[x] = 0.0f;
+  __syncthreads();
+  for (int u = 0; u < s_steps; ++u) {
+    const int pos = N - s_steps + u;
+    if (pos < 0) continue;
+    const int bb = div_S(pos, hi.S);
+    const float *a = A + (((size_t)i * c.dm.Hkv + h) * s_steps + u) * c.dm.key_stride;
+    for (int x = threadIdx.x; x <= bb && x < nb_all; x += 256) {
+      pv[x] = __fadd_rn(__fmul_rn(r, pv[x]), __fmul_rn(omr, a[x]));
+      ps[x] = __fadd_rn(__fmul_rn(r, ps[x]), __fmul_rn(omr, a[bb - x]));
+    }
+    __syncthreads();
+  }
+}
+
 // Union of a KV head's per-query-head selections (one workgroup per
 // (KV head, sequence)): a byte of head bits per scored block in LDS, set from
 // the G lists, then compacted in block order into block | mask << 24 entries
@@ -2711,13 +3026,22 @@ template <int D, int G>
 __global__ __launch_bounds__(256) void k_fuse(Ctx c, SeqBatch b, int with_maw, int P,
                                               const float *__restrict__ o_part,
                                               const float *__restrict__ lse_part, int p_cap,
-                                              float *__restrict__ o, float *__restrict__ lse) {
+                                              float *__restrict__ o, float *__restrict__ lse,
+                                              const int32_t *__restrict__ sel_idx,
+                                              const int32_t *__restrict__ sel_cnt, int k_cap) {
   __shared__ FuseSmem<G> sm;
+  extern __shared__ __align__(16) float ablk[];  // the tables' block masses (lfps)
   const int h = blockIdx.x, i = blockIdx.y;
   const HeadInfo hi = c.heads[h];
   if (with_maw) {
     const UG g = unit_geom(b.len[i], hi, c.dm);
     fuse_unit<D, G>(c, i, h, unit_parts(g, P, c.dm), o_part, lse_part, p_cap, o, lse, sm);
+    if (c.dm.lfps && g.N > 0) {
+      const size_t row = (size_t)i * c.dm.Hkv + h;
+      const int cnt = min(min(max(sel_cnt[row], 0), k_cap), hi.kcap);
+      lfps_update_unit<D, G>(c, b.seq[i], h, hi, g, sel_idx + row * k_cap, cnt, sm.lse, ablk);
+      __syncthreads();
+    }
     dense_maw<D, G>(c, b.seq[i], h, hi, g, NewTok(), sm.pm, sm.dm, sm.dz);
   } else {
     fuse_unit<D, G>(c, i, h, p_cap, o_part, lse_part, p_cap, o, lse, sm);
@@ -2869,12 +3193,39 @@ hipError_t launch_step(const Ctx &c, const SeqBatch &b, int max_blocks, int P, c
 
 hipError_t launch_fuse(const Ctx &c, const SeqBatch &b, bool with_maw, int P,
                        const float *o_part, const float *lse_part, int32_t p_cap,
-                       float *o, float *lse, hipStream_t st) {
+                       float *o, float *lse, const int32_t *sel_idx, const int32_t *sel_cnt,
+                       int32_t k_cap, int max_blocks, hipStream_t st) {
   if (b.n <= 0) return hipSuccess;
   dim3 grid(c.dm.Hkv, b.n);
+  const size_t lds = (with_maw && c.dm.lfps) ? sizeof(float) * (size_t)max(1, max_blocks) : 0;
+  if (lds > 40960) return hipErrorInvalidValue;
   SD_DISPATCH_DG(c.dm.d, c.dm.G,
-                 hipLaunchKernelGGL((k_fuse<D_, G_>), grid, dim3(256), 0, st, c, b,
-                                    with_maw ? 1 : 0, P, o_part, lse_part, p_cap, o, lse));
+                 hipLaunchKernelGGL((k_fuse<D_, G_>), grid, dim3(256), lds, st, c, b,
+                                    with_maw ? 1 : 0, P, o_part, lse_part, p_cap, o, lse,
+                                    sel_idx, sel_cnt, k_cap));
+  return hipGetLastError();
+}
+
+hipError_t launch_lfps_select(const Ctx &c, const SeqBatch &b, int max_blocks, const uint16_t *q,
+                              int32_t *blk_idx, int32_t *blk_cnt, int32_t k_cap, hipStream_t st) {
+  if (b.n <= 0) return hipSuccess;
+  const size_t lds = sizeof(LfpsSmem) + sizeof(uint32_t) * (size_t)((max_blocks + 31) / 32 + 1);
+  if (lds > 65536) return hipErrorInvalidValue;
+  SD_DISPATCH_DG(c.dm.d, c.dm.G,
+                 hipLaunchKernelGGL((k_lfps_select<D_, G_>), dim3(c.dm.Hkv * b.n), dim3(256), lds,
+                                    st, c, b, blk_idx, blk_cnt, k_cap, q));
+  return hipGetLastError();
+}
+
+hipError_t launch_lfps_init(const Ctx &c, const SeqBatch &b, int max_blocks, const uint16_t *q_prefill,
+                            int s_steps, float *A, hipStream_t st) {
+  if (b.n <= 0 || s_steps <= 0) return hipSuccess;
+  const size_t lds = sizeof(float) * (size_t)max(1, max_blocks);
+  if (lds > 49152) return hipErrorInvalidValue;
+  SD_DISPATCH_DG(c.dm.d, c.dm.G,
+                 hipLaunchKernelGGL((k_lfps_init_mass<D_, G_>), dim3(s_steps, c.dm.Hkv, b.n),
+                                    dim3(256), lds, st, c, b, q_prefill, s_steps, A));
+  hipLaunchKernelGGL(k_lfps_init_tables, dim3(c.dm.Hkv, b.n), dim3(256), 0, st, c, b, s_steps, A);
   return hipGetLastError();
 }
 

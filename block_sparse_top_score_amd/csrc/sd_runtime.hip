@@ -58,6 +58,10 @@ struct sd_ctx {
   std::vector<int32_t> S, ppm;
   int D = 0, Hq = 0, Hkv = 0, G = 0, pps = 0, max_S = 0;
   bool pqh = false;  // one selection per query head
+  bool lfps = false;  // selection among the learn-from-the-past table candidates
+  // the selection the last attend call took (the table update reads it)
+  const int32_t *pend_idx = nullptr, *pend_cnt = nullptr;
+  int32_t pend_kcap = 0;
   int sel_rows = 0;  // selections per sequence: Hq with pqh, else Hkv
   hipStream_t stream = nullptr;
   int device = 0;
@@ -252,6 +256,14 @@ sd_status sd_validate_config(const sd_config *cfg, char *err, size_t err_len) {
     return bad("maw_beta must be finite");
   if (cfg->select_per_query_head != 0 && cfg->select_per_query_head != 1)
     return bad("select_per_query_head %d not in {0,1}", cfg->select_per_query_head);
+  if (cfg->lfps_select != 0 && cfg->lfps_select != 1)
+    return bad("lfps_select %d not in {0,1}", cfg->lfps_select);
+  if (cfg->lfps_select) {
+    if (!(cfg->lfps_a >= 0.0f && cfg->lfps_a <= 1.0f))
+      return bad("lfps_a %g outside [0,1]", (double)cfg->lfps_a);
+    if (cfg->maw_beta > 0.0f) return bad("lfps_select ranks no MAW flags: maw_beta must be <= 0");
+    if (cfg->select_per_query_head) return bad("lfps_select selects per KV head");
+  }
   if (err && err_len) err[0] = 0;
   return SD_OK;
 #undef bad
@@ -274,6 +286,7 @@ sd_status sparse_decode_init(const sd_config *cfg, sd_ctx **out) {
   c->Hkv = cfg->num_kv_heads;
   c->G = c->Hq / c->Hkv;
   c->pqh = cfg->select_per_query_head == 1;
+  c->lfps = cfg->lfps_select == 1;
   c->sel_rows = c->pqh ? c->Hq : c->Hkv;
   c->D = cfg->head_dim;
   c->pps = (int)cdiv(cfg->max_seq_len, kPage);
@@ -349,10 +362,14 @@ sd_status sparse_decode_init(const sd_config *cfg, sd_ctx **out) {
   key_stride = (int)cdiv(key_stride, 256) * 256;
   c->dims.key_stride = key_stride;
   c->dims.lm_sel0 = lm_sel0;
-  c->dims.lm_cap = lm_sel0;  // the dense pages' log-masses (MAW's input)
+  // the dense pages' log-masses (MAW's input); with the tables also the
+  // selected pages'
+  c->dims.lm_cap = c->lfps ? lm_sel0 + sel_pages : lm_sel0;
   c->dims.kcap = c->k_cap;
   c->dims.pqh = c->pqh ? 1 : 0;
   c->dims.ucap = (int32_t)ucap;
+  c->dims.lfps = c->lfps ? 1 : 0;
+  c->dims.lfps_a = cfg->lfps_a;
 
   // scratch (the selection's per-unit arrays are per query head with one
   // set per query head)
@@ -427,6 +444,10 @@ sd_status sparse_decode_init(const sd_config *cfg, sd_ctx **out) {
     if ((s = dev_alloc(c, &L.dev.pt, (size_t)max_seqs * c->pps)) != SD_OK) return s;
     if ((s = dev_alloc(c, &L.dev.summ, (size_t)summ_elems)) != SD_OK) return s;
     if ((s = dev_alloc(c, &L.dev.maw, (size_t)maw_elems)) != SD_OK) return s;
+    if (c->lfps) {
+      if ((s = dev_alloc(c, &L.dev.phi, (size_t)maw_elems * 2)) != SD_OK) return s;
+      SD_HIP(c, hipMemset(L.dev.phi, 0, sizeof(float) * maw_elems * 2));
+    }
     SD_HIP(c, hipMemset(L.dev.pt, 0, sizeof(int32_t) * max_seqs * c->pps));
     SD_HIP(c, hipMemset(L.dev.maw, 0, sizeof(float) * maw_elems));
     SD_HIP(c, hipMemset(L.dev.summ, 0, sizeof(uint16_t) * summ_elems));
@@ -660,8 +681,12 @@ sd_status select_topk(sd_ctx *c, int32_t layer, int32_t n_seqs,
     int mb = 0;
     fill_batch(c, layer, seq_ids, base, std::min(kLaunchSeqs, n_seqs - base), &b, &mb);
     const uint16_t *qb = q + (size_t)base * c->Hq * c->D;
-    SD_HIP(c, launch_select(kc, b, mb, qb, blk_idx + (size_t)base * c->sel_rows * k_cap,
-                            blk_cnt + (size_t)base * c->sel_rows, k_cap, c->stream));
+    if (c->lfps)
+      SD_HIP(c, launch_lfps_select(kc, b, mb, qb, blk_idx + (size_t)base * c->Hkv * k_cap,
+                                   blk_cnt + (size_t)base * c->Hkv, k_cap, c->stream));
+    else
+      SD_HIP(c, launch_select(kc, b, mb, qb, blk_idx + (size_t)base * c->sel_rows * k_cap,
+                              blk_cnt + (size_t)base * c->sel_rows, k_cap, c->stream));
   }
   return SD_OK;
 }
@@ -701,6 +726,9 @@ sd_status sparse_attend(sd_ctx *c, int32_t layer, int32_t n_seqs,
   c->pend_layer = layer;
   c->pend_seqs.assign(seq_ids, seq_ids + n_seqs);
   c->pend_pcap = p_cap;
+  c->pend_idx = blk_idx;
+  c->pend_cnt = blk_cnt;
+  c->pend_kcap = k_cap;
   return SD_OK;
 }
 
@@ -733,8 +761,9 @@ sd_status fuse_lse(sd_ctx *c, int32_t layer, int32_t n_seqs,
   for (int base = 0; base < n_seqs; base += kLaunchSeqs) {
     SeqBatch b;
     const int n = std::min(kLaunchSeqs, n_seqs - base);
+    int mb = 0;
     if (with_maw) {
-      fill_batch(c, layer, seq_ids, base, n, &b, nullptr);
+      fill_batch(c, layer, seq_ids, base, n, &b, &mb);
     } else {
       b.n = n;
       b.max_scored = 0;
@@ -744,10 +773,71 @@ sd_status fuse_lse(sd_ctx *c, int32_t layer, int32_t n_seqs,
     SD_HIP(c, launch_fuse(kc, b, with_maw, P, o_part + (size_t)base * c->Hq * p_cap * c->D,
                           lse_part + (size_t)base * c->Hq * p_cap, p_cap,
                           o + (size_t)base * c->Hq * c->D, lse + (size_t)base * c->Hq,
-                          c->stream));
+                          c->pend_idx ? c->pend_idx + (size_t)base * c->Hkv * c->pend_kcap : nullptr,
+                          c->pend_cnt ? c->pend_cnt + (size_t)base * c->Hkv : nullptr,
+                          c->pend_kcap, mb, c->stream));
   }
   if (with_maw) c->pend_layer = -2;
   return SD_OK;
+}
+
+sd_status sd_debug_set_lfps(sd_ctx *c, int32_t layer, int32_t seq,
+                            const float *host_src, size_t bytes) {
+  if (!c) return SD_EINVAL;
+  size_t need = 0;
+  const sd_status st = sd_debug_bytes(c, SD_DEBUG_LFPS, layer, seq, &need);
+  if (st != SD_OK) return fail(c, st, "bad table request (layer %d, seq %d)", layer, seq);
+  if (bytes != need || (need && !host_src))
+    return fail(c, SD_EINVAL, "table upload needs %zu bytes, got %zu", need, bytes);
+  SD_HIP(c, hipStreamSynchronize(c->stream));
+  const int64_t len = c->layers[layer].len[seq];
+  for (int h = 0; h < c->Hkv; ++h) {
+    const HeadInfo &hi = c->heads[h];
+    const int64_t nb = cdiv(len, hi.S);
+    float *dst = c->layers[layer].dev.phi + 2 * hi.maw_off + (size_t)seq * 2 * hi.nbmax;
+    if (nb) {
+      SD_HIP(c, hipMemcpy(dst, host_src, sizeof(float) * nb, hipMemcpyHostToDevice));
+      SD_HIP(c, hipMemcpy(dst + hi.nbmax, host_src + nb, sizeof(float) * nb,
+                          hipMemcpyHostToDevice));
+    }
+    host_src += 2 * nb;
+  }
+  return SD_OK;
+}
+
+sd_status sd_lfps_init(sd_ctx *c, int32_t layer, int32_t n_seqs, const int32_t *seq_ids,
+                       const void *q_prefill, int32_t s_steps) {
+  if (!c) return SD_EINVAL;
+  if (!c->lfps) return fail(c, SD_EUNSUPPORTED, "sd_lfps_init needs lfps_select");
+  sd_status s = check_seqs(c, layer, n_seqs, seq_ids);
+  if (s != SD_OK) return s;
+  if (n_seqs == 0) return SD_OK;
+  if (!q_prefill) return fail(c, SD_EINVAL, "q_prefill is NULL");
+  if (s_steps < 1) return fail(c, SD_EINVAL, "s_steps %d < 1", s_steps);
+  for (int i = 0; i < n_seqs; ++i)
+    if (c->layers[layer].len[seq_ids[i]] < s_steps)
+      return fail(c, SD_EINVAL, "sequence %d holds %d tokens, fewer than s_steps %d", seq_ids[i],
+                  c->layers[layer].len[seq_ids[i]], s_steps);
+  const Ctx kc = kctx(c, layer);
+  const uint16_t *q = static_cast<const uint16_t *>(q_prefill);
+  const int n0 = std::min(kLaunchSeqs, n_seqs);
+  float *A = nullptr;
+  SD_HIP(c, hipMalloc(reinterpret_cast<void **>(&A),
+                      sizeof(float) * (size_t)n0 * c->Hkv * s_steps * c->dims.key_stride));
+  sd_status st = SD_OK;
+  for (int base = 0; base < n_seqs && st == SD_OK; base += kLaunchSeqs) {
+    SeqBatch b;
+    int mb = 0;
+    fill_batch(c, layer, seq_ids, base, std::min(kLaunchSeqs, n_seqs - base), &b, &mb);
+    const hipError_t e = launch_lfps_init(kc, b, mb, q + (size_t)base * s_steps * c->Hq * c->D,
+                                          s_steps, A, c->stream);
+    if (e != hipSuccess) st = fail(c, SD_EHIP, "table init launch failed: %s", hipGetErrorString(e));
+  }
+  const hipError_t e1 = hipStreamSynchronize(c->stream);
+  const hipError_t e2 = hipFree(A);
+  if (st == SD_OK && (e1 != hipSuccess || e2 != hipSuccess))
+    st = fail(c, SD_EHIP, "table init: %s", hipGetErrorString(e1 != hipSuccess ? e1 : e2));
+  return st;
 }
 
 }  // extern "C"
@@ -765,10 +855,10 @@ sd_status decode_step_impl(sd_ctx *c, int32_t layer, int32_t n_seqs, const int32
                            const Scratch &sc, uint32_t *clear, size_t clear_words) {
   sd_status s = check_seqs(c, layer, n_seqs, seq_ids);
   if (s != SD_OK) return s;
-  if (c->pqh)
+  if (c->pqh || c->lfps)
     return fail(c, SD_EUNSUPPORTED,
-                "the one-launch step selects per KV head; with select_per_query_head use "
-                "select_topk, sparse_attend and fuse_lse");
+                "the one-launch step ranks every block per KV head; with %s use select_topk, "
+                "sparse_attend and fuse_lse", c->pqh ? "select_per_query_head" : "lfps_select");
   if (n_seqs == 0) return SD_OK;
   if (!q_bf16 || !blk_idx || !blk_cnt || !o_part || !lse_part || !o || !lse)
     return fail(c, SD_EINVAL, "a device pointer is NULL");
@@ -890,6 +980,9 @@ sd_status sd_release_seq(sd_ctx *c, int32_t seq) {
       const HeadInfo &hi = c->heads[h];
       SD_HIP(c, launch_fill_f32(L.dev.maw + hi.maw_off + (size_t)seq * hi.nbmax,
                                 hi.nbmax, 0.0f, c->stream));
+      if (L.dev.phi)
+        SD_HIP(c, launch_fill_f32(L.dev.phi + 2 * hi.maw_off + (size_t)seq * 2 * hi.nbmax,
+                                  2 * hi.nbmax, 0.0f, c->stream));
     }
   }
   if (c->pend_layer >= 0 &&
@@ -916,8 +1009,16 @@ sd_status sd_debug_bytes(const sd_ctx *c, int32_t what, int32_t layer,
       break;
     case SD_DEBUG_K:
     case SD_DEBUG_V: b = sizeof(uint16_t) * len * c->Hkv * c->D; break;
+    case SD_DEBUG_LFPS_CAND:
+      if (!c->lfps) return SD_EUNSUPPORTED;
+      b = sizeof(int32_t) * c->Hkv;
+      break;
+    case SD_DEBUG_LFPS:
+      if (!c->lfps) return SD_EUNSUPPORTED;
+      for (int h = 0; h < c->Hkv; ++h) b += sizeof(float) * 2 * cdiv(len, c->S[h]);
+      break;
     case SD_DEBUG_SCORES:
-      if (c->pqh) return SD_EUNSUPPORTED;  // (the keys are per query head)
+      if (c->pqh || c->lfps) return SD_EUNSUPPORTED;  // (other key layouts)
       for (int h = 0; h < c->Hkv; ++h) b += sizeof(float) * (1 + cdiv(len, c->S[h]));
       break;
     default: return SD_EINVAL;
@@ -965,6 +1066,23 @@ sd_status sd_debug_copy(sd_ctx *c, int32_t what, int32_t layer, int32_t seq,
         SD_HIP(c, hipMemcpy(dst, L.dev.maw + hi.maw_off + (size_t)seq * hi.nbmax,
                             sizeof(float) * nb, hipMemcpyDeviceToHost));
       dst += nb;
+    }
+  } else if (what == SD_DEBUG_LFPS_CAND) {
+    int32_t *dst = static_cast<int32_t *>(host_dst);
+    for (int h = 0; h < c->Hkv; ++h)
+      SD_HIP(c, hipMemcpy(dst + h, c->sc.unit_acc + 4 * ((size_t)seq * c->Hkv + h) + 3,
+                          sizeof(int32_t), hipMemcpyDeviceToHost));
+  } else if (what == SD_DEBUG_LFPS) {
+    float *dst = static_cast<float *>(host_dst);
+    for (int h = 0; h < c->Hkv; ++h) {
+      const HeadInfo &hi = c->heads[h];
+      const int64_t nb = cdiv(len, hi.S);
+      const float *src = L.dev.phi + 2 * hi.maw_off + (size_t)seq * 2 * hi.nbmax;
+      if (nb) {
+        SD_HIP(c, hipMemcpy(dst, src, sizeof(float) * nb, hipMemcpyDeviceToHost));
+        SD_HIP(c, hipMemcpy(dst + nb, src + hi.nbmax, sizeof(float) * nb, hipMemcpyDeviceToHost));
+      }
+      dst += 2 * nb;
     }
   } else if (what == SD_DEBUG_SCORES) {
     // the unit's keys as its score tiles wrote them (order key of the fp32

@@ -104,6 +104,23 @@ typedef struct {
                                     head's sets are read once, each query head
                                     attends D and its own blocks; the
                                     one-launch step returns SD_EUNSUPPORTED */
+  int32_t lfps_select;    /* 1: select among the candidates of the
+                             learn-from-the-past tables ([LFPS] What carries
+                             the argument, Figure 4) at block granularity: a
+                             vertical table per block and a slash table per
+                             block offset from the newest block; candidates
+                             above tau = mean + a (max - mean) of either table,
+                             grown by the offsets {-1,0,1,2} and kept when above
+                             a table's mean and outside D; only they are scored
+                             (exact group bound), the k = min(|C|, budget)
+                             best taken.  fuse_lse then updates the tables with
+                             decay maw_decay by each block's mass under the
+                             softmax over the attended set.  Needs maw_beta <= 0
+                             and select_per_query_head = 0; the one-launch step
+                             returns SD_EUNSUPPORTED.  Tables start at 0
+                             (sd_lfps_init fills them from the prefill)       */
+  float lfps_a;           /* the threshold parameter a in [0, 1] ([LFPS]
+                             Assumptions & free parameters: 0.2)             */
 } sd_config;
 
 /* Host-only check of a configuration (no device is touched).  err may be NULL;
@@ -256,6 +273,18 @@ sd_status sd_seq_len(const sd_ctx *ctx, int32_t layer, int32_t seq_id,
 /* Wait for all work on the context's stream; reports deferred HIP errors. */
 sd_status sd_sync(sd_ctx *ctx);
 
+/* Learn-from-the-past tables of one layer from the prefill ([LFPS]
+ * Assumptions & free parameters: the last s = 32 prefill steps initialise the
+ * tables, Eq. (4)): for each sequence the queries of its last s_steps
+ * positions p = N - s_steps + u, u = 0 .. s_steps-1 (q_prefill: dev
+ * [n_seqs][s_steps][Hq][d] bf16), each attending causally and densely to
+ * [0, p]; the tables are zeroed, then take the s_steps block-mass updates in
+ * order.  Needs lfps_select; SD_EINVAL for s_steps < 1 or more than N of a
+ * sequence.  Allocates and frees a scratch of n_seqs * Hkv * s_steps *
+ * max_blocks floats (not for use inside graph capture). */
+sd_status sd_lfps_init(sd_ctx *ctx, int32_t layer, int32_t n_seqs, const int32_t *seq_ids,
+                       const void *q_prefill, int32_t s_steps);
+
 /* Text of the last error on this context (never NULL). */
 const char *sd_last_error(const sd_ctx *ctx);
 
@@ -268,6 +297,11 @@ const char *sd_last_error(const sd_ctx *ctx);
  *                        [ceil(len/S_h)][d][2] = (min, max)
  *   SD_DEBUG_MAW         for each KV head h in order: fp32 [ceil(len/S_h)]
  *   SD_DEBUG_K / _V      bf16 [len][Hkv][d], gathered through the page table
+ *   SD_DEBUG_LFPS        for each KV head h in order: fp32 [2][ceil(len/S_h)],
+ *                        the vertical table by block, then the slash table by
+ *                        block offset (SD_EUNSUPPORTED without lfps_select)
+ *   SD_DEBUG_LFPS_CAND   int32 [Hkv]: the number of table candidates |C| of
+ *                        each KV head's last select_topk (lfps_select only)
  *   SD_DEBUG_SCORES      for each KV head h in order: fp32 [1 + ceil(len/S_h)]:
  *                        element 0 the error bound eps the head's last
  *                        selection used, then per block the approximate group
@@ -289,6 +323,8 @@ const char *sd_last_error(const sd_ctx *ctx);
 #define SD_DEBUG_K 3
 #define SD_DEBUG_V 4
 #define SD_DEBUG_SCORES 5
+#define SD_DEBUG_LFPS 6
+#define SD_DEBUG_LFPS_CAND 7
 sd_status sd_debug_bytes(const sd_ctx *ctx, int32_t what, int32_t layer,
                          int32_t seq_id, size_t *bytes);
 sd_status sd_debug_copy(sd_ctx *ctx, int32_t what, int32_t layer,
@@ -298,6 +334,11 @@ sd_status sd_debug_copy(sd_ctx *ctx, int32_t what, int32_t layer,
  * out as SD_DEBUG_MAW (test hook for threshold cases; waits for the stream). */
 sd_status sd_debug_set_maw(sd_ctx *ctx, int32_t layer, int32_t seq_id,
                            const float *host_src, size_t bytes);
+
+/* Overwrite the learn-from-the-past tables of one (layer, sequence) from host
+ * fp32 values laid out as SD_DEBUG_LFPS (test hook; waits for the stream). */
+sd_status sd_debug_set_lfps(sd_ctx *ctx, int32_t layer, int32_t seq_id,
+                            const float *host_src, size_t bytes);
 
 /* Streaming-read probe, for measurement only (no part of the decode path):
  * the HBM read rate a plain kernel reaches on this GPU, against which the
