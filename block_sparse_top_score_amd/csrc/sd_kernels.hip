@@ -836,6 +836,59 @@ __device__ double exact_score_quad(const Ctx &c, int seq, const HeadInfo &hi, in
   return ps;
 }
 
+// Exact group scores of NB blocks per lane quad (the quad's lanes split the
+// channels): every block's summary is loaded once, then each head's sum is
+// taken as in exact_score_quad (the quad's partial sums where that order is
+// exact, else the plain sum in channel order); best: the maximum over the G
+// heads (qs: LDS [G][D]).  Every lane of the wave takes part.
+template <int D, int G, int NB>
+__device__ __forceinline__ void exact_group_quads(const Ctx &c, int seq, const HeadInfo &hi,
+                                                  const int (&blk)[NB], const bool (&on)[NB],
+                                                  const float *qs, double (&best)[NB]) {
+  constexpr int C4 = D / 4, P4 = C4 / 4;
+  const int part = threadIdx.x & 3;
+  const uint4 *sp = reinterpret_cast<const uint4 *>(c.L.summ + hi.summ_off +
+                                                    (size_t)seq * C4 * hi.nbmax * 8);
+  uint4 w[NB][P4];
+#pragma unroll
+  for (int n = 0; n < NB; ++n)
+#pragma unroll
+    for (int t = 0; t < P4; ++t)
+      w[n][t] = on[n] ? sp[(size_t)(part * P4 + t) * hi.nbmax + blk[n]] : make_uint4(0, 0, 0, 0);
+#pragma unroll
+  for (int n = 0; n < NB; ++n) best[n] = -INFINITY;
+#pragma unroll 1
+  for (int hh = 0; hh < G; ++hh) {
+    const float *qh = qs + hh * D;
+#pragma unroll
+    for (int n = 0; n < NB; ++n) {
+      double ps = 0.0, sabs = 0.0;
+      int emin = 4096;
+#pragma unroll
+      for (int t = 0; t < P4; ++t) {
+        const uint32_t ws[4] = {w[n][t].x, w[n][t].y, w[n][t].z, w[n][t].w};
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          const float qv = qh[4 * (part * P4 + t) + j];
+          const double pr = (double)qv * (double)upper_term(qv, ws[j]);
+          ps += pr;
+          sabs += fabs(pr);
+          emin = min(emin, pr != 0.0 ? __builtin_amdgcn_frexp_exp(pr) : 4096);
+        }
+      }
+      ps += dpp_quad_f64(ps, 1);
+      ps += dpp_quad_f64(ps, 2);
+      sabs += dpp_quad_f64(sabs, 1);
+      sabs += dpp_quad_f64(sabs, 2);
+      emin = min(emin, dpp_quad_i32(emin, 1));
+      emin = min(emin, dpp_quad_i32(emin, 2));
+      const bool exact = sabs == 0.0 || __builtin_amdgcn_frexp_exp(sabs) <= emin + 36;
+      if (on[n] && !exact) ps = exact_score_seq<D>(c, seq, hi, blk[n], qh);
+      best[n] = fmax(best[n], ps);
+    }
+  }
+}
+
 // ---------------------------------------------------------------------------
 // Top-k of one unit, in one wave, ordered by (MAW flag desc, exact fp32 score
 // desc, index asc) ([FLX] per-head top-k; [HGCA] MAW threshold first; R5,
@@ -2515,7 +2568,7 @@ __global__ __launch_bounds__(256) void k_lfps_select(Ctx c, SeqBatch b, int32_t 
                                                      const uint16_t *__restrict__ q) {
   extern __shared__ __align__(16) unsigned char smem_raw[];
   LfpsSmem &sm = *reinterpret_cast<LfpsSmem *>(smem_raw);
-  uint32_t *c0w = reinterpret_cast<uint32_t *>(smem_raw + sizeof(LfpsSmem));  // C0 bits
+  uint32_t *c0w = reinterpret_cast<uint32_t *>(smem_raw + sizeof(LfpsSmem));  // bit rows
   const int tid = threadIdx.x;
   const int h = blockIdx.x % c.dm.Hkv, i = blockIdx.x / c.dm.Hkv;
   const HeadInfo hi = c.heads[h];
@@ -2537,15 +2590,27 @@ __global__ __launch_bounds__(256) void k_lfps_select(Ctx c, SeqBatch b, int32_t 
   auto key_st = [&](int p, uint32_t v) { if (p < kLfpsLds) sm.key[p] = v; else st_dev(&gk[p], v); };
   const uint16_t *qg = q + out * G * D;
   for (int x = tid; x < G * D; x += 256) sm.qs[x] = __uint_as_float((uint32_t)qg[x] << 16);
-  // 1. mean and maximum of each table over [0, b]
+  // 1. mean and maximum of each table over [0, b] (eight loads in flight per
+  // thread and table)
+  constexpr int LB = 8;
   double sv = 0.0, ss = 0.0;
   float mv = -INFINITY, ms = -INFINITY;
-  for (int t = tid; t <= bb; t += 256) {
-    const float a = pv[t], e = ps[t];
-    sv += (double)a;
-    ss += (double)e;
-    mv = fmaxf(mv, a);
-    ms = fmaxf(ms, e);
+  for (int t0 = tid; t0 <= bb; t0 += 256 * LB) {
+    float a[LB], e[LB];
+#pragma unroll
+    for (int u = 0; u < LB; ++u) {
+      const int t = t0 + 256 * u;
+      a[u] = t <= bb ? pv[t] : 0.0f;
+      e[u] = t <= bb ? ps[t] : 0.0f;
+    }
+#pragma unroll
+    for (int u = 0; u < LB; ++u) {
+      if (t0 + 256 * u > bb) break;
+      sv += (double)a[u];
+      ss += (double)e[u];
+      mv = fmaxf(mv, a[u]);
+      ms = fmaxf(ms, e[u]);
+    }
   }
   sv = wg_sum_f64(sv, sm.rd);
   ss = wg_sum_f64(ss, sm.rd + 4);
@@ -2554,17 +2619,32 @@ __global__ __launch_bounds__(256) void k_lfps_select(Ctx c, SeqBatch b, int32_t 
   const double mu_v = sv / (double)nb, mu_s = ss / (double)nb;
   const double a = (double)c.dm.lfps_a;
   const double tau_v = mu_v + a * ((double)mv - mu_v), tau_s = mu_s + a * ((double)ms - mu_s);
-  // 2. C0 over [0, b], as bits
+  // 2. over [0, b], as bits: C0 (above a threshold) and "above a mean"
   const int words = (nb + 31) >> 5;
-  for (int w = tid; w < words; w += 256) c0w[w] = 0u;
+  uint32_t *abw = c0w + words;
+  for (int w = tid; w < 2 * words; w += 256) c0w[w] = 0u;
   __syncthreads();
-  for (int t = tid; t <= bb; t += 256)
-    if ((double)pv[t] > tau_v || (double)ps[bb - t] > tau_s) atomicOr(&c0w[t >> 5], 1u << (t & 31));
+  for (int t0 = tid; t0 <= bb; t0 += 256 * LB) {
+    float a[LB], e[LB];
+#pragma unroll
+    for (int u = 0; u < LB; ++u) {
+      const int t = t0 + 256 * u;
+      a[u] = t <= bb ? pv[t] : 0.0f;
+      e[u] = t <= bb ? ps[bb - t] : 0.0f;
+    }
+#pragma unroll
+    for (int u = 0; u < LB; ++u) {
+      const int t = t0 + 256 * u;
+      if (t > bb) break;
+      if ((double)a[u] > tau_v || (double)e[u] > tau_s) atomicOr(&c0w[t >> 5], 1u << (t & 31));
+      if ((double)a[u] > mu_v || (double)e[u] > mu_s) atomicOr(&abw[t >> 5], 1u << (t & 31));
+    }
+  }
   __syncthreads();
   auto c0 = [&](int x) -> bool { return x >= 0 && x <= bb && ((c0w[x >> 5] >> (x & 31)) & 1u); };
   auto in_c = [&](int x) -> bool {
-    if (!is_candidate(g, x) || !(c0(x + 1) || c0(x) || c0(x - 1) || c0(x - 2))) return false;
-    return (double)pv[x] > mu_v || (double)ps[bb - x] > mu_s;
+    return is_candidate(g, x) && (c0(x + 1) || c0(x) || c0(x - 1) || c0(x - 2)) &&
+           ((abw[x >> 5] >> (x & 31)) & 1u);
   };
   // 3. C in block order: thread t takes blocks [t m, t m + m) of the scored ones
   const int n_sc = g.n_sc, m = cdiv(n_sc, 256), j0 = tid * m;
@@ -2581,16 +2661,22 @@ __global__ __launch_bounds__(256) void k_lfps_select(Ctx c, SeqBatch b, int32_t 
     if (tid == 0) st_dev(&blk_cnt[out], 0);
     return;
   }
-  // 4. exact group scores: one lane quad per block, the heads in turn
-  for (int p0 = 0; p0 < nC; p0 += 64) {
-    const int p = p0 + (tid >> 2);
-    const bool on = p < nC;
-    const int blk = on ? lst_ld(p) : 0;
-    double best = -INFINITY;
-#pragma unroll 1
-    for (int hh = 0; hh < G; ++hh)
-      best = fmax(best, exact_score_quad<D>(c, seq, hi, blk, sm.qs + hh * D, on));
-    if (on && (tid & 3) == 0) key_st(p, order_key((float)best));
+  // 4. exact group scores: one lane quad per two blocks, each block's summary
+  // loaded once for all the group's heads
+  for (int p0 = 0; p0 < nC; p0 += 128) {
+    int blk[2];
+    bool on[2];
+#pragma unroll
+    for (int n = 0; n < 2; ++n) {
+      const int p = p0 + 64 * n + (tid >> 2);
+      on[n] = p < nC;
+      blk[n] = on[n] ? lst_ld(p) : 0;
+    }
+    double best[2];
+    exact_group_quads<D, G, 2>(c, seq, hi, blk, on, sm.qs, best);
+#pragma unroll
+    for (int n = 0; n < 2; ++n)
+      if (on[n] && (tid & 3) == 0) key_st(p0 + 64 * n + (tid >> 2), order_key((float)best[n]));
   }
   __syncthreads();
   // 5. the kq-th largest key T: keys above T are in, of the keys equal to T
@@ -3209,7 +3295,7 @@ hipError_t launch_fuse(const Ctx &c, const SeqBatch &b, bool with_maw, int P,
 hipError_t launch_lfps_select(const Ctx &c, const SeqBatch &b, int max_blocks, const uint16_t *q,
                               int32_t *blk_idx, int32_t *blk_cnt, int32_t k_cap, hipStream_t st) {
   if (b.n <= 0) return hipSuccess;
-  const size_t lds = sizeof(LfpsSmem) + sizeof(uint32_t) * (size_t)((max_blocks + 31) / 32 + 1);
+  const size_t lds = sizeof(LfpsSmem) + sizeof(uint32_t) * 2 * (size_t)((max_blocks + 31) / 32 + 1);
   if (lds > 65536) return hipErrorInvalidValue;
   SD_DISPATCH_DG(c.dm.d, c.dm.G,
                  hipLaunchKernelGGL((k_lfps_select<D_, G_>), dim3(c.dm.Hkv * b.n), dim3(256), lds,
