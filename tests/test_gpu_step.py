@@ -65,6 +65,17 @@ def test_fused_sweep_points(B, S, pct):
     _check(harness.run_single_step(synth.sweep(B, S, pct), 22, fused=True))
 
 
+@pytest.mark.parametrize("B", [1, 8, 32, 64])
+@pytest.mark.parametrize("S", [16, 32, 64])
+@pytest.mark.parametrize("pct", [2, 5, 10])
+def test_fused_sweep_grid_sampled(B, S, pct):
+    """Every point of the batch x block size x budget sweep in the one-launch
+    form, four sampled sequences (all when fewer) against the oracle."""
+    log("case: fused sweep grid B=%d S=%d budget=%d%%" % (B, S, pct))
+    units = sorted({(b, 0) for b in (0, B // 3, (2 * B) // 3, B - 1)})
+    _check(harness.run_single_step(synth.sweep(B, S, pct), 23, fused=True, units=units))
+
+
 def test_fused_llama32k_full():
     """The benchmarked workload at full size, every unit against the oracle."""
     log("case: fused llama32k full")
@@ -142,6 +153,49 @@ def test_qwen128k_drift_multistep_fused():
             st = harness.check_units(w, eng, 0, list(range(w.B)), synth.bits(q), K_bits,
                                      V_bits, {b: N for b in range(w.B)}, gpu,
                                      check_summ=(e == 0))
+            _check(st)
+    finally:
+        eng.close()
+
+
+def test_qwen128k_drift_consecutive_steps_across_epoch():
+    """qwen128k at full size: eight consecutive decode steps (60 .. 67, each
+    with its one-token append) that cross the boundary between the first and
+    the second planted set at step 64; four sampled units against the oracle
+    at every step."""
+    w = synth.qwen128k(0)
+    log("case: qwen128k drift, consecutive steps 60..67")
+    seed, N0 = 6, w.N - 8
+    qe, dirs = synth.drift_setup(w, seed, 4, device="cuda")
+    K, V, _ = synth.prefill_with_directions(w, seed, 0, N0, dirs, device="cuda")
+    units = [(0, 0), (1, 1), (2, 2), (3, 3)]
+    eng = harness.make_engine(w, w.N + 64)
+    try:
+        harness.prefill(eng, 0, K, V)
+        Kb, Vb = synth.bits(K), synth.bits(V)
+        del K, V
+        K_bits = {b: Kb[b] for b in range(w.B)}
+        V_bits = {b: Vb[b] for b in range(w.B)}
+        N = N0
+        bufs = eng.alloc_step(w.B)
+        for step in range(60, 68):
+            kn, vn = synth.step_kv(w, seed, 0, step, device="cuda")
+            q = synth.drift_query(w, seed, step, qe, device="cuda")
+            eng.decode_step(0, list(range(w.B)), q, bufs["blk_idx"], bufs["blk_cnt"],
+                            bufs["o_part"], bufs["lse_part"], bufs["o"], bufs["lse"],
+                            k_new=kn.view(w.B, w.Hkv, w.d).contiguous(),
+                            v_new=vn.view(w.B, w.Hkv, w.d).contiguous())
+            eng.sync()
+            gpu = {k: v.cpu().numpy() for k, v in bufs.items()}
+            N += 1
+            knb, vnb = synth.bits(kn), synth.bits(vn)
+            for b in range(w.B):
+                K_bits[b] = np.concatenate([K_bits[b], knb[b]], 0)
+                V_bits[b] = np.concatenate([V_bits[b], vnb[b]], 0)
+            log("  step %d (epoch %d) N=%d" % (step, step // 64, N))
+            st = harness.check_units(w, eng, 0, list(range(w.B)), synth.bits(q), K_bits,
+                                     V_bits, {b: N for b in range(w.B)}, gpu, units=units,
+                                     check_summ=(step == 60))
             _check(st)
     finally:
         eng.close()
