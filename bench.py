@@ -555,9 +555,10 @@ def timeline(args, w, eng, step, s0, L):
              out["last_event_us"]["max"]), flush=True)
 
 
-def read_ceiling(nbytes, kstep_gbs, n_buf=8, reps=64, wgs=8192):
+def read_ceiling(nbytes, kstep_gbs, n_buf=8, reps=64, wgs=4096):
     """A plain streaming read on the same GPU, for context: the library's read
-    probe (each 16-byte word once, coalesced, 8192 workgroups) over n_buf
+    probe (each 16-byte word once, coalesced, eight in flight per thread, 4096
+    workgroups) over n_buf
     rotating buffers of the step's algorithmic size (8 x ~106 MB, so the reads
     are not served from the 256 MB last-level cache), timed with events on
     torch's stream.  `k_step_frac` is k_step's rate over this one."""
@@ -588,7 +589,7 @@ def read_ceiling(nbytes, kstep_gbs, n_buf=8, reps=64, wgs=8192):
     t_ms = ea.elapsed_time(eb) / reps
     gbs = n / (t_ms * 1e-3) / 1e9
     del bufs
-    return {"kind": "k_read_probe, %d rotating buffers, %d workgroups" % (n_buf, wgs), "bytes": n,
+    return {"kind": "k_read_probe, %d rotating buffers, %d workgroups, 8 loads in flight per thread" % (n_buf, wgs), "bytes": n,
             "ms": t_ms, "achieved_GBs": gbs, "frac_of_8TBs": gbs / HBM_PEAK_GBS,
             "k_step_frac": kstep_gbs / gbs}
 

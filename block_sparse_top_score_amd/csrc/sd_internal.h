@@ -68,7 +68,8 @@ struct AppendBatch {
 
 // Device state of one layer.
 struct LayerDev {
-  uint16_t *k;     // [num_pages][Hkv][16][d] bf16
+  uint16_t *k;     // [num_pages][Hkv][d/8][16][8] bf16: per page and head, each group of
+                   // 8 channels holds the 16 tokens' values contiguously (256 B)
   uint16_t *v;     // [num_pages][Hkv][d][16] bf16: V pages stored transposed
   int32_t *pt;     // [max_seqs][pages_per_seq]
   uint16_t *summ;  // per head h: [max_seqs][d/4][nbmax_h][8] bf16

@@ -242,7 +242,8 @@ __device__ void append_scatter(const Ctx &c, const AppendBatch &b, int i,
     const int h = r / V8, c8 = r - h * V8;
     const int pos = b.old_len[i] + t0 + t;
     const int page = c.L.pt[(size_t)seq * c.dm.pages_per_seq + pos / kPage];
-    const size_t dst = (((size_t)page * Hkv + h) * kPage + (pos % kPage)) * V8 + c8;
+    // K page: channel group c8 of the 16 tokens is 256 contiguous bytes
+    const size_t dst = (((size_t)page * Hkv + h) * V8 + c8) * kPage + (pos % kPage);
     reinterpret_cast<uint4 *>(c.L.k)[dst] = ks[idx];
     // V page transposed: element (channel ch, token t) at ch * 16 + t
     const uint4 vv = vs[idx];
@@ -1807,12 +1808,15 @@ __device__ __forceinline__ void load_stage(const Ctx &c, int h, int pg0, int pg1
   for (int pi = 0; pi < 2; ++pi) {
     const int pg = pi ? pg1 : pg0;
     // the lane of the step's new token reads its K from the caller's row
-    const uint16_t *kp = (pg == tok.pg && r16 == tok.slot)
-                             ? tok.k + lgrp * (D / 4)
-                             : c.L.k + ((((size_t)pg * c.dm.Hkv + h) * kPage + r16) * D +
-                                        lgrp * (D / 4));
+    // MFMA m, lane (token r16, lgrp): channel group 4 m + lgrp, so that one
+    // load instruction reads 1 KB of the page's K contiguously; the lane of
+    // the step's new token reads its K from the caller's row
+    const bool nt = pg == tok.pg && r16 == tok.slot;
+    const uint16_t *kb = nt ? tok.k : c.L.k + ((size_t)pg * c.dm.Hkv + h) * kPage * D + r16 * 8;
+    const int gstride = nt ? 8 : kPage * 8;  // elements from one channel group to the next
 #pragma unroll
-    for (int m = 0; m < D / 32; ++m) st.k[pi][m] = *reinterpret_cast<const uint4 *>(kp + 8 * m);
+    for (int m = 0; m < D / 32; ++m)
+      st.k[pi][m] = *reinterpret_cast<const uint4 *>(kb + (size_t)(4 * m + lgrp) * gstride);
   }
   const uint16_t *vp = c.L.v + (((size_t)(lgrp >= 2 ? pg1 : pg0) * c.dm.Hkv + h) * D + r16) * kPage +
                        8 * (lgrp & 1);
@@ -2021,7 +2025,7 @@ __device__ __attribute__((always_inline)) void attend_part(const Ctx &c, int i, 
 #pragma unroll
   for (int m = 0; m < D / 32; ++m)
     qa[m] = r16 < G ? *reinterpret_cast<const uint4 *>(q + ((size_t)i * c.dm.Hq + qh0 + r16) * D +
-                                                       lgrp * (D / 4) + 8 * m)
+                                                       8 * (4 * m + lgrp))
                     : make_uint4(0, 0, 0, 0);
   AttWave<D> W;
 #pragma unroll
@@ -2409,8 +2413,9 @@ __device__ __attribute__((always_inline)) void dense_maw(const Ctx &c, int seq, 
     mw[blk] = __fadd_rn(__fmul_rn(r, m_old), __fmul_rn(omr, a * inv_g));
   }
   if (app) {
-    const size_t pk = (((size_t)tok.pg * c.dm.Hkv + h) * kPage + tok.slot) * D;
-    if (tid < D / 8) reinterpret_cast<uint4 *>(c.L.k + pk)[tid] = k8;
+    if (tid < D / 8)
+      reinterpret_cast<uint4 *>(c.L.k)[(((size_t)tok.pg * c.dm.Hkv + h) * (D / 8) + tid) * kPage +
+                                       tok.slot] = k8;
     if (tid < D) c.L.v[(((size_t)tok.pg * c.dm.Hkv + h) * D + tid) * kPage + tok.slot] = v1;
     if (tid < C4) {
       const uint32_t kw[2] = {k4.x, k4.y}, ow[4] = {s_old.x, s_old.y, s_old.z, s_old.w};
@@ -2790,11 +2795,11 @@ __global__ __launch_bounds__(256) void k_lfps_init_mass(Ctx c, SeqBatch b, const
   __syncthreads();
   const int32_t *pts = c.L.pt + (size_t)seq * c.dm.pages_per_seq;
   auto logits = [&](int j, float (&sc)[G]) {
-    const uint16_t *kr = c.L.k + (((size_t)pts[j >> 4] * c.dm.Hkv + h) * kPage + (j & 15)) * D;
+    const uint16_t *kr = c.L.k + ((size_t)pts[j >> 4] * c.dm.Hkv + h) * kPage * D + (j & 15) * 8;
 #pragma unroll
     for (int gg = 0; gg < G; ++gg) sc[gg] = 0.0f;
     for (int ch = 0; ch < D; ch += 8) {
-      const uint4 w = *reinterpret_cast<const uint4 *>(kr + ch);
+      const uint4 w = *reinterpret_cast<const uint4 *>(kr + (size_t)(ch / 8) * kPage * 8);
       const uint32_t ws[4] = {w.x, w.y, w.z, w.w};
 #pragma unroll
       for (int e = 0; e < 4; ++e) {

@@ -1129,8 +1129,9 @@ sd_status sd_debug_copy(sd_ctx *c, int32_t what, int32_t layer, int32_t seq,
       for (int r = 0; r < kPage && p * kPage + r < len; ++r)
         for (int h = 0; h < c->Hkv; ++h) {
           uint16_t *row = dst + (((size_t)(p * kPage + r)) * c->Hkv + h) * D;
-          if (what == SD_DEBUG_K)
-            memcpy(row, page.data() + ((size_t)h * kPage + r) * D, sizeof(uint16_t) * D);
+          if (what == SD_DEBUG_K)  // K pages: [Hkv][d/8][16][8]
+            for (int ch = 0; ch < D; ++ch)
+              row[ch] = page[(((size_t)h * (D / 8) + ch / 8) * kPage + r) * 8 + ch % 8];
           else  // V pages are stored transposed: [Hkv][d][16]
             for (int ch = 0; ch < D; ++ch) row[ch] = page[((size_t)h * D + ch) * kPage + r];
         }

@@ -345,7 +345,7 @@ sd_status sd_debug_set_lfps(sd_ctx *ctx, int32_t layer, int32_t seq_id,
  * decode step's own rate can be read.  Reads `bytes` bytes at `src` once
  * (device memory, 16-byte aligned, bytes > 0 and a multiple of 16) with
  * `sink_words` workgroups of 256 threads, each thread reading 16-byte words
- * grid-stride, four in flight; writes the XOR of each workgroup's words to
+ * grid-stride, eight in flight; writes the XOR of each workgroup's words to
  * sink[0 .. sink_words) (device, caller-owned).  Needs no context;
  * stream-ordered and asynchronous on `stream` (hipStream_t, NULL = the null
  * stream).  Returns SD_EINVAL (nothing launched) for a NULL pointer, a
