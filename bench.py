@@ -95,6 +95,12 @@ def parse():
                     help="measurement build only (build.py --timeline): record the per-phase "
                          "timestamps of STEPS one-launch steps after the warm-up, print their "
                          "per-role medians and exit")
+    ap.add_argument("--timeline-b2b", action="store_true",
+                    help="with --timeline: launch each recorded step right behind another one "
+                         "(no synchronisation between them) and record the second")
+    ap.add_argument("--timeline-dump", default="", metavar="NPY",
+                    help="with --timeline: also save the raw timestamp tables "
+                         "([steps][workgroups][slots] ticks, 0 = not reached) to NPY")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="run a plain 1 GiB device copy (counter calibration) and exit")
     ap.add_argument("--traffic-summary", nargs=4, metavar=("FETCH", "WRITE", "CAL_FETCH", "CAL_WRITE"),
@@ -491,35 +497,47 @@ def timeline(args, w, eng, step, s0, L):
     tiles = -(-max(-(-max(0, n_now - w.window) // S) for S in w.block_size) // 256)
     n_wg = w.Hkv * w.B * 64
     names = {"score": ["first instruction", "keys written", "tile list published", "arrived",
-                       "top-k done", "MAW updated (by the top-k)",
+                       "top-k done", "(unused)",
                        "fast top-k gave up (full top-k runs)", "band re-score started"],
              "part": ["first instruction", "dense pages done (wave 0)", "selection count seen",
                       "selected pages done (wave 0)", "partial written, arrived",
-                      "fusion done", "(unused)", "MAW updated (by a part)"]}
+                      "fusion done", "first dense page ids read (wave 0)", "(unused)"],
+             "maw": ["first instruction", "(unused)", "(unused)", "(unused)", "(unused)",
+                     "(unused)", "arrivals seen", "MAW updated"]}
     acc = {r: {k: [] for k in range(len(v))} for r, v in names.items()}
     # durations inside the last-arriver roles, per workgroup (us)
     spans = {"top-k (last tile: arrived -> done)": ("score", 3, 4),
              "fusion (last part: arrived -> done)": ("part", 4, 5),
-             "MAW by the top-k (top-k done -> MAW done)": ("score", 4, 5),
-             "MAW by a part (dense done -> MAW done)": ("part", 1, 7),
+             "MAW worker (arrivals seen -> MAW done)": ("maw", 6, 7),
              "top-k with the band re-score (arrived -> done)": ("score", 7, 4),
              "top-k after the fast one gave up (gave up -> done)": ("score", 6, 4),
              "tile: keys -> list published": ("score", 1, 2),
              "tile: list published -> arrived": ("score", 2, 3),
              "part: selected pages done -> partial written, arrived": ("part", 3, 4)}
     dur = {k: [] for k in spans}
-    ends = []
+    ends, raw = [], []
     _abi.timeline_read(n_wg)  # clear
     for t in range(args.timeline):
-        step(s0 + t)
+        if args.timeline_b2b:  # the recorded launch queued right behind another
+            step(s0 + 2 * t)
+            step(s0 + 2 * t + 1)
+        else:
+            step(s0 + t)
         torch.cuda.synchronize()
         tl = _abi.timeline_read(n_wg).astype(np.int64)
         used = tl[:, 0] > 0
         t0 = tl[used, 0].min()
+        # (back to back: slots the recorded launch did not reach may still hold
+        # the earlier launch's stamps, all before its first start)
+        tl[tl < t0] = 0
+        raw.append(tl)
         us = (tl - t0) / 100.0  # 100 MHz ticks -> us
         for wg in np.nonzero(used)[0]:
             z = wg // (w.Hkv * w.B)
-            role = "score" if z < tiles else "part"
+            # (the MAW worker, last in z, is the role that stamps slot 6
+            # without slot 1)
+            role = ("score" if z < tiles else
+                    "maw" if tl[wg, 6] > 0 and tl[wg, 1] == 0 else "part")
             for k in range(len(names[role])):
                 if tl[wg, k] > 0:
                     acc[role][k].append(us[wg, k])
@@ -527,14 +545,29 @@ def timeline(args, w, eng, step, s0, L):
                 if r_ == role and tl[wg, a_] > 0 and tl[wg, b_] > 0:
                     dur[name].append(us[wg, b_] - us[wg, a_])
         ends.append(float(us[used].max()))
+    if args.timeline_dump:
+        np.save(args.timeline_dump, np.stack(raw))
+    # dispatch: first instruction by XCD (workgroups go round-robin over the 8
+    # XCDs in flat order) and by position in the flat order (octiles)
+    first = np.stack([(r[:, 0] - r[r[:, 0] > 0, 0].min()) / 100.0 for r in raw])
+    ok = np.stack([r[:, 0] > 0 for r in raw])
+    wg_ids = np.arange(n_wg)
+    by_xcd = [float(np.median(first[:, wg_ids % 8 == x][ok[:, wg_ids % 8 == x]])) for x in range(8)]
+    n_used = int(ok.any(0).nonzero()[0].max()) + 1
+    octile = wg_ids * 8 // n_used
+    by_order = [float(np.median(first[:, octile == o][ok[:, octile == o]])) for o in range(8)]
+    # (octiles of the flat order over the launch's workgroups)
     out = {"workload": w.name, "steps": args.timeline, "tiles_per_unit": tiles,
+           "back_to_back": bool(args.timeline_b2b),
+           "first_instruction_median_by_xcd_us": by_xcd,
+           "first_instruction_median_by_order_octile_us": by_order,
            "last_event_us": {"median": float(np.median(ends)), "min": float(np.min(ends)),
                              "max": float(np.max(ends))}}
     for role, ph in names.items():
         rows = []
         for k, name in enumerate(ph):
             v = np.array(acc[role][k])
-            if v.size:
+            if v.size and name != "(unused)":
                 rows.append({"phase": name, "n": int(v.size), "p10": float(np.percentile(v, 10)),
                              "median": float(np.median(v)), "p90": float(np.percentile(v, 90)),
                              "max": float(v.max())})
@@ -550,6 +583,8 @@ def timeline(args, w, eng, step, s0, L):
     print("durations:")
     for r in out["durations"]:
         print("  %-62s n=%5d  median %5.2f  p90 %5.2f us" % (r["span"], r["n"], r["median"], r["p90"]))
+    print("first instruction, median by XCD:", " ".join("%.2f" % v for v in by_xcd), "us")
+    print("first instruction, median by flat-order octile:", " ".join("%.2f" % v for v in by_order), "us")
     print("last event per step: median %.2f us (min %.2f, max %.2f)"
           % (out["last_event_us"]["median"], out["last_event_us"]["min"],
              out["last_event_us"]["max"]), flush=True)

@@ -15,6 +15,7 @@ constexpr int kPage = SD_PAGE_SIZE;  // tokens per KV page
 constexpr int kLaunchSeqs = 64;      // sequences per kernel launch
 constexpr int kPartPages = 40;       // attended pages per attention workgroup (target)
 constexpr int kScoreTile = 256;      // blocks scored by one workgroup
+constexpr int kTileAhead = 2;        // 16-block summary groups a score wave keeps in flight
 constexpr int kTopkRegRows = 20;     // top-k rows of 64 block words kept in registers
 constexpr int kTopkUnc = 512;        // uncertain blocks the top-k lists in LDS
 constexpr int kFastTiles = 8;        // score tiles per unit of the fast top-k, at most

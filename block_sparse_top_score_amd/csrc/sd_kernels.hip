@@ -86,6 +86,15 @@ __device__ __forceinline__ bool arrive_last(uint32_t *counter, unsigned expected
   return *flag != 0;
 }
 
+// Arrival of one workgroup that needs no answer: its memory operations are
+// done before the increment.  Every thread of the workgroup must call it.
+__device__ __forceinline__ void arrive(uint32_t *counter) {
+  wait_vmem();
+  __syncthreads();
+  if (threadIdx.x == 0)
+    __hip_atomic_fetch_add(counter, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
 // Bound of every wait inside a launch.
 constexpr unsigned long long kWaitTicks = 20000000ull;  // 0.2 s of the 100 MHz clock
 
@@ -592,17 +601,20 @@ __device__ __attribute__((always_inline)) bool score_tile(const Ctx &c, int i, i
   const int base = tile * kScoreTile + wv * 16 * GPW;
   const uint4 *sp = reinterpret_cast<const uint4 *>(c.L.summ + hi.summ_off +
                                                     (size_t)seq * C4 * hi.nbmax * 8);
-  // every load of the tile is issued first, before any is used and before
-  // the rest of the unit's geometry is worked out (block indices are clamped,
-  // so the loads of a wave past the last block stay in bounds)
+  // the first kTileAhead 16-block groups are loaded before anything else;
+  // each later group is issued once the group kTileAhead before it has been
+  // scored, so a wave keeps kTileAhead groups in flight (block indices are
+  // clamped, so the loads of a wave past the last block stay in bounds)
+  constexpr int AHEAD = kTileAhead < GPW ? kTileAhead : GPW;
   uint4 kf[GPW][MM];
   const int nb_last = max(n_blk - 1, 0);
-#pragma unroll
-  for (int gi = 0; gi < GPW; ++gi) {
+  auto load_group = [&](int gi) {
     const int blk = min(base + gi * 16 + r16, nb_last);
 #pragma unroll
     for (int mm = 0; mm < MM; ++mm) kf[gi][mm] = sp[(size_t)(4 * mm + lgrp) * hi.nbmax + blk];
-  }
+  };
+#pragma unroll
+  for (int gi = 0; gi < AHEAD; ++gi) load_group(gi);
   const int qh0 = h * G;
   const uint16_t *qrow = q + ((size_t)i * c.dm.Hq + qh0 + min(r16, G - 1)) * D;
   uint2 qw[MM];
@@ -645,6 +657,11 @@ __device__ __attribute__((always_inline)) bool score_tile(const Ctx &c, int i, i
   int n_flag = 0;
 #pragma unroll
   for (int gi = 0; gi < GPW; ++gi) {
+    if (gi >= 1 && gi - 1 + AHEAD < GPW) {  // group gi - 1 is scored
+      __builtin_amdgcn_sched_barrier(0);
+      load_group(gi - 1 + AHEAD);
+      __builtin_amdgcn_sched_barrier(0);
+    }
     // partial sums over 64 (min, max) values (two chained MFMAs), added in
     // fp32: a tighter error bound than one chain over all 2d values
     f32x4 acc = {0.f, 0.f, 0.f, 0.f}, acce = {0.f, 0.f, 0.f, 0.f};
@@ -1960,7 +1977,8 @@ __device__ __forceinline__ void compute_stage(const Ctx &c, KVStage<D> &st, int 
 template <int D, int G, class Resolve>
 __device__ __forceinline__ void wave_pages(const Ctx &c, int h, int gw, int NW, int total,
                                            Resolve resolve, const uint4 (&qa)[D / 32], AttWave<D> &W,
-                                           float (*pl)[32], float *lmb, const NewTok &tok) {
+                                           float (*pl)[32], float *lmb, const NewTok &tok,
+                                           int tl_slot = -1) {
   const int lane = threadIdx.x & 63;
   const int nw = total > gw ? cdiv(total - gw, NW) : 0;
   for (int b0 = 0; b0 < nw; b0 += 64) {
@@ -1980,6 +1998,7 @@ __device__ __forceinline__ void wave_pages(const Ctx &c, int h, int gw, int NW, 
     auto NP = [&](int t) { return PG(2 * t) == tok.pg ? 0 : (PG(2 * t + 1) == tok.pg ? 1 : -1); };
     KVStage<D> A, B;
     load_stage<D>(c, h, PG(0), PG(1), A, tok);
+    if (tl_slot >= 0 && b0 == 0) SD_TL(tl_slot);  // (measurement build) page ids read
     for (int s = 0;; s += 2) {
       load_stage<D>(c, h, PG(2 * s + 2), PG(2 * s + 3), B, tok);
       compute_stage<D, G>(c, A, MK(2 * s), MK(2 * s + 1), SL(2 * s), SL(2 * s + 1), qa, ones, W,
@@ -2010,12 +2029,10 @@ __device__ __attribute__((always_inline)) void attend_part(const Ctx &c, int i, 
                                                            float *__restrict__ o_part,
                                                            float *__restrict__ lse_part, int p_cap,
                                                            AttLds<D, G> &sm,
-                                                           const int32_t *ptl /* LDS or null */,
+                                                           int32_t *ptl /* LDS or null */,
                                                            int *s_cnt, const NewTok &tok,
                                                            const HeadInfo &hi,
-                                                           uint32_t *dctr = nullptr,
-                                                           unsigned d_expected = 0,
-                                                           int *s_dflag = nullptr) {
+                                                           uint32_t *dctr = nullptr) {
   const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6, r16 = lane & 15, lgrp = lane >> 4;
   constexpr int NT = D / 16;
   const int qh0 = h * G, NW = 4 * P, gw = 4 * part + wv;
@@ -2038,6 +2055,23 @@ __device__ __attribute__((always_inline)) void attend_part(const Ctx &c, int i, 
   float(*pl)[32] = sm.p[wv];
   float *lmb = c.sc.lm_pg + ((size_t)seq * c.dm.Hq + qh0) * c.dm.lm_cap;
 
+  if (ptl) {
+    // the page table to LDS (one batch of loads); the selected pages read it
+    // after the barriers below
+    constexpr int PER = (kPtLds + 255) / 256;
+    const int np = cdiv(g.N, kPage);
+    int32_t v[PER];
+#pragma unroll
+    for (int k = 0; k < PER; ++k) {
+      const int x = tid + 256 * k;
+      v[k] = x < np ? pts[x] : 0;
+    }
+#pragma unroll
+    for (int k = 0; k < PER; ++k) {
+      const int x = tid + 256 * k;
+      if (x < np) ptl[x] = v[k];
+    }
+  }
   // dense pages
   const DenseList dl = dense_list(g);
   wave_pages<D, G>(
@@ -2048,21 +2082,9 @@ __device__ __attribute__((always_inline)) void attend_part(const Ctx &c, int i, 
         mk = page_dense16(g, pn);
         sl = t;
       },
-      qa, W, pl, lmb, tok);
+      qa, W, pl, lmb, tok, 6);
 
   SD_TL(1);  // dense pages done (wave 0)
-  // one-launch step: every part, and the unit's top-k, arrive here once the
-  // dense pages' log-masses are written; the last to arrive updates MAW (and
-  // writes the folded append's token), off the unit's critical path
-  // (its own LDS flag: thread 0 rewrites *s_cnt below while other waves may
-  // still be reading the arrival's result)
-  if (dctr) {
-    if (arrive_last(dctr, d_expected, s_dflag)) {
-      dense_maw<D, G>(c, seq, h, hi, g, tok, &sm.p[0][0][0], &sm.wm[0][0], &sm.wz[0][0]);
-      if (threadIdx.x == 0) st_dev(dctr, 0u);
-      SD_TL(7);  // MAW updated here
-    }
-  }
   // the selection
   int cnt = si.cnt;
   if (si.rtag) {
@@ -2087,6 +2109,10 @@ __device__ __attribute__((always_inline)) void attend_part(const Ctx &c, int i, 
     cnt = *s_cnt;
   }
   SD_TL(2);  // selection count seen
+  // one-launch step: every part, and the unit's top-k, arrive once the dense
+  // pages' log-masses are written (by now their stores are long done); the
+  // unit's MAW worker then updates MAW, off the parts' path
+  if (dctr) arrive(dctr);
   if (cnt > 0 && g.N > 0) {
     wave_pages<D, G>(
         c, h, gw, NW, cnt * PPB,
@@ -2960,12 +2986,15 @@ __global__ __launch_bounds__(256, 2) void k_attend(Ctx c, SeqBatch b, int P,
 // One decode step in one launch.  Workgroups by index: score tiles (the last
 // of a unit runs its top-k and publishes the selection, tagged with the step
 // number), then P attention parts per unit (a unit uses unit_parts of them,
-// the rest exit at once).  A part streams its dense pages from the start,
-// then waits for the selection and streams its selected pages; the last part
-// of a unit to finish fuses the partials and updates MAW.  Workgroups start in index order on each XCD and
-// every wait is on a score tile, which never waits, so no wait is on a
-// workgroup that cannot start; each wait is also bounded in time (after
-// kWaitTicks it gives up and raises the error flag).
+// the rest exit at once), then one MAW worker per unit.  A part streams its
+// dense pages from the start, then waits for the selection and streams its
+// selected pages; the last part of a unit to finish fuses the partials.  The
+// MAW worker updates MAW once the parts' dense pages and the top-k are done.
+// Workgroups start in index order on each XCD; a part waits on a score tile,
+// which never waits, and a MAW worker on parts and score tiles, which never
+// wait on it, so no wait is on a workgroup that cannot start; each wait is
+// also bounded in time (after kWaitTicks it gives up and raises the error
+// flag).
 template <int D, int G>
 __global__ __launch_bounds__(256, 2) void k_step(Ctx c, SeqBatch b, int tiles_x, int P,
                                                  int32_t *__restrict__ blk_idx,
@@ -3049,44 +3078,50 @@ __global__ __launch_bounds__(256, 2) void k_step(Ctx c, SeqBatch b, int tiles_x,
         st_dev(&c.sc.rtag[unit], ((unsigned long long)epoch << 32) |
                                      (uint32_t)min(min(g.kk, k_cap), hi.kcap));
     }
-    // the unit's MAW update (and the folded append's writes) once every part
-    // has written its dense pages' log-masses: the last of the parts and this
-    // top-k to arrive does it; here that is usually this workgroup, which has
-    // nothing else left to do
+    // the unit's MAW worker waits for this arrival too: the tiles have read
+    // the MAW values and summaries that its update writes
+    arrive(&c.sc.arrive[unit * 4 + 2]);
+    return;
+  }
+  if ((int)blockIdx.z == tiles_x + P) {
+    // the unit's MAW worker: once every part has written its dense pages'
+    // log-masses and the top-k has arrived, the MAW update and the folded
+    // append's writes.  It waits on workgroups of lower index only.
+    const UG g = unit_geom(N, hi, c.dm);
+    const bool no_sel = selects_nothing(hi, N, c.dm);
+    const unsigned expected = (unsigned)unit_parts(g, P, c.dm) + (no_sel ? 0u : 1u);
     uint32_t *dctr = &c.sc.arrive[unit * 4 + 2];
-    if (arrive_last(dctr, (unsigned)unit_parts(g, P, c.dm) + 1u, &s_flag)) {
-      float *pm = reinterpret_cast<float *>(smem_raw);
-      dense_maw<D, G>(c, seq, h, hi, g, new_tok(N), pm, pm + kFuseDenseLds,
-                      pm + kFuseDenseLds + 4 * G);
-      if (threadIdx.x == 0) st_dev(dctr, 0u);
-      SD_TL(5);  // MAW updated here
+    if (threadIdx.x == 0) {
+      int ok = 1;
+      const unsigned long long t0 = wall_clock64();
+      while (ld_dev(dctr) < expected) {
+        if (wall_clock64() - t0 > kWaitTicks) {
+          st_dev(&c.sc.err[0], 1u);
+          ok = 0;
+          break;
+        }
+        __builtin_amdgcn_s_sleep(8);
+      }
+      s_flag = ok;
     }
+    __syncthreads();
+    SD_TL(6);  // arrivals seen
+    if (!s_flag) return;
+    float *pm = reinterpret_cast<float *>(smem_raw);
+    dense_maw<D, G>(c, seq, h, hi, g, new_tok(N), pm, pm + kFuseDenseLds,
+                    pm + kFuseDenseLds + 4 * G);
+    if (threadIdx.x == 0) st_dev(dctr, 0u);
+    SD_TL(7);  // MAW updated
     return;
   }
   const UG g = unit_geom(N, hi, c.dm);
   const int PU = unit_parts(g, P, c.dm);
   if (idx >= PU) return;
-  // attention part idx of the unit; the sequence's page table is copied to LDS
-  // (one batch of loads) for the selected pages
-  const int32_t *ptl = nullptr;
-  const int np = cdiv(g.N, kPage);
-  if (np <= ptl_cap) {
-    int32_t *t = reinterpret_cast<int32_t *>(smem_raw + ((sizeof(AttLds<D, G>) + 15) & ~15));
-    constexpr int PER = (kPtLds + 255) / 256;
-    const int32_t *pts = c.L.pt + (size_t)seq * c.dm.pages_per_seq;
-    int32_t v[PER];
-#pragma unroll
-    for (int k = 0; k < PER; ++k) {
-      const int x = (int)threadIdx.x + 256 * k;
-      v[k] = x < np ? pts[x] : 0;
-    }
-#pragma unroll
-    for (int k = 0; k < PER; ++k) {
-      const int x = (int)threadIdx.x + 256 * k;
-      if (x < np) t[x] = v[k];
-    }
-    ptl = t;  // visible to all waves after the barrier of the selection wait
-  }
+  // attention part idx of the unit; the sequence's page table goes to LDS
+  // for the selected pages
+  int32_t *ptl = cdiv(g.N, kPage) <= ptl_cap
+                     ? reinterpret_cast<int32_t *>(smem_raw + ((sizeof(AttLds<D, G>) + 15) & ~15))
+                     : nullptr;
   if (idx == 0) empty_slots<D, G>(c, i, h, PU, p_cap, o_part, lse_part);
   // a unit that selects nothing has no score tiles: its parts take the dense
   // pages only and part 0 writes the count
@@ -3098,8 +3133,7 @@ __global__ __launch_bounds__(256, 2) void k_step(Ctx c, SeqBatch b, int tiles_x,
   si.cnt = 0;
   si.epoch = epoch;
   attend_part<D, G>(c, i, seq, h, g, idx, PU, q, si, o_part, lse_part, p_cap, smem_att, ptl,
-                    &s_cnt, new_tok(N), hi, &c.sc.arrive[unit * 4 + 2],
-                    (unsigned)PU + (no_sel ? 0u : 1u), &s_flag);
+                    &s_cnt, new_tok(N), hi, &c.sc.arrive[unit * 4 + 2]);
   uint32_t *fctr = &c.sc.arrive[unit * 4 + 1];
   const bool last_part = arrive_last(fctr, (unsigned)PU, &s_flag);
   SD_TL(4);  // partial written, arrived
@@ -3268,7 +3302,7 @@ hipError_t launch_step(const Ctx &c, const SeqBatch &b, int max_blocks, int P, c
   if (b.n <= 0) return hipSuccess;
   if (P < 1 || P > p_cap) return hipErrorInvalidValue;
   const int tiles_x = max(1, (b.max_scored + kScoreTile - 1) / kScoreTile);
-  const dim3 grid(c.dm.Hkv, b.n, tiles_x + P);
+  const dim3 grid(c.dm.Hkv, b.n, tiles_x + P + 1);  // + the MAW workers
   size_t topk_bytes;
   const int lrows_words = topk_lds(max_blocks, &topk_bytes);
   if (topk_bytes > 65536) return hipErrorInvalidValue;

@@ -499,7 +499,11 @@ sd_status sd_sync(sd_ctx *c) {
   uint32_t e = 0;
   SD_HIP(c, hipMemcpy(&e, c->sc.err, sizeof e, hipMemcpyDeviceToHost));
   if (e) {
+    // a wait gave up: the hand-off counters may be left part-way; they start
+    // from zero again for the next call
     SD_HIP(c, hipMemset(c->sc.err, 0, sizeof e));
+    SD_HIP(c, hipMemset(c->sc.arrive, 0, sizeof(uint32_t) * c->cfg.max_seqs * c->Hkv * 4));
+    SD_HIP(c, hipMemset(c->sc.unit_acc, 0, sizeof(uint32_t) * c->cfg.max_seqs * c->sel_rows * 4));
     return fail(c, SD_EHIP, "a decode step kernel timed out waiting for a unit's selection; "
                 "its outputs are invalid");
   }

@@ -7,16 +7,18 @@
  * workgroup, wall_clock64() timestamps (a 100 MHz counter common to the
  * device) at the phase boundaries of its role, indexed by the flat workgroup
  * number x + X (y + Y z) of the (KV head, sequence, role) grid, role z < tiles
- * being a score tile and z >= tiles an attention part:
+ * being a score tile, tiles <= z < tiles + P an attention part and
+ * z = tiles + P the unit's MAW worker:
  *   score tile:     0 first instruction, 1 keys written, 2 tile list published,
- *                   3 arrived, 4 top-k done (last arriver only), 5 the unit's
- *                   MAW updated (when this top-k arrived last after the
- *                   parts' dense pages), 6 the fast top-k gave up (the full
- *                   top-k runs), 7 the band's exact re-score started
+ *                   3 arrived, 4 top-k done (last arriver only), 6 the fast
+ *                   top-k gave up (the full top-k runs), 7 the band's exact
+ *                   re-score started
  *   attention part: 0 first instruction, 1 dense pages done (wave 0), 2 selection count
  *                   seen, 3 selected pages done (wave 0), 4 partial written
- *                   and arrived, 5 fusion done (last part only), 7 the unit's
- *                   MAW updated (when this part arrived last)
+ *                   and arrived, 5 fusion done (last part only), 6 the
+ *                   first dense page ids read (wave 0)
+ *   MAW worker:     0 first instruction, 6 the parts' and the top-k's
+ *                   arrivals seen, 7 the unit's MAW updated
  * Slots not reached stay 0.
  */
 #ifndef SPARSE_DECODE_TIMELINE_H
