@@ -202,7 +202,8 @@ __device__ __forceinline__ uint32_t order_key(float u) {
 
 // ---------------------------------------------------------------------------
 // Shared memory of the roles (one launch may host several roles).
-constexpr int kTileList = 64;  // blocks a score tile lists for the fast top-k, at most
+constexpr int kTileList = 64;  // keys a score tile lists per lane register for the fast top-k
+constexpr int kFastK = 2 * kTileList;  // the fast top-k's largest k (lists of two registers)
 // The four-wave top-k ranks units of (kTopkRegRows * 64, 256 * kWideM]
 // blocks; its thread t holds blocks [t m, t m + m), m = ceil(n / 256).
 static_assert(kWideM <= 64, "a thread's blocks span at most two mask words");
@@ -210,7 +211,7 @@ struct TopkSmem {
   int32_t ulist[kTopkUnc];  // uncertain blocks of the top-k, in index order
   uint32_t ukey[kTopkUnc];  // their exact keys
   uint32_t tk[kScoreTile];  // keys of a score tile (fast top-k)
-  double ue[kTileList * SD_MAX_GROUP];  // exact scores of the fast top-k's band, per head
+  double ue[kFastK * SD_MAX_GROUP];  // exact scores of the fast top-k's band, per head
   unsigned long long bm[kFastTiles * kScoreTile / 64];  // chosen blocks (fast top-k)
   unsigned long long srt[4][kTileList];  // the waves' sorted keys (tile list)
   float qs[SD_MAX_GROUP * 128];
@@ -524,6 +525,48 @@ __device__ __forceinline__ unsigned long long merge_top64(unsigned long long a, 
   v = half_clean<1>(v);
   return v;
 }
+// The 64 smallest of the same two lists, descending: min(a, b reversed).
+__device__ __forceinline__ unsigned long long merge_bottom64(unsigned long long a,
+                                                             unsigned long long b) {
+  const unsigned long long br =
+      ((unsigned long long)lane_rev((uint32_t)(b >> 32)) << 32) | lane_rev((uint32_t)b);
+  unsigned long long v = a > br ? br : a;
+  v = half_clean<32>(v);
+  v = half_clean<16>(v);
+  v = half_clean<8>(v);
+  v = half_clean<4>(v);
+  v = half_clean<2>(v);
+  v = half_clean<1>(v);
+  return v;
+}
+__device__ __forceinline__ unsigned long long key_rev(unsigned long long v) {
+  return ((unsigned long long)lane_rev((uint32_t)(v >> 32)) << 32) | lane_rev((uint32_t)v);
+}
+// Lists of 128 keys in two registers, descending: rank l in h (lane l), rank
+// 64 + l in lo.  The 128 largest of two such lists: the elementwise maximum
+// of one list and the other reversed is bitonic and holds them; the
+// half-cleaner at distance 64 pairs the two registers lane by lane, then each
+// register is sorted by the cleaners at distances 32 .. 1.
+__device__ __forceinline__ void merge_top128(unsigned long long &ah, unsigned long long &al,
+                                             unsigned long long bh, unsigned long long bl) {
+  const unsigned long long rbl = key_rev(bl), rbh = key_rev(bh);
+  const unsigned long long mh = ah > rbl ? ah : rbl, ml = al > rbh ? al : rbh;
+  unsigned long long h = mh > ml ? mh : ml, lo = mh > ml ? ml : mh;
+  h = half_clean<32>(h);
+  lo = half_clean<32>(lo);
+  h = half_clean<16>(h);
+  lo = half_clean<16>(lo);
+  h = half_clean<8>(h);
+  lo = half_clean<8>(lo);
+  h = half_clean<4>(h);
+  lo = half_clean<4>(lo);
+  h = half_clean<2>(h);
+  lo = half_clean<2>(lo);
+  h = half_clean<1>(h);
+  lo = half_clean<1>(lo);
+  ah = h;
+  al = lo;
+}
 // One compare-exchange step of a bitonic sort into descending order: lane l
 // and lane l ^ J compare; in a run of K lanes sorted descending (l & K = 0)
 // the lower lane keeps the larger key, in an ascending run the smaller.
@@ -583,6 +626,27 @@ __device__ __forceinline__ void tile_list(const Ctx &c, int seq, int h, int tile
            merge_top64(m01, m23));
   }
 }
+// The same for kTileList < k <= kFastK: the tile's 128 largest keys,
+// descending, as two lists of 64 (ranks l and 64 + l of lane l) at
+// [128 t, 128 t + 128) of the unit's candidate lists.
+__device__ __forceinline__ void tile_list128(const Ctx &c, int seq, int h, int tile, TopkSmem &sm) {
+  const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
+  const size_t unit = (size_t)seq * c.dm.Hkv + h;
+  const int b = wv * 64 + lane;
+  unsigned long long v =
+      ((unsigned long long)sm.tk[b] << 32) | (uint32_t)~(uint32_t)(tile * kScoreTile + b);
+  v = sort64_desc(v);
+  if (wv > 0) sm.srt[wv][lane] = v;
+  __syncthreads();
+  if (wv == 0) {
+    const unsigned long long w1 = sm.srt[1][lane], w2 = sm.srt[2][lane], w3 = sm.srt[3][lane];
+    unsigned long long ah = merge_top64(v, w1), al = merge_bottom64(v, w1);
+    merge_top128(ah, al, merge_top64(w2, w3), merge_bottom64(w2, w3));
+    unsigned long long *cl = c.sc.cand + unit * c.dm.key_stride + (size_t)tile * kFastK;
+    st_dev(&cl[lane], ah);
+    st_dev(&cl[kTileList + lane], al);
+  }
+}
 
 // fast_ok: also write the tile's candidate list for the fast top-k (tile <
 // kFastTiles).  PQH: one key per query head (each head ranks its own bounds;
@@ -633,7 +697,7 @@ __device__ __attribute__((always_inline)) bool score_tile(const Ctx &c, int i, i
   }
   __builtin_amdgcn_sched_barrier(0);
   g = unit_geom(N, hi, c.dm);
-  const bool publish = !PQH && fast_ok && g.kk <= kTileList;
+  const bool publish = !PQH && fast_ok && g.kk <= kFastK;
   // A operand: lane = head r16 (zero rows past G), channel quad 4*mm + lgrp,
   // pairs (q-, q+) matching the (min, max) pairs of the summaries
   uint4 qa[MM];
@@ -770,7 +834,12 @@ __device__ __attribute__((always_inline)) bool score_tile(const Ctx &c, int i, i
     if (f) __hip_atomic_fetch_add(acc + 1, f, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
   }
   SD_TL(1);  // keys written
-  if (publish) tile_list(c, seq, h, tile, sm);
+  if (publish) {
+    if (g.kk <= kTileList)
+      tile_list(c, seq, h, tile, sm);
+    else
+      tile_list128(c, seq, h, tile, sm);
+  }
   return publish;
 }
 
@@ -1531,6 +1600,45 @@ __device__ __attribute__((always_inline)) void topk_wide(const Ctx &c, int seq, 
 
 // Value of lane ^ J within the wave (J = 1, 2, 4, 8 by DPP inside 16-lane
 // rows; 16 and 32 through ds_bpermute).
+// The fast top-k's outputs (wave 0): the chosen blocks of the LDS bitmap in
+// ascending order, the count, and the unit's accumulators cleared for the
+// next step.
+__device__ __forceinline__ void fast_out(const Ctx &c, size_t unit, size_t out, int nw, int kk,
+                                         int k_cap, int32_t *__restrict__ blk_idx,
+                                         int32_t *__restrict__ blk_cnt, TopkSmem &sm,
+                                         uint32_t eps_bits) {
+  const int lane = threadIdx.x & 63;
+  __builtin_amdgcn_s_waitcnt(0xc07f);
+  __builtin_amdgcn_wave_barrier();
+  // ascending order: exclusive prefix of the words' popcounts, then each
+  // lane writes the chosen blocks of its word
+  unsigned long long wbits = lane < nw ? sm.bm[lane] : 0ull;
+  const int cw = __popcll(wbits);
+  // inclusive prefix: DPP shifts inside 16-lane rows, then the row totals
+  int incl = cw;
+  incl += __builtin_amdgcn_update_dpp(0, incl, 0x111, 0xF, 0xF, true);  // row_shr:1
+  incl += __builtin_amdgcn_update_dpp(0, incl, 0x112, 0xF, 0xF, true);  // row_shr:2
+  incl += __builtin_amdgcn_update_dpp(0, incl, 0x114, 0xF, 0xF, true);  // row_shr:4
+  incl += __builtin_amdgcn_update_dpp(0, incl, 0x118, 0xF, 0xF, true);  // row_shr:8
+  const int r0 = __builtin_amdgcn_readlane(incl, 15), r1 = __builtin_amdgcn_readlane(incl, 31),
+            r2 = __builtin_amdgcn_readlane(incl, 47);
+  incl += (lane >= 16 ? r0 : 0) + (lane >= 32 ? r1 : 0) + (lane >= 48 ? r2 : 0);
+  int o = incl - cw;
+  int32_t *dst = blk_idx + out * k_cap;
+  while (wbits) {
+    const int bb = lane * 64 + (__ffsll((long long)wbits) - 1);
+    if (o < k_cap) st_dev(&dst[o], bb);
+    ++o;
+    wbits &= wbits - 1ull;
+  }
+  if (lane == 0) {
+    st_dev(&blk_cnt[out], kk);
+    st_dev(&c.sc.unit_acc[4 * unit], 0u);  // cleared for the next step
+    st_dev(&c.sc.unit_acc[4 * unit + 1], 0u);
+    st_dev(&c.sc.unit_acc[4 * unit + 2], eps_bits);  // the bound this selection used
+  }
+}
+
 // Fast top-k of one unit from the score tiles' lists (no MAW flags, kk <=
 // kTileList; every thread of the workgroup calls it and gets the same
 // result).  The steps of topk_unit run on the listed keys, which hold the
@@ -1675,37 +1783,157 @@ __device__ __attribute__((always_inline)) bool topk_fast(const Ctx &c, int seq, 
       if (tagd && lane == 0) st_dev(rtag, etag | (uint32_t)kk);
     }
   }
+  if (wv == 0) fast_out(c, unit, out, nw, kk, k_cap, blk_idx, blk_cnt, sm, eps_bits);
+  return true;
+}
+
+// Fast top-k for kTileList < k <= kFastK: the steps of topk_fast on the
+// tiles' 128-key lists (ranks l and 64 + l in lane l's two registers), merged
+// pairwise keeping the 128 largest; the band must end above the 128th merged
+// key, else (false, before writing anything) the caller runs topk_unit.
+template <int D, int G>
+__device__ __attribute__((always_inline)) bool topk_fast128(const Ctx &c, int seq, size_t unit,
+                                                            size_t out, const HeadInfo &hi, const UG &g,
+                                                            const uint16_t *__restrict__ q,
+                                                            int32_t *__restrict__ blk_idx,
+                                                            int32_t *__restrict__ blk_cnt, int k_cap,
+                                                            TopkSmem &sm,
+                                                            unsigned long long *tagd = nullptr,
+                                                            unsigned long long *rtag = nullptr,
+                                                            uint32_t epoch = 0) {
+  const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
+  const int n_tiles = max(1, cdiv(g.n_sc, kScoreTile));
+  const unsigned long long etag = (unsigned long long)epoch << 32;
+  const unsigned long long *cl = c.sc.cand + unit * c.dm.key_stride;
+  const int kk = g.kk;  // kTileList < kk <= kFastK
+  const int nw = cdiv(g.n_sc, 64);
+  // one batch of loads: lists (wave 0), error bound, the query
+  unsigned long long eh[kFastTiles], el[kFastTiles];
+#pragma unroll
+  for (int r = 0; r < kFastTiles; ++r) {
+    const bool on = wv == 0 && r < n_tiles;
+    eh[r] = on ? ld_dev(&cl[(size_t)r * kFastK + lane]) : 0ull;
+    el[r] = on ? ld_dev(&cl[(size_t)r * kFastK + kTileList + lane]) : 0ull;
+  }
+  const uint32_t eps_bits = ld_dev(&c.sc.unit_acc[4 * unit]);
+  const uint16_t *qg = q + out * G * D;
+  constexpr int QT = (G * D + 255) / 256;
+  uint16_t qv[QT];
+#pragma unroll
+  for (int t = 0; t < QT; ++t) qv[t] = qg[min(tid + 256 * t, G * D - 1)];
+#pragma unroll
+  for (int t = 0; t < QT; ++t)
+    if (tid + 256 * t < G * D) sm.qs[tid + 256 * t] = __uint_as_float((uint32_t)qv[t] << 16);
+
   if (wv == 0) {
+    if (lane < nw) sm.bm[lane] = 0ull;
     __builtin_amdgcn_s_waitcnt(0xc07f);
     __builtin_amdgcn_wave_barrier();
-    // ascending order: exclusive prefix of the words' popcounts, then each
-    // lane writes the chosen blocks of its word
-    unsigned long long wbits = lane < nw ? sm.bm[lane] : 0ull;
-    const int cw = __popcll(wbits);
-    // inclusive prefix: DPP shifts inside 16-lane rows, then the row totals
-    int incl = cw;
-    incl += __builtin_amdgcn_update_dpp(0, incl, 0x111, 0xF, 0xF, true);  // row_shr:1
-    incl += __builtin_amdgcn_update_dpp(0, incl, 0x112, 0xF, 0xF, true);  // row_shr:2
-    incl += __builtin_amdgcn_update_dpp(0, incl, 0x114, 0xF, 0xF, true);  // row_shr:4
-    incl += __builtin_amdgcn_update_dpp(0, incl, 0x118, 0xF, 0xF, true);  // row_shr:8
-    const int r0 = __builtin_amdgcn_readlane(incl, 15), r1 = __builtin_amdgcn_readlane(incl, 31),
-              r2 = __builtin_amdgcn_readlane(incl, 47);
-    incl += (lane >= 16 ? r0 : 0) + (lane >= 32 ? r1 : 0) + (lane >= 48 ? r2 : 0);
-    int o = incl - cw;
-    int32_t *dst = blk_idx + out * k_cap;
-    while (wbits) {
-      const int bb = lane * 64 + (__ffsll((long long)wbits) - 1);
-      if (o < k_cap) st_dev(&dst[o], bb);
-      ++o;
-      wbits &= wbits - 1ull;
+    const double eps = (double)__uint_as_float(eps_bits);
+#pragma unroll
+    for (int w = 1; w < kFastTiles; w <<= 1)
+#pragma unroll
+      for (int r = 0; r + w < kFastTiles; r += 2 * w)
+        if (r + w < n_tiles) merge_top128(eh[r], el[r], eh[r + w], el[r + w]);
+    const uint32_t kh = (uint32_t)(eh[0] >> 32), kl = (uint32_t)(el[0] >> 32);
+    const uint32_t T = (uint32_t)__builtin_amdgcn_readlane((int)kl, kk - 1 - kTileList);
+    const uint32_t kb_hi = order_key(__double2float_rd((double)key_to_float(T) + 2.0 * eps));
+    const uint32_t kb_lo = order_key(__double2float_ru((double)key_to_float(T) - 2.0 * eps));
+    // a band reaching below the 128 kept keys could miss blocks
+    const uint32_t k127 = (uint32_t)__builtin_amdgcn_readlane((int)kl, kTileList - 1);
+    const bool whole = k127 < 2u || k127 < kb_lo;
+    const int bh = (int)~(uint32_t)eh[0], bl = (int)~(uint32_t)el[0];
+    const bool inh = kh >= 2u && kh > kb_hi, inl = kl >= 2u && kl > kb_hi;
+    const bool unh = kh >= 2u && kh >= kb_lo && kh <= kb_hi;
+    const bool unl = kl >= 2u && kl >= kb_lo && kl <= kb_hi;
+    if (inh) atomicOr(&sm.bm[bh >> 6], 1ull << (bh & 63));
+    if (inl) atomicOr(&sm.bm[bl >> 6], 1ull << (bl & 63));
+    // the band in key order (every key of h is above every key of lo)
+    const unsigned long long muh = __ballot(unh), mul = __ballot(unl);
+    const int nuh = __popcll(muh);
+    if (unh) sm.ulist[lanes_below(muh)] = bh;
+    if (unl) sm.ulist[nuh + lanes_below(mul)] = bl;
+    const int n_unc = nuh + __popcll(mul);
+    const unsigned long long mih = __ballot(inh), mil = __ballot(inl);
+    const int nih = __popcll(mih), n_in = nih + __popcll(mil);
+    const bool ok = whole && n_in <= kk && n_in + n_unc >= kk;
+    if (ok && tagd) {
+      // the tagged selection in key order, as in topk_fast
+      const bool whole_band = n_in + n_unc == kk;
+      const int ph = inh ? lanes_below(mih) : n_in + lanes_below(muh);
+      const int pl = inl ? nih + lanes_below(mil) : n_in + nuh + lanes_below(mul);
+      if ((inh || (whole_band && unh)) && ph < c.dm.kcap) st_dev(&tagd[ph], etag | (uint32_t)bh);
+      if ((inl || (whole_band && unl)) && pl < c.dm.kcap) st_dev(&tagd[pl], etag | (uint32_t)bl);
+      if (lane == 0 && (whole_band || n_in == kk)) st_dev(rtag, etag | (uint32_t)kk);
     }
     if (lane == 0) {
-      st_dev(&blk_cnt[out], kk);
-      st_dev(&c.sc.unit_acc[4 * unit], 0u);  // cleared for the next step
-      st_dev(&c.sc.unit_acc[4 * unit + 1], 0u);
-      st_dev(&c.sc.unit_acc[4 * unit + 2], eps_bits);  // the bound this selection used
+      sm.ok = ok;
+      sm.nin = n_in;
+      sm.nlist = n_unc;
     }
   }
+  __syncthreads();
+  if (!sm.ok) {
+    SD_TL(6);  // the fast top-k gave up: the full top-k runs
+    return false;
+  }
+  const int n_unc = sm.nlist, kr2 = kk - sm.nin;
+  if (kr2 > 0 && kr2 == n_unc) {  // every band block is taken: no exact keys needed
+    if (wv == 0)
+      for (int u = lane; u < n_unc; u += 64) {
+        const int blk = sm.ulist[u];
+        atomicOr(&sm.bm[blk >> 6], 1ull << (blk & 63));
+      }
+  } else if (kr2 > 0) {
+    SD_TL(7);  // the band's exact re-score starts
+    // exact keys of the band, one lane quad per (block, head), in passes of 64
+    for (int p0 = 0; p0 < n_unc * G; p0 += 64) {
+      const int pair = p0 + (tid >> 2);
+      const bool on = pair < n_unc * G;
+      const int u = on ? pair / G : 0, gg = on ? pair - u * G : 0;
+      const double U = exact_score_quad<D>(c, seq, hi, on ? sm.ulist[u] : 0, sm.qs + gg * D, on);
+      if (on && (tid & 3) == 0) sm.ue[pair] = U;
+    }
+    __syncthreads();
+    if (wv == 0) {
+      // exact keys of the listed blocks, two per lane (u = lane, 64 + lane),
+      // ranked by (exact key desc, index asc)
+      unsigned long long ek[2];
+#pragma unroll
+      for (int x = 0; x < 2; ++x) {
+        const int u = lane + kTileList * x;
+        ek[x] = 0ull;
+        if (u < n_unc) {
+          double best = sm.ue[u * G];
+#pragma unroll
+          for (int gg = 1; gg < G; ++gg) best = sm.ue[u * G + gg] > best ? sm.ue[u * G + gg] : best;
+          ek[x] = ((unsigned long long)order_key((float)best) << 32) | (uint32_t)~(uint32_t)sm.ulist[u];
+        }
+      }
+      int rank[2] = {0, 0};
+      for (int t = 0; t < n_unc; ++t) {
+        const unsigned long long src = t < kTileList ? ek[0] : ek[1];
+        const int tl = t & (kTileList - 1);
+        const unsigned long long o =
+            ((unsigned long long)(uint32_t)__builtin_amdgcn_readlane((int)(src >> 32), tl) << 32) |
+            (uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)src, tl);
+        rank[0] += o > ek[0] ? 1 : 0;
+        rank[1] += o > ek[1] ? 1 : 0;
+      }
+#pragma unroll
+      for (int x = 0; x < 2; ++x) {
+        const int u = lane + kTileList * x;
+        if (u < n_unc && rank[x] < kr2) {
+          const int blk = sm.ulist[u];
+          atomicOr(&sm.bm[blk >> 6], 1ull << (blk & 63));
+          if (tagd && sm.nin + rank[x] < c.dm.kcap)
+            st_dev(&tagd[sm.nin + rank[x]], etag | (uint32_t)blk);
+        }
+      }
+      if (tagd && lane == 0) st_dev(rtag, etag | (uint32_t)kk);
+    }
+  }
+  if (wv == 0) fast_out(c, unit, out, nw, kk, k_cap, blk_idx, blk_cnt, sm, eps_bits);
   return true;
 }
 
@@ -3059,8 +3287,12 @@ __global__ __launch_bounds__(256, 2) void k_step(Ctx c, SeqBatch b, int tiles_x,
     unsigned long long *tagd = c.sc.seltag + unit * c.dm.kcap;
     // the fast top-k publishes the count itself, right after the entries
     const size_t out = (size_t)i * c.dm.Hkv + h;
-    const bool fast_done = fast && topk_fast<D, G>(c, seq, unit, out, hi, g, q, blk_idx, blk_cnt, k_cap,
-                                                   smem_topk, tagd, &c.sc.rtag[unit], epoch);
+    const bool fast_done =
+        fast && (g.kk <= kTileList
+                     ? topk_fast<D, G>(c, seq, unit, out, hi, g, q, blk_idx, blk_cnt, k_cap,
+                                       smem_topk, tagd, &c.sc.rtag[unit], epoch)
+                     : topk_fast128<D, G>(c, seq, unit, out, hi, g, q, blk_idx, blk_cnt, k_cap,
+                                          smem_topk, tagd, &c.sc.rtag[unit], epoch));
     if (!fast_done) {
       unsigned long long *dmask = reinterpret_cast<unsigned long long *>(lrows + lrows_words);
       if (wide_unit(g.n_sc))

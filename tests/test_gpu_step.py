@@ -90,18 +90,22 @@ def test_fused_qwen128k_full():
     _check(harness.run_single_step(w, 2, fused=True))
 
 
-def test_fused_equal_scores_tie_order():
+@pytest.mark.parametrize("n_eq,ppm", [(161, 50_000), (100, 175_000)],
+                         ids=["k26_of_161_equal", "k90_of_100_equal"])
+def test_fused_equal_scores_tie_order(n_eq, ppm):
     """Blocks with bitwise equal summaries have equal scores: the one-launch
-    top-k must take them by index, as the oracle does."""
-    w = _w(synth.llama32k(), B=1, Hq=8, Hkv=2, N=16384)
-    log("case: fused equal-score ties")
+    top-k must take them by index, as the oracle does.  With k = 26 the
+    equal blocks fill the 64-key lists; with k = 90 the k-th place falls
+    among 100 equal blocks, inside the 128-key lists of the fast top-k."""
+    w = _w(synth.llama32k(), B=1, Hq=8, Hkv=2, N=16384, budget_ppm=[ppm, ppm])
+    log("case: fused equal-score ties, %d equal blocks, ppm %d" % (n_eq, ppm))
     x = synth.single_step(w, 4, N=w.N)
     K, V, q = x["K"], x["V"], x["q"]
     # block 40's keys scaled x4 (a bound well above the rest), copied over
-    # blocks 41..200 of KV head 0: 161 equal top scores
+    # blocks 41..40 + n_eq - 1 of KV head 0: n_eq equal top scores
     S = w.block_size[0]
     src = (K[0, 40 * S:41 * S, 0].float() * 4.0).to(torch.bfloat16)
-    for blk in range(40, 201):
+    for blk in range(40, 40 + n_eq):
         K[0, blk * S:(blk + 1) * S, 0] = src
     eng = harness.make_engine(w, w.N + 64)
     try:
