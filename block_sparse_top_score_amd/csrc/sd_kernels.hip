@@ -2830,6 +2830,11 @@ __global__ __launch_bounds__(256) void k_lfps_select(Ctx c, SeqBatch b, int32_t 
   uint32_t *c0w = reinterpret_cast<uint32_t *>(smem_raw + sizeof(LfpsSmem));  // bit rows
   const int tid = threadIdx.x;
   const int h = blockIdx.x % c.dm.Hkv, i = blockIdx.x / c.dm.Hkv;
+  // wpu workgroups per unit (blockIdx.y): each works out C, scores its share
+  // of C's passes of 128 blocks (pass x belongs to workgroup x % wpu) and
+  // writes their keys to the unit's global scratch; the last to arrive takes
+  // the k-th key and writes the selection
+  const int wpu = gridDim.y, wi = blockIdx.y;
   const HeadInfo hi = c.heads[h];
   const int seq = b.seq[i], N = b.len[i];
   const size_t unit = (size_t)seq * c.dm.Hkv + h, out = (size_t)i * c.dm.Hkv + h;
@@ -2844,7 +2849,6 @@ __global__ __launch_bounds__(256) void k_lfps_select(Ctx c, SeqBatch b, int32_t 
   int32_t *gl = c.sc.ulist + unit * c.dm.key_stride;
   uint32_t *gk = c.sc.ukeys + unit * c.dm.key_stride;
   auto lst_ld = [&](int p) -> int { return p < kLfpsLds ? sm.list[p] : ld_dev(&gl[p]); };
-  auto lst_st = [&](int p, int v) { if (p < kLfpsLds) sm.list[p] = v; else st_dev(&gl[p], v); };
   auto key_ld = [&](int p) -> uint32_t { return p < kLfpsLds ? sm.key[p] : ld_dev(&gk[p]); };
   auto key_st = [&](int p, uint32_t v) { if (p < kLfpsLds) sm.key[p] = v; else st_dev(&gk[p], v); };
   const uint16_t *qg = q + out * G * D;
@@ -2911,18 +2915,23 @@ __global__ __launch_bounds__(256) void k_lfps_select(Ctx c, SeqBatch b, int32_t 
   for (int x = j0; x < min(j0 + m, n_sc); ++x) mine += in_c(x) ? 1 : 0;
   int slot = 0, nC = 0;
   int o = wg_scan(mine, sm.red, slot, nC);
-  for (int x = j0; x < min(j0 + m, n_sc); ++x)
-    if (in_c(x)) lst_st(o++, x);
+  for (int x = j0; x < min(j0 + m, n_sc); ++x) {
+    if (!in_c(x)) continue;
+    // (past the LDS list each entry is written once, by its pass's owner)
+    if (o < kLfpsLds) sm.list[o] = x;
+    else if ((o >> 7) % wpu == wi) st_dev(&gl[o], x);
+    ++o;
+  }
   __syncthreads();
-  if (tid == 0) st_dev(&c.sc.unit_acc[4 * unit + 3], (uint32_t)nC);  // |C|, for inspection
+  if (tid == 0 && wi == 0) st_dev(&c.sc.unit_acc[4 * unit + 3], (uint32_t)nC);  // |C|, for inspection
   const int kq = min(g.kk, nC);
   if (kq == 0) {
-    if (tid == 0) st_dev(&blk_cnt[out], 0);
+    if (tid == 0 && wi == 0) st_dev(&blk_cnt[out], 0);
     return;
   }
   // 4. exact group scores: one lane quad per two blocks, each block's summary
-  // loaded once for all the group's heads
-  for (int p0 = 0; p0 < nC; p0 += 128) {
+  // loaded once for all the group's heads; this workgroup's passes
+  for (int p0 = 128 * wi; p0 < nC; p0 += 128 * wpu) {
     int blk[2];
     bool on[2];
 #pragma unroll
@@ -2935,7 +2944,19 @@ __global__ __launch_bounds__(256) void k_lfps_select(Ctx c, SeqBatch b, int32_t 
     exact_group_quads<D, G, 2>(c, seq, hi, blk, on, sm.qs, best);
 #pragma unroll
     for (int n = 0; n < 2; ++n)
-      if (on[n] && (tid & 3) == 0) key_st(p0 + 64 * n + (tid >> 2), order_key((float)best[n]));
+      if (on[n] && (tid & 3) == 0) {
+        const int p = p0 + 64 * n + (tid >> 2);
+        const uint32_t kv = order_key((float)best[n]);
+        if (wpu == 1) key_st(p, kv); else st_dev(&gk[p], kv);
+      }
+  }
+  if (wpu > 1) {
+    // the last workgroup of the unit to arrive has every key: those within
+    // the LDS list come to LDS, the rest are read from the scratch
+    uint32_t *ctr = &c.sc.arrive[unit * 4];
+    if (!arrive_last(ctr, (unsigned)wpu, reinterpret_cast<int *>(&sm.red[15]))) return;
+    if (tid == 0) st_dev(ctr, 0u);
+    for (int p = tid; p < min(nC, kLfpsLds); p += 256) sm.key[p] = ld_dev(&gk[p]);
   }
   __syncthreads();
   // 5. the kq-th largest key T: keys above T are in, of the keys equal to T
@@ -3568,9 +3589,12 @@ hipError_t launch_lfps_select(const Ctx &c, const SeqBatch &b, int max_blocks, c
   if (b.n <= 0) return hipSuccess;
   const size_t lds = sizeof(LfpsSmem) + sizeof(uint32_t) * 2 * (size_t)((max_blocks + 31) / 32 + 1);
   if (lds > 65536) return hipErrorInvalidValue;
+  // workgroups per unit: one per 512 blocks of the longest unit, at most 16
+  // (units of up to 1024 blocks keep one)
+  const int wpu = b.max_scored <= 1024 ? 1 : std::min(16, (b.max_scored + 511) / 512);
   SD_DISPATCH_DG(c.dm.d, c.dm.G,
-                 hipLaunchKernelGGL((k_lfps_select<D_, G_>), dim3(c.dm.Hkv * b.n), dim3(256), lds,
-                                    st, c, b, blk_idx, blk_cnt, k_cap, q));
+                 hipLaunchKernelGGL((k_lfps_select<D_, G_>), dim3(c.dm.Hkv * b.n, wpu), dim3(256),
+                                    lds, st, c, b, blk_idx, blk_cnt, k_cap, q));
   return hipGetLastError();
 }
 
