@@ -2313,7 +2313,12 @@ __device__ __attribute__((always_inline)) void attend_part(const Ctx &c, int i, 
       qa, W, pl, lmb, tok, 6);
 
   SD_TL(1);  // dense pages done (wave 0)
-  // the selection
+  // the selection.  Each lane's first selected page's entry is read while
+  // the count is awaited; when its tag is this step's the page resolves
+  // without a second round trip
+  const int t_pre = gw + lane * NW;
+  const unsigned long long e_pre =
+      si.tag ? ld_dev(&si.tag[min(div_m(t_pre, PPB), c.dm.kcap - 1)]) : 0ull;
   int cnt = si.cnt;
   if (si.rtag) {
     if (tid == 0) {
@@ -2348,7 +2353,8 @@ __device__ __attribute__((always_inline)) void attend_part(const Ctx &c, int i, 
           const int j = div_m(t, PPB), pp = t - j * PPB;
           int blk, hx = 0;
           if (si.tag) {  // published before the count; the tag confirms it
-            unsigned long long e = ld_dev(&si.tag[j]);
+            unsigned long long e = t == t_pre && (uint32_t)(e_pre >> 32) == si.epoch
+                                       ? e_pre : ld_dev(&si.tag[j]);
             const unsigned long long t0 = wall_clock64();
             while ((uint32_t)(e >> 32) != si.epoch && wall_clock64() - t0 < kWaitTicks)
               e = ld_dev(&si.tag[j]);
